@@ -1,0 +1,424 @@
+/*
+ * CPU oracle for sparse matrix-vector multiply-accumulate, y <- A*x + y.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this file.  No product code path calls
+ * it, and it shares no code, header or table with the GPU library.
+ *
+ * Plain single-threaded C.  Each function restates its definition from the
+ * source pages:
+ *   [P1] PMPP notes ch.14, "Sparse Matrices and Basic Formats (COO & CSR)"
+ *   [P2] PMPP notes ch.14, "Regularized Formats (ELL, Hybrid ELL-COO, JDS)"
+ *   [P3] "SpMV storage-format choice and performance comparison" (CUDA tuning
+ *        article), numbered sections
+ *   [P5] SpGEMM/AIA article, section 5.3 "common problems" (input checks)
+ *
+ * Arithmetic: products of two fp32 numbers are exact in fp64 (24+24 < 53
+ * significand bits); sums are taken in fp64 in row order.  Values are moved by
+ * the builders as raw 32-bit patterns, never re-rounded.
+ *
+ * Readings of points the pages leave open (each listed in the design notes):
+ *   - SpMV accumulates (y += A x), as the P1 background and kernels define it.
+ *   - ELL padding: value +0.0f (bit pattern 0), column index 0.
+ *   - HYB tail: entries past position K of each row, rows in order, positions
+ *     in order; ELL part of width min(K, W).
+ *   - JDS: rows sorted by length, longest first, ties by ascending original row.
+ *   - The selector's comparison operators (lost from P3 4.3) are restored as
+ *     W*R <= 2*nnz -> ELL; nnz < 10*R -> COO; W*R > 5*nnz -> HYB; else CSR,
+ *     with the HYB width/budget extension described at orc_select().
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Status numbers: the same values the library documents for its C ABI. */
+enum {
+    ORC_OK = 0,
+    ORC_ERR_INVALID_ARG = 1,
+    ORC_ERR_BAD_ROWPTRS = 2,
+    ORC_ERR_BAD_COLIDX = 3,
+    ORC_ERR_BAD_ROWIDX = 4,
+    ORC_ERR_TOO_LARGE = 5,
+};
+
+/* Format numbers for the selector's answer (same values as the C ABI). */
+enum {
+    ORC_FMT_COO_ATOMIC = 1,
+    ORC_FMT_COO_SEGMENTED = 2,
+    ORC_FMT_CSR_SCALAR = 3,
+    ORC_FMT_CSR_VECTOR = 4,
+    ORC_FMT_ELL = 5,
+    ORC_FMT_HYB = 6,
+    ORC_FMT_JDS = 7,
+    ORC_FMT_CSR_MERGE = 8,
+};
+
+#define ORC_INT32_MAX 2147483647LL
+
+/* ------------------------------------------------------------------------ */
+/* Input checks [P1 CSR section: rowPtrs[numRows] = nnz; P5 5.3: row_ptr    */
+/* monotone, every column index below the column count, value length = nnz] */
+/* ------------------------------------------------------------------------ */
+
+int orc_validate_csr(int64_t R, int64_t C, int64_t nnz, const int32_t *row_ptrs,
+                     const int32_t *col_idx)
+{
+    if (R < 0 || C < 0 || nnz < 0 || R > ORC_INT32_MAX || C > ORC_INT32_MAX ||
+        nnz > ORC_INT32_MAX || row_ptrs == NULL || (nnz > 0 && col_idx == NULL))
+        return ORC_ERR_INVALID_ARG;
+    if (row_ptrs[0] != 0)
+        return ORC_ERR_BAD_ROWPTRS;
+    for (int64_t r = 0; r < R; ++r)
+        if (row_ptrs[r + 1] < row_ptrs[r])
+            return ORC_ERR_BAD_ROWPTRS;
+    if ((int64_t)row_ptrs[R] != nnz)
+        return ORC_ERR_BAD_ROWPTRS;
+    for (int64_t i = 0; i < nnz; ++i)
+        if (col_idx[i] < 0 || (int64_t)col_idx[i] >= C)
+            return ORC_ERR_BAD_COLIDX;
+    return ORC_OK;
+}
+
+int orc_validate_coo(int64_t R, int64_t C, int64_t nnz, const int32_t *row_idx,
+                     const int32_t *col_idx)
+{
+    if (R < 0 || C < 0 || nnz < 0 || R > ORC_INT32_MAX || C > ORC_INT32_MAX ||
+        nnz > ORC_INT32_MAX || (nnz > 0 && (row_idx == NULL || col_idx == NULL)))
+        return ORC_ERR_INVALID_ARG;
+    for (int64_t i = 0; i < nnz; ++i)
+        if (row_idx[i] < 0 || (int64_t)row_idx[i] >= R)
+            return ORC_ERR_BAD_ROWIDX;
+    for (int64_t i = 0; i < nnz; ++i)
+        if (col_idx[i] < 0 || (int64_t)col_idx[i] >= C)
+            return ORC_ERR_BAD_COLIDX;
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* SpMV by definition [P1 background: SpMV computes A*X + Y; P1 CSR section:*/
+/* row r holds value/colIdx[rowPtrs[r] .. rowPtrs[r+1]-1]]                  */
+/*                                                                          */
+/*   y_ref[r] = y[r] + sum_i value[i] * x[colIdx[i]]                        */
+/*   bound[r] = |y[r]| + sum_i |value[i] * x[colIdx[i]]|                    */
+/* ------------------------------------------------------------------------ */
+
+void orc_spmv_csr(int64_t R, const int32_t *row_ptrs, const int32_t *col_idx,
+                  const float *values, const float *x, const float *y_in,
+                  double *y_ref, double *bound)
+{
+    for (int64_t r = 0; r < R; ++r) {
+        double s = (double)y_in[r];
+        double b = fabs((double)y_in[r]);
+        for (int64_t i = row_ptrs[r]; i < row_ptrs[r + 1]; ++i) {
+            double p = (double)values[i] * (double)x[col_idx[i]];
+            s += p;
+            b += fabs(p);
+        }
+        y_ref[r] = s;
+        if (bound)
+            bound[r] = b;
+    }
+}
+
+/* The same definition over COO triples (no grouping needed): used to check
+ * that COO input and its CSR conversion describe the same matrix. */
+void orc_spmv_coo(int64_t R, int64_t nnz, const int32_t *row_idx, const int32_t *col_idx,
+                  const float *values, const float *x, const float *y_in,
+                  double *y_ref, double *bound)
+{
+    for (int64_t r = 0; r < R; ++r) {
+        y_ref[r] = (double)y_in[r];
+        if (bound)
+            bound[r] = fabs((double)y_in[r]);
+    }
+    for (int64_t i = 0; i < nnz; ++i) {
+        double p = (double)values[i] * (double)x[col_idx[i]];
+        y_ref[row_idx[i]] += p;
+        if (bound)
+            bound[row_idx[i]] += fabs(p);
+    }
+}
+
+/* Row-wise acceptance test: |y_gpu - y_ref| <= rtol * bound, and y_gpu finite
+ * wherever y_ref is.  Where y_ref is not finite, y_gpu must not be finite
+ * either (and an infinity must carry the same sign).  Returns the number of
+ * failing rows; *first_bad is the first such row (or -1); *worst is the
+ * largest |y_gpu - y_ref| / bound over rows with a nonzero bound. */
+int64_t orc_check(int64_t R, const float *y_gpu, const double *y_ref, const double *bound,
+                  double rtol, int64_t *first_bad, double *worst)
+{
+    int64_t bad = 0;
+    double w = 0.0;
+    if (first_bad)
+        *first_bad = -1;
+    for (int64_t r = 0; r < R; ++r) {
+        double g = (double)y_gpu[r];
+        double ref = y_ref[r];
+        int ok;
+        if (isfinite(ref)) {
+            double err = fabs(g - ref);
+            ok = isfinite(g) && err <= rtol * bound[r];
+            if (bound[r] > 0.0 && isfinite(g) && err / bound[r] > w)
+                w = err / bound[r];
+        } else if (isnan(ref)) {
+            ok = isnan(g);
+        } else {
+            ok = isinf(g) && (signbit(g) == signbit(ref));
+        }
+        if (!ok) {
+            if (bad == 0 && first_bad)
+                *first_bad = r;
+            ++bad;
+        }
+    }
+    if (worst)
+        *worst = w;
+    return bad;
+}
+
+/* ------------------------------------------------------------------------ */
+/* COO -> CSR [P1 COO section: one (row, col, value) per nonzero; P1 CSR    */
+/* section: nonzeros grouped by row, rowPtrs[r] = offset of row r's first   */
+/* nonzero, rowPtrs[numRows] = nnz].  Count per row, prefix sum of the      */
+/* counts, then place entries in input order, so each row keeps the order   */
+/* its entries had in the COO input.                                        */
+/* ------------------------------------------------------------------------ */
+
+int orc_coo_to_csr(int64_t R, int64_t nnz, const int32_t *row_idx, const int32_t *col_idx,
+                   const uint32_t *values, int32_t *row_ptrs, int32_t *csr_col,
+                   uint32_t *csr_val)
+{
+    int64_t *next = (int64_t *)calloc((size_t)R + 1, sizeof(int64_t));
+    if (!next)
+        return ORC_ERR_INVALID_ARG;
+    for (int64_t i = 0; i < nnz; ++i)
+        next[row_idx[i] + 1] += 1;                      /* counts, shifted by one */
+    for (int64_t r = 0; r < R; ++r)
+        next[r + 1] += next[r];                         /* running total */
+    for (int64_t r = 0; r <= R; ++r)
+        row_ptrs[r] = (int32_t)next[r];
+    for (int64_t i = 0; i < nnz; ++i) {
+        int64_t p = next[row_idx[i]]++;
+        csr_col[p] = col_idx[i];
+        csr_val[p] = values[i];
+    }
+    free(next);
+    return ORC_OK;
+}
+
+/* CSR -> COO: the row index of every nonzero. */
+void orc_csr_to_coo(int64_t R, const int32_t *row_ptrs, int32_t *row_idx)
+{
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t i = row_ptrs[r]; i < row_ptrs[r + 1]; ++i)
+            row_idx[i] = (int32_t)r;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Row-length statistics [P3 4.1: nonzero-per-row histogram and row-length  */
+/* variance; P3 4.3: mean and max row length; "Introduction to sparse       */
+/* computing", parallel-efficiency check: max/mean of the work per worker]. */
+/* out[0] = W (max length), out[1] = sum len, out[2] = sum len^2,           */
+/* out[3] = number of empty rows.                                           */
+/* ------------------------------------------------------------------------ */
+
+void orc_row_stats(int64_t R, const int32_t *row_ptrs, int64_t *out)
+{
+    int64_t W = 0, s1 = 0, s2 = 0, empty = 0;
+    for (int64_t r = 0; r < R; ++r) {
+        int64_t len = (int64_t)row_ptrs[r + 1] - row_ptrs[r];
+        if (len > W)
+            W = len;
+        s1 += len;
+        s2 += len * len;
+        if (len == 0)
+            ++empty;
+    }
+    out[0] = W;
+    out[1] = s1;
+    out[2] = s2;
+    out[3] = empty;
+}
+
+/* hist[l] = number of rows of length l, l = 0..W. */
+void orc_len_hist(int64_t R, const int32_t *row_ptrs, int64_t W, int64_t *hist)
+{
+    for (int64_t l = 0; l <= W; ++l)
+        hist[l] = 0;
+    for (int64_t r = 0; r < R; ++r)
+        hist[row_ptrs[r + 1] - row_ptrs[r]] += 1;
+}
+
+/* ------------------------------------------------------------------------ */
+/* ELL [P2 ELL section]: (1) pad every row with zeros to the longest row's  */
+/* length W (column indices padded as well), (2) store the padded R x W     */
+/* array column-major, so slot t of row r sits at i = t*R + r.  nnzPerRow   */
+/* keeps each row's true length.  Refused when R*W exceeds int32 range.     */
+/*                                                                          */
+/* HYB [P2 hybrid ELL-COO section]: before building the ELL part, the       */
+/* entries of a row beyond position K go to a separate COO list; the ELL    */
+/* part then has width min(K, W).  This builder with K >= W is plain ELL.   */
+/* ------------------------------------------------------------------------ */
+
+int64_t orc_hyb_tail_count(int64_t R, const int32_t *row_ptrs, int64_t K)
+{
+    int64_t n = 0;
+    for (int64_t r = 0; r < R; ++r) {
+        int64_t len = (int64_t)row_ptrs[r + 1] - row_ptrs[r];
+        if (len > K)
+            n += len - K;
+    }
+    return n;
+}
+
+int orc_csr_to_hyb(int64_t R, const int32_t *row_ptrs, const int32_t *col_idx,
+                   const uint32_t *values, int64_t Kw, int32_t *ell_col, uint32_t *ell_val,
+                   int32_t *ell_nnz, int32_t *tail_row, int32_t *tail_col, uint32_t *tail_val)
+{
+    if (Kw < 0)
+        return ORC_ERR_INVALID_ARG;
+    if (R * Kw > ORC_INT32_MAX)
+        return ORC_ERR_TOO_LARGE;
+    /* padded slots: value +0.0f, column 0 */
+    for (int64_t i = 0; i < R * Kw; ++i) {
+        ell_col[i] = 0;
+        ell_val[i] = 0u;
+    }
+    int64_t tail = 0;
+    for (int64_t r = 0; r < R; ++r) {
+        int64_t start = row_ptrs[r];
+        int64_t len = (int64_t)row_ptrs[r + 1] - start;
+        int64_t in_ell = len < Kw ? len : Kw;
+        for (int64_t t = 0; t < in_ell; ++t) {
+            ell_col[t * R + r] = col_idx[start + t];
+            ell_val[t * R + r] = values[start + t];
+        }
+        ell_nnz[r] = (int32_t)in_ell;
+        for (int64_t t = in_ell; t < len; ++t) {
+            tail_row[tail] = (int32_t)r;
+            tail_col[tail] = col_idx[start + t];
+            tail_val[tail] = values[start + t];
+            ++tail;
+        }
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* JDS [P2 JDS section]: (1) group by row, (2) sort rows by nonzero count,  */
+/* longest first, recording each sorted row's original index, (3) store the */
+/* sorted rows column-major without padding, (4) iterPtr[t] marks where     */
+/* iteration (jagged column) t starts.  Entry t of sorted row s lives at    */
+/* iterPtr[t] + s; iterPtr[W] = nnz.                                        */
+/* ------------------------------------------------------------------------ */
+
+static const int32_t *g_sort_len;
+
+static int orc_cmp_len_desc(const void *a, const void *b)
+{
+    int32_t ra = *(const int32_t *)a, rb = *(const int32_t *)b;
+    int32_t la = g_sort_len[ra], lb = g_sort_len[rb];
+    if (la != lb)
+        return la > lb ? -1 : 1;     /* longer rows first */
+    return ra < rb ? -1 : (ra > rb); /* equal lengths keep original order */
+}
+
+int orc_csr_to_jds(int64_t R, const int32_t *row_ptrs, const int32_t *col_idx,
+                   const uint32_t *values, int64_t W, int32_t *perm, int32_t *jds_len,
+                   int32_t *iter_ptr, int32_t *jds_col, uint32_t *jds_val)
+{
+    int32_t *len = (int32_t *)malloc(((size_t)R + 1) * sizeof(int32_t));
+    if (!len)
+        return ORC_ERR_INVALID_ARG;
+    for (int64_t r = 0; r < R; ++r) {
+        len[r] = row_ptrs[r + 1] - row_ptrs[r];
+        perm[r] = (int32_t)r;
+    }
+    g_sort_len = len;
+    qsort(perm, (size_t)R, sizeof(int32_t), orc_cmp_len_desc);
+    for (int64_t s = 0; s < R; ++s)
+        jds_len[s] = len[perm[s]];
+    /* iteration t holds one entry for every sorted row longer than t */
+    iter_ptr[0] = 0;
+    for (int64_t t = 0; t < W; ++t) {
+        int64_t rows = 0;
+        for (int64_t s = 0; s < R && jds_len[s] > t; ++s)
+            ++rows;
+        iter_ptr[t + 1] = iter_ptr[t] + (int32_t)rows;
+    }
+    for (int64_t s = 0; s < R; ++s) {
+        int64_t start = row_ptrs[perm[s]];
+        for (int64_t t = 0; t < jds_len[s]; ++t) {
+            jds_col[iter_ptr[t] + s] = col_idx[start + t];
+            jds_val[iter_ptr[t] + s] = values[start + t];
+        }
+    }
+    free(len);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Format selector [P3 4.3, automatic selection by mean and max row length; */
+/* P3 4.1: HYB with ELL width 20 for rows mostly 10-20 long; P3 5.2: power- */
+/* law graphs -> merge-based CSR; P3 2.2: one vector group per row].        */
+/*                                                                          */
+/* With mean = nnz/R, comparisons kept exact in integers:                   */
+/*   W*R <= 2*nnz            -> ELL                                         */
+/*   nnz <  10*R             -> COO (segmented)                             */
+/*   W*R >  5*nnz            -> HYB with K = smallest k such that at least  */
+/*                              99% of rows have length <= k, taken only    */
+/*                              if R*K <= 1.5*nnz, else merge-based CSR     */
+/*   otherwise               -> CSR vector, lanes = smallest power of two   */
+/*                              >= ceil(mean), clamped to [2, 64]           */
+/* hyb_width > 0 replaces the percentile K; lanes > 0 replaces the lane     */
+/* rule.  hist has W+1 entries.  out[0]=format, out[1]=K (0 if not HYB),    */
+/* out[2]=lanes (0 if not CSR vector).                                      */
+/* ------------------------------------------------------------------------ */
+
+int64_t orc_hyb_width(int64_t R, int64_t W, const int64_t *hist)
+{
+    /* smallest k with 100 * #{len <= k} >= 99 * R */
+    int64_t cum = 0;
+    for (int64_t k = 0; k <= W; ++k) {
+        cum += hist[k];
+        if (100 * cum >= 99 * R)
+            return k;
+    }
+    return W;
+}
+
+int64_t orc_vector_lanes(int64_t R, int64_t nnz)
+{
+    int64_t mean_ceil = R > 0 ? (nnz + R - 1) / R : 0;
+    int64_t L = 2;
+    while (L < mean_ceil && L < 64)
+        L *= 2;
+    return L;
+}
+
+void orc_select(int64_t R, int64_t nnz, int64_t W, const int64_t *hist, int64_t hyb_width,
+                int64_t lanes, int64_t *out)
+{
+    out[0] = ORC_FMT_ELL;
+    out[1] = 0;
+    out[2] = 0;
+    if (W * R <= 2 * nnz)
+        return;                                   /* ELL */
+    if (nnz < 10 * R) {
+        out[0] = ORC_FMT_COO_SEGMENTED;
+        return;
+    }
+    if (W * R > 5 * nnz) {
+        int64_t K = hyb_width > 0 ? hyb_width : orc_hyb_width(R, W, hist);
+        if (2 * R * K <= 3 * nnz) {               /* R*K <= 1.5*nnz */
+            out[0] = ORC_FMT_HYB;
+            out[1] = K;
+        } else {
+            out[0] = ORC_FMT_CSR_MERGE;
+        }
+        return;
+    }
+    out[0] = ORC_FMT_CSR_VECTOR;
+    out[2] = lanes > 0 ? lanes : orc_vector_lanes(R, nnz);
+}

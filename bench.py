@@ -1,0 +1,240 @@
+"""SpMV benchmark on one MI355X: y <- A*x + y, fp32, synthetic matrices.
+
+Default workload: 1,000,000 x 1,000,000, exactly 5 random columns per row
+(5M nonzeros), the format the selector picks (ELL).  One step = one full
+y <- A x + y pass of that format with every input resident in HBM and the
+caches flushed just before it (a 1 GiB fill kernel, untimed), timed with HIP
+events on the stream the kernels run on.
+
+Printed (one JSON line on stdout): GFLOP/s (2 flops per nonzero), effective
+GB/s on the algorithmic bytes
+    B_alg = 8*nnz + 4*(R+1) + 4*C + 8*R      (values+columns, row structure,
+                                               x once, y read+write)
+the fraction of the 8 TB/s HBM peak, every format's figures on the same
+matrix, the builders' times, and the single-threaded CPU oracle as baseline.
+
+    python bench.py [--steps K] [--warmup W] [--config c2] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, vendor figure
+FLUSH_BYTES = 1 << 30       # > 256 MB MALL + 8 x 4 MB L2
+FORMATS = ["coo_atomic", "coo_segmented", "csr_scalar", "csr_vector", "ell", "hyb", "jds",
+           "csr_merge"]
+WORKLOAD_NAMES = {
+    "c1": "laplacian2d_256 (65,536 rows, 5-point, 326,656 nnz)",
+    "c2": "random_rows_1Mx5 (1,000,000 x 1,000,000, 5 random cols/row, 5,000,000 nnz)",
+    "c3": "stencil27_128 (2,097,152 rows, 27-point truncated, 55,742,968 nnz)",
+    "c4": "skewed_2M (2,000,000 rows, 10-20 nnz + 50 rows of 1000-5000, HYB width 20)",
+    "c5": "power_law_4M (4,000,000 rows, Zipf 2.1 row lengths, ~64M nnz)",
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def alg_bytes(R, C, nnz):
+    return 8 * nnz + 4 * (R + 1) + 4 * C + 8 * R
+
+
+def time_format(spmv, torch, h, x, y, steps, warmup, flush_buf, flush=True):
+    """Per-step kernel time (ms) with an untimed cache flush before each step."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        if flush:
+            flush_buf.zero_()
+        h.run(x, y)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        if flush:
+            flush_buf.zero_()
+        a.record(stream)
+        h.run(x, y)
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return [a.elapsed_time(b) for a, b in evs], wall
+
+
+def cpu_baseline(w, budget_s=10.0):
+    """The oracle as it is (single thread, fp64 sums) on full passes of the
+    same matrix, repeated for about `budget_s` seconds."""
+    import oracle
+    oracle.spmv_csr(w.row_ptrs, w.col_idx, w.values, w.x, w.y)  # load / warm
+    n, t_total = 0, 0.0
+    while t_total < budget_s or n < 3:
+        t0 = time.perf_counter()
+        oracle.spmv_csr(w.row_ptrs, w.col_idx, w.values, w.x, w.y)
+        t_total += time.perf_counter() - t0
+        n += 1
+    t = t_total / n
+    return {"value": round(2 * w.nnz / t / 1e9, 4), "unit": "GFLOP/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n} full passes of the same {w.num_rows}-row matrix "
+                      f"({w.nnz} nnz), {t * 1e3:.1f} ms each, single thread, fp64 sums"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c2", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--format", default="auto")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only-selected", action="store_true",
+                    help="time only the selected format (for profiling runs)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this engine runs on one GPU; --gpus N > 1 is not supported "
+              "(the row-sharded multi-GPU design is documented, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import oracle
+    import spmv_storage_formats_amd as spmv
+    from spmv_storage_formats_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    spmv.load_library()
+    log(f"generating {args.config}")
+    w = synth.workload(args.config)
+    R, C, nnz = w.num_rows, w.num_cols, w.nnz
+    B = alg_bytes(R, C, nnz)
+    flops = 2 * nnz
+    rp = torch.from_numpy(w.row_ptrs).to(dev)
+    ci = torch.from_numpy(w.col_idx).to(dev)
+    va = torch.from_numpy(w.values).to(dev)
+    x = torch.from_numpy(w.x).to(dev)
+    y0 = torch.from_numpy(w.y).to(dev)
+    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    y_ref, bound = oracle.spmv_csr(w.row_ptrs, w.col_idx, w.values, w.x, w.y)
+
+    kw = {"hyb_width": 20} if args.config == "c4" else {}
+
+    def build_and_check(fmt):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        h = spmv.build(fmt, rp, ci, va, C, **kw)
+        build_ms = (time.perf_counter() - t0) * 1e3
+        y = y0.clone()
+        h.run(x, y)
+        torch.cuda.synchronize()
+        n_bad, first, worst = oracle.check(y.cpu().numpy(), y_ref, bound)
+        if n_bad:
+            raise SystemExit(f"parity failure {args.config}/{fmt}: {n_bad} rows (first {first})")
+        return h, build_ms, worst
+
+    log(f"building {args.format}")
+    h, build_ms, worst = build_and_check(args.format)
+    selected = h.format
+    log(f"selected {selected}; parity ok (worst err/bound {worst:.2e}); timing {args.steps} steps")
+    y = y0.clone()
+    times, wall = time_format(spmv, torch, h, x, y, args.steps, args.warmup, flush_buf)
+    ms = statistics.mean(times)
+    med = statistics.median(times)
+    warm_times, _ = time_format(spmv, torch, h, x, y, args.steps, args.warmup, flush_buf,
+                                flush=False)
+    gbs = B / (ms * 1e-3) / 1e9
+
+    # the same matrix in every format (parity-checked, cold-cache timing)
+    per_format = {}
+    if not args.only_selected:
+        for fmt in FORMATS:
+            try:
+                hf, bms, wst = build_and_check(fmt)
+            except spmv.SpmvError as e:
+                per_format[fmt] = {"refused": e.name}
+                continue
+            tf, _ = time_format(spmv, torch, hf, x, y0.clone(), max(10, args.steps // 2), 2,
+                                flush_buf)
+            mf = statistics.median(tf)
+            per_format[fmt] = {
+                "us_median": round(mf * 1e3, 2),
+                "gflops": round(flops / (mf * 1e-3) / 1e9, 1),
+                "gbs_alg": round(B / (mf * 1e-3) / 1e9, 1),
+                "frac_hbm": round(B / (mf * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "build_ms": round(bms, 2),
+                "device_MB": round(hf.info["device_bytes"] / 1e6, 1),
+                "worst_err_over_bound": float(f"{wst:.3g}"),
+            }
+            log(f"{fmt}: {per_format[fmt]}")
+            hf.close()
+
+    traffic = None
+    prof = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(prof):
+        with open(prof) as f:
+            tr = json.load(f)
+        key = f"{args.config}/{selected}"
+        if key in tr and tr[key].get("kernel_source_sha") == kernel_source_sha():
+            traffic = tr[key]["hbm_bytes_per_launch"]
+
+    result = {
+        "metric": "SpMV GFLOP/s and effective HBM GB/s (% of MI355X peak) per format, 1 GPU",
+        "value": round(flops / (ms * 1e-3) / 1e9, 2),
+        "unit": "GFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded), inputs resident in HBM, caches flushed before each step",
+        "config": {"workload": WORKLOAD_NAMES[args.config], "format": selected,
+                   "rows": R, "cols": C, "nnz": nnz, "parallelism": "single GPU"},
+        "effective_gbs": round(gbs, 1),
+        "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "ms_median": round(med, 5),
+        "warm_ms_per_step": round(statistics.mean(warm_times), 5),
+        "wall_s_timed_loop_incl_flush": round(wall, 4),
+        "build_ms": round(build_ms, 2),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "bytes_per_launch_alg": B},
+        "formats": per_format,
+    }
+    if not args.no_cpu:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def kernel_source_sha():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "spmv_storage_formats_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,254 @@
+/*
+ * spmv.h -- C ABI of the MI355X (gfx950) sparse matrix-vector
+ * multiply-accumulate engine.
+ *
+ * Operation: y <- A*x + y, with A sparse (fp32 values, int32 indices) and x, y
+ * dense fp32 vectors.  This is the SpMV defined on the PMPP notes page
+ * "Sparse Matrices and Basic Formats (COO & CSR)", background section:
+ * sparse matrix-vector multiplication AND accumulation, the core of iterative
+ * solvers such as conjugate gradient, with a standard library interface.
+ *
+ * Pages cited below:
+ *   [COO/CSR]   PMPP notes ch.14, "Sparse Matrices and Basic Formats (COO & CSR)"
+ *   [REG]       PMPP notes ch.14, "Regularized Formats (ELL, Hybrid ELL-COO, JDS)"
+ *   [CHOICE]    "SpMV storage-format choice and performance comparison"
+ *               (CUDA tuning article), numbered sections
+ *   [INTRO]     "Introduction to sparse computing and locating performance
+ *               bottlenecks", section on the three checks (density, memory
+ *               efficiency, parallel efficiency)
+ *   [SPGEMM]    SpGEMM/AIA article, section 5.3 (input checks for CSR)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Device pointers.  Every array argument named *_dev is a device pointer
+ *    on the current HIP device (e.g. torch.Tensor.data_ptr() of a cuda
+ *    tensor).  Host pointers are named *_host.
+ *  - Streams.  `stream` is a hipStream_t passed as void* (NULL = the null
+ *    stream).  Work is ordered on that stream.
+ *  - Index types.  int32, signed.  nnz, rows and columns are below 2^31; an
+ *    ELL slot index t*R + r must also stay below 2^31 (else
+ *    SPMV_ERR_TOO_LARGE).
+ *  - Ownership.  The caller owns every input array, x and y.  A handle owns
+ *    device copies of every format array it needs; inputs may be freed or
+ *    reused as soon as spmv_build / spmv_build_coo return.  spmv_destroy
+ *    frees the handle's memory.
+ *  - Synchronisation.  spmv_analyze, spmv_build, spmv_build_coo and
+ *    spmv_coo_to_csr are host-synchronous (they read row statistics back and
+ *    wait for their own stream before returning).  spmv_run is asynchronous on
+ *    `stream`: it allocates nothing, never synchronises and only enqueues
+ *    kernels.
+ *  - Errors.  Every call returns a spmv_status; nothing throws across the ABI.
+ *    On error no handle is returned (*out is set to NULL) and no memory is
+ *    leaked.  A HIP runtime or launch failure maps to SPMV_ERR_HIP.
+ *  - Concurrency.  A handle is read-only after build; it may be run from
+ *    several streams at once provided each run writes a distinct y.  x and y
+ *    must not overlap.
+ */
+#ifndef SPMV_MI355X_H
+#define SPMV_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum spmv_status {
+    SPMV_OK = 0,
+    SPMV_ERR_INVALID_ARG = 1,  /* null pointer, negative size, bad option      */
+    SPMV_ERR_BAD_ROWPTRS = 2,  /* rowPtrs[0] != 0, decreasing, or != nnz at end */
+    SPMV_ERR_BAD_COLIDX = 3,   /* a column index outside [0, num_cols)          */
+    SPMV_ERR_BAD_ROWIDX = 4,   /* a COO row index outside [0, num_rows)         */
+    SPMV_ERR_TOO_LARGE = 5,    /* format exceeds int32 slots or opts.max_bytes  */
+    SPMV_ERR_OOM = 6,          /* device allocation failed                      */
+    SPMV_ERR_HIP = 7,          /* HIP runtime or kernel launch error            */
+    SPMV_ERR_DEVICE = 8        /* handle used on another device than its own    */
+} spmv_status;
+
+/* Storage formats / kernels.  SPMV_AUTO lets the selector choose. */
+typedef enum spmv_format {
+    SPMV_AUTO = 0,
+    SPMV_COO_ATOMIC = 1,    /* one lane per nonzero, atomic add [COO/CSR, COO kernel]       */
+    SPMV_COO_SEGMENTED = 2, /* wave-wide segmented sum of row runs, one atomic per run     */
+    SPMV_CSR_SCALAR = 3,    /* one lane per row, row pointers staged in LDS [COO/CSR, CSR
+                               kernel; CHOICE 2.1 and 4.2]                                  */
+    SPMV_CSR_VECTOR = 4,    /* a group of 2..64 lanes per row [CHOICE 2.2]                 */
+    SPMV_ELL = 5,           /* padded, column-major, one lane per row [REG, ELL]           */
+    SPMV_HYB = 6,           /* ELL of width K + COO tail [REG, hybrid; CHOICE 3.2, 4.1]    */
+    SPMV_JDS = 7,           /* rows sorted by length, jagged column-major [REG, JDS]       */
+    SPMV_CSR_MERGE = 8      /* merge-path: equal shares of rows+nonzeros per block
+                               [CHOICE 5.2; INTRO, parallel efficiency]                    */
+} spmv_format;
+
+typedef struct spmv_opts {
+    int32_t hyb_width;      /* HYB: ELL width K.  <= 0: smallest width that holds 99% of
+                               rows entirely (the 99th percentile of row length).          */
+    int32_t lanes_per_row;  /* CSR vector: 1,2,4,...,64.  0: smallest power of two >=
+                               ceil(mean row length), clamped to [2, 64].                  */
+    int32_t validate;       /* nonzero: also check every column index (one pass over
+                               colIdx).  Row pointers are always checked.                  */
+    int32_t jds_depth;      /* JDS: depth of one tile (jagged columns per wave).  0: 128.  */
+    int64_t max_bytes;      /* > 0: refuse (SPMV_ERR_TOO_LARGE) a format whose device
+                               arrays would exceed this many bytes.                        */
+} spmv_opts;
+
+/* Fills the defaults: hyb_width 0, lanes 0, validate 1, jds_depth 0, max_bytes 0. */
+void spmv_opts_default(spmv_opts *opts);
+
+/* Row-length statistics [CHOICE 4.1 histogram/variance, 4.3 mean and max;
+ * INTRO: max/mean of work per worker]. */
+typedef struct spmv_stats {
+    int64_t num_rows;
+    int64_t num_cols;
+    int64_t nnz;
+    int64_t max_len;     /* W = longest row                         */
+    int64_t sum_len_sq;  /* sum over rows of len^2 (variance = E[len^2] - mean^2) */
+    int64_t empty_rows;
+} spmv_stats;
+
+/* What a handle holds (spmv_get_info). */
+typedef struct spmv_info {
+    int32_t format;        /* built format (never SPMV_AUTO)              */
+    int32_t hyb_width;     /* K used by HYB, else 0                       */
+    int32_t lanes_per_row; /* lanes used by CSR vector, else 0            */
+    int32_t ell_width;     /* width of the ELL arrays (ELL: W; HYB: min(K, W)) */
+    spmv_stats stats;
+    int64_t tail_nnz;      /* HYB: entries in the COO tail                */
+    int64_t num_tiles;     /* JDS: wave tiles; CSR merge: blocks          */
+    int64_t device_bytes;  /* device memory owned by the handle           */
+} spmv_info;
+
+/* Arrays a handle can export (spmv_export) for bit-exact comparison. */
+typedef enum spmv_array {
+    SPMV_A_ROW_PTRS = 0,   /* int32 [R+1]   CSR formats                       */
+    SPMV_A_COL_IDX = 1,    /* int32 [nnz]   CSR and COO formats               */
+    SPMV_A_VALUES = 2,     /* fp32  [nnz]   CSR and COO formats               */
+    SPMV_A_ROW_IDX = 3,    /* int32 [nnz]   COO formats (sorted by row)       */
+    SPMV_A_ELL_COL = 4,    /* int32 [R*w]   ELL/HYB, slot t of row r at t*R+r */
+    SPMV_A_ELL_VAL = 5,    /* fp32  [R*w]                                     */
+    SPMV_A_ELL_NNZ = 6,    /* int32 [R]     entries of row r in the ELL part  */
+    SPMV_A_TAIL_ROW = 7,   /* int32 [tail]  HYB COO tail                      */
+    SPMV_A_TAIL_COL = 8,   /* int32 [tail]                                    */
+    SPMV_A_TAIL_VAL = 9,   /* fp32  [tail]                                    */
+    SPMV_A_JDS_PERM = 10,  /* int32 [R]     original row of sorted row s      */
+    SPMV_A_JDS_LEN = 11,   /* int32 [R]     length of sorted row s            */
+    SPMV_A_JDS_ITER_PTR = 12, /* int32 [W+1] start of jagged column t         */
+    SPMV_A_JDS_COL = 13,   /* int32 [nnz]   entry t of sorted row s at iterPtr[t]+s */
+    SPMV_A_JDS_VAL = 14,   /* fp32  [nnz]                                     */
+    SPMV_A_LEN_HIST = 15   /* int64 [W+1]   rows of each length (every handle) */
+} spmv_array;
+
+typedef struct spmv_handle spmv_handle;
+
+/*
+ * spmv_analyze -- input checks and row-length statistics of a CSR matrix.
+ *   Checks [COO/CSR, CSR section: rowPtrs[numRows] = nnz; SPGEMM 5.3: row_ptr
+ *   monotone, column index below the column count, value count = nnz]:
+ *   rowPtrs[0] = 0, rowPtrs non-decreasing, rowPtrs[R] = nnz
+ *   (-> SPMV_ERR_BAD_ROWPTRS), and, if `validate`, 0 <= colIdx < C
+ *   (-> SPMV_ERR_BAD_COLIDX).  Row pointers are checked first.
+ *   row_ptrs_dev: int32[R+1]; col_idx_dev: int32[nnz] (may be NULL if nnz = 0).
+ *   stats_host: filled on success.  hist_host (nullable): int64 buffer of
+ *   hist_cap entries; on success entries 0..min(hist_cap, W+1)-1 receive the
+ *   number of rows of each length.
+ */
+spmv_status spmv_analyze(int32_t num_rows, int32_t num_cols, int32_t nnz,
+                         const int32_t *row_ptrs_dev, const int32_t *col_idx_dev,
+                         int32_t validate, spmv_stats *stats_host, int64_t *hist_host,
+                         int64_t hist_cap, void *stream);
+
+/*
+ * spmv_select -- the format selector, a pure host function of the statistics
+ * [CHOICE 4.3 rule on mean and max row length, operators restored as
+ * W*R <= 2*nnz -> ELL; nnz < 10*R -> COO (segmented); W*R > 5*nnz -> HYB;
+ * else CSR (vector); CHOICE 4.1 for the HYB width; CHOICE 5.2: power-law rows
+ * -> merge-based CSR, taken when HYB's ELL part would exceed 1.5*nnz slots].
+ *   hist_host: int64[max_len+1] from spmv_analyze.  opts (nullable):
+ *   hyb_width / lanes_per_row override the width and lane rules.
+ *   Outputs: *format, *hyb_width (0 unless HYB), *lanes (0 unless CSR vector).
+ */
+spmv_status spmv_select(const spmv_stats *stats_host, const int64_t *hist_host,
+                        const spmv_opts *opts, int32_t *format, int32_t *hyb_width,
+                        int32_t *lanes);
+
+/*
+ * spmv_build -- build a handle in `format` from a CSR matrix on the device
+ * [COO/CSR, CSR section: value/colIdx grouped by row, rowPtrs[r] = start of
+ * row r, rowPtrs[numRows] = nnz; column order inside a row is free].
+ *   Validates (as spmv_analyze), computes the statistics, resolves SPMV_AUTO
+ *   with spmv_select, then runs the device builders:
+ *     ELL  [REG, ELL: pad to the longest row with value 0 / column 0,
+ *           transpose to column-major]
+ *     HYB  [REG, hybrid: entries past position K of each row move to a COO
+ *           list in row order; ELL of width min(K, W) for the rest]
+ *     JDS  [REG, JDS: stable sort of rows by length, longest first; perm;
+ *           iterPtr from the length counts; jagged column-major arrays]
+ *     COO  row index expanded from rowPtrs [COO/CSR, COO section]
+ *     CSR merge: per-block starting rows of the merge path
+ *   Fails with SPMV_ERR_TOO_LARGE when an ELL (or HYB ELL part) would need
+ *   R*width > 2^31-1 slots or when opts->max_bytes is exceeded.
+ *   values_dev: fp32[nnz], moved bit for bit.  opts nullable (defaults).
+ */
+spmv_status spmv_build(spmv_handle **out, spmv_format format, int32_t num_rows,
+                       int32_t num_cols, int32_t nnz, const int32_t *row_ptrs_dev,
+                       const int32_t *col_idx_dev, const float *values_dev,
+                       const spmv_opts *opts, void *stream);
+
+/*
+ * spmv_coo_to_csr -- COO -> CSR on the device [COO/CSR: COO stores one
+ * (row, col, value) per nonzero; CSR groups them by row with rowPtrs].
+ *   Count entries per row, exclusive scan of the counts -> rowPtrs, then a
+ *   stable scatter: entries of one row keep their order in the COO input.
+ *   Duplicates are kept (they add up in SpMV).  Checks row indices
+ *   (SPMV_ERR_BAD_ROWIDX) and, if validate, column indices.
+ *   Outputs (caller-allocated device arrays): row_ptrs_out int32[R+1],
+ *   col_idx_out int32[nnz], values_out fp32[nnz].  Outputs must not alias
+ *   inputs.
+ */
+spmv_status spmv_coo_to_csr(int32_t num_rows, int32_t num_cols, int32_t nnz,
+                            const int32_t *row_idx_dev, const int32_t *col_idx_dev,
+                            const float *values_dev, int32_t *row_ptrs_out_dev,
+                            int32_t *col_idx_out_dev, float *values_out_dev,
+                            int32_t validate, void *stream);
+
+/* spmv_build_coo -- spmv_coo_to_csr into temporaries, then spmv_build. */
+spmv_status spmv_build_coo(spmv_handle **out, spmv_format format, int32_t num_rows,
+                           int32_t num_cols, int32_t nnz, const int32_t *row_idx_dev,
+                           const int32_t *col_idx_dev, const float *values_dev,
+                           const spmv_opts *opts, void *stream);
+
+/*
+ * spmv_run -- y <- A*x + y [COO/CSR background: SpMV computes A*X + Y].
+ *   x_dev: fp32[num_cols]; y_dev: fp32[num_rows], read and written.
+ *   Enqueues 1-2 kernels on `stream` (HYB: ELL part, then COO tail, in stream
+ *   order).  No allocation, no synchronisation.  Rows with no nonzeros are
+ *   left untouched.  Summation order is the kernel's own: results agree with
+ *   the exact sum within |err| <= 1e-5 * (|y| + sum |a*x|) per row; the
+ *   atomic formats (COO, HYB tail, JDS long rows, CSR merge) are not bit-
+ *   reproducible from run to run.
+ *   Must be called on the device the handle was built on (SPMV_ERR_DEVICE).
+ */
+spmv_status spmv_run(const spmv_handle *h, const float *x_dev, float *y_dev, void *stream);
+
+spmv_status spmv_get_info(const spmv_handle *h, spmv_info *info_host);
+
+/* Size in bytes of an exportable array (0 if the handle's format has none). */
+spmv_status spmv_array_bytes(const spmv_handle *h, spmv_array which, size_t *bytes);
+
+/* Copy an array of the handle to host memory (synchronous).  `bytes` must
+ * equal spmv_array_bytes(); else SPMV_ERR_INVALID_ARG. */
+spmv_status spmv_export(const spmv_handle *h, spmv_array which, void *host_dst, size_t bytes);
+
+/* Free the handle and its device memory (synchronises its device first).
+ * NULL is accepted. */
+spmv_status spmv_destroy(spmv_handle *h);
+
+const char *spmv_status_string(spmv_status status);
+const char *spmv_format_name(spmv_format format);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPMV_MI355X_H */

@@ -1,0 +1,142 @@
+// Input checks and row-length statistics.
+//
+// Checks follow the CSR definition of the PMPP notes page "Sparse Matrices
+// and Basic Formats (COO & CSR)" (rowPtrs[r] is where row r starts, so the
+// pointers never decrease, rowPtrs[0] = 0 and rowPtrs[numRows] = nnz) and the
+// input checks listed in section 5.3 of the SpGEMM/AIA article (row_ptr
+// monotone, every column index below the column count).  Statistics are the
+// ones the format-choice article uses to pick a format (section 4.1: row
+// length histogram and variance; 4.3: mean and maximum row length).
+#include "internal.h"
+
+namespace spmv {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kHistLds = 4096;   // lengths below this are binned in LDS first
+
+__device__ inline int wave_max(int v) {
+    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ inline unsigned long long wave_sum(unsigned long long v) {
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// One lane per row: length, monotonicity, the two end conditions, and the
+// reductions W = max len, sum len^2, number of empty rows.
+__global__ __launch_bounds__(kThreads) void k_row_checks(int32_t R, int32_t nnz,
+                                                         const int32_t *__restrict__ rp,
+                                                         RowStatsDev *__restrict__ st) {
+    const int64_t r = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    int bad = 0, len = 0;
+    unsigned long long sq = 0, empty = 0;
+    if (r < R) {
+        const int a = rp[r], b = rp[r + 1];
+        len = b - a;
+        if (len < 0) bad = 1;
+        if (r == 0 && a != 0) bad = 1;
+        if (r == R - 1 && b != nnz) bad = 1;
+        if (len < 0) len = 0;
+        sq = static_cast<unsigned long long>(len) * static_cast<unsigned long long>(len);
+        empty = (len == 0);
+    } else if (r == 0) {  // R == 0: rowPtrs = [0] and nnz must be 0
+        if (rp[0] != 0 || nnz != 0) bad = 1;
+    }
+    const unsigned long long any_bad = __ballot(bad != 0);
+    const int wmax = wave_max(len);
+    const unsigned long long wsq = wave_sum(sq);
+    const unsigned long long wempty = wave_sum(empty);
+    if (__lane_id() == 0) {
+        if (any_bad) atomicOr(&st->flags, kFlagBadRowPtrs);
+        if (wmax > 0) atomicMax(&st->max_len, wmax);
+        if (wsq) atomicAdd(&st->sum_len_sq, wsq);
+        if (wempty) atomicAdd(&st->empty_rows, wempty);
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_col_checks(int32_t nnz, int32_t C,
+                                                         const int32_t *__restrict__ col,
+                                                         RowStatsDev *__restrict__ st) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    bool bad = false;
+    if (i < nnz) {
+        const int32_t c = ld_nt(col + i);
+        bad = static_cast<uint32_t>(c) >= static_cast<uint32_t>(C);
+    }
+    if (__ballot(bad) != 0 && __lane_id() == 0) atomicOr(&st->flags, kFlagBadCol);
+}
+
+__global__ __launch_bounds__(kThreads) void k_coo_checks(int32_t nnz, int32_t R, int32_t C,
+                                                         const int32_t *__restrict__ row,
+                                                         const int32_t *__restrict__ col,
+                                                         int check_cols,
+                                                         RowStatsDev *__restrict__ st) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    bool bad_row = false, bad_col = false, unsorted = false;
+    if (i < nnz) {
+        const int32_t r = row[i];
+        bad_row = static_cast<uint32_t>(r) >= static_cast<uint32_t>(R);
+        if (check_cols) bad_col = static_cast<uint32_t>(col[i]) >= static_cast<uint32_t>(C);
+        if (i + 1 < nnz) unsorted = row[i + 1] < r;
+    }
+    const bool br = __ballot(bad_row) != 0, bc = __ballot(bad_col) != 0,
+               un = __ballot(unsorted) != 0;
+    if (__lane_id() == 0 && (br || bc || un))
+        atomicOr(&st->flags, (br ? kFlagBadRow : 0) | (bc ? kFlagBadCol : 0) |
+                                 (un ? kFlagUnsortedRows : 0));
+}
+
+// hist[len] += 1 per row; short lengths are binned in LDS, long ones directly.
+__global__ __launch_bounds__(kThreads) void k_len_hist(int32_t R, const int32_t *__restrict__ rp,
+                                                       int32_t W, int32_t *__restrict__ hist) {
+    __shared__ int sh[kHistLds];
+    const int nb = W + 1 < kHistLds ? W + 1 : kHistLds;
+    for (int i = threadIdx.x; i < nb; i += kThreads) sh[i] = 0;
+    __syncthreads();
+    for (int64_t r = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; r < R;
+         r += static_cast<int64_t>(gridDim.x) * kThreads) {
+        const int len = rp[r + 1] - rp[r];
+        if (len < kHistLds) atomicAdd(&sh[len], 1);
+        else atomicAdd(&hist[len], 1);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < nb; i += kThreads)
+        if (sh[i]) atomicAdd(&hist[i], sh[i]);
+}
+
+}  // namespace
+
+hipError_t launch_row_checks(int32_t R, int32_t nnz, const int32_t *rp, RowStatsDev *st,
+                             hipStream_t s) {
+    k_row_checks<<<grid_for(R > 0 ? R : 1, kThreads), kThreads, 0, s>>>(R, nnz, rp, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_col_checks(int32_t nnz, int32_t C, const int32_t *col, RowStatsDev *st,
+                             hipStream_t s) {
+    if (nnz <= 0) return hipSuccess;
+    k_col_checks<<<grid_for(nnz, kThreads), kThreads, 0, s>>>(nnz, C, col, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_coo_checks(int32_t nnz, int32_t R, int32_t C, const int32_t *row,
+                             const int32_t *col, int check_cols, RowStatsDev *st, hipStream_t s) {
+    if (nnz <= 0) return hipSuccess;
+    k_coo_checks<<<grid_for(nnz, kThreads), kThreads, 0, s>>>(nnz, R, C, row, col, check_cols,
+                                                              st);
+    return hipGetLastError();
+}
+
+hipError_t launch_len_hist(int32_t R, const int32_t *rp, int32_t W, int32_t *hist,
+                           hipStream_t s) {
+    if (R <= 0) return hipSuccess;
+    unsigned g = grid_for(R, kThreads);
+    if (g > 2048) g = 2048;
+    k_len_hist<<<g, kThreads, 0, s>>>(R, rp, W, hist);
+    return hipGetLastError();
+}
+
+}  // namespace spmv

@@ -1,0 +1,609 @@
+// C ABI of the SpMV engine (include/spmv.h): argument checks, the analysis and
+// build flow, the format selector, run dispatch, export and teardown.
+#include <algorithm>
+#include <cstring>
+#include <memory>
+
+#include "internal.h"
+
+namespace spmv {
+
+spmv_status from_hip(hipError_t e) {
+    return e == hipErrorOutOfMemory ? SPMV_ERR_OOM : SPMV_ERR_HIP;
+}
+
+Scratch::~Scratch() {
+    if (ptrs_.empty()) return;
+    (void)hipStreamSynchronize(stream_);
+    for (void *p : ptrs_) (void)hipFree(p);
+}
+
+spmv_status Scratch::alloc_bytes(void **p, size_t bytes) {
+    *p = nullptr;
+    hipError_t e = hipMalloc(p, bytes < 4 ? 4 : bytes);
+    if (e != hipSuccess) {
+        *p = nullptr;
+        (void)hipGetLastError();
+        return from_hip(e);
+    }
+    ptrs_.push_back(*p);
+    return SPMV_OK;
+}
+
+namespace {
+
+constexpr int64_t kInt32Max = 2147483647LL;
+
+struct HandleDeleter {
+    void operator()(spmv_handle *h) const {
+        if (!h) return;
+        for (void *p : h->owned) (void)hipFree(p);
+        delete h;
+    }
+};
+using HandlePtr = std::unique_ptr<spmv_handle, HandleDeleter>;
+
+template <typename T>
+spmv_status halloc(spmv_handle *h, T **p, int64_t count) {
+    *p = nullptr;
+    const size_t bytes = static_cast<size_t>(count) * sizeof(T);
+    void *q = nullptr;
+    hipError_t e = hipMalloc(&q, bytes < 4 ? 4 : bytes);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return from_hip(e);
+    }
+    h->owned.push_back(q);
+    h->device_bytes += static_cast<int64_t>(bytes);
+    *p = static_cast<T *>(q);
+    return SPMV_OK;
+}
+
+spmv_opts resolve_opts(const spmv_opts *o) {
+    spmv_opts r;
+    spmv_opts_default(&r);
+    if (o) r = *o;
+    return r;
+}
+
+bool valid_lanes(int32_t l) { return l == 0 || (l >= 1 && l <= 64 && (l & (l - 1)) == 0); }
+
+// ---------------------------------------------------------------- analysis
+struct Analysis {
+    spmv_stats st{};
+    std::vector<int64_t> hist;
+};
+
+spmv_status analyze_csr(int32_t R, int32_t C, int32_t nnz, const int32_t *rp,
+                        const int32_t *col, bool validate, bool want_hist, Analysis &out,
+                        hipStream_t s, Scratch &scratch) {
+    RowStatsDev *d = nullptr;
+    SPMV_TRY(scratch.alloc(&d, 1));
+    SPMV_HIP(hipMemsetAsync(d, 0, sizeof(RowStatsDev), s));
+    SPMV_HIP(launch_row_checks(R, nnz, rp, d, s));
+    if (validate) SPMV_HIP(launch_col_checks(nnz, C, col, d, s));
+    RowStatsDev h{};
+    SPMV_HIP(hipMemcpyAsync(&h, d, sizeof(h), hipMemcpyDeviceToHost, s));
+    SPMV_HIP(hipStreamSynchronize(s));
+    if (h.flags & kFlagBadRowPtrs) return SPMV_ERR_BAD_ROWPTRS;
+    if (h.flags & kFlagBadCol) return SPMV_ERR_BAD_COLIDX;
+    out.st.num_rows = R;
+    out.st.num_cols = C;
+    out.st.nnz = nnz;
+    out.st.max_len = h.max_len;
+    out.st.sum_len_sq = static_cast<int64_t>(h.sum_len_sq);
+    out.st.empty_rows = static_cast<int64_t>(h.empty_rows);
+    if (want_hist) {
+        const int64_t bins = out.st.max_len + 1;
+        out.hist.assign(static_cast<size_t>(bins), 0);
+        if (R > 0) {
+            int32_t *dh = nullptr;
+            SPMV_TRY(scratch.alloc(&dh, static_cast<size_t>(bins)));
+            SPMV_HIP(hipMemsetAsync(dh, 0, sizeof(int32_t) * bins, s));
+            SPMV_HIP(launch_len_hist(R, rp, static_cast<int32_t>(out.st.max_len), dh, s));
+            std::vector<int32_t> tmp(static_cast<size_t>(bins));
+            SPMV_HIP(hipMemcpyAsync(tmp.data(), dh, sizeof(int32_t) * bins,
+                                    hipMemcpyDeviceToHost, s));
+            SPMV_HIP(hipStreamSynchronize(s));
+            for (int64_t i = 0; i < bins; ++i) out.hist[i] = tmp[i];
+        }
+    }
+    return SPMV_OK;
+}
+
+// ---------------------------------------------------------------- selector
+// Smallest k such that at least 99% of the rows have length <= k.
+int64_t hyb_percentile_width(int64_t R, const int64_t *hist, int64_t bins) {
+    int64_t below = 0;
+    for (int64_t k = 0; k < bins; ++k) {
+        below += hist[k];
+        if (below * 100 >= R * 99) return k;
+    }
+    return bins - 1;
+}
+
+int32_t lanes_from_mean(int64_t R, int64_t nnz) {
+    const int64_t mean_up = R > 0 ? (nnz + R - 1) / R : 0;
+    int32_t L = 2;
+    while (L < 64 && L < mean_up) L <<= 1;
+    return L;
+}
+
+void select_format(const spmv_stats &st, const int64_t *hist, const spmv_opts &o,
+                   int32_t *fmt, int32_t *K, int32_t *L) {
+    const int64_t R = st.num_rows, nnz = st.nnz, W = st.max_len;
+    *K = 0;
+    *L = 0;
+    const int64_t padded = W * R;             // slots of a full-width ELL
+    if (padded <= 2 * nnz) {                  // max <= 2 * mean
+        *fmt = SPMV_ELL;
+    } else if (nnz < 10 * R) {                // mean < 10
+        *fmt = SPMV_COO_SEGMENTED;
+    } else if (padded > 5 * nnz) {            // max > 5 * mean
+        const int64_t k = o.hyb_width > 0 ? o.hyb_width : hyb_percentile_width(R, hist, W + 1);
+        if (2 * R * k <= 3 * nnz) {           // ELL part <= 1.5 * nnz slots
+            *fmt = SPMV_HYB;
+            *K = static_cast<int32_t>(k);
+        } else {
+            *fmt = SPMV_CSR_MERGE;
+        }
+    } else {
+        *fmt = SPMV_CSR_VECTOR;
+        *L = o.lanes_per_row > 0 ? o.lanes_per_row : lanes_from_mean(R, nnz);
+    }
+}
+
+// ------------------------------------------------------------------ builds
+spmv_status check_budget(const spmv_opts &o, int64_t bytes) {
+    if (o.max_bytes > 0 && bytes > o.max_bytes) return SPMV_ERR_TOO_LARGE;
+    return SPMV_OK;
+}
+
+spmv_status copy_csr(spmv_handle *h, int32_t R, int32_t nnz, const int32_t *rp,
+                     const int32_t *col, const float *val, hipStream_t s) {
+    SPMV_TRY(halloc(h, &h->a.row_ptrs, static_cast<int64_t>(R) + 1));
+    SPMV_TRY(halloc(h, &h->a.col_idx, nnz));
+    SPMV_TRY(halloc(h, &h->a.values, nnz));
+    SPMV_HIP(hipMemcpyAsync(h->a.row_ptrs, rp, sizeof(int32_t) * (static_cast<size_t>(R) + 1),
+                            hipMemcpyDeviceToDevice, s));
+    if (nnz > 0) {
+        SPMV_HIP(hipMemcpyAsync(h->a.col_idx, col, sizeof(int32_t) * nnz,
+                                hipMemcpyDeviceToDevice, s));
+        SPMV_HIP(hipMemcpyAsync(h->a.values, val, sizeof(float) * nnz, hipMemcpyDeviceToDevice,
+                                s));
+    }
+    return SPMV_OK;
+}
+
+spmv_status build_ell_part(spmv_handle *h, int32_t R, int32_t width, const int32_t *rp,
+                           const int32_t *col, const float *val, hipStream_t s) {
+    const int64_t slots = static_cast<int64_t>(R) * width;
+    if (slots > kInt32Max) return SPMV_ERR_TOO_LARGE;
+    h->ell_width = width;
+    SPMV_TRY(halloc(h, &h->a.ell_col, slots));
+    SPMV_TRY(halloc(h, &h->a.ell_val, slots));
+    SPMV_TRY(halloc(h, &h->a.ell_nnz, R));
+    SPMV_HIP(launch_build_ell(R, width, rp, col, val, h->a.ell_col, h->a.ell_val, h->a.ell_nnz,
+                              s));
+    return SPMV_OK;
+}
+
+spmv_status build_hyb_tail(spmv_handle *h, int32_t R, int32_t K, const int32_t *rp,
+                           const int32_t *col, const float *val, hipStream_t s,
+                           Scratch &scratch) {
+    int32_t *off = nullptr;
+    SPMV_TRY(scratch.alloc(&off, static_cast<size_t>(R) + 1));
+    SPMV_HIP(launch_tail_lengths(R, K, rp, off, s));
+    SPMV_TRY(exclusive_scan(off, off, R, true, s, scratch));
+    int32_t ntail = 0;
+    SPMV_HIP(hipMemcpyAsync(&ntail, off + R, sizeof(int32_t), hipMemcpyDeviceToHost, s));
+    SPMV_HIP(hipStreamSynchronize(s));
+    h->tail_nnz = ntail;
+    SPMV_TRY(halloc(h, &h->a.tail_row, ntail));
+    SPMV_TRY(halloc(h, &h->a.tail_col, ntail));
+    SPMV_TRY(halloc(h, &h->a.tail_val, ntail));
+    SPMV_HIP(launch_fill_tail(R, K, ntail, rp, off, col, val, h->a.tail_row, h->a.tail_col,
+                              h->a.tail_val, s));
+    return SPMV_OK;
+}
+
+spmv_status build_jds(spmv_handle *h, int32_t R, int32_t nnz, const int32_t *rp,
+                      const int32_t *col, const float *val, hipStream_t s, Scratch &scratch) {
+    const int32_t W = static_cast<int32_t>(h->stats.max_len);
+    uint32_t *keys = nullptr, *sorted = nullptr;
+    int32_t *rows = nullptr;
+    SPMV_TRY(scratch.alloc(&keys, R));
+    SPMV_TRY(scratch.alloc(&sorted, R));
+    SPMV_TRY(scratch.alloc(&rows, R));
+    SPMV_TRY(halloc(h, &h->a.jds_perm, R));
+    SPMV_TRY(halloc(h, &h->a.jds_len, R));
+    SPMV_TRY(halloc(h, &h->a.jds_iter_ptr, static_cast<int64_t>(W) + 1));
+    SPMV_TRY(halloc(h, &h->a.jds_col, nnz));
+    SPMV_TRY(halloc(h, &h->a.jds_val, nnz));
+    SPMV_HIP(launch_jds_keys(R, W, rp, keys, rows, s));
+    SPMV_TRY(radix_sort_pairs(keys, rows, sorted, h->a.jds_perm, R, bits_for(W), s, scratch));
+    SPMV_HIP(launch_jds_lengths(R, W, sorted, h->a.jds_len, s));
+    SPMV_HIP(launch_jds_counts(R, W, h->a.jds_len, h->a.jds_iter_ptr, s));
+    SPMV_TRY(exclusive_scan(h->a.jds_iter_ptr, h->a.jds_iter_ptr, W, true, s, scratch));
+    SPMV_HIP(launch_jds_fill(nnz, W, h->a.jds_iter_ptr, h->a.jds_perm, rp, col, val,
+                             h->a.jds_col, h->a.jds_val, s));
+    // wave tiles: (group of 64 sorted rows, chunk of `depth` jagged columns)
+    const int32_t groups = static_cast<int32_t>((static_cast<int64_t>(R) + kWave - 1) / kWave);
+    int32_t *off = nullptr;
+    SPMV_TRY(scratch.alloc(&off, static_cast<size_t>(groups) + 1));
+    SPMV_HIP(launch_jds_chunks(R, h->jds_depth, h->a.jds_len, off, s));
+    SPMV_TRY(exclusive_scan(off, off, groups, true, s, scratch));
+    int32_t ntiles = 0;
+    SPMV_HIP(hipMemcpyAsync(&ntiles, off + groups, sizeof(int32_t), hipMemcpyDeviceToHost, s));
+    SPMV_HIP(hipStreamSynchronize(s));
+    h->num_tiles = ntiles;
+    SPMV_TRY(halloc(h, &h->a.jds_tiles, ntiles));
+    SPMV_HIP(launch_jds_tiles(groups, ntiles, off, h->a.jds_tiles, s));
+    return SPMV_OK;
+}
+
+// Device bytes a format needs (checked against opts.max_bytes before building).
+int64_t format_bytes(int32_t fmt, int64_t R, int64_t nnz, int64_t W, int64_t K,
+                     const std::vector<int64_t> &hist) {
+    switch (fmt) {
+    case SPMV_COO_ATOMIC:
+    case SPMV_COO_SEGMENTED: return 12 * nnz;
+    case SPMV_CSR_SCALAR:
+    case SPMV_CSR_VECTOR: return 8 * nnz + 4 * (R + 1);
+    case SPMV_CSR_MERGE:
+        return 8 * nnz + 4 * (R + 1) + 4 * ((R + nnz) / kMergeItemsPerBlock + 2);
+    case SPMV_ELL: return 8 * R * W + 4 * R;
+    case SPMV_HYB: {
+        const int64_t w = std::min(K, W);
+        int64_t tail = 0;
+        for (int64_t l = w + 1; l < static_cast<int64_t>(hist.size()); ++l) tail += (l - w) * hist[l];
+        return 8 * R * w + 4 * R + 12 * tail;
+    }
+    case SPMV_JDS: return 8 * nnz + 8 * R + 4 * (W + 1) + 8 * (R / kWave + 1 + nnz / kWave);
+    default: return 0;
+    }
+}
+
+spmv_status build_csr_impl(spmv_handle **out, spmv_format fmt, int32_t R, int32_t C,
+                           int32_t nnz, const int32_t *rp, const int32_t *col,
+                           const float *val, const spmv_opts &o, hipStream_t s,
+                           Scratch &scratch) {
+    Analysis an;
+    SPMV_TRY(analyze_csr(R, C, nnz, rp, col, o.validate != 0, true, an, s, scratch));
+    int32_t f = fmt, K = 0, L = 0;
+    if (f == SPMV_AUTO) {
+        select_format(an.st, an.hist.data(), o, &f, &K, &L);
+    } else if (f == SPMV_HYB) {
+        K = o.hyb_width > 0 ? o.hyb_width
+                            : static_cast<int32_t>(hyb_percentile_width(
+                                  R, an.hist.data(), static_cast<int64_t>(an.hist.size())));
+    } else if (f == SPMV_CSR_VECTOR) {
+        L = o.lanes_per_row > 0 ? o.lanes_per_row : lanes_from_mean(R, nnz);
+    }
+    const int64_t W = an.st.max_len;
+    if (f == SPMV_ELL && static_cast<int64_t>(R) * W > kInt32Max) return SPMV_ERR_TOO_LARGE;
+    if (f == SPMV_HYB && static_cast<int64_t>(R) * std::min<int64_t>(K, W) > kInt32Max)
+        return SPMV_ERR_TOO_LARGE;
+    SPMV_TRY(check_budget(o, format_bytes(f, R, nnz, W, K, an.hist)));
+
+    HandlePtr h(new spmv_handle());
+    SPMV_HIP(hipGetDevice(&h->device));
+    h->format = f;
+    h->stats = an.st;
+    h->hist = an.hist;
+    h->jds_depth = o.jds_depth > 0 ? o.jds_depth : kJdsDepthDefault;
+    switch (f) {
+    case SPMV_COO_ATOMIC:
+    case SPMV_COO_SEGMENTED:
+        SPMV_TRY(halloc(h.get(), &h->a.row_idx, nnz));
+        SPMV_TRY(halloc(h.get(), &h->a.col_idx, nnz));
+        SPMV_TRY(halloc(h.get(), &h->a.values, nnz));
+        SPMV_HIP(launch_expand_rows(R, nnz, rp, h->a.row_idx, s));
+        if (nnz > 0) {
+            SPMV_HIP(hipMemcpyAsync(h->a.col_idx, col, sizeof(int32_t) * nnz,
+                                    hipMemcpyDeviceToDevice, s));
+            SPMV_HIP(hipMemcpyAsync(h->a.values, val, sizeof(float) * nnz,
+                                    hipMemcpyDeviceToDevice, s));
+        }
+        break;
+    case SPMV_CSR_SCALAR:
+        SPMV_TRY(copy_csr(h.get(), R, nnz, rp, col, val, s));
+        break;
+    case SPMV_CSR_VECTOR:
+        h->lanes = L;
+        SPMV_TRY(copy_csr(h.get(), R, nnz, rp, col, val, s));
+        break;
+    case SPMV_CSR_MERGE: {
+        SPMV_TRY(copy_csr(h.get(), R, nnz, rp, col, val, s));
+        const int64_t blocks =
+            (static_cast<int64_t>(R) + nnz + kMergeItemsPerBlock - 1) / kMergeItemsPerBlock;
+        h->num_tiles = blocks;
+        SPMV_TRY(halloc(h.get(), &h->a.merge_row_start, blocks + 1));
+        SPMV_HIP(launch_merge_partition(R, nnz, h->a.row_ptrs, static_cast<int32_t>(blocks),
+                                        h->a.merge_row_start, s));
+        break;
+    }
+    case SPMV_ELL:
+        SPMV_TRY(build_ell_part(h.get(), R, static_cast<int32_t>(W), rp, col, val, s));
+        break;
+    case SPMV_HYB: {
+        h->hyb_width = K;
+        const int32_t w = static_cast<int32_t>(std::min<int64_t>(K, W));
+        SPMV_TRY(build_ell_part(h.get(), R, w, rp, col, val, s));
+        SPMV_TRY(build_hyb_tail(h.get(), R, w, rp, col, val, s, scratch));
+        break;
+    }
+    case SPMV_JDS:
+        SPMV_TRY(build_jds(h.get(), R, nnz, rp, col, val, s, scratch));
+        break;
+    default:
+        return SPMV_ERR_INVALID_ARG;
+    }
+    SPMV_HIP(hipStreamSynchronize(s));
+    *out = h.release();
+    return SPMV_OK;
+}
+
+spmv_status coo_to_csr_impl(int32_t R, int32_t C, int32_t nnz, const int32_t *ri,
+                            const int32_t *ci, const float *v, int32_t *rp_out, int32_t *c_out,
+                            float *v_out, bool validate, hipStream_t s, Scratch &scratch) {
+    RowStatsDev *d = nullptr;
+    SPMV_TRY(scratch.alloc(&d, 1));
+    SPMV_HIP(hipMemsetAsync(d, 0, sizeof(RowStatsDev), s));
+    SPMV_HIP(launch_coo_checks(nnz, R, C, ri, ci, validate ? 1 : 0, d, s));
+    RowStatsDev h{};
+    SPMV_HIP(hipMemcpyAsync(&h, d, sizeof(h), hipMemcpyDeviceToHost, s));
+    SPMV_HIP(hipStreamSynchronize(s));
+    if (h.flags & kFlagBadRow) return SPMV_ERR_BAD_ROWIDX;
+    if (h.flags & kFlagBadCol) return SPMV_ERR_BAD_COLIDX;
+    // (i) entries per row, (ii) exclusive scan -> rowPtrs (rowPtrs[R] = nnz)
+    SPMV_HIP(hipMemsetAsync(rp_out, 0, sizeof(int32_t) * (static_cast<size_t>(R) + 1), s));
+    SPMV_HIP(launch_count_rows(nnz, ri, rp_out, s));
+    SPMV_TRY(exclusive_scan(rp_out, rp_out, R, true, s, scratch));
+    if (nnz == 0) return SPMV_OK;
+    // (iii) stable scatter by row
+    if (!(h.flags & kFlagUnsortedRows)) {
+        SPMV_HIP(hipMemcpyAsync(c_out, ci, sizeof(int32_t) * nnz, hipMemcpyDeviceToDevice, s));
+        SPMV_HIP(hipMemcpyAsync(v_out, v, sizeof(float) * nnz, hipMemcpyDeviceToDevice, s));
+        return SPMV_OK;
+    }
+    int32_t *idx = nullptr, *perm = nullptr;
+    uint32_t *keys_sorted = nullptr;
+    SPMV_TRY(scratch.alloc(&idx, nnz));
+    SPMV_TRY(scratch.alloc(&perm, nnz));
+    SPMV_TRY(scratch.alloc(&keys_sorted, nnz));
+    SPMV_HIP(launch_iota(nnz, idx, s));
+    SPMV_TRY(radix_sort_pairs(reinterpret_cast<const uint32_t *>(ri), idx, keys_sorted, perm, nnz,
+                              bits_for(R > 0 ? static_cast<uint64_t>(R - 1) : 0), s, scratch));
+    SPMV_HIP(launch_gather_pairs(nnz, perm, ci, v, c_out, v_out, s));
+    return SPMV_OK;
+}
+
+bool bad_sizes(int32_t R, int32_t C, int32_t nnz) { return R < 0 || C < 0 || nnz < 0; }
+
+spmv_status check_device(const spmv_handle *h) {
+    int dev = -1;
+    SPMV_HIP(hipGetDevice(&dev));
+    return dev == h->device ? SPMV_OK : SPMV_ERR_DEVICE;
+}
+
+}  // namespace
+}  // namespace spmv
+
+using namespace spmv;
+
+extern "C" {
+
+void spmv_opts_default(spmv_opts *o) {
+    if (!o) return;
+    std::memset(o, 0, sizeof(*o));
+    o->validate = 1;
+}
+
+spmv_status spmv_analyze(int32_t R, int32_t C, int32_t nnz, const int32_t *rp,
+                         const int32_t *col, int32_t validate, spmv_stats *st, int64_t *hist,
+                         int64_t hist_cap, void *stream) {
+    if (bad_sizes(R, C, nnz) || !rp || !st || (nnz > 0 && validate && !col) ||
+        (hist && hist_cap < 0))
+        return SPMV_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Scratch scratch(s);
+    Analysis an;
+    SPMV_TRY(analyze_csr(R, C, nnz, rp, col, validate != 0, hist != nullptr, an, s, scratch));
+    *st = an.st;
+    if (hist) {
+        const int64_t n = std::min<int64_t>(hist_cap, static_cast<int64_t>(an.hist.size()));
+        for (int64_t i = 0; i < n; ++i) hist[i] = an.hist[i];
+    }
+    return SPMV_OK;
+}
+
+spmv_status spmv_select(const spmv_stats *st, const int64_t *hist, const spmv_opts *opts,
+                        int32_t *fmt, int32_t *K, int32_t *L) {
+    if (!st || !hist || !fmt || !K || !L) return SPMV_ERR_INVALID_ARG;
+    const spmv_opts o = resolve_opts(opts);
+    if (!valid_lanes(o.lanes_per_row) || st->num_rows < 0 || st->nnz < 0 || st->max_len < 0)
+        return SPMV_ERR_INVALID_ARG;
+    select_format(*st, hist, o, fmt, K, L);
+    return SPMV_OK;
+}
+
+spmv_status spmv_build(spmv_handle **out, spmv_format fmt, int32_t R, int32_t C, int32_t nnz,
+                       const int32_t *rp, const int32_t *col, const float *val,
+                       const spmv_opts *opts, void *stream) {
+    if (!out) return SPMV_ERR_INVALID_ARG;
+    *out = nullptr;
+    const spmv_opts o = resolve_opts(opts);
+    if (bad_sizes(R, C, nnz) || !rp || (nnz > 0 && (!col || !val)) || fmt < SPMV_AUTO ||
+        fmt > SPMV_CSR_MERGE || !valid_lanes(o.lanes_per_row) || o.jds_depth < 0 ||
+        o.max_bytes < 0)
+        return SPMV_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Scratch scratch(s);
+    return build_csr_impl(out, fmt, R, C, nnz, rp, col, val, o, s, scratch);
+}
+
+spmv_status spmv_coo_to_csr(int32_t R, int32_t C, int32_t nnz, const int32_t *ri,
+                            const int32_t *ci, const float *v, int32_t *rp_out, int32_t *c_out,
+                            float *v_out, int32_t validate, void *stream) {
+    if (bad_sizes(R, C, nnz) || !rp_out || (nnz > 0 && (!ri || !ci || !v || !c_out || !v_out)))
+        return SPMV_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Scratch scratch(s);
+    SPMV_TRY(coo_to_csr_impl(R, C, nnz, ri, ci, v, rp_out, c_out, v_out, validate != 0, s,
+                             scratch));
+    SPMV_HIP(hipStreamSynchronize(s));
+    return SPMV_OK;
+}
+
+spmv_status spmv_build_coo(spmv_handle **out, spmv_format fmt, int32_t R, int32_t C,
+                           int32_t nnz, const int32_t *ri, const int32_t *ci, const float *v,
+                           const spmv_opts *opts, void *stream) {
+    if (!out) return SPMV_ERR_INVALID_ARG;
+    *out = nullptr;
+    const spmv_opts o = resolve_opts(opts);
+    if (bad_sizes(R, C, nnz) || (nnz > 0 && (!ri || !ci || !v)) || fmt < SPMV_AUTO ||
+        fmt > SPMV_CSR_MERGE || !valid_lanes(o.lanes_per_row) || o.jds_depth < 0 ||
+        o.max_bytes < 0)
+        return SPMV_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Scratch scratch(s);
+    int32_t *rp = nullptr, *c = nullptr;
+    float *val = nullptr;
+    SPMV_TRY(scratch.alloc(&rp, static_cast<size_t>(R) + 1));
+    SPMV_TRY(scratch.alloc(&c, static_cast<size_t>(nnz)));
+    SPMV_TRY(scratch.alloc(&val, static_cast<size_t>(nnz)));
+    SPMV_TRY(coo_to_csr_impl(R, C, nnz, ri, ci, v, rp, c, val, o.validate != 0, s, scratch));
+    spmv_opts o2 = o;
+    o2.validate = 0;  // columns were checked on the COO input
+    return build_csr_impl(out, fmt, R, C, nnz, rp, c, val, o2, s, scratch);
+}
+
+spmv_status spmv_run(const spmv_handle *h, const float *x, float *y, void *stream) {
+    if (!h) return SPMV_ERR_INVALID_ARG;
+    if (h->stats.num_rows == 0 || h->stats.nnz == 0) return SPMV_OK;
+    if (!x || !y) return SPMV_ERR_INVALID_ARG;
+    SPMV_TRY(check_device(h));
+    return launch_spmv(h, x, y, static_cast<hipStream_t>(stream));
+}
+
+spmv_status spmv_get_info(const spmv_handle *h, spmv_info *info) {
+    if (!h || !info) return SPMV_ERR_INVALID_ARG;
+    std::memset(info, 0, sizeof(*info));
+    info->format = h->format;
+    info->hyb_width = h->hyb_width;
+    info->lanes_per_row = h->lanes;
+    info->ell_width = h->ell_width;
+    info->stats = h->stats;
+    info->tail_nnz = h->tail_nnz;
+    info->num_tiles = h->num_tiles;
+    info->device_bytes = h->device_bytes;
+    return SPMV_OK;
+}
+
+namespace {
+struct ArrayRef {
+    const void *dev = nullptr;
+    const void *host = nullptr;
+    size_t bytes = 0;
+};
+
+ArrayRef array_ref(const spmv_handle *h, spmv_array which) {
+    const int64_t R = h->stats.num_rows, nnz = h->stats.nnz, W = h->stats.max_len;
+    const int64_t slots = R * h->ell_width;
+    const DevArrays &a = h->a;
+    ArrayRef r;
+    auto set = [&](const void *p, int64_t n, size_t elem) {
+        if (p) {
+            r.dev = p;
+            r.bytes = static_cast<size_t>(n) * elem;
+        }
+    };
+    switch (which) {
+    case SPMV_A_ROW_PTRS: set(a.row_ptrs, R + 1, 4); break;
+    case SPMV_A_COL_IDX: set(a.col_idx, nnz, 4); break;
+    case SPMV_A_VALUES: set(a.values, nnz, 4); break;
+    case SPMV_A_ROW_IDX: set(a.row_idx, nnz, 4); break;
+    case SPMV_A_ELL_COL: set(a.ell_col, slots, 4); break;
+    case SPMV_A_ELL_VAL: set(a.ell_val, slots, 4); break;
+    case SPMV_A_ELL_NNZ: set(a.ell_nnz, R, 4); break;
+    case SPMV_A_TAIL_ROW: set(a.tail_row, h->tail_nnz, 4); break;
+    case SPMV_A_TAIL_COL: set(a.tail_col, h->tail_nnz, 4); break;
+    case SPMV_A_TAIL_VAL: set(a.tail_val, h->tail_nnz, 4); break;
+    case SPMV_A_JDS_PERM: set(a.jds_perm, R, 4); break;
+    case SPMV_A_JDS_LEN: set(a.jds_len, R, 4); break;
+    case SPMV_A_JDS_ITER_PTR: set(a.jds_iter_ptr, W + 1, 4); break;
+    case SPMV_A_JDS_COL: set(a.jds_col, nnz, 4); break;
+    case SPMV_A_JDS_VAL: set(a.jds_val, nnz, 4); break;
+    case SPMV_A_LEN_HIST:
+        r.host = h->hist.data();
+        r.bytes = h->hist.size() * sizeof(int64_t);
+        break;
+    default: break;
+    }
+    return r;
+}
+}  // namespace
+
+spmv_status spmv_array_bytes(const spmv_handle *h, spmv_array which, size_t *bytes) {
+    if (!h || !bytes) return SPMV_ERR_INVALID_ARG;
+    *bytes = array_ref(h, which).bytes;
+    return SPMV_OK;
+}
+
+spmv_status spmv_export(const spmv_handle *h, spmv_array which, void *dst, size_t bytes) {
+    if (!h) return SPMV_ERR_INVALID_ARG;
+    const ArrayRef r = array_ref(h, which);
+    if (bytes != r.bytes || (bytes > 0 && !dst)) return SPMV_ERR_INVALID_ARG;
+    if (bytes == 0) return SPMV_OK;
+    if (r.host) {
+        std::memcpy(dst, r.host, bytes);
+        return SPMV_OK;
+    }
+    SPMV_TRY(check_device(h));
+    SPMV_HIP(hipMemcpy(dst, r.dev, bytes, hipMemcpyDeviceToHost));
+    return SPMV_OK;
+}
+
+spmv_status spmv_destroy(spmv_handle *h) {
+    if (!h) return SPMV_OK;
+    int prev = -1;
+    (void)hipGetDevice(&prev);
+    if (prev != h->device) (void)hipSetDevice(h->device);
+    (void)hipDeviceSynchronize();
+    HandleDeleter()(h);
+    if (prev >= 0 && prev != h->device) (void)hipSetDevice(prev);
+    return SPMV_OK;
+}
+
+const char *spmv_status_string(spmv_status st) {
+    switch (st) {
+    case SPMV_OK: return "ok";
+    case SPMV_ERR_INVALID_ARG: return "invalid argument";
+    case SPMV_ERR_BAD_ROWPTRS: return "bad row pointers (rowPtrs[0] != 0, decreasing, or rowPtrs[R] != nnz)";
+    case SPMV_ERR_BAD_COLIDX: return "column index out of range";
+    case SPMV_ERR_BAD_ROWIDX: return "row index out of range";
+    case SPMV_ERR_TOO_LARGE: return "format too large (int32 slots or max_bytes)";
+    case SPMV_ERR_OOM: return "device out of memory";
+    case SPMV_ERR_HIP: return "HIP runtime error";
+    case SPMV_ERR_DEVICE: return "handle used on a different device";
+    default: return "unknown status";
+    }
+}
+
+const char *spmv_format_name(spmv_format f) {
+    switch (f) {
+    case SPMV_AUTO: return "auto";
+    case SPMV_COO_ATOMIC: return "coo_atomic";
+    case SPMV_COO_SEGMENTED: return "coo_segmented";
+    case SPMV_CSR_SCALAR: return "csr_scalar";
+    case SPMV_CSR_VECTOR: return "csr_vector";
+    case SPMV_ELL: return "ell";
+    case SPMV_HYB: return "hyb";
+    case SPMV_JDS: return "jds";
+    case SPMV_CSR_MERGE: return "csr_merge";
+    default: return "unknown";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,344 @@
+// Device format builders.  Every builder moves values as raw 32-bit words,
+// so the built arrays hold exactly the input's bits.
+//
+//   COO -> CSR   PMPP notes, "Sparse Matrices and Basic Formats (COO & CSR)":
+//                count entries per row, exclusive scan (scan.hip), then a
+//                stable scatter (sort.hip) so each row keeps its input order.
+//   CSR -> ELL   PMPP notes, "Regularized Formats", ELL section: pad every row
+//                to the longest one (value 0, column 0) and store the padded
+//                rows column-major, slot t of row r at t*R + r.
+//   CSR -> HYB   same page, hybrid ELL-COO section: entries past position K of
+//                each row go to a COO tail (rows in order, positions in
+//                order); the rest is an ELL of width min(K, W).
+//   CSR -> JDS   same page, JDS section: rows sorted by length, longest first
+//                (original order among equals), perm records the original
+//                row, iterPtr[t] = where jagged column t starts, entry t of
+//                sorted row s at iterPtr[t] + s.
+//   merge path   format-choice article 5.2 (merge-based CSR for power-law
+//                rows): first row of each block's equal share of the
+//                rows-plus-nonzeros sequence.
+#include "internal.h"
+
+namespace spmv {
+namespace {
+
+constexpr int kThreads = 256;
+
+// Per-row counts with one atomic per run of equal row indices in a wave: a
+// row-sorted COO list costs one atomic per row segment, not per entry.
+__global__ __launch_bounds__(kThreads) void k_count_rows(int32_t nnz,
+                                                         const int32_t *__restrict__ row,
+                                                         int32_t *__restrict__ counts) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    const int lane = __lane_id();
+    const bool valid = i < nnz;
+    const int32_t r = valid ? row[i] : -1;
+    const int32_t prev = __shfl_up(r, 1);
+    const bool head = valid && (lane == 0 || prev != r);
+    const unsigned long long heads = __ballot(head);
+    const unsigned long long live = __ballot(valid);
+    if (head) {
+        const unsigned long long after = heads & ~((2ull << lane) - 1ull);
+        const int end = after ? (__ffsll(static_cast<long long>(after)) - 1)
+                              : (64 - __clzll(static_cast<long long>(live)));
+        atomicAdd(&counts[r], end - lane);
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_iota(int32_t n, int32_t *__restrict__ out) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (i < n) out[i] = static_cast<int32_t>(i);
+}
+
+__global__ __launch_bounds__(kThreads) void k_gather_pairs(int32_t n,
+                                                           const int32_t *__restrict__ perm,
+                                                           const int32_t *__restrict__ col_in,
+                                                           const uint32_t *__restrict__ val_in,
+                                                           int32_t *__restrict__ col_out,
+                                                           uint32_t *__restrict__ val_out) {
+    const int64_t p = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (p < n) {
+        const int32_t src = perm[p];
+        col_out[p] = col_in[src];
+        val_out[p] = val_in[src];
+    }
+}
+
+// One wave per 64 consecutive rows; all 64 lanes fill each row's range in turn.
+__global__ __launch_bounds__(kThreads) void k_expand_rows(int32_t R,
+                                                          const int32_t *__restrict__ rp,
+                                                          int32_t *__restrict__ row_idx) {
+    const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) / kWave;
+    const int lane = __lane_id();
+    const int64_t r0 = wave * kWave;
+    if (r0 >= R) return;
+    const int64_t my = r0 + lane;
+    const int32_t a = my < R ? rp[my] : 0;
+    const int32_t b = my < R ? rp[my + 1] : 0;
+    for (int k = 0; k < kWave && r0 + k < R; ++k) {
+        const int32_t ak = __shfl(a, k), bk = __shfl(b, k);
+        for (int32_t i = ak + lane; i < bk; i += kWave) row_idx[i] = static_cast<int32_t>(r0 + k);
+    }
+}
+
+// One lane per row writes its `width` slots; for a fixed slot t neighbouring
+// lanes write neighbouring words (t*R + r), so the stores coalesce.
+__global__ __launch_bounds__(kThreads) void k_build_ell(int32_t R, int32_t width,
+                                                        const int32_t *__restrict__ rp,
+                                                        const int32_t *__restrict__ col,
+                                                        const uint32_t *__restrict__ val,
+                                                        int32_t *__restrict__ ell_col,
+                                                        uint32_t *__restrict__ ell_val,
+                                                        int32_t *__restrict__ ell_nnz) {
+    const int64_t r = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (r >= R) return;
+    const int32_t a = rp[r];
+    int32_t n = rp[r + 1] - a;
+    if (n > width) n = width;
+    ell_nnz[r] = n;
+    for (int32_t t = 0; t < width; ++t) {
+        const int64_t slot = static_cast<int64_t>(t) * R + r;
+        if (t < n) {
+            ell_col[slot] = col[a + t];
+            ell_val[slot] = val[a + t];
+        } else {
+            ell_col[slot] = 0;
+            ell_val[slot] = 0u;  // +0.0f
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_tail_lengths(int32_t R, int32_t K,
+                                                           const int32_t *__restrict__ rp,
+                                                           int32_t *__restrict__ tail_len) {
+    const int64_t r = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (r < R) {
+        const int32_t len = rp[r + 1] - rp[r];
+        tail_len[r] = len > K ? len - K : 0;
+    }
+}
+
+// One lane per tail entry e: its row is the last r with tail_off[r] <= e.
+__global__ __launch_bounds__(kThreads) void k_fill_tail(
+    int32_t R, int32_t K, int32_t ntail, const int32_t *__restrict__ rp,
+    const int32_t *__restrict__ tail_off, const int32_t *__restrict__ col,
+    const uint32_t *__restrict__ val, int32_t *__restrict__ tail_row,
+    int32_t *__restrict__ tail_col, uint32_t *__restrict__ tail_val) {
+    const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (e >= ntail) return;
+    const int64_t r = upper_index(tail_off, R, e);
+    const int64_t src = static_cast<int64_t>(rp[r]) + K + (e - tail_off[r]);
+    tail_row[e] = static_cast<int32_t>(r);
+    tail_col[e] = col[src];
+    tail_val[e] = val[src];
+}
+
+// JDS sort key: W - len, so an ascending stable sort puts longer rows first and
+// keeps the original order among equal lengths.
+__global__ __launch_bounds__(kThreads) void k_jds_keys(int32_t R, int32_t W,
+                                                       const int32_t *__restrict__ rp,
+                                                       uint32_t *__restrict__ keys,
+                                                       int32_t *__restrict__ rows) {
+    const int64_t r = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (r < R) {
+        keys[r] = static_cast<uint32_t>(W - (rp[r + 1] - rp[r]));
+        rows[r] = static_cast<int32_t>(r);
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_jds_lengths(int32_t R, int32_t W,
+                                                          const uint32_t *__restrict__ keys,
+                                                          int32_t *__restrict__ jds_len) {
+    const int64_t s = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (s < R) jds_len[s] = W - static_cast<int32_t>(keys[s]);
+}
+
+// counts[t] = number of sorted rows longer than t = first s with len[s] <= t.
+__global__ __launch_bounds__(kThreads) void k_jds_counts(int32_t R, int32_t W,
+                                                         const int32_t *__restrict__ jds_len,
+                                                         int32_t *__restrict__ counts) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (t >= W) return;
+    int64_t lo = 0, hi = R;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (jds_len[mid] > t) lo = mid + 1; else hi = mid;
+    }
+    counts[t] = static_cast<int32_t>(lo);
+}
+
+// One lane per JDS slot e: jagged column t = last t with iter_ptr[t] <= e,
+// sorted row s = e - iter_ptr[t], source entry t of original row perm[s].
+__global__ __launch_bounds__(kThreads) void k_jds_fill(int32_t nnz, int32_t W,
+                                                       const int32_t *__restrict__ iter_ptr,
+                                                       const int32_t *__restrict__ perm,
+                                                       const int32_t *__restrict__ rp,
+                                                       const int32_t *__restrict__ col,
+                                                       const uint32_t *__restrict__ val,
+                                                       int32_t *__restrict__ jds_col,
+                                                       uint32_t *__restrict__ jds_val) {
+    const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (e >= nnz) return;
+    const int64_t t = upper_index(iter_ptr, W, e);
+    const int64_t s = e - iter_ptr[t];
+    const int64_t src = static_cast<int64_t>(rp[perm[s]]) + t;
+    jds_col[e] = col[src];
+    jds_val[e] = val[src];
+}
+
+// Tiles of the JDS kernel: 64 consecutive sorted rows x `depth` jagged columns.
+// Group g needs ceil(len[64 g] / depth) tiles (its first row is its longest).
+__global__ __launch_bounds__(kThreads) void k_jds_chunks(int32_t R, int32_t depth,
+                                                         const int32_t *__restrict__ jds_len,
+                                                         int32_t *__restrict__ chunks) {
+    const int64_t g = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    const int64_t groups = (static_cast<int64_t>(R) + kWave - 1) / kWave;
+    if (g < groups) {
+        const int32_t len = jds_len[g * kWave];
+        chunks[g] = (len + depth - 1) / depth;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_jds_tiles(int32_t groups, int32_t ntiles,
+                                                        const int32_t *__restrict__ tile_off,
+                                                        int2 *__restrict__ tiles) {
+    const int64_t tile = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (tile >= ntiles) return;
+    const int64_t g = upper_index(tile_off, groups, tile);
+    tiles[tile] = make_int2(static_cast<int>(g), static_cast<int>(tile - tile_off[g]));
+}
+
+// Merge path over rows (their end markers) and nonzeros: row r's end marker
+// sits at position rowPtrs[r+1] + r.  row_start[b] = number of rows whose end
+// marker lies before diagonal b * items_per_block.
+__global__ __launch_bounds__(kThreads) void k_merge_partition(int32_t R, int32_t nnz,
+                                                              const int32_t *__restrict__ rp,
+                                                              int32_t nblocks,
+                                                              int32_t *__restrict__ row_start) {
+    const int64_t b = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (b > nblocks) return;
+    const int64_t total = static_cast<int64_t>(R) + nnz;
+    int64_t d = b * kMergeItemsPerBlock;
+    if (d > total) d = total;
+    int64_t lo = 0, hi = R;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (static_cast<int64_t>(rp[mid + 1]) + mid < d) lo = mid + 1; else hi = mid;
+    }
+    row_start[b] = static_cast<int32_t>(lo);
+}
+
+}  // namespace
+
+hipError_t launch_count_rows(int32_t nnz, const int32_t *row, int32_t *counts, hipStream_t s) {
+    if (nnz <= 0) return hipSuccess;
+    k_count_rows<<<grid_for(nnz, kThreads), kThreads, 0, s>>>(nnz, row, counts);
+    return hipGetLastError();
+}
+
+hipError_t launch_iota(int32_t n, int32_t *out, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    k_iota<<<grid_for(n, kThreads), kThreads, 0, s>>>(n, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_pairs(int32_t nnz, const int32_t *perm, const int32_t *col_in,
+                               const float *val_in, int32_t *col_out, float *val_out,
+                               hipStream_t s) {
+    if (nnz <= 0) return hipSuccess;
+    k_gather_pairs<<<grid_for(nnz, kThreads), kThreads, 0, s>>>(
+        nnz, perm, col_in, reinterpret_cast<const uint32_t *>(val_in), col_out,
+        reinterpret_cast<uint32_t *>(val_out));
+    return hipGetLastError();
+}
+
+hipError_t launch_expand_rows(int32_t R, int32_t nnz, const int32_t *rp, int32_t *row_idx,
+                              hipStream_t s) {
+    if (R <= 0 || nnz <= 0) return hipSuccess;
+    const int64_t waves = (static_cast<int64_t>(R) + kWave - 1) / kWave;
+    k_expand_rows<<<grid_for(waves * kWave, kThreads), kThreads, 0, s>>>(R, rp, row_idx);
+    return hipGetLastError();
+}
+
+hipError_t launch_build_ell(int32_t R, int32_t width, const int32_t *rp, const int32_t *col,
+                            const float *val, int32_t *ell_col, float *ell_val,
+                            int32_t *ell_nnz, hipStream_t s) {
+    if (R <= 0) return hipSuccess;
+    k_build_ell<<<grid_for(R, kThreads), kThreads, 0, s>>>(
+        R, width, rp, col, reinterpret_cast<const uint32_t *>(val), ell_col,
+        reinterpret_cast<uint32_t *>(ell_val), ell_nnz);
+    return hipGetLastError();
+}
+
+hipError_t launch_tail_lengths(int32_t R, int32_t K, const int32_t *rp, int32_t *tail_len,
+                               hipStream_t s) {
+    if (R <= 0) return hipSuccess;
+    k_tail_lengths<<<grid_for(R, kThreads), kThreads, 0, s>>>(R, K, rp, tail_len);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_tail(int32_t R, int32_t K, int32_t ntail, const int32_t *rp,
+                            const int32_t *tail_off, const int32_t *col, const float *val,
+                            int32_t *tail_row, int32_t *tail_col, float *tail_val,
+                            hipStream_t s) {
+    if (ntail <= 0) return hipSuccess;
+    k_fill_tail<<<grid_for(ntail, kThreads), kThreads, 0, s>>>(
+        R, K, ntail, rp, tail_off, col, reinterpret_cast<const uint32_t *>(val), tail_row,
+        tail_col, reinterpret_cast<uint32_t *>(tail_val));
+    return hipGetLastError();
+}
+
+hipError_t launch_jds_keys(int32_t R, int32_t W, const int32_t *rp, uint32_t *keys,
+                           int32_t *rows, hipStream_t s) {
+    if (R <= 0) return hipSuccess;
+    k_jds_keys<<<grid_for(R, kThreads), kThreads, 0, s>>>(R, W, rp, keys, rows);
+    return hipGetLastError();
+}
+
+hipError_t launch_jds_lengths(int32_t R, int32_t W, const uint32_t *sorted_keys,
+                              int32_t *jds_len, hipStream_t s) {
+    if (R <= 0) return hipSuccess;
+    k_jds_lengths<<<grid_for(R, kThreads), kThreads, 0, s>>>(R, W, sorted_keys, jds_len);
+    return hipGetLastError();
+}
+
+hipError_t launch_jds_counts(int32_t R, int32_t W, const int32_t *jds_len, int32_t *counts,
+                             hipStream_t s) {
+    if (W <= 0) return hipSuccess;
+    k_jds_counts<<<grid_for(W, kThreads), kThreads, 0, s>>>(R, W, jds_len, counts);
+    return hipGetLastError();
+}
+
+hipError_t launch_jds_fill(int32_t nnz, int32_t W, const int32_t *iter_ptr,
+                           const int32_t *perm, const int32_t *rp, const int32_t *col,
+                           const float *val, int32_t *jds_col, float *jds_val, hipStream_t s) {
+    if (nnz <= 0) return hipSuccess;
+    k_jds_fill<<<grid_for(nnz, kThreads), kThreads, 0, s>>>(
+        nnz, W, iter_ptr, perm, rp, col, reinterpret_cast<const uint32_t *>(val), jds_col,
+        reinterpret_cast<uint32_t *>(jds_val));
+    return hipGetLastError();
+}
+
+hipError_t launch_jds_chunks(int32_t R, int32_t depth, const int32_t *jds_len,
+                             int32_t *chunks, hipStream_t s) {
+    if (R <= 0) return hipSuccess;
+    const int64_t groups = (static_cast<int64_t>(R) + kWave - 1) / kWave;
+    k_jds_chunks<<<grid_for(groups, kThreads), kThreads, 0, s>>>(R, depth, jds_len, chunks);
+    return hipGetLastError();
+}
+
+hipError_t launch_jds_tiles(int32_t groups, int32_t ntiles, const int32_t *tile_off,
+                            int2 *tiles, hipStream_t s) {
+    if (ntiles <= 0) return hipSuccess;
+    k_jds_tiles<<<grid_for(ntiles, kThreads), kThreads, 0, s>>>(groups, ntiles, tile_off, tiles);
+    return hipGetLastError();
+}
+
+hipError_t launch_merge_partition(int32_t R, int32_t nnz, const int32_t *rp, int32_t nblocks,
+                                  int32_t *row_start, hipStream_t s) {
+    k_merge_partition<<<grid_for(static_cast<int64_t>(nblocks) + 1, kThreads), kThreads, 0, s>>>(
+        R, nnz, rp, nblocks, row_start);
+    return hipGetLastError();
+}
+
+}  // namespace spmv

@@ -1,0 +1,250 @@
+// Internal declarations of the gfx950 SpMV library: handle layout, device
+// helpers shared by the kernels, and the host-side launchers each .hip file
+// provides.  Nothing here is part of the public C ABI (include/spmv.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include "spmv.h"
+
+namespace spmv {
+
+constexpr int kWave = 64;       // CDNA wavefront width
+constexpr int kNumXcd = 8;      // MI355X: 8 accelerator complex dies, 32 CUs each
+constexpr int kJdsDepthDefault = 128;
+
+// Merge-path CSR: 256 threads x 8 merge items (row ends + nonzeros) per block.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeItemsPerThread = 8;
+constexpr int kMergeItemsPerBlock = kMergeThreads * kMergeItemsPerThread;
+
+// Validation flags written by the analysis kernels.
+enum : int { kFlagBadRowPtrs = 1, kFlagBadCol = 2, kFlagBadRow = 4, kFlagUnsortedRows = 8 };
+
+// ---------------------------------------------------------------------------
+// Handle: every device array the built format needs.  Unused ones are null.
+// ---------------------------------------------------------------------------
+struct DevArrays {
+    // CSR (CSR scalar / vector / merge)
+    int32_t *row_ptrs = nullptr;
+    int32_t *col_idx = nullptr;
+    float *values = nullptr;
+    // COO (COO atomic / segmented): col_idx, values above plus row_idx
+    int32_t *row_idx = nullptr;
+    // ELL or the ELL part of HYB
+    int32_t *ell_col = nullptr;
+    float *ell_val = nullptr;
+    int32_t *ell_nnz = nullptr;
+    // HYB COO tail
+    int32_t *tail_row = nullptr;
+    int32_t *tail_col = nullptr;
+    float *tail_val = nullptr;
+    // JDS
+    int32_t *jds_perm = nullptr;
+    int32_t *jds_len = nullptr;
+    int32_t *jds_iter_ptr = nullptr;
+    int32_t *jds_col = nullptr;
+    float *jds_val = nullptr;
+    int2 *jds_tiles = nullptr;      // (group of 64 sorted rows, depth chunk)
+    // CSR merge: first row of each block's merge-path segment, [blocks + 1]
+    int32_t *merge_row_start = nullptr;
+};
+
+}  // namespace spmv
+
+struct spmv_handle {
+    int device = 0;
+    int32_t format = 0;
+    int32_t hyb_width = 0;
+    int32_t lanes = 0;
+    int32_t ell_width = 0;
+    int32_t jds_depth = spmv::kJdsDepthDefault;
+    spmv_stats stats{};
+    std::vector<int64_t> hist;      // host copy of the row-length histogram
+    int64_t tail_nnz = 0;
+    int64_t num_tiles = 0;
+    int64_t device_bytes = 0;
+    spmv::DevArrays a;
+    std::vector<void *> owned;      // every device allocation of this handle
+};
+
+namespace spmv {
+
+// ---------------------------------------------------------------------------
+// Host helpers
+// ---------------------------------------------------------------------------
+spmv_status from_hip(hipError_t e);
+
+#define SPMV_HIP(expr)                                      \
+    do {                                                    \
+        hipError_t _e = (expr);                             \
+        if (_e != hipSuccess) return ::spmv::from_hip(_e);  \
+    } while (0)
+
+#define SPMV_TRY(expr)                                      \
+    do {                                                    \
+        spmv_status _s = (expr);                            \
+        if (_s != SPMV_OK) return _s;                       \
+    } while (0)
+
+// Temporary device buffers of one host call; freed (after the stream drains)
+// when the object goes out of scope.
+class Scratch {
+  public:
+    explicit Scratch(hipStream_t s) : stream_(s) {}
+    ~Scratch();
+    Scratch(const Scratch &) = delete;
+    Scratch &operator=(const Scratch &) = delete;
+    template <typename T>
+    spmv_status alloc(T **p, size_t count) {
+        return alloc_bytes(reinterpret_cast<void **>(p), count * sizeof(T));
+    }
+    spmv_status alloc_bytes(void **p, size_t bytes);
+
+  private:
+    hipStream_t stream_;
+    std::vector<void *> ptrs_;
+};
+
+inline unsigned grid_for(int64_t n, int per_block) {
+    int64_t g = (n + per_block - 1) / per_block;
+    return static_cast<unsigned>(g < 1 ? 1 : g);
+}
+
+inline int bits_for(uint64_t max_value) {
+    int b = 0;
+    while (b < 64 && (max_value >> b) != 0) ++b;
+    return b;
+}
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+
+// Workgroups are dispatched to the 8 XCDs round-robin (block b -> XCD b % 8).
+// Re-number blocks so each XCD works on one contiguous range of logical
+// blocks: neighbouring rows (and the x entries they share) then meet in the
+// same 4 MB L2.
+__device__ inline uint32_t xcd_remap(uint32_t b, uint32_t nblocks) {
+    uint32_t per = nblocks / kNumXcd, rem = nblocks % kNumXcd;
+    uint32_t xcd = b % kNumXcd, idx = b / kNumXcd;
+    return xcd * per + (xcd < rem ? xcd : rem) + idx;
+}
+
+template <typename T>
+__device__ inline T ld_nt(const T *p) {
+    return __builtin_nontemporal_load(p);
+}
+
+// DPP controls (gfx9 encoding)
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+#define SPMV_DPP_F32(v, ctrl)                                                              \
+    __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, (v)), \
+                                                          (ctrl), 0xF, 0xF, false))
+
+// Sum over aligned groups of L lanes (L = 1..64, power of two).  Every lane of
+// the wave must execute this with EXEC full; the result is valid in every lane
+// of the group for L <= 32 and wave-uniform for L = 64.
+template <int L>
+__device__ inline float group_sum(float v) {
+    if constexpr (L >= 2) v += SPMV_DPP_F32(v, kDppQuadXor1);
+    if constexpr (L >= 4) v += SPMV_DPP_F32(v, kDppQuadXor2);
+    if constexpr (L >= 8) v += SPMV_DPP_F32(v, kDppRowHalfMirror);
+    if constexpr (L >= 16) v += SPMV_DPP_F32(v, kDppRowMirror);
+    if constexpr (L >= 32) {
+        // ds_swizzle bit mode within 32 lanes: and 0x1f, or 0, xor 0x10
+        v += __builtin_bit_cast(float,
+                                __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+    }
+    if constexpr (L >= 64) {
+        int bits = __builtin_bit_cast(int, v);
+        v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(bits, 0)) +
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(bits, 32));
+    }
+    return v;
+}
+
+// Largest i in [0, n) with a[i] <= key, for non-decreasing a with a[0] <= key.
+__device__ inline int64_t upper_index(const int32_t *a, int64_t n, int64_t key) {
+    int64_t lo = 0, hi = n - 1;
+    while (lo < hi) {
+        int64_t mid = (lo + hi + 1) >> 1;
+        if (a[mid] <= key) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// ---------------------------------------------------------------------------
+// Launchers provided by the .hip files (all enqueue on `s`)
+// ---------------------------------------------------------------------------
+
+// analyze.hip
+struct RowStatsDev {                 // device-side accumulators
+    int flags;
+    int max_len;
+    unsigned long long sum_len_sq;
+    unsigned long long empty_rows;
+};
+hipError_t launch_row_checks(int32_t R, int32_t nnz, const int32_t *rp, RowStatsDev *st,
+                             hipStream_t s);
+hipError_t launch_col_checks(int32_t nnz, int32_t C, const int32_t *col, RowStatsDev *st,
+                             hipStream_t s);
+hipError_t launch_coo_checks(int32_t nnz, int32_t R, int32_t C, const int32_t *row,
+                             const int32_t *col, int check_cols, RowStatsDev *st, hipStream_t s);
+hipError_t launch_len_hist(int32_t R, const int32_t *rp, int32_t W, int32_t *hist, hipStream_t s);
+
+// scan.hip: exclusive scan of n int32 values; out[n] receives the total when
+// write_total.  in and out may alias.
+spmv_status exclusive_scan(const int32_t *in, int32_t *out, int64_t n, bool write_total,
+                           hipStream_t s, Scratch &scratch);
+
+// sort.hip: stable LSD radix sort of (key, value) pairs by the low key_bits.
+spmv_status radix_sort_pairs(const uint32_t *keys_in, const int32_t *vals_in,
+                             uint32_t *keys_out, int32_t *vals_out, int64_t n, int key_bits,
+                             hipStream_t s, Scratch &scratch);
+
+// build.hip
+hipError_t launch_count_rows(int32_t nnz, const int32_t *row, int32_t *counts, hipStream_t s);
+hipError_t launch_iota(int32_t n, int32_t *out, hipStream_t s);
+hipError_t launch_gather_pairs(int32_t nnz, const int32_t *perm, const int32_t *col_in,
+                               const float *val_in, int32_t *col_out, float *val_out,
+                               hipStream_t s);
+hipError_t launch_expand_rows(int32_t R, int32_t nnz, const int32_t *rp, int32_t *row_idx,
+                              hipStream_t s);
+hipError_t launch_build_ell(int32_t R, int32_t width, const int32_t *rp, const int32_t *col,
+                            const float *val, int32_t *ell_col, float *ell_val,
+                            int32_t *ell_nnz, hipStream_t s);
+hipError_t launch_tail_lengths(int32_t R, int32_t K, const int32_t *rp, int32_t *tail_len,
+                               hipStream_t s);
+hipError_t launch_fill_tail(int32_t R, int32_t K, int32_t ntail, const int32_t *rp,
+                            const int32_t *tail_off, const int32_t *col, const float *val,
+                            int32_t *tail_row, int32_t *tail_col, float *tail_val,
+                            hipStream_t s);
+hipError_t launch_jds_keys(int32_t R, int32_t W, const int32_t *rp, uint32_t *keys,
+                           int32_t *rows, hipStream_t s);
+hipError_t launch_jds_lengths(int32_t R, int32_t W, const uint32_t *sorted_keys,
+                              int32_t *jds_len, hipStream_t s);
+hipError_t launch_jds_counts(int32_t R, int32_t W, const int32_t *jds_len, int32_t *counts,
+                             hipStream_t s);
+hipError_t launch_jds_fill(int32_t nnz, int32_t W, const int32_t *iter_ptr,
+                           const int32_t *perm, const int32_t *rp, const int32_t *col,
+                           const float *val, int32_t *jds_col, float *jds_val, hipStream_t s);
+hipError_t launch_jds_chunks(int32_t R, int32_t depth, const int32_t *jds_len,
+                             int32_t *chunks, hipStream_t s);
+hipError_t launch_jds_tiles(int32_t groups, int32_t ntiles, const int32_t *tile_off,
+                            int2 *tiles, hipStream_t s);
+hipError_t launch_merge_partition(int32_t R, int32_t nnz, const int32_t *rp, int32_t nblocks,
+                                  int32_t *row_start, hipStream_t s);
+
+// spmv_kernels.hip: y <- A x + y for the handle's format
+spmv_status launch_spmv(const spmv_handle *h, const float *x, float *y, hipStream_t s);
+
+}  // namespace spmv

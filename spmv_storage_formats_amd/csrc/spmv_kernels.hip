@@ -1,0 +1,423 @@
+// SpMV kernels for gfx950: y <- A*x + y.
+//
+// All kernels accumulate into y (PMPP notes, "Sparse Matrices and Basic
+// Formats (COO & CSR)": SpMV computes A*X + Y; its CSR kernel adds the row sum
+// into y[row]).  Streams of matrix data are read with non-temporal loads so the
+// gathered x stays resident in the per-XCD L2.  Kernels that own whole rows
+// (CSR scalar/vector, ELL, JDS rows of one tile) write y with a plain
+// read-modify-write; kernels whose rows can be split across waves or blocks
+// (COO, HYB tail, long JDS rows, merge-path boundary rows) use hardware fp32
+// global atomics for exactly those rows.  Rows without nonzeros are never
+// written.
+#include "internal.h"
+
+namespace spmv {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ inline void atomic_add_f32(float *p, float v) { unsafeAtomicAdd(p, v); }
+
+__device__ inline void lds_add_f32(float *p, float v) {
+    __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// ---------------------------------------------------------------------------
+// COO, one lane per nonzero [COO/CSR page, COO kernel: each thread takes one
+// nonzero; two threads may hit the same y[row], hence the atomic add].
+// ---------------------------------------------------------------------------
+constexpr int kCooPerThread = 4;
+
+__global__ __launch_bounds__(kThreads) void k_coo_atomic(int32_t nnz,
+                                                         const int32_t *__restrict__ row,
+                                                         const int32_t *__restrict__ col,
+                                                         const float *__restrict__ val,
+                                                         const float *__restrict__ x,
+                                                         float *__restrict__ y) {
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * kThreads * kCooPerThread + threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < kCooPerThread; ++j) {
+        const int64_t i = base + j * kThreads;
+        if (i < nnz) atomic_add_f32(&y[ld_nt(row + i)], ld_nt(val + i) * x[ld_nt(col + i)]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// COO segmented: the COO entries are sorted by row.  One wave walks 64*8
+// consecutive entries, 64 at a time (coalesced); a segmented inclusive scan
+// over the wave sums each run of equal rows, the last lane of a run adds the
+// run's total with one atomic, and the wave's last run is carried into the
+// next 64 entries.  Used for COO input and for the HYB tail.
+// ---------------------------------------------------------------------------
+constexpr int kSegIters = 8;
+
+__global__ __launch_bounds__(kThreads) void k_coo_segmented(int32_t nnz,
+                                                            const int32_t *__restrict__ row,
+                                                            const int32_t *__restrict__ col,
+                                                            const float *__restrict__ val,
+                                                            const float *__restrict__ x,
+                                                            float *__restrict__ y) {
+    const int lane = __lane_id();
+    const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) / kWave;
+    const int64_t base = wave * (kWave * kSegIters);
+    if (base >= nnz) return;
+    int carry_row = INT32_MAX;
+    float carry = 0.f;
+    for (int it = 0; it < kSegIters; ++it) {
+        const int64_t i = base + it * kWave + lane;
+        const bool valid = i < nnz;
+        const int32_t r = valid ? ld_nt(row + i) : INT32_MAX;
+        float p = valid ? ld_nt(val + i) * x[ld_nt(col + i)] : 0.f;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int32_t ru = __shfl_up(r, off);
+            const float pu = __shfl_up(p, off);
+            if (lane >= off && ru == r) p += pu;
+        }
+        if (r == carry_row) p += carry;
+        const int32_t rn = __shfl_down(r, 1);
+        if (valid && lane != kWave - 1 && rn != r) atomic_add_f32(&y[r], p);
+        carry_row = __builtin_amdgcn_readlane(r, kWave - 1);
+        carry = __builtin_bit_cast(float,
+                                   __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), kWave - 1));
+        if (base + (it + 1) * kWave >= nnz) break;
+    }
+    if (lane == 0 && carry_row != INT32_MAX) atomic_add_f32(&y[carry_row], carry);
+}
+
+// ---------------------------------------------------------------------------
+// CSR scalar: one lane per row [COO/CSR page, CSR kernel; format-choice
+// article 2.1], with the block's 257 row pointers staged in LDS (article 4.2).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_csr_scalar(int32_t R, const int32_t *__restrict__ rp,
+                                                         const int32_t *__restrict__ col,
+                                                         const float *__restrict__ val,
+                                                         const float *__restrict__ x,
+                                                         float *__restrict__ y) {
+    __shared__ int32_t srp[kThreads + 1];
+    const uint32_t b = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t r0 = static_cast<int64_t>(b) * kThreads;
+    const int64_t r = r0 + threadIdx.x;
+    if (r <= R) srp[threadIdx.x] = rp[r];
+    if (threadIdx.x == 0 && r0 + kThreads <= R) srp[kThreads] = rp[r0 + kThreads];
+    __syncthreads();
+    if (r >= R) return;
+    const int32_t a = srp[threadIdx.x], e = srp[threadIdx.x + 1];
+    if (a == e) return;
+    float sum = 0.f;
+    int32_t i = a;
+    for (; i + 4 <= e; i += 4) {
+        const int32_t c0 = ld_nt(col + i), c1 = ld_nt(col + i + 1), c2 = ld_nt(col + i + 2),
+                      c3 = ld_nt(col + i + 3);
+        const float v0 = ld_nt(val + i), v1 = ld_nt(val + i + 1), v2 = ld_nt(val + i + 2),
+                    v3 = ld_nt(val + i + 3);
+        sum += v0 * x[c0];
+        sum += v1 * x[c1];
+        sum += v2 * x[c2];
+        sum += v3 * x[c3];
+    }
+    for (; i < e; ++i) sum += ld_nt(val + i) * x[ld_nt(col + i)];
+    y[r] += sum;
+}
+
+// ---------------------------------------------------------------------------
+// CSR vector: a group of L lanes per row (format-choice article 2.2 gives one
+// 32-lane warp per row; here L = 2..64 of a 64-lane wavefront).  Lanes stride
+// the row by L; the group sum uses DPP / ds_swizzle (group_sum).
+// ---------------------------------------------------------------------------
+template <int L>
+__global__ __launch_bounds__(kThreads) void k_csr_vector(int32_t R, const int32_t *__restrict__ rp,
+                                                         const int32_t *__restrict__ col,
+                                                         const float *__restrict__ val,
+                                                         const float *__restrict__ x,
+                                                         float *__restrict__ y) {
+    constexpr int kRows = kThreads / L;
+    __shared__ int32_t srp[kRows + 1];
+    const uint32_t b = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t r0 = static_cast<int64_t>(b) * kRows;
+    if (threadIdx.x <= kRows && r0 + threadIdx.x <= R) srp[threadIdx.x] = rp[r0 + threadIdx.x];
+    __syncthreads();
+    const int g = threadIdx.x / L, lg = threadIdx.x % L;
+    const int64_t r = r0 + g;
+    int32_t a = 0, e = 0;
+    if (r < R) {
+        a = srp[g];
+        e = srp[g + 1];
+    }
+    float s0 = 0.f, s1 = 0.f;
+    int32_t j = a + lg;
+    for (; j + L < e; j += 2 * L) {
+        const int32_t c0 = ld_nt(col + j), c1 = ld_nt(col + j + L);
+        const float v0 = ld_nt(val + j), v1 = ld_nt(val + j + L);
+        s0 += v0 * x[c0];
+        s1 += v1 * x[c1];
+    }
+    if (j < e) s0 += ld_nt(val + j) * x[ld_nt(col + j)];
+    const float sum = group_sum<L>(s0 + s1);
+    if (lg == 0 && e > a) y[r] += sum;
+}
+
+// ---------------------------------------------------------------------------
+// ELL: one lane per row, slot t of row r at t*R + r, so at every step the
+// lanes of a wave read one contiguous 256-byte run of values and of columns
+// [Regularized formats page, ELL section].  Slots past nnzPerRow[r] are
+// padding and contribute nothing (the padded loads are part of the stream).
+// ---------------------------------------------------------------------------
+template <int U>
+__global__ __launch_bounds__(kThreads) void k_ell(int32_t R, int32_t W,
+                                                  const int32_t *__restrict__ ell_col,
+                                                  const float *__restrict__ ell_val,
+                                                  const int32_t *__restrict__ ell_nnz,
+                                                  const float *__restrict__ x,
+                                                  float *__restrict__ y) {
+    const uint32_t b = xcd_remap(blockIdx.x, gridDim.x);
+    const uint32_t r = b * kThreads + threadIdx.x;
+    if (r >= static_cast<uint32_t>(R)) return;
+    const int32_t n = ld_nt(ell_nnz + r);
+    float sum = 0.f;
+    for (int32_t t0 = 0; t0 < W; t0 += U) {
+        int32_t c[U];
+        float v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int32_t t = t0 + u;
+            const uint32_t slot = static_cast<uint32_t>(t) * static_cast<uint32_t>(R) + r;
+            c[u] = t < W ? ld_nt(ell_col + slot) : 0;
+            v[u] = t < W ? ld_nt(ell_val + slot) : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (t0 + u < n) sum += v[u] * x[c[u]];
+    }
+    if (n > 0) y[r] += sum;
+}
+
+// ---------------------------------------------------------------------------
+// JDS: rows sorted by length (longest first) in jagged columns; entry t of
+// sorted row s at iterPtr[t] + s [Regularized formats page, JDS section: one
+// thread per row, iterPtr gives each iteration's start].  One wave takes a
+// tile of 64 consecutive sorted rows x `depth` jagged columns, so a few very
+// long rows are split over many waves instead of serialising one lane; the
+// split rows are combined with atomics.  iterPtr[t] is wave-uniform (scalar
+// load); lane s reads iterPtr[t] + s, contiguous across the wave.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_jds(int32_t R, int32_t ntiles, int32_t depth,
+                                                  const int2 *__restrict__ tiles,
+                                                  const int32_t *__restrict__ jds_len,
+                                                  const int32_t *__restrict__ iter_ptr,
+                                                  const int32_t *__restrict__ perm,
+                                                  const int32_t *__restrict__ col,
+                                                  const float *__restrict__ val,
+                                                  const float *__restrict__ x,
+                                                  float *__restrict__ y) {
+    const int64_t tile = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) / kWave;
+    if (tile >= ntiles) return;
+    const int lane = __lane_id();
+    const int2 gc = tiles[tile];
+    const int g = __builtin_amdgcn_readfirstlane(gc.x);
+    const int chunk = __builtin_amdgcn_readfirstlane(gc.y);
+    const int64_t s = static_cast<int64_t>(g) * kWave + lane;
+    const int32_t len = s < R ? jds_len[s] : 0;
+    const int32_t glen = __builtin_amdgcn_readfirstlane(jds_len[static_cast<int64_t>(g) * kWave]);
+    const int32_t t0 = chunk * depth;
+    const int32_t t1 = min(t0 + depth, glen);
+    float s0 = 0.f, s1 = 0.f;
+    int32_t t = t0;
+    for (; t + 1 < t1; t += 2) {
+        const int32_t p0 = iter_ptr[t], p1 = iter_ptr[t + 1];
+        if (t < len) s0 += ld_nt(val + p0 + s) * x[ld_nt(col + p0 + s)];
+        if (t + 1 < len) s1 += ld_nt(val + p1 + s) * x[ld_nt(col + p1 + s)];
+    }
+    if (t < t1 && t < len) {
+        const int32_t p0 = iter_ptr[t];
+        s0 += ld_nt(val + p0 + s) * x[ld_nt(col + p0 + s)];
+    }
+    if (len > t0) {
+        const int32_t r = perm[s];
+        if (glen > depth) atomic_add_f32(&y[r], s0 + s1);
+        else y[r] += s0 + s1;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Merge-path CSR [format-choice article 5.2: merge-based CSR for power-law
+// graphs; "Introduction to sparse computing", parallel efficiency: split by
+// nonzero count, split long rows].  The rows' end markers and the nonzeros
+// form one sequence of R + nnz items; block b owns items
+// [b*2048, (b+1)*2048), starting at row row_start[b].  The block stages its
+// row ends and its products val*x[col] (coalesced loads) in LDS, each thread
+// consumes 8 items of the merged sequence and adds its per-row partial sums
+// into LDS accumulators, then the block writes its rows: rows that begin and
+// end inside the block with a plain update, the (at most two) rows cut by the
+// block's ends with an atomic add.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kMergeThreads) void k_merge(int32_t R, int32_t nnz,
+                                                         const int32_t *__restrict__ row_start,
+                                                         const int32_t *__restrict__ rp,
+                                                         const int32_t *__restrict__ col,
+                                                         const float *__restrict__ val,
+                                                         const float *__restrict__ x,
+                                                         float *__restrict__ y) {
+    constexpr int NB = kMergeItemsPerBlock;
+    constexpr int IPT = kMergeItemsPerThread;
+    __shared__ int32_t s_end[NB];
+    __shared__ float s_prod[NB];
+    __shared__ float s_acc[NB + 1];
+    const int tid = threadIdx.x;
+    const int64_t total = static_cast<int64_t>(R) + nnz;
+    const int64_t d0 = static_cast<int64_t>(blockIdx.x) * NB;
+    const int64_t d1 = min(d0 + NB, total);
+    const int32_t r0 = row_start[blockIdx.x];
+    const int32_t r1 = row_start[blockIdx.x + 1];
+    const int32_t k0 = static_cast<int32_t>(d0 - r0);
+    const int32_t k1 = static_cast<int32_t>(d1 - r1);
+    const int32_t nr = r1 - r0;
+    const int32_t nk = k1 - k0;
+
+    for (int i = tid; i < nr; i += kMergeThreads) s_end[i] = rp[r0 + 1 + i] - k0;
+    for (int j = tid; j < nk; j += kMergeThreads) {
+        const int32_t kk = k0 + j;
+        s_prod[j] = ld_nt(val + kk) * x[ld_nt(col + kk)];
+    }
+    for (int i = tid; i <= nr; i += kMergeThreads) s_acc[i] = 0.f;
+    __syncthreads();
+
+    // Start of this thread's 8 items on the merge path: the number i of row
+    // ends before diagonal dt (row end i sits at local position s_end[i] + i).
+    const int32_t items = nr + nk;
+    const int32_t dt = min(tid * IPT, items);
+    int32_t lo = max(0, dt - nk), hi = min(dt, nr);
+    while (lo < hi) {
+        const int32_t mid = (lo + hi) >> 1;
+        if (s_end[mid] + mid < dt) lo = mid + 1; else hi = mid;
+    }
+    int32_t i = lo, k = dt - lo;
+    const int32_t dend = min(dt + IPT, items);
+    float sum = 0.f;
+    bool any = false;
+    for (int32_t d = dt; d < dend; ++d) {
+        if (i < nr && k >= s_end[i]) {   // row i ends here
+            if (any) lds_add_f32(&s_acc[i], sum);
+            sum = 0.f;
+            any = false;
+            ++i;
+        } else {
+            sum += s_prod[k];
+            ++k;
+            any = true;
+        }
+    }
+    if (any) lds_add_f32(&s_acc[i], sum);
+    __syncthreads();
+
+    for (int li = tid; li <= nr; li += kMergeThreads) {
+        const int32_t r = r0 + li;
+        if (r >= R) continue;
+        const int32_t start = li == 0 ? rp[r0] - k0 : s_end[li - 1];   // local offsets
+        const int32_t end = li < nr ? s_end[li] : nk;
+        const int32_t lo_k = max(start, 0), hi_k = min(end, nk);
+        if (hi_k <= lo_k) continue;                 // no nonzero of row r in this block
+        const float v = s_acc[li];
+        if (li == nr || start < 0) atomic_add_f32(&y[r], v);
+        else y[r] += v;
+    }
+}
+
+unsigned blocks_of(int64_t n, int per_block) { return grid_for(n, per_block); }
+
+template <int L>
+hipError_t run_vector(const spmv_handle *h, const float *x, float *y, hipStream_t s) {
+    constexpr int kRows = kThreads / L;
+    const int32_t R = static_cast<int32_t>(h->stats.num_rows);
+    k_csr_vector<L><<<blocks_of(R, kRows), kThreads, 0, s>>>(R, h->a.row_ptrs, h->a.col_idx,
+                                                             h->a.values, x, y);
+    return hipGetLastError();
+}
+
+hipError_t run_ell(int32_t R, int32_t W, const int32_t *col, const float *val,
+                   const int32_t *nnz_per_row, const float *x, float *y, hipStream_t s) {
+    if (R <= 0 || W <= 0) return hipSuccess;
+    const unsigned g = blocks_of(R, kThreads);
+    if (W <= 4) k_ell<4><<<g, kThreads, 0, s>>>(R, W, col, val, nnz_per_row, x, y);
+    else k_ell<8><<<g, kThreads, 0, s>>>(R, W, col, val, nnz_per_row, x, y);
+    return hipGetLastError();
+}
+
+hipError_t run_coo_segmented(int32_t n, const int32_t *row, const int32_t *col,
+                             const float *val, const float *x, float *y, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    const int64_t waves = (static_cast<int64_t>(n) + kWave * kSegIters - 1) / (kWave * kSegIters);
+    k_coo_segmented<<<blocks_of(waves * kWave, kThreads), kThreads, 0, s>>>(n, row, col, val, x,
+                                                                            y);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+spmv_status launch_spmv(const spmv_handle *h, const float *x, float *y, hipStream_t s) {
+    const int32_t R = static_cast<int32_t>(h->stats.num_rows);
+    const int32_t nnz = static_cast<int32_t>(h->stats.nnz);
+    if (R == 0 || nnz == 0) return SPMV_OK;
+    const DevArrays &a = h->a;
+    hipError_t e = hipSuccess;
+    switch (h->format) {
+    case SPMV_COO_ATOMIC:
+        k_coo_atomic<<<blocks_of(nnz, kThreads * kCooPerThread), kThreads, 0, s>>>(
+            nnz, a.row_idx, a.col_idx, a.values, x, y);
+        e = hipGetLastError();
+        break;
+    case SPMV_COO_SEGMENTED:
+        e = run_coo_segmented(nnz, a.row_idx, a.col_idx, a.values, x, y, s);
+        break;
+    case SPMV_CSR_SCALAR:
+        k_csr_scalar<<<blocks_of(R, kThreads), kThreads, 0, s>>>(R, a.row_ptrs, a.col_idx,
+                                                                a.values, x, y);
+        e = hipGetLastError();
+        break;
+    case SPMV_CSR_VECTOR:
+        switch (h->lanes) {
+        case 1:
+            k_csr_scalar<<<blocks_of(R, kThreads), kThreads, 0, s>>>(R, a.row_ptrs, a.col_idx,
+                                                                    a.values, x, y);
+            e = hipGetLastError();
+            break;
+        case 2: e = run_vector<2>(h, x, y, s); break;
+        case 4: e = run_vector<4>(h, x, y, s); break;
+        case 8: e = run_vector<8>(h, x, y, s); break;
+        case 16: e = run_vector<16>(h, x, y, s); break;
+        case 32: e = run_vector<32>(h, x, y, s); break;
+        case 64: e = run_vector<64>(h, x, y, s); break;
+        default: return SPMV_ERR_INVALID_ARG;
+        }
+        break;
+    case SPMV_ELL:
+        e = run_ell(R, h->ell_width, a.ell_col, a.ell_val, a.ell_nnz, x, y, s);
+        break;
+    case SPMV_HYB:
+        // ELL part first (plain y update per row), then the COO tail with
+        // atomics, in stream order: the two never touch y concurrently.
+        e = run_ell(R, h->ell_width, a.ell_col, a.ell_val, a.ell_nnz, x, y, s);
+        if (e == hipSuccess)
+            e = run_coo_segmented(static_cast<int32_t>(h->tail_nnz), a.tail_row, a.tail_col,
+                                  a.tail_val, x, y, s);
+        break;
+    case SPMV_JDS:
+        if (h->num_tiles > 0) {
+            k_jds<<<blocks_of(h->num_tiles * kWave, kThreads), kThreads, 0, s>>>(
+                R, static_cast<int32_t>(h->num_tiles), h->jds_depth, a.jds_tiles, a.jds_len,
+                a.jds_iter_ptr, a.jds_perm, a.jds_col, a.jds_val, x, y);
+            e = hipGetLastError();
+        }
+        break;
+    case SPMV_CSR_MERGE:
+        k_merge<<<static_cast<unsigned>(h->num_tiles), kMergeThreads, 0, s>>>(
+            R, nnz, a.merge_row_start, a.row_ptrs, a.col_idx, a.values, x, y);
+        e = hipGetLastError();
+        break;
+    default:
+        return SPMV_ERR_INVALID_ARG;
+    }
+    return e == hipSuccess ? SPMV_OK : from_hip(e);
+}
+
+}  // namespace spmv

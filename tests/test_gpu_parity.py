@@ -1,0 +1,440 @@
+"""GPU parity: every builder and kernel of the HIP library against the CPU oracle.
+
+Index arrays and moved values must match the oracle bit for bit; y must meet
+the row bound |y_gpu - y_ref| <= 1e-5 * (|y| + sum |a*x|) on every row.
+All calls go through the C ABI (the ctypes binding in spmv_storage_formats_amd).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from spmv_storage_formats_amd import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import spmv_storage_formats_amd as spmv  # noqa: E402
+
+ALL_FORMATS = ["coo_atomic", "coo_segmented", "csr_scalar", "csr_vector", "ell", "hyb", "jds",
+               "csr_merge"]
+# formats whose rows are each summed by one lane group with a plain y update
+DETERMINISTIC = ["csr_scalar", "csr_vector", "ell"]
+
+_cache = {}
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    spmv.load_library()
+    return torch.device("cuda:0")
+
+
+def W(name):
+    if name not in _cache:
+        _cache[name] = synth.workload(name)
+    return _cache[name]
+
+
+def ref(name):
+    key = ("ref", name)
+    if key not in _cache:
+        w = W(name)
+        _cache[key] = oracle.spmv_csr(w.row_ptrs, w.col_idx, w.values, w.x, w.y)
+    return _cache[key]
+
+
+def to_dev(w, dev):
+    return (torch.from_numpy(w.row_ptrs).to(dev), torch.from_numpy(w.col_idx).to(dev),
+            torch.from_numpy(w.values).to(dev), torch.from_numpy(w.x).to(dev),
+            torch.from_numpy(w.y).to(dev))
+
+
+def run_once(h, x, y0):
+    y = y0.clone()
+    h.run(x, y)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def assert_rows(y_gpu, y_ref, bound, what):
+    n, first, worst = oracle.check(y_gpu, y_ref, bound)
+    assert n == 0, (f"{what}: {n} rows out of bound, first row {first}: gpu {y_gpu[first]!r} "
+                    f"ref {y_ref[first]!r} bound {bound[first]!r}")
+    return worst
+
+
+def bits(a):
+    return np.ascontiguousarray(a).view(np.uint32)
+
+
+def build(fmt, w, dev, **kw):
+    rp, ci, v, _, _ = to_dev(w, dev)
+    return spmv.build(fmt, rp, ci, v, w.num_cols, **kw)
+
+
+# --------------------------------------------------------------- worked example
+
+@pytest.mark.parametrize("fmt", ALL_FORMATS)
+def test_fig14_1_every_format(dev, fmt):
+    w = synth.fig14_1()
+    rp, ci, v, x, _ = to_dev(w, dev)
+    h = spmv.build(fmt, rp, ci, v, 4)
+    y = torch.zeros(4, device=dev)
+    h.run(x, y)
+    assert y.cpu().tolist() == [15, 50, 28, 24]
+    y = torch.ones(4, device=dev)
+    h.run(x, y)
+    assert y.cpu().tolist() == [16, 51, 29, 25]
+
+
+def test_fig14_1_printed_arrays(dev):
+    """Device builders reproduce the printed ELL and JDS arrays of Fig. 14.1."""
+    w = synth.fig14_1()
+    h = build("ell", w, dev)
+    assert h.info["ell_width"] == 3
+    assert h.array("ell_val").tolist() == [1, 5, 2, 6, 7, 3, 8, 0, 0, 9, 0, 0]
+    assert h.array("ell_col").tolist() == [0, 0, 1, 3, 1, 2, 2, 0, 0, 3, 0, 0]
+    assert h.array("ell_nnz").tolist() == [2, 3, 2, 1]
+    h = build("jds", w, dev)
+    assert h.array("jds_perm").tolist() == [1, 0, 2, 3]
+    assert h.array("jds_iter_ptr").tolist() == [0, 4, 7, 8]
+    assert h.array("jds_val").tolist() == [5, 1, 2, 6, 3, 7, 8, 9]
+    h = build("hyb", w, dev, hyb_width=2)
+    assert h.array("tail_row").tolist() == [1] and h.array("tail_val").tolist() == [9]
+    assert build("auto", w, dev).format == "ell"
+
+
+# -------------------------------------------------------------- builder parity
+
+def check_builder(h, w, K=None):
+    fmt = h.format
+    if fmt in ("csr_scalar", "csr_vector", "csr_merge"):
+        assert np.array_equal(h.array("row_ptrs"), w.row_ptrs)
+        assert np.array_equal(h.array("col_idx"), w.col_idx)
+        assert np.array_equal(bits(h.array("values")), bits(w.values))
+    elif fmt in ("coo_atomic", "coo_segmented"):
+        assert np.array_equal(h.array("row_idx"), oracle.csr_to_coo(w.row_ptrs))
+        assert np.array_equal(h.array("col_idx"), w.col_idx)
+        assert np.array_equal(bits(h.array("values")), bits(w.values))
+    elif fmt == "ell":
+        e = oracle.csr_to_ell(w.row_ptrs, w.col_idx, w.values)
+        assert h.info["ell_width"] == e["width"]
+        assert np.array_equal(h.array("ell_col"), e["col"])
+        assert np.array_equal(bits(h.array("ell_val")), bits(e["val"]))
+        assert np.array_equal(h.array("ell_nnz"), e["nnz"])
+    elif fmt == "hyb":
+        o = oracle.csr_to_hyb(w.row_ptrs, w.col_idx, w.values, h.info["hyb_width"])
+        assert h.info["ell_width"] == o["width"]
+        assert np.array_equal(h.array("ell_col"), o["ell_col"])
+        assert np.array_equal(bits(h.array("ell_val")), bits(o["ell_val"]))
+        assert np.array_equal(h.array("ell_nnz"), o["ell_nnz"])
+        assert h.info["tail_nnz"] == o["tail_row"].size
+        assert np.array_equal(h.array("tail_row"), o["tail_row"])
+        assert np.array_equal(h.array("tail_col"), o["tail_col"])
+        assert np.array_equal(bits(h.array("tail_val")), bits(o["tail_val"]))
+    elif fmt == "jds":
+        o = oracle.csr_to_jds(w.row_ptrs, w.col_idx, w.values)
+        assert np.array_equal(h.array("jds_perm"), o["perm"])
+        assert np.array_equal(h.array("jds_len"), o["len"])
+        assert np.array_equal(h.array("jds_iter_ptr"), o["iter_ptr"])
+        assert np.array_equal(h.array("jds_col"), o["col"])
+        assert np.array_equal(bits(h.array("jds_val")), bits(o["val"]))
+    st = oracle.row_stats(w.row_ptrs)
+    assert np.array_equal(h.array("len_hist"), st["hist"])
+    assert (h.info["max_len"], h.info["sum_len_sq"], h.info["empty_rows"]) == \
+        (st["W"], st["sum_len_sq"], st["empty_rows"])
+
+
+REDUCED = ["c1s", "c2s", "c3s", "c4s", "c5s"]
+
+
+@pytest.mark.parametrize("name", REDUCED)
+@pytest.mark.parametrize("fmt", ALL_FORMATS)
+def test_reduced_builders_and_spmv(dev, name, fmt):
+    w = W(name)
+    slots = w.num_rows * oracle.row_stats(w.row_ptrs)["W"]
+    print(f"[case] {name} {fmt} R={w.num_rows} nnz={w.nnz}", flush=True)
+    if fmt == "ell" and slots > 2**31 - 1:
+        with pytest.raises(spmv.SpmvError) as ei:
+            build(fmt, w, dev)
+        assert ei.value.name == "SPMV_ERR_TOO_LARGE"
+        return
+    if fmt == "ell" and slots > 64_000_000:
+        pytest.skip("ELL of this skewed shape is >99% padding (multi-GB); covered at full size")
+    h = build(fmt, w, dev)
+    assert h.format == fmt
+    check_builder(h, w)
+    _, _, _, x, y0 = to_dev(w, dev)
+    y_ref, bound = ref(name)
+    assert_rows(run_once(h, x, y0), y_ref, bound, f"{name}/{fmt}")
+
+
+@pytest.mark.parametrize("K", [0, 1, 2, 5, 13, 20, 64, 100000])
+def test_hyb_widths(dev, K):
+    w = W("c4s")
+    h = build("hyb", w, dev, hyb_width=K)
+    check_builder(h, w)
+    _, _, _, x, y0 = to_dev(w, dev)
+    assert_rows(run_once(h, x, y0), *ref("c4s"), f"hyb K={K}")
+
+
+@pytest.mark.parametrize("lanes", [1, 2, 4, 8, 16, 32, 64])
+@pytest.mark.parametrize("name", ["c2s", "c4s", "c5s"])
+def test_csr_vector_lanes(dev, lanes, name):
+    w = W(name)
+    h = build("csr_vector", w, dev, lanes=lanes)
+    assert h.info["lanes_per_row"] == lanes
+    _, _, _, x, y0 = to_dev(w, dev)
+    assert_rows(run_once(h, x, y0), *ref(name), f"{name} lanes={lanes}")
+
+
+@pytest.mark.parametrize("depth", [1, 3, 64, 128, 1000])
+def test_jds_depths(dev, depth):
+    w = W("c5s")
+    h = build("jds", w, dev, jds_depth=depth)
+    _, _, _, x, y0 = to_dev(w, dev)
+    assert_rows(run_once(h, x, y0), *ref("c5s"), f"jds depth={depth}")
+
+
+@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("fmt", ALL_FORMATS)
+def test_small_irregular(dev, seed, fmt):
+    """Tiny matrices with empty rows, duplicate and unsorted columns, R != C."""
+    rng = np.random.default_rng(100 + seed)
+    R, C = int(rng.integers(1, 300)), int(rng.integers(1, 300))
+    w = synth.small_random(rng, R, C, max_len=int(rng.integers(1, 40)))
+    h = build(fmt, w, dev)
+    check_builder(h, w)
+    y_ref, bound = oracle.spmv_csr(w.row_ptrs, w.col_idx, w.values, w.x, w.y)
+    _, _, _, x, y0 = to_dev(w, dev)
+    assert_rows(run_once(h, x, y0), y_ref, bound, f"small seed={seed} {fmt}")
+
+
+# ----------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("fmt", ALL_FORMATS)
+def test_empty_matrices(dev, fmt):
+    for R, C in ((0, 0), (0, 5), (7, 3)):
+        rp = torch.zeros(R + 1, dtype=torch.int32, device=dev)
+        e = torch.zeros(0, dtype=torch.int32, device=dev)
+        h = spmv.build(fmt, rp, e, torch.zeros(0, device=dev), C)
+        y = torch.arange(R, dtype=torch.float32, device=dev)
+        h.run(torch.ones(C, device=dev), y)
+        assert y.cpu().tolist() == list(range(R))
+
+
+@pytest.mark.parametrize("fmt", ALL_FORMATS)
+def test_one_huge_row(dev, fmt):
+    """One 200k-long row among empty and short rows: the merge path spans
+    ~100 blocks, JDS splits the row over many tiles."""
+    rng = np.random.default_rng(5)
+    R, C = 20000, 300_000          # R * 200000 > 2^31: ELL must be refused
+    lens = rng.integers(0, 4, size=R)
+    lens[1234] = 200_000
+    rp = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    ci = np.concatenate([np.sort(rng.choice(C, l, replace=False)) if l else np.zeros(0, np.int64)
+                         for l in lens]).astype(np.int32)
+    w = synth.Workload("huge_row", R, C, rp, ci, rng.uniform(-1, 1, ci.size).astype(np.float32),
+                       rng.uniform(-1, 1, C).astype(np.float32),
+                       rng.uniform(-1, 1, R).astype(np.float32))
+    if fmt == "ell" and R * 200_000 > 2**31 - 1:
+        with pytest.raises(spmv.SpmvError) as ei:
+            build(fmt, w, dev)
+        assert ei.value.name == "SPMV_ERR_TOO_LARGE"
+        return
+    h = build(fmt, w, dev)
+    check_builder(h, w)
+    y_ref, bound = oracle.spmv_csr(w.row_ptrs, w.col_idx, w.values, w.x, w.y)
+    _, _, _, x, y0 = to_dev(w, dev)
+    assert_rows(run_once(h, x, y0), y_ref, bound, f"huge row {fmt}")
+
+
+@pytest.mark.parametrize("fmt", ALL_FORMATS)
+def test_closed_forms(dev, fmt):
+    """5-point Laplacian, x = 1, y = 0: 0 inside, 1 on edges, 2 at corners --
+    exact in fp32 in any summation order; x = 0 leaves y bit-identical."""
+    w = W("c1s")
+    n = 61
+    h = build(fmt, w, dev)
+    y = torch.zeros(n * n, device=dev)
+    h.run(torch.ones(n * n, device=dev), y)
+    g = y.cpu().numpy().reshape(n, n)
+    expect = np.zeros((n, n), np.float32)
+    expect[0] += 1; expect[-1] += 1; expect[:, 0] += 1; expect[:, -1] += 1
+    assert np.array_equal(g, expect)
+    y0 = torch.from_numpy(w.y).to(dev)
+    y = y0.clone()
+    h.run(torch.zeros(n * n, device=dev), y)
+    assert np.array_equal(bits(y.cpu().numpy()), bits(w.y))
+
+
+@pytest.mark.parametrize("fmt", DETERMINISTIC)
+def test_repeat_runs_bit_identical(dev, fmt):
+    """Kernels without atomics give the same bits on every run (no races)."""
+    w = W("c3s")
+    h = build(fmt, w, dev)
+    _, _, _, x, y0 = to_dev(w, dev)
+    a = run_once(h, x, y0)
+    for _ in range(3):
+        assert np.array_equal(bits(run_once(h, x, y0)), bits(a))
+
+
+def test_non_default_stream(dev):
+    w = W("c2s")
+    h = build("ell", w, dev)
+    _, _, _, x, y0 = to_dev(w, dev)
+    s = torch.cuda.Stream()
+    y = y0.clone()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        h.run(x, y)
+    s.synchronize()
+    assert_rows(y.cpu().numpy(), *ref("c2s"), "side stream")
+
+
+# ----------------------------------------------------------- analyze / validate
+
+@pytest.mark.parametrize("name", ["fig14_1", "c1s", "c4s", "c5s"])
+def test_analyze_matches_oracle(dev, name):
+    w = synth.fig14_1() if name == "fig14_1" else W(name)
+    rp, ci, _, _, _ = to_dev(w, dev)
+    got = spmv.analyze(rp, ci, w.num_cols)
+    st = oracle.row_stats(w.row_ptrs)
+    assert (got["max_len"], got["nnz"], got["sum_len_sq"], got["empty_rows"]) == \
+        (st["W"], st["nnz"], st["sum_len_sq"], st["empty_rows"])
+    assert np.array_equal(got["hist"], st["hist"])
+
+
+def _bad_inputs():
+    w = synth.fig14_1()
+    rp, ci = w.row_ptrs, w.col_idx
+    cases = []
+    b = rp.copy(); b[2] = 1; cases.append(("decreasing", b, ci, 4))
+    b = rp.copy(); b[0] = 1; cases.append(("start", b, ci, 4))
+    b = rp.copy(); b[4] = 7; cases.append(("end", b, ci[:7].copy(), 4))
+    cases.append(("nnz mismatch", rp.copy(), ci[:7].copy(), 4))
+    b = ci.copy(); b[3] = 4; cases.append(("col high", rp.copy(), b, 4))
+    b = ci.copy(); b[0] = -1; cases.append(("col negative", rp.copy(), b, 4))
+    cases.append(("too few columns", rp.copy(), ci.copy(), 3))
+    return cases
+
+
+@pytest.mark.parametrize("case", range(7))
+def test_validation_codes_match_oracle(dev, case):
+    name, rp, ci, C = _bad_inputs()[case]
+    expect = oracle.validate_csr(4, C, rp, ci)
+    assert expect != oracle.OK
+    vals = torch.ones(ci.size, device=dev)
+    with pytest.raises(spmv.SpmvError) as ei:
+        spmv.build("auto", torch.from_numpy(rp).to(dev), torch.from_numpy(ci).to(dev), vals, C)
+    assert ei.value.status == expect, name
+
+
+def test_validate_off_skips_column_pass(dev):
+    w = synth.fig14_1()
+    ci = w.col_idx.copy()
+    ci[3] = 9  # out of range, not checked when validate=False (caller's promise)
+    a = spmv.analyze(torch.from_numpy(w.row_ptrs).to(dev), torch.from_numpy(ci).to(dev), 4,
+                     validate=False)
+    assert a["max_len"] == 3
+
+
+def test_too_large_and_budget(dev):
+    w = W("c4s")
+    R, Wd = w.num_rows, oracle.row_stats(w.row_ptrs)["W"]
+    assert R * Wd < 2**31  # reduced skewed fits; the budget refuses it
+    with pytest.raises(spmv.SpmvError) as ei:
+        build("ell", w, dev, max_bytes=1 << 20)
+    assert ei.value.name == "SPMV_ERR_TOO_LARGE"
+    h = build("hyb", w, dev, max_bytes=1 << 30)
+    assert h.info["device_bytes"] <= 1 << 30
+
+
+# ------------------------------------------------------------------ COO input
+
+def _coo_of(w, rng, shuffle):
+    ri = oracle.csr_to_coo(w.row_ptrs)
+    p = rng.permutation(w.nnz) if shuffle else np.arange(w.nnz)
+    return ri[p].copy(), w.col_idx[p].copy(), w.values[p].copy()
+
+
+@pytest.mark.parametrize("name", ["fig14_1", "c2s", "c4s", "c5s"])
+@pytest.mark.parametrize("shuffle", [False, True])
+def test_coo_to_csr_bitexact(dev, name, shuffle):
+    w = synth.fig14_1() if name == "fig14_1" else W(name)
+    rng = np.random.default_rng(77)
+    ri, ci, v = _coo_of(w, rng, shuffle)
+    # duplicates: repeat a few entries (they stay, in input order)
+    if w.nnz > 10:
+        extra = rng.integers(0, w.nnz, 10)
+        ri = np.concatenate([ri, ri[extra]]); ci = np.concatenate([ci, ci[extra]])
+        v = np.concatenate([v, v[extra]])
+    rp_o, ci_o, v_o = oracle.coo_to_csr(w.num_rows, ri, ci, v)
+    t = lambda a: torch.from_numpy(a).to(dev)  # noqa: E731
+    rp_d, ci_d, v_d = spmv.coo_to_csr(t(ri), t(ci), t(v), w.num_rows, w.num_cols)
+    assert np.array_equal(rp_d.cpu().numpy(), rp_o)
+    assert np.array_equal(ci_d.cpu().numpy(), ci_o)
+    assert np.array_equal(bits(v_d.cpu().numpy()), bits(v_o))
+
+
+@pytest.mark.parametrize("fmt", ALL_FORMATS)
+def test_build_coo_spmv(dev, fmt):
+    w = W("c4s")
+    rng = np.random.default_rng(3)
+    ri, ci, v = _coo_of(w, rng, True)
+    t = lambda a: torch.from_numpy(a).to(dev)  # noqa: E731
+    if fmt == "ell":
+        w = W("c2s")
+        ri, ci, v = _coo_of(w, rng, True)
+    h = spmv.build_coo(fmt, t(ri), t(ci), t(v), w.num_rows, w.num_cols)
+    y_ref, bound = oracle.spmv_coo(w.num_rows, ri, ci, v, w.x, w.y)
+    assert_rows(run_once(h, t(w.x), t(w.y)), y_ref, bound, f"coo input {fmt}")
+
+
+def test_coo_bad_row_index(dev):
+    t = lambda a: torch.from_numpy(np.asarray(a, np.int32)).to(dev)  # noqa: E731
+    for ri, ci, code in (([0, 4], [0, 0], 4), ([0, -1], [0, 0], 4), ([0, 1], [0, 9], 3)):
+        assert oracle.validate_coo(4, 4, ri, ci) == code
+        with pytest.raises(spmv.SpmvError) as ei:
+            spmv.coo_to_csr(t(ri), t(ci), torch.ones(2, device=dev), 4, 4)
+        assert ei.value.status == code
+
+
+# ------------------------------------------------------ full-size workloads
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+@pytest.mark.parametrize("fmt", ALL_FORMATS + ["auto"])
+def test_full_size_parity(dev, name, fmt):
+    """Full-size workloads, every format, every row against the oracle.
+    ELL is refused where R * W overflows int32 slots (skewed, power law)."""
+    w = W(name)
+    Wd = int(np.diff(w.row_ptrs).max())
+    print(f"[case] full {name} {fmt} R={w.num_rows} nnz={w.nnz} W={Wd}", flush=True)
+    if fmt == "ell" and w.num_rows * Wd > 2**31 - 1:
+        with pytest.raises(spmv.SpmvError) as ei:
+            build(fmt, w, dev)
+        assert ei.value.name == "SPMV_ERR_TOO_LARGE"
+        return
+    kw = {"hyb_width": 20} if (fmt == "hyb" and name == "c4") else {}
+    h = build(fmt, w, dev, **kw)
+    if fmt == "auto":
+        assert h.format == {"c1": "ell", "c2": "ell", "c3": "ell", "c4": "hyb",
+                            "c5": "csr_merge"}[name]
+        if name == "c4":
+            assert h.info["hyb_width"] == 20
+    _, _, _, x, y0 = to_dev(w, dev)
+    y_ref, bound = ref(name)
+    assert_rows(run_once(h, x, y0), y_ref, bound, f"full {name}/{fmt}")
+
+
+@pytest.mark.parametrize("name,fmt", [("c1", "ell"), ("c2", "ell"), ("c3", "ell"),
+                                      ("c4", "hyb"), ("c4", "jds"), ("c5", "jds"),
+                                      ("c5", "coo_segmented")])
+def test_full_size_builders_bitexact(dev, name, fmt):
+    w = W(name)
+    print(f"[case] full builder {name} {fmt}", flush=True)
+    kw = {"hyb_width": 20} if fmt == "hyb" else {}
+    h = build(fmt, w, dev, **kw)
+    check_builder(h, w)

@@ -100,6 +100,9 @@ def main():
     ap.add_argument("--only-selected", action="store_true",
                     help="time only the selected format (for profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 512 MiB device copy 5 times (reads 512 MiB, writes "
+                         "512 MiB per launch) to scale PMC byte counters")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -184,14 +187,7 @@ def main():
             log(f"{fmt}: {per_format[fmt]}")
             hf.close()
 
-    traffic = None
-    prof = os.path.join(ROOT, "profiles", "traffic.json")
-    if os.path.exists(prof):
-        with open(prof) as f:
-            tr = json.load(f)
-        key = f"{args.config}/{selected}"
-        if key in tr and tr[key].get("kernel_source_sha") == kernel_source_sha():
-            traffic = tr[key]["hbm_bytes_per_launch"]
+    traffic = measured_traffic(f"{args.config}/{selected}")
 
     result = {
         "metric": "SpMV GFLOP/s and effective HBM GB/s (% of MI355X peak) per format, 1 GPU",
@@ -219,10 +215,37 @@ def main():
                      "traffic": traffic, "bytes_per_launch_alg": B},
         "formats": per_format,
     }
+    if args.calibrate_copy:
+        n = 512 << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            flush_buf.zero_()
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = {"read": n, "write": n}
     if not args.no_cpu:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def measured_traffic(key):
+    """HBM bytes per launch from the committed PMC summary, or None when the
+    summary has no entry for `key` or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    start = text.find("```json")
+    if start < 0:
+        return None
+    end = text.find("```", start + 7)
+    table = json.loads(text[start + 7:end])
+    entry = table.get(key)
+    if entry and entry.get("kernel_source_sha") == kernel_source_sha():
+        return entry["hbm_bytes_per_launch"]
+    return None
 
 
 def kernel_source_sha():

@@ -74,6 +74,11 @@ __global__ __launch_bounds__(kThreads) void k_coo_segmented(int32_t nnz,
             const float pu = __shfl_up(p, off);
             if (lane >= off && ru == r) p += pu;
         }
+        // The carried run either continues into this batch (same row as lane
+        // 0) or ended exactly at the previous batch's last entry: flush it.
+        const int32_t r_first = __builtin_amdgcn_readfirstlane(r);
+        if (carry_row != INT32_MAX && carry_row != r_first && lane == 0)
+            atomic_add_f32(&y[carry_row], carry);
         if (r == carry_row) p += carry;
         const int32_t rn = __shfl_down(r, 1);
         if (valid && lane != kWave - 1 && rn != r) atomic_add_f32(&y[r], p);

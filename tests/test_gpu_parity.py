@@ -313,7 +313,7 @@ def _bad_inputs():
     cases = []
     b = rp.copy(); b[2] = 1; cases.append(("decreasing", b, ci, 4))
     b = rp.copy(); b[0] = 1; cases.append(("start", b, ci, 4))
-    b = rp.copy(); b[4] = 7; cases.append(("end", b, ci[:7].copy(), 4))
+    b = rp.copy(); b[4] = 9; cases.append(("end beyond nnz", b, ci.copy(), 4))
     cases.append(("nnz mismatch", rp.copy(), ci[:7].copy(), 4))
     b = ci.copy(); b[3] = 4; cases.append(("col high", rp.copy(), b, 4))
     b = ci.copy(); b[0] = -1; cases.append(("col negative", rp.copy(), b, 4))

@@ -100,6 +100,8 @@ def main():
     ap.add_argument("--only-selected", action="store_true",
                     help="time only the selected format (for profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--col-blocks", type=int, default=0,
+                    help="x slices for every build (0 = library default)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 512 MiB device copy 5 times (reads 512 MiB, writes "
                          "512 MiB per launch) to scale PMC byte counters")
@@ -137,6 +139,8 @@ def main():
     y_ref, bound = oracle.spmv_csr(w.row_ptrs, w.col_idx, w.values, w.x, w.y)
 
     kw = {"hyb_width": 20} if args.config == "c4" else {}
+    if args.col_blocks:
+        kw["col_blocks"] = args.col_blocks
 
     def build_and_check(fmt):
         torch.cuda.synchronize()
@@ -182,6 +186,7 @@ def main():
                 "frac_hbm": round(B / (mf * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "build_ms": round(bms, 2),
                 "device_MB": round(hf.info["device_bytes"] / 1e6, 1),
+                "col_blocks": hf.info["col_blocks"],
                 "worst_err_over_bound": float(f"{wst:.3g}"),
             }
             log(f"{fmt}: {per_format[fmt]}")
@@ -203,6 +208,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic (seeded), inputs resident in HBM, caches flushed before each step",
         "config": {"workload": WORKLOAD_NAMES[args.config], "format": selected,
+                   "col_blocks": h.info["col_blocks"],
                    "rows": R, "cols": C, "nnz": nnz, "parallelism": "single GPU"},
         "effective_gbs": round(gbs, 1),
         "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),

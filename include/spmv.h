@@ -89,11 +89,17 @@ typedef struct spmv_opts {
     int32_t validate;       /* nonzero: also check every column index (one pass over
                                colIdx).  Row pointers are always checked.                  */
     int32_t jds_depth;      /* JDS: depth of one tile (jagged columns per wave).  0: 128.  */
+    int32_t col_blocks;     /* x slices (column blocks), each run as its own pass over y.
+                               0: automatic for SPMV_AUTO builds (slices of at most 4 MiB
+                               of x when x exceeds the 4 MiB L2 of one XCD and the rows'
+                               columns are scattered; otherwise 1).  1: never split.
+                               K > 1: exactly K slices, any format.                        */
+    int32_t reserved;       /* must be 0                                                   */
     int64_t max_bytes;      /* > 0: refuse (SPMV_ERR_TOO_LARGE) a format whose device
                                arrays would exceed this many bytes.                        */
 } spmv_opts;
 
-/* Fills the defaults: hyb_width 0, lanes 0, validate 1, jds_depth 0, max_bytes 0. */
+/* Fills the defaults: every field 0 except validate = 1. */
 void spmv_opts_default(spmv_opts *opts);
 
 /* Row-length statistics [CHOICE 4.1 histogram/variance, 4.3 mean and max;
@@ -105,6 +111,8 @@ typedef struct spmv_stats {
     int64_t max_len;     /* W = longest row                         */
     int64_t sum_len_sq;  /* sum over rows of len^2 (variance = E[len^2] - mean^2) */
     int64_t empty_rows;
+    int64_t col_spread;  /* mean over non-empty rows of |first column - r*C/R|: how far a
+                            row's columns sit from its diagonal (small for banded matrices) */
 } spmv_stats;
 
 /* What a handle holds (spmv_get_info). */
@@ -113,6 +121,8 @@ typedef struct spmv_info {
     int32_t hyb_width;     /* K used by HYB, else 0                       */
     int32_t lanes_per_row; /* lanes used by CSR vector, else 0            */
     int32_t ell_width;     /* width of the ELL arrays (ELL: W; HYB: min(K, W)) */
+    int32_t col_blocks;    /* x slices the handle runs (1 = unsplit)      */
+    int32_t slice_cols;    /* columns per x slice (num_cols if unsplit)   */
     spmv_stats stats;
     int64_t tail_nnz;      /* HYB: entries in the COO tail                */
     int64_t num_tiles;     /* JDS: wave tiles; CSR merge: blocks          */
@@ -148,7 +158,8 @@ typedef struct spmv_handle spmv_handle;
  *   rowPtrs[0] = 0, rowPtrs non-decreasing, rowPtrs[R] = nnz
  *   (-> SPMV_ERR_BAD_ROWPTRS), and, if `validate`, 0 <= colIdx < C
  *   (-> SPMV_ERR_BAD_COLIDX).  Row pointers are checked first.
- *   row_ptrs_dev: int32[R+1]; col_idx_dev: int32[nnz] (may be NULL if nnz = 0).
+ *   row_ptrs_dev: int32[R+1]; col_idx_dev: int32[nnz] (may be NULL only if nnz = 0;
+ *   the first column of each row is read even when `validate` is 0).
  *   stats_host: filled on success.  hist_host (nullable): int64 buffer of
  *   hist_cap entries; on success entries 0..min(hist_cap, W+1)-1 receive the
  *   number of rows of each length.
@@ -233,7 +244,8 @@ spmv_status spmv_run(const spmv_handle *h, const float *x_dev, float *y_dev, voi
 
 spmv_status spmv_get_info(const spmv_handle *h, spmv_info *info_host);
 
-/* Size in bytes of an exportable array (0 if the handle's format has none). */
+/* Size in bytes of an exportable array (0 if the handle's format has none;
+ * a handle split into x slices exports only SPMV_A_LEN_HIST). */
 spmv_status spmv_array_bytes(const spmv_handle *h, spmv_array which, size_t *bytes);
 
 /* Copy an array of the handle to host memory (synchronous).  `bytes` must

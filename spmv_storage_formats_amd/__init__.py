@@ -56,18 +56,21 @@ class SpmvError(RuntimeError):
 class _Opts(ctypes.Structure):
     _fields_ = [("hyb_width", ctypes.c_int32), ("lanes_per_row", ctypes.c_int32),
                 ("validate", ctypes.c_int32), ("jds_depth", ctypes.c_int32),
+                ("col_blocks", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("max_bytes", ctypes.c_int64)]
 
 
 class _Stats(ctypes.Structure):
     _fields_ = [("num_rows", ctypes.c_int64), ("num_cols", ctypes.c_int64),
                 ("nnz", ctypes.c_int64), ("max_len", ctypes.c_int64),
-                ("sum_len_sq", ctypes.c_int64), ("empty_rows", ctypes.c_int64)]
+                ("sum_len_sq", ctypes.c_int64), ("empty_rows", ctypes.c_int64),
+                ("col_spread", ctypes.c_int64)]
 
 
 class _Info(ctypes.Structure):
     _fields_ = [("format", ctypes.c_int32), ("hyb_width", ctypes.c_int32),
                 ("lanes_per_row", ctypes.c_int32), ("ell_width", ctypes.c_int32),
+                ("col_blocks", ctypes.c_int32), ("slice_cols", ctypes.c_int32),
                 ("stats", _Stats), ("tail_nnz", ctypes.c_int64), ("num_tiles", ctypes.c_int64),
                 ("device_bytes", ctypes.c_int64)]
 
@@ -141,9 +144,9 @@ def _check(st: int, what: str):
         raise SpmvError(st, what)
 
 
-def _opts(hyb_width=0, lanes=0, validate=True, jds_depth=0, max_bytes=0) -> _Opts:
+def _opts(hyb_width=0, lanes=0, validate=True, jds_depth=0, max_bytes=0, col_blocks=0) -> _Opts:
     return _Opts(int(hyb_width), int(lanes), 1 if validate else 0, int(jds_depth),
-                 int(max_bytes))
+                 int(col_blocks), 0, int(max_bytes))
 
 
 def _fmt(fmt) -> int:
@@ -224,6 +227,7 @@ class Handle:
         _check(lib.spmv_get_info(self._ptr, ctypes.byref(info)), "spmv_get_info")
         self.info = {"format": FORMAT_NAMES[info.format], "hyb_width": info.hyb_width,
                      "lanes_per_row": info.lanes_per_row, "ell_width": info.ell_width,
+                     "col_blocks": info.col_blocks, "slice_cols": info.slice_cols,
                      "tail_nnz": info.tail_nnz, "num_tiles": info.num_tiles,
                      "device_bytes": info.device_bytes, **_stats_dict(info.stats)}
 
@@ -297,7 +301,8 @@ class Handle:
 
 
 def build(fmt, row_ptrs, col_idx, values, num_cols: int, *, hyb_width: int = 0, lanes: int = 0,
-          validate: bool = True, jds_depth: int = 0, max_bytes: int = 0, stream=None) -> Handle:
+          validate: bool = True, jds_depth: int = 0, max_bytes: int = 0, col_blocks: int = 0,
+          stream=None) -> Handle:
     """Build a handle in `fmt` ("auto" = selector) from CSR cuda tensors."""
     import torch
     lib = load_library()
@@ -307,7 +312,7 @@ def build(fmt, row_ptrs, col_idx, values, num_cols: int, *, hyb_width: int = 0, 
     ci = _dev(col_idx, torch.int32, "col_idx")
     va = _dev(values, torch.float32, "values", nnz)
     out = ctypes.c_void_p()
-    o = _opts(hyb_width, lanes, validate, jds_depth, max_bytes)
+    o = _opts(hyb_width, lanes, validate, jds_depth, max_bytes, col_blocks)
     _check(lib.spmv_build(ctypes.byref(out), _fmt(fmt), R, int(num_cols), nnz, rp, ci, va,
                           ctypes.byref(o), _stream(stream, row_ptrs.device)), "spmv_build")
     return Handle(out.value, row_ptrs.device)
@@ -315,7 +320,7 @@ def build(fmt, row_ptrs, col_idx, values, num_cols: int, *, hyb_width: int = 0, 
 
 def build_coo(fmt, row_idx, col_idx, values, num_rows: int, num_cols: int, *, hyb_width: int = 0,
               lanes: int = 0, validate: bool = True, jds_depth: int = 0, max_bytes: int = 0,
-              stream=None) -> Handle:
+              col_blocks: int = 0, stream=None) -> Handle:
     """Build a handle from COO cuda tensors (converted to CSR on the device)."""
     import torch
     lib = load_library()
@@ -324,7 +329,7 @@ def build_coo(fmt, row_idx, col_idx, values, num_rows: int, num_cols: int, *, hy
     ci = _dev(col_idx, torch.int32, "col_idx")
     va = _dev(values, torch.float32, "values", nnz)
     out = ctypes.c_void_p()
-    o = _opts(hyb_width, lanes, validate, jds_depth, max_bytes)
+    o = _opts(hyb_width, lanes, validate, jds_depth, max_bytes, col_blocks)
     _check(lib.spmv_build_coo(ctypes.byref(out), _fmt(fmt), int(num_rows), int(num_cols), nnz,
                               ri, ci, va, ctypes.byref(o), _stream(stream, col_idx.device)),
            "spmv_build_coo")

@@ -27,33 +27,52 @@ __device__ inline unsigned long long wave_sum(unsigned long long v) {
 
 // One lane per row: length, monotonicity, the two end conditions, and the
 // reductions W = max len, sum len^2, number of empty rows.
-__global__ __launch_bounds__(kThreads) void k_row_checks(int32_t R, int32_t nnz,
+//
+// Also sums, over non-empty rows, the distance between the row's first column
+// and its diagonal position r*C/R: small for banded matrices, about C/3 for
+// uniformly scattered columns (used to decide on x slices).  The column is
+// read only when the row's start lies inside [0, nnz).
+//
+// Grid-stride with one set of atomics per wave and a capped grid: the
+// accumulators are single addresses, so their atomics must stay few.
+__global__ __launch_bounds__(kThreads) void k_row_checks(int32_t R, int32_t C, int32_t nnz,
                                                          const int32_t *__restrict__ rp,
+                                                         const int32_t *__restrict__ col,
                                                          RowStatsDev *__restrict__ st) {
-    const int64_t r = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-    int bad = 0, len = 0;
-    unsigned long long sq = 0, empty = 0;
-    if (r < R) {
+    int bad = 0, wlen = 0;
+    unsigned long long sq = 0, empty = 0, dist = 0;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+    for (int64_t r = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; r < R;
+         r += stride) {
         const int a = rp[r], b = rp[r + 1];
-        len = b - a;
+        int len = b - a;
         if (len < 0) bad = 1;
         if (r == 0 && a != 0) bad = 1;
         if (r == R - 1 && b != nnz) bad = 1;
         if (len < 0) len = 0;
-        sq = static_cast<unsigned long long>(len) * static_cast<unsigned long long>(len);
-        empty = (len == 0);
-    } else if (r == 0) {  // R == 0: rowPtrs = [0] and nnz must be 0
+        wlen = max(wlen, len);
+        sq += static_cast<unsigned long long>(len) * static_cast<unsigned long long>(len);
+        empty += (len == 0);
+        if (len > 0 && a >= 0 && a < nnz) {
+            const int64_t diag = r * static_cast<int64_t>(C) / R;
+            const int64_t d = static_cast<int64_t>(col[a]) - diag;
+            dist += static_cast<unsigned long long>(d < 0 ? -d : d);
+        }
+    }
+    if (R == 0 && blockIdx.x == 0 && threadIdx.x == 0) {  // rowPtrs = [0], nnz must be 0
         if (rp[0] != 0 || nnz != 0) bad = 1;
     }
     const unsigned long long any_bad = __ballot(bad != 0);
-    const int wmax = wave_max(len);
+    const int wmax = wave_max(wlen);
     const unsigned long long wsq = wave_sum(sq);
     const unsigned long long wempty = wave_sum(empty);
+    const unsigned long long wdist = wave_sum(dist);
     if (__lane_id() == 0) {
         if (any_bad) atomicOr(&st->flags, kFlagBadRowPtrs);
         if (wmax > 0) atomicMax(&st->max_len, wmax);
         if (wsq) atomicAdd(&st->sum_len_sq, wsq);
         if (wempty) atomicAdd(&st->empty_rows, wempty);
+        if (wdist) atomicAdd(&st->sum_first_dist, wdist);
     }
 }
 
@@ -109,9 +128,11 @@ __global__ __launch_bounds__(kThreads) void k_len_hist(int32_t R, const int32_t 
 
 }  // namespace
 
-hipError_t launch_row_checks(int32_t R, int32_t nnz, const int32_t *rp, RowStatsDev *st,
-                             hipStream_t s) {
-    k_row_checks<<<grid_for(R > 0 ? R : 1, kThreads), kThreads, 0, s>>>(R, nnz, rp, st);
+hipError_t launch_row_checks(int32_t R, int32_t C, int32_t nnz, const int32_t *rp,
+                             const int32_t *col, RowStatsDev *st, hipStream_t s) {
+    unsigned g = grid_for(R > 0 ? R : 1, kThreads);
+    if (g > 1024) g = 1024;
+    k_row_checks<<<g, kThreads, 0, s>>>(R, C, nnz, rp, col, st);
     return hipGetLastError();
 }
 

@@ -37,6 +37,7 @@ constexpr int64_t kInt32Max = 2147483647LL;
 struct HandleDeleter {
     void operator()(spmv_handle *h) const {
         if (!h) return;
+        for (spmv_handle *p : h->parts) (*this)(p);
         for (void *p : h->owned) (void)hipFree(p);
         delete h;
     }
@@ -68,6 +69,13 @@ spmv_opts resolve_opts(const spmv_opts *o) {
 
 bool valid_lanes(int32_t l) { return l == 0 || (l >= 1 && l <= 64 && (l & (l - 1)) == 0); }
 
+bool valid_opts(const spmv_opts &o) {
+    return valid_lanes(o.lanes_per_row) && o.jds_depth >= 0 && o.max_bytes >= 0 &&
+           o.col_blocks >= 0 && o.col_blocks <= kMaxColBlocks && o.reserved == 0;
+}
+
+bool valid_format(int32_t f) { return f >= SPMV_AUTO && f <= SPMV_CSR_MERGE; }
+
 // ---------------------------------------------------------------- analysis
 struct Analysis {
     spmv_stats st{};
@@ -80,7 +88,7 @@ spmv_status analyze_csr(int32_t R, int32_t C, int32_t nnz, const int32_t *rp,
     RowStatsDev *d = nullptr;
     SPMV_TRY(scratch.alloc(&d, 1));
     SPMV_HIP(hipMemsetAsync(d, 0, sizeof(RowStatsDev), s));
-    SPMV_HIP(launch_row_checks(R, nnz, rp, d, s));
+    SPMV_HIP(launch_row_checks(R, C, nnz, rp, col, d, s));
     if (validate) SPMV_HIP(launch_col_checks(nnz, C, col, d, s));
     RowStatsDev h{};
     SPMV_HIP(hipMemcpyAsync(&h, d, sizeof(h), hipMemcpyDeviceToHost, s));
@@ -93,6 +101,9 @@ spmv_status analyze_csr(int32_t R, int32_t C, int32_t nnz, const int32_t *rp,
     out.st.max_len = h.max_len;
     out.st.sum_len_sq = static_cast<int64_t>(h.sum_len_sq);
     out.st.empty_rows = static_cast<int64_t>(h.empty_rows);
+    const int64_t nonempty = static_cast<int64_t>(R) - out.st.empty_rows;
+    out.st.col_spread =
+        nonempty > 0 ? static_cast<int64_t>(h.sum_first_dist / static_cast<uint64_t>(nonempty)) : 0;
     if (want_hist) {
         const int64_t bins = out.st.max_len + 1;
         out.hist.assign(static_cast<size_t>(bins), 0);
@@ -264,12 +275,88 @@ int64_t format_bytes(int32_t fmt, int64_t R, int64_t nnz, int64_t W, int64_t K,
     }
 }
 
+// Number of x slices.  Automatic only for SPMV_AUTO: when x is larger than
+// one XCD's L2 and the rows' columns are scattered (their first column lies
+// more than C/8 from the diagonal on average), gathers from the whole x miss
+// the L2 and go to the Infinity Cache; slices of kXSliceBytes keep every
+// pass's gathers L2-resident at the price of one extra y read+write per slice.
+int32_t choose_col_blocks(const spmv_stats &st, spmv_format fmt, const spmv_opts &o) {
+    const int64_t C = st.num_cols;
+    int64_t K = 1;
+    if (o.col_blocks > 0) {
+        K = o.col_blocks;
+    } else if (fmt == SPMV_AUTO && 4 * C > kL2Bytes && st.col_spread * 8 > C && st.nnz > 0) {
+        K = (4 * C + kXSliceBytes - 1) / kXSliceBytes;
+    }
+    K = std::min<int64_t>(K, kMaxColBlocks);
+    K = std::min<int64_t>(K, std::max<int64_t>(C, 1));
+    return static_cast<int32_t>(std::max<int64_t>(K, 1));
+}
+
+spmv_status build_csr_impl(spmv_handle **out, spmv_format fmt, int32_t R, int32_t C,
+                           int32_t nnz, const int32_t *rp, const int32_t *col,
+                           const float *val, const spmv_opts &o, hipStream_t s,
+                           Scratch &scratch);
+
+// A handle made of column slices: slice k holds the entries with column in
+// [k*slice, (k+1)*slice) in their original order (global column indices) and
+// is built as a matrix of its own (for SPMV_AUTO the selector runs on each
+// slice's statistics).  Running the handle runs the slices in stream order.
+spmv_status build_sliced(spmv_handle **out, spmv_format fmt, int32_t R, int32_t C, int32_t nnz,
+                         const int32_t *rp, const int32_t *col, const float *val,
+                         const spmv_opts &o, int32_t K, const Analysis &an, hipStream_t s,
+                         Scratch &scratch) {
+    HandlePtr h(new spmv_handle());
+    SPMV_HIP(hipGetDevice(&h->device));
+    h->stats = an.st;
+    h->hist = an.hist;
+    const int64_t slice = (static_cast<int64_t>(C) + K - 1) / K;
+    h->slice_cols = static_cast<int32_t>(slice);
+    h->col_blocks = static_cast<int32_t>((C + slice - 1) / slice);
+    spmv_opts po = o;
+    po.col_blocks = 1;
+    po.validate = 0;
+    int64_t best_nnz = -1;
+    for (int32_t b = 0; b < h->col_blocks; ++b) {
+        const int32_t lo = static_cast<int32_t>(b * slice);
+        const int32_t hi = static_cast<int32_t>(std::min<int64_t>(C, (b + 1) * slice));
+        int32_t *prp = nullptr;
+        SPMV_TRY(scratch.alloc(&prp, static_cast<size_t>(R) + 1));
+        SPMV_HIP(launch_slice_count(R, rp, col, lo, hi, prp, s));
+        SPMV_TRY(exclusive_scan(prp, prp, R, true, s, scratch));
+        int32_t pn = 0;
+        SPMV_HIP(hipMemcpyAsync(&pn, prp + R, sizeof(int32_t), hipMemcpyDeviceToHost, s));
+        SPMV_HIP(hipStreamSynchronize(s));
+        if (pn == 0) continue;
+        int32_t *pcol = nullptr;
+        float *pval = nullptr;
+        SPMV_TRY(scratch.alloc(&pcol, pn));
+        SPMV_TRY(scratch.alloc(&pval, pn));
+        SPMV_HIP(launch_slice_fill(R, rp, col, val, lo, hi, prp, pcol, pval, s));
+        spmv_handle *part = nullptr;
+        SPMV_TRY(build_csr_impl(&part, fmt, R, C, pn, prp, pcol, pval, po, s, scratch));
+        h->parts.push_back(part);
+        h->device_bytes += part->device_bytes;
+        if (pn > best_nnz) {
+            best_nnz = pn;
+            h->format = part->format;
+        }
+    }
+    if (h->parts.empty()) h->format = SPMV_ELL;
+    SPMV_HIP(hipStreamSynchronize(s));
+    *out = h.release();
+    return SPMV_OK;
+}
+
 spmv_status build_csr_impl(spmv_handle **out, spmv_format fmt, int32_t R, int32_t C,
                            int32_t nnz, const int32_t *rp, const int32_t *col,
                            const float *val, const spmv_opts &o, hipStream_t s,
                            Scratch &scratch) {
     Analysis an;
     SPMV_TRY(analyze_csr(R, C, nnz, rp, col, o.validate != 0, true, an, s, scratch));
+    const int32_t K_slices = choose_col_blocks(an.st, fmt, o);
+    if (K_slices > 1) return build_sliced(out, fmt, R, C, nnz, rp, col, val, o, K_slices, an, s,
+                                          scratch);
     int32_t f = fmt, K = 0, L = 0;
     if (f == SPMV_AUTO) {
         select_format(an.st, an.hist.data(), o, &f, &K, &L);
@@ -292,6 +379,7 @@ spmv_status build_csr_impl(spmv_handle **out, spmv_format fmt, int32_t R, int32_
     h->stats = an.st;
     h->hist = an.hist;
     h->jds_depth = o.jds_depth > 0 ? o.jds_depth : kJdsDepthDefault;
+    h->slice_cols = C;
     switch (f) {
     case SPMV_COO_ATOMIC:
     case SPMV_COO_SEGMENTED:
@@ -403,7 +491,7 @@ void spmv_opts_default(spmv_opts *o) {
 spmv_status spmv_analyze(int32_t R, int32_t C, int32_t nnz, const int32_t *rp,
                          const int32_t *col, int32_t validate, spmv_stats *st, int64_t *hist,
                          int64_t hist_cap, void *stream) {
-    if (bad_sizes(R, C, nnz) || !rp || !st || (nnz > 0 && validate && !col) ||
+    if (bad_sizes(R, C, nnz) || !rp || !st || (nnz > 0 && !col) ||
         (hist && hist_cap < 0))
         return SPMV_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -434,9 +522,8 @@ spmv_status spmv_build(spmv_handle **out, spmv_format fmt, int32_t R, int32_t C,
     if (!out) return SPMV_ERR_INVALID_ARG;
     *out = nullptr;
     const spmv_opts o = resolve_opts(opts);
-    if (bad_sizes(R, C, nnz) || !rp || (nnz > 0 && (!col || !val)) || fmt < SPMV_AUTO ||
-        fmt > SPMV_CSR_MERGE || !valid_lanes(o.lanes_per_row) || o.jds_depth < 0 ||
-        o.max_bytes < 0)
+    if (bad_sizes(R, C, nnz) || !rp || (nnz > 0 && (!col || !val)) || !valid_format(fmt) ||
+        !valid_opts(o))
         return SPMV_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
     Scratch scratch(s);
@@ -462,9 +549,8 @@ spmv_status spmv_build_coo(spmv_handle **out, spmv_format fmt, int32_t R, int32_
     if (!out) return SPMV_ERR_INVALID_ARG;
     *out = nullptr;
     const spmv_opts o = resolve_opts(opts);
-    if (bad_sizes(R, C, nnz) || (nnz > 0 && (!ri || !ci || !v)) || fmt < SPMV_AUTO ||
-        fmt > SPMV_CSR_MERGE || !valid_lanes(o.lanes_per_row) || o.jds_depth < 0 ||
-        o.max_bytes < 0)
+    if (bad_sizes(R, C, nnz) || (nnz > 0 && (!ri || !ci || !v)) || !valid_format(fmt) ||
+        !valid_opts(o))
         return SPMV_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
     Scratch scratch(s);
@@ -494,6 +580,8 @@ spmv_status spmv_get_info(const spmv_handle *h, spmv_info *info) {
     info->hyb_width = h->hyb_width;
     info->lanes_per_row = h->lanes;
     info->ell_width = h->ell_width;
+    info->col_blocks = h->col_blocks;
+    info->slice_cols = h->slice_cols;
     info->stats = h->stats;
     info->tail_nnz = h->tail_nnz;
     info->num_tiles = h->num_tiles;

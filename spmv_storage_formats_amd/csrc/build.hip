@@ -208,6 +208,45 @@ __global__ __launch_bounds__(kThreads) void k_jds_tiles(int32_t groups, int32_t 
     tiles[tile] = make_int2(static_cast<int>(g), static_cast<int>(tile - tile_off[g]));
 }
 
+// Column slice [lo, hi): one lane per row counts, then copies, the row's
+// entries whose column falls in the slice, keeping their order.  Each slice is
+// a matrix of its own (same rows, global column indices) run as one pass.
+__global__ __launch_bounds__(kThreads) void k_slice_count(int32_t R,
+                                                          const int32_t *__restrict__ rp,
+                                                          const int32_t *__restrict__ col,
+                                                          int32_t lo, int32_t hi,
+                                                          int32_t *__restrict__ counts) {
+    const int64_t r = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (r >= R) return;
+    int32_t n = 0;
+    for (int32_t i = rp[r]; i < rp[r + 1]; ++i) {
+        const int32_t c = col[i];
+        n += (c >= lo && c < hi);
+    }
+    counts[r] = n;
+}
+
+__global__ __launch_bounds__(kThreads) void k_slice_fill(int32_t R, const int32_t *__restrict__ rp,
+                                                         const int32_t *__restrict__ col,
+                                                         const uint32_t *__restrict__ val,
+                                                         int32_t lo, int32_t hi,
+                                                         const int32_t *__restrict__ rp_out,
+                                                         int32_t *__restrict__ col_out,
+                                                         uint32_t *__restrict__ val_out) {
+    const int64_t r = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (r >= R) return;
+    int32_t p = rp_out[r];
+    const int32_t end = rp_out[r + 1];
+    for (int32_t i = rp[r]; i < rp[r + 1] && p < end; ++i) {
+        const int32_t c = col[i];
+        if (c >= lo && c < hi) {
+            col_out[p] = c;
+            val_out[p] = val[i];
+            ++p;
+        }
+    }
+}
+
 // Merge path over rows (their end markers) and nonzeros: row r's end marker
 // sits at position rowPtrs[r+1] + r.  row_start[b] = number of rows whose end
 // marker lies before diagonal b * items_per_block.
@@ -331,6 +370,23 @@ hipError_t launch_jds_tiles(int32_t groups, int32_t ntiles, const int32_t *tile_
                             int2 *tiles, hipStream_t s) {
     if (ntiles <= 0) return hipSuccess;
     k_jds_tiles<<<grid_for(ntiles, kThreads), kThreads, 0, s>>>(groups, ntiles, tile_off, tiles);
+    return hipGetLastError();
+}
+
+hipError_t launch_slice_count(int32_t R, const int32_t *rp, const int32_t *col, int32_t lo,
+                              int32_t hi, int32_t *counts, hipStream_t s) {
+    if (R <= 0) return hipSuccess;
+    k_slice_count<<<grid_for(R, kThreads), kThreads, 0, s>>>(R, rp, col, lo, hi, counts);
+    return hipGetLastError();
+}
+
+hipError_t launch_slice_fill(int32_t R, const int32_t *rp, const int32_t *col, const float *val,
+                             int32_t lo, int32_t hi, const int32_t *rp_out, int32_t *col_out,
+                             float *val_out, hipStream_t s) {
+    if (R <= 0) return hipSuccess;
+    k_slice_fill<<<grid_for(R, kThreads), kThreads, 0, s>>>(
+        R, rp, col, reinterpret_cast<const uint32_t *>(val), lo, hi, rp_out, col_out,
+        reinterpret_cast<uint32_t *>(val_out));
     return hipGetLastError();
 }
 

@@ -16,6 +16,12 @@ namespace spmv {
 constexpr int kWave = 64;       // CDNA wavefront width
 constexpr int kNumXcd = 8;      // MI355X: 8 accelerator complex dies, 32 CUs each
 constexpr int kJdsDepthDefault = 128;
+// x slice for column splitting: the 4 MiB L2 of one XCD.  (Measured on
+// MI355X: 4 MiB slices beat 2 MiB ones once each slice pays its own pass over
+// the rows and y.)
+constexpr int64_t kXSliceBytes = 4 << 20;
+constexpr int64_t kL2Bytes = 4 << 20;
+constexpr int kMaxColBlocks = 64;
 
 // Merge-path CSR: 256 threads x 8 merge items (row ends + nonzeros) per block.
 constexpr int kMergeThreads = 256;
@@ -70,6 +76,11 @@ struct spmv_handle {
     int64_t device_bytes = 0;
     spmv::DevArrays a;
     std::vector<void *> owned;      // every device allocation of this handle
+    // x slices: when non-empty the handle runs parts[k] (the columns of slice k)
+    // in order and holds no arrays of its own.
+    std::vector<spmv_handle *> parts;
+    int32_t col_blocks = 1;
+    int32_t slice_cols = 0;
 };
 
 namespace spmv {
@@ -192,9 +203,10 @@ struct RowStatsDev {                 // device-side accumulators
     int max_len;
     unsigned long long sum_len_sq;
     unsigned long long empty_rows;
+    unsigned long long sum_first_dist;   // sum over non-empty rows of |col[rp[r]] - r*C/R|
 };
-hipError_t launch_row_checks(int32_t R, int32_t nnz, const int32_t *rp, RowStatsDev *st,
-                             hipStream_t s);
+hipError_t launch_row_checks(int32_t R, int32_t C, int32_t nnz, const int32_t *rp,
+                             const int32_t *col, RowStatsDev *st, hipStream_t s);
 hipError_t launch_col_checks(int32_t nnz, int32_t C, const int32_t *col, RowStatsDev *st,
                              hipStream_t s);
 hipError_t launch_coo_checks(int32_t nnz, int32_t R, int32_t C, const int32_t *row,
@@ -241,6 +253,13 @@ hipError_t launch_jds_chunks(int32_t R, int32_t depth, const int32_t *jds_len,
                              int32_t *chunks, hipStream_t s);
 hipError_t launch_jds_tiles(int32_t groups, int32_t ntiles, const int32_t *tile_off,
                             int2 *tiles, hipStream_t s);
+// Column slice [lo, hi) of a CSR matrix: per-row counts, then the entries in
+// their original order (row pointers come from an exclusive scan of counts).
+hipError_t launch_slice_count(int32_t R, const int32_t *rp, const int32_t *col, int32_t lo,
+                              int32_t hi, int32_t *counts, hipStream_t s);
+hipError_t launch_slice_fill(int32_t R, const int32_t *rp, const int32_t *col, const float *val,
+                             int32_t lo, int32_t hi, const int32_t *rp_out, int32_t *col_out,
+                             float *val_out, hipStream_t s);
 hipError_t launch_merge_partition(int32_t R, int32_t nnz, const int32_t *rp, int32_t nblocks,
                                   int32_t *row_start, hipStream_t s);
 

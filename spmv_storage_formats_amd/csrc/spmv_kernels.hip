@@ -167,6 +167,9 @@ __global__ __launch_bounds__(kThreads) void k_csr_vector(int32_t R, const int32_
 // lanes of a wave read one contiguous 256-byte run of values and of columns
 // [Regularized formats page, ELL section].  Slots past nnzPerRow[r] are
 // padding and contribute nothing (the padded loads are part of the stream).
+// The slots are walked U at a time with the next U slots' loads issued before
+// the current U gathers, so every wave keeps its HBM stream in flight while
+// it waits on x.
 // ---------------------------------------------------------------------------
 template <int U>
 __global__ __launch_bounds__(kThreads) void k_ell(int32_t R, int32_t W,
@@ -178,23 +181,40 @@ __global__ __launch_bounds__(kThreads) void k_ell(int32_t R, int32_t W,
     const uint32_t b = xcd_remap(blockIdx.x, gridDim.x);
     const uint32_t r = b * kThreads + threadIdx.x;
     if (r >= static_cast<uint32_t>(R)) return;
+    const uint32_t ru = static_cast<uint32_t>(R);
     const int32_t n = ld_nt(ell_nnz + r);
+    const float y0 = y[r];
+    int32_t c[U];
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t slot = static_cast<uint32_t>(u) * ru + r;
+        c[u] = u < W ? ld_nt(ell_col + slot) : 0;
+        v[u] = u < W ? ld_nt(ell_val + slot) : 0.f;
+    }
     float sum = 0.f;
     for (int32_t t0 = 0; t0 < W; t0 += U) {
-        int32_t c[U];
-        float v[U];
+        int32_t cn[U];
+        float vn[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int32_t t = t0 + u;
-            const uint32_t slot = static_cast<uint32_t>(t) * static_cast<uint32_t>(R) + r;
-            c[u] = t < W ? ld_nt(ell_col + slot) : 0;
-            v[u] = t < W ? ld_nt(ell_val + slot) : 0.f;
+            const int32_t t = t0 + U + u;
+            const uint32_t slot = static_cast<uint32_t>(t) * ru + r;
+            cn[u] = t < W ? ld_nt(ell_col + slot) : 0;
+            vn[u] = t < W ? ld_nt(ell_val + slot) : 0.f;
         }
+        float xv[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-            if (t0 + u < n) sum += v[u] * x[c[u]];
+        for (int u = 0; u < U; ++u) xv[u] = (t0 + u < n) ? x[c[u]] : 0.f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) sum += v[u] * xv[u];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            c[u] = cn[u];
+            v[u] = vn[u];
+        }
     }
-    if (n > 0) y[r] += sum;
+    if (n > 0) y[r] = y0 + sum;
 }
 
 // ---------------------------------------------------------------------------
@@ -363,6 +383,14 @@ spmv_status launch_spmv(const spmv_handle *h, const float *x, float *y, hipStrea
     const int32_t R = static_cast<int32_t>(h->stats.num_rows);
     const int32_t nnz = static_cast<int32_t>(h->stats.nnz);
     if (R == 0 || nnz == 0) return SPMV_OK;
+    if (!h->parts.empty()) {
+        // x slices, one pass each over y, in stream order
+        for (const spmv_handle *p : h->parts) {
+            const spmv_status st = launch_spmv(p, x, y, s);
+            if (st != SPMV_OK) return st;
+        }
+        return SPMV_OK;
+    }
     const DevArrays &a = h->a;
     hipError_t e = hipSuccess;
     switch (h->format) {

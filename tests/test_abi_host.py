@@ -41,7 +41,8 @@ def test_status_and_format_names(lib):
 def test_opts_default(lib):
     o = spmv._Opts()
     lib.spmv_opts_default(ctypes.byref(o))
-    assert (o.hyb_width, o.lanes_per_row, o.validate, o.jds_depth, o.max_bytes) == (0, 0, 1, 0, 0)
+    assert (o.hyb_width, o.lanes_per_row, o.validate, o.jds_depth, o.col_blocks, o.reserved,
+            o.max_bytes) == (0, 0, 1, 0, 0, 0, 0)
 
 
 def test_argument_checks_before_device(lib):
@@ -63,7 +64,8 @@ def test_argument_checks_before_device(lib):
 def _stats(R, lens):
     lens = np.asarray(lens, np.int64)
     return {"num_rows": R, "num_cols": R, "nnz": int(lens.sum()), "max_len": int(lens.max()),
-            "sum_len_sq": int((lens * lens).sum()), "empty_rows": int((lens == 0).sum())}
+            "sum_len_sq": int((lens * lens).sum()), "empty_rows": int((lens == 0).sum()),
+            "col_spread": 0}
 
 
 def _hist(lens):
@@ -101,7 +103,7 @@ def test_selector_on_workloads(name):
     w = synth.workload(name)
     st = oracle.row_stats(w.row_ptrs)
     stats = {"num_rows": w.num_rows, "num_cols": w.num_cols, "nnz": w.nnz, "max_len": st["W"],
-             "sum_len_sq": st["sum_len_sq"], "empty_rows": st["empty_rows"]}
+             "sum_len_sq": st["sum_len_sq"], "empty_rows": st["empty_rows"], "col_spread": 0}
     assert spmv.select(stats, st["hist"]) == oracle.select(w.num_rows, w.nnz, st["hist"])
     expect = {"c1s": "ell", "c2s": "ell", "c3s": "ell", "c4s": "hyb", "c5s": "csr_merge",
               "fig14_1": "ell"}[name]

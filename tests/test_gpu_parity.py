@@ -420,10 +420,13 @@ def test_full_size_parity(dev, name, fmt):
     kw = {"hyb_width": 20} if (fmt == "hyb" and name == "c4") else {}
     h = build(fmt, w, dev, **kw)
     if fmt == "auto":
-        assert h.format == {"c1": "ell", "c2": "ell", "c3": "ell", "c4": "hyb",
-                            "c5": "csr_merge"}[name]
-        if name == "c4":
-            assert h.info["hyb_width"] == 20
+        # x fits one XCD's L2 (c1, c2) or rows are banded (c3): one slice;
+        # scattered columns over 8 / 16 MB of x: 4 MiB x slices
+        assert h.info["col_blocks"] == {"c1": 1, "c2": 1, "c3": 1, "c4": 2, "c5": 4}[name]
+        if name in ("c1", "c2", "c3"):
+            assert h.format == "ell"
+    else:
+        assert h.info["col_blocks"] == 1
     _, _, _, x, y0 = to_dev(w, dev)
     y_ref, bound = ref(name)
     assert_rows(run_once(h, x, y0), y_ref, bound, f"full {name}/{fmt}")
@@ -438,3 +441,35 @@ def test_full_size_builders_bitexact(dev, name, fmt):
     kw = {"hyb_width": 20} if fmt == "hyb" else {}
     h = build(fmt, w, dev, **kw)
     check_builder(h, w)
+
+
+@pytest.mark.parametrize("name,expect", [("c4", ("hyb", 20)), ("c5", ("csr_merge", 0))])
+def test_full_size_selector_unsliced(dev, name, expect):
+    """Without x slices the selector picks HYB(20) for the skewed matrix (the
+    width the format-choice article found best) and merge CSR for power law."""
+    h = build("auto", W(name), dev, col_blocks=1)
+    assert (h.format, h.info["hyb_width"]) == expect and h.info["col_blocks"] == 1
+
+
+@pytest.mark.parametrize("name", ["c2s", "c4s", "c5s", "c3s"])
+@pytest.mark.parametrize("fmt", ALL_FORMATS + ["auto"])
+def test_col_slices_parity(dev, name, fmt):
+    """Every format split into 3 x slices (and auto) still meets the row bound;
+    a sliced handle exports only the histogram."""
+    w = W(name)
+    if fmt == "ell" and name in ("c4s", "c5s"):
+        pytest.skip("ELL of a skewed slice is mostly padding")
+    h = build(fmt, w, dev, col_blocks=3)
+    assert h.info["col_blocks"] == 3
+    assert h.info["slice_cols"] == -(-w.num_cols // 3)
+    assert not h.has_array("col_idx") and not h.has_array("ell_col")
+    _, _, _, x, y0 = to_dev(w, dev)
+    assert_rows(run_once(h, x, y0), *ref(name), f"{name}/{fmt} 3 slices")
+
+
+@pytest.mark.parametrize("fmt", ["auto", "csr_merge", "coo_segmented", "csr_vector", "jds", "hyb"])
+def test_full_size_power_law_slices(dev, fmt):
+    w = W("c5")
+    h = build(fmt, w, dev, col_blocks=8)
+    _, _, _, x, y0 = to_dev(w, dev)
+    assert_rows(run_once(h, x, y0), *ref("c5"), f"c5/{fmt} 8 slices")

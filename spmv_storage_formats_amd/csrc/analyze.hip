@@ -33,12 +33,13 @@ __device__ inline unsigned long long wave_sum(unsigned long long v) {
 // uniformly scattered columns (used to decide on x slices).  The column is
 // read only when the row's start lies inside [0, nnz).
 //
-// Grid-stride with one set of atomics per wave and a capped grid: the
-// accumulators are single addresses, so their atomics must stay few.
+// Grid-stride over rows with a capped grid; each block reduces its waves in
+// LDS and writes one partial record (no atomics: same-address atomics from
+// thousands of waves serialise in the L2).  The host adds the partials.
 __global__ __launch_bounds__(kThreads) void k_row_checks(int32_t R, int32_t C, int32_t nnz,
                                                          const int32_t *__restrict__ rp,
                                                          const int32_t *__restrict__ col,
-                                                         RowStatsDev *__restrict__ st) {
+                                                         RowStatsDev *__restrict__ partial) {
     int bad = 0, wlen = 0;
     unsigned long long sq = 0, empty = 0, dist = 0;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
@@ -62,17 +63,31 @@ __global__ __launch_bounds__(kThreads) void k_row_checks(int32_t R, int32_t C, i
     if (R == 0 && blockIdx.x == 0 && threadIdx.x == 0) {  // rowPtrs = [0], nnz must be 0
         if (rp[0] != 0 || nnz != 0) bad = 1;
     }
+    __shared__ RowStatsDev waves[kThreads / kWave];
     const unsigned long long any_bad = __ballot(bad != 0);
     const int wmax = wave_max(wlen);
     const unsigned long long wsq = wave_sum(sq);
     const unsigned long long wempty = wave_sum(empty);
     const unsigned long long wdist = wave_sum(dist);
+    const int w = threadIdx.x / kWave;
     if (__lane_id() == 0) {
-        if (any_bad) atomicOr(&st->flags, kFlagBadRowPtrs);
-        if (wmax > 0) atomicMax(&st->max_len, wmax);
-        if (wsq) atomicAdd(&st->sum_len_sq, wsq);
-        if (wempty) atomicAdd(&st->empty_rows, wempty);
-        if (wdist) atomicAdd(&st->sum_first_dist, wdist);
+        waves[w].flags = any_bad ? kFlagBadRowPtrs : 0;
+        waves[w].max_len = wmax;
+        waves[w].sum_len_sq = wsq;
+        waves[w].empty_rows = wempty;
+        waves[w].sum_first_dist = wdist;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        RowStatsDev t = waves[0];
+        for (int i = 1; i < kThreads / kWave; ++i) {
+            t.flags |= waves[i].flags;
+            t.max_len = max(t.max_len, waves[i].max_len);
+            t.sum_len_sq += waves[i].sum_len_sq;
+            t.empty_rows += waves[i].empty_rows;
+            t.sum_first_dist += waves[i].sum_first_dist;
+        }
+        partial[blockIdx.x] = t;
     }
 }
 
@@ -128,11 +143,14 @@ __global__ __launch_bounds__(kThreads) void k_len_hist(int32_t R, const int32_t 
 
 }  // namespace
 
-hipError_t launch_row_checks(int32_t R, int32_t C, int32_t nnz, const int32_t *rp,
-                             const int32_t *col, RowStatsDev *st, hipStream_t s) {
+int row_check_blocks(int32_t R) {
     unsigned g = grid_for(R > 0 ? R : 1, kThreads);
-    if (g > 1024) g = 1024;
-    k_row_checks<<<g, kThreads, 0, s>>>(R, C, nnz, rp, col, st);
+    return static_cast<int>(g > kRowCheckMaxBlocks ? kRowCheckMaxBlocks : g);
+}
+
+hipError_t launch_row_checks(int32_t R, int32_t C, int32_t nnz, const int32_t *rp,
+                             const int32_t *col, RowStatsDev *partial, hipStream_t s) {
+    k_row_checks<<<row_check_blocks(R), kThreads, 0, s>>>(R, C, nnz, rp, col, partial);
     return hipGetLastError();
 }
 

@@ -85,14 +85,25 @@ struct Analysis {
 spmv_status analyze_csr(int32_t R, int32_t C, int32_t nnz, const int32_t *rp,
                         const int32_t *col, bool validate, bool want_hist, Analysis &out,
                         hipStream_t s, Scratch &scratch) {
+    // record 0: column-check flags; records 1..G: per-block row statistics
+    const int G = row_check_blocks(R);
     RowStatsDev *d = nullptr;
-    SPMV_TRY(scratch.alloc(&d, 1));
+    SPMV_TRY(scratch.alloc(&d, static_cast<size_t>(G) + 1));
     SPMV_HIP(hipMemsetAsync(d, 0, sizeof(RowStatsDev), s));
-    SPMV_HIP(launch_row_checks(R, C, nnz, rp, col, d, s));
+    SPMV_HIP(launch_row_checks(R, C, nnz, rp, col, d + 1, s));
     if (validate) SPMV_HIP(launch_col_checks(nnz, C, col, d, s));
-    RowStatsDev h{};
-    SPMV_HIP(hipMemcpyAsync(&h, d, sizeof(h), hipMemcpyDeviceToHost, s));
+    std::vector<RowStatsDev> parts(static_cast<size_t>(G) + 1);
+    SPMV_HIP(hipMemcpyAsync(parts.data(), d, sizeof(RowStatsDev) * parts.size(),
+                            hipMemcpyDeviceToHost, s));
     SPMV_HIP(hipStreamSynchronize(s));
+    RowStatsDev h = parts[0];
+    for (int i = 1; i <= G; ++i) {
+        h.flags |= parts[i].flags;
+        h.max_len = std::max(h.max_len, parts[i].max_len);
+        h.sum_len_sq += parts[i].sum_len_sq;
+        h.empty_rows += parts[i].empty_rows;
+        h.sum_first_dist += parts[i].sum_first_dist;
+    }
     if (h.flags & kFlagBadRowPtrs) return SPMV_ERR_BAD_ROWPTRS;
     if (h.flags & kFlagBadCol) return SPMV_ERR_BAD_COLIDX;
     out.st.num_rows = R;

@@ -68,13 +68,27 @@ __global__ __launch_bounds__(kThreads) void k_coo_segmented(int32_t nnz,
     // plain read-modify-write it never makes the wave wait on a scattered load
     // (measured faster on MI355X even for runs no other wave touches).
     auto flush = [&](int32_t r, float v) { atomic_add_f32(&y[r], v); };
-    int carry_row = INT32_MAX;
-    float carry = 0.f;
+    // all 8 batches' loads, then all 8 gathers, before the first scan
+    int32_t rr[kSegIters], cc[kSegIters];
+    float vv[kSegIters], pp[kSegIters];
+#pragma unroll
     for (int it = 0; it < kSegIters; ++it) {
         const int64_t i = base + it * kWave + lane;
         const bool valid = i < nnz;
-        const int32_t r = valid ? ld_nt(row + i) : INT32_MAX;
-        float p = valid ? ld_nt(val + i) * x[ld_nt(col + i)] : 0.f;
+        rr[it] = valid ? ld_nt(row + i) : INT32_MAX;
+        cc[it] = valid ? ld_nt(col + i) : 0;
+        vv[it] = valid ? ld_nt(val + i) : 0.f;
+    }
+#pragma unroll
+    for (int it = 0; it < kSegIters; ++it) pp[it] = rr[it] != INT32_MAX ? vv[it] * x[cc[it]] : 0.f;
+    int carry_row = INT32_MAX;
+    float carry = 0.f;
+#pragma unroll
+    for (int it = 0; it < kSegIters; ++it) {
+        const int64_t i = base + it * kWave + lane;
+        const bool valid = i < nnz;
+        const int32_t r = rr[it];
+        float p = pp[it];
 #pragma unroll
         for (int off = 1; off < kWave; off <<= 1) {
             const int32_t ru = __shfl_up(r, off);
@@ -91,7 +105,6 @@ __global__ __launch_bounds__(kThreads) void k_coo_segmented(int32_t nnz,
         carry_row = __builtin_amdgcn_readlane(r, kWave - 1);
         carry = __builtin_bit_cast(float,
                                    __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), kWave - 1));
-        if (base + (it + 1) * kWave >= nnz) break;
     }
     if (lane == 0 && carry_row != INT32_MAX) flush(carry_row, carry);
 }
@@ -136,36 +149,68 @@ __global__ __launch_bounds__(kThreads) void k_csr_scalar(int32_t R, const int32_
 // 32-lane warp per row; here L = 2..64 of a 64-lane wavefront).  Lanes stride
 // the row by L; the group sum uses DPP / ds_swizzle (group_sum).
 // ---------------------------------------------------------------------------
-template <int L>
+template <int L, int kRpg>
 __global__ __launch_bounds__(kThreads) void k_csr_vector(int32_t R, const int32_t *__restrict__ rp,
                                                          const int32_t *__restrict__ col,
                                                          const float *__restrict__ val,
                                                          const float *__restrict__ x,
                                                          float *__restrict__ y) {
-    constexpr int kRows = kThreads / L;
+    // Each group of L lanes takes kRpg rows, interleaved so that at every step
+    // the block's groups work on consecutive rows (contiguous nonzeros).  The
+    // first 2 elements per lane of all kRpg rows are loaded before any gather,
+    // so a wave keeps 2*kRpg loads per lane in flight; longer rows finish in a
+    // remainder loop.  kRpg = 4 only when no row needs the remainder loop and
+    // the grid stays large (run_vector); otherwise one row per group.
+    constexpr int kGroups = kThreads / L;
+    constexpr int kRows = kGroups * kRpg;
     __shared__ int32_t srp[kRows + 1];
     const uint32_t b = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t r0 = static_cast<int64_t>(b) * kRows;
-    if (threadIdx.x <= kRows && r0 + threadIdx.x <= R) srp[threadIdx.x] = rp[r0 + threadIdx.x];
+    for (int i = threadIdx.x; i <= kRows; i += kThreads)
+        if (r0 + i <= R) srp[i] = rp[r0 + i];
     __syncthreads();
     const int g = threadIdx.x / L, lg = threadIdx.x % L;
-    const int64_t r = r0 + g;
-    int32_t a = 0, e = 0;
-    if (r < R) {
-        a = srp[g];
-        e = srp[g + 1];
+    int32_t a[kRpg], e[kRpg], c0[kRpg], c1[kRpg];
+    float v0[kRpg], v1[kRpg], acc[kRpg];
+#pragma unroll
+    for (int m = 0; m < kRpg; ++m) {
+        const int lr = m * kGroups + g;
+        const bool ok = r0 + lr < R;
+        a[m] = ok ? srp[lr] : 0;
+        e[m] = ok ? srp[lr + 1] : 0;
+        const int32_t j = a[m] + lg;
+        c0[m] = j < e[m] ? ld_nt(col + j) : 0;
+        v0[m] = j < e[m] ? ld_nt(val + j) : 0.f;
+        c1[m] = j + L < e[m] ? ld_nt(col + j + L) : 0;
+        v1[m] = j + L < e[m] ? ld_nt(val + j + L) : 0.f;
     }
-    float s0 = 0.f, s1 = 0.f;
-    int32_t j = a + lg;
-    for (; j + L < e; j += 2 * L) {
-        const int32_t c0 = ld_nt(col + j), c1 = ld_nt(col + j + L);
-        const float v0 = ld_nt(val + j), v1 = ld_nt(val + j + L);
-        s0 += v0 * x[c0];
-        s1 += v1 * x[c1];
+#pragma unroll
+    for (int m = 0; m < kRpg; ++m) {
+        const int32_t j = a[m] + lg;
+        const float x0 = j < e[m] ? x[c0[m]] : 0.f;
+        const float x1 = j + L < e[m] ? x[c1[m]] : 0.f;
+        acc[m] = v0[m] * x0 + v1[m] * x1;
+        // long rows: 4 elements per lane per step, loads before gathers
+        int32_t jj = j + 2 * L;
+        for (; jj + 3 * L < e[m]; jj += 4 * L) {
+            int32_t cq[4];
+            float vq[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                cq[q] = ld_nt(col + jj + q * L);
+                vq[q] = ld_nt(val + jj + q * L);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[m] += vq[q] * x[cq[q]];
+        }
+        for (; jj < e[m]; jj += L) acc[m] += ld_nt(val + jj) * x[ld_nt(col + jj)];
     }
-    if (j < e) s0 += ld_nt(val + j) * x[ld_nt(col + j)];
-    const float sum = group_sum<L>(s0 + s1);
-    if (lg == 0 && e > a) atomic_add_f32(&y[r], sum);
+#pragma unroll
+    for (int m = 0; m < kRpg; ++m) {
+        const float sum = group_sum<L>(acc[m]);
+        const int64_t r = r0 + m * kGroups + g;
+        if (lg == 0 && e[m] > a[m]) atomic_add_f32(&y[r], sum);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -252,20 +297,41 @@ __global__ __launch_bounds__(kThreads) void k_jds(int32_t R, int32_t ntiles, int
     const int32_t glen = __builtin_amdgcn_readfirstlane(jds_len[static_cast<int64_t>(g) * kWave]);
     const int32_t t0 = chunk * depth;
     const int32_t t1 = min(t0 + depth, glen);
-    float s0 = 0.f, s1 = 0.f;
-    int32_t t = t0;
-    for (; t + 1 < t1; t += 2) {
-        const int32_t p0 = iter_ptr[t], p1 = iter_ptr[t + 1];
-        if (t < len) s0 += ld_nt(val + p0 + s) * x[ld_nt(col + p0 + s)];
-        if (t + 1 < len) s1 += ld_nt(val + p1 + s) * x[ld_nt(col + p1 + s)];
-    }
-    if (t < t1 && t < len) {
-        const int32_t p0 = iter_ptr[t];
-        s0 += ld_nt(val + p0 + s) * x[ld_nt(col + p0 + s)];
+    // jagged columns U at a time, the next U columns' loads issued before the
+    // current U gathers (as in ELL)
+    constexpr int U = 8;
+    int32_t c[U];
+    float v[U];
+    auto load = [&](int32_t tb, int32_t *cc, float *vv) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int32_t t = tb + u;
+            const int32_t p = t < t1 ? iter_ptr[t] : 0;   // wave-uniform
+            const bool ok = t < t1 && t < len;
+            cc[u] = ok ? ld_nt(col + p + s) : 0;
+            vv[u] = ok ? ld_nt(val + p + s) : 0.f;
+        }
+    };
+    load(t0, c, v);
+    float sum = 0.f;
+    for (int32_t tb = t0; tb < t1; tb += U) {
+        int32_t cn[U];
+        float vn[U];
+        load(tb + U, cn, vn);
+        float xv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) xv[u] = (tb + u < t1 && tb + u < len) ? x[c[u]] : 0.f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) sum += v[u] * xv[u];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            c[u] = cn[u];
+            v[u] = vn[u];
+        }
     }
     // y[perm[s]] is scattered: a non-returning atomic never stalls the wave on a
     // load (and with one contribution per row the result is still exact-order).
-    if (len > t0) atomic_add_f32(&y[perm[s]], s0 + s1);
+    if (len > t0) atomic_add_f32(&y[perm[s]], sum);
 }
 
 // ---------------------------------------------------------------------------
@@ -353,10 +419,15 @@ unsigned blocks_of(int64_t n, int per_block) { return grid_for(n, per_block); }
 
 template <int L>
 hipError_t run_vector(const spmv_handle *h, const float *x, float *y, hipStream_t s) {
-    constexpr int kRows = kThreads / L;
     const int32_t R = static_cast<int32_t>(h->stats.num_rows);
-    k_csr_vector<L><<<blocks_of(R, kRows), kThreads, 0, s>>>(R, h->a.row_ptrs, h->a.col_idx,
-                                                             h->a.values, x, y);
+    constexpr int kRows4 = kThreads / L * 4;
+    const bool four = h->stats.max_len <= 2 * L && blocks_of(R, kRows4) >= 2048;
+    if (four)
+        k_csr_vector<L, 4><<<blocks_of(R, kRows4), kThreads, 0, s>>>(
+            R, h->a.row_ptrs, h->a.col_idx, h->a.values, x, y);
+    else
+        k_csr_vector<L, 1><<<blocks_of(R, kThreads / L), kThreads, 0, s>>>(
+            R, h->a.row_ptrs, h->a.col_idx, h->a.values, x, y);
     return hipGetLastError();
 }
 

@@ -26,7 +26,7 @@ _lib = None
 
 OK, ERR_INVALID_ARG, ERR_BAD_ROWPTRS, ERR_BAD_COLIDX, ERR_BAD_ROWIDX, ERR_TOO_LARGE = range(6)
 FMT_NAMES = {1: "coo_atomic", 2: "coo_segmented", 3: "csr_scalar", 4: "csr_vector",
-             5: "ell", 6: "hyb", 7: "jds", 8: "csr_merge"}
+             5: "ell", 6: "hyb", 7: "jds", 8: "csr_merge", 9: "sell"}
 RTOL = 1e-5
 
 _i32p = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
@@ -70,6 +70,9 @@ def _load():
                                           _i32p, _i32p, _u32p]),
         "orc_csr_to_jds": (ctypes.c_int, [_i64, _i32p, _i32p, _u32p, _i64, _i32p, _i32p, _i32p,
                                           _i32p, _u32p]),
+        "orc_sell_slots": (_i64, [_i64, _i32p, _i64]),
+        "orc_csr_to_sell": (ctypes.c_int, [_i64, _i32p, _i32p, _u32p, _i64, _i32p, _i32p, _i32p,
+                                           _i32p, _u32p]),
         "orc_hyb_width": (_i64, [_i64, _i64, _i64p]),
         "orc_vector_lanes": (_i64, [_i64, _i64]),
         "orc_select": (None, [_i64, _i64, _i64, _i64p, _i64, _i64, _i64p]),
@@ -229,6 +232,28 @@ def csr_to_jds(row_ptrs, col_idx, values):
     jv = np.empty(nnz, np.uint32)
     _load().orc_csr_to_jds(R, rp, _i32(col_idx), _bits(values), W, perm, jlen, iptr, jc, jv)
     return {"perm": perm, "len": jlen, "iter_ptr": iptr, "col": jc, "val": jv.view(np.float32)}
+
+
+def csr_to_sell(row_ptrs, col_idx, values, section=64):
+    """Sectioned ELL (JDS variant): perm/len as JDS, section pointers, slots."""
+    rp = _i32(row_ptrs)
+    R = rp.shape[0] - 1
+    lib = _load()
+    slots = int(lib.orc_sell_slots(R, rp, section))
+    if slots > 2**31 - 1:
+        raise ValueError("too large")
+    nsect = (R + section - 1) // section
+    perm = np.empty(R, np.int32)
+    slen = np.empty(R, np.int32)
+    sptr = np.empty(nsect + 1, np.int32)
+    sc = np.empty(slots, np.int32)
+    sv = np.empty(slots, np.uint32)
+    st = lib.orc_csr_to_sell(R, rp, _i32(col_idx), _bits(values), section, perm, slen, sptr,
+                             sc, sv)
+    if st == ERR_TOO_LARGE:
+        raise ValueError("too large")
+    return {"perm": perm, "len": slen, "sect_ptr": sptr, "col": sc, "val": sv.view(np.float32),
+            "section": section}
 
 
 # ------------------------------------------------------------------ selector

@@ -23,6 +23,9 @@
  *   - HYB tail: entries past position K of each row, rows in order, positions
  *     in order; ELL part of width min(K, W).
  *   - JDS: rows sorted by length, longest first, ties by ascending original row.
+ *   - Sectioned ELL: sections of S consecutive sorted rows (the last one may be
+ *     shorter), each padded to its own longest row, column-major inside the
+ *     section.
  *   - The selector's comparison operators (lost from P3 4.3) are restored as
  *     W*R <= 2*nnz -> ELL; nnz < 10*R -> COO; W*R > 5*nnz -> HYB; else CSR,
  *     with the HYB width/budget extension described at orc_select().
@@ -52,6 +55,7 @@ enum {
     ORC_FMT_HYB = 6,
     ORC_FMT_JDS = 7,
     ORC_FMT_CSR_MERGE = 8,
+    ORC_FMT_SELL = 9,
 };
 
 #define ORC_INT32_MAX 2147483647LL
@@ -421,4 +425,89 @@ void orc_select(int64_t R, int64_t nnz, int64_t W, const int64_t *hist, int64_t 
     }
     out[0] = ORC_FMT_CSR_VECTOR;
     out[2] = lanes > 0 ? lanes : orc_vector_lanes(R, nnz);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Sectioned ELL, the JDS variant [REG, JDS variant section]: after the JDS */
+/* sort, cut the sorted rows into sections; each section is an ELL padded   */
+/* only to the longest row of that section; section pointers replace        */
+/* iterPtr.  Section k holds sorted rows [k*S, k*S + m_k), m_k = min(S,     */
+/* R - k*S), width w_k = its longest row; entry t of its row i sits at      */
+/* sect_ptr[k] + t*m_k + i; padding is (column 0, +0.0f).                   */
+/* perm and sell_len are the JDS ones.  Returns ORC_ERR_TOO_LARGE when the  */
+/* padded total exceeds int32.                                              */
+/* ------------------------------------------------------------------------ */
+
+int64_t orc_sell_slots(int64_t R, const int32_t *row_ptrs, int64_t S)
+{
+    /* padded slots = sum over sections of m_k * (longest row in section) */
+    int32_t *len = (int32_t *)malloc(((size_t)R + 1) * sizeof(int32_t));
+    int32_t *perm = (int32_t *)malloc(((size_t)R + 1) * sizeof(int32_t));
+    int64_t total = 0;
+    for (int64_t r = 0; r < R; ++r) {
+        len[r] = row_ptrs[r + 1] - row_ptrs[r];
+        perm[r] = (int32_t)r;
+    }
+    g_sort_len = len;
+    qsort(perm, (size_t)R, sizeof(int32_t), orc_cmp_len_desc);
+    for (int64_t k0 = 0; k0 < R; k0 += S) {
+        int64_t m = R - k0 < S ? R - k0 : S;
+        total += m * (int64_t)len[perm[k0]];
+    }
+    free(len);
+    free(perm);
+    return total;
+}
+
+int orc_csr_to_sell(int64_t R, const int32_t *row_ptrs, const int32_t *col_idx,
+                    const uint32_t *values, int64_t S, int32_t *perm, int32_t *sell_len,
+                    int32_t *sect_ptr, int32_t *sell_col, uint32_t *sell_val)
+{
+    if (S <= 0)
+        return ORC_ERR_INVALID_ARG;
+    int32_t *len = (int32_t *)malloc(((size_t)R + 1) * sizeof(int32_t));
+    if (!len)
+        return ORC_ERR_INVALID_ARG;
+    for (int64_t r = 0; r < R; ++r) {
+        len[r] = row_ptrs[r + 1] - row_ptrs[r];
+        perm[r] = (int32_t)r;
+    }
+    g_sort_len = len;
+    qsort(perm, (size_t)R, sizeof(int32_t), orc_cmp_len_desc);
+    for (int64_t s = 0; s < R; ++s)
+        sell_len[s] = len[perm[s]];
+    int64_t nsect = (R + S - 1) / S;
+    int64_t off = 0;
+    for (int64_t k = 0; k < nsect; ++k) {
+        int64_t first = k * S;
+        int64_t m = R - first < S ? R - first : S;
+        int64_t w = sell_len[first];            /* longest row of the section */
+        if (off > ORC_INT32_MAX) {
+            free(len);
+            return ORC_ERR_TOO_LARGE;
+        }
+        sect_ptr[k] = (int32_t)off;
+        for (int64_t t = 0; t < w; ++t) {
+            for (int64_t i = 0; i < m; ++i) {
+                int64_t slot = off + t * m + i;
+                int64_t s = first + i;
+                if (t < sell_len[s]) {
+                    int64_t src = row_ptrs[perm[s]] + t;
+                    sell_col[slot] = col_idx[src];
+                    sell_val[slot] = values[src];
+                } else {
+                    sell_col[slot] = 0;
+                    sell_val[slot] = 0u;
+                }
+            }
+        }
+        off += m * w;
+    }
+    if (off > ORC_INT32_MAX) {
+        free(len);
+        return ORC_ERR_TOO_LARGE;
+    }
+    sect_ptr[nsect] = (int32_t)off;
+    free(len);
+    return ORC_OK;
 }

@@ -459,3 +459,64 @@ def test_validate_page_checks():
     bad = ci.copy(); bad[1] = 9
     assert oracle.validate_coo(4, 4, ri, bad) == oracle.ERR_BAD_COLIDX
     assert oracle.validate_csr(0, 0, np.zeros(1, np.int32), np.zeros(0, np.int32)) == oracle.OK
+
+
+# ------------------------------------------------------ sectioned ELL (JDS variant)
+
+def test_sell_hand_derived_example():
+    """Sections of 2 sorted rows of Fig. 14.1, derived by hand from the page's
+    definition; less padding than the single ELL (2 vs 4 slots)."""
+    g = _gold("sell_fig14_1.json")
+    w = _fig()
+    o = oracle.csr_to_sell(w.row_ptrs, w.col_idx, w.values, g["section_rows"])
+    assert o["perm"].tolist() == g["row"]
+    assert o["sect_ptr"].tolist() == g["sect_ptr"]
+    assert o["val"].tolist() == [0.0 if v == "*" else v for v in g["value"]]
+    assert o["col"].tolist() == [0 if c == "*" else c for c in g["colIdx"]]
+    assert int(o["sect_ptr"][-1]) - w.nnz == g["padding_sectioned"]
+    e = oracle.csr_to_ell(w.row_ptrs, w.col_idx, w.values)
+    assert 4 * e["width"] - w.nnz == g["padding_single_ell"]
+
+
+@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("S", [1, 2, 3, 64])
+def test_sell_semantics_bruteforce(seed, S):
+    """Slot (section k, row i, position t) at sect_ptr[k] + t*m_k + i holds
+    entry t of sorted row k*S + i; pads are (0, +0.0f); the arrays rebuild A."""
+    rng = np.random.default_rng(9500 + seed)
+    w = synth.small_random(rng, int(rng.integers(1, 40)), 11, max_len=9)
+    R = w.num_rows
+    lens = np.diff(w.row_ptrs).astype(int)
+    o = oracle.csr_to_sell(w.row_ptrs, w.col_idx, w.values, S)
+    perm, sl, sp = o["perm"], o["len"], o["sect_ptr"]
+    j = oracle.csr_to_jds(w.row_ptrs, w.col_idx, w.values)
+    assert perm.tolist() == j["perm"].tolist() and sl.tolist() == j["len"].tolist()
+    nsect = -(-R // S)
+    assert sp.shape == (nsect + 1,) and sp[0] == 0
+    A = _dense_from_csr(R, 11, w.row_ptrs, w.col_idx, w.values)
+    B = np.zeros_like(A)
+    for k in range(nsect):
+        m = min(S, R - k * S)
+        width = max(lens[perm[k * S:k * S + m]])   # the section's longest row
+        assert sp[k + 1] - sp[k] == m * width
+        for t in range(width):
+            for i in range(m):
+                slot = sp[k] + t * m + i
+                s = k * S + i
+                if t < sl[s]:
+                    assert o["col"][slot] == w.col_idx[w.row_ptrs[perm[s]] + t]
+                    B[perm[s], o["col"][slot]] += o["val"][slot]
+                else:
+                    assert o["col"][slot] == 0 and o["val"].view(np.uint32)[slot] == 0
+    assert np.array_equal(A, B)
+    # never more padding than one ELL of the whole matrix
+    assert sp[-1] <= R * lens.max()
+
+
+def test_sell_padding_on_skewed_shape():
+    """On the reduced skewed workload, sections pad far less than a single ELL
+    (the page's reason for the variant)."""
+    w = synth.workload("c4s")
+    o = oracle.csr_to_sell(w.row_ptrs, w.col_idx, w.values, 64)
+    ell_slots = w.num_rows * int(np.diff(w.row_ptrs).max())
+    assert int(o["sect_ptr"][-1]) < 1.1 * w.nnz < 0.01 * ell_slots

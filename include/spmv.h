@@ -77,8 +77,12 @@ typedef enum spmv_format {
     SPMV_ELL = 5,           /* padded, column-major, one lane per row [REG, ELL]           */
     SPMV_HYB = 6,           /* ELL of width K + COO tail [REG, hybrid; CHOICE 3.2, 4.1]    */
     SPMV_JDS = 7,           /* rows sorted by length, jagged column-major [REG, JDS]       */
-    SPMV_CSR_MERGE = 8      /* merge-path: equal shares of rows+nonzeros per block
+    SPMV_CSR_MERGE = 8,     /* merge-path: equal shares of rows+nonzeros per block
                                [CHOICE 5.2; INTRO, parallel efficiency]                    */
+    SPMV_SELL = 9           /* sectioned ELL, the JDS variant: rows sorted by length, cut
+                               into sections of 64 sorted rows, each an ELL padded to its
+                               own longest row [REG, JDS variant].  Never picked by
+                               SPMV_AUTO (the selector rule has no branch for it).         */
 } spmv_format;
 
 typedef struct spmv_opts {
@@ -146,7 +150,13 @@ typedef enum spmv_array {
     SPMV_A_JDS_ITER_PTR = 12, /* int32 [W+1] start of jagged column t         */
     SPMV_A_JDS_COL = 13,   /* int32 [nnz]   entry t of sorted row s at iterPtr[t]+s */
     SPMV_A_JDS_VAL = 14,   /* fp32  [nnz]                                     */
-    SPMV_A_LEN_HIST = 15   /* int64 [W+1]   rows of each length (every handle) */
+    SPMV_A_LEN_HIST = 15,  /* int64 [W+1]   rows of each length (every handle) */
+    SPMV_A_SELL_SECT_PTR = 16, /* int32 [S+1] start of section k (S = ceil(R/64))  */
+    SPMV_A_SELL_COL = 17,  /* int32 [slots] entry t of the section's row i at
+                              sect_ptr[k] + t*m_k + i, m_k = rows in section k;
+                              padding (0, +0.0f).  Sorted-row order and lengths
+                              are SPMV_A_JDS_PERM / SPMV_A_JDS_LEN.          */
+    SPMV_A_SELL_VAL = 18   /* fp32  [slots]                                    */
 } spmv_array;
 
 typedef struct spmv_handle spmv_handle;
@@ -195,10 +205,13 @@ spmv_status spmv_select(const spmv_stats *stats_host, const int64_t *hist_host,
  *           list in row order; ELL of width min(K, W) for the rest]
  *     JDS  [REG, JDS: stable sort of rows by length, longest first; perm;
  *           iterPtr from the length counts; jagged column-major arrays]
+ *     SELL [REG, JDS variant: the JDS sort, then sections of 64 sorted rows,
+ *           each an ELL padded to its own longest row; section pointers]
  *     COO  row index expanded from rowPtrs [COO/CSR, COO section]
  *     CSR merge: per-block starting rows of the merge path
- *   Fails with SPMV_ERR_TOO_LARGE when an ELL (or HYB ELL part) would need
- *   R*width > 2^31-1 slots or when opts->max_bytes is exceeded.
+ *   Fails with SPMV_ERR_TOO_LARGE when an ELL (or HYB ELL part, or the padded
+ *   SELL sections) would need more than 2^31-1 slots or when opts->max_bytes
+ *   is exceeded.
  *   values_dev: fp32[nnz], moved bit for bit.  opts nullable (defaults).
  */
 spmv_status spmv_build(spmv_handle **out, spmv_format format, int32_t num_rows,

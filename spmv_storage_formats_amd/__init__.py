@@ -29,7 +29,7 @@ _LIB_PATH = os.path.join(_PKG, "libspmv_mi355x.so")
 _HEADER = os.path.join(_ROOT, "include", "spmv.h")
 
 FORMATS = {"auto": 0, "coo_atomic": 1, "coo_segmented": 2, "csr_scalar": 3, "csr_vector": 4,
-           "ell": 5, "hyb": 6, "jds": 7, "csr_merge": 8}
+           "ell": 5, "hyb": 6, "jds": 7, "csr_merge": 8, "sell": 9}
 FORMAT_NAMES = {v: k for k, v in FORMATS.items()}
 # name -> (enum value, numpy dtype)
 ARRAYS = {
@@ -38,7 +38,8 @@ ARRAYS = {
     "ell_nnz": (6, np.int32), "tail_row": (7, np.int32), "tail_col": (8, np.int32),
     "tail_val": (9, np.float32), "jds_perm": (10, np.int32), "jds_len": (11, np.int32),
     "jds_iter_ptr": (12, np.int32), "jds_col": (13, np.int32), "jds_val": (14, np.float32),
-    "len_hist": (15, np.int64),
+    "len_hist": (15, np.int64), "sell_sect_ptr": (16, np.int32), "sell_col": (17, np.int32),
+    "sell_val": (18, np.float32),
 }
 STATUS = {0: "SPMV_OK", 1: "SPMV_ERR_INVALID_ARG", 2: "SPMV_ERR_BAD_ROWPTRS",
           3: "SPMV_ERR_BAD_COLIDX", 4: "SPMV_ERR_BAD_ROWIDX", 5: "SPMV_ERR_TOO_LARGE",

@@ -74,7 +74,7 @@ bool valid_opts(const spmv_opts &o) {
            o.col_blocks >= 0 && o.col_blocks <= kMaxColBlocks && o.reserved == 0;
 }
 
-bool valid_format(int32_t f) { return f >= SPMV_AUTO && f <= SPMV_CSR_MERGE; }
+bool valid_format(int32_t f) { return f >= SPMV_AUTO && f <= SPMV_SELL; }
 
 // ---------------------------------------------------------------- analysis
 struct Analysis {
@@ -229,8 +229,10 @@ spmv_status build_hyb_tail(spmv_handle *h, int32_t R, int32_t K, const int32_t *
     return SPMV_OK;
 }
 
-spmv_status build_jds(spmv_handle *h, int32_t R, int32_t nnz, const int32_t *rp,
-                      const int32_t *col, const float *val, hipStream_t s, Scratch &scratch) {
+// JDS sort [REG, JDS: sort rows by nonzero count, longest first, recording
+// the original index]: stable radix sort of (W - len, row) -> perm, lengths.
+spmv_status jds_sort(spmv_handle *h, int32_t R, const int32_t *rp, hipStream_t s,
+                     Scratch &scratch) {
     const int32_t W = static_cast<int32_t>(h->stats.max_len);
     uint32_t *keys = nullptr, *sorted = nullptr;
     int32_t *rows = nullptr;
@@ -239,17 +241,14 @@ spmv_status build_jds(spmv_handle *h, int32_t R, int32_t nnz, const int32_t *rp,
     SPMV_TRY(scratch.alloc(&rows, R));
     SPMV_TRY(halloc(h, &h->a.jds_perm, R));
     SPMV_TRY(halloc(h, &h->a.jds_len, R));
-    SPMV_TRY(halloc(h, &h->a.jds_iter_ptr, static_cast<int64_t>(W) + 1));
-    SPMV_TRY(halloc(h, &h->a.jds_col, nnz));
-    SPMV_TRY(halloc(h, &h->a.jds_val, nnz));
     SPMV_HIP(launch_jds_keys(R, W, rp, keys, rows, s));
     SPMV_TRY(radix_sort_pairs(keys, rows, sorted, h->a.jds_perm, R, bits_for(W), s, scratch));
     SPMV_HIP(launch_jds_lengths(R, W, sorted, h->a.jds_len, s));
-    SPMV_HIP(launch_jds_counts(R, W, h->a.jds_len, h->a.jds_iter_ptr, s));
-    SPMV_TRY(exclusive_scan(h->a.jds_iter_ptr, h->a.jds_iter_ptr, W, true, s, scratch));
-    SPMV_HIP(launch_jds_fill(nnz, W, h->a.jds_iter_ptr, h->a.jds_perm, rp, col, val,
-                             h->a.jds_col, h->a.jds_val, s));
-    // wave tiles: (group of 64 sorted rows, chunk of `depth` jagged columns)
+    return SPMV_OK;
+}
+
+// Wave tiles over groups of 64 sorted rows: (group, chunk of `depth` columns).
+spmv_status jds_tiles(spmv_handle *h, int32_t R, hipStream_t s, Scratch &scratch) {
     const int32_t groups = static_cast<int32_t>((static_cast<int64_t>(R) + kWave - 1) / kWave);
     int32_t *off = nullptr;
     SPMV_TRY(scratch.alloc(&off, static_cast<size_t>(groups) + 1));
@@ -262,6 +261,53 @@ spmv_status build_jds(spmv_handle *h, int32_t R, int32_t nnz, const int32_t *rp,
     SPMV_TRY(halloc(h, &h->a.jds_tiles, ntiles));
     SPMV_HIP(launch_jds_tiles(groups, ntiles, off, h->a.jds_tiles, s));
     return SPMV_OK;
+}
+
+spmv_status build_jds(spmv_handle *h, int32_t R, int32_t nnz, const int32_t *rp,
+                      const int32_t *col, const float *val, hipStream_t s, Scratch &scratch) {
+    const int32_t W = static_cast<int32_t>(h->stats.max_len);
+    SPMV_TRY(jds_sort(h, R, rp, s, scratch));
+    SPMV_TRY(halloc(h, &h->a.jds_iter_ptr, static_cast<int64_t>(W) + 1));
+    SPMV_TRY(halloc(h, &h->a.jds_col, nnz));
+    SPMV_TRY(halloc(h, &h->a.jds_val, nnz));
+    SPMV_HIP(launch_jds_counts(R, W, h->a.jds_len, h->a.jds_iter_ptr, s));
+    SPMV_TRY(exclusive_scan(h->a.jds_iter_ptr, h->a.jds_iter_ptr, W, true, s, scratch));
+    SPMV_HIP(launch_jds_fill(nnz, W, h->a.jds_iter_ptr, h->a.jds_perm, rp, col, val,
+                             h->a.jds_col, h->a.jds_val, s));
+    return jds_tiles(h, R, s, scratch);
+}
+
+// Padded slots of the sectioned ELL, exactly, from the length histogram: the
+// sorted lengths run from W down; section k starts at sorted position 64k and
+// is as wide as the length found there.
+int64_t sell_slots_from_hist(int64_t R, const std::vector<int64_t> &hist) {
+    int64_t total = 0, pos = 0;
+    for (int64_t l = static_cast<int64_t>(hist.size()) - 1; l >= 0; --l) {
+        const int64_t c = hist[l];
+        if (c == 0) continue;
+        for (int64_t st = (pos + kWave - 1) / kWave * kWave; st < pos + c; st += kWave)
+            total += std::min<int64_t>(kWave, R - st) * l;
+        pos += c;
+    }
+    return total;
+}
+
+spmv_status build_sell(spmv_handle *h, int32_t R, const int32_t *rp, const int32_t *col,
+                       const float *val, hipStream_t s, Scratch &scratch) {
+    const int64_t slots = sell_slots_from_hist(R, h->hist);
+    if (slots > kInt32Max) return SPMV_ERR_TOO_LARGE;
+    h->sell_slots = slots;
+    const int32_t nsect = static_cast<int32_t>((static_cast<int64_t>(R) + kWave - 1) / kWave);
+    SPMV_TRY(jds_sort(h, R, rp, s, scratch));
+    SPMV_TRY(halloc(h, &h->a.sell_ptr, static_cast<int64_t>(nsect) + 1));
+    SPMV_TRY(halloc(h, &h->a.sell_col, slots));
+    SPMV_TRY(halloc(h, &h->a.sell_val, slots));
+    SPMV_HIP(launch_sell_sizes(R, h->a.jds_len, h->a.sell_ptr, s));
+    SPMV_TRY(exclusive_scan(h->a.sell_ptr, h->a.sell_ptr, nsect, true, s, scratch));
+    SPMV_HIP(launch_sell_fill(R, nsect, static_cast<int32_t>(slots), h->a.sell_ptr,
+                              h->a.jds_len, h->a.jds_perm, rp, col, val, h->a.sell_col,
+                              h->a.sell_val, s));
+    return jds_tiles(h, R, s, scratch);
 }
 
 // Device bytes a format needs (checked against opts.max_bytes before building).
@@ -282,6 +328,10 @@ int64_t format_bytes(int32_t fmt, int64_t R, int64_t nnz, int64_t W, int64_t K,
         return 8 * R * w + 4 * R + 12 * tail;
     }
     case SPMV_JDS: return 8 * nnz + 8 * R + 4 * (W + 1) + 8 * (R / kWave + 1 + nnz / kWave);
+    case SPMV_SELL: {
+        const int64_t slots = sell_slots_from_hist(R, hist);
+        return 8 * slots + 8 * R + 4 * (R / kWave + 2) + 8 * (R / kWave + 1 + slots / kWave);
+    }
     default: return 0;
     }
 }
@@ -434,6 +484,9 @@ spmv_status build_csr_impl(spmv_handle **out, spmv_format fmt, int32_t R, int32_
     }
     case SPMV_JDS:
         SPMV_TRY(build_jds(h.get(), R, nnz, rp, col, val, s, scratch));
+        break;
+    case SPMV_SELL:
+        SPMV_TRY(build_sell(h.get(), R, rp, col, val, s, scratch));
         break;
     default:
         return SPMV_ERR_INVALID_ARG;
@@ -634,6 +687,9 @@ ArrayRef array_ref(const spmv_handle *h, spmv_array which) {
     case SPMV_A_JDS_ITER_PTR: set(a.jds_iter_ptr, W + 1, 4); break;
     case SPMV_A_JDS_COL: set(a.jds_col, nnz, 4); break;
     case SPMV_A_JDS_VAL: set(a.jds_val, nnz, 4); break;
+    case SPMV_A_SELL_SECT_PTR: set(a.sell_ptr, (R + kWave - 1) / kWave + 1, 4); break;
+    case SPMV_A_SELL_COL: set(a.sell_col, h->sell_slots, 4); break;
+    case SPMV_A_SELL_VAL: set(a.sell_val, h->sell_slots, 4); break;
     case SPMV_A_LEN_HIST:
         r.host = h->hist.data();
         r.bytes = h->hist.size() * sizeof(int64_t);
@@ -701,6 +757,7 @@ const char *spmv_format_name(spmv_format f) {
     case SPMV_HYB: return "hyb";
     case SPMV_JDS: return "jds";
     case SPMV_CSR_MERGE: return "csr_merge";
+    case SPMV_SELL: return "sell";
     default: return "unknown";
     }
 }

@@ -186,6 +186,42 @@ __global__ __launch_bounds__(kThreads) void k_jds_fill(int32_t nnz, int32_t W,
     jds_val[e] = val[src];
 }
 
+// Sectioned ELL (JDS variant): section k = sorted rows [64k, 64k + m_k),
+// padded to its first (longest) row; slot (t, i) at sect_ptr[k] + t*m_k + i.
+__global__ __launch_bounds__(kThreads) void k_sell_sizes(int32_t R,
+                                                         const int32_t *__restrict__ jds_len,
+                                                         int32_t *__restrict__ sizes) {
+    const int64_t k = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    const int64_t nsect = (static_cast<int64_t>(R) + kWave - 1) / kWave;
+    if (k < nsect) {
+        const int64_t m = min(static_cast<int64_t>(kWave), R - k * kWave);
+        sizes[k] = static_cast<int32_t>(m * jds_len[k * kWave]);   // total checked on the host
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_sell_fill(
+    int32_t R, int32_t nsect, int32_t slots, const int32_t *__restrict__ sect_ptr,
+    const int32_t *__restrict__ jds_len, const int32_t *__restrict__ perm,
+    const int32_t *__restrict__ rp, const int32_t *__restrict__ col,
+    const uint32_t *__restrict__ val, int32_t *__restrict__ sell_col,
+    uint32_t *__restrict__ sell_val) {
+    const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (e >= slots) return;
+    const int64_t k = upper_index(sect_ptr, nsect, e);
+    const int64_t m = min(static_cast<int64_t>(kWave), R - k * kWave);
+    const int64_t off = e - sect_ptr[k];
+    const int64_t t = off / m, i = off % m;
+    const int64_t s = k * kWave + i;
+    if (t < jds_len[s]) {
+        const int64_t src = static_cast<int64_t>(rp[perm[s]]) + t;
+        sell_col[e] = col[src];
+        sell_val[e] = val[src];
+    } else {
+        sell_col[e] = 0;
+        sell_val[e] = 0u;
+    }
+}
+
 // Tiles of the JDS kernel: 64 consecutive sorted rows x `depth` jagged columns.
 // Group g needs ceil(len[64 g] / depth) tiles (its first row is its longest).
 __global__ __launch_bounds__(kThreads) void k_jds_chunks(int32_t R, int32_t depth,
@@ -355,6 +391,24 @@ hipError_t launch_jds_fill(int32_t nnz, int32_t W, const int32_t *iter_ptr,
     k_jds_fill<<<grid_for(nnz, kThreads), kThreads, 0, s>>>(
         nnz, W, iter_ptr, perm, rp, col, reinterpret_cast<const uint32_t *>(val), jds_col,
         reinterpret_cast<uint32_t *>(jds_val));
+    return hipGetLastError();
+}
+
+hipError_t launch_sell_sizes(int32_t R, const int32_t *jds_len, int32_t *sizes, hipStream_t s) {
+    if (R <= 0) return hipSuccess;
+    const int64_t nsect = (static_cast<int64_t>(R) + kWave - 1) / kWave;
+    k_sell_sizes<<<grid_for(nsect, kThreads), kThreads, 0, s>>>(R, jds_len, sizes);
+    return hipGetLastError();
+}
+
+hipError_t launch_sell_fill(int32_t R, int32_t nsect, int32_t slots, const int32_t *sect_ptr,
+                            const int32_t *jds_len, const int32_t *perm, const int32_t *rp,
+                            const int32_t *col, const float *val, int32_t *sell_col,
+                            float *sell_val, hipStream_t s) {
+    if (slots <= 0) return hipSuccess;
+    k_sell_fill<<<grid_for(slots, kThreads), kThreads, 0, s>>>(
+        R, nsect, slots, sect_ptr, jds_len, perm, rp, col,
+        reinterpret_cast<const uint32_t *>(val), sell_col, reinterpret_cast<uint32_t *>(sell_val));
     return hipGetLastError();
 }
 

@@ -55,7 +55,11 @@ struct DevArrays {
     int32_t *jds_iter_ptr = nullptr;
     int32_t *jds_col = nullptr;
     float *jds_val = nullptr;
-    int2 *jds_tiles = nullptr;      // (group of 64 sorted rows, depth chunk)
+    int2 *jds_tiles = nullptr;      // (group of 64 sorted rows, depth chunk); SELL too
+    // sectioned ELL (uses jds_perm, jds_len, jds_tiles as well)
+    int32_t *sell_ptr = nullptr;    // [sections + 1]
+    int32_t *sell_col = nullptr;
+    float *sell_val = nullptr;
     // CSR merge: first row of each block's merge-path segment, [blocks + 1]
     int32_t *merge_row_start = nullptr;
 };
@@ -72,6 +76,7 @@ struct spmv_handle {
     spmv_stats stats{};
     std::vector<int64_t> hist;      // host copy of the row-length histogram
     int64_t tail_nnz = 0;
+    int64_t sell_slots = 0;
     int64_t num_tiles = 0;
     int64_t device_bytes = 0;
     spmv::DevArrays a;
@@ -253,6 +258,12 @@ hipError_t launch_jds_counts(int32_t R, int32_t W, const int32_t *jds_len, int32
 hipError_t launch_jds_fill(int32_t nnz, int32_t W, const int32_t *iter_ptr,
                            const int32_t *perm, const int32_t *rp, const int32_t *col,
                            const float *val, int32_t *jds_col, float *jds_val, hipStream_t s);
+// Sectioned ELL: slots of each section of 64 sorted rows, and the fill.
+hipError_t launch_sell_sizes(int32_t R, const int32_t *jds_len, int32_t *sizes, hipStream_t s);
+hipError_t launch_sell_fill(int32_t R, int32_t nsect, int32_t slots, const int32_t *sect_ptr,
+                            const int32_t *jds_len, const int32_t *perm, const int32_t *rp,
+                            const int32_t *col, const float *val, int32_t *sell_col,
+                            float *sell_val, hipStream_t s);
 hipError_t launch_jds_chunks(int32_t R, int32_t depth, const int32_t *jds_len,
                              int32_t *chunks, hipStream_t s);
 hipError_t launch_jds_tiles(int32_t groups, int32_t ntiles, const int32_t *tile_off,

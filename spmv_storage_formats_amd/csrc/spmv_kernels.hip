@@ -335,6 +335,71 @@ __global__ __launch_bounds__(kThreads) void k_jds(int32_t R, int32_t ntiles, int
 }
 
 // ---------------------------------------------------------------------------
+// Sectioned ELL, the JDS variant [Regularized formats page, JDS variant
+// section]: section k = 64 consecutive sorted rows, an ELL padded to its own
+// longest row, column-major inside the section: entry t of its row i at
+// sect_ptr[k] + t*m_k + i.  One wave per (section, chunk of `depth` padded
+// columns); a step reads one contiguous run of m_k words, with no per-column
+// pointer load (unlike JDS); the next U columns are loaded before the current
+// U gathers.  Padding lanes (t >= the row's length) load nothing.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_sell(int32_t R, int32_t ntiles, int32_t depth,
+                                                   const int2 *__restrict__ tiles,
+                                                   const int32_t *__restrict__ sell_len,
+                                                   const int32_t *__restrict__ sect_ptr,
+                                                   const int32_t *__restrict__ perm,
+                                                   const int32_t *__restrict__ col,
+                                                   const float *__restrict__ val,
+                                                   const float *__restrict__ x,
+                                                   float *__restrict__ y) {
+    const int64_t tile = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) / kWave;
+    if (tile >= ntiles) return;
+    const int lane = __lane_id();
+    const int2 gc = tiles[tile];
+    const int k = __builtin_amdgcn_readfirstlane(gc.x);
+    const int chunk = __builtin_amdgcn_readfirstlane(gc.y);
+    const int64_t first = static_cast<int64_t>(k) * kWave;
+    const int32_t m = static_cast<int32_t>(min(static_cast<int64_t>(kWave), R - first));
+    const int64_t s = first + lane;
+    const int32_t len = lane < m ? sell_len[s] : 0;
+    const int32_t width = __builtin_amdgcn_readfirstlane(sell_len[first]);
+    const int64_t base = __builtin_amdgcn_readfirstlane(sect_ptr[k]);
+    const int32_t t0 = chunk * depth;
+    const int32_t t1 = min(t0 + depth, width);
+    constexpr int U = 8;
+    int32_t c[U];
+    float v[U];
+    auto load = [&](int32_t tb, int32_t *cc, float *vv) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int32_t t = tb + u;
+            const bool ok = t < t1 && t < len;
+            const int64_t slot = base + static_cast<int64_t>(t) * m + lane;
+            cc[u] = ok ? ld_nt(col + slot) : 0;
+            vv[u] = ok ? ld_nt(val + slot) : 0.f;
+        }
+    };
+    load(t0, c, v);
+    float sum = 0.f;
+    for (int32_t tb = t0; tb < t1; tb += U) {
+        int32_t cn[U];
+        float vn[U];
+        load(tb + U, cn, vn);
+        float xv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) xv[u] = (tb + u < t1 && tb + u < len) ? x[c[u]] : 0.f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) sum += v[u] * xv[u];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            c[u] = cn[u];
+            v[u] = vn[u];
+        }
+    }
+    if (len > t0) atomic_add_f32(&y[perm[s]], sum);
+}
+
+// ---------------------------------------------------------------------------
 // Merge-path CSR [format-choice article 5.2: merge-based CSR for power-law
 // graphs; "Introduction to sparse computing", parallel efficiency: split by
 // nonzero count, split long rows].  The rows' end markers and the nonzeros
@@ -511,6 +576,14 @@ spmv_status launch_spmv(const spmv_handle *h, const float *x, float *y, hipStrea
             k_jds<<<blocks_of(h->num_tiles * kWave, kThreads), kThreads, 0, s>>>(
                 R, static_cast<int32_t>(h->num_tiles), h->jds_depth, a.jds_tiles, a.jds_len,
                 a.jds_iter_ptr, a.jds_perm, a.jds_col, a.jds_val, x, y);
+            e = hipGetLastError();
+        }
+        break;
+    case SPMV_SELL:
+        if (h->num_tiles > 0) {
+            k_sell<<<blocks_of(h->num_tiles * kWave, kThreads), kThreads, 0, s>>>(
+                R, static_cast<int32_t>(h->num_tiles), h->jds_depth, a.jds_tiles, a.jds_len,
+                a.sell_ptr, a.jds_perm, a.sell_col, a.sell_val, x, y);
             e = hipGetLastError();
         }
         break;

@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 import spmv_storage_formats_amd as spmv  # noqa: E402
 
 ALL_FORMATS = ["coo_atomic", "coo_segmented", "csr_scalar", "csr_vector", "ell", "hyb", "jds",
-               "csr_merge"]
+               "csr_merge", "sell"]
 # formats whose rows are each summed by one lane group with a plain y update
 DETERMINISTIC = ["csr_scalar", "csr_vector", "ell"]
 
@@ -89,6 +89,16 @@ def test_fig14_1_every_format(dev, fmt):
     assert y.cpu().tolist() == [16, 51, 29, 25]
 
 
+def test_fig14_1_sectioned_ell(dev):
+    """Sections of 64 rows on Fig. 14.1: one section of the 4 sorted rows,
+    width 3, pointers [0, 12]; the arrays equal the oracle's."""
+    w = synth.fig14_1()
+    h = build("sell", w, dev)
+    assert h.array("sell_sect_ptr").tolist() == [0, 12]
+    assert h.array("jds_perm").tolist() == [1, 0, 2, 3]
+    check_builder(h, w)
+
+
 def test_fig14_1_printed_arrays(dev):
     """Device builders reproduce the printed ELL and JDS arrays of Fig. 14.1."""
     w = synth.fig14_1()
@@ -141,6 +151,13 @@ def check_builder(h, w, K=None):
         assert np.array_equal(h.array("jds_iter_ptr"), o["iter_ptr"])
         assert np.array_equal(h.array("jds_col"), o["col"])
         assert np.array_equal(bits(h.array("jds_val")), bits(o["val"]))
+    elif fmt == "sell":
+        o = oracle.csr_to_sell(w.row_ptrs, w.col_idx, w.values, 64)
+        assert np.array_equal(h.array("jds_perm"), o["perm"])
+        assert np.array_equal(h.array("jds_len"), o["len"])
+        assert np.array_equal(h.array("sell_sect_ptr"), o["sect_ptr"])
+        assert np.array_equal(h.array("sell_col"), o["col"])
+        assert np.array_equal(bits(h.array("sell_val")), bits(o["val"]))
     st = oracle.row_stats(w.row_ptrs)
     assert np.array_equal(h.array("len_hist"), st["hist"])
     assert (h.info["max_len"], h.info["sum_len_sq"], h.info["empty_rows"]) == \
@@ -190,10 +207,11 @@ def test_csr_vector_lanes(dev, lanes, name):
     assert_rows(run_once(h, x, y0), *ref(name), f"{name} lanes={lanes}")
 
 
+@pytest.mark.parametrize("fmt", ["jds", "sell"])
 @pytest.mark.parametrize("depth", [1, 3, 64, 128, 1000])
-def test_jds_depths(dev, depth):
+def test_jds_depths(dev, depth, fmt):
     w = W("c5s")
-    h = build("jds", w, dev, jds_depth=depth)
+    h = build(fmt, w, dev, jds_depth=depth)
     _, _, _, x, y0 = to_dev(w, dev)
     assert_rows(run_once(h, x, y0), *ref("c5s"), f"jds depth={depth}")
 
@@ -434,7 +452,7 @@ def test_full_size_parity(dev, name, fmt):
 
 @pytest.mark.parametrize("name,fmt", [("c1", "ell"), ("c2", "ell"), ("c3", "ell"),
                                       ("c4", "hyb"), ("c4", "jds"), ("c5", "jds"),
-                                      ("c5", "coo_segmented")])
+                                      ("c5", "coo_segmented"), ("c4", "sell"), ("c5", "sell")])
 def test_full_size_builders_bitexact(dev, name, fmt):
     w = W(name)
     print(f"[case] full builder {name} {fmt}", flush=True)

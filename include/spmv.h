@@ -161,6 +161,21 @@ typedef enum spmv_array {
 
 typedef struct spmv_handle spmv_handle;
 
+/* One candidate timed by spmv_build_tuned. */
+typedef struct spmv_tune_entry {
+    int32_t format;      /* spmv_format tried                                          */
+    int32_t col_blocks;  /* x slices of this candidate (1 = unsplit)                   */
+    int32_t status;      /* SPMV_OK, or why it could not be built (e.g. TOO_LARGE)     */
+    float us;            /* median time of one spmv_run, microseconds (0 if not built) */
+} spmv_tune_entry;
+
+#define SPMV_TUNE_MAX 32
+typedef struct spmv_tune_report {
+    int32_t count;                        /* entries filled                         */
+    int32_t chosen;                       /* index of the fastest entry (-1: none)  */
+    spmv_tune_entry entry[SPMV_TUNE_MAX];
+} spmv_tune_report;
+
 /*
  * spmv_analyze -- input checks and row-length statistics of a CSR matrix.
  *   Checks [COO/CSR, CSR section: rowPtrs[numRows] = nnz; SPGEMM 5.3: row_ptr
@@ -235,6 +250,30 @@ spmv_status spmv_coo_to_csr(int32_t num_rows, int32_t num_cols, int32_t nnz,
                             const float *values_dev, int32_t *row_ptrs_out_dev,
                             int32_t *col_idx_out_dev, float *values_out_dev,
                             int32_t validate, void *stream);
+
+/*
+ * spmv_build_tuned -- the empirical selector [CHOICE 4.3: a tool that times
+ * the formats on the matrix itself and keeps the fastest].
+ *   Tries every concrete format whose bit is set in `format_mask` (bit f for
+ *   spmv_format f, 1..9; 0 = all nine), each unsplit and -- when the matrix
+ *   is one that SPMV_AUTO would cut into x slices -- also sliced.  Each
+ *   candidate that builds is run once to warm up and then `runs` times
+ *   (0: 5) back to back on device scratch vectors (x = 0, y = 0: the kernels
+ *   do the same work for any values), each run timed with HIP events on
+ *   `stream`; its median is its time.  The fastest candidate is returned in
+ *   *out; all others are freed as soon as they lose.  `report` (nullable)
+ *   receives one entry per candidate, including the ones that could not be
+ *   built (status).  A candidate whose device arrays would exceed
+ *   opts->max_bytes (0: 8x the CSR arrays, at least 64 MiB) is reported as
+ *   SPMV_ERR_TOO_LARGE and not built.  Host-synchronous.  Input checks as
+ *   spmv_build (once).
+ *   Fails with the first candidate's error only when no candidate builds.
+ */
+spmv_status spmv_build_tuned(spmv_handle **out, int32_t num_rows, int32_t num_cols,
+                             int32_t nnz, const int32_t *row_ptrs_dev,
+                             const int32_t *col_idx_dev, const float *values_dev,
+                             const spmv_opts *opts, uint32_t format_mask, int32_t runs,
+                             spmv_tune_report *report, void *stream);
 
 /* spmv_build_coo -- spmv_coo_to_csr into temporaries, then spmv_build. */
 spmv_status spmv_build_coo(spmv_handle **out, spmv_format format, int32_t num_rows,

@@ -21,7 +21,8 @@ import threading
 import numpy as np
 
 __all__ = ["SpmvError", "Handle", "FORMATS", "ARRAYS", "load_library", "analyze", "select",
-           "build", "build_coo", "coo_to_csr", "library_path", "declared_functions"]
+           "build", "build_coo", "build_tuned", "coo_to_csr", "library_path",
+           "declared_functions"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_PKG)
@@ -76,6 +77,19 @@ class _Info(ctypes.Structure):
                 ("device_bytes", ctypes.c_int64)]
 
 
+class _TuneEntry(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int32), ("col_blocks", ctypes.c_int32),
+                ("status", ctypes.c_int32), ("us", ctypes.c_float)]
+
+
+TUNE_MAX = 32
+
+
+class _TuneReport(ctypes.Structure):
+    _fields_ = [("count", ctypes.c_int32), ("chosen", ctypes.c_int32),
+                ("entry", _TuneEntry * TUNE_MAX)]
+
+
 _lock = threading.Lock()
 _lib = None
 _vp = ctypes.c_void_p
@@ -117,6 +131,8 @@ def load_library():
                                               _vp, P(_Opts), _vp]),
             "spmv_coo_to_csr": (ctypes.c_int, [_i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                                                _i32, _vp]),
+            "spmv_build_tuned": (ctypes.c_int, [P(_vp), _i32, _i32, _i32, _vp, _vp, _vp, P(_Opts),
+                                                ctypes.c_uint32, _i32, P(_TuneReport), _vp]),
             "spmv_run": (ctypes.c_int, [_vp, _vp, _vp, _vp]),
             "spmv_get_info": (ctypes.c_int, [_vp, P(_Info)]),
             "spmv_array_bytes": (ctypes.c_int, [_vp, ctypes.c_int, P(ctypes.c_size_t)]),
@@ -355,3 +371,34 @@ def coo_to_csr(row_idx, col_idx, values, num_rows: int, num_cols: int, validate:
                                _dev(vo, torch.float32, "out"), 1 if validate else 0,
                                _stream(stream, dev)), "spmv_coo_to_csr")
     return rp, co, vo
+
+
+def build_tuned(row_ptrs, col_idx, values, num_cols: int, *, formats=None, runs: int = 5,
+                hyb_width: int = 0, lanes: int = 0, validate: bool = True, jds_depth: int = 0,
+                stream=None):
+    """Empirical selector: time every candidate format on this matrix, keep the
+    fastest.  Returns (handle, report) where report is a list of dicts
+    {format, col_blocks, status, us} and report[i]["chosen"] marks the winner."""
+    import torch
+    lib = load_library()
+    R = row_ptrs.numel() - 1
+    nnz = col_idx.numel()
+    mask = 0
+    for f in (formats or []):
+        mask |= 1 << _fmt(f)
+    out = ctypes.c_void_p()
+    rep = _TuneReport()
+    o = _opts(hyb_width, lanes, validate, jds_depth, 0, 0)
+    _check(lib.spmv_build_tuned(ctypes.byref(out), R, int(num_cols), nnz,
+                                _dev(row_ptrs, torch.int32, "row_ptrs"),
+                                _dev(col_idx, torch.int32, "col_idx"),
+                                _dev(values, torch.float32, "values", nnz), ctypes.byref(o),
+                                mask, int(runs), ctypes.byref(rep),
+                                _stream(stream, row_ptrs.device)), "spmv_build_tuned")
+    report = []
+    for i in range(rep.count):
+        e = rep.entry[i]
+        report.append({"format": FORMAT_NAMES[e.format], "col_blocks": e.col_blocks,
+                       "status": STATUS.get(e.status, e.status), "us": float(e.us),
+                       "chosen": i == rep.chosen})
+    return Handle(out.value, row_ptrs.device), report

@@ -594,6 +594,105 @@ spmv_status spmv_build(spmv_handle **out, spmv_format fmt, int32_t R, int32_t C,
     return build_csr_impl(out, fmt, R, C, nnz, rp, col, val, o, s, scratch);
 }
 
+spmv_status spmv_build_tuned(spmv_handle **out, int32_t R, int32_t C, int32_t nnz,
+                             const int32_t *rp, const int32_t *col, const float *val,
+                             const spmv_opts *opts, uint32_t format_mask, int32_t runs,
+                             spmv_tune_report *report, void *stream) {
+    if (!out) return SPMV_ERR_INVALID_ARG;
+    *out = nullptr;
+    const spmv_opts o = resolve_opts(opts);
+    if (bad_sizes(R, C, nnz) || !rp || (nnz > 0 && (!col || !val)) || !valid_opts(o) ||
+        runs < 0 || runs > 1000 || (format_mask & ~0x3FEu) != 0)
+        return SPMV_ERR_INVALID_ARG;
+    if (format_mask == 0) format_mask = 0x3FEu;   // formats 1..9
+    if (runs == 0) runs = 5;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Scratch scratch(s);
+    // checks and statistics once; candidates then build without the column pass
+    Analysis an;
+    SPMV_TRY(analyze_csr(R, C, nnz, rp, col, o.validate != 0, true, an, s, scratch));
+    const int32_t auto_slices = choose_col_blocks(an.st, SPMV_AUTO, spmv_opts{});
+    float *x = nullptr, *y = nullptr;
+    SPMV_TRY(scratch.alloc(&x, static_cast<size_t>(std::max(C, 1))));
+    SPMV_TRY(scratch.alloc(&y, static_cast<size_t>(std::max(R, 1))));
+    SPMV_HIP(hipMemsetAsync(x, 0, sizeof(float) * std::max(C, 1), s));
+    SPMV_HIP(hipMemsetAsync(y, 0, sizeof(float) * std::max(R, 1), s));
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    SPMV_HIP(hipEventCreate(&e0));
+    hipError_t ee = hipEventCreate(&e1);
+    if (ee != hipSuccess) {
+        (void)hipEventDestroy(e0);
+        return from_hip(ee);
+    }
+    spmv_tune_report rep{};
+    rep.chosen = -1;
+    HandlePtr best;
+    float best_us = 0.f;
+    spmv_status first_err = SPMV_OK;
+    spmv_status fatal = SPMV_OK;
+    for (int f = SPMV_COO_ATOMIC; f <= SPMV_SELL && fatal == SPMV_OK; ++f) {
+        if (!(format_mask & (1u << f))) continue;
+        for (int variant = 0; variant < 2 && fatal == SPMV_OK; ++variant) {
+            const int32_t K = variant == 0 ? 1 : auto_slices;
+            if (variant == 1 && auto_slices <= 1) continue;
+            if (rep.count >= SPMV_TUNE_MAX) break;
+            spmv_tune_entry &ent = rep.entry[rep.count++];
+            ent.format = f;
+            ent.col_blocks = K;
+            spmv_opts oc = o;
+            oc.validate = 0;
+            oc.col_blocks = K;
+            if (oc.max_bytes == 0) {   // not worth timing: more than 8x the CSR arrays
+                const int64_t csr = 8 * static_cast<int64_t>(nnz) + 4 * (static_cast<int64_t>(R) + 1);
+                oc.max_bytes = std::max<int64_t>(int64_t(64) << 20, 8 * csr);
+            }
+            spmv_handle *raw = nullptr;
+            spmv_status st = build_csr_impl(&raw, static_cast<spmv_format>(f), R, C, nnz, rp,
+                                            col, val, oc, s, scratch);
+            HandlePtr h(raw);
+            ent.status = st;
+            if (st != SPMV_OK) {
+                if (first_err == SPMV_OK) first_err = st;
+                if (st == SPMV_ERR_HIP) fatal = st;   // the device is in trouble: stop
+                continue;
+            }
+            // one warm-up run, then `runs` individually timed runs
+            std::vector<float> t;
+            st = launch_spmv(h.get(), x, y, s);
+            for (int i = 0; i < runs && st == SPMV_OK; ++i) {
+                hipError_t he = hipEventRecord(e0, s);
+                if (he == hipSuccess) st = launch_spmv(h.get(), x, y, s);
+                if (he == hipSuccess && st == SPMV_OK) he = hipEventRecord(e1, s);
+                if (he == hipSuccess && st == SPMV_OK) he = hipEventSynchronize(e1);
+                float ms = 0.f;
+                if (he == hipSuccess && st == SPMV_OK) he = hipEventElapsedTime(&ms, e0, e1);
+                if (he != hipSuccess) st = from_hip(he);
+                t.push_back(ms);
+            }
+            if (st != SPMV_OK) {
+                ent.status = st;
+                fatal = st;
+                continue;
+            }
+            std::sort(t.begin(), t.end());
+            ent.us = 1000.f * t[t.size() / 2];
+            if (!best || ent.us < best_us) {
+                best = std::move(h);
+                best_us = ent.us;
+                rep.chosen = rep.count - 1;
+            }
+        }
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (report) *report = rep;
+    if (fatal != SPMV_OK) return fatal;
+    if (!best) return first_err != SPMV_OK ? first_err : SPMV_ERR_INVALID_ARG;
+    SPMV_HIP(hipStreamSynchronize(s));
+    *out = best.release();
+    return SPMV_OK;
+}
+
 spmv_status spmv_coo_to_csr(int32_t R, int32_t C, int32_t nnz, const int32_t *ri,
                             const int32_t *ci, const float *v, int32_t *rp_out, int32_t *c_out,
                             float *v_out, int32_t validate, void *stream) {

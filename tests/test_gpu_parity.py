@@ -491,3 +491,28 @@ def test_full_size_power_law_slices(dev, fmt):
     h = build(fmt, w, dev, col_blocks=8)
     _, _, _, x, y0 = to_dev(w, dev)
     assert_rows(run_once(h, x, y0), *ref("c5"), f"c5/{fmt} 8 slices")
+
+
+@pytest.mark.parametrize("name", ["c1s", "c2s", "c4s", "c5s"])
+def test_empirical_selector(dev, name):
+    """The tuned handle is the fastest built candidate, computes y within the
+    bound, and the candidates that cannot exist are reported as refused."""
+    w = W(name)
+    rp, ci, v, x, y0 = to_dev(w, dev)
+    h, rep = spmv.build_tuned(rp, ci, v, w.num_cols, runs=3)
+    built = [e for e in rep if e["status"] == "SPMV_OK"]
+    chosen = [e for e in rep if e["chosen"]]
+    assert len(chosen) == 1 and chosen[0]["us"] == min(e["us"] for e in built)
+    assert h.format == chosen[0]["format"] and h.info["col_blocks"] == chosen[0]["col_blocks"]
+    assert {e["format"] for e in rep} >= set(ALL_FORMATS)
+    if name in ("c5s",):
+        assert any(e["format"] == "ell" and e["status"] == "SPMV_ERR_TOO_LARGE" for e in rep)
+    assert_rows(run_once(h, x, y0), *ref(name), f"tuned {name}")
+
+
+def test_empirical_selector_mask(dev):
+    w = W("c2s")
+    rp, ci, v, _, _ = to_dev(w, dev)
+    h, rep = spmv.build_tuned(rp, ci, v, w.num_cols, formats=["csr_scalar", "jds"], runs=2)
+    assert {e["format"] for e in rep} == {"csr_scalar", "jds"}
+    assert h.format in ("csr_scalar", "jds")

@@ -96,8 +96,9 @@ typedef struct spmv_opts {
     int32_t col_blocks;     /* x slices (column blocks), each run as its own pass over y.
                                0: automatic for SPMV_AUTO builds (slices of at most 4 MiB
                                of x when x exceeds the 4 MiB L2 of one XCD and the rows'
-                               columns are scattered; otherwise 1).  1: never split.
-                               K > 1: exactly K slices, any format.                        */
+                               columns are scattered; otherwise 1); an automatic sliced
+                               build runs every slice as merge-path CSR.  1: never split.
+                               K > 1: exactly K slices, each in the requested format.     */
     int32_t reserved;       /* must be 0                                                   */
     int64_t max_bytes;      /* > 0: refuse (SPMV_ERR_TOO_LARGE) a format whose device
                                arrays would exceed this many bytes.                        */

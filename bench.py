@@ -104,6 +104,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--col-blocks", type=int, default=0,
                     help="x slices for every build (0 = library default)")
+    ap.add_argument("--cg", action="store_true",
+                    help="also solve A x = b by conjugate gradient on the 256x256 Laplacian "
+                         "(b = A x_true) and report the per-iteration cost")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 512 MiB device copy 5 times (reads 512 MiB, writes "
                          "512 MiB per launch) to scale PMC byte counters")
@@ -227,6 +230,8 @@ def main():
                      "traffic": traffic, "bytes_per_launch_alg": B},
         "formats": per_format,
     }
+    if args.cg:
+        result["cg"] = cg_section(spmv, torch, oracle, synth, dev, flush_buf)
     if args.calibrate_copy:
         n = 512 << 20
         src = torch.ones(n // 4, dtype=torch.float32, device=dev)
@@ -240,6 +245,38 @@ def main():
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def cg_section(spmv, torch, oracle, synth, dev, flush_buf):
+    """Conjugate gradient on the 2-D Laplacian: iterations, time per iteration and
+    the share of it spent in SpMV (the step the pages call the core of the method)."""
+    import numpy as np
+    w = synth.workload("c1")
+    b, _ = oracle.spmv_csr(w.row_ptrs, w.col_idx, w.values, w.x,
+                           np.zeros(w.num_rows, np.float32))
+    bt = torch.from_numpy(b.astype(np.float32)).to(dev)
+    h = spmv.build("auto", torch.from_numpy(w.row_ptrs).to(dev),
+                   torch.from_numpy(w.col_idx).to(dev), torch.from_numpy(w.values).to(dev),
+                   w.num_cols)
+    xg = torch.zeros(w.num_rows, device=dev)
+    h.cg(bt, xg, max_iter=16, rtol=0.0)             # warm-up
+    xg.zero_()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    iters, rel = h.cg(bt, xg, max_iter=5000, rtol=1e-5)
+    torch.cuda.synchronize()
+    total = time.perf_counter() - t0
+    # SpMV alone, warm, on the same handle (the CG loop keeps the matrix resident)
+    xs, ys = torch.ones(w.num_rows, device=dev), torch.zeros(w.num_rows, device=dev)
+    tf, _ = time_format(spmv, torch, h, xs, ys, 50, 5, flush_buf, flush=False)
+    spmv_ms = statistics.median(tf)
+    err = float(np.max(np.abs(xg.cpu().numpy() - w.x)))
+    return {"workload": "laplacian2d_256 (65,536 rows), b = A x_true, x0 = 0, rtol 1e-5",
+            "format": h.format, "iterations": iters, "rel_residual": rel,
+            "max_abs_error": err, "total_ms": round(total * 1e3, 3),
+            "ms_per_iteration": round(total * 1e3 / max(iters, 1), 5),
+            "spmv_ms_warm": round(spmv_ms, 5),
+            "spmv_share": round(spmv_ms * iters / (total * 1e3), 3)}
 
 
 def measured_traffic(key):

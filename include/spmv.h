@@ -295,6 +295,22 @@ spmv_status spmv_build_coo(spmv_handle **out, spmv_format format, int32_t num_ro
  */
 spmv_status spmv_run(const spmv_handle *h, const float *x_dev, float *y_dev, void *stream);
 
+/*
+ * spmv_cg -- conjugate gradient for A x = b, A symmetric positive definite
+ * (square), built in any format [COO/CSR, background: the iterative methods
+ * SpMV serves; for positive-definite A, conjugate gradient evaluates A·X each
+ * iteration and corrects X along the search direction].
+ *   b_dev: fp32[R]; x_dev: fp32[R], the initial guess in, the solution out.
+ *   Stops when ||b - A x|| <= rtol * ||b|| (the recurrence residual, checked
+ *   every 8 iterations, fp64 dot products) or after max_iter iterations
+ *   (rounded up to a multiple of 8 only while unconverged).  *iters and
+ *   *rel_resid report the iterations run and ||r|| / ||b||.  Allocates its
+ *   three work vectors, runs every step on `stream`, host-synchronous.
+ *   Symmetry and definiteness are the caller's promise (not checked).
+ */
+spmv_status spmv_cg(const spmv_handle *h, const float *b_dev, float *x_dev, int32_t max_iter,
+                    float rtol, int32_t *iters, float *rel_resid, void *stream);
+
 spmv_status spmv_get_info(const spmv_handle *h, spmv_info *info_host);
 
 /* Size in bytes of an exportable array (0 if the handle's format has none;

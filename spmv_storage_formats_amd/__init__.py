@@ -134,6 +134,8 @@ def load_library():
             "spmv_build_tuned": (ctypes.c_int, [P(_vp), _i32, _i32, _i32, _vp, _vp, _vp, P(_Opts),
                                                 ctypes.c_uint32, _i32, P(_TuneReport), _vp]),
             "spmv_run": (ctypes.c_int, [_vp, _vp, _vp, _vp]),
+            "spmv_cg": (ctypes.c_int, [_vp, _vp, _vp, _i32, ctypes.c_float, P(_i32),
+                                       P(ctypes.c_float), _vp]),
             "spmv_get_info": (ctypes.c_int, [_vp, P(_Info)]),
             "spmv_array_bytes": (ctypes.c_int, [_vp, ctypes.c_int, P(ctypes.c_size_t)]),
             "spmv_export": (ctypes.c_int, [_vp, ctypes.c_int, _vp, ctypes.c_size_t]),
@@ -279,6 +281,20 @@ class Handle:
         _check(load_library().spmv_run(self._ptr, xp, yp, _stream(stream, y.device)),
                "spmv_run")
         return y
+
+    def cg(self, b, x, max_iter: int = 1000, rtol: float = 1e-6, stream=None):
+        """Conjugate gradient for A x = b (A square, symmetric positive definite).
+        x holds the initial guess and receives the solution.  Returns
+        (iterations, ||b - A x|| / ||b|| of the recurrence)."""
+        import torch
+        bp = _dev(b, torch.float32, "b", self.num_rows)
+        xp = _dev(x, torch.float32, "x", self.num_rows)
+        it = _i32()
+        rr = ctypes.c_float()
+        _check(load_library().spmv_cg(self._ptr, bp, xp, int(max_iter), float(rtol),
+                                      ctypes.byref(it), ctypes.byref(rr),
+                                      _stream(stream, x.device)), "spmv_cg")
+        return it.value, rr.value
 
     def array(self, name: str) -> np.ndarray:
         """Copy one of the handle's arrays to a numpy array (bit-exact)."""

@@ -281,4 +281,9 @@ hipError_t launch_merge_partition(int32_t R, int32_t nnz, const int32_t *rp, int
 // spmv_kernels.hip: y <- A x + y for the handle's format
 spmv_status launch_spmv(const spmv_handle *h, const float *x, float *y, hipStream_t s);
 
+// cg.hip: conjugate gradient on a square handle (host-synchronous)
+spmv_status conjugate_gradient(const spmv_handle *A, const float *b, float *x, int32_t max_iter,
+                               float rtol, int32_t *iters, float *rel_resid, hipStream_t s,
+                               Scratch &scratch);
+
 }  // namespace spmv

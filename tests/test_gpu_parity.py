@@ -516,3 +516,35 @@ def test_empirical_selector_mask(dev):
     h, rep = spmv.build_tuned(rp, ci, v, w.num_cols, formats=["csr_scalar", "jds"], runs=2)
     assert {e["format"] for e in rep} == {"csr_scalar", "jds"}
     assert h.format in ("csr_scalar", "jds")
+
+
+@pytest.mark.parametrize("fmt", ["ell", "csr_vector", "csr_merge", "sell"])
+@pytest.mark.parametrize("name", ["c1s", "c1"])
+def test_conjugate_gradient(dev, fmt, name):
+    """CG on the 5-point Laplacian (symmetric positive definite) recovers a
+    known solution: b = A x_true (fp64 oracle product), x0 = 0.  The final
+    true residual is checked with the oracle's exact SpMV."""
+    w = W(name)
+    x_true = w.x.astype(np.float64)
+    b, _ = oracle.spmv_csr(w.row_ptrs, w.col_idx, w.values, w.x, np.zeros(w.num_rows, np.float32))
+    b32 = b.astype(np.float32)
+    h = build(fmt, w, dev)
+    x = torch.zeros(w.num_rows, device=dev)
+    rtol = 1e-5
+    iters, rel = h.cg(torch.from_numpy(b32).to(dev), x, max_iter=5000, rtol=rtol)
+    assert rel <= rtol and 0 < iters < 5000
+    xs = x.cpu().numpy()
+    ax, _ = oracle.spmv_csr(w.row_ptrs, w.col_idx, w.values, xs, -b32)   # A x - b in fp64
+    assert np.linalg.norm(ax) / np.linalg.norm(b32.astype(np.float64)) <= 10 * rtol
+    # condition number of the n x n Laplacian ~ (2n/pi)^2
+    n = int(round(np.sqrt(w.num_rows)))
+    kappa = (2 * n / np.pi) ** 2
+    assert np.max(np.abs(xs - x_true)) <= 10 * kappa * rtol
+
+
+def test_conjugate_gradient_rejects_rectangular(dev):
+    rng = np.random.default_rng(1)
+    w = synth.small_random(rng, 5, 7, max_len=3)
+    h = build("csr_scalar", w, dev)
+    with pytest.raises(spmv.SpmvError):
+        h.cg(torch.zeros(5, device=dev), torch.zeros(5, device=dev))

@@ -105,8 +105,8 @@ def main():
     ap.add_argument("--col-blocks", type=int, default=0,
                     help="x slices for every build (0 = library default)")
     ap.add_argument("--cg", action="store_true",
-                    help="also solve A x = b by conjugate gradient on the 256x256 Laplacian "
-                         "(b = A x_true) and report the per-iteration cost")
+                    help="also run conjugate gradient on the 256^2 and 2048^2 Laplacians "
+                         "and report the per-iteration cost")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 512 MiB device copy 5 times (reads 512 MiB, writes "
                          "512 MiB per launch) to scale PMC byte counters")
@@ -248,35 +248,54 @@ def main():
 
 
 def cg_section(spmv, torch, oracle, synth, dev, flush_buf):
-    """Conjugate gradient on the 2-D Laplacian: iterations, time per iteration and
-    the share of it spent in SpMV (the step the pages call the core of the method)."""
+    """Conjugate gradient on 2-D Laplacians: iterations, time per iteration and
+    the share of it spent in SpMV (the step the pages call the core of the
+    method).  The 256^2 grid is solved to rtol 1e-5 from b = A x_true; the
+    2048^2 grid (4.2M rows) runs a fixed 200 iterations to time the
+    bandwidth-bound regime."""
     import numpy as np
-    w = synth.workload("c1")
-    b, _ = oracle.spmv_csr(w.row_ptrs, w.col_idx, w.values, w.x,
-                           np.zeros(w.num_rows, np.float32))
-    bt = torch.from_numpy(b.astype(np.float32)).to(dev)
-    h = spmv.build("auto", torch.from_numpy(w.row_ptrs).to(dev),
-                   torch.from_numpy(w.col_idx).to(dev), torch.from_numpy(w.values).to(dev),
-                   w.num_cols)
-    xg = torch.zeros(w.num_rows, device=dev)
-    h.cg(bt, xg, max_iter=16, rtol=0.0)             # warm-up
-    xg.zero_()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    iters, rel = h.cg(bt, xg, max_iter=5000, rtol=1e-5)
-    torch.cuda.synchronize()
-    total = time.perf_counter() - t0
-    # SpMV alone, warm, on the same handle (the CG loop keeps the matrix resident)
-    xs, ys = torch.ones(w.num_rows, device=dev), torch.zeros(w.num_rows, device=dev)
-    tf, _ = time_format(spmv, torch, h, xs, ys, 50, 5, flush_buf, flush=False)
-    spmv_ms = statistics.median(tf)
-    err = float(np.max(np.abs(xg.cpu().numpy() - w.x)))
-    return {"workload": "laplacian2d_256 (65,536 rows), b = A x_true, x0 = 0, rtol 1e-5",
-            "format": h.format, "iterations": iters, "rel_residual": rel,
-            "max_abs_error": err, "total_ms": round(total * 1e3, 3),
-            "ms_per_iteration": round(total * 1e3 / max(iters, 1), 5),
-            "spmv_ms_warm": round(spmv_ms, 5),
-            "spmv_share": round(spmv_ms * iters / (total * 1e3), 3)}
+    out = []
+    for n, fixed in ((256, 0), (2048, 200)):
+        w = synth.laplacian2d(n)
+        b, _ = oracle.spmv_csr(w.row_ptrs, w.col_idx, w.values, w.x,
+                               np.zeros(w.num_rows, np.float32))
+        bt = torch.from_numpy(b.astype(np.float32)).to(dev)
+        h = spmv.build("auto", torch.from_numpy(w.row_ptrs).to(dev),
+                       torch.from_numpy(w.col_idx).to(dev), torch.from_numpy(w.values).to(dev),
+                       w.num_cols)
+        xg = torch.zeros(w.num_rows, device=dev)
+        h.cg(bt, xg, max_iter=16, rtol=0.0)             # warm-up
+        xg.zero_()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        if fixed:
+            iters, rel = h.cg(bt, xg, max_iter=fixed, rtol=0.0)
+        else:
+            iters, rel = h.cg(bt, xg, max_iter=5000, rtol=1e-5)
+        torch.cuda.synchronize()
+        total = time.perf_counter() - t0
+        xs, ys = torch.ones(w.num_rows, device=dev), torch.zeros(w.num_rows, device=dev)
+        tf, _ = time_format(spmv, torch, h, xs, ys, 50, 5, flush_buf, flush=False)
+        spmv_ms = statistics.median(tf)
+        per_it = total * 1e3 / max(iters, 1)
+        # algorithmic bytes per iteration: the SpMV's plus 48 B per row of vector
+        # traffic (p.Ap reads 8; the x, r update reads 16 and writes 8; the new
+        # direction reads 8 and writes 8)
+        it_bytes = alg_bytes(w.num_rows, w.num_cols, w.nnz) + 48 * w.num_rows
+        entry = {"workload": f"laplacian2d_{n} ({w.num_rows:,} rows, {w.nnz:,} nnz), "
+                             f"b = A x_true, x0 = 0, "
+                             + (f"{fixed} iterations" if fixed else "rtol 1e-5"),
+                 "format": h.format, "iterations": iters, "rel_residual": rel,
+                 "total_ms": round(total * 1e3, 3), "ms_per_iteration": round(per_it, 5),
+                 "spmv_ms_warm": round(spmv_ms, 5),
+                 "spmv_share": round(spmv_ms / per_it, 3),
+                 "alg_bytes_per_iteration": it_bytes,
+                 "gbs_per_iteration": round(it_bytes / (per_it * 1e-3) / 1e9, 1)}
+        if not fixed:
+            entry["max_abs_error"] = float(np.max(np.abs(xg.cpu().numpy() - w.x)))
+        out.append(entry)
+        h.close()
+    return out
 
 
 def measured_traffic(key):
@@ -298,13 +317,14 @@ def measured_traffic(key):
 
 
 def kernel_source_sha():
+    """Hash of the sources the SpMV kernels are compiled from (the kernels
+    file and the shared header); builders and CG live elsewhere."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "spmv_storage_formats_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(fh.read())
+    for f in ("internal.h", "spmv_kernels.hip"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()[:16]
 
 

@@ -301,10 +301,10 @@ spmv_status spmv_run(const spmv_handle *h, const float *x_dev, float *y_dev, voi
  * SpMV serves; for positive-definite A, conjugate gradient evaluates A·X each
  * iteration and corrects X along the search direction].
  *   b_dev: fp32[R]; x_dev: fp32[R], the initial guess in, the solution out.
- *   Stops when ||b - A x|| <= rtol * ||b|| (the recurrence residual, checked
- *   every 8 iterations, fp64 dot products) or after max_iter iterations
- *   (rounded up to a multiple of 8 only while unconverged).  *iters and
- *   *rel_resid report the iterations run and ||r|| / ||b||.  Allocates its
+ *   Stops when ||b - A x|| <= rtol * ||b|| (the recurrence residual, fp64
+ *   dot products, tested every 8 iterations, so up to 7 iterations may run
+ *   past the first that meets it) or after max_iter iterations, never more.
+ *   *iters and *rel_resid report the iterations run and ||r|| / ||b||.  Allocates its
  *   three work vectors, runs every step on `stream`, host-synchronous.
  *   Symmetry and definiteness are the caller's promise (not checked).
  */

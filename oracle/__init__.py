@@ -76,6 +76,8 @@ def _load():
         "orc_hyb_width": (_i64, [_i64, _i64, _i64p]),
         "orc_vector_lanes": (_i64, [_i64, _i64]),
         "orc_select": (None, [_i64, _i64, _i64, _i64p, _i64, _i64, _i64p]),
+        "orc_cg": (ctypes.c_int, [_i64, _i32p, _i32p, _f32p, _f64p, _f64p, _i64,
+                                  ctypes.c_double, _f64p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -273,3 +275,16 @@ def select(num_rows, nnz, hist, hyb_width_override: int = 0, lanes_override: int
     out = np.zeros(3, np.int64)
     _load().orc_select(num_rows, nnz, h.shape[0] - 1, h, hyb_width_override, lanes_override, out)
     return FMT_NAMES[int(out[0])], int(out[1]), int(out[2])
+
+
+# ------------------------------------------------------------------ CG
+
+def cg(row_ptrs, col_idx, values, b, x0=None, max_iter=1000, rtol=1e-6):
+    """Conjugate gradient for A x = b in fp64.  Returns (x, iterations, ||r||/||b||)."""
+    rp = _i32(row_ptrs)
+    R = rp.shape[0] - 1
+    x = (np.zeros(R, np.float64) if x0 is None else np.array(x0, np.float64, copy=True))
+    out = np.zeros(2, np.float64)
+    _load().orc_cg(R, rp, _i32(col_idx), _f32(values), np.ascontiguousarray(b, np.float64), x,
+                   int(max_iter), float(rtol), out)
+    return x, int(out[0]), float(out[1])

@@ -511,3 +511,78 @@ int orc_csr_to_sell(int64_t R, const int32_t *row_ptrs, const int32_t *col_idx,
     free(len);
     return ORC_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Conjugate gradient [P1 background: for positive-definite A the iterative  */
+/* method guesses X, evaluates A*X + Y, tests how close it is to zero and    */
+/* corrects X along the gradient].  The system here is A x = b (Y = -b), and */
+/* the correction is the conjugate-gradient one of Hestenes and Stiefel:     */
+/*                                                                          */
+/*   r = b - A x;  p = r                                                    */
+/*   repeat:  stop if ||r|| <= rtol * ||b||  (or max_iter steps done)        */
+/*            alpha = (r.r) / (p.Ap);  x = x + alpha p;  r = r - alpha Ap    */
+/*            beta  = (r'.r') / (r.r); p = r' + beta p                       */
+/*                                                                          */
+/* Everything in fp64 (the fp32 values widened).  alpha is 0 when p.Ap = 0   */
+/* and beta is 0 when r.r = 0, so an exactly solved system stays put.        */
+/* out[0] = iterations run, out[1] = ||r|| / ||b|| (||r|| when b = 0).       */
+/* ------------------------------------------------------------------------ */
+
+static void orc_csr_apply(int64_t R, const int32_t *row_ptrs, const int32_t *col_idx,
+                          const float *values, const double *v, double *out)
+{
+    for (int64_t r = 0; r < R; ++r) {
+        double s = 0.0;
+        for (int64_t i = row_ptrs[r]; i < row_ptrs[r + 1]; ++i)
+            s += (double)values[i] * v[col_idx[i]];
+        out[r] = s;
+    }
+}
+
+static double orc_dot(int64_t n, const double *a, const double *b)
+{
+    double s = 0.0;
+    for (int64_t i = 0; i < n; ++i)
+        s += a[i] * b[i];
+    return s;
+}
+
+int orc_cg(int64_t R, const int32_t *row_ptrs, const int32_t *col_idx, const float *values,
+           const double *b, double *x, int64_t max_iter, double rtol, double *out)
+{
+    double *r = (double *)malloc(sizeof(double) * (size_t)(R > 0 ? R : 1));
+    double *p = (double *)malloc(sizeof(double) * (size_t)(R > 0 ? R : 1));
+    double *ap = (double *)malloc(sizeof(double) * (size_t)(R > 0 ? R : 1));
+    if (!r || !p || !ap) {
+        free(r); free(p); free(ap);
+        return ORC_ERR_INVALID_ARG;
+    }
+    orc_csr_apply(R, row_ptrs, col_idx, values, x, ap);
+    for (int64_t i = 0; i < R; ++i) {
+        r[i] = b[i] - ap[i];
+        p[i] = r[i];
+    }
+    const double bnorm = sqrt(orc_dot(R, b, b));
+    const double target = rtol * (bnorm > 0.0 ? bnorm : 1.0);
+    double rr = orc_dot(R, r, r);
+    int64_t k = 0;
+    while (k < max_iter && sqrt(rr) > target) {
+        orc_csr_apply(R, row_ptrs, col_idx, values, p, ap);
+        const double pap = orc_dot(R, p, ap);
+        const double alpha = pap != 0.0 ? rr / pap : 0.0;
+        for (int64_t i = 0; i < R; ++i) {
+            x[i] += alpha * p[i];
+            r[i] -= alpha * ap[i];
+        }
+        const double rr_new = orc_dot(R, r, r);
+        const double beta = rr != 0.0 ? rr_new / rr : 0.0;
+        for (int64_t i = 0; i < R; ++i)
+            p[i] = r[i] + beta * p[i];
+        rr = rr_new;
+        ++k;
+    }
+    out[0] = (double)k;
+    out[1] = bnorm > 0.0 ? sqrt(rr) / bnorm : sqrt(rr);
+    free(r); free(p); free(ap);
+    return ORC_OK;
+}

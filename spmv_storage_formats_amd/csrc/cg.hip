@@ -4,12 +4,18 @@
 // guesses X, evaluates A·X, and corrects X along the gradient; the SpMV is
 // the most expensive step of each iteration).
 //
-// Per iteration: Ap = A p (the handle's spmv, into a zeroed Ap), pAp = p·Ap,
-// alpha = rr / pAp, x += alpha p, r -= alpha Ap (fused with the partial sums
-// of r·r), beta = rr_new / rr, p = r + beta p.  Dot products reduce in fp64
-// (per-block partials, then one block); alpha and beta are computed on the
-// device from device scalars, so an iteration never waits on the host.  The
-// host reads r·r every kCheckEvery iterations to test convergence.
+// Per iteration, three launches besides the handle's SpMV:
+//   Ap = A p                         the handle's spmv, into an Ap already zero
+//   k_dot:          partials of p·Ap
+//   k_cg_update:    alpha = rr / pAp; x += alpha p; r -= alpha Ap; partials of r'·r'
+//   k_cg_direction: beta = r'·r' / rr; p = r' + beta p; Ap = 0
+// Dot products are fp64 per-block partials.  A kernel that needs a dot product
+// adds the partials itself, every block in the same order, so all blocks agree
+// bit for bit and the whole solve is deterministic when the SpMV is; no grid-
+// wide synchronisation or atomics are needed (the launch boundary orders the
+// partials' writes before their reads).  rr partials alternate between two
+// buffers.  The host adds the rr partials every kCheckEvery iterations to test
+// convergence.
 #include <cmath>
 #include <vector>
 
@@ -19,21 +25,27 @@ namespace spmv {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kDotBlocks = 1024;
+constexpr int kDotBlocks = 1024;   // partials per dot product (grid of the dot kernels)
 constexpr int kCheckEvery = 8;
 
-// device scalars
-enum { kRR = 0, kPAP = 1, kRRNew = 2, kBB = 3, kNumScalars = 4 };
-
-__device__ inline double block_sum(double v, double *lds) {
+// Sum over the block of one double per thread; the result is returned to
+// every thread.
+__device__ inline double block_sum_all(double v, double *lds) {
     for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
     const int w = threadIdx.x / kWave;
+    __syncthreads();   // lds may still be read from a previous call
     if (__lane_id() == 0) lds[w] = v;
     __syncthreads();
     double t = 0.0;
-    if (threadIdx.x == 0)
-        for (int i = 0; i < kThreads / kWave; ++i) t += lds[i];
-    return t;   // valid in thread 0
+    for (int i = 0; i < kThreads / kWave; ++i) t += lds[i];
+    return t;
+}
+
+// part[0..np) added in a fixed order: the same value in every block.
+__device__ inline double sum_partials(const double *__restrict__ part, int np, double *lds) {
+    double s = 0.0;
+    for (int i = threadIdx.x; i < np; i += kThreads) s += part[i];
+    return block_sum_all(s, lds);
 }
 
 __global__ __launch_bounds__(kThreads) void k_fill(int32_t n, float v, float *__restrict__ a) {
@@ -41,53 +53,59 @@ __global__ __launch_bounds__(kThreads) void k_fill(int32_t n, float v, float *__
     if (i < n) a[i] = v;
 }
 
-// partial[b] = sum over the block's grid-stride share of a[i] * b[i]
-__global__ __launch_bounds__(kThreads) void k_dot_partial(int32_t n, const float *__restrict__ a,
-                                                          const float *__restrict__ b,
-                                                          double *__restrict__ partial) {
+// part[block] = the block's grid-stride share of a·b
+__global__ __launch_bounds__(kThreads) void k_dot(int32_t n, const float *__restrict__ a,
+                                                  const float *__restrict__ b,
+                                                  double *__restrict__ part) {
     __shared__ double lds[kThreads / kWave];
     double s = 0.0;
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n;
          i += static_cast<int64_t>(gridDim.x) * kThreads)
         s += static_cast<double>(a[i]) * static_cast<double>(b[i]);
-    const double t = block_sum(s, lds);
-    if (threadIdx.x == 0) partial[blockIdx.x] = t;
+    const double t = block_sum_all(s, lds);
+    if (threadIdx.x == 0) part[blockIdx.x] = t;
 }
 
-// scalars[slot] = sum of partial[0..np)
-__global__ __launch_bounds__(kThreads) void k_dot_final(int32_t np, const double *__restrict__ partial,
-                                                        double *__restrict__ scalars, int slot) {
-    __shared__ double lds[kThreads / kWave];
-    double s = 0.0;
-    for (int i = threadIdx.x; i < np; i += kThreads) s += partial[i];
-    const double t = block_sum(s, lds);
-    if (threadIdx.x == 0) scalars[slot] = t;
-}
-
-// r = b - Ap (Ap holds A x), p = r
+// r = b - Ap (Ap holds A x), p = r, Ap = 0; partials of r·r and b·b
 __global__ __launch_bounds__(kThreads) void k_cg_start(int32_t n, const float *__restrict__ b,
-                                                       const float *__restrict__ ax,
+                                                       float *__restrict__ ap,
                                                        float *__restrict__ r,
-                                                       float *__restrict__ p) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-    if (i < n) {
-        const float v = b[i] - ax[i];
+                                                       float *__restrict__ p,
+                                                       double *__restrict__ part_rr,
+                                                       double *__restrict__ part_bb) {
+    __shared__ double lds[kThreads / kWave];
+    double srr = 0.0, sbb = 0.0;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * kThreads) {
+        const float bi = b[i];
+        const float v = bi - ap[i];
         r[i] = v;
         p[i] = v;
+        ap[i] = 0.f;
+        srr += static_cast<double>(v) * static_cast<double>(v);
+        sbb += static_cast<double>(bi) * static_cast<double>(bi);
+    }
+    const double trr = block_sum_all(srr, lds);
+    const double tbb = block_sum_all(sbb, lds);
+    if (threadIdx.x == 0) {
+        part_rr[blockIdx.x] = trr;
+        part_bb[blockIdx.x] = tbb;
     }
 }
 
-// alpha = rr / pAp (0 when pAp == 0); x += alpha p; r -= alpha Ap;
-// partial sums of the new r·r
-__global__ __launch_bounds__(kThreads) void k_cg_update(int32_t n, const double *__restrict__ sc,
+// alpha = rr / pAp (0 when pAp == 0); x += alpha p; r -= alpha Ap; partials of r·r
+__global__ __launch_bounds__(kThreads) void k_cg_update(int32_t n, int np,
+                                                        const double *__restrict__ part_rr,
+                                                        const double *__restrict__ part_pap,
                                                         const float *__restrict__ p,
                                                         const float *__restrict__ ap,
                                                         float *__restrict__ x,
                                                         float *__restrict__ r,
-                                                        double *__restrict__ partial) {
+                                                        double *__restrict__ part_rr_new) {
     __shared__ double lds[kThreads / kWave];
-    const double pap = sc[kPAP];
-    const float alpha = pap != 0.0 ? static_cast<float>(sc[kRR] / pap) : 0.f;
+    const double rr = sum_partials(part_rr, np, lds);
+    const double pap = sum_partials(part_pap, np, lds);
+    const float alpha = pap != 0.0 ? static_cast<float>(rr / pap) : 0.f;
     double s = 0.0;
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n;
          i += static_cast<int64_t>(gridDim.x) * kThreads) {
@@ -96,40 +114,37 @@ __global__ __launch_bounds__(kThreads) void k_cg_update(int32_t n, const double 
         r[i] = ri;
         s += static_cast<double>(ri) * static_cast<double>(ri);
     }
-    const double t = block_sum(s, lds);
-    if (threadIdx.x == 0) partial[blockIdx.x] = t;
+    const double t = block_sum_all(s, lds);
+    if (threadIdx.x == 0) part_rr_new[blockIdx.x] = t;
 }
 
-// beta = rr_new / rr; p = r + beta p; Ap = 0 for the next SpMV; (rr <- rr_new
-// is done by k_cg_roll after every block has read rr)
-__global__ __launch_bounds__(kThreads) void k_cg_direction(int32_t n, const double *__restrict__ sc,
+// beta = rr_new / rr (0 when rr == 0); p = r + beta p; Ap = 0 for the next SpMV
+__global__ __launch_bounds__(kThreads) void k_cg_direction(int32_t n, int np,
+                                                           const double *__restrict__ part_rr,
+                                                           const double *__restrict__ part_rr_new,
                                                            const float *__restrict__ r,
                                                            float *__restrict__ p,
                                                            float *__restrict__ ap) {
-    const double rr = sc[kRR];
-    const float beta = rr != 0.0 ? static_cast<float>(sc[kRRNew] / rr) : 0.f;
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-    if (i < n) {
+    __shared__ double lds[kThreads / kWave];
+    const double rr = sum_partials(part_rr, np, lds);
+    const double rr_new = sum_partials(part_rr_new, np, lds);
+    const float beta = rr != 0.0 ? static_cast<float>(rr_new / rr) : 0.f;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * kThreads) {
         p[i] = r[i] + beta * p[i];
         ap[i] = 0.f;
     }
 }
 
-__global__ void k_cg_roll(double *__restrict__ sc) {
-    if (threadIdx.x == 0) sc[kRR] = sc[kRRNew];
-}
-
-unsigned dot_blocks(int32_t n) {
-    unsigned g = grid_for(n, kThreads);
-    return g > kDotBlocks ? kDotBlocks : g;
-}
-
-hipError_t dot(int32_t n, const float *a, const float *b, double *partial, double *sc, int slot,
-               hipStream_t s) {
-    const unsigned g = dot_blocks(n);
-    k_dot_partial<<<g, kThreads, 0, s>>>(n, a, b, partial);
-    k_dot_final<<<1, kThreads, 0, s>>>(static_cast<int32_t>(g), partial, sc, slot);
-    return hipGetLastError();
+// Host sum of device partials, in block order.
+spmv_status host_sum(const double *part, int np, std::vector<double> &buf, double *out,
+                     hipStream_t s) {
+    SPMV_HIP(hipMemcpyAsync(buf.data(), part, sizeof(double) * np, hipMemcpyDeviceToHost, s));
+    SPMV_HIP(hipStreamSynchronize(s));
+    double t = 0.0;
+    for (int i = 0; i < np; ++i) t += buf[i];
+    *out = t;
+    return SPMV_OK;
 }
 
 }  // namespace
@@ -142,49 +157,46 @@ spmv_status conjugate_gradient(const spmv_handle *A, const float *b, float *x, i
     *rel_resid = 0.f;
     if (n == 0) return SPMV_OK;
     float *r = nullptr, *p = nullptr, *ap = nullptr;
-    double *partial = nullptr, *sc = nullptr;
+    double *part = nullptr;   // [pAp | rr slot 0 | rr slot 1 | bb], kDotBlocks each
     SPMV_TRY(scratch.alloc(&r, n));
     SPMV_TRY(scratch.alloc(&p, n));
     SPMV_TRY(scratch.alloc(&ap, n));
-    SPMV_TRY(scratch.alloc(&partial, kDotBlocks));
-    SPMV_TRY(scratch.alloc(&sc, kNumScalars));
+    SPMV_TRY(scratch.alloc(&part, 4 * kDotBlocks));
+    double *part_pap = part, *part_bb = part + 3 * kDotBlocks;
+    double *part_rr[2] = {part + kDotBlocks, part + 2 * kDotBlocks};
     const unsigned gn = grid_for(n, kThreads);
-    const unsigned gd = dot_blocks(n);
-    // Ap = A x (into zeros), r = p = b - A x, rr = r.r, bb = b.b
+    const int np = static_cast<int>(gn < static_cast<unsigned>(kDotBlocks) ? gn : kDotBlocks);
+    std::vector<double> host(kDotBlocks);
+
+    // Ap = A x (into zeros); r = p = b - A x; Ap = 0; partials of r·r and b·b
     k_fill<<<gn, kThreads, 0, s>>>(n, 0.f, ap);
     SPMV_HIP(hipGetLastError());
     SPMV_TRY(launch_spmv(A, x, ap, s));
-    k_cg_start<<<gn, kThreads, 0, s>>>(n, b, ap, r, p);
+    k_cg_start<<<np, kThreads, 0, s>>>(n, b, ap, r, p, part_rr[0], part_bb);
     SPMV_HIP(hipGetLastError());
-    SPMV_HIP(dot(n, r, r, partial, sc, kRR, s));
-    SPMV_HIP(dot(n, b, b, partial, sc, kBB, s));
-    double host[kNumScalars] = {0, 0, 0, 0};
-    SPMV_HIP(hipMemcpyAsync(host, sc, sizeof(host), hipMemcpyDeviceToHost, s));
-    SPMV_HIP(hipStreamSynchronize(s));
-    const double bnorm = std::sqrt(host[kBB]);
+    double bb = 0.0, rr = 0.0;
+    SPMV_TRY(host_sum(part_bb, np, host, &bb, s));
+    SPMV_TRY(host_sum(part_rr[0], np, host, &rr, s));
+    const double bnorm = std::sqrt(bb);
     const double target = static_cast<double>(rtol) * (bnorm > 0.0 ? bnorm : 1.0);
-    double rnorm = std::sqrt(host[kRR]);
+    double rnorm = std::sqrt(rr);
+    int cur = 0;   // part_rr[cur] holds the current r·r partials
     int32_t it = 0;
     while (it < max_iter && rnorm > target) {
         const int32_t batch = std::min(kCheckEvery, max_iter - it);
         for (int32_t k = 0; k < batch; ++k) {
-            k_fill<<<gn, kThreads, 0, s>>>(n, 0.f, ap);
-            SPMV_HIP(hipGetLastError());
             SPMV_TRY(launch_spmv(A, p, ap, s));
-            SPMV_HIP(dot(n, p, ap, partial, sc, kPAP, s));
-            k_cg_update<<<gd, kThreads, 0, s>>>(n, sc, p, ap, x, r, partial);
+            k_dot<<<np, kThreads, 0, s>>>(n, p, ap, part_pap);
+            k_cg_update<<<np, kThreads, 0, s>>>(n, np, part_rr[cur], part_pap, p, ap, x, r,
+                                                part_rr[cur ^ 1]);
+            k_cg_direction<<<np, kThreads, 0, s>>>(n, np, part_rr[cur], part_rr[cur ^ 1], r, p,
+                                                   ap);
             SPMV_HIP(hipGetLastError());
-            k_dot_final<<<1, kThreads, 0, s>>>(static_cast<int32_t>(gd), partial, sc, kRRNew);
-            SPMV_HIP(hipGetLastError());
-            k_cg_direction<<<gn, kThreads, 0, s>>>(n, sc, r, p, ap);
-            SPMV_HIP(hipGetLastError());
-            k_cg_roll<<<1, 64, 0, s>>>(sc);
-            SPMV_HIP(hipGetLastError());
+            cur ^= 1;
         }
         it += batch;
-        SPMV_HIP(hipMemcpyAsync(host, sc, sizeof(host), hipMemcpyDeviceToHost, s));
-        SPMV_HIP(hipStreamSynchronize(s));
-        rnorm = std::sqrt(host[kRR]);
+        SPMV_TRY(host_sum(part_rr[cur], np, host, &rr, s));
+        rnorm = std::sqrt(rr);
         if (!std::isfinite(rnorm)) break;
     }
     *iters = it;

@@ -548,3 +548,89 @@ def test_conjugate_gradient_rejects_rectangular(dev):
     h = build("csr_scalar", w, dev)
     with pytest.raises(spmv.SpmvError):
         h.cg(torch.zeros(5, device=dev), torch.zeros(5, device=dev))
+
+
+def _cg_rhs(w):
+    """b = A x_true rounded to fp32 (the oracle's fp64 product)."""
+    b, _ = oracle.spmv_csr(w.row_ptrs, w.col_idx, w.values, w.x, np.zeros(w.num_rows, np.float32))
+    return b.astype(np.float32)
+
+
+@pytest.mark.parametrize("fmt", ["ell", "csr_merge", "sell", "sliced"])
+@pytest.mark.parametrize("k", [1, 2, 5, 8, 13, 40])
+def test_cg_iterates_match_oracle(dev, fmt, k):
+    """After exactly k iterations (rtol 0) the device's x equals the oracle's
+    fp64 CG iterate within k * kappa * 2^-24 * max|x| (k fp32 steps, each
+    rounding error amplified at most by the condition number kappa)."""
+    w = W("c1s")
+    b32 = _cg_rhs(w)
+    h = build("csr_merge", w, dev, col_blocks=2) if fmt == "sliced" else build(fmt, w, dev)
+    x = torch.zeros(w.num_rows, device=dev)
+    iters, _ = h.cg(torch.from_numpy(b32).to(dev), x, max_iter=k, rtol=0.0)
+    assert iters == k
+    xo, ko, _ = oracle.cg(w.row_ptrs, w.col_idx, w.values, b32.astype(np.float64),
+                          max_iter=k, rtol=0.0)
+    assert ko == k
+    n = int(round(np.sqrt(w.num_rows)))
+    kappa = (2 * (n + 1) / np.pi) ** 2
+    tol = k * kappa * 2.0**-24 * np.max(np.abs(xo))
+    err = np.max(np.abs(x.cpu().numpy().astype(np.float64) - xo))
+    print(f"cg {fmt} k={k}: max err {err:.3e} tol {tol:.3e}")
+    assert err <= tol
+
+
+@pytest.mark.parametrize("name", ["c1s", "c1"])
+def test_cg_iteration_count_matches_oracle(dev, name):
+    """To rtol 1e-5 the device stops at the first multiple of 8 at or past the
+    oracle's iteration count, give or take one check for fp32 rounding."""
+    w = W(name)
+    b32 = _cg_rhs(w)
+    h = build("ell", w, dev)
+    x = torch.zeros(w.num_rows, device=dev)
+    iters, rel = h.cg(torch.from_numpy(b32).to(dev), x, max_iter=5000, rtol=1e-5)
+    _, ko, _ = oracle.cg(w.row_ptrs, w.col_idx, w.values, b32.astype(np.float64),
+                         max_iter=5000, rtol=1e-5)
+    print(f"cg {name}: device {iters} iterations, oracle {ko}")
+    ceil8 = -(-ko // 8) * 8
+    assert iters % 8 == 0 and ceil8 - 8 <= iters <= ceil8 + 8
+
+
+def test_cg_deterministic_with_ell(dev):
+    """ELL's SpMV and the block-ordered fp64 dot products have a fixed summation
+    order: two solves give bit-identical x."""
+    w = W("c1s")
+    b = torch.from_numpy(_cg_rhs(w)).to(dev)
+    h = build("ell", w, dev)
+    xs = []
+    for _ in range(2):
+        x = torch.zeros(w.num_rows, device=dev)
+        h.cg(b, x, max_iter=50, rtol=0.0)
+        xs.append(x.cpu().numpy())
+    assert np.array_equal(xs[0].view(np.uint32), xs[1].view(np.uint32))
+
+
+def test_cg_degenerate_cases(dev):
+    w = W("c1s")
+    h = build("ell", w, dev)
+    b = torch.from_numpy(_cg_rhs(w)).to(dev)
+    # max_iter 0: x untouched, residual of the start reported
+    x = torch.full((w.num_rows,), 0.5, device=dev)
+    iters, rel = h.cg(b, x, max_iter=0, rtol=1e-6)
+    assert iters == 0 and rel > 0 and torch.all(x == 0.5)
+    # b = 0 from x = 0: already solved
+    x = torch.zeros(w.num_rows, device=dev)
+    iters, rel = h.cg(torch.zeros_like(b), x, max_iter=100, rtol=1e-6)
+    assert iters == 0 and rel == 0.0 and not torch.any(x)
+    # 1 x 1 system: one step gives b / a
+    rp = torch.tensor([0, 1], dtype=torch.int32, device=dev)
+    ci = torch.tensor([0], dtype=torch.int32, device=dev)
+    v = torch.tensor([4.0], device=dev)
+    h1 = spmv.build("csr_scalar", rp, ci, v, 1)
+    x = torch.zeros(1, device=dev)
+    iters, rel = h1.cg(torch.tensor([2.0], device=dev), x, max_iter=100, rtol=1e-6)
+    assert x.item() == 0.5 and rel == 0.0 and iters == 8   # checked after 8 steps
+    # empty matrix
+    h0 = spmv.build("ell", torch.zeros(1, dtype=torch.int32, device=dev),
+                    torch.zeros(0, dtype=torch.int32, device=dev),
+                    torch.zeros(0, device=dev), 0)
+    assert h0.cg(torch.zeros(0, device=dev), torch.zeros(0, device=dev)) == (0, 0.0)

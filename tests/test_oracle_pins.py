@@ -520,3 +520,126 @@ def test_sell_padding_on_skewed_shape():
     o = oracle.csr_to_sell(w.row_ptrs, w.col_idx, w.values, 64)
     ell_slots = w.num_rows * int(np.diff(w.row_ptrs).max())
     assert int(o["sect_ptr"][-1]) < 1.1 * w.nnz < 0.01 * ell_slots
+
+
+# ---------------------------------------------------------------- conjugate gradient
+# The pages name conjugate gradient as the iterative method SpMV serves.  The
+# oracle's CG is pinned to facts about CG that do not come from its recurrence:
+# a hand-worked 2x2 system, finite termination, the exact solution from a dense
+# solver, the Krylov-minimisation definition, and the textbook error bound.
+
+def _csr_from_dense(a):
+    R, C = a.shape
+    rp, ci, v = [0], [], []
+    for r in range(R):
+        for c in range(C):
+            if a[r, c] != 0:
+                ci.append(c)
+                v.append(a[r, c])
+        rp.append(len(ci))
+    return (np.array(rp, np.int32), np.array(ci, np.int32), np.array(v, np.float32))
+
+
+def test_cg_two_by_two_by_hand():
+    """A = [[4,1],[1,3]], b = [1,2], x0 = [2,1].  By hand: r0 = b - A x0 = [-8,-3],
+    A r0 = [-35,-17], r0.r0 = 73, r0.A r0 = 331, so x1 = x0 + (73/331) r0 =
+    [78/331, 112/331].  Two steps reach the exact solution (Cramer: [1/11, 7/11]).
+    Catches a wrong alpha, a wrong sign of the residual or of the update."""
+    rp, ci, v = _csr_from_dense(np.array([[4.0, 1.0], [1.0, 3.0]]))
+    x1, k1, _ = oracle.cg(rp, ci, v, [1.0, 2.0], x0=[2.0, 1.0], max_iter=1, rtol=0.0)
+    assert k1 == 1
+    np.testing.assert_allclose(x1, [78 / 331, 112 / 331], rtol=0, atol=1e-15)
+    x2, k2, rel = oracle.cg(rp, ci, v, [1.0, 2.0], x0=[2.0, 1.0], max_iter=2, rtol=0.0)
+    np.testing.assert_allclose(x2, [1 / 11, 7 / 11], rtol=0, atol=1e-15)
+    assert rel < 1e-14
+
+
+def test_cg_one_by_one():
+    rp, ci, v = _csr_from_dense(np.array([[2.5]]))
+    x, k, rel = oracle.cg(rp, ci, v, [5.0], max_iter=10, rtol=1e-12)
+    assert k == 1 and x[0] == 2.0 and rel == 0.0
+
+
+def test_cg_finite_termination_three_eigenvalues():
+    """A diagonal A with 3 distinct eigenvalues: CG's residual is zero after 3
+    steps (its Krylov space has dimension 3), and not after 2.  Catches a wrong
+    beta (steepest descent does not terminate)."""
+    rng = np.random.default_rng(11)
+    d = np.tile([1.0, 3.0, 10.0], 100)
+    n = d.shape[0]
+    rp = np.arange(n + 1, dtype=np.int32)
+    ci = np.arange(n, dtype=np.int32)
+    b = rng.uniform(-1, 1, n)
+    _, _, rel2 = oracle.cg(rp, ci, d.astype(np.float32), b, max_iter=2, rtol=0.0)
+    x3, k3, rel3 = oracle.cg(rp, ci, d.astype(np.float32), b, max_iter=3, rtol=0.0)
+    assert rel2 > 1e-3
+    assert k3 == 3 and rel3 < 1e-12
+    np.testing.assert_allclose(x3, b / d, rtol=1e-12)
+
+
+def test_cg_zero_rhs_and_exact_start():
+    w = synth.laplacian2d(8)
+    x, k, rel = oracle.cg(w.row_ptrs, w.col_idx, w.values, np.zeros(w.num_rows))
+    assert k == 0 and rel == 0.0 and not x.any()
+    a = _dense_from_csr(w.num_rows, w.num_cols, w.row_ptrs, w.col_idx, w.values)
+    xs = np.linalg.solve(a, np.ones(w.num_rows))
+    _, k, _ = oracle.cg(w.row_ptrs, w.col_idx, w.values, np.ones(w.num_rows), x0=xs, rtol=1e-8)
+    assert k == 0
+
+
+@pytest.mark.parametrize("n", [6, 15])
+def test_cg_matches_dense_solve(n):
+    """The 5-point Laplacian (SPD): CG to rtol 1e-12 agrees with numpy's dense
+    solve within the condition-number bound."""
+    w = synth.laplacian2d(n)
+    a = _dense_from_csr(w.num_rows, w.num_cols, w.row_ptrs, w.col_idx, w.values)
+    b = a @ w.x.astype(np.float64)
+    x, k, rel = oracle.cg(w.row_ptrs, w.col_idx, w.values, b, max_iter=5000, rtol=1e-12)
+    assert rel <= 1e-12 and k <= w.num_rows
+    kappa = np.linalg.cond(a)
+    np.testing.assert_allclose(x, np.linalg.solve(a, b), rtol=0, atol=10 * kappa * 1e-12)
+
+
+def test_cg_is_the_krylov_minimiser():
+    """Definition of CG: x_k minimises the A-norm of the error over
+    x0 + span{r0, A r0, ..., A^(k-1) r0}.  The minimiser is computed
+    independently from the normal equations of that basis."""
+    rng = np.random.default_rng(5)
+    n = 40
+    m = rng.normal(size=(n, n))
+    a = m @ m.T + n * np.eye(n)
+    a[np.abs(a) < 3.0] = 0.0                      # sparsify, keeping symmetry
+    a = np.round(a).astype(np.float32).astype(np.float64) + 60 * np.eye(n)
+    assert np.all(np.linalg.eigvalsh(a) > 0)
+    rp, ci, v = _csr_from_dense(a)
+    b = rng.uniform(-1, 1, n)
+    x0 = rng.uniform(-1, 1, n)
+    r0 = b - a @ x0
+    for k in (1, 2, 4):
+        basis = np.stack([np.linalg.matrix_power(a, j) @ r0 for j in range(k)], axis=1)
+        y = np.linalg.solve(basis.T @ a @ basis, basis.T @ r0)
+        want = x0 + basis @ y
+        got, _, _ = oracle.cg(rp, ci, v, b, x0=x0, max_iter=k, rtol=0.0)
+        np.testing.assert_allclose(got, want, rtol=0, atol=1e-9)
+
+
+def test_cg_energy_error_bound():
+    """Textbook bound: ||e_k||_A <= 2 ((sqrt(kappa)-1)/(sqrt(kappa)+1))^k ||e_0||_A,
+    and ||e_k||_A never increases."""
+    w = synth.laplacian2d(12)
+    a = _dense_from_csr(w.num_rows, w.num_cols, w.row_ptrs, w.col_idx, w.values)
+    ev = np.linalg.eigvalsh(a)
+    q = (np.sqrt(ev[-1] / ev[0]) - 1) / (np.sqrt(ev[-1] / ev[0]) + 1)
+    xs = w.x.astype(np.float64)
+    b = a @ xs
+    def enorm(x):
+        e = x - xs
+        return np.sqrt(e @ a @ e)
+    e0 = enorm(np.zeros(w.num_rows))
+    prev = e0
+    for k in range(1, 30):
+        x, _, _ = oracle.cg(w.row_ptrs, w.col_idx, w.values, b, max_iter=k, rtol=0.0)
+        ek = enorm(x)
+        assert ek <= 2 * q**k * e0 * (1 + 1e-9)
+        assert ek <= prev * (1 + 1e-12)
+        prev = ek

@@ -201,6 +201,9 @@ spmv_status spmv_analyze(int32_t num_rows, int32_t num_cols, int32_t nnz,
  * W*R <= 2*nnz -> ELL; nnz < 10*R -> COO (segmented); W*R > 5*nnz -> HYB;
  * else CSR (vector); CHOICE 4.1 for the HYB width; CHOICE 5.2: power-law rows
  * -> merge-based CSR, taken when HYB's ELL part would exceed 1.5*nnz slots].
+ *   ELL is not chosen when W*R exceeds INT32_MAX (the later rules decide), nor
+ *   HYB when R*K does (merge-based CSR instead), so an automatic build never
+ *   fails on the int32 slot limit.
  *   hist_host: int64[max_len+1] from spmv_analyze.  opts (nullable):
  *   hyb_width / lanes_per_row override the width and lane rules.
  *   Outputs: *format, *hyb_width (0 unless HYB), *lanes (0 unless CSR vector).

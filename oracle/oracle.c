@@ -375,6 +375,9 @@ int orc_csr_to_jds(int64_t R, const int32_t *row_ptrs, const int32_t *col_idx,
 /*                              if R*K <= 1.5*nnz, else merge-based CSR     */
 /*   otherwise               -> CSR vector, lanes = smallest power of two   */
 /*                              >= ceil(mean), clamped to [2, 64]           */
+/* A padded choice whose slot count W*R (ELL) or R*K (HYB) exceeds the      */
+/* int32 index range is not taken: ELL falls through to the later rules,    */
+/* HYB becomes merge-based CSR.                                             */
 /* hyb_width > 0 replaces the percentile K; lanes > 0 replaces the lane     */
 /* rule.  hist has W+1 entries.  out[0]=format, out[1]=K (0 if not HYB),    */
 /* out[2]=lanes (0 if not CSR vector).                                      */
@@ -407,7 +410,7 @@ void orc_select(int64_t R, int64_t nnz, int64_t W, const int64_t *hist, int64_t 
     out[0] = ORC_FMT_ELL;
     out[1] = 0;
     out[2] = 0;
-    if (W * R <= 2 * nnz)
+    if (W * R <= 2 * nnz && W * R <= ORC_INT32_MAX)
         return;                                   /* ELL */
     if (nnz < 10 * R) {
         out[0] = ORC_FMT_COO_SEGMENTED;
@@ -415,7 +418,7 @@ void orc_select(int64_t R, int64_t nnz, int64_t W, const int64_t *hist, int64_t 
     }
     if (W * R > 5 * nnz) {
         int64_t K = hyb_width > 0 ? hyb_width : orc_hyb_width(R, W, hist);
-        if (2 * R * K <= 3 * nnz) {               /* R*K <= 1.5*nnz */
+        if (2 * R * K <= 3 * nnz && R * K <= ORC_INT32_MAX) {   /* R*K <= 1.5*nnz */
             out[0] = ORC_FMT_HYB;
             out[1] = K;
         } else {

@@ -157,13 +157,14 @@ void select_format(const spmv_stats &st, const int64_t *hist, const spmv_opts &o
     *K = 0;
     *L = 0;
     const int64_t padded = W * R;             // slots of a full-width ELL
-    if (padded <= 2 * nnz) {                  // max <= 2 * mean
+    // a padded format is taken only while its slots fit int32 indices
+    if (padded <= 2 * nnz && padded <= kInt32Max) {   // max <= 2 * mean
         *fmt = SPMV_ELL;
     } else if (nnz < 10 * R) {                // mean < 10
         *fmt = SPMV_COO_SEGMENTED;
     } else if (padded > 5 * nnz) {            // max > 5 * mean
         const int64_t k = o.hyb_width > 0 ? o.hyb_width : hyb_percentile_width(R, hist, W + 1);
-        if (2 * R * k <= 3 * nnz) {           // ELL part <= 1.5 * nnz slots
+        if (2 * R * k <= 3 * nnz && R * k <= kInt32Max) {   // ELL part <= 1.5 * nnz slots
             *fmt = SPMV_HYB;
             *K = static_cast<int32_t>(k);
         } else {

@@ -77,7 +77,9 @@ __global__ __launch_bounds__(kThreads) void k_expand_rows(int32_t R,
     const int32_t b = my < R ? rp[my + 1] : 0;
     for (int k = 0; k < kWave && r0 + k < R; ++k) {
         const int32_t ak = __shfl(a, k), bk = __shfl(b, k);
-        for (int32_t i = ak + lane; i < bk; i += kWave) row_idx[i] = static_cast<int32_t>(r0 + k);
+        // 64-bit position: a row may end at INT32_MAX
+        for (int64_t i = static_cast<int64_t>(ak) + lane; i < bk; i += kWave)
+            row_idx[i] = static_cast<int32_t>(r0 + k);
     }
 }
 
@@ -230,8 +232,8 @@ __global__ __launch_bounds__(kThreads) void k_jds_chunks(int32_t R, int32_t dept
     const int64_t g = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
     const int64_t groups = (static_cast<int64_t>(R) + kWave - 1) / kWave;
     if (g < groups) {
-        const int32_t len = jds_len[g * kWave];
-        chunks[g] = (len + depth - 1) / depth;
+        const int64_t len = jds_len[g * kWave];
+        chunks[g] = static_cast<int32_t>((len + depth - 1) / depth);
     }
 }
 

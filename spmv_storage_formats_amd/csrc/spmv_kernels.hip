@@ -128,19 +128,24 @@ __global__ __launch_bounds__(kThreads) void k_csr_scalar(int32_t R, const int32_
     if (r >= R) return;
     const int32_t a = srp[threadIdx.x], e = srp[threadIdx.x + 1];
     if (a == e) return;
+    // offsets inside the row, unsigned: a row may end at INT32_MAX, and
+    // o + 4 <= len < 2^31 + 4 cannot wrap in 32 bits
+    const int32_t *rc = col + a;
+    const float *rv = val + a;
+    const uint32_t len = static_cast<uint32_t>(e - a);
     float sum = 0.f;
-    int32_t i = a;
-    for (; i + 4 <= e; i += 4) {
-        const int32_t c0 = ld_nt(col + i), c1 = ld_nt(col + i + 1), c2 = ld_nt(col + i + 2),
-                      c3 = ld_nt(col + i + 3);
-        const float v0 = ld_nt(val + i), v1 = ld_nt(val + i + 1), v2 = ld_nt(val + i + 2),
-                    v3 = ld_nt(val + i + 3);
+    uint32_t o = 0;
+    for (; o + 4 <= len; o += 4) {
+        const int32_t c0 = ld_nt(rc + o), c1 = ld_nt(rc + o + 1), c2 = ld_nt(rc + o + 2),
+                      c3 = ld_nt(rc + o + 3);
+        const float v0 = ld_nt(rv + o), v1 = ld_nt(rv + o + 1), v2 = ld_nt(rv + o + 2),
+                    v3 = ld_nt(rv + o + 3);
         sum += v0 * x[c0];
         sum += v1 * x[c1];
         sum += v2 * x[c2];
         sum += v3 * x[c3];
     }
-    for (; i < e; ++i) sum += ld_nt(val + i) * x[ld_nt(col + i)];
+    for (; o < len; ++o) sum += ld_nt(rv + o) * x[ld_nt(rc + o)];
     atomic_add_f32(&y[r], sum);
 }
 
@@ -170,46 +175,51 @@ __global__ __launch_bounds__(kThreads) void k_csr_vector(int32_t R, const int32_
         if (r0 + i <= R) srp[i] = rp[r0 + i];
     __syncthreads();
     const int g = threadIdx.x / L, lg = threadIdx.x % L;
-    int32_t a[kRpg], e[kRpg], c0[kRpg], c1[kRpg];
+    // Offsets inside a row are unsigned and relative to the row start: a row
+    // may end at INT32_MAX, and offset + 4L stays below 2^32.
+    int32_t a[kRpg], c0[kRpg], c1[kRpg];
+    uint32_t n[kRpg];
     float v0[kRpg], v1[kRpg], acc[kRpg];
 #pragma unroll
     for (int m = 0; m < kRpg; ++m) {
         const int lr = m * kGroups + g;
         const bool ok = r0 + lr < R;
         a[m] = ok ? srp[lr] : 0;
-        e[m] = ok ? srp[lr + 1] : 0;
-        const int32_t j = a[m] + lg;
-        c0[m] = j < e[m] ? ld_nt(col + j) : 0;
-        v0[m] = j < e[m] ? ld_nt(val + j) : 0.f;
-        c1[m] = j + L < e[m] ? ld_nt(col + j + L) : 0;
-        v1[m] = j + L < e[m] ? ld_nt(val + j + L) : 0.f;
+        n[m] = ok ? static_cast<uint32_t>(srp[lr + 1] - a[m]) : 0u;
+        const uint32_t j = lg;
+        c0[m] = j < n[m] ? ld_nt(col + a[m] + j) : 0;
+        v0[m] = j < n[m] ? ld_nt(val + a[m] + j) : 0.f;
+        c1[m] = j + L < n[m] ? ld_nt(col + a[m] + (j + L)) : 0;
+        v1[m] = j + L < n[m] ? ld_nt(val + a[m] + (j + L)) : 0.f;
     }
 #pragma unroll
     for (int m = 0; m < kRpg; ++m) {
-        const int32_t j = a[m] + lg;
-        const float x0 = j < e[m] ? x[c0[m]] : 0.f;
-        const float x1 = j + L < e[m] ? x[c1[m]] : 0.f;
+        const uint32_t j = lg;
+        const float x0 = j < n[m] ? x[c0[m]] : 0.f;
+        const float x1 = j + L < n[m] ? x[c1[m]] : 0.f;
         acc[m] = v0[m] * x0 + v1[m] * x1;
         // long rows: 4 elements per lane per step, loads before gathers
-        int32_t jj = j + 2 * L;
-        for (; jj + 3 * L < e[m]; jj += 4 * L) {
+        const int32_t *rc = col + a[m];
+        const float *rv = val + a[m];
+        uint32_t jj = j + 2 * L;
+        for (; jj + 3 * L < n[m]; jj += 4 * L) {
             int32_t cq[4];
             float vq[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                cq[q] = ld_nt(col + jj + q * L);
-                vq[q] = ld_nt(val + jj + q * L);
+                cq[q] = ld_nt(rc + (jj + q * L));
+                vq[q] = ld_nt(rv + (jj + q * L));
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q) acc[m] += vq[q] * x[cq[q]];
         }
-        for (; jj < e[m]; jj += L) acc[m] += ld_nt(val + jj) * x[ld_nt(col + jj)];
+        for (; jj < n[m]; jj += L) acc[m] += ld_nt(rv + jj) * x[ld_nt(rc + jj)];
     }
 #pragma unroll
     for (int m = 0; m < kRpg; ++m) {
         const float sum = group_sum<L>(acc[m]);
         const int64_t r = r0 + m * kGroups + g;
-        if (lg == 0 && e[m] > a[m]) atomic_add_f32(&y[r], sum);
+        if (lg == 0 && n[m] > 0) atomic_add_f32(&y[r], sum);
     }
 }
 
@@ -244,19 +254,22 @@ __global__ __launch_bounds__(kThreads) void k_ell(int32_t R, int32_t W,
         v[u] = u < W ? ld_nt(ell_val + slot) : 0.f;
     }
     float sum = 0.f;
-    for (int32_t t0 = 0; t0 < W; t0 += U) {
+    // slot counters unsigned: W may be INT32_MAX (one row), and t0 + 2U stays
+    // below 2^32; a slot t*R + r is formed only for t < W, where it is < 2^31
+    const uint32_t wu = static_cast<uint32_t>(W), nu = static_cast<uint32_t>(n);
+    for (uint32_t t0 = 0; t0 < wu; t0 += U) {
         int32_t cn[U];
         float vn[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int32_t t = t0 + U + u;
-            const uint32_t slot = static_cast<uint32_t>(t) * ru + r;
-            cn[u] = t < W ? ld_nt(ell_col + slot) : 0;
-            vn[u] = t < W ? ld_nt(ell_val + slot) : 0.f;
+            const uint32_t t = t0 + U + u;
+            const uint32_t slot = t * ru + r;
+            cn[u] = t < wu ? ld_nt(ell_col + slot) : 0;
+            vn[u] = t < wu ? ld_nt(ell_val + slot) : 0.f;
         }
         float xv[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) xv[u] = (t0 + u < n) ? x[c[u]] : 0.f;
+        for (int u = 0; u < U; ++u) xv[u] = (t0 + u < nu) ? x[c[u]] : 0.f;
 #pragma unroll
         for (int u = 0; u < U; ++u) sum += v[u] * xv[u];
 #pragma unroll
@@ -295,17 +308,18 @@ __global__ __launch_bounds__(kThreads) void k_jds(int32_t R, int32_t ntiles, int
     const int64_t s = static_cast<int64_t>(g) * kWave + lane;
     const int32_t len = s < R ? jds_len[s] : 0;
     const int32_t glen = __builtin_amdgcn_readfirstlane(jds_len[static_cast<int64_t>(g) * kWave]);
-    const int32_t t0 = chunk * depth;
-    const int32_t t1 = min(t0 + depth, glen);
+    // jagged-column counters in 64 bits: a row may hold INT32_MAX entries
+    const int64_t t0 = static_cast<int64_t>(chunk) * depth;
+    const int64_t t1 = min(t0 + depth, static_cast<int64_t>(glen));
     // jagged columns U at a time, the next U columns' loads issued before the
     // current U gathers (as in ELL)
     constexpr int U = 8;
     int32_t c[U];
     float v[U];
-    auto load = [&](int32_t tb, int32_t *cc, float *vv) {
+    auto load = [&](int64_t tb, int32_t *cc, float *vv) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int32_t t = tb + u;
+            const int64_t t = tb + u;
             const int32_t p = t < t1 ? iter_ptr[t] : 0;   // wave-uniform
             const bool ok = t < t1 && t < len;
             cc[u] = ok ? ld_nt(col + p + s) : 0;
@@ -314,7 +328,7 @@ __global__ __launch_bounds__(kThreads) void k_jds(int32_t R, int32_t ntiles, int
     };
     load(t0, c, v);
     float sum = 0.f;
-    for (int32_t tb = t0; tb < t1; tb += U) {
+    for (int64_t tb = t0; tb < t1; tb += U) {
         int32_t cn[U];
         float vn[U];
         load(tb + U, cn, vn);
@@ -364,24 +378,24 @@ __global__ __launch_bounds__(kThreads) void k_sell(int32_t R, int32_t ntiles, in
     const int32_t len = lane < m ? sell_len[s] : 0;
     const int32_t width = __builtin_amdgcn_readfirstlane(sell_len[first]);
     const int64_t base = __builtin_amdgcn_readfirstlane(sect_ptr[k]);
-    const int32_t t0 = chunk * depth;
-    const int32_t t1 = min(t0 + depth, width);
+    const int64_t t0 = static_cast<int64_t>(chunk) * depth;
+    const int64_t t1 = min(t0 + depth, static_cast<int64_t>(width));
     constexpr int U = 8;
     int32_t c[U];
     float v[U];
-    auto load = [&](int32_t tb, int32_t *cc, float *vv) {
+    auto load = [&](int64_t tb, int32_t *cc, float *vv) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int32_t t = tb + u;
+            const int64_t t = tb + u;
             const bool ok = t < t1 && t < len;
-            const int64_t slot = base + static_cast<int64_t>(t) * m + lane;
+            const int64_t slot = base + t * m + lane;
             cc[u] = ok ? ld_nt(col + slot) : 0;
             vv[u] = ok ? ld_nt(val + slot) : 0.f;
         }
     };
     load(t0, c, v);
     float sum = 0.f;
-    for (int32_t tb = t0; tb < t1; tb += U) {
+    for (int64_t tb = t0; tb < t1; tb += U) {
         int32_t cn[U];
         float vn[U];
         load(tb + U, cn, vn);

@@ -38,6 +38,8 @@ __all__ = [
     "skewed",
     "power_law",
     "small_random",
+    "max_band",
+    "BandMatrix",
     "workload",
     "WORKLOADS",
 ]
@@ -220,6 +222,70 @@ def power_law(num_rows: int = 4_000_000, seed: int = 5, cap: int = 100_000,
     return Workload(f"power_law_{num_rows}", num_rows, num_rows, _ptrs_from_lengths(lengths),
                     col_idx, values, _vec(rx, num_rows), _vec(ry, num_rows),
                     {"seed": seed, "cap": cap})
+
+
+@dataclass
+class BandMatrix:
+    """The largest matrix int32 indices allow: ``num_rows`` rows of ``per_row``
+    entries, the last row one shorter, so nnz = 2^31 - 1 at the defaults
+    (2^26 rows of 32).
+
+    Entry d of row r sits in column (r + d * (num_rows // per_row)) mod num_rows
+    (a wrapped band: each row touches columns spread over the whole of x, in
+    increasing order except where the band wraps) and has value v[d], one of
+    ``per_row`` seeded U[-1, 1] values.  At full size the arrays (17 GB) are
+    generated where they are used -- ``csr_tensors`` builds them with torch on
+    the target device -- and ``row`` gives any row's entries on the host.
+    """
+    num_rows: int
+    per_row: int
+    v: np.ndarray   # float32 [per_row]
+    x: np.ndarray   # float32 [num_rows]
+    y: np.ndarray   # float32 [num_rows]
+
+    @property
+    def nnz(self) -> int:
+        return self.num_rows * self.per_row - 1
+
+    @property
+    def stride(self) -> int:
+        return self.num_rows // self.per_row
+
+    def row(self, r: int):
+        """(columns, values) of row r, in storage order."""
+        n = self.per_row - (1 if r == self.num_rows - 1 else 0)
+        d = np.arange(n, dtype=np.int64)
+        cols = ((r + d * self.stride) % self.num_rows).astype(np.int32)
+        return cols, self.v[:n].copy()
+
+    def csr_tensors(self, torch, device):
+        """(row_ptrs int32 [R+1], col_idx int32 [nnz], values fp32 [nnz]) on `device`."""
+        R, P = self.num_rows, self.per_row
+        rp = torch.arange(R + 1, dtype=torch.int64, device=device) * P
+        rp[-1] -= 1
+        base = torch.arange(R, dtype=torch.int32, device=device)
+        offs = torch.arange(P, dtype=torch.int32, device=device) * self.stride
+        cols = base[:, None] + offs[None, :]            # < 2R, no int32 overflow
+        cols = torch.where(cols >= R, cols - R, cols)
+        vals = torch.from_numpy(self.v).to(device)[None, :].expand(R, P).contiguous()
+        return (rp.to(torch.int32), cols.reshape(-1)[:self.nnz],
+                vals.reshape(-1)[:self.nnz])
+
+    def to_workload(self) -> Workload:
+        """Host CSR arrays (for small instances)."""
+        lengths = np.full(self.num_rows, self.per_row, dtype=np.int64)
+        lengths[-1] -= 1
+        cols = np.concatenate([self.row(r)[0] for r in range(self.num_rows)])
+        vals = np.concatenate([self.row(r)[1] for r in range(self.num_rows)])
+        return Workload(f"max_band_{self.num_rows}x{self.per_row}", self.num_rows,
+                        self.num_rows, _ptrs_from_lengths(lengths), cols, vals, self.x,
+                        self.y, {"per_row": self.per_row})
+
+
+def max_band(num_rows: int = 2**26, per_row: int = 32, seed: int = 6) -> BandMatrix:
+    _, rv, rx, ry = _streams(seed)
+    v = rv.uniform(-1.0, 1.0, size=per_row).astype(np.float32)
+    return BandMatrix(num_rows, per_row, v, _vec(rx, num_rows), _vec(ry, num_rows))
 
 
 def small_random(rng: np.random.Generator, num_rows: int, num_cols: int, max_len: int,

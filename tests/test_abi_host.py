@@ -125,3 +125,34 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(TypeError):
         spmv.build("ell", torch.zeros(5, dtype=torch.int32), torch.zeros(0, dtype=torch.int32),
                    torch.zeros(0), 4)
+
+
+def test_selector_respects_int32_slots():
+    """At the largest matrix the ABI accepts (nnz = INT32_MAX: 2^26 rows of 32,
+    the last of 31) ELL would need 2^31 slots: both selectors fall through to
+    CSR vector with 32 lanes.  A HYB choice whose ELL part exceeds int32 becomes
+    merge-based CSR."""
+    R = 2**26
+    lens = np.full(R, 32, np.int64)
+    lens[-1] = 31
+    st = _stats(R, lens)
+    assert st["nnz"] == 2**31 - 1
+    h = _hist(lens)
+    assert spmv.select(st, h) == ("csr_vector", 0, 32)
+    assert oracle.select(R, st["nnz"], h) == ("csr_vector", 0, 32)
+    # one row fewer: W*R = 2^31 - 32 fits, ELL
+    st2 = _stats(R - 1, lens[:-1])
+    assert spmv.select(st2, _hist(lens[:-1])) == ("ell", 0, 0)
+    assert oracle.select(R - 1, st2["nnz"], _hist(lens[:-1])) == ("ell", 0, 0)
+    # HYB: 2^26 rows of 20 plus 1000 rows of 150,000 (nnz ~1.49e9).  Forced width 33
+    # passes the 1.5*nnz rule (2RK = 4.43e9 <= 3 nnz = 4.48e9) but R*K = 2.2e9 exceeds
+    # int32 -> merge; width 31 fits both -> HYB.
+    lens3 = np.full(R, 20, np.int64)
+    lens3[:1000] = 150_000
+    st3 = _stats(R, lens3)
+    h3 = _hist(lens3)
+    assert 2 * R * 33 <= 3 * st3["nnz"] and R * 33 > 2**31 - 1
+    assert spmv.select(st3, h3, hyb_width=31) == ("hyb", 31, 0)
+    assert oracle.select(R, st3["nnz"], h3, 31) == ("hyb", 31, 0)
+    assert spmv.select(st3, h3, hyb_width=33) == ("csr_merge", 0, 0)
+    assert oracle.select(R, st3["nnz"], h3, 33) == ("csr_merge", 0, 0)

@@ -107,3 +107,30 @@ def test_power_law_mean_length():
     k = np.arange(1, 100_000, dtype=np.float64)
     tail = np.where(k <= xm, 1.0, (k ** -a - B) / (A - B))  # P(len >= k)
     assert abs(tail.sum() - 16.0) < 1e-5
+
+
+def test_max_band_structure():
+    """Small instance of the int32-limit generator: nnz = R*per_row - 1, entry d
+    of row r in column (r + d*R/per_row) mod R with value v[d]; the torch
+    builder (run on the CPU here) gives the same arrays as the host rows."""
+    torch = pytest.importorskip("torch")
+    R, P = 64, 4
+    m = synth.max_band(R, P, seed=6)
+    w = m.to_workload()
+    assert w.nnz == m.nnz == R * P - 1
+    lens = w.lengths()
+    assert np.all(lens[:-1] == P) and lens[-1] == P - 1
+    for r in (0, 1, 17, R - 1):
+        s, e = w.row_ptrs[r], w.row_ptrs[r + 1]
+        d = np.arange(e - s)
+        assert np.array_equal(w.col_idx[s:e], (r + d * (R // P)) % R)
+        assert np.array_equal(w.values[s:e], m.v[d])
+    rp, ci, v = m.csr_tensors(torch, "cpu")
+    assert np.array_equal(rp.numpy(), w.row_ptrs)
+    assert np.array_equal(ci.numpy(), w.col_idx)
+    assert np.array_equal(v.numpy().view(np.uint32), w.values.view(np.uint32))
+
+
+def test_max_band_default_size_is_int32_max():
+    m = synth.max_band()
+    assert m.nnz == np.iinfo(np.int32).max and m.x.shape == (2**26,)

@@ -273,9 +273,11 @@ spmv_status build_jds(spmv_handle *h, int32_t R, int32_t nnz, const int32_t *rp,
     SPMV_TRY(halloc(h, &h->a.jds_val, nnz));
     SPMV_HIP(launch_jds_counts(R, W, h->a.jds_len, h->a.jds_iter_ptr, s));
     SPMV_TRY(exclusive_scan(h->a.jds_iter_ptr, h->a.jds_iter_ptr, W, true, s, scratch));
-    SPMV_HIP(launch_jds_fill(nnz, W, h->a.jds_iter_ptr, h->a.jds_perm, rp, col, val,
-                             h->a.jds_col, h->a.jds_val, s));
-    return jds_tiles(h, R, s, scratch);
+    SPMV_TRY(jds_tiles(h, R, s, scratch));
+    SPMV_HIP(launch_jds_fill(R, h->num_tiles, h->jds_depth, h->a.jds_tiles, h->a.jds_iter_ptr,
+                             h->a.jds_perm, h->a.jds_len, rp, col, val, h->a.jds_col,
+                             h->a.jds_val, s));
+    return SPMV_OK;
 }
 
 // Padded slots of the sectioned ELL, exactly, from the length histogram: the
@@ -305,10 +307,11 @@ spmv_status build_sell(spmv_handle *h, int32_t R, const int32_t *rp, const int32
     SPMV_TRY(halloc(h, &h->a.sell_val, slots));
     SPMV_HIP(launch_sell_sizes(R, h->a.jds_len, h->a.sell_ptr, s));
     SPMV_TRY(exclusive_scan(h->a.sell_ptr, h->a.sell_ptr, nsect, true, s, scratch));
-    SPMV_HIP(launch_sell_fill(R, nsect, static_cast<int32_t>(slots), h->a.sell_ptr,
+    SPMV_TRY(jds_tiles(h, R, s, scratch));
+    SPMV_HIP(launch_sell_fill(R, h->num_tiles, h->jds_depth, h->a.jds_tiles, h->a.sell_ptr,
                               h->a.jds_len, h->a.jds_perm, rp, col, val, h->a.sell_col,
                               h->a.sell_val, s));
-    return jds_tiles(h, R, s, scratch);
+    return SPMV_OK;
 }
 
 // Device bytes a format needs (checked against opts.max_bytes before building).
@@ -384,25 +387,50 @@ spmv_status build_sliced(spmv_handle **out, spmv_format fmt, int32_t R, int32_t 
     // per slice on the skewed and power-law workloads).  An explicit format is
     // kept as asked.
     if (fmt == SPMV_AUTO) fmt = SPMV_CSR_MERGE;
+    // Group the entries by slice: row index per entry, a stable sort on the
+    // slice number (entries of a slice keep their row-major order), then the
+    // rows, columns and values gathered in that order.  Slice b is the sorted
+    // range [bounds[b], bounds[b+1]); its row pointers come from counting its
+    // row indices and scanning, as in COO -> CSR.
+    const int32_t nb = h->col_blocks;
+    int32_t *row_idx = nullptr, *iota = nullptr, *perm = nullptr, *bounds = nullptr;
+    uint32_t *keys = nullptr, *keys_sorted = nullptr;
+    int32_t *rows_s = nullptr, *col_s = nullptr;
+    float *val_s = nullptr;
+    SPMV_TRY(scratch.alloc(&row_idx, nnz));
+    SPMV_TRY(scratch.alloc(&keys, nnz));
+    SPMV_TRY(scratch.alloc(&keys_sorted, nnz));
+    SPMV_TRY(scratch.alloc(&iota, nnz));
+    SPMV_TRY(scratch.alloc(&perm, nnz));
+    SPMV_TRY(scratch.alloc(&rows_s, nnz));
+    SPMV_TRY(scratch.alloc(&col_s, nnz));
+    SPMV_TRY(scratch.alloc(&val_s, nnz));
+    SPMV_TRY(scratch.alloc(&bounds, static_cast<size_t>(nb) + 1));
+    SPMV_HIP(launch_expand_rows(R, nnz, rp, row_idx, s));
+    SPMV_HIP(launch_slice_keys(nnz, col, static_cast<int32_t>(slice), keys, s));
+    SPMV_HIP(launch_iota(nnz, iota, s));
+    SPMV_TRY(radix_sort_pairs(keys, iota, keys_sorted, perm, nnz,
+                              bits_for(static_cast<uint64_t>(nb - 1)), s, scratch));
+    SPMV_HIP(launch_slice_bounds(nnz, nb, keys_sorted, bounds, s));
+    SPMV_HIP(launch_gather_u32(nnz, perm, reinterpret_cast<const uint32_t *>(row_idx),
+                               reinterpret_cast<uint32_t *>(rows_s), s));
+    SPMV_HIP(launch_gather_pairs(nnz, perm, col, val, col_s, val_s, s));
+    std::vector<int32_t> hb(static_cast<size_t>(nb) + 1);
+    SPMV_HIP(hipMemcpyAsync(hb.data(), bounds, sizeof(int32_t) * hb.size(), hipMemcpyDeviceToHost,
+                            s));
+    SPMV_HIP(hipStreamSynchronize(s));
     int64_t best_nnz = -1;
-    for (int32_t b = 0; b < h->col_blocks; ++b) {
-        const int32_t lo = static_cast<int32_t>(b * slice);
-        const int32_t hi = static_cast<int32_t>(std::min<int64_t>(C, (b + 1) * slice));
+    for (int32_t b = 0; b < nb; ++b) {
+        const int32_t p0 = hb[b], pn = hb[b + 1] - hb[b];
+        if (pn == 0) continue;
         int32_t *prp = nullptr;
         SPMV_TRY(scratch.alloc(&prp, static_cast<size_t>(R) + 1));
-        SPMV_HIP(launch_slice_count(R, rp, col, lo, hi, prp, s));
+        SPMV_HIP(hipMemsetAsync(prp, 0, sizeof(int32_t) * (static_cast<size_t>(R) + 1), s));
+        SPMV_HIP(launch_count_rows(pn, rows_s + p0, prp, s));
         SPMV_TRY(exclusive_scan(prp, prp, R, true, s, scratch));
-        int32_t pn = 0;
-        SPMV_HIP(hipMemcpyAsync(&pn, prp + R, sizeof(int32_t), hipMemcpyDeviceToHost, s));
-        SPMV_HIP(hipStreamSynchronize(s));
-        if (pn == 0) continue;
-        int32_t *pcol = nullptr;
-        float *pval = nullptr;
-        SPMV_TRY(scratch.alloc(&pcol, pn));
-        SPMV_TRY(scratch.alloc(&pval, pn));
-        SPMV_HIP(launch_slice_fill(R, rp, col, val, lo, hi, prp, pcol, pval, s));
         spmv_handle *part = nullptr;
-        SPMV_TRY(build_csr_impl(&part, fmt, R, C, pn, prp, pcol, pval, po, s, scratch));
+        SPMV_TRY(build_csr_impl(&part, fmt, R, C, pn, prp, col_s + p0, val_s + p0, po, s,
+                                scratch));
         h->parts.push_back(part);
         h->device_bytes += part->device_bytes;
         if (pn > best_nnz) {

@@ -83,8 +83,39 @@ __global__ __launch_bounds__(kThreads) void k_expand_rows(int32_t R,
     }
 }
 
-// One lane per row writes its `width` slots; for a fixed slot t neighbouring
-// lanes write neighbouring words (t*R + r), so the stores coalesce.
+// ---------------------------------------------------------------------------
+// Row-to-column transposes (ELL, JDS, sectioned ELL).  One lane per row; for a
+// fixed entry position t the lanes of a wave write neighbouring words, so the
+// stores coalesce.  Reading row r's entries lane by lane would touch a
+// different cache line in every lane, so when the wave's rows form one
+// contiguous CSR segment of at most kStage entries the wave first copies the
+// segment into LDS with coalesced loads and each lane then reads its row from
+// LDS.  Word i of the segment is stored at i + i/32, so rows of a power-of-two
+// length do not fall in one bank.  Columns and values are staged in two
+// phases to halve the LDS footprint.  Other waves read global memory directly.
+// ---------------------------------------------------------------------------
+constexpr int kStage = 2048;
+constexpr int kStageWords = kStage + kStage / 32;
+
+__device__ inline int32_t skew(int32_t i) { return i + (i >> 5); }
+
+// lds[skew(i)] = src[i] for i in [0, n), the wave's 64 lanes together.
+template <typename T>
+__device__ inline void stage_segment(const T *__restrict__ src, int32_t n, T *lds, int lane) {
+    int32_t i = lane;
+    for (; i + 3 * kWave < n; i += 4 * kWave) {
+        const T v0 = src[i], v1 = src[i + kWave], v2 = src[i + 2 * kWave], v3 = src[i + 3 * kWave];
+        lds[skew(i)] = v0;
+        lds[skew(i + kWave)] = v1;
+        lds[skew(i + 2 * kWave)] = v2;
+        lds[skew(i + 3 * kWave)] = v3;
+    }
+    for (; i < n; i += kWave) lds[skew(i)] = src[i];
+}
+
+// CSR -> ELL [Regularized formats page, ELL section]: row r's entry t goes to
+// slot t*R + r; slots past the row's length (or past `width`) are padding
+// (column 0, +0.0f).
 __global__ __launch_bounds__(kThreads) void k_build_ell(int32_t R, int32_t width,
                                                         const int32_t *__restrict__ rp,
                                                         const int32_t *__restrict__ col,
@@ -92,21 +123,37 @@ __global__ __launch_bounds__(kThreads) void k_build_ell(int32_t R, int32_t width
                                                         int32_t *__restrict__ ell_col,
                                                         uint32_t *__restrict__ ell_val,
                                                         int32_t *__restrict__ ell_nnz) {
+    __shared__ uint32_t lds[kThreads / kWave][kStageWords];
+    const int w = threadIdx.x / kWave;
+    const int lane = __lane_id();
     const int64_t r = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-    if (r >= R) return;
-    const int32_t a = rp[r];
-    int32_t n = rp[r + 1] - a;
+    const bool ok = r < R;
+    const int32_t a = ok ? rp[r] : 0;
+    const int32_t e = ok ? rp[r + 1] : 0;
+    int32_t n = e - a;
     if (n > width) n = width;
-    ell_nnz[r] = n;
-    for (int32_t t = 0; t < width; ++t) {
-        const int64_t slot = static_cast<int64_t>(t) * R + r;
-        if (t < n) {
-            ell_col[slot] = col[a + t];
-            ell_val[slot] = val[a + t];
-        } else {
-            ell_col[slot] = 0;
-            ell_val[slot] = 0u;  // +0.0f
+    if (ok) ell_nnz[r] = n;
+    // the wave's segment [s0, s1): lane 0's start to the last valid lane's end
+    const unsigned long long live = __ballot(ok);
+    const int last = live ? 63 - __clzll(static_cast<long long>(live)) : 0;
+    const int32_t s0 = __builtin_amdgcn_readfirstlane(a);
+    const int32_t s1 = __shfl(e, last);
+    const int64_t seg = live ? static_cast<int64_t>(s1) - s0 : 0;
+    const bool staged = seg <= kStage;   // wave-uniform
+    const int32_t off = a - s0;
+    for (int phase = 0; phase < 2; ++phase) {
+        const uint32_t *src = phase == 0 ? reinterpret_cast<const uint32_t *>(col) : val;
+        uint32_t *dst = phase == 0 ? reinterpret_cast<uint32_t *>(ell_col) : ell_val;
+        if (staged) stage_segment(src + s0, static_cast<int32_t>(seg), lds[w], lane);
+        __syncthreads();
+        if (ok) {
+            for (int32_t t = 0; t < width; ++t) {
+                uint32_t v = 0u;   // padding: column 0 / +0.0f
+                if (t < n) v = staged ? lds[w][skew(off + t)] : src[static_cast<int64_t>(a) + t];
+                dst[static_cast<int64_t>(t) * R + r] = v;
+            }
         }
+        __syncthreads();
     }
 }
 
@@ -169,23 +216,57 @@ __global__ __launch_bounds__(kThreads) void k_jds_counts(int32_t R, int32_t W,
     counts[t] = static_cast<int32_t>(lo);
 }
 
-// One lane per JDS slot e: jagged column t = last t with iter_ptr[t] <= e,
-// sorted row s = e - iter_ptr[t], source entry t of original row perm[s].
-__global__ __launch_bounds__(kThreads) void k_jds_fill(int32_t nnz, int32_t W,
+// One wave per JDS tile (64 consecutive sorted rows x `depth` jagged columns,
+// the tiles the SpMV kernel walks): lane i takes sorted row s = 64g + i and
+// copies its entries t in the tile's column range from original row perm[s]
+// to iter_ptr[t] + s.  A first-chunk tile whose rows are consecutive original
+// rows (the common case: equal lengths keep their order) stages its CSR
+// segment in LDS as the ELL builder does.
+__global__ __launch_bounds__(kThreads) void k_jds_fill(int32_t R, int32_t ntiles, int32_t depth,
+                                                       const int2 *__restrict__ tiles,
                                                        const int32_t *__restrict__ iter_ptr,
                                                        const int32_t *__restrict__ perm,
+                                                       const int32_t *__restrict__ jds_len,
                                                        const int32_t *__restrict__ rp,
                                                        const int32_t *__restrict__ col,
                                                        const uint32_t *__restrict__ val,
                                                        int32_t *__restrict__ jds_col,
                                                        uint32_t *__restrict__ jds_val) {
-    const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-    if (e >= nnz) return;
-    const int64_t t = upper_index(iter_ptr, W, e);
-    const int64_t s = e - iter_ptr[t];
-    const int64_t src = static_cast<int64_t>(rp[perm[s]]) + t;
-    jds_col[e] = col[src];
-    jds_val[e] = val[src];
+    __shared__ uint32_t lds[kThreads / kWave][kStageWords];
+    const int w = threadIdx.x / kWave;
+    const int lane = __lane_id();
+    const int64_t tile = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) / kWave;
+    const bool tile_ok = tile < ntiles;
+    const int2 gc = tile_ok ? tiles[tile] : make_int2(0, 0);
+    const int64_t s = static_cast<int64_t>(gc.x) * kWave + lane;
+    const bool ok = tile_ok && s < R;
+    const int64_t t0 = static_cast<int64_t>(gc.y) * depth;
+    const int64_t t1 = ok ? min(t0 + depth, static_cast<int64_t>(jds_len[s])) : 0;
+    const int32_t p = ok ? perm[s] : 0;
+    const int32_t a = ok ? rp[p] : 0;
+    // staged when the tile is its group's first chunk and the rows are
+    // consecutive original rows forming one segment of <= kStage entries
+    const unsigned long long live = __ballot(ok);
+    const int last = live ? 63 - __clzll(static_cast<long long>(live)) : 0;
+    const int32_t p0 = __builtin_amdgcn_readfirstlane(p);
+    const bool consecutive = __ballot(ok && p != p0 + lane) == 0;
+    const int32_t s0 = __builtin_amdgcn_readfirstlane(a);
+    const int32_t s1 = live ? rp[__shfl(p, last) + 1] : s0;
+    const int64_t seg = static_cast<int64_t>(s1) - s0;
+    const bool staged = live && gc.y == 0 && consecutive && seg <= kStage;   // wave-uniform
+    const int32_t off = a - s0;
+    for (int phase = 0; phase < 2; ++phase) {
+        const uint32_t *src = phase == 0 ? reinterpret_cast<const uint32_t *>(col) : val;
+        uint32_t *dst = phase == 0 ? reinterpret_cast<uint32_t *>(jds_col) : jds_val;
+        if (staged) stage_segment(src + s0, static_cast<int32_t>(seg), lds[w], lane);
+        __syncthreads();
+        for (int64_t t = t0; t < t1; ++t) {
+            const uint32_t v = staged ? lds[w][skew(off + static_cast<int32_t>(t))]
+                                      : src[static_cast<int64_t>(a) + t];
+            dst[static_cast<int64_t>(iter_ptr[t]) + s] = v;
+        }
+        __syncthreads();
+    }
 }
 
 // Sectioned ELL (JDS variant): section k = sorted rows [64k, 64k + m_k),
@@ -201,26 +282,57 @@ __global__ __launch_bounds__(kThreads) void k_sell_sizes(int32_t R,
     }
 }
 
+// One wave per tile (section k, chunk of `depth` padded columns), the tiles
+// the SpMV kernel walks: lane i writes slots sect_ptr[k] + t*m + i of the
+// chunk, its row's entry t or padding (column 0, +0.0f) past its length.
+// Staged in LDS like the JDS fill when the section's rows are consecutive.
 __global__ __launch_bounds__(kThreads) void k_sell_fill(
-    int32_t R, int32_t nsect, int32_t slots, const int32_t *__restrict__ sect_ptr,
-    const int32_t *__restrict__ jds_len, const int32_t *__restrict__ perm,
-    const int32_t *__restrict__ rp, const int32_t *__restrict__ col,
-    const uint32_t *__restrict__ val, int32_t *__restrict__ sell_col,
-    uint32_t *__restrict__ sell_val) {
-    const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-    if (e >= slots) return;
-    const int64_t k = upper_index(sect_ptr, nsect, e);
-    const int64_t m = min(static_cast<int64_t>(kWave), R - k * kWave);
-    const int64_t off = e - sect_ptr[k];
-    const int64_t t = off / m, i = off % m;
-    const int64_t s = k * kWave + i;
-    if (t < jds_len[s]) {
-        const int64_t src = static_cast<int64_t>(rp[perm[s]]) + t;
-        sell_col[e] = col[src];
-        sell_val[e] = val[src];
-    } else {
-        sell_col[e] = 0;
-        sell_val[e] = 0u;
+    int32_t R, int32_t ntiles, int32_t depth, const int2 *__restrict__ tiles,
+    const int32_t *__restrict__ sect_ptr, const int32_t *__restrict__ jds_len,
+    const int32_t *__restrict__ perm, const int32_t *__restrict__ rp,
+    const int32_t *__restrict__ col, const uint32_t *__restrict__ val,
+    int32_t *__restrict__ sell_col, uint32_t *__restrict__ sell_val) {
+    __shared__ uint32_t lds[kThreads / kWave][kStageWords];
+    const int w = threadIdx.x / kWave;
+    const int lane = __lane_id();
+    const int64_t tile = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) / kWave;
+    const bool tile_ok = tile < ntiles;
+    const int2 gc = tile_ok ? tiles[tile] : make_int2(0, 0);
+    const int64_t first = static_cast<int64_t>(gc.x) * kWave;
+    const int64_t m = tile_ok ? min(static_cast<int64_t>(kWave), R - first) : 0;
+    const bool ok = lane < m;
+    const int64_t s = first + lane;
+    const int64_t width = tile_ok ? jds_len[first] : 0;
+    const int64_t t0 = static_cast<int64_t>(gc.y) * depth;
+    const int64_t t1 = min(t0 + depth, width);
+    const int64_t len = ok ? jds_len[s] : 0;
+    const int32_t p = ok ? perm[s] : 0;
+    const int32_t a = ok ? rp[p] : 0;
+    const int64_t base = tile_ok ? static_cast<int64_t>(sect_ptr[gc.x]) + lane : 0;
+    const unsigned long long live = __ballot(ok);
+    const int last = live ? 63 - __clzll(static_cast<long long>(live)) : 0;
+    const int32_t p0 = __builtin_amdgcn_readfirstlane(p);
+    const bool consecutive = __ballot(ok && p != p0 + lane) == 0;
+    const int32_t s0 = __builtin_amdgcn_readfirstlane(a);
+    const int32_t s1 = live ? rp[__shfl(p, last) + 1] : s0;
+    const int64_t seg = static_cast<int64_t>(s1) - s0;
+    const bool staged = live && gc.y == 0 && consecutive && seg <= kStage;   // wave-uniform
+    const int32_t off = a - s0;
+    for (int phase = 0; phase < 2; ++phase) {
+        const uint32_t *src = phase == 0 ? reinterpret_cast<const uint32_t *>(col) : val;
+        uint32_t *dst = phase == 0 ? reinterpret_cast<uint32_t *>(sell_col) : sell_val;
+        if (staged) stage_segment(src + s0, static_cast<int32_t>(seg), lds[w], lane);
+        __syncthreads();
+        if (ok) {
+            for (int64_t t = t0; t < t1; ++t) {
+                uint32_t v = 0u;   // padding: column 0 / +0.0f
+                if (t < len)
+                    v = staged ? lds[w][skew(off + static_cast<int32_t>(t))]
+                               : src[static_cast<int64_t>(a) + t];
+                dst[base + t * m] = v;
+            }
+        }
+        __syncthreads();
     }
 }
 
@@ -246,43 +358,35 @@ __global__ __launch_bounds__(kThreads) void k_jds_tiles(int32_t groups, int32_t 
     tiles[tile] = make_int2(static_cast<int>(g), static_cast<int>(tile - tile_off[g]));
 }
 
-// Column slice [lo, hi): one lane per row counts, then copies, the row's
-// entries whose column falls in the slice, keeping their order.  Each slice is
-// a matrix of its own (same rows, global column indices) run as one pass.
-__global__ __launch_bounds__(kThreads) void k_slice_count(int32_t R,
-                                                          const int32_t *__restrict__ rp,
-                                                          const int32_t *__restrict__ col,
-                                                          int32_t lo, int32_t hi,
-                                                          int32_t *__restrict__ counts) {
-    const int64_t r = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-    if (r >= R) return;
-    int32_t n = 0;
-    for (int32_t i = rp[r]; i < rp[r + 1]; ++i) {
-        const int32_t c = col[i];
-        n += (c >= lo && c < hi);
-    }
-    counts[r] = n;
+// Column slices: entry i belongs to slice col[i] / slice_cols.  A stable sort
+// by slice (sort.hip) groups each slice's entries in their original, row-major
+// order; bounds[b] = first sorted position of slice b (binary search).
+__global__ __launch_bounds__(kThreads) void k_slice_keys(int32_t nnz,
+                                                         const int32_t *__restrict__ col,
+                                                         int32_t slice_cols,
+                                                         uint32_t *__restrict__ keys) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (i < nnz) keys[i] = static_cast<uint32_t>(col[i] / slice_cols);
 }
 
-__global__ __launch_bounds__(kThreads) void k_slice_fill(int32_t R, const int32_t *__restrict__ rp,
-                                                         const int32_t *__restrict__ col,
-                                                         const uint32_t *__restrict__ val,
-                                                         int32_t lo, int32_t hi,
-                                                         const int32_t *__restrict__ rp_out,
-                                                         int32_t *__restrict__ col_out,
-                                                         uint32_t *__restrict__ val_out) {
-    const int64_t r = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-    if (r >= R) return;
-    int32_t p = rp_out[r];
-    const int32_t end = rp_out[r + 1];
-    for (int32_t i = rp[r]; i < rp[r + 1] && p < end; ++i) {
-        const int32_t c = col[i];
-        if (c >= lo && c < hi) {
-            col_out[p] = c;
-            val_out[p] = val[i];
-            ++p;
-        }
+__global__ __launch_bounds__(kThreads) void k_slice_bounds(int32_t nnz, int32_t K,
+                                                           const uint32_t *__restrict__ keys,
+                                                           int32_t *__restrict__ bounds) {
+    const int b = blockIdx.x * kThreads + threadIdx.x;
+    if (b > K) return;
+    int64_t lo = 0, hi = nnz;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (keys[mid] < static_cast<uint32_t>(b)) lo = mid + 1; else hi = mid;
     }
+    bounds[b] = static_cast<int32_t>(lo);
+}
+
+__global__ __launch_bounds__(kThreads) void k_gather_u32(int32_t n, const int32_t *__restrict__ perm,
+                                                         const uint32_t *__restrict__ in,
+                                                         uint32_t *__restrict__ out) {
+    const int64_t p = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (p < n) out[p] = in[perm[p]];
 }
 
 // Merge path over rows (their end markers) and nonzeros: row r's end marker
@@ -386,13 +490,14 @@ hipError_t launch_jds_counts(int32_t R, int32_t W, const int32_t *jds_len, int32
     return hipGetLastError();
 }
 
-hipError_t launch_jds_fill(int32_t nnz, int32_t W, const int32_t *iter_ptr,
-                           const int32_t *perm, const int32_t *rp, const int32_t *col,
-                           const float *val, int32_t *jds_col, float *jds_val, hipStream_t s) {
-    if (nnz <= 0) return hipSuccess;
-    k_jds_fill<<<grid_for(nnz, kThreads), kThreads, 0, s>>>(
-        nnz, W, iter_ptr, perm, rp, col, reinterpret_cast<const uint32_t *>(val), jds_col,
-        reinterpret_cast<uint32_t *>(jds_val));
+hipError_t launch_jds_fill(int32_t R, int32_t ntiles, int32_t depth, const int2 *tiles,
+                           const int32_t *iter_ptr, const int32_t *perm, const int32_t *jds_len,
+                           const int32_t *rp, const int32_t *col, const float *val,
+                           int32_t *jds_col, float *jds_val, hipStream_t s) {
+    if (ntiles <= 0) return hipSuccess;
+    k_jds_fill<<<grid_for(static_cast<int64_t>(ntiles) * kWave, kThreads), kThreads, 0, s>>>(
+        R, ntiles, depth, tiles, iter_ptr, perm, jds_len, rp, col,
+        reinterpret_cast<const uint32_t *>(val), jds_col, reinterpret_cast<uint32_t *>(jds_val));
     return hipGetLastError();
 }
 
@@ -403,13 +508,13 @@ hipError_t launch_sell_sizes(int32_t R, const int32_t *jds_len, int32_t *sizes, 
     return hipGetLastError();
 }
 
-hipError_t launch_sell_fill(int32_t R, int32_t nsect, int32_t slots, const int32_t *sect_ptr,
-                            const int32_t *jds_len, const int32_t *perm, const int32_t *rp,
-                            const int32_t *col, const float *val, int32_t *sell_col,
-                            float *sell_val, hipStream_t s) {
-    if (slots <= 0) return hipSuccess;
-    k_sell_fill<<<grid_for(slots, kThreads), kThreads, 0, s>>>(
-        R, nsect, slots, sect_ptr, jds_len, perm, rp, col,
+hipError_t launch_sell_fill(int32_t R, int32_t ntiles, int32_t depth, const int2 *tiles,
+                            const int32_t *sect_ptr, const int32_t *jds_len, const int32_t *perm,
+                            const int32_t *rp, const int32_t *col, const float *val,
+                            int32_t *sell_col, float *sell_val, hipStream_t s) {
+    if (ntiles <= 0) return hipSuccess;
+    k_sell_fill<<<grid_for(static_cast<int64_t>(ntiles) * kWave, kThreads), kThreads, 0, s>>>(
+        R, ntiles, depth, tiles, sect_ptr, jds_len, perm, rp, col,
         reinterpret_cast<const uint32_t *>(val), sell_col, reinterpret_cast<uint32_t *>(sell_val));
     return hipGetLastError();
 }
@@ -429,20 +534,24 @@ hipError_t launch_jds_tiles(int32_t groups, int32_t ntiles, const int32_t *tile_
     return hipGetLastError();
 }
 
-hipError_t launch_slice_count(int32_t R, const int32_t *rp, const int32_t *col, int32_t lo,
-                              int32_t hi, int32_t *counts, hipStream_t s) {
-    if (R <= 0) return hipSuccess;
-    k_slice_count<<<grid_for(R, kThreads), kThreads, 0, s>>>(R, rp, col, lo, hi, counts);
+hipError_t launch_slice_keys(int32_t nnz, const int32_t *col, int32_t slice_cols,
+                             uint32_t *keys, hipStream_t s) {
+    if (nnz <= 0) return hipSuccess;
+    k_slice_keys<<<grid_for(nnz, kThreads), kThreads, 0, s>>>(nnz, col, slice_cols, keys);
     return hipGetLastError();
 }
 
-hipError_t launch_slice_fill(int32_t R, const int32_t *rp, const int32_t *col, const float *val,
-                             int32_t lo, int32_t hi, const int32_t *rp_out, int32_t *col_out,
-                             float *val_out, hipStream_t s) {
-    if (R <= 0) return hipSuccess;
-    k_slice_fill<<<grid_for(R, kThreads), kThreads, 0, s>>>(
-        R, rp, col, reinterpret_cast<const uint32_t *>(val), lo, hi, rp_out, col_out,
-        reinterpret_cast<uint32_t *>(val_out));
+hipError_t launch_slice_bounds(int32_t nnz, int32_t K, const uint32_t *keys, int32_t *bounds,
+                               hipStream_t s) {
+    k_slice_bounds<<<grid_for(static_cast<int64_t>(K) + 1, kThreads), kThreads, 0, s>>>(
+        nnz, K, keys, bounds);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_u32(int32_t n, const int32_t *perm, const uint32_t *in, uint32_t *out,
+                             hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    k_gather_u32<<<grid_for(n, kThreads), kThreads, 0, s>>>(n, perm, in, out);
     return hipGetLastError();
 }
 

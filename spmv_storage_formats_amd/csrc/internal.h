@@ -255,26 +255,28 @@ hipError_t launch_jds_lengths(int32_t R, int32_t W, const uint32_t *sorted_keys,
                               int32_t *jds_len, hipStream_t s);
 hipError_t launch_jds_counts(int32_t R, int32_t W, const int32_t *jds_len, int32_t *counts,
                              hipStream_t s);
-hipError_t launch_jds_fill(int32_t nnz, int32_t W, const int32_t *iter_ptr,
-                           const int32_t *perm, const int32_t *rp, const int32_t *col,
-                           const float *val, int32_t *jds_col, float *jds_val, hipStream_t s);
+hipError_t launch_jds_fill(int32_t R, int32_t ntiles, int32_t depth, const int2 *tiles,
+                           const int32_t *iter_ptr, const int32_t *perm, const int32_t *jds_len,
+                           const int32_t *rp, const int32_t *col, const float *val,
+                           int32_t *jds_col, float *jds_val, hipStream_t s);
 // Sectioned ELL: slots of each section of 64 sorted rows, and the fill.
 hipError_t launch_sell_sizes(int32_t R, const int32_t *jds_len, int32_t *sizes, hipStream_t s);
-hipError_t launch_sell_fill(int32_t R, int32_t nsect, int32_t slots, const int32_t *sect_ptr,
-                            const int32_t *jds_len, const int32_t *perm, const int32_t *rp,
-                            const int32_t *col, const float *val, int32_t *sell_col,
-                            float *sell_val, hipStream_t s);
+hipError_t launch_sell_fill(int32_t R, int32_t ntiles, int32_t depth, const int2 *tiles,
+                            const int32_t *sect_ptr, const int32_t *jds_len, const int32_t *perm,
+                            const int32_t *rp, const int32_t *col, const float *val,
+                            int32_t *sell_col, float *sell_val, hipStream_t s);
 hipError_t launch_jds_chunks(int32_t R, int32_t depth, const int32_t *jds_len,
                              int32_t *chunks, hipStream_t s);
 hipError_t launch_jds_tiles(int32_t groups, int32_t ntiles, const int32_t *tile_off,
                             int2 *tiles, hipStream_t s);
 // Column slice [lo, hi) of a CSR matrix: per-row counts, then the entries in
 // their original order (row pointers come from an exclusive scan of counts).
-hipError_t launch_slice_count(int32_t R, const int32_t *rp, const int32_t *col, int32_t lo,
-                              int32_t hi, int32_t *counts, hipStream_t s);
-hipError_t launch_slice_fill(int32_t R, const int32_t *rp, const int32_t *col, const float *val,
-                             int32_t lo, int32_t hi, const int32_t *rp_out, int32_t *col_out,
-                             float *val_out, hipStream_t s);
+hipError_t launch_slice_keys(int32_t nnz, const int32_t *col, int32_t slice_cols,
+                             uint32_t *keys, hipStream_t s);
+hipError_t launch_slice_bounds(int32_t nnz, int32_t K, const uint32_t *keys, int32_t *bounds,
+                               hipStream_t s);
+hipError_t launch_gather_u32(int32_t n, const int32_t *perm, const uint32_t *in, uint32_t *out,
+                             hipStream_t s);
 hipError_t launch_merge_partition(int32_t R, int32_t nnz, const int32_t *rp, int32_t nblocks,
                                   int32_t *row_start, hipStream_t s);
 

@@ -634,3 +634,45 @@ def test_cg_degenerate_cases(dev):
                     torch.zeros(0, dtype=torch.int32, device=dev),
                     torch.zeros(0, device=dev), 0)
     assert h0.cg(torch.zeros(0, device=dev), torch.zeros(0, device=dev)) == (0, 0.0)
+
+
+def _ragged_narrow():
+    """2^20 rows of 0..8 random entries (about 11 % empty): the 4-rows-per-lane
+    ELL path (R % 4 == 0, narrow width, large grid) with ragged rows."""
+    key = ("ragged_narrow",)
+    if key not in _cache:
+        rng = np.random.default_rng(2024)
+        w = synth.small_random(rng, 1 << 20, 1 << 20, max_len=8, empty_frac=0.0)
+        _cache[key] = (w, oracle.spmv_csr(w.row_ptrs, w.col_idx, w.values, w.x, w.y))
+    return _cache[key]
+
+
+@pytest.mark.parametrize("fmt,kw", [("ell", {}), ("hyb", {"hyb_width": 4}), ("hyb", {"hyb_width": 8})])
+def test_ell_four_rows_per_lane_ragged(dev, fmt, kw):
+    w, (yref, bound) = _ragged_narrow()
+    assert int(np.diff(w.row_ptrs).max()) == 8 and (np.diff(w.row_ptrs) == 0).any()
+    rp, ci, v, x, y0 = to_dev(w, dev)
+    h = spmv.build(fmt, rp, ci, v, w.num_cols, **kw)
+    yg = run_once(h, x, y0)
+    n_bad, first, worst = oracle.check(yg, yref, bound)
+    assert n_bad == 0, (first, worst)
+    # empty rows come back bit-identical
+    empty = np.diff(w.row_ptrs) == 0
+    assert np.array_equal(yg[empty].view(np.uint32), w.y[empty].view(np.uint32))
+
+
+def test_ell_unaligned_y_takes_the_row_per_lane_path(dev):
+    """y at a 4-byte offset (not 16-byte aligned): the launcher falls back to
+    one row per lane; results are the same."""
+    w, (yref, bound) = _ragged_narrow()
+    rp, ci, v, x, y0 = to_dev(w, dev)
+    h = spmv.build("ell", rp, ci, v, w.num_cols)
+    buf = torch.zeros(w.num_rows + 1, device=dev)
+    y = buf[1:]
+    y.copy_(y0)
+    assert y.data_ptr() % 16 != 0
+    h.run(x, y)
+    torch.cuda.synchronize()
+    n_bad, first, worst = oracle.check(y.cpu().numpy(), yref, bound)
+    assert n_bad == 0, (first, worst)
+    assert buf[0].item() == 0.0

@@ -122,8 +122,8 @@ __global__ __launch_bounds__(kThreads) void k_csr_scalar(int32_t R, const int32_
     const uint32_t b = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t r0 = static_cast<int64_t>(b) * kThreads;
     const int64_t r = r0 + threadIdx.x;
-    if (r <= R) srp[threadIdx.x] = rp[r];
-    if (threadIdx.x == 0 && r0 + kThreads <= R) srp[kThreads] = rp[r0 + kThreads];
+    if (r <= R) srp[threadIdx.x] = ld_nt(rp + r);
+    if (threadIdx.x == 0 && r0 + kThreads <= R) srp[kThreads] = ld_nt(rp + r0 + kThreads);
     __syncthreads();
     if (r >= R) return;
     const int32_t a = srp[threadIdx.x], e = srp[threadIdx.x + 1];
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kThreads) void k_csr_vector(int32_t R, const int32_
     const uint32_t b = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t r0 = static_cast<int64_t>(b) * kRows;
     for (int i = threadIdx.x; i <= kRows; i += kThreads)
-        if (r0 + i <= R) srp[i] = rp[r0 + i];
+        if (r0 + i <= R) srp[i] = ld_nt(rp + r0 + i);
     __syncthreads();
     const int g = threadIdx.x / L, lg = threadIdx.x % L;
     // Offsets inside a row are unsigned and relative to the row start: a row
@@ -374,7 +374,7 @@ __global__ __launch_bounds__(kThreads) void k_jds(int32_t R, int32_t ntiles, int
     const int g = __builtin_amdgcn_readfirstlane(gc.x);
     const int chunk = __builtin_amdgcn_readfirstlane(gc.y);
     const int64_t s = static_cast<int64_t>(g) * kWave + lane;
-    const int32_t len = s < R ? jds_len[s] : 0;
+    const int32_t len = s < R ? ld_nt(jds_len + s) : 0;
     const int32_t glen = __builtin_amdgcn_readfirstlane(jds_len[static_cast<int64_t>(g) * kWave]);
     // jagged-column counters in 64 bits: a row may hold INT32_MAX entries
     const int64_t t0 = static_cast<int64_t>(chunk) * depth;
@@ -413,7 +413,7 @@ __global__ __launch_bounds__(kThreads) void k_jds(int32_t R, int32_t ntiles, int
     }
     // y[perm[s]] is scattered: a non-returning atomic never stalls the wave on a
     // load (and with one contribution per row the result is still exact-order).
-    if (len > t0) atomic_add_f32(&y[perm[s]], sum);
+    if (len > t0) atomic_add_f32(&y[ld_nt(perm + s)], sum);
 }
 
 // ---------------------------------------------------------------------------
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(kThreads) void k_sell(int32_t R, int32_t ntiles, in
     const int64_t first = static_cast<int64_t>(k) * kWave;
     const int32_t m = static_cast<int32_t>(min(static_cast<int64_t>(kWave), R - first));
     const int64_t s = first + lane;
-    const int32_t len = lane < m ? sell_len[s] : 0;
+    const int32_t len = lane < m ? ld_nt(sell_len + s) : 0;
     const int32_t width = __builtin_amdgcn_readfirstlane(sell_len[first]);
     const int64_t base = __builtin_amdgcn_readfirstlane(sect_ptr[k]);
     const int64_t t0 = static_cast<int64_t>(chunk) * depth;
@@ -478,7 +478,7 @@ __global__ __launch_bounds__(kThreads) void k_sell(int32_t R, int32_t ntiles, in
             v[u] = vn[u];
         }
     }
-    if (len > t0) atomic_add_f32(&y[perm[s]], sum);
+    if (len > t0) atomic_add_f32(&y[ld_nt(perm + s)], sum);
 }
 
 // ---------------------------------------------------------------------------
@@ -515,7 +515,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(int32_t R, int32_t nnz,
     const int32_t nr = r1 - r0;
     const int32_t nk = k1 - k0;
 
-    for (int i = tid; i < nr; i += kMergeThreads) s_end[i] = rp[r0 + 1 + i] - k0;
+    for (int i = tid; i < nr; i += kMergeThreads) s_end[i] = ld_nt(rp + r0 + 1 + i) - k0;
     for (int j = tid; j < nk; j += kMergeThreads) {
         const int32_t kk = k0 + j;
         s_prod[j] = ld_nt(val + kk) * x[ld_nt(col + kk)];

@@ -578,12 +578,14 @@ hipError_t run_vector(const spmv_handle *h, const float *x, float *y, hipStream_
     return hipGetLastError();
 }
 
-hipError_t run_ell(int32_t R, int32_t W, const int32_t *col, const float *val,
+hipError_t run_ell(int32_t R, int32_t W, bool scattered, const int32_t *col, const float *val,
                    const int32_t *nnz_per_row, const float *x, float *y, hipStream_t s) {
     if (R <= 0 || W <= 0) return hipSuccess;
-    // 4 rows per lane only while the grid still spreads over the chip (>= 2
-    // blocks per CU); small matrices keep one row per lane
-    if (W <= 8 && R % 4 == 0 && blocks_of(R / 4, kThreads) >= 512 &&
+    // 4 rows per lane only for scattered columns (with banded columns the
+    // gathers of neighbouring one-row lanes coalesce, which 4 interleaved rows
+    // per lane break) and while the grid still spreads over the chip (>= 2
+    // blocks per CU)
+    if (scattered && W <= 8 && R % 4 == 0 && blocks_of(R / 4, kThreads) >= 512 &&
         reinterpret_cast<uintptr_t>(y) % 16 == 0) {
         k_ell4<4><<<blocks_of(R / 4, kThreads), kThreads, 0, s>>>(R, W, col, val, nnz_per_row, x,
                                                                  y);
@@ -619,6 +621,9 @@ spmv_status launch_spmv(const spmv_handle *h, const float *x, float *y, hipStrea
         return SPMV_OK;
     }
     const DevArrays &a = h->a;
+    // scattered columns: rows' first columns lie more than C/8 from the
+    // diagonal on average (the statistic the x-slice decision uses)
+    const bool scattered = h->stats.col_spread * 8 > h->stats.num_cols;
     hipError_t e = hipSuccess;
     switch (h->format) {
     case SPMV_COO_ATOMIC:
@@ -651,12 +656,12 @@ spmv_status launch_spmv(const spmv_handle *h, const float *x, float *y, hipStrea
         }
         break;
     case SPMV_ELL:
-        e = run_ell(R, h->ell_width, a.ell_col, a.ell_val, a.ell_nnz, x, y, s);
+        e = run_ell(R, h->ell_width, scattered, a.ell_col, a.ell_val, a.ell_nnz, x, y, s);
         break;
     case SPMV_HYB:
         // ELL part first (plain y update per row), then the COO tail with
         // atomics, in stream order: the two never touch y concurrently.
-        e = run_ell(R, h->ell_width, a.ell_col, a.ell_val, a.ell_nnz, x, y, s);
+        e = run_ell(R, h->ell_width, scattered, a.ell_col, a.ell_val, a.ell_nnz, x, y, s);
         if (e == hipSuccess)
             e = run_coo_segmented(static_cast<int32_t>(h->tail_nnz), a.tail_row, a.tail_col,
                                   a.tail_val, x, y, s);

@@ -202,6 +202,7 @@ def main():
         warm_ms = round(statistics.mean(warm_times), 5)
 
     traffic = measured_traffic(f"{args.config}/{selected}")
+    overhead_us = event_overhead_us(torch)
 
     result = {
         "metric": "SpMV GFLOP/s and effective HBM GB/s (% of MI355X peak) per format, 1 GPU",
@@ -222,6 +223,7 @@ def main():
         "effective_gbs": round(gbs, 1),
         "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
         "ms_median": round(med, 5),
+        "event_overhead_us": overhead_us,
         "warm_ms_per_step": warm_ms,
         "wall_s_timed_loop_incl_flush": round(wall, 4),
         "build_ms": round(build_ms, 2),
@@ -296,6 +298,23 @@ def cg_section(spmv, torch, oracle, synth, dev, flush_buf):
         out.append(entry)
         h.close()
     return out
+
+
+def event_overhead_us(torch):
+    """Median HIP-event time around one empty kernel (torch's spin kernel with
+    a zero count) on the same stream: the dispatch latency that per-step event
+    timing adds to a kernel's execution time (rocprofv3 counts execution only)."""
+    stream = torch.cuda.current_stream()
+    times = []
+    for i in range(60):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        torch.cuda._sleep(0)
+        b.record(stream)
+        b.synchronize()
+        if i >= 10:
+            times.append(a.elapsed_time(b))
+    return round(statistics.median(times) * 1e3, 2)
 
 
 def measured_traffic(key):

@@ -307,7 +307,11 @@ spmv_status spmv_run(const spmv_handle *h, const float *x_dev, float *y_dev, voi
  *   Stops when ||b - A x|| <= rtol * ||b|| (the recurrence residual, fp64
  *   dot products, tested every 8 iterations, so up to 7 iterations may run
  *   past the first that meets it) or after max_iter iterations, never more.
- *   *iters and *rel_resid report the iterations run and ||r|| / ||b||.  Allocates its
+ *   *iters and *rel_resid report the iterations run and ||r|| / ||b||.
+ *   From max_iter >= 16 on, each batch of 8 iterations is captured once as a
+ *   HIP graph and replayed (one launch per batch); setting the environment
+ *   variable SPMV_CG_GRAPH=0 launches every kernel directly instead (same
+ *   arithmetic, same results).  Allocates its
  *   three work vectors, runs every step on `stream`, host-synchronous.
  *   Symmetry and definiteness are the caller's promise (not checked).
  */

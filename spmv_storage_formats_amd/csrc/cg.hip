@@ -17,6 +17,8 @@
 // buffers.  The host adds the rr partials every kCheckEvery iterations to test
 // convergence.
 #include <cmath>
+#include <cstdlib>
+#include <cstring>
 #include <vector>
 
 #include "internal.h"
@@ -136,6 +138,61 @@ __global__ __launch_bounds__(kThreads) void k_cg_direction(int32_t n, int np,
     }
 }
 
+// One CG iteration's launches on `st`: SpMV, p·Ap, update, new direction.
+spmv_status enqueue_iteration(const spmv_handle *A, int32_t n, int np, float *x, float *r,
+                              float *p, float *ap, double *part_pap, double *const part_rr[2],
+                              int cur, hipStream_t st) {
+    SPMV_TRY(launch_spmv(A, p, ap, st));
+    k_dot<<<np, kThreads, 0, st>>>(n, p, ap, part_pap);
+    k_cg_update<<<np, kThreads, 0, st>>>(n, np, part_rr[cur], part_pap, p, ap, x, r,
+                                         part_rr[cur ^ 1]);
+    k_cg_direction<<<np, kThreads, 0, st>>>(n, np, part_rr[cur], part_rr[cur ^ 1], r, p, ap);
+    SPMV_HIP(hipGetLastError());
+    return SPMV_OK;
+}
+
+// A batch of kCheckEvery iterations captured once as a HIP graph and replayed
+// for every full batch: one launch instead of 4 * kCheckEvery (plus the
+// SpMV's own).  kCheckEvery is even, so every batch starts with the r·r
+// partials in the same buffer and one graph serves them all.  Nothing in the
+// batch allocates, synchronises or sets memory.
+struct BatchGraph {
+    hipStream_t launch = nullptr;   // where the replays run (drained before teardown)
+    hipStream_t cs = nullptr;       // capture stream
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    explicit BatchGraph(hipStream_t s) : launch(s) {}
+    ~BatchGraph() {
+        if (exec) (void)hipStreamSynchronize(launch);
+        if (exec) (void)hipGraphExecDestroy(exec);
+        if (graph) (void)hipGraphDestroy(graph);
+        if (cs) (void)hipStreamDestroy(cs);
+    }
+};
+
+static_assert(kCheckEvery % 2 == 0, "a batch must return the r.r partials to their buffer");
+
+spmv_status capture_batch(BatchGraph &g, const spmv_handle *A, int32_t n, int np, float *x,
+                          float *r, float *p, float *ap, double *part_pap,
+                          double *const part_rr[2], int cur) {
+    SPMV_HIP(hipStreamCreateWithFlags(&g.cs, hipStreamNonBlocking));
+    SPMV_HIP(hipStreamBeginCapture(g.cs, hipStreamCaptureModeThreadLocal));
+    spmv_status st = SPMV_OK;
+    for (int k = 0; k < kCheckEvery && st == SPMV_OK; ++k)
+        st = enqueue_iteration(A, n, np, x, r, p, ap, part_pap, part_rr, cur ^ (k & 1), g.cs);
+    const hipError_t e = hipStreamEndCapture(g.cs, &g.graph);
+    if (st != SPMV_OK) return st;
+    SPMV_HIP(e);
+    SPMV_HIP(hipGraphInstantiate(&g.exec, g.graph, nullptr, nullptr, 0));
+    return SPMV_OK;
+}
+
+// Graphs are used unless SPMV_CG_GRAPH=0 (eager launches, for comparison).
+bool graphs_enabled() {
+    const char *v = std::getenv("SPMV_CG_GRAPH");
+    return !(v && std::strcmp(v, "0") == 0);
+}
+
 // Host sum of device partials, in block order.
 spmv_status host_sum(const double *part, int np, std::vector<double> &buf, double *out,
                      hipStream_t s) {
@@ -182,17 +239,19 @@ spmv_status conjugate_gradient(const spmv_handle *A, const float *b, float *x, i
     double rnorm = std::sqrt(rr);
     int cur = 0;   // part_rr[cur] holds the current r·r partials
     int32_t it = 0;
+    // a graph pays for its capture from the second full batch on
+    const bool use_graph = graphs_enabled() && max_iter >= 2 * kCheckEvery;
+    BatchGraph g(s);
     while (it < max_iter && rnorm > target) {
         const int32_t batch = std::min(kCheckEvery, max_iter - it);
-        for (int32_t k = 0; k < batch; ++k) {
-            SPMV_TRY(launch_spmv(A, p, ap, s));
-            k_dot<<<np, kThreads, 0, s>>>(n, p, ap, part_pap);
-            k_cg_update<<<np, kThreads, 0, s>>>(n, np, part_rr[cur], part_pap, p, ap, x, r,
-                                                part_rr[cur ^ 1]);
-            k_cg_direction<<<np, kThreads, 0, s>>>(n, np, part_rr[cur], part_rr[cur ^ 1], r, p,
-                                                   ap);
-            SPMV_HIP(hipGetLastError());
-            cur ^= 1;
+        if (use_graph && batch == kCheckEvery) {
+            if (!g.exec) SPMV_TRY(capture_batch(g, A, n, np, x, r, p, ap, part_pap, part_rr, cur));
+            SPMV_HIP(hipGraphLaunch(g.exec, s));
+        } else {
+            for (int32_t k = 0; k < batch; ++k) {
+                SPMV_TRY(enqueue_iteration(A, n, np, x, r, p, ap, part_pap, part_rr, cur, s));
+                cur ^= 1;
+            }
         }
         it += batch;
         SPMV_TRY(host_sum(part_rr[cur], np, host, &rr, s));

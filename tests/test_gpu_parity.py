@@ -676,3 +676,30 @@ def test_ell_unaligned_y_takes_the_row_per_lane_path(dev):
     n_bad, first, worst = oracle.check(y.cpu().numpy(), yref, bound)
     assert n_bad == 0, (first, worst)
     assert buf[0].item() == 0.0
+
+
+@pytest.mark.parametrize("fmt", ["ell", "sell", "sliced"])
+def test_cg_graph_replays_match_eager(dev, fmt, monkeypatch):
+    """From 16 iterations on, CG replays one captured 8-iteration graph per
+    batch, with host synchronisation and reads between replays.  After every
+    number of replays tried, x equals the eager launches' x: bit for bit for
+    formats with a fixed summation order, else within k*kappa*2^-24*max|x|."""
+    w = W("c1s")
+    b = torch.from_numpy(_cg_rhs(w)).to(dev)
+    h = build("csr_merge", w, dev, col_blocks=2) if fmt == "sliced" else build(fmt, w, dev)
+    n = int(round(np.sqrt(w.num_rows)))
+    kappa = (2 * (n + 1) / np.pi) ** 2
+    for batches in (2, 3, 5):
+        k = 8 * batches
+        xs = {}
+        for mode in ("1", "0"):
+            monkeypatch.setenv("SPMV_CG_GRAPH", mode)
+            x = torch.zeros(w.num_rows, device=dev)
+            iters, _ = h.cg(b, x, max_iter=k, rtol=0.0)
+            assert iters == k
+            xs[mode] = x.cpu().numpy()
+        if fmt == "sliced":
+            tol = k * kappa * 2.0**-24 * np.max(np.abs(xs["0"]))
+            assert np.max(np.abs(xs["1"] - xs["0"])) <= tol, batches
+        else:
+            assert np.array_equal(xs["1"].view(np.uint32), xs["0"].view(np.uint32)), batches

@@ -682,8 +682,12 @@ spmv_status spmv_build_tuned(spmv_handle **out, int32_t R, int32_t C, int32_t nn
                 oc.max_bytes = std::max<int64_t>(int64_t(64) << 20, 8 * csr);
             }
             spmv_handle *raw = nullptr;
-            spmv_status st = build_csr_impl(&raw, static_cast<spmv_format>(f), R, C, nnz, rp,
-                                            col, val, oc, s, scratch);
+            spmv_status st;
+            {
+                Scratch cand(s);   // the candidate's build scratch, freed before the next
+                st = build_csr_impl(&raw, static_cast<spmv_format>(f), R, C, nnz, rp, col, val,
+                                    oc, s, cand);
+            }
             HandlePtr h(raw);
             ent.status = st;
             if (st != SPMV_OK) {

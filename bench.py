@@ -86,7 +86,32 @@ def cpu_baseline(w, budget_s=10.0):
     return {"value": round(2 * w.nnz / t / 1e9, 4), "unit": "GFLOP/s", "cores": 1,
             "kind": "oracle",
             "sample": f"{n} full passes of the same {w.num_rows}-row matrix "
-                      f"({w.nnz} nnz), {t * 1e3:.1f} ms each, single thread, fp64 sums"}
+                      f"({w.nnz} nnz), {t * 1e3:.1f} ms each, single thread, fp64 sums",
+            "openmp": openmp_baseline(w, budget_s / 2)}
+
+
+def openmp_baseline(w, budget_s=5.0):
+    """An OpenMP CSR SpMV (rows split over the host's threads, fp64 row sums)
+    on full passes of the same matrix, checked against the oracle first."""
+    import numpy as np
+    import oracle
+    y_ref, bound = oracle.spmv_csr(w.row_ptrs, w.col_idx, w.values, w.x, w.y)
+    y = oracle.spmv_csr_omp(w.row_ptrs, w.col_idx, w.values, w.x, w.y)
+    n_bad, _, _ = oracle.check(y, y_ref, bound)
+    if n_bad:
+        raise RuntimeError(f"OpenMP CSR baseline: {n_bad} rows out of bound")
+    n, t_total = 0, 0.0
+    while t_total < budget_s or n < 3:
+        t0 = time.perf_counter()
+        oracle.spmv_csr_omp(w.row_ptrs, w.col_idx, w.values, w.x, w.y)
+        t_total += time.perf_counter() - t0
+        n += 1
+    t = t_total / n
+    threads = oracle.omp_threads()
+    return {"value": round(2 * w.nnz / t / 1e9, 4), "unit": "GFLOP/s", "cores": threads,
+            "kind": "openmp_csr",
+            "sample": f"{n} full passes of the same {w.num_rows}-row matrix, {t * 1e3:.2f} ms "
+                      f"each, {threads} OpenMP threads, fp64 row sums (includes a y copy)"}
 
 
 def main():

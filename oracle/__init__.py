@@ -21,6 +21,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+_OMP_SRC = os.path.join(_HERE, "csr_omp.c")
+_OMP_LIB = os.path.join(_HERE, "libcsr_omp.so")
+_omp = None
 _lock = threading.Lock()
 _lib = None
 
@@ -38,13 +41,20 @@ _i64 = ctypes.c_int64
 
 
 def build(force: bool = False) -> str:
-    """Compile oracle.c into liboracle.so (gcc, no fast-math, no FMA contraction)."""
+    """Compile oracle.c into liboracle.so (gcc, no fast-math, no FMA contraction)
+    and the OpenMP CSR baseline csr_omp.c into libcsr_omp.so."""
     with _lock:
         if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
             tmp = _LIB + f".tmp{os.getpid()}"
             subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared",
                                    "-ffp-contract=off", "-fno-fast-math", _SRC, "-o", tmp, "-lm"])
             os.replace(tmp, _LIB)
+        if (force or not os.path.exists(_OMP_LIB)
+                or os.path.getmtime(_OMP_LIB) < os.path.getmtime(_OMP_SRC)):
+            tmp = _OMP_LIB + f".tmp{os.getpid()}"
+            subprocess.check_call(["gcc", "-O3", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+                                   "-ffp-contract=off", "-fno-fast-math", _OMP_SRC, "-o", tmp])
+            os.replace(tmp, _OMP_LIB)
     return _LIB
 
 
@@ -288,3 +298,32 @@ def cg(row_ptrs, col_idx, values, b, x0=None, max_iter=1000, rtol=1e-6):
     _load().orc_cg(R, rp, _i32(col_idx), _f32(values), np.ascontiguousarray(b, np.float64), x,
                    int(max_iter), float(rtol), out)
     return x, int(out[0]), float(out[1])
+
+
+# ------------------------------------------------------------------ OpenMP baseline
+
+def _load_omp():
+    global _omp
+    if _omp is not None:
+        return _omp
+    build()
+    lib = ctypes.CDLL(_OMP_LIB)
+    lib.csr_omp_threads.restype = ctypes.c_int
+    lib.csr_omp_threads.argtypes = []
+    lib.csr_spmv_omp.restype = None
+    lib.csr_spmv_omp.argtypes = [_i64, _i32p, _i32p, _f32p, _f32p, _f32p]
+    _omp = lib
+    return lib
+
+
+def omp_threads() -> int:
+    """Threads the OpenMP baseline runs with (OMP_NUM_THREADS or all cores)."""
+    return int(_load_omp().csr_omp_threads())
+
+
+def spmv_csr_omp(row_ptrs, col_idx, values, x, y):
+    """OpenMP CSR baseline: returns fp32 y + A x (fp64 row sums, row order)."""
+    rp = _i32(row_ptrs)
+    out = np.array(y, dtype=np.float32, copy=True)
+    _load_omp().csr_spmv_omp(rp.shape[0] - 1, rp, _i32(col_idx), _f32(values), _f32(x), out)
+    return out

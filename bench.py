@@ -345,7 +345,7 @@ def event_overhead_us(torch):
 def measured_traffic(key):
     """HBM bytes per launch from the committed PMC summary, or None when the
     summary has no entry for `key` or the kernels changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", "pmc_traffic.md")
+    path = os.path.join(ROOT, "profiles", "ell_random_rows_1Mx5_stencil27_128_pmc_traffic.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()

@@ -703,3 +703,71 @@ def test_cg_graph_replays_match_eager(dev, fmt, monkeypatch):
             assert np.max(np.abs(xs["1"] - xs["0"])) <= tol, batches
         else:
             assert np.array_equal(xs["1"].view(np.uint32), xs["0"].view(np.uint32)), batches
+
+
+def test_build_destroy_cycles_release_device_memory(dev):
+    """Handles own their device arrays and free them on destroy; builders free
+    their scratch: 30 build/run/destroy cycles over every format leave the
+    device's free memory where it was."""
+    w = W("c2s")
+    rp, ci, v, x, y0 = to_dev(w, dev)
+
+    def cycle(i):
+        fmt = ALL_FORMATS[i % len(ALL_FORMATS)]
+        h = spmv.build(fmt, rp, ci, v, w.num_cols, col_blocks=2 if i % 3 == 0 else 0)
+        y = y0.clone()
+        h.run(x, y)
+        h.close()
+
+    # one pass first: the runtime loads each kernel's code and sets up its own
+    # pools on first use
+    for i in range(2 * len(ALL_FORMATS)):
+        cycle(i)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    free0, _ = torch.cuda.mem_get_info()
+    for i in range(30):
+        cycle(i)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    free1, _ = torch.cuda.mem_get_info()
+    assert free1 >= free0 - (2 << 20), (free0, free1)
+
+
+def test_concurrent_host_threads_and_streams(dev):
+    """Four host threads each build a handle and run it 20 times on their own
+    stream (ctypes releases the GIL during library calls); every result is
+    checked against the oracle."""
+    import threading
+    names = ["c1s", "c2s", "c3s", "c4s"]
+    fmts = ["ell", "csr_merge", "sell", "hyb"]
+    results, errors = {}, []
+    inputs = {n: to_dev(W(n), dev) for n in names}
+    torch.cuda.synchronize()   # the copies above ran on the default stream
+
+    def work(name, fmt):
+        try:
+            w = W(name)
+            rp, ci, v, x, y0 = inputs[name]
+            st = torch.cuda.Stream(device=dev)
+            with torch.cuda.stream(st):
+                h = spmv.build(fmt, rp, ci, v, w.num_cols, stream=st)
+                for _ in range(20):
+                    y = y0.clone()
+                    h.run(x, y, stream=st)
+                st.synchronize()
+                results[name] = y.cpu().numpy()
+                h.close()
+        except Exception as e:   # reported below
+            errors.append((name, fmt, repr(e)))
+
+    threads = [threading.Thread(target=work, args=a) for a in zip(names, fmts)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for name in names:
+        yref, bound = ref(name)
+        n_bad, first, worst = oracle.check(results[name], yref, bound)
+        assert n_bad == 0, (name, first, worst)

@@ -257,6 +257,7 @@ def main():
                      "traffic": traffic, "bytes_per_launch_alg": B},
         "formats": per_format,
     }
+    result["coo_to_csr"] = coo_section(spmv, torch, w, dev)
     if args.cg:
         result["cg"] = cg_section(spmv, torch, oracle, synth, dev, flush_buf)
     if args.calibrate_copy:
@@ -272,6 +273,33 @@ def main():
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def coo_section(spmv, torch, w, dev):
+    """COO -> CSR on the device for the same matrix given as a COO list in
+    random order (the stable-sort path) and in row order (count and scan
+    only): median of 5 host-timed calls, each host-synchronous."""
+    import numpy as np
+    rows = np.repeat(np.arange(w.num_rows, dtype=np.int32), np.diff(w.row_ptrs))
+    p = np.random.default_rng(0).permutation(w.nnz)
+    out = {}
+    for label, order in (("shuffled", p), ("row_sorted", None)):
+        sel = (lambda a: a[order]) if order is not None else (lambda a: a)
+        ri = torch.from_numpy(sel(rows)).to(dev)
+        ci = torch.from_numpy(sel(w.col_idx)).to(dev)
+        va = torch.from_numpy(sel(w.values)).to(dev)
+        spmv.coo_to_csr(ri, ci, va, w.num_rows, w.num_cols)
+        ts = []
+        for _ in range(5):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            spmv.coo_to_csr(ri, ci, va, w.num_rows, w.num_cols)
+            ts.append(time.perf_counter() - t0)
+        ms = statistics.median(ts) * 1e3
+        out[label + "_ms"] = round(ms, 3)
+        out[label + "_g_entries_per_s"] = round(w.nnz / ms / 1e6, 2)
+        del ri, ci, va
+    return out
 
 
 def cg_section(spmv, torch, oracle, synth, dev, flush_buf):

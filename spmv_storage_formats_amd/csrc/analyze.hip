@@ -103,24 +103,34 @@ __global__ __launch_bounds__(kThreads) void k_col_checks(int32_t nnz, int32_t C,
     if (__ballot(bad) != 0 && __lane_id() == 0) atomicOr(&st->flags, kFlagBadCol);
 }
 
+// COO input checks: row and column ranges, and whether the rows are already
+// sorted.  Grid-stride over a capped grid; each block writes its flags to
+// partial[blockIdx.x] (no same-address atomics: on an unsorted list every wave
+// would set the flag) and the host ORs them.
 __global__ __launch_bounds__(kThreads) void k_coo_checks(int32_t nnz, int32_t R, int32_t C,
                                                          const int32_t *__restrict__ row,
                                                          const int32_t *__restrict__ col,
                                                          int check_cols,
-                                                         RowStatsDev *__restrict__ st) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+                                                         int *__restrict__ partial) {
     bool bad_row = false, bad_col = false, unsorted = false;
-    if (i < nnz) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < nnz;
+         i += stride) {
         const int32_t r = row[i];
-        bad_row = static_cast<uint32_t>(r) >= static_cast<uint32_t>(R);
-        if (check_cols) bad_col = static_cast<uint32_t>(col[i]) >= static_cast<uint32_t>(C);
-        if (i + 1 < nnz) unsorted = row[i + 1] < r;
+        bad_row |= static_cast<uint32_t>(r) >= static_cast<uint32_t>(R);
+        if (check_cols) bad_col |= static_cast<uint32_t>(col[i]) >= static_cast<uint32_t>(C);
+        if (i + 1 < nnz) unsorted |= row[i + 1] < r;
     }
-    const bool br = __ballot(bad_row) != 0, bc = __ballot(bad_col) != 0,
-               un = __ballot(unsorted) != 0;
-    if (__lane_id() == 0 && (br || bc || un))
-        atomicOr(&st->flags, (br ? kFlagBadRow : 0) | (bc ? kFlagBadCol : 0) |
-                                 (un ? kFlagUnsortedRows : 0));
+    const int f = (__ballot(bad_row) ? kFlagBadRow : 0) | (__ballot(bad_col) ? kFlagBadCol : 0) |
+                  (__ballot(unsorted) ? kFlagUnsortedRows : 0);
+    __shared__ int wf[kThreads / kWave];
+    if (__lane_id() == 0) wf[threadIdx.x / kWave] = f;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int t = 0;
+        for (int k = 0; k < kThreads / kWave; ++k) t |= wf[k];
+        partial[blockIdx.x] = t;
+    }
 }
 
 // hist[len] += 1 per row; short lengths are binned in LDS, long ones directly.
@@ -161,11 +171,15 @@ hipError_t launch_col_checks(int32_t nnz, int32_t C, const int32_t *col, RowStat
     return hipGetLastError();
 }
 
+int coo_check_blocks(int32_t nnz) {
+    unsigned g = grid_for(nnz > 0 ? nnz : 1, kThreads);
+    return static_cast<int>(g > kCooCheckMaxBlocks ? kCooCheckMaxBlocks : g);
+}
+
 hipError_t launch_coo_checks(int32_t nnz, int32_t R, int32_t C, const int32_t *row,
-                             const int32_t *col, int check_cols, RowStatsDev *st, hipStream_t s) {
-    if (nnz <= 0) return hipSuccess;
-    k_coo_checks<<<grid_for(nnz, kThreads), kThreads, 0, s>>>(nnz, R, C, row, col, check_cols,
-                                                              st);
+                             const int32_t *col, int check_cols, int *partial, hipStream_t s) {
+    k_coo_checks<<<coo_check_blocks(nnz), kThreads, 0, s>>>(nnz, R, C, row, col, check_cols,
+                                                            partial);
     return hipGetLastError();
 }
 

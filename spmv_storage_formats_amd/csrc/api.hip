@@ -534,26 +534,37 @@ spmv_status build_csr_impl(spmv_handle **out, spmv_format fmt, int32_t R, int32_
 spmv_status coo_to_csr_impl(int32_t R, int32_t C, int32_t nnz, const int32_t *ri,
                             const int32_t *ci, const float *v, int32_t *rp_out, int32_t *c_out,
                             float *v_out, bool validate, hipStream_t s, Scratch &scratch) {
-    RowStatsDev *d = nullptr;
-    SPMV_TRY(scratch.alloc(&d, 1));
-    SPMV_HIP(hipMemsetAsync(d, 0, sizeof(RowStatsDev), s));
-    SPMV_HIP(launch_coo_checks(nnz, R, C, ri, ci, validate ? 1 : 0, d, s));
-    RowStatsDev h{};
-    SPMV_HIP(hipMemcpyAsync(&h, d, sizeof(h), hipMemcpyDeviceToHost, s));
-    SPMV_HIP(hipStreamSynchronize(s));
-    if (h.flags & kFlagBadRow) return SPMV_ERR_BAD_ROWIDX;
-    if (h.flags & kFlagBadCol) return SPMV_ERR_BAD_COLIDX;
-    // (i) entries per row, (ii) exclusive scan -> rowPtrs (rowPtrs[R] = nnz)
-    SPMV_HIP(hipMemsetAsync(rp_out, 0, sizeof(int32_t) * (static_cast<size_t>(R) + 1), s));
-    SPMV_HIP(launch_count_rows(nnz, ri, rp_out, s));
-    SPMV_TRY(exclusive_scan(rp_out, rp_out, R, true, s, scratch));
-    if (nnz == 0) return SPMV_OK;
-    // (iii) stable scatter by row
-    if (!(h.flags & kFlagUnsortedRows)) {
+    int flags = 0;
+    if (nnz > 0) {
+        const int nb = coo_check_blocks(nnz);
+        int *part = nullptr;
+        SPMV_TRY(scratch.alloc(&part, static_cast<size_t>(nb)));
+        SPMV_HIP(launch_coo_checks(nnz, R, C, ri, ci, validate ? 1 : 0, part, s));
+        std::vector<int> hp(static_cast<size_t>(nb));
+        SPMV_HIP(hipMemcpyAsync(hp.data(), part, sizeof(int) * nb, hipMemcpyDeviceToHost, s));
+        SPMV_HIP(hipStreamSynchronize(s));
+        for (int f : hp) flags |= f;
+    }
+    if (flags & kFlagBadRow) return SPMV_ERR_BAD_ROWIDX;
+    if (flags & kFlagBadCol) return SPMV_ERR_BAD_COLIDX;
+    if (nnz == 0) {
+        SPMV_HIP(hipMemsetAsync(rp_out, 0, sizeof(int32_t) * (static_cast<size_t>(R) + 1), s));
+        return SPMV_OK;
+    }
+    if (!(flags & kFlagUnsortedRows)) {
+        // already grouped by row: (i) entries per row (one atomic per run),
+        // (ii) exclusive scan -> rowPtrs, (iii) the entries stay where they are
+        SPMV_HIP(hipMemsetAsync(rp_out, 0, sizeof(int32_t) * (static_cast<size_t>(R) + 1), s));
+        SPMV_HIP(launch_count_rows(nnz, ri, rp_out, s));
+        SPMV_TRY(exclusive_scan(rp_out, rp_out, R, true, s, scratch));
         SPMV_HIP(hipMemcpyAsync(c_out, ci, sizeof(int32_t) * nnz, hipMemcpyDeviceToDevice, s));
         SPMV_HIP(hipMemcpyAsync(v_out, v, sizeof(float) * nnz, hipMemcpyDeviceToDevice, s));
         return SPMV_OK;
     }
+    // stable sort of the entries by row (entries of a row keep their input
+    // order); the row counts are then taken on the sorted rows (one atomic per
+    // run of equal rows per wave instead of one per entry), scanned into
+    // rowPtrs, and the columns and values moved
     int32_t *idx = nullptr, *perm = nullptr;
     uint32_t *keys_sorted = nullptr;
     SPMV_TRY(scratch.alloc(&idx, nnz));
@@ -562,6 +573,9 @@ spmv_status coo_to_csr_impl(int32_t R, int32_t C, int32_t nnz, const int32_t *ri
     SPMV_HIP(launch_iota(nnz, idx, s));
     SPMV_TRY(radix_sort_pairs(reinterpret_cast<const uint32_t *>(ri), idx, keys_sorted, perm, nnz,
                               bits_for(R > 0 ? static_cast<uint64_t>(R - 1) : 0), s, scratch));
+    SPMV_HIP(hipMemsetAsync(rp_out, 0, sizeof(int32_t) * (static_cast<size_t>(R) + 1), s));
+    SPMV_HIP(launch_count_rows(nnz, reinterpret_cast<const int32_t *>(keys_sorted), rp_out, s));
+    SPMV_TRY(exclusive_scan(rp_out, rp_out, R, true, s, scratch));
     SPMV_HIP(launch_gather_pairs(nnz, perm, ci, v, c_out, v_out, s));
     return SPMV_OK;
 }

@@ -218,8 +218,12 @@ hipError_t launch_row_checks(int32_t R, int32_t C, int32_t nnz, const int32_t *r
                              const int32_t *col, RowStatsDev *partial, hipStream_t s);
 hipError_t launch_col_checks(int32_t nnz, int32_t C, const int32_t *col, RowStatsDev *st,
                              hipStream_t s);
+// COO checks write one flags word per block (coo_check_blocks(nnz) words, at
+// most kCooCheckMaxBlocks); the caller ORs them.
+constexpr int kCooCheckMaxBlocks = 1024;
+int coo_check_blocks(int32_t nnz);
 hipError_t launch_coo_checks(int32_t nnz, int32_t R, int32_t C, const int32_t *row,
-                             const int32_t *col, int check_cols, RowStatsDev *st, hipStream_t s);
+                             const int32_t *col, int check_cols, int *partial, hipStream_t s);
 hipError_t launch_len_hist(int32_t R, const int32_t *rp, int32_t W, int32_t *hist, hipStream_t s);
 
 // scan.hip: exclusive scan of n int32 values; out[n] receives the total when

@@ -257,7 +257,8 @@ def main():
                      "traffic": traffic, "bytes_per_launch_alg": B},
         "formats": per_format,
     }
-    result["coo_to_csr"] = coo_section(spmv, torch, w, dev)
+    if not args.only_selected:
+        result["coo_to_csr"] = coo_section(spmv, torch, w, dev)
     if args.cg:
         result["cg"] = cg_section(spmv, torch, oracle, synth, dev, flush_buf)
     if args.calibrate_copy:

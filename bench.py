@@ -31,7 +31,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, vendor figure
 FLUSH_BYTES = 1 << 30       # > 256 MB MALL + 8 x 4 MB L2
 FORMATS = ["coo_atomic", "coo_segmented", "csr_scalar", "csr_vector", "ell", "hyb", "jds",
-           "csr_merge", "sell"]
+           "csr_merge", "sell", "ell_xtile"]
 WORKLOAD_NAMES = {
     "c1": "laplacian2d_256 (65,536 rows, 5-point, 326,656 nnz)",
     "c2": "random_rows_1Mx5 (1,000,000 x 1,000,000, 5 random cols/row, 5,000,000 nnz)",

@@ -79,10 +79,21 @@ typedef enum spmv_format {
     SPMV_JDS = 7,           /* rows sorted by length, jagged column-major [REG, JDS]       */
     SPMV_CSR_MERGE = 8,     /* merge-path: equal shares of rows+nonzeros per block
                                [CHOICE 5.2; INTRO, parallel efficiency]                    */
-    SPMV_SELL = 9           /* sectioned ELL, the JDS variant: rows sorted by length, cut
+    SPMV_SELL = 9,          /* sectioned ELL, the JDS variant: rows sorted by length, cut
                                into sections of 64 sorted rows, each an ELL padded to its
                                own longest row [REG, JDS variant].  Never picked by
                                SPMV_AUTO (the selector rule has no branch for it).         */
+    SPMV_ELL_XTILE = 10     /* ELL whose x gathers come from LDS [REG, ELL slot layout;
+                               INTRO x blocking; CHOICE 4.2 staging]: rows in blocks of
+                               256; a block's tile is the sorted set of the distinct
+                               columns of its entries, kept as runs of consecutive
+                               columns; the column array holds int16 tile positions.
+                               Refused (SPMV_ERR_TOO_LARGE) unless every block spans
+                               < 2^18 columns, has <= 8192 distinct ones in <= 1024 runs,
+                               and R*W <= INT32_MAX.  SPMV_AUTO takes it in place of ELL
+                               for R >= 16384 when every block qualifies and nnz >= 2 *
+                               (sum over blocks of the tile sizes): each x word staged
+                               serves two gathers or more, as on banded 3-D stencils.    */
 } spmv_format;
 
 typedef struct spmv_opts {
@@ -157,7 +168,14 @@ typedef enum spmv_array {
                               sect_ptr[k] + t*m_k + i, m_k = rows in section k;
                               padding (0, +0.0f).  Sorted-row order and lengths
                               are SPMV_A_JDS_PERM / SPMV_A_JDS_LEN.          */
-    SPMV_A_SELL_VAL = 18   /* fp32  [slots]                                    */
+    SPMV_A_SELL_VAL = 18,  /* fp32  [slots]                                    */
+    SPMV_A_XT_RUN_PTR = 19, /* int32 [B+1]  ELL x tiles: runs of block b (rows 256b ..
+                              256b+255) are [run_ptr[b], run_ptr[b+1]), B = ceil(R/256) */
+    SPMV_A_XT_RUNS = 20,   /* int32 [3*runs] run k: first column, offset in its block's
+                              tile, length                                          */
+    SPMV_A_XT_LIDX = 21    /* int16 [R*W]   slot t of row r at t*R+r: tile position of
+                              the entry's column, padding 0.  Values and row lengths:
+                              SPMV_A_ELL_VAL, SPMV_A_ELL_NNZ.                       */
 } spmv_array;
 
 typedef struct spmv_handle spmv_handle;
@@ -259,7 +277,7 @@ spmv_status spmv_coo_to_csr(int32_t num_rows, int32_t num_cols, int32_t nnz,
  * spmv_build_tuned -- the empirical selector [CHOICE 4.3: a tool that times
  * the formats on the matrix itself and keeps the fastest].
  *   Tries every concrete format whose bit is set in `format_mask` (bit f for
- *   spmv_format f, 1..9; 0 = all nine), each unsplit and -- when the matrix
+ *   spmv_format f, 1..10; 0 = all ten), each unsplit and -- when the matrix
  *   is one that SPMV_AUTO would cut into x slices -- also sliced.  Each
  *   candidate that builds is run once to warm up and then `runs` times
  *   (0: 5) back to back on device scratch vectors (x = 0, y = 0: the kernels

@@ -88,6 +88,10 @@ def _load():
         "orc_select": (None, [_i64, _i64, _i64, _i64p, _i64, _i64, _i64p]),
         "orc_cg": (ctypes.c_int, [_i64, _i32p, _i32p, _f32p, _f64p, _f64p, _i64,
                                   ctypes.c_double, _f64p]),
+        "orc_csr_to_ell_xtile": (ctypes.c_int, [_i64, _i32p, _i32p, _u32p, _i64, _i64,
+                                                ctypes.c_void_p, ctypes.c_void_p,
+                                                ctypes.c_void_p, ctypes.c_void_p,
+                                                ctypes.c_void_p, ctypes.POINTER(_i64)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -244,6 +248,35 @@ def csr_to_jds(row_ptrs, col_idx, values):
     jv = np.empty(nnz, np.uint32)
     _load().orc_csr_to_jds(R, rp, _i32(col_idx), _bits(values), W, perm, jlen, iptr, jc, jv)
     return {"perm": perm, "len": jlen, "iter_ptr": iptr, "col": jc, "val": jv.view(np.float32)}
+
+
+def csr_to_ell_xtile(row_ptrs, col_idx, values, block_rows=256):
+    """ELL with x tiles: run_ptr, runs (k x 3: first column, tile offset, length),
+    lidx (int16, column-major slots), val, nnz.  ValueError("too large") when refused."""
+    rp = _i32(row_ptrs)
+    R = rp.shape[0] - 1
+    ci = _i32(col_idx)
+    vb = _bits(values)
+    W = int(np.diff(rp.astype(np.int64)).max()) if R > 0 else 0
+    lib = _load()
+    total = _i64(0)
+    st = lib.orc_csr_to_ell_xtile(R, rp, ci, vb, W, block_rows, None, None, None, None, None,
+                                  ctypes.byref(total))
+    if st == ERR_TOO_LARGE:
+        raise ValueError("too large")
+    nb = (R + block_rows - 1) // block_rows
+    run_ptr = np.zeros(nb + 1, np.int32)
+    runs = np.zeros(3 * max(total.value, 1), np.int32)
+    lidx = np.zeros(max(R * W, 1), np.int16)
+    val = np.zeros(max(R * W, 1), np.uint32)
+    nnz = np.zeros(max(R, 1), np.int32)
+    st = lib.orc_csr_to_ell_xtile(R, rp, ci, vb, W, block_rows, run_ptr.ctypes.data,
+                                  runs.ctypes.data, lidx.ctypes.data, val.ctypes.data,
+                                  nnz.ctypes.data, ctypes.byref(total))
+    assert st == OK
+    return {"run_ptr": run_ptr, "runs": runs[:3 * total.value].reshape(-1, 3),
+            "lidx": lidx[:R * W], "val": val[:R * W].view(np.float32), "nnz": nnz[:R],
+            "width": W, "block_rows": block_rows}
 
 
 def csr_to_sell(row_ptrs, col_idx, values, section=64):

@@ -589,3 +589,105 @@ int orc_cg(int64_t R, const int32_t *row_ptrs, const int32_t *col_idx, const flo
     free(r); free(p); free(ap);
     return ORC_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* ELL with x tiles [REG, ELL slot layout; INTRO, x blocking].  Rows in      */
+/* blocks of B.  Block b's tile is the set of distinct columns of its        */
+/* entries in increasing order; a run is a maximal stretch of consecutive    */
+/* columns in the tile, stored as (first column, offset of that column in    */
+/* the tile, length).  Slot t of row r (at t*R + r, as in ELL) holds the     */
+/* tile position of the entry's column (int16) and its value; slots past     */
+/* the row's length hold (0, +0.0f).  ell_nnz[r] = row length.              */
+/* Refused (ORC_ERR_TOO_LARGE) when R*W > INT32_MAX or a block's columns     */
+/* span more than 2^18 (greatest - least + 1) or it has more than 8192       */
+/* distinct columns or more than 1024 runs.                                  */
+/* With runs == NULL only *runs_total is computed (sizing call).             */
+/* ------------------------------------------------------------------------ */
+
+static int orc_cmp_i32(const void *a, const void *b)
+{
+    const int32_t x = *(const int32_t *)a, y = *(const int32_t *)b;
+    return (x > y) - (x < y);
+}
+
+int orc_csr_to_ell_xtile(int64_t R, const int32_t *row_ptrs, const int32_t *col_idx,
+                         const uint32_t *val_bits, int64_t W, int64_t B, int32_t *run_ptr,
+                         int32_t *runs, int16_t *lidx, uint32_t *ell_val, int32_t *ell_nnz,
+                         int64_t *runs_total)
+{
+    if (R * W > ORC_INT32_MAX)
+        return ORC_ERR_TOO_LARGE;
+    int64_t nb = (R + B - 1) / B;
+    int64_t maxn = 0;
+    for (int64_t b = 0; b < nb; ++b) {
+        int64_t r0 = b * B, r1 = r0 + B < R ? r0 + B : R;
+        int64_t n = (int64_t)row_ptrs[r1] - row_ptrs[r0];
+        if (n > maxn)
+            maxn = n;
+    }
+    int32_t *tile = (int32_t *)malloc(sizeof(int32_t) * (size_t)(maxn > 0 ? maxn : 1));
+    if (!tile)
+        return ORC_ERR_INVALID_ARG;
+    int64_t total = 0;
+    if (run_ptr)
+        run_ptr[0] = 0;
+    int status = ORC_OK;
+    for (int64_t b = 0; b < nb && status == ORC_OK; ++b) {
+        int64_t r0 = b * B, r1 = r0 + B < R ? r0 + B : R;
+        int64_t s0 = row_ptrs[r0], n = (int64_t)row_ptrs[r1] - s0;
+        /* the tile: sorted distinct columns */
+        for (int64_t i = 0; i < n; ++i)
+            tile[i] = col_idx[s0 + i];
+        qsort(tile, (size_t)n, sizeof(int32_t), orc_cmp_i32);
+        int64_t u = 0;
+        for (int64_t i = 0; i < n; ++i)
+            if (u == 0 || tile[i] != tile[u - 1])
+                tile[u++] = tile[i];
+        int64_t nruns = 0;
+        for (int64_t i = 0; i < u; ++i)
+            if (i == 0 || tile[i] != tile[i - 1] + 1)
+                ++nruns;
+        if (u > 0 && (int64_t)tile[u - 1] - tile[0] + 1 > (1 << 18))
+            status = ORC_ERR_TOO_LARGE;
+        if (u > 8192 || nruns > 1024)
+            status = ORC_ERR_TOO_LARGE;
+        if (status != ORC_OK)
+            break;
+        if (runs) {
+            int64_t k = total;
+            for (int64_t i = 0; i < u; ++i) {
+                if (i == 0 || tile[i] != tile[i - 1] + 1) {
+                    runs[3 * k] = tile[i];
+                    runs[3 * k + 1] = (int32_t)i;
+                    runs[3 * k + 2] = 1;
+                    ++k;
+                } else {
+                    runs[3 * (k - 1) + 2] += 1;
+                }
+            }
+            for (int64_t r = r0; r < r1; ++r) {
+                int64_t a = row_ptrs[r], len = (int64_t)row_ptrs[r + 1] - a;
+                ell_nnz[r] = (int32_t)len;
+                for (int64_t t = 0; t < W; ++t) {
+                    int64_t slot = t * R + r;
+                    if (t < len) {
+                        const int32_t *hit = (const int32_t *)bsearch(
+                            &col_idx[a + t], tile, (size_t)u, sizeof(int32_t), orc_cmp_i32);
+                        lidx[slot] = (int16_t)(hit - tile);
+                        ell_val[slot] = val_bits[a + t];
+                    } else {
+                        lidx[slot] = 0;
+                        ell_val[slot] = 0u;
+                    }
+                }
+            }
+        }
+        total += nruns;
+        if (run_ptr)
+            run_ptr[b + 1] = (int32_t)total;
+    }
+    free(tile);
+    if (runs_total)
+        *runs_total = total;
+    return status;
+}

@@ -30,7 +30,7 @@ _LIB_PATH = os.path.join(_PKG, "libspmv_mi355x.so")
 _HEADER = os.path.join(_ROOT, "include", "spmv.h")
 
 FORMATS = {"auto": 0, "coo_atomic": 1, "coo_segmented": 2, "csr_scalar": 3, "csr_vector": 4,
-           "ell": 5, "hyb": 6, "jds": 7, "csr_merge": 8, "sell": 9}
+           "ell": 5, "hyb": 6, "jds": 7, "csr_merge": 8, "sell": 9, "ell_xtile": 10}
 FORMAT_NAMES = {v: k for k, v in FORMATS.items()}
 # name -> (enum value, numpy dtype)
 ARRAYS = {
@@ -40,7 +40,8 @@ ARRAYS = {
     "tail_val": (9, np.float32), "jds_perm": (10, np.int32), "jds_len": (11, np.int32),
     "jds_iter_ptr": (12, np.int32), "jds_col": (13, np.int32), "jds_val": (14, np.float32),
     "len_hist": (15, np.int64), "sell_sect_ptr": (16, np.int32), "sell_col": (17, np.int32),
-    "sell_val": (18, np.float32),
+    "sell_val": (18, np.float32), "xt_run_ptr": (19, np.int32), "xt_runs": (20, np.int32),
+    "xt_lidx": (21, np.int16),
 }
 STATUS = {0: "SPMV_OK", 1: "SPMV_ERR_INVALID_ARG", 2: "SPMV_ERR_BAD_ROWPTRS",
           3: "SPMV_ERR_BAD_COLIDX", 4: "SPMV_ERR_BAD_ROWIDX", 5: "SPMV_ERR_TOO_LARGE",

@@ -74,7 +74,7 @@ bool valid_opts(const spmv_opts &o) {
            o.col_blocks >= 0 && o.col_blocks <= kMaxColBlocks && o.reserved == 0;
 }
 
-bool valid_format(int32_t f) { return f >= SPMV_AUTO && f <= SPMV_SELL; }
+bool valid_format(int32_t f) { return f >= SPMV_AUTO && f <= SPMV_ELL_XTILE; }
 
 // ---------------------------------------------------------------- analysis
 struct Analysis {
@@ -340,6 +340,66 @@ int64_t format_bytes(int32_t fmt, int64_t R, int64_t nnz, int64_t W, int64_t K,
     }
 }
 
+// ELL with x tiles: per-block counts from the device, checked and summed on
+// the host.
+struct XtPlan {
+    bool ok = false;
+    int64_t blocks = 0, tile_total = 0, runs = 0;
+    int32_t max_tile = 0;
+    std::vector<int32_t> run_ptr;   // [blocks + 1]
+};
+
+spmv_status plan_xtiles(int32_t R, const int32_t *rp, const int32_t *col, XtPlan &p,
+                        hipStream_t s, Scratch &scratch) {
+    p = XtPlan{};
+    p.blocks = (static_cast<int64_t>(R) + kTileRows - 1) / kTileRows;
+    p.run_ptr.assign(static_cast<size_t>(p.blocks) + 1, 0);
+    if (p.blocks == 0) {
+        p.ok = true;
+        return SPMV_OK;
+    }
+    int32_t *counts = nullptr;
+    SPMV_TRY(scratch.alloc(&counts, static_cast<size_t>(3 * p.blocks)));
+    SPMV_HIP(launch_xt_count(R, rp, col, counts, s));
+    std::vector<int32_t> hc(static_cast<size_t>(3 * p.blocks));
+    SPMV_HIP(hipMemcpyAsync(hc.data(), counts, sizeof(int32_t) * hc.size(), hipMemcpyDeviceToHost,
+                            s));
+    SPMV_HIP(hipStreamSynchronize(s));
+    p.ok = true;
+    for (int64_t b = 0; b < p.blocks; ++b) {
+        const int32_t d = hc[3 * b], n = hc[3 * b + 1], fits = hc[3 * b + 2];
+        if (!fits || d > kTileMaxCols || n > kTileMaxRuns) p.ok = false;
+        p.tile_total += d;
+        p.max_tile = std::max(p.max_tile, d);
+        p.run_ptr[b + 1] = static_cast<int32_t>(p.run_ptr[b] + n);
+    }
+    p.runs = p.run_ptr[p.blocks];
+    return SPMV_OK;
+}
+
+int64_t xtile_bytes(int64_t R, int64_t W, const XtPlan &p) {
+    return 6 * R * W + 4 * R + 12 * p.runs + 4 * (p.blocks + 1);
+}
+
+spmv_status build_ell_xtile(spmv_handle *h, int32_t R, int32_t W, const int32_t *rp,
+                            const int32_t *col, const float *val, const XtPlan &p,
+                            hipStream_t s) {
+    h->ell_width = W;
+    h->xt_runs = p.runs;
+    h->xt_max_tile = p.max_tile;
+    const int64_t slots = static_cast<int64_t>(R) * W;
+    SPMV_TRY(halloc(h, &h->a.xt_run_ptr, p.blocks + 1));
+    SPMV_TRY(halloc(h, &h->a.xt_runs, 3 * p.runs));
+    SPMV_TRY(halloc(h, &h->a.xt_lidx, slots));
+    SPMV_TRY(halloc(h, &h->a.ell_val, slots));
+    SPMV_TRY(halloc(h, &h->a.ell_nnz, R));
+    SPMV_HIP(hipMemcpyAsync(h->a.xt_run_ptr, p.run_ptr.data(), sizeof(int32_t) * p.run_ptr.size(),
+                            hipMemcpyHostToDevice, s));
+    SPMV_HIP(launch_xt_fill(R, W, rp, col, val, h->a.xt_run_ptr, h->a.xt_runs, h->a.xt_lidx,
+                            h->a.ell_val, h->a.ell_nnz, s));
+    return SPMV_OK;
+}
+
 // Number of x slices.  Automatic only for SPMV_AUTO: when x is larger than
 // one XCD's L2 and the rows' columns are scattered (their first column lies
 // more than C/8 from the diagonal on average), gathers from the whole x miss
@@ -464,10 +524,24 @@ spmv_status build_csr_impl(spmv_handle **out, spmv_format fmt, int32_t R, int32_
         L = o.lanes_per_row > 0 ? o.lanes_per_row : lanes_from_mean(R, nnz);
     }
     const int64_t W = an.st.max_len;
-    if (f == SPMV_ELL && static_cast<int64_t>(R) * W > kInt32Max) return SPMV_ERR_TOO_LARGE;
+    // x tiles: asked for explicitly, or taken by SPMV_AUTO in place of ELL when
+    // the matrix has at least kXtileAutoRows rows, every 256-row block
+    // qualifies and each staged x word serves two gathers or more on average
+    // (nnz >= 2 * total tile size)
+    XtPlan xt;
+    const bool ell_fits = static_cast<int64_t>(R) * W <= kInt32Max;
+    if (f == SPMV_ELL_XTILE ||
+        (fmt == SPMV_AUTO && f == SPMV_ELL && ell_fits && R >= kXtileAutoRows)) {
+        SPMV_TRY(plan_xtiles(R, rp, col, xt, s, scratch));
+        if (f == SPMV_ELL_XTILE && !xt.ok) return SPMV_ERR_TOO_LARGE;
+        if (f == SPMV_ELL && xt.ok && static_cast<int64_t>(nnz) >= 2 * xt.tile_total)
+            f = SPMV_ELL_XTILE;
+    }
+    if ((f == SPMV_ELL || f == SPMV_ELL_XTILE) && !ell_fits) return SPMV_ERR_TOO_LARGE;
     if (f == SPMV_HYB && static_cast<int64_t>(R) * std::min<int64_t>(K, W) > kInt32Max)
         return SPMV_ERR_TOO_LARGE;
-    SPMV_TRY(check_budget(o, format_bytes(f, R, nnz, W, K, an.hist)));
+    SPMV_TRY(check_budget(o, f == SPMV_ELL_XTILE ? xtile_bytes(R, W, xt)
+                                                : format_bytes(f, R, nnz, W, K, an.hist)));
 
     HandlePtr h(new spmv_handle());
     SPMV_HIP(hipGetDevice(&h->device));
@@ -522,6 +596,9 @@ spmv_status build_csr_impl(spmv_handle **out, spmv_format fmt, int32_t R, int32_
         break;
     case SPMV_SELL:
         SPMV_TRY(build_sell(h.get(), R, rp, col, val, s, scratch));
+        break;
+    case SPMV_ELL_XTILE:
+        SPMV_TRY(build_ell_xtile(h.get(), R, static_cast<int32_t>(W), rp, col, val, xt, s));
         break;
     default:
         return SPMV_ERR_INVALID_ARG;
@@ -651,9 +728,9 @@ spmv_status spmv_build_tuned(spmv_handle **out, int32_t R, int32_t C, int32_t nn
     *out = nullptr;
     const spmv_opts o = resolve_opts(opts);
     if (bad_sizes(R, C, nnz) || !rp || (nnz > 0 && (!col || !val)) || !valid_opts(o) ||
-        runs < 0 || runs > 1000 || (format_mask & ~0x3FEu) != 0)
+        runs < 0 || runs > 1000 || (format_mask & ~0x7FEu) != 0)
         return SPMV_ERR_INVALID_ARG;
-    if (format_mask == 0) format_mask = 0x3FEu;   // formats 1..9
+    if (format_mask == 0) format_mask = 0x7FEu;   // formats 1..10
     if (runs == 0) runs = 5;
     hipStream_t s = static_cast<hipStream_t>(stream);
     Scratch scratch(s);
@@ -679,7 +756,7 @@ spmv_status spmv_build_tuned(spmv_handle **out, int32_t R, int32_t C, int32_t nn
     float best_us = 0.f;
     spmv_status first_err = SPMV_OK;
     spmv_status fatal = SPMV_OK;
-    for (int f = SPMV_COO_ATOMIC; f <= SPMV_SELL && fatal == SPMV_OK; ++f) {
+    for (int f = SPMV_COO_ATOMIC; f <= SPMV_ELL_XTILE && fatal == SPMV_OK; ++f) {
         if (!(format_mask & (1u << f))) continue;
         for (int variant = 0; variant < 2 && fatal == SPMV_OK; ++variant) {
             const int32_t K = variant == 0 ? 1 : auto_slices;
@@ -854,6 +931,11 @@ ArrayRef array_ref(const spmv_handle *h, spmv_array which) {
     case SPMV_A_SELL_SECT_PTR: set(a.sell_ptr, (R + kWave - 1) / kWave + 1, 4); break;
     case SPMV_A_SELL_COL: set(a.sell_col, h->sell_slots, 4); break;
     case SPMV_A_SELL_VAL: set(a.sell_val, h->sell_slots, 4); break;
+    case SPMV_A_XT_RUN_PTR:
+        set(a.xt_run_ptr, (R + kTileRows - 1) / kTileRows + 1, 4);
+        break;
+    case SPMV_A_XT_RUNS: set(a.xt_runs, 3 * h->xt_runs, 4); break;
+    case SPMV_A_XT_LIDX: set(a.xt_lidx, slots, 2); break;
     case SPMV_A_LEN_HIST:
         r.host = h->hist.data();
         r.bytes = h->hist.size() * sizeof(int64_t);
@@ -922,6 +1004,7 @@ const char *spmv_format_name(spmv_format f) {
     case SPMV_JDS: return "jds";
     case SPMV_CSR_MERGE: return "csr_merge";
     case SPMV_SELL: return "sell";
+    case SPMV_ELL_XTILE: return "ell_xtile";
     default: return "unknown";
     }
 }

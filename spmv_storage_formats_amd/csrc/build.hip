@@ -182,6 +182,200 @@ __global__ __launch_bounds__(kThreads) void k_fill_tail(
     tail_val[e] = val[src];
 }
 
+// ---------------------------------------------------------------------------
+// ELL with x tiles [Regularized formats page, ELL section, for the slot layout;
+// "Introduction to sparse computing", x blocking: keep the x a block gathers
+// in fast memory; format-choice article 4.2: stage in shared memory].
+// Block b = rows [256b, 256b + 256).  Its tile is the sorted set of distinct
+// columns of its entries; a run is a maximal stretch of consecutive columns
+// in the tile; a column's tile position is the number of tile columns below
+// it.  The block marks its columns in an LDS bitmap over [lo, lo + span)
+// (lo = least column, span = greatest - lo + 1), so tile positions are
+// popcounts and runs are bit boundaries.
+// ---------------------------------------------------------------------------
+constexpr int kBmWords = kTileMaxSpan / 32;
+static_assert(kTileRows == kThreads, "one row per thread in the x-tile kernels");
+
+__device__ inline int block_min_max(int v, bool want_max, int *red) {
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        const int u = __shfl_xor(v, o);
+        v = want_max ? max(v, u) : min(v, u);
+    }
+    __syncthreads();
+    if (__lane_id() == 0) red[threadIdx.x / kWave] = v;
+    __syncthreads();
+    int t = red[0];
+    for (int i = 1; i < kThreads / kWave; ++i) t = want_max ? max(t, red[i]) : min(t, red[i]);
+    return t;
+}
+
+// Exclusive prefix over the block of one int per thread; *total = block sum.
+__device__ inline int block_excl_scan(int v, int *total, int *red) {
+    const int lane = __lane_id();
+    int incl = v;
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int u = __shfl_up(incl, o);
+        if (lane >= o) incl += u;
+    }
+    __syncthreads();
+    if (lane == kWave - 1) red[threadIdx.x / kWave] = incl;
+    __syncthreads();
+    int before = 0, tot = 0;
+    for (int i = 0; i < kThreads / kWave; ++i) {
+        const int x = red[i];
+        before += i < static_cast<int>(threadIdx.x / kWave) ? x : 0;
+        tot += x;
+    }
+    *total = tot;
+    return before + incl - v;
+}
+
+struct XtBlock {
+    int32_t r0, r1;     // rows of the block
+    int64_t s0, s1;     // its entries [s0, s1)
+    int32_t lo, span;   // column window
+};
+
+// Marks the block's columns in bm.  Returns false (the same in every thread)
+// when the window exceeds the bitmap.  Every thread passes every barrier.
+__device__ bool xt_mark(int32_t R, const int32_t *__restrict__ rp,
+                        const int32_t *__restrict__ col, uint32_t *bm, int *red, XtBlock &xb) {
+    xb.r0 = static_cast<int32_t>(blockIdx.x) * kTileRows;
+    xb.r1 = min(R, xb.r0 + kTileRows);
+    xb.s0 = rp[xb.r0];
+    xb.s1 = rp[xb.r1];
+    int lo = INT32_MAX, hi = -1;
+    for (int64_t i = xb.s0 + threadIdx.x; i < xb.s1; i += kThreads) {
+        const int c = col[i];
+        lo = min(lo, c);
+        hi = max(hi, c);
+    }
+    lo = block_min_max(lo, false, red);
+    hi = block_min_max(hi, true, red);
+    xb.lo = lo;
+    xb.span = hi < lo ? 0 : (static_cast<int64_t>(hi) - lo + 1 > kTileMaxSpan ? -1 : hi - lo + 1);
+    if (xb.span < 0) return false;
+    const int words = (xb.span + 31) / 32;
+    for (int w = threadIdx.x; w < words; w += kThreads) bm[w] = 0u;
+    __syncthreads();
+    for (int64_t i = xb.s0 + threadIdx.x; i < xb.s1; i += kThreads) {
+        const int c = col[i] - lo;
+        atomicOr(&bm[c >> 5], 1u << (c & 31));
+    }
+    __syncthreads();
+    return true;
+}
+
+// bits of word w that start / end a run (a set bit whose lower / upper
+// neighbour is clear)
+__device__ inline uint32_t run_starts(const uint32_t *bm, int w) {
+    const uint32_t m = bm[w];
+    const uint32_t below = w > 0 ? bm[w - 1] >> 31 : 0u;
+    return m & ~((m << 1) | below);
+}
+__device__ inline uint32_t run_ends(const uint32_t *bm, int w, int words) {
+    const uint32_t m = bm[w];
+    const uint32_t above = w + 1 < words ? (bm[w + 1] & 1u) << 31 : 0u;
+    return m & ~((m >> 1) | above);
+}
+
+// counts[3b] = distinct columns, counts[3b+1] = runs, counts[3b+2] = 1 if the
+// window fits the bitmap (else 0 and the other two are 0)
+__global__ __launch_bounds__(kThreads) void k_xt_count(int32_t R, const int32_t *__restrict__ rp,
+                                                       const int32_t *__restrict__ col,
+                                                       int32_t *__restrict__ counts) {
+    __shared__ uint32_t bm[kBmWords];
+    __shared__ int red[kThreads / kWave];
+    XtBlock xb;
+    const bool ok = xt_mark(R, rp, col, bm, red, xb);
+    int distinct = 0, runs = 0;
+    if (ok) {
+        const int words = (xb.span + 31) / 32;
+        int d = 0, n = 0;
+        for (int w = threadIdx.x; w < words; w += kThreads) {
+            d += __popc(bm[w]);
+            n += __popc(run_starts(bm, w));
+        }
+        block_excl_scan(d, &distinct, red);
+        block_excl_scan(n, &runs, red);
+    }
+    if (threadIdx.x == 0) {
+        counts[3 * blockIdx.x] = distinct;
+        counts[3 * blockIdx.x + 1] = runs;
+        counts[3 * blockIdx.x + 2] = ok ? 1 : 0;
+    }
+}
+
+// Writes the block's runs (first column, tile offset, length) at
+// runs[3 * (run_ptr[b] + k)] and, for every row, its ELL slots: tile position
+// (int16) and value, padding (0, +0.0f) past the row's length.  The host has
+// checked that every block fits (window, kTileMaxCols, kTileMaxRuns).
+__global__ __launch_bounds__(kThreads) void k_xt_fill(int32_t R, int32_t W,
+                                                      const int32_t *__restrict__ rp,
+                                                      const int32_t *__restrict__ col,
+                                                      const uint32_t *__restrict__ val,
+                                                      const int32_t *__restrict__ run_ptr,
+                                                      int32_t *__restrict__ runs,
+                                                      int16_t *__restrict__ lidx,
+                                                      uint32_t *__restrict__ ell_val,
+                                                      int32_t *__restrict__ ell_nnz) {
+    __shared__ uint32_t bm[kBmWords];
+    __shared__ int32_t rank[kBmWords];      // tile position of each word's first bit
+    __shared__ int32_t rstart[kTileMaxRuns], rend[kTileMaxRuns];   // relative columns
+    __shared__ int red[kThreads / kWave];
+    XtBlock xb;
+    if (!xt_mark(R, rp, col, bm, red, xb)) return;   // (excluded by the host)
+    const int words = (xb.span + 31) / 32;
+    // each thread owns a contiguous chunk of words
+    const int cw = (words + kThreads - 1) / kThreads;
+    const int w0 = min(words, static_cast<int>(threadIdx.x) * cw), w1 = min(words, w0 + cw);
+    int d = 0, ns = 0, ne = 0;
+    for (int w = w0; w < w1; ++w) {
+        d += __popc(bm[w]);
+        ns += __popc(run_starts(bm, w));
+        ne += __popc(run_ends(bm, w, words));
+    }
+    int tot;
+    int rk = block_excl_scan(d, &tot, red);
+    int sk = block_excl_scan(ns, &tot, red);
+    int ek = block_excl_scan(ne, &tot, red);
+    for (int w = w0; w < w1; ++w) {
+        rank[w] = rk;
+        rk += __popc(bm[w]);
+        for (uint32_t m = run_starts(bm, w); m; m &= m - 1) rstart[sk++] = 32 * w + __ffs(m) - 1;
+        for (uint32_t m = run_ends(bm, w, words); m; m &= m - 1) rend[ek++] = 32 * w + __ffs(m) - 1;
+    }
+    __syncthreads();
+    auto position = [&](int c) {   // tile position of relative column c (a tile column)
+        const int w = c >> 5, bit = c & 31;
+        return rank[w] + __popc(bm[w] & ((1u << bit) - 1u));
+    };
+    const int base = run_ptr[blockIdx.x];
+    const int nruns = run_ptr[blockIdx.x + 1] - base;
+    for (int k = threadIdx.x; k < nruns; k += kThreads) {
+        const int st = rstart[k];
+        runs[3 * (static_cast<int64_t>(base) + k)] = xb.lo + st;
+        runs[3 * (static_cast<int64_t>(base) + k) + 1] = position(st);
+        runs[3 * (static_cast<int64_t>(base) + k) + 2] = rend[k] - st + 1;
+    }
+    const int32_t r = xb.r0 + static_cast<int32_t>(threadIdx.x);
+    if (r >= xb.r1) return;
+    const int32_t a = rp[r];
+    const int32_t n = rp[r + 1] - a;
+    ell_nnz[r] = n;
+    for (int32_t t = 0; t < W; ++t) {
+        const int64_t slot = static_cast<int64_t>(t) * R + r;
+        int16_t p = 0;
+        uint32_t v = 0u;   // padding: position 0, +0.0f
+        if (t < n) {
+            p = static_cast<int16_t>(position(col[static_cast<int64_t>(a) + t] - xb.lo));
+            v = val[static_cast<int64_t>(a) + t];
+        }
+        lidx[slot] = p;
+        ell_val[slot] = v;
+    }
+}
+
 // JDS sort key: W - len, so an ascending stable sort puts longer rows first and
 // keeps the original order among equal lengths.
 __global__ __launch_bounds__(kThreads) void k_jds_keys(int32_t R, int32_t W,
@@ -447,6 +641,23 @@ hipError_t launch_build_ell(int32_t R, int32_t width, const int32_t *rp, const i
     if (R <= 0) return hipSuccess;
     k_build_ell<<<grid_for(R, kThreads), kThreads, 0, s>>>(
         R, width, rp, col, reinterpret_cast<const uint32_t *>(val), ell_col,
+        reinterpret_cast<uint32_t *>(ell_val), ell_nnz);
+    return hipGetLastError();
+}
+
+hipError_t launch_xt_count(int32_t R, const int32_t *rp, const int32_t *col, int32_t *counts,
+                           hipStream_t s) {
+    if (R <= 0) return hipSuccess;
+    k_xt_count<<<grid_for(R, kTileRows), kThreads, 0, s>>>(R, rp, col, counts);
+    return hipGetLastError();
+}
+
+hipError_t launch_xt_fill(int32_t R, int32_t W, const int32_t *rp, const int32_t *col,
+                          const float *val, const int32_t *run_ptr, int32_t *runs,
+                          int16_t *lidx, float *ell_val, int32_t *ell_nnz, hipStream_t s) {
+    if (R <= 0) return hipSuccess;
+    k_xt_fill<<<grid_for(R, kTileRows), kThreads, 0, s>>>(
+        R, W, rp, col, reinterpret_cast<const uint32_t *>(val), run_ptr, runs, lidx,
         reinterpret_cast<uint32_t *>(ell_val), ell_nnz);
     return hipGetLastError();
 }

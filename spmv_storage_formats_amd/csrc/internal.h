@@ -28,6 +28,16 @@ constexpr int kMergeThreads = 256;
 constexpr int kMergeItemsPerThread = 8;
 constexpr int kMergeItemsPerBlock = kMergeThreads * kMergeItemsPerThread;
 
+// ELL with x tiles: rows in blocks of kTileRows; a block qualifies when its
+// columns span fewer than kTileMaxSpan and it has at most kTileMaxCols
+// distinct columns in at most kTileMaxRuns runs of consecutive columns.
+constexpr int kTileRows = 256;
+constexpr int kTileMaxSpan = 1 << 18;
+constexpr int kTileMaxCols = 8192;
+constexpr int kTileMaxRuns = 1024;
+// SPMV_AUTO considers x tiles only from this many rows on (8 blocks per XCD)
+constexpr int kXtileAutoRows = 64 * kTileRows;
+
 // Validation flags written by the analysis kernels.
 enum : int { kFlagBadRowPtrs = 1, kFlagBadCol = 2, kFlagBadRow = 4, kFlagUnsortedRows = 8 };
 
@@ -62,6 +72,10 @@ struct DevArrays {
     float *sell_val = nullptr;
     // CSR merge: first row of each block's merge-path segment, [blocks + 1]
     int32_t *merge_row_start = nullptr;
+    // ELL with x tiles (values and row lengths in ell_val / ell_nnz)
+    int32_t *xt_run_ptr = nullptr;  // [blocks + 1]
+    int32_t *xt_runs = nullptr;     // [3 * runs]: first column, offset in the tile, length
+    int16_t *xt_lidx = nullptr;     // [R * W]: slot t of row r at t*R + r, tile position
 };
 
 }  // namespace spmv
@@ -77,6 +91,8 @@ struct spmv_handle {
     std::vector<int64_t> hist;      // host copy of the row-length histogram
     int64_t tail_nnz = 0;
     int64_t sell_slots = 0;
+    int64_t xt_runs = 0;            // ELL x tiles: runs over all blocks
+    int32_t xt_max_tile = 0;        // ELL x tiles: largest tile (floats of LDS)
     int64_t num_tiles = 0;
     int64_t device_bytes = 0;
     spmv::DevArrays a;
@@ -244,6 +260,14 @@ hipError_t launch_gather_pairs(int32_t nnz, const int32_t *perm, const int32_t *
                                hipStream_t s);
 hipError_t launch_expand_rows(int32_t R, int32_t nnz, const int32_t *rp, int32_t *row_idx,
                               hipStream_t s);
+// ELL x tiles.  counts[3*b + {0,1,2}] = distinct columns, runs, span ok (1/0)
+// of block b (kTileRows rows); xt_fill writes run_ptr must already hold the
+// exclusive scan of the run counts.
+hipError_t launch_xt_count(int32_t R, const int32_t *rp, const int32_t *col, int32_t *counts,
+                           hipStream_t s);
+hipError_t launch_xt_fill(int32_t R, int32_t W, const int32_t *rp, const int32_t *col,
+                          const float *val, const int32_t *run_ptr, int32_t *runs,
+                          int16_t *lidx, float *ell_val, int32_t *ell_nnz, hipStream_t s);
 hipError_t launch_build_ell(int32_t R, int32_t width, const int32_t *rp, const int32_t *col,
                             const float *val, int32_t *ell_col, float *ell_val,
                             int32_t *ell_nnz, hipStream_t s);

@@ -350,6 +350,68 @@ __global__ __launch_bounds__(kThreads) void k_ell4(int32_t R, int32_t W,
 }
 
 // ---------------------------------------------------------------------------
+// ELL with x tiles: the block of 256 rows first copies its x tile into LDS,
+// run by run (a wave per run, lanes over consecutive columns: coalesced), then
+// each lane walks its row's ELL slots as k_ell does, reading 16-bit tile
+// positions instead of 32-bit columns and gathering x from LDS instead of
+// through the vector memory path (which bounds k_ell on banded matrices).
+// ---------------------------------------------------------------------------
+template <int U>
+__global__ __launch_bounds__(kThreads) void k_ell_xtile(int32_t R, int32_t W,
+                                                        const int32_t *__restrict__ run_ptr,
+                                                        const int32_t *__restrict__ runs,
+                                                        const int16_t *__restrict__ lidx,
+                                                        const float *__restrict__ ell_val,
+                                                        const int32_t *__restrict__ ell_nnz,
+                                                        const float *__restrict__ x,
+                                                        float *__restrict__ y) {
+    extern __shared__ float tile[];
+    const uint32_t b = xcd_remap(blockIdx.x, gridDim.x);
+    const int k0 = run_ptr[b], k1 = run_ptr[b + 1];
+    const int lane = __lane_id();
+    for (int k = k0 + static_cast<int>(threadIdx.x / kWave); k < k1; k += kThreads / kWave) {
+        const int64_t q = 3 * static_cast<int64_t>(k);
+        const int32_t start = runs[q], off = runs[q + 1], len = runs[q + 2];
+        for (int i = lane; i < len; i += kWave) tile[off + i] = x[start + i];
+    }
+    __syncthreads();
+    const uint32_t r = b * kThreads + threadIdx.x;
+    if (r >= static_cast<uint32_t>(R)) return;
+    const uint32_t ru = static_cast<uint32_t>(R), wu = static_cast<uint32_t>(W);
+    const int32_t n = ld_nt(ell_nnz + r);
+    const float y0 = ld_nt(y + r);
+    int32_t c[U];
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t slot = static_cast<uint32_t>(u) * ru + r;
+        c[u] = u < W ? ld_nt(lidx + slot) : 0;
+        v[u] = u < W ? ld_nt(ell_val + slot) : 0.f;
+    }
+    float sum = 0.f;
+    for (uint32_t t0 = 0; t0 < wu; t0 += U) {
+        int32_t cn[U];
+        float vn[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t t = t0 + U + u;
+            const uint32_t slot = t * ru + r;
+            cn[u] = t < wu ? ld_nt(lidx + slot) : 0;
+            vn[u] = t < wu ? ld_nt(ell_val + slot) : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (t0 + u < static_cast<uint32_t>(n)) sum += v[u] * tile[c[u]];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            c[u] = cn[u];
+            v[u] = vn[u];
+        }
+    }
+    if (n > 0) __builtin_nontemporal_store(y0 + sum, y + r);
+}
+
+// ---------------------------------------------------------------------------
 // JDS: rows sorted by length (longest first) in jagged columns; entry t of
 // sorted row s at iterPtr[t] + s [Regularized formats page, JDS section: one
 // thread per row, iterPtr gives each iteration's start].  One wave takes a
@@ -665,6 +727,19 @@ spmv_status launch_spmv(const spmv_handle *h, const float *x, float *y, hipStrea
         if (e == hipSuccess)
             e = run_coo_segmented(static_cast<int32_t>(h->tail_nnz), a.tail_row, a.tail_col,
                                   a.tail_val, x, y, s);
+        break;
+    case SPMV_ELL_XTILE:
+        if (h->ell_width > 0) {
+            const unsigned g = blocks_of(R, kTileRows);
+            const size_t lds = sizeof(float) * static_cast<size_t>(std::max(h->xt_max_tile, 1));
+            if (h->ell_width <= 4)
+                k_ell_xtile<4><<<g, kThreads, lds, s>>>(R, h->ell_width, a.xt_run_ptr, a.xt_runs,
+                                                        a.xt_lidx, a.ell_val, a.ell_nnz, x, y);
+            else
+                k_ell_xtile<8><<<g, kThreads, lds, s>>>(R, h->ell_width, a.xt_run_ptr, a.xt_runs,
+                                                        a.xt_lidx, a.ell_val, a.ell_nnz, x, y);
+            e = hipGetLastError();
+        }
         break;
     case SPMV_JDS:
         if (h->num_tiles > 0) {

@@ -16,9 +16,9 @@ pytestmark = pytest.mark.gpu
 import spmv_storage_formats_amd as spmv  # noqa: E402
 
 ALL_FORMATS = ["coo_atomic", "coo_segmented", "csr_scalar", "csr_vector", "ell", "hyb", "jds",
-               "csr_merge", "sell"]
+               "csr_merge", "sell", "ell_xtile"]
 # formats whose rows are each summed by one lane group with a plain y update
-DETERMINISTIC = ["csr_scalar", "csr_vector", "ell"]
+DETERMINISTIC = ["csr_scalar", "csr_vector", "ell", "ell_xtile"]
 
 _cache = {}
 
@@ -29,6 +29,22 @@ def dev():
         pytest.skip("no GPU")
     spmv.load_library()
     return torch.device("cuda:0")
+
+
+def xtile_refused(row_ptrs, col_idx, values):
+    """Whether the oracle refuses the x-tile format for this CSR matrix."""
+    try:
+        oracle.csr_to_ell_xtile(row_ptrs, col_idx, values)
+        return False
+    except ValueError:
+        return True
+
+
+def expect_refused(fmt, w, dev, **kw):
+    """For a format the oracle refuses on w: the build fails with TOO_LARGE."""
+    with pytest.raises(spmv.SpmvError) as ei:
+        build(fmt, w, dev, **kw)
+    assert ei.value.name == "SPMV_ERR_TOO_LARGE"
 
 
 def W(name):
@@ -151,6 +167,14 @@ def check_builder(h, w, K=None):
         assert np.array_equal(h.array("jds_iter_ptr"), o["iter_ptr"])
         assert np.array_equal(h.array("jds_col"), o["col"])
         assert np.array_equal(bits(h.array("jds_val")), bits(o["val"]))
+    elif fmt == "ell_xtile":
+        o = oracle.csr_to_ell_xtile(w.row_ptrs, w.col_idx, w.values)
+        assert h.info["ell_width"] == o["width"]
+        assert np.array_equal(h.array("xt_run_ptr"), o["run_ptr"])
+        assert np.array_equal(h.array("xt_runs"), o["runs"].reshape(-1))
+        assert np.array_equal(h.array("xt_lidx"), o["lidx"])
+        assert np.array_equal(bits(h.array("ell_val")), bits(o["val"]))
+        assert np.array_equal(h.array("ell_nnz"), o["nnz"])
     elif fmt == "sell":
         o = oracle.csr_to_sell(w.row_ptrs, w.col_idx, w.values, 64)
         assert np.array_equal(h.array("jds_perm"), o["perm"])
@@ -180,6 +204,9 @@ def test_reduced_builders_and_spmv(dev, name, fmt):
         return
     if fmt == "ell" and slots > 64_000_000:
         pytest.skip("ELL of this skewed shape is >99% padding (multi-GB); covered at full size")
+    if fmt == "ell_xtile" and xtile_refused(w.row_ptrs, w.col_idx, w.values):
+        expect_refused(fmt, w, dev)
+        return
     h = build(fmt, w, dev)
     assert h.format == fmt
     check_builder(h, w)
@@ -257,10 +284,8 @@ def test_one_huge_row(dev, fmt):
     w = synth.Workload("huge_row", R, C, rp, ci, rng.uniform(-1, 1, ci.size).astype(np.float32),
                        rng.uniform(-1, 1, C).astype(np.float32),
                        rng.uniform(-1, 1, R).astype(np.float32))
-    if fmt == "ell" and R * 200_000 > 2**31 - 1:
-        with pytest.raises(spmv.SpmvError) as ei:
-            build(fmt, w, dev)
-        assert ei.value.name == "SPMV_ERR_TOO_LARGE"
+    if fmt in ("ell", "ell_xtile") and R * 200_000 > 2**31 - 1:
+        expect_refused(fmt, w, dev)
         return
     h = build(fmt, w, dev)
     check_builder(h, w)
@@ -403,8 +428,8 @@ def test_build_coo_spmv(dev, fmt):
     rng = np.random.default_rng(3)
     ri, ci, v = _coo_of(w, rng, True)
     t = lambda a: torch.from_numpy(a).to(dev)  # noqa: E731
-    if fmt == "ell":
-        w = W("c2s")
+    if fmt in ("ell", "ell_xtile"):
+        w = W("c2s" if fmt == "ell" else "c3s")
         ri, ci, v = _coo_of(w, rng, True)
     h = spmv.build_coo(fmt, t(ri), t(ci), t(v), w.num_rows, w.num_cols)
     y_ref, bound = oracle.spmv_coo(w.num_rows, ri, ci, v, w.x, w.y)
@@ -431,9 +456,10 @@ def test_full_size_parity(dev, name, fmt):
     Wd = int(np.diff(w.row_ptrs).max())
     print(f"[case] full {name} {fmt} R={w.num_rows} nnz={w.nnz} W={Wd}", flush=True)
     if fmt == "ell" and w.num_rows * Wd > 2**31 - 1:
-        with pytest.raises(spmv.SpmvError) as ei:
-            build(fmt, w, dev)
-        assert ei.value.name == "SPMV_ERR_TOO_LARGE"
+        expect_refused(fmt, w, dev)
+        return
+    if fmt == "ell_xtile" and xtile_refused(w.row_ptrs, w.col_idx, w.values):
+        expect_refused(fmt, w, dev)
         return
     kw = {"hyb_width": 20} if (fmt == "hyb" and name == "c4") else {}
     h = build(fmt, w, dev, **kw)
@@ -442,7 +468,8 @@ def test_full_size_parity(dev, name, fmt):
         # scattered columns over 8 / 16 MB of x: 4 MiB x slices
         assert h.info["col_blocks"] == {"c1": 1, "c2": 1, "c3": 1, "c4": 2, "c5": 4}[name]
         if name in ("c1", "c2", "c3"):
-            assert h.format == "ell"
+            # the 3-D stencil reuses each staged x word ~4.5 times: x tiles
+            assert h.format == ("ell_xtile" if name == "c3" else "ell")
     else:
         assert h.info["col_blocks"] == 1
     _, _, _, x, y0 = to_dev(w, dev)
@@ -451,6 +478,7 @@ def test_full_size_parity(dev, name, fmt):
 
 
 @pytest.mark.parametrize("name,fmt", [("c1", "ell"), ("c2", "ell"), ("c3", "ell"),
+                                      ("c1", "ell_xtile"), ("c3", "ell_xtile"),
                                       ("c4", "hyb"), ("c4", "jds"), ("c5", "jds"),
                                       ("c5", "coo_segmented"), ("c4", "sell"), ("c5", "sell")])
 def test_full_size_builders_bitexact(dev, name, fmt):
@@ -469,6 +497,22 @@ def test_full_size_selector_unsliced(dev, name, expect):
     assert (h.format, h.info["hyb_width"]) == expect and h.info["col_blocks"] == 1
 
 
+def _slices(w, K):
+    """The CSR arrays of the K column slices (entries with column in
+    [k*ceil(C/K), (k+1)*ceil(C/K)), row order kept), built with numpy."""
+    sc = -(-w.num_cols // K)
+    rows = np.repeat(np.arange(w.num_rows), np.diff(w.row_ptrs))
+    out = []
+    for k in range(K):
+        m = (w.col_idx >= k * sc) & (w.col_idx < (k + 1) * sc)
+        if not m.any():
+            continue
+        counts = np.bincount(rows[m], minlength=w.num_rows)
+        rp = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+        out.append((rp, w.col_idx[m], w.values[m]))
+    return out
+
+
 @pytest.mark.parametrize("name", ["c2s", "c4s", "c5s", "c3s"])
 @pytest.mark.parametrize("fmt", ALL_FORMATS + ["auto"])
 def test_col_slices_parity(dev, name, fmt):
@@ -477,6 +521,9 @@ def test_col_slices_parity(dev, name, fmt):
     w = W(name)
     if fmt == "ell" and name in ("c4s", "c5s"):
         pytest.skip("ELL of a skewed slice is mostly padding")
+    if fmt == "ell_xtile" and any(xtile_refused(*sl) for sl in _slices(w, 3)):
+        expect_refused(fmt, w, dev, col_blocks=3)
+        return
     h = build(fmt, w, dev, col_blocks=3)
     assert h.info["col_blocks"] == 3
     assert h.info["slice_cols"] == -(-w.num_cols // 3)
@@ -712,8 +759,18 @@ def test_build_destroy_cycles_release_device_memory(dev):
     w = W("c2s")
     rp, ci, v, x, y0 = to_dev(w, dev)
 
+    formats = [f for f in ALL_FORMATS if f != "ell_xtile"] + ["ell_xtile_c3s"]
+    w3 = W("c3s")
+    rp3, ci3, v3, x3, y3 = to_dev(w3, dev)
+
     def cycle(i):
-        fmt = ALL_FORMATS[i % len(ALL_FORMATS)]
+        fmt = formats[i % len(formats)]
+        if fmt == "ell_xtile_c3s":   # the x-tile format needs a banded matrix
+            h = spmv.build("ell_xtile", rp3, ci3, v3, w3.num_cols)
+            y = y3.clone()
+            h.run(x3, y)
+            h.close()
+            return
         h = spmv.build(fmt, rp, ci, v, w.num_cols, col_blocks=2 if i % 3 == 0 else 0)
         y = y0.clone()
         h.run(x, y)

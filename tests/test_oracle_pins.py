@@ -643,3 +643,92 @@ def test_cg_energy_error_bound():
         assert ek <= 2 * q**k * e0 * (1 + 1e-9)
         assert ek <= prev * (1 + 1e-12)
         prev = ek
+
+
+# ---------------------------------------------------------------- ELL with x tiles
+
+def test_xtile_hand_example():
+    """The hand-derived 3-row example (blocks of 2 rows) in tests/golden: runs,
+    tile positions and padded slots.  Catches a wrong tile order, run split or
+    slot layout."""
+    g = _gold("xtile_example.json")
+    o = oracle.csr_to_ell_xtile(np.array(g["row_ptrs"]), np.array(g["col_idx"]),
+                                np.array(g["values"], np.float32), block_rows=g["block_rows"])
+    assert o["run_ptr"].tolist() == g["run_ptr"]
+    assert o["runs"].tolist() == g["runs"]
+    assert o["lidx"].tolist() == g["lidx"]
+    assert o["val"].tolist() == g["val"]
+    assert o["nnz"].tolist() == g["nnz"]
+
+
+def test_xtile_fig14_1_is_plain_ell_columns():
+    """Fig. 14.1 in one block: the tile is {0,1,2,3} (one run), so tile
+    positions equal the printed ELL column indices."""
+    w = synth.fig14_1()
+    o = oracle.csr_to_ell_xtile(w.row_ptrs, w.col_idx, w.values)
+    g = _gold("fig14_1.json")["ell"]     # printed with '*' at the padded slots
+    assert o["runs"].tolist() == [[0, 0, 4]]
+    assert o["lidx"].tolist() == [0 if c == "*" else c for c in g["colIdx"]]
+    assert o["val"].tolist() == [0 if v == "*" else v for v in g["value"]]
+
+
+def _xtile_semantics(rp, ci, vals, B):
+    """Brute-force check of the definition with plain Python: per block, the
+    runs rebuild the sorted distinct columns; every real slot maps back to its
+    column and value; padding is (0, +0.0)."""
+    o = oracle.csr_to_ell_xtile(rp, ci, vals, block_rows=B)
+    R = rp.size - 1
+    W = o["width"]
+    for b in range(-(-R // B)):
+        r0, r1 = b * B, min(R, b * B + B)
+        cols = sorted(set(ci[rp[r0]:rp[r1]].tolist()))
+        runs = o["runs"][o["run_ptr"][b]:o["run_ptr"][b + 1]]
+        tile = []
+        for start, off, ln in runs.tolist():
+            assert off == len(tile)
+            tile.extend(range(start, start + ln))
+        assert tile == cols
+        for k in range(1, len(runs)):   # runs are maximal
+            assert runs[k][0] > runs[k - 1][0] + runs[k - 1][2]
+        for r in range(r0, r1):
+            for t in range(W):
+                slot = t * R + r
+                if t < rp[r + 1] - rp[r]:
+                    assert tile[o["lidx"][slot]] == ci[rp[r] + t]
+                    assert o["val"][slot] == vals[rp[r] + t]
+                else:
+                    assert o["lidx"][slot] == 0 and o["val"][slot].view(np.uint32) == 0
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_xtile_brute_force_banded(seed):
+    rng = np.random.default_rng(300 + seed)
+    R = int(rng.integers(1, 700))
+    B = int(rng.choice([1, 2, 7, 64, 256]))
+    lens = rng.integers(0, 9, size=R)
+    rp = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    rows = np.repeat(np.arange(R), lens)
+    ci = np.clip(rows + rng.integers(-40, 41, size=rows.size), 0, R + 40).astype(np.int32)
+    vals = rng.uniform(-1, 1, ci.size).astype(np.float32)
+    _xtile_semantics(rp, ci, vals, B)
+
+
+def test_xtile_refusals():
+    """Refused past the limits: a block spanning more than 2^18 columns,
+    more than 8192 distinct columns, or more than 1024 runs."""
+    rp = np.array([0, 2], np.int32)
+    ok = oracle.csr_to_ell_xtile(rp, np.array([0, (1 << 18) - 1], np.int32),
+                                 np.ones(2, np.float32))
+    assert ok["runs"].tolist() == [[0, 0, 1], [(1 << 18) - 1, 1, 1]]
+    with pytest.raises(ValueError):
+        oracle.csr_to_ell_xtile(rp, np.array([0, 1 << 18], np.int32), np.ones(2, np.float32))
+    n = 8193   # one row of 8193 distinct consecutive columns: one run, too many columns
+    with pytest.raises(ValueError):
+        oracle.csr_to_ell_xtile(np.array([0, n], np.int32), np.arange(n, dtype=np.int32),
+                                np.ones(n, np.float32))
+    n = 1025   # 1025 isolated columns: 1025 runs
+    with pytest.raises(ValueError):
+        oracle.csr_to_ell_xtile(np.array([0, n], np.int32),
+                                (2 * np.arange(n)).astype(np.int32), np.ones(n, np.float32))
+    oracle.csr_to_ell_xtile(np.array([0, 1024], np.int32),
+                            (2 * np.arange(1024)).astype(np.int32), np.ones(1024, np.float32))

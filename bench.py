@@ -372,17 +372,22 @@ def event_overhead_us(torch):
 
 
 def measured_traffic(key):
-    """HBM bytes per launch from the committed PMC summary, or None when the
-    summary has no entry for `key` or the kernels changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", "ell_random_rows_1Mx5_stencil27_128_pmc_traffic.md")
-    if not os.path.exists(path):
+    """HBM bytes per launch from the committed PMC summaries (profiles/
+    *_pmc_traffic.md, a JSON block each), or None when none has an entry for
+    `key` or the kernels changed since it was taken."""
+    pdir = os.path.join(ROOT, "profiles")
+    if not os.path.isdir(pdir):
         return None
-    text = open(path).read()
-    start = text.find("```json")
-    if start < 0:
-        return None
-    end = text.find("```", start + 7)
-    table = json.loads(text[start + 7:end])
+    table = {}
+    for f in sorted(os.listdir(pdir)):
+        if not f.endswith("_pmc_traffic.md"):
+            continue
+        text = open(os.path.join(pdir, f)).read()
+        start = text.find("```json")
+        if start < 0:
+            continue
+        end = text.find("```", start + 7)
+        table.update(json.loads(text[start + 7:end]))
     entry = table.get(key)
     if entry and entry.get("kernel_source_sha") == kernel_source_sha():
         return entry["hbm_bytes_per_launch"]

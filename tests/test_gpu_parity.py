@@ -565,7 +565,7 @@ def test_empirical_selector_mask(dev):
     assert h.format in ("csr_scalar", "jds")
 
 
-@pytest.mark.parametrize("fmt", ["ell", "csr_vector", "csr_merge", "sell"])
+@pytest.mark.parametrize("fmt", ["ell", "csr_vector", "csr_merge", "sell", "ell_xtile"])
 @pytest.mark.parametrize("name", ["c1s", "c1"])
 def test_conjugate_gradient(dev, fmt, name):
     """CG on the 5-point Laplacian (symmetric positive definite) recovers a

@@ -447,34 +447,33 @@ spmv_status build_sliced(spmv_handle **out, spmv_format fmt, int32_t R, int32_t 
     // per slice on the skewed and power-law workloads).  An explicit format is
     // kept as asked.
     if (fmt == SPMV_AUTO) fmt = SPMV_CSR_MERGE;
-    // Group the entries by slice: row index per entry, a stable sort on the
-    // slice number (entries of a slice keep their row-major order), then the
-    // rows, columns and values gathered in that order.  Slice b is the sorted
-    // range [bounds[b], bounds[b+1]); its row pointers come from counting its
-    // row indices and scanning, as in COO -> CSR.
+    // Group the entries by slice: row index per entry, then a stable sort on
+    // the slice number (entries of a slice keep their row-major order) that
+    // carries each entry's row, column and value along.  Slice b is the
+    // sorted range [bounds[b], bounds[b+1]); its row pointers come from
+    // counting its row indices and scanning, as in COO -> CSR.
     const int32_t nb = h->col_blocks;
-    int32_t *row_idx = nullptr, *iota = nullptr, *perm = nullptr, *bounds = nullptr;
+    int32_t *row_idx = nullptr, *bounds = nullptr;
     uint32_t *keys = nullptr, *keys_sorted = nullptr;
     int32_t *rows_s = nullptr, *col_s = nullptr;
     float *val_s = nullptr;
     SPMV_TRY(scratch.alloc(&row_idx, nnz));
     SPMV_TRY(scratch.alloc(&keys, nnz));
     SPMV_TRY(scratch.alloc(&keys_sorted, nnz));
-    SPMV_TRY(scratch.alloc(&iota, nnz));
-    SPMV_TRY(scratch.alloc(&perm, nnz));
     SPMV_TRY(scratch.alloc(&rows_s, nnz));
     SPMV_TRY(scratch.alloc(&col_s, nnz));
     SPMV_TRY(scratch.alloc(&val_s, nnz));
     SPMV_TRY(scratch.alloc(&bounds, static_cast<size_t>(nb) + 1));
     SPMV_HIP(launch_expand_rows(R, nnz, rp, row_idx, s));
     SPMV_HIP(launch_slice_keys(nnz, col, static_cast<int32_t>(slice), keys, s));
-    SPMV_HIP(launch_iota(nnz, iota, s));
-    SPMV_TRY(radix_sort_pairs(keys, iota, keys_sorted, perm, nnz,
-                              bits_for(static_cast<uint64_t>(nb - 1)), s, scratch));
+    const uint32_t *pin[3] = {reinterpret_cast<const uint32_t *>(row_idx),
+                              reinterpret_cast<const uint32_t *>(col),
+                              reinterpret_cast<const uint32_t *>(val)};
+    uint32_t *pout[3] = {reinterpret_cast<uint32_t *>(rows_s), reinterpret_cast<uint32_t *>(col_s),
+                         reinterpret_cast<uint32_t *>(val_s)};
+    SPMV_TRY(radix_sort(keys, keys_sorted, 3, pin, pout, nnz,
+                        bits_for(static_cast<uint64_t>(nb - 1)), s, scratch));
     SPMV_HIP(launch_slice_bounds(nnz, nb, keys_sorted, bounds, s));
-    SPMV_HIP(launch_gather_u32(nnz, perm, reinterpret_cast<const uint32_t *>(row_idx),
-                               reinterpret_cast<uint32_t *>(rows_s), s));
-    SPMV_HIP(launch_gather_pairs(nnz, perm, col, val, col_s, val_s, s));
     std::vector<int32_t> hb(static_cast<size_t>(nb) + 1);
     SPMV_HIP(hipMemcpyAsync(hb.data(), bounds, sizeof(int32_t) * hb.size(), hipMemcpyDeviceToHost,
                             s));
@@ -639,21 +638,20 @@ spmv_status coo_to_csr_impl(int32_t R, int32_t C, int32_t nnz, const int32_t *ri
         return SPMV_OK;
     }
     // stable sort of the entries by row (entries of a row keep their input
-    // order); the row counts are then taken on the sorted rows (one atomic per
-    // run of equal rows per wave instead of one per entry), scanned into
-    // rowPtrs, and the columns and values moved
-    int32_t *idx = nullptr, *perm = nullptr;
+    // order), columns and values moving with their rows straight into the
+    // outputs; the row counts are then taken on the sorted rows (one atomic
+    // per run of equal rows per wave instead of one per entry) and scanned
+    // into rowPtrs
     uint32_t *keys_sorted = nullptr;
-    SPMV_TRY(scratch.alloc(&idx, nnz));
-    SPMV_TRY(scratch.alloc(&perm, nnz));
     SPMV_TRY(scratch.alloc(&keys_sorted, nnz));
-    SPMV_HIP(launch_iota(nnz, idx, s));
-    SPMV_TRY(radix_sort_pairs(reinterpret_cast<const uint32_t *>(ri), idx, keys_sorted, perm, nnz,
-                              bits_for(R > 0 ? static_cast<uint64_t>(R - 1) : 0), s, scratch));
+    const uint32_t *pin[2] = {reinterpret_cast<const uint32_t *>(ci),
+                              reinterpret_cast<const uint32_t *>(v)};
+    uint32_t *pout[2] = {reinterpret_cast<uint32_t *>(c_out), reinterpret_cast<uint32_t *>(v_out)};
+    SPMV_TRY(radix_sort(reinterpret_cast<const uint32_t *>(ri), keys_sorted, 2, pin, pout, nnz,
+                        bits_for(R > 0 ? static_cast<uint64_t>(R - 1) : 0), s, scratch));
     SPMV_HIP(hipMemsetAsync(rp_out, 0, sizeof(int32_t) * (static_cast<size_t>(R) + 1), s));
     SPMV_HIP(launch_count_rows(nnz, reinterpret_cast<const int32_t *>(keys_sorted), rp_out, s));
     SPMV_TRY(exclusive_scan(rp_out, rp_out, R, true, s, scratch));
-    SPMV_HIP(launch_gather_pairs(nnz, perm, ci, v, c_out, v_out, s));
     return SPMV_OK;
 }
 

@@ -45,25 +45,6 @@ __global__ __launch_bounds__(kThreads) void k_count_rows(int32_t nnz,
     }
 }
 
-__global__ __launch_bounds__(kThreads) void k_iota(int32_t n, int32_t *__restrict__ out) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-    if (i < n) out[i] = static_cast<int32_t>(i);
-}
-
-__global__ __launch_bounds__(kThreads) void k_gather_pairs(int32_t n,
-                                                           const int32_t *__restrict__ perm,
-                                                           const int32_t *__restrict__ col_in,
-                                                           const uint32_t *__restrict__ val_in,
-                                                           int32_t *__restrict__ col_out,
-                                                           uint32_t *__restrict__ val_out) {
-    const int64_t p = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-    if (p < n) {
-        const int32_t src = perm[p];
-        col_out[p] = col_in[src];
-        val_out[p] = val_in[src];
-    }
-}
-
 // One wave per 64 consecutive rows; all 64 lanes fill each row's range in turn.
 __global__ __launch_bounds__(kThreads) void k_expand_rows(int32_t R,
                                                           const int32_t *__restrict__ rp,
@@ -576,13 +557,6 @@ __global__ __launch_bounds__(kThreads) void k_slice_bounds(int32_t nnz, int32_t 
     bounds[b] = static_cast<int32_t>(lo);
 }
 
-__global__ __launch_bounds__(kThreads) void k_gather_u32(int32_t n, const int32_t *__restrict__ perm,
-                                                         const uint32_t *__restrict__ in,
-                                                         uint32_t *__restrict__ out) {
-    const int64_t p = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-    if (p < n) out[p] = in[perm[p]];
-}
-
 // Merge path over rows (their end markers) and nonzeros: row r's end marker
 // sits at position rowPtrs[r+1] + r.  row_start[b] = number of rows whose end
 // marker lies before diagonal b * items_per_block.
@@ -608,22 +582,6 @@ __global__ __launch_bounds__(kThreads) void k_merge_partition(int32_t R, int32_t
 hipError_t launch_count_rows(int32_t nnz, const int32_t *row, int32_t *counts, hipStream_t s) {
     if (nnz <= 0) return hipSuccess;
     k_count_rows<<<grid_for(nnz, kThreads), kThreads, 0, s>>>(nnz, row, counts);
-    return hipGetLastError();
-}
-
-hipError_t launch_iota(int32_t n, int32_t *out, hipStream_t s) {
-    if (n <= 0) return hipSuccess;
-    k_iota<<<grid_for(n, kThreads), kThreads, 0, s>>>(n, out);
-    return hipGetLastError();
-}
-
-hipError_t launch_gather_pairs(int32_t nnz, const int32_t *perm, const int32_t *col_in,
-                               const float *val_in, int32_t *col_out, float *val_out,
-                               hipStream_t s) {
-    if (nnz <= 0) return hipSuccess;
-    k_gather_pairs<<<grid_for(nnz, kThreads), kThreads, 0, s>>>(
-        nnz, perm, col_in, reinterpret_cast<const uint32_t *>(val_in), col_out,
-        reinterpret_cast<uint32_t *>(val_out));
     return hipGetLastError();
 }
 
@@ -756,13 +714,6 @@ hipError_t launch_slice_bounds(int32_t nnz, int32_t K, const uint32_t *keys, int
                                hipStream_t s) {
     k_slice_bounds<<<grid_for(static_cast<int64_t>(K) + 1, kThreads), kThreads, 0, s>>>(
         nnz, K, keys, bounds);
-    return hipGetLastError();
-}
-
-hipError_t launch_gather_u32(int32_t n, const int32_t *perm, const uint32_t *in, uint32_t *out,
-                             hipStream_t s) {
-    if (n <= 0) return hipSuccess;
-    k_gather_u32<<<grid_for(n, kThreads), kThreads, 0, s>>>(n, perm, in, out);
     return hipGetLastError();
 }
 

@@ -247,17 +247,19 @@ hipError_t launch_len_hist(int32_t R, const int32_t *rp, int32_t W, int32_t *his
 spmv_status exclusive_scan(const int32_t *in, int32_t *out, int64_t n, bool write_total,
                            hipStream_t s, Scratch &scratch);
 
-// sort.hip: stable LSD radix sort of (key, value) pairs by the low key_bits.
+// sort.hip: stable LSD radix sort by the low key_bits of the keys; the
+// num_payloads (1..3) arrays pay_in[q] move with them into pay_out[q].
+// Outputs must not alias inputs.
+spmv_status radix_sort(const uint32_t *keys_in, uint32_t *keys_out, int num_payloads,
+                       const uint32_t *const *pay_in, uint32_t *const *pay_out, int64_t n,
+                       int key_bits, hipStream_t s, Scratch &scratch);
+// The same with one int32 payload.
 spmv_status radix_sort_pairs(const uint32_t *keys_in, const int32_t *vals_in,
                              uint32_t *keys_out, int32_t *vals_out, int64_t n, int key_bits,
                              hipStream_t s, Scratch &scratch);
 
 // build.hip
 hipError_t launch_count_rows(int32_t nnz, const int32_t *row, int32_t *counts, hipStream_t s);
-hipError_t launch_iota(int32_t n, int32_t *out, hipStream_t s);
-hipError_t launch_gather_pairs(int32_t nnz, const int32_t *perm, const int32_t *col_in,
-                               const float *val_in, int32_t *col_out, float *val_out,
-                               hipStream_t s);
 hipError_t launch_expand_rows(int32_t R, int32_t nnz, const int32_t *rp, int32_t *row_idx,
                               hipStream_t s);
 // ELL x tiles.  counts[3*b + {0,1,2}] = distinct columns, runs, span ok (1/0)
@@ -297,14 +299,12 @@ hipError_t launch_jds_chunks(int32_t R, int32_t depth, const int32_t *jds_len,
                              int32_t *chunks, hipStream_t s);
 hipError_t launch_jds_tiles(int32_t groups, int32_t ntiles, const int32_t *tile_off,
                             int2 *tiles, hipStream_t s);
-// Column slice [lo, hi) of a CSR matrix: per-row counts, then the entries in
-// their original order (row pointers come from an exclusive scan of counts).
+// x slices: keys[i] = col[i] / slice_cols; bounds[b] = first sorted entry
+// of slice b (bounds[K] = nnz).
 hipError_t launch_slice_keys(int32_t nnz, const int32_t *col, int32_t slice_cols,
                              uint32_t *keys, hipStream_t s);
 hipError_t launch_slice_bounds(int32_t nnz, int32_t K, const uint32_t *keys, int32_t *bounds,
                                hipStream_t s);
-hipError_t launch_gather_u32(int32_t n, const int32_t *perm, const uint32_t *in, uint32_t *out,
-                             hipStream_t s);
 hipError_t launch_merge_partition(int32_t R, int32_t nnz, const int32_t *rp, int32_t nblocks,
                                   int32_t *row_start, hipStream_t s);
 

@@ -454,15 +454,20 @@ spmv_status build_sliced(spmv_handle **out, spmv_format fmt, int32_t R, int32_t 
     // counting its row indices and scanning, as in COO -> CSR.
     const int32_t nb = h->col_blocks;
     int32_t *row_idx = nullptr, *bounds = nullptr;
-    uint32_t *keys = nullptr, *keys_sorted = nullptr;
+    uint32_t *keys = nullptr;
+    const uint32_t *keys_sorted = nullptr;
     int32_t *rows_s = nullptr, *col_s = nullptr;
     float *val_s = nullptr;
-    SPMV_TRY(scratch.alloc(&row_idx, nnz));
-    SPMV_TRY(scratch.alloc(&keys, nnz));
-    SPMV_TRY(scratch.alloc(&keys_sorted, nnz));
-    SPMV_TRY(scratch.alloc(&rows_s, nnz));
-    SPMV_TRY(scratch.alloc(&col_s, nnz));
-    SPMV_TRY(scratch.alloc(&val_s, nnz));
+    // one allocation for the five entry arrays (row index and slice key in,
+    // rows, columns and values out), each 256-byte aligned
+    const size_t nw = (static_cast<size_t>(nnz) + 63) & ~size_t{63};
+    uint32_t *arrays = nullptr;
+    SPMV_TRY(scratch.alloc(&arrays, 5 * nw));
+    row_idx = reinterpret_cast<int32_t *>(arrays);
+    keys = arrays + nw;
+    rows_s = reinterpret_cast<int32_t *>(arrays + 2 * nw);
+    col_s = reinterpret_cast<int32_t *>(arrays + 3 * nw);
+    val_s = reinterpret_cast<float *>(arrays + 4 * nw);
     SPMV_TRY(scratch.alloc(&bounds, static_cast<size_t>(nb) + 1));
     SPMV_HIP(launch_expand_rows(R, nnz, rp, row_idx, s));
     SPMV_HIP(launch_slice_keys(nnz, col, static_cast<int32_t>(slice), keys, s));
@@ -471,19 +476,21 @@ spmv_status build_sliced(spmv_handle **out, spmv_format fmt, int32_t R, int32_t 
                               reinterpret_cast<const uint32_t *>(val)};
     uint32_t *pout[3] = {reinterpret_cast<uint32_t *>(rows_s), reinterpret_cast<uint32_t *>(col_s),
                          reinterpret_cast<uint32_t *>(val_s)};
-    SPMV_TRY(radix_sort(keys, keys_sorted, 3, pin, pout, nnz,
-                        bits_for(static_cast<uint64_t>(nb - 1)), s, scratch));
+    SPMV_TRY(radix_sort(keys, nullptr, 3, pin, pout, nnz, bits_for(static_cast<uint64_t>(nb - 1)),
+                        s, scratch, &keys_sorted));
     SPMV_HIP(launch_slice_bounds(nnz, nb, keys_sorted, bounds, s));
     std::vector<int32_t> hb(static_cast<size_t>(nb) + 1);
     SPMV_HIP(hipMemcpyAsync(hb.data(), bounds, sizeof(int32_t) * hb.size(), hipMemcpyDeviceToHost,
                             s));
     SPMV_HIP(hipStreamSynchronize(s));
     int64_t best_nnz = -1;
+    // one row-pointer buffer serves every slice: each sub-build copies or
+    // consumes it on this stream before the next slice overwrites it
+    int32_t *prp = nullptr;
+    SPMV_TRY(scratch.alloc(&prp, static_cast<size_t>(R) + 1));
     for (int32_t b = 0; b < nb; ++b) {
         const int32_t p0 = hb[b], pn = hb[b + 1] - hb[b];
         if (pn == 0) continue;
-        int32_t *prp = nullptr;
-        SPMV_TRY(scratch.alloc(&prp, static_cast<size_t>(R) + 1));
         SPMV_HIP(hipMemsetAsync(prp, 0, sizeof(int32_t) * (static_cast<size_t>(R) + 1), s));
         SPMV_HIP(launch_count_rows(pn, rows_s + p0, prp, s));
         SPMV_TRY(exclusive_scan(prp, prp, R, true, s, scratch));
@@ -642,13 +649,13 @@ spmv_status coo_to_csr_impl(int32_t R, int32_t C, int32_t nnz, const int32_t *ri
     // outputs; the row counts are then taken on the sorted rows (one atomic
     // per run of equal rows per wave instead of one per entry) and scanned
     // into rowPtrs
-    uint32_t *keys_sorted = nullptr;
-    SPMV_TRY(scratch.alloc(&keys_sorted, nnz));
+    const uint32_t *keys_sorted = nullptr;
     const uint32_t *pin[2] = {reinterpret_cast<const uint32_t *>(ci),
                               reinterpret_cast<const uint32_t *>(v)};
     uint32_t *pout[2] = {reinterpret_cast<uint32_t *>(c_out), reinterpret_cast<uint32_t *>(v_out)};
-    SPMV_TRY(radix_sort(reinterpret_cast<const uint32_t *>(ri), keys_sorted, 2, pin, pout, nnz,
-                        bits_for(R > 0 ? static_cast<uint64_t>(R - 1) : 0), s, scratch));
+    SPMV_TRY(radix_sort(reinterpret_cast<const uint32_t *>(ri), nullptr, 2, pin, pout, nnz,
+                        bits_for(R > 0 ? static_cast<uint64_t>(R - 1) : 0), s, scratch,
+                        &keys_sorted));
     SPMV_HIP(hipMemsetAsync(rp_out, 0, sizeof(int32_t) * (static_cast<size_t>(R) + 1), s));
     SPMV_HIP(launch_count_rows(nnz, reinterpret_cast<const int32_t *>(keys_sorted), rp_out, s));
     SPMV_TRY(exclusive_scan(rp_out, rp_out, R, true, s, scratch));

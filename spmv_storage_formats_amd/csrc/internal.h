@@ -124,7 +124,9 @@ spmv_status from_hip(hipError_t e);
     } while (0)
 
 // Temporary device buffers of one host call; freed (after the stream drains)
-// when the object goes out of scope.
+// when the object goes out of scope.  Freeing a large buffer costs ~0.1-0.25
+// ms of host time (small ones next to nothing), so callers that need several
+// large temporaries at once take them as one allocation.
 class Scratch {
   public:
     explicit Scratch(hipStream_t s) : stream_(s) {}
@@ -249,10 +251,12 @@ spmv_status exclusive_scan(const int32_t *in, int32_t *out, int64_t n, bool writ
 
 // sort.hip: stable LSD radix sort by the low key_bits of the keys; the
 // num_payloads (1..3) arrays pay_in[q] move with them into pay_out[q].
-// Outputs must not alias inputs.
+// Outputs must not alias inputs.  keys_out may be null: the sorted keys then
+// live in scratch and *keys_result points to them.
 spmv_status radix_sort(const uint32_t *keys_in, uint32_t *keys_out, int num_payloads,
                        const uint32_t *const *pay_in, uint32_t *const *pay_out, int64_t n,
-                       int key_bits, hipStream_t s, Scratch &scratch);
+                       int key_bits, hipStream_t s, Scratch &scratch,
+                       const uint32_t **keys_result = nullptr);
 // The same with one int32 payload.
 spmv_status radix_sort_pairs(const uint32_t *keys_in, const int32_t *vals_in,
                              uint32_t *keys_out, int32_t *vals_out, int64_t n, int key_bits,

@@ -167,15 +167,29 @@ __global__ __launch_bounds__(kThreads) void k_radix_scatter(
 
 spmv_status radix_sort(const uint32_t *keys_in, uint32_t *keys_out, int num_payloads,
                        const uint32_t *const *pay_in, uint32_t *const *pay_out, int64_t n,
-                       int key_bits, hipStream_t s, Scratch &scratch) {
+                       int key_bits, hipStream_t s, Scratch &scratch,
+                       const uint32_t **keys_result) {
     if (num_payloads < 1 || num_payloads > kMaxPayload) return SPMV_ERR_INVALID_ARG;
+    if (!keys_out && !keys_result) return SPMV_ERR_INVALID_ARG;
     if (n <= 0) return SPMV_OK;
     if (n > INT32_MAX) return SPMV_ERR_TOO_LARGE;
     const int passes = key_bits <= 8 ? 1 : (key_bits + 7) / 8;
     const int32_t nblocks = static_cast<int32_t>((n + kTile - 1) / kTile);
     if (static_cast<int64_t>(nblocks) * kRadix > INT32_MAX) return SPMV_ERR_TOO_LARGE;
-    int32_t *counts = nullptr;
-    SPMV_TRY(scratch.alloc(&counts, static_cast<size_t>(nblocks) * kRadix));
+    // one allocation (each free of a large buffer costs host time): the
+    // [digit][tile] counts, the sorted keys when the caller leaves them to
+    // scratch, then (more than one pass) the ping-pong keys and payloads;
+    // every array 256-byte aligned
+    const size_t n_counts = (static_cast<size_t>(nblocks) * kRadix + 63) & ~size_t{63};
+    const size_t n_words = (static_cast<size_t>(n) + 63) & ~size_t{63};
+    const size_t own_keys = keys_out ? 0 : n_words;
+    const int tmp_arrays = passes > 1 ? 1 + num_payloads : 0;
+    uint32_t *block = nullptr;
+    SPMV_TRY(scratch.alloc(&block, n_counts + own_keys + n_words * tmp_arrays));
+    int32_t *counts = reinterpret_cast<int32_t *>(block);
+    if (!keys_out) keys_out = block + n_counts;
+    if (keys_result) *keys_result = keys_out;
+    block += own_keys;
     uint32_t *kt = nullptr;
     PayloadOut tmp{}, out{};
     PayloadIn src{};
@@ -184,9 +198,8 @@ spmv_status radix_sort(const uint32_t *keys_in, uint32_t *keys_out, int num_payl
         src.p[q] = pay_in[q];
     }
     if (passes > 1) {
-        SPMV_TRY(scratch.alloc(&kt, static_cast<size_t>(n)));
-        for (int q = 0; q < num_payloads; ++q)
-            SPMV_TRY(scratch.alloc(&tmp.p[q], static_cast<size_t>(n)));
+        kt = block + n_counts;
+        for (int q = 0; q < num_payloads; ++q) tmp.p[q] = block + n_counts + n_words * (1 + q);
     }
     // Ping-pong so that the last pass lands in the outputs.
     const uint32_t *src_k = keys_in;

@@ -369,10 +369,24 @@ __global__ __launch_bounds__(kThreads) void k_ell_xtile(int32_t R, int32_t W,
     const uint32_t b = xcd_remap(blockIdx.x, gridDim.x);
     const int k0 = run_ptr[b], k1 = run_ptr[b + 1];
     const int lane = __lane_id();
+    // a wave per run; each lane keeps 8 loads in flight before its LDS stores
+    constexpr int kCopy = 8;
     for (int k = k0 + static_cast<int>(threadIdx.x / kWave); k < k1; k += kThreads / kWave) {
         const int64_t q = 3 * static_cast<int64_t>(k);
         const int32_t start = runs[q], off = runs[q + 1], len = runs[q + 2];
-        for (int i = lane; i < len; i += kWave) tile[off + i] = x[start + i];
+        for (int i0 = 0; i0 < len; i0 += kCopy * kWave) {
+            float v[kCopy];
+#pragma unroll
+            for (int u = 0; u < kCopy; ++u) {
+                const int i = i0 + u * kWave + lane;
+                v[u] = i < len ? x[start + i] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < kCopy; ++u) {
+                const int i = i0 + u * kWave + lane;
+                if (i < len) tile[off + i] = v[u];
+            }
+        }
     }
     __syncthreads();
     const uint32_t r = b * kThreads + threadIdx.x;

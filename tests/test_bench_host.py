@@ -49,3 +49,13 @@ def test_oracle_only_in_cpu_baseline_leg():
     for n in top_imports:
         names = [a.name for a in n.names] + [getattr(n, "module", None) or ""]
         assert not any(x.split(".")[0] == "oracle" for x in names)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert p.returncode == 2
+    assert "one GPU" in p.stderr
+    assert p.stdout == ""

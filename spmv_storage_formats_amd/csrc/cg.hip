@@ -9,6 +9,9 @@
 //   k_dot:          partials of p·Ap
 //   k_cg_update:    alpha = rr / pAp; x += alpha p; r -= alpha Ap; partials of r'·r'
 //   k_cg_direction: beta = r'·r' / rr; p = r' + beta p; Ap = 0
+// On a plain ELL handle of up to kDotBlocks * kThreads rows two launches do
+// the same arithmetic: k_cg_ell_step (the previous iteration's new direction,
+// Ap = A p and p·Ap) and k_cg_update.
 // Dot products are fp64 per-block partials.  A kernel that needs a dot product
 // adds the partials itself, every block in the same order, so all blocks agree
 // bit for bit and the whole solve is deterministic when the SpMV is; no grid-
@@ -138,10 +141,90 @@ __global__ __launch_bounds__(kThreads) void k_cg_direction(int32_t n, int np,
     }
 }
 
+// ELL handles: one kernel for the new direction, the SpMV and p·Ap.
+// beta = rr_new / rr_old (0 when rr_old == 0) from the partials, the same
+// expression as k_cg_direction; every row of p_new is r + beta p_old, formed
+// again wherever the SpMV gathers it (the same fp32 expression, so the same
+// bits), and written once by its own lane into the other p buffer (the
+// gathers read only p_old, so no block sees a half-updated p).  Row i is
+// handled by block (i / kThreads) % gridDim.x, in the thread and order k_dot
+// uses for element i, so the p·Ap partials equal k_dot's, and each row sums
+// its slots in slot order like k_ell: the iterates are those of the
+// four-launch iteration.
+__global__ __launch_bounds__(kThreads) void k_cg_ell_step(
+    int32_t n, int32_t W, const int32_t *__restrict__ col, const float *__restrict__ val,
+    const int32_t *__restrict__ len, int np, const double *__restrict__ part_rr_old,
+    const double *__restrict__ part_rr_new, const float *__restrict__ r,
+    const float *__restrict__ p_old, float *__restrict__ p_new, float *__restrict__ ap,
+    double *__restrict__ part_pap) {
+    constexpr int U = 4;
+    __shared__ double lds[kThreads / kWave];
+    const double rr = sum_partials(part_rr_old, np, lds);
+    const double rr_new = sum_partials(part_rr_new, np, lds);
+    const float beta = rr != 0.0 ? static_cast<float>(rr_new / rr) : 0.f;
+    const uint32_t nu = static_cast<uint32_t>(n), wu = static_cast<uint32_t>(W);
+    double s = 0.0;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * kThreads) {
+        const uint32_t row = static_cast<uint32_t>(i);
+        const int32_t m = len[row];
+        float sum = 0.f;
+        for (uint32_t t0 = 0; t0 < wu; t0 += U) {
+            int32_t c[U];
+            float v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t t = t0 + u;
+                const uint32_t slot = t * nu + row;
+                c[u] = t < wu ? ld_nt(col + slot) : 0;
+                v[u] = t < wu ? ld_nt(val + slot) : 0.f;
+            }
+            float pv[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                pv[u] = (t0 + u < static_cast<uint32_t>(m)) ? r[c[u]] + beta * p_old[c[u]] : 0.f;
+#pragma unroll
+            for (int u = 0; u < U; ++u) sum += v[u] * pv[u];
+        }
+        const float pi = r[row] + beta * p_old[row];
+        const float q = 0.f + sum;
+        p_new[row] = pi;
+        ap[row] = q;
+        s += static_cast<double>(pi) * static_cast<double>(q);
+    }
+    const double t = block_sum_all(s, lds);
+    if (threadIdx.x == 0) part_pap[blockIdx.x] = t;
+}
+
+// The fused step applies to a plain (unsliced) ELL handle whose rows one pass
+// of the dot grid covers (a row per thread): past that its threads walk rows
+// one after another and the kernel runs at well under half of k_ell's rate
+// (2048^2 Laplacian: 97 against 41 us), so the four-launch iteration is
+// faster.  SPMV_CG_FUSED=0 asks for the four launches everywhere.
+bool fused_ell(const spmv_handle *A) {
+    const char *v = std::getenv("SPMV_CG_FUSED");
+    if (v && std::strcmp(v, "0") == 0) return false;
+    return A->format == SPMV_ELL && A->parts.empty() && A->ell_width > 0 &&
+           A->stats.num_rows <= static_cast<int64_t>(kDotBlocks) * kThreads;
+}
+
 // One CG iteration's launches on `st`: SpMV, p·Ap, update, new direction.
 spmv_status enqueue_iteration(const spmv_handle *A, int32_t n, int np, float *x, float *r,
-                              float *p, float *ap, double *part_pap, double *const part_rr[2],
-                              int cur, hipStream_t st) {
+                              float *const pbuf[2], float *ap, double *part_pap,
+                              double *const part_rr[2], int cur, bool fused, hipStream_t st) {
+    if (fused) {
+        // direction of the previous iteration, SpMV and p·Ap in one launch;
+        // the new p goes to the other buffer
+        float *p_old = pbuf[cur], *p = pbuf[cur ^ 1];
+        k_cg_ell_step<<<np, kThreads, 0, st>>>(n, A->ell_width, A->a.ell_col, A->a.ell_val,
+                                               A->a.ell_nnz, np, part_rr[cur ^ 1], part_rr[cur],
+                                               r, p_old, p, ap, part_pap);
+        k_cg_update<<<np, kThreads, 0, st>>>(n, np, part_rr[cur], part_pap, p, ap, x, r,
+                                             part_rr[cur ^ 1]);
+        SPMV_HIP(hipGetLastError());
+        return SPMV_OK;
+    }
+    float *p = pbuf[0];
     SPMV_TRY(launch_spmv(A, p, ap, st));
     k_dot<<<np, kThreads, 0, st>>>(n, p, ap, part_pap);
     k_cg_update<<<np, kThreads, 0, st>>>(n, np, part_rr[cur], part_pap, p, ap, x, r,
@@ -170,16 +253,18 @@ struct BatchGraph {
     }
 };
 
-static_assert(kCheckEvery % 2 == 0, "a batch must return the r.r partials to their buffer");
+static_assert(kCheckEvery % 2 == 0,
+              "a batch must return the r.r partials and the p buffers to their places");
 
 spmv_status capture_batch(BatchGraph &g, const spmv_handle *A, int32_t n, int np, float *x,
-                          float *r, float *p, float *ap, double *part_pap,
-                          double *const part_rr[2], int cur) {
+                          float *r, float *const pbuf[2], float *ap, double *part_pap,
+                          double *const part_rr[2], int cur, bool fused) {
     SPMV_HIP(hipStreamCreateWithFlags(&g.cs, hipStreamNonBlocking));
     SPMV_HIP(hipStreamBeginCapture(g.cs, hipStreamCaptureModeThreadLocal));
     spmv_status st = SPMV_OK;
     for (int k = 0; k < kCheckEvery && st == SPMV_OK; ++k)
-        st = enqueue_iteration(A, n, np, x, r, p, ap, part_pap, part_rr, cur ^ (k & 1), g.cs);
+        st = enqueue_iteration(A, n, np, x, r, pbuf, ap, part_pap, part_rr, cur ^ (k & 1), fused,
+                               g.cs);
     const hipError_t e = hipStreamEndCapture(g.cs, &g.graph);
     if (st != SPMV_OK) return st;
     SPMV_HIP(e);
@@ -213,12 +298,15 @@ spmv_status conjugate_gradient(const spmv_handle *A, const float *b, float *x, i
     *iters = 0;
     *rel_resid = 0.f;
     if (n == 0) return SPMV_OK;
-    float *r = nullptr, *p = nullptr, *ap = nullptr;
-    double *part = nullptr;   // [pAp | rr slot 0 | rr slot 1 | bb], kDotBlocks each
-    SPMV_TRY(scratch.alloc(&r, n));
-    SPMV_TRY(scratch.alloc(&p, n));
-    SPMV_TRY(scratch.alloc(&ap, n));
-    SPMV_TRY(scratch.alloc(&part, 4 * kDotBlocks));
+    const bool fused = fused_ell(A);
+    // one allocation: r, two p buffers, Ap (each 256-byte aligned), then the
+    // partials [pAp | rr slot 0 | rr slot 1 | bb], kDotBlocks each
+    const size_t nv = (static_cast<size_t>(n) + 63) & ~size_t{63};
+    float *vecs = nullptr;
+    SPMV_TRY(scratch.alloc(&vecs, 4 * nv + 2 * 4 * kDotBlocks));
+    float *r = vecs, *ap = vecs + 3 * nv;
+    float *const pbuf[2] = {vecs + nv, vecs + 2 * nv};
+    double *part = reinterpret_cast<double *>(vecs + 4 * nv);
     double *part_pap = part, *part_bb = part + 3 * kDotBlocks;
     double *part_rr[2] = {part + kDotBlocks, part + 2 * kDotBlocks};
     const unsigned gn = grid_for(n, kThreads);
@@ -229,8 +317,17 @@ spmv_status conjugate_gradient(const spmv_handle *A, const float *b, float *x, i
     k_fill<<<gn, kThreads, 0, s>>>(n, 0.f, ap);
     SPMV_HIP(hipGetLastError());
     SPMV_TRY(launch_spmv(A, x, ap, s));
-    k_cg_start<<<np, kThreads, 0, s>>>(n, b, ap, r, p, part_rr[0], part_bb);
+    k_cg_start<<<np, kThreads, 0, s>>>(n, b, ap, r, pbuf[0], part_rr[0], part_bb);
     SPMV_HIP(hipGetLastError());
+    if (fused) {
+        // the fused iteration forms p = r + beta p_old: p_old = 0 and the
+        // previous r·r slot equal to the current one give p = r at the start
+        // (beta = 1, or 0 when r·r = 0), with every iteration alike
+        k_fill<<<gn, kThreads, 0, s>>>(n, 0.f, pbuf[0]);
+        SPMV_HIP(hipGetLastError());
+        SPMV_HIP(hipMemcpyAsync(part_rr[1], part_rr[0], sizeof(double) * kDotBlocks,
+                                hipMemcpyDeviceToDevice, s));
+    }
     double bb = 0.0, rr = 0.0;
     SPMV_TRY(host_sum(part_bb, np, host, &bb, s));
     SPMV_TRY(host_sum(part_rr[0], np, host, &rr, s));
@@ -245,11 +342,14 @@ spmv_status conjugate_gradient(const spmv_handle *A, const float *b, float *x, i
     while (it < max_iter && rnorm > target) {
         const int32_t batch = std::min(kCheckEvery, max_iter - it);
         if (use_graph && batch == kCheckEvery) {
-            if (!g.exec) SPMV_TRY(capture_batch(g, A, n, np, x, r, p, ap, part_pap, part_rr, cur));
+            if (!g.exec)
+                SPMV_TRY(capture_batch(g, A, n, np, x, r, pbuf, ap, part_pap, part_rr, cur,
+                                       fused));
             SPMV_HIP(hipGraphLaunch(g.exec, s));
         } else {
             for (int32_t k = 0; k < batch; ++k) {
-                SPMV_TRY(enqueue_iteration(A, n, np, x, r, p, ap, part_pap, part_rr, cur, s));
+                SPMV_TRY(enqueue_iteration(A, n, np, x, r, pbuf, ap, part_pap, part_rr, cur,
+                                           fused, s));
                 cur ^= 1;
             }
         }

@@ -752,6 +752,28 @@ def test_cg_graph_replays_match_eager(dev, fmt, monkeypatch):
             assert np.array_equal(xs["1"].view(np.uint32), xs["0"].view(np.uint32)), batches
 
 
+@pytest.mark.parametrize("name", ["c1s", "c1"])
+@pytest.mark.parametrize("k", [1, 5, 16, 40])
+def test_cg_fused_ell_iteration_matches_four_launches(dev, name, k, monkeypatch):
+    """On an ELL handle CG runs two launches per iteration (direction, SpMV
+    and p.Ap fused); the arithmetic is the four-launch iteration's, so after k
+    iterations (eager below 16, graph replays from 16) x is bit-identical with
+    SPMV_CG_FUSED=0."""
+    w = W(name)
+    b = torch.from_numpy(_cg_rhs(w)).to(dev)
+    h = build("ell", w, dev)
+    assert h.format == "ell"
+    xs = {}
+    for mode in ("1", "0"):
+        monkeypatch.setenv("SPMV_CG_FUSED", mode)
+        x = torch.zeros(w.num_rows, device=dev)
+        iters, rel = h.cg(b, x, max_iter=k, rtol=0.0)
+        assert iters == k
+        xs[mode] = (x.cpu().numpy(), rel)
+    assert np.array_equal(xs["1"][0].view(np.uint32), xs["0"][0].view(np.uint32))
+    assert xs["1"][1] == xs["0"][1]
+
+
 def test_build_destroy_cycles_release_device_memory(dev):
     """Handles own their device arrays and free them on destroy; builders free
     their scratch: 30 build/run/destroy cycles over every format leave the

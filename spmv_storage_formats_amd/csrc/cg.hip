@@ -108,14 +108,28 @@ __global__ __launch_bounds__(kThreads) void k_cg_update(int32_t n, int np,
                                                         float *__restrict__ r,
                                                         double *__restrict__ part_rr_new) {
     __shared__ double lds[kThreads / kWave];
+    // the thread's first element is loaded before the partials are added
+    const int64_t i0 = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    float xv = 0.f, pv = 0.f, rv = 0.f, av = 0.f;
+    if (i0 < n) {
+        xv = x[i0];
+        pv = p[i0];
+        rv = r[i0];
+        av = ap[i0];
+    }
     const double rr = sum_partials(part_rr, np, lds);
     const double pap = sum_partials(part_pap, np, lds);
     const float alpha = pap != 0.0 ? static_cast<float>(rr / pap) : 0.f;
     double s = 0.0;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n;
-         i += static_cast<int64_t>(gridDim.x) * kThreads) {
-        x[i] += alpha * p[i];
-        const float ri = r[i] - alpha * ap[i];
+    for (int64_t i = i0; i < n; i += static_cast<int64_t>(gridDim.x) * kThreads) {
+        if (i != i0) {
+            xv = x[i];
+            pv = p[i];
+            rv = r[i];
+            av = ap[i];
+        }
+        x[i] = xv + alpha * pv;
+        const float ri = rv - alpha * av;
         r[i] = ri;
         s += static_cast<double>(ri) * static_cast<double>(ri);
     }
@@ -131,12 +145,21 @@ __global__ __launch_bounds__(kThreads) void k_cg_direction(int32_t n, int np,
                                                            float *__restrict__ p,
                                                            float *__restrict__ ap) {
     __shared__ double lds[kThreads / kWave];
+    const int64_t i0 = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    float rv = 0.f, pv = 0.f;
+    if (i0 < n) {
+        rv = r[i0];
+        pv = p[i0];
+    }
     const double rr = sum_partials(part_rr, np, lds);
     const double rr_new = sum_partials(part_rr_new, np, lds);
     const float beta = rr != 0.0 ? static_cast<float>(rr_new / rr) : 0.f;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n;
-         i += static_cast<int64_t>(gridDim.x) * kThreads) {
-        p[i] = r[i] + beta * p[i];
+    for (int64_t i = i0; i < n; i += static_cast<int64_t>(gridDim.x) * kThreads) {
+        if (i != i0) {
+            rv = r[i];
+            pv = p[i];
+        }
+        p[i] = rv + beta * pv;
         ap[i] = 0.f;
     }
 }
@@ -157,36 +180,51 @@ __global__ __launch_bounds__(kThreads) void k_cg_ell_step(
     const double *__restrict__ part_rr_new, const float *__restrict__ r,
     const float *__restrict__ p_old, float *__restrict__ p_new, float *__restrict__ ap,
     double *__restrict__ part_pap) {
-    constexpr int U = 4;
+    // one row per thread (the host launches this only when the grid covers
+    // every row); the first kPre slots, their gathers and the row's own r and
+    // p are loaded before the partials are added, hiding that latency
+    constexpr int kPre = 8;
     __shared__ double lds[kThreads / kWave];
+    const uint32_t nu = static_cast<uint32_t>(n), wu = static_cast<uint32_t>(W);
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    const bool has = i < n;
+    const uint32_t row = has ? static_cast<uint32_t>(i) : 0u;
+    const int32_t m = has ? len[row] : 0;
+    int32_t c[kPre];
+    float v[kPre], rc[kPre], pc[kPre];
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+        const bool ok = has && static_cast<uint32_t>(u) < wu;
+        const uint32_t slot = static_cast<uint32_t>(u) * nu + row;
+        c[u] = ok ? ld_nt(col + slot) : 0;
+        v[u] = ok ? ld_nt(val + slot) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+        const bool live = u < m;
+        rc[u] = live ? r[c[u]] : 0.f;
+        pc[u] = live ? p_old[c[u]] : 0.f;
+    }
+    const float r_own = has ? r[row] : 0.f, p_own = has ? p_old[row] : 0.f;
     const double rr = sum_partials(part_rr_old, np, lds);
     const double rr_new = sum_partials(part_rr_new, np, lds);
     const float beta = rr != 0.0 ? static_cast<float>(rr_new / rr) : 0.f;
-    const uint32_t nu = static_cast<uint32_t>(n), wu = static_cast<uint32_t>(W);
     double s = 0.0;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n;
-         i += static_cast<int64_t>(gridDim.x) * kThreads) {
-        const uint32_t row = static_cast<uint32_t>(i);
-        const int32_t m = len[row];
+    if (has) {
         float sum = 0.f;
-        for (uint32_t t0 = 0; t0 < wu; t0 += U) {
-            int32_t c[U];
-            float v[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const uint32_t t = t0 + u;
-                const uint32_t slot = t * nu + row;
-                c[u] = t < wu ? ld_nt(col + slot) : 0;
-                v[u] = t < wu ? ld_nt(val + slot) : 0.f;
-            }
-            float pv[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                pv[u] = (t0 + u < static_cast<uint32_t>(m)) ? r[c[u]] + beta * p_old[c[u]] : 0.f;
-#pragma unroll
-            for (int u = 0; u < U; ++u) sum += v[u] * pv[u];
+        for (int u = 0; u < kPre; ++u) {
+            const float pv = u < m ? rc[u] + beta * pc[u] : 0.f;
+            if (static_cast<uint32_t>(u) < wu) sum += v[u] * pv;
         }
-        const float pi = r[row] + beta * p_old[row];
+        for (uint32_t t = kPre; t < wu; ++t) {
+            const uint32_t slot = t * nu + row;
+            const int32_t ct = ld_nt(col + slot);
+            const float vt = ld_nt(val + slot);
+            const float pv = t < static_cast<uint32_t>(m) ? r[ct] + beta * p_old[ct] : 0.f;
+            sum += vt * pv;
+        }
+        const float pi = r_own + beta * p_own;
         const float q = 0.f + sum;
         p_new[row] = pi;
         ap[row] = q;

@@ -422,6 +422,33 @@ def test_coo_to_csr_bitexact(dev, name, shuffle):
     assert np.array_equal(bits(v_d.cpu().numpy()), bits(v_o))
 
 
+@pytest.mark.parametrize("num_rows,nnz,hot", [
+    (200, 4096 * 3 + 17, 0.0),          # one 8-bit pass, ragged last tile
+    (70_000, 1_000_003, 0.0),           # three passes (17-bit rows), ragged tile
+    (300_000, 2_500_001, 0.6),          # three passes; 60 % of entries in 5 rows
+    (1 << 20, 4096, 0.5),               # fewer entries than one tile, mostly one row
+])
+def test_coo_to_csr_sort_shapes(dev, num_rows, nnz, hot):
+    """The COO -> CSR stable sort at the shapes its passes and tiles take:
+    one or three digit passes, a ragged last tile, and runs of equal rows
+    that span many 4096-entry tiles (stability across tiles and passes).
+    Columns are the entry's input position, so the output columns also show
+    the order inside each row; bit-exact against the oracle."""
+    rng = np.random.default_rng(num_rows + nnz)
+    ri = rng.integers(0, num_rows, nnz).astype(np.int32)
+    if hot:
+        k = int(hot * nnz)
+        ri[rng.permutation(nnz)[:k]] = rng.integers(0, num_rows, 5)[rng.integers(0, 5, k)]
+    ci = (np.arange(nnz) % (1 << 30)).astype(np.int32)
+    v = rng.standard_normal(nnz).astype(np.float32)
+    rp_o, ci_o, v_o = oracle.coo_to_csr(num_rows, ri, ci, v)
+    t = lambda a: torch.from_numpy(a).to(dev)  # noqa: E731
+    rp_d, ci_d, v_d = spmv.coo_to_csr(t(ri), t(ci), t(v), num_rows, 1 << 30)
+    assert np.array_equal(rp_d.cpu().numpy(), rp_o)
+    assert np.array_equal(ci_d.cpu().numpy(), ci_o)
+    assert np.array_equal(bits(v_d.cpu().numpy()), bits(v_o))
+
+
 @pytest.mark.parametrize("fmt", ALL_FORMATS)
 def test_build_coo_spmv(dev, fmt):
     w = W("c4s")

@@ -23,9 +23,12 @@ constexpr int64_t kXSliceBytes = 4 << 20;
 constexpr int64_t kL2Bytes = 4 << 20;
 constexpr int kMaxColBlocks = 64;
 
-// Merge-path CSR: 256 threads x 8 merge items (row ends + nonzeros) per block.
-constexpr int kMergeThreads = 256;
-constexpr int kMergeItemsPerThread = 8;
+// Merge-path CSR: 512 threads x 5 merge items (row ends + nonzeros) per block.
+// (Swept on MI355X over 2-16 items and 128-1024 threads: short per-thread
+// chains in large blocks win; the power-law matrix in 4 x slices 512 -> 478
+// us, the skewed one in 2 slices 235 -> 222 us against 256 x 8.)
+constexpr int kMergeThreads = 512;
+constexpr int kMergeItemsPerThread = 5;
 constexpr int kMergeItemsPerBlock = kMergeThreads * kMergeItemsPerThread;
 
 // ELL with x tiles: rows in blocks of kTileRows; a block qualifies when its

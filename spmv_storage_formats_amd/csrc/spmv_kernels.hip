@@ -562,9 +562,10 @@ __global__ __launch_bounds__(kThreads) void k_sell(int32_t R, int32_t ntiles, in
 // graphs; "Introduction to sparse computing", parallel efficiency: split by
 // nonzero count, split long rows].  The rows' end markers and the nonzeros
 // form one sequence of R + nnz items; block b owns items
-// [b*2048, (b+1)*2048), starting at row row_start[b].  The block stages its
-// row ends and its products val*x[col] (coalesced loads) in LDS, each thread
-// consumes 8 items of the merged sequence and adds its per-row partial sums
+// [b*NB, (b+1)*NB) (NB = kMergeItemsPerBlock), starting at row row_start[b].
+// The block stages its row ends and its products val*x[col] (coalesced loads)
+// in LDS, each thread consumes kMergeItemsPerThread items of the merged
+// sequence and adds its per-row partial sums
 // into LDS accumulators, then the block adds each row's sum into y (a row cut
 // by the block's ends receives one piece from each block it touches).
 // ---------------------------------------------------------------------------
@@ -599,7 +600,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(int32_t R, int32_t nnz,
     for (int i = tid; i <= nr; i += kMergeThreads) s_acc[i] = 0.f;
     __syncthreads();
 
-    // Start of this thread's 8 items on the merge path: the number i of row
+    // Start of this thread's IPT items on the merge path: the number i of row
     // ends before diagonal dt (row end i sits at local position s_end[i] + i).
     const int32_t items = nr + nk;
     const int32_t dt = min(tid * IPT, items);

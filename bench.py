@@ -257,6 +257,10 @@ def main():
 
     traffic = measured_traffic(f"{args.config}/{selected}")
     overhead_us = event_overhead_us(torch)
+    gather_ref = None
+    if args.config in ("c2", "c4", "c5"):   # uniformly random columns
+        gather_ref = gather_reference(torch, dev, C, nnz, flush_buf)
+        gather_ref["spmv_g_gathers_per_s"] = round(nnz / (med * 1e3) / 1e3, 1)
 
     result = {
         "metric": "SpMV GFLOP/s and effective HBM GB/s (% of MI355X peak) per format, 1 GPU",
@@ -285,6 +289,7 @@ def main():
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "bytes_per_launch_alg": B},
         "formats": per_format,
+        "gather_reference": gather_ref,
     }
     if not args.only_selected:
         result["coo_to_csr"] = coo_section(spmv, torch, w, dev)
@@ -383,6 +388,36 @@ def cg_section(spmv, torch, synth, dev, flush_buf):
         out.append(entry)
         h.close()
     return out
+
+
+def gather_reference(torch, dev, num_cols, n, flush_buf, steps=20):
+    """A library random gather for context on the random-column workloads:
+    torch.index_select of n uniform random int32 column indices from an x of
+    num_cols floats, timed like a step (cache flush, HIP events).  It moves
+    no matrix values and no y, so an SpMV that does the same number of
+    gathers in less time is at the device's random-gather limit, not at a
+    byte limit."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(12345)
+    x = torch.rand(num_cols, device=dev, generator=g)
+    idx = torch.randint(0, num_cols, (n,), device=dev, generator=g, dtype=torch.int64)
+    idx = idx.to(torch.int32)
+    out = torch.empty(n, device=dev)
+    stream = torch.cuda.current_stream()
+    torch.index_select(x, 0, idx, out=out)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(steps):
+        flush_buf.zero_()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        torch.index_select(x, 0, idx, out=out)
+        b.record(stream)
+        b.synchronize()
+        ts.append(a.elapsed_time(b))
+    us = statistics.median(ts) * 1e3
+    return {"kernel": "torch.index_select, int32 indices", "gathers": n, "x_floats": num_cols,
+            "us_median": round(us, 2), "g_gathers_per_s": round(n / us / 1e3, 1)}
 
 
 def event_overhead_us(torch):

@@ -329,8 +329,12 @@ spmv_status spmv_run(const spmv_handle *h, const float *x_dev, float *y_dev, voi
  *   From max_iter >= 16 on, each batch of 8 iterations is captured once as a
  *   HIP graph and replayed (one launch per batch); setting the environment
  *   variable SPMV_CG_GRAPH=0 launches every kernel directly instead (same
- *   arithmetic, same results).  Allocates its
- *   three work vectors, runs every step on `stream`, host-synchronous.
+ *   arithmetic, same results).  On a plain ELL handle of at most 262,144
+ *   rows an iteration is two kernels (the new direction, A·p and p·Ap fused;
+ *   then the update) instead of the SpMV and three vector kernels, with the
+ *   same results bit for bit; SPMV_CG_FUSED=0 selects the four launches.
+ *   Allocates its four work vectors (r, two p buffers, A·p) and the dot
+ *   partials, runs every step on `stream`, host-synchronous.
  *   Symmetry and definiteness are the caller's promise (not checked).
  */
 spmv_status spmv_cg(const spmv_handle *h, const float *b_dev, float *x_dev, int32_t max_iter,

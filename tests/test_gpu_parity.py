@@ -801,6 +801,49 @@ def test_cg_fused_ell_iteration_matches_four_launches(dev, name, k, monkeypatch)
     assert xs["1"][1] == xs["0"][1]
 
 
+def _spd27(n):
+    """The 27-point structure on an n^3 grid with diagonal 26 and off-diagonals
+    -1: symmetric, diagonally dominant (strictly on the faces), irreducible,
+    so positive definite; ELL width 27."""
+    w = synth.stencil27(n)
+    rows = oracle.csr_to_coo(w.row_ptrs)
+    w.values = np.where(w.col_idx == rows, 26.0, -1.0).astype(np.float32)
+    return w
+
+
+@pytest.mark.parametrize("k", [3, 16])
+def test_cg_fused_ell_wide_rows(dev, k, monkeypatch):
+    """Rows wider than the fused step's 8 preloaded slots (width 27): the fused
+    iteration stays bit-identical to the four launches, and after k steps x
+    matches the oracle's CG iterate within k * kappa * 2^-24 * max|x|, kappa
+    from the operator's extreme eigenvalues (scipy, fp64)."""
+    n = 16
+    w = _spd27(n)
+    b32 = _cg_rhs(w)
+    b = torch.from_numpy(b32).to(dev)
+    h = build("ell", w, dev)
+    assert h.format == "ell" and h.info["ell_width"] == 27
+    xs = {}
+    for mode in ("1", "0"):
+        monkeypatch.setenv("SPMV_CG_FUSED", mode)
+        x = torch.zeros(w.num_rows, device=dev)
+        iters, _ = h.cg(b, x, max_iter=k, rtol=0.0)
+        assert iters == k
+        xs[mode] = x.cpu().numpy()
+    assert np.array_equal(xs["1"].view(np.uint32), xs["0"].view(np.uint32))
+    xo, ko, _ = oracle.cg(w.row_ptrs, w.col_idx, w.values, b32.astype(np.float64),
+                          max_iter=k, rtol=0.0)
+    assert ko == k
+    import scipy.sparse as sp
+    import scipy.sparse.linalg as sl
+    a = sp.csr_matrix((w.values.astype(np.float64), w.col_idx, w.row_ptrs))
+    lo = sl.eigsh(a, k=1, which="SA", return_eigenvectors=False)[0]
+    hi = sl.eigsh(a, k=1, which="LA", return_eigenvectors=False)[0]
+    assert lo > 0
+    tol = k * (hi / lo) * 2.0**-24 * np.max(np.abs(xo))
+    assert np.max(np.abs(xs["1"].astype(np.float64) - xo)) <= tol
+
+
 def test_build_destroy_cycles_release_device_memory(dev):
     """Handles own their device arrays and free them on destroy; builders free
     their scratch: 30 build/run/destroy cycles over every format leave the

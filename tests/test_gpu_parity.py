@@ -844,6 +844,44 @@ def test_cg_fused_ell_wide_rows(dev, k, monkeypatch):
     assert np.max(np.abs(xs["1"].astype(np.float64) - xo)) <= tol
 
 
+@pytest.mark.parametrize("fmt", ALL_FORMATS + ["sliced"])
+def test_run_captured_in_a_graph(dev, fmt):
+    """spmv_run allocates, sets and synchronises nothing, so a caller can capture
+    it in a HIP graph (here torch's).  The graph is replayed 1..4 times, with
+    eager work and host reads between replays; after each, y (accumulating
+    y += A x) equals the same number of eager runs: bit for bit for the formats
+    with a fixed summation order, else within k times the row bound."""
+    name = "c3s" if fmt == "ell_xtile" else "c2s"
+    w = W(name)
+    rp, ci, v, x, y0 = to_dev(w, dev)
+    kw = {"col_blocks": 3} if fmt == "sliced" else {}
+    h = spmv.build("csr_merge" if fmt == "sliced" else fmt, rp, ci, v, w.num_cols, **kw)
+    _, bound = ref(name)
+    y_g = y0.clone()
+    y_e = y0.clone()
+    h.run(x, y_g)                       # warm-up outside the capture, then undo it
+    y_g.copy_(y0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        h.run(x, y_g)
+    torch.cuda.synchronize()
+    assert torch.equal(y_g, y0)         # capturing ran nothing
+    for k in range(1, 5):
+        g.replay()
+        h.run(x, y_e)
+        junk = torch.ones(1 << 20, device=dev).sum()   # eager work between replays
+        torch.cuda.synchronize()
+        assert junk.item() == float(1 << 20)
+        a, b = y_g.cpu().numpy(), y_e.cpu().numpy()
+        if fmt in DETERMINISTIC:
+            assert np.array_equal(bits(a), bits(b)), (fmt, k)
+        else:
+            err = np.abs(a.astype(np.float64) - b)
+            assert np.all(err <= 2e-5 * k * bound), (fmt, k, float(np.max(err / bound)))
+    del g
+
+
 def test_build_destroy_cycles_release_device_memory(dev):
     """Handles own their device arrays and free them on destroy; builders free
     their scratch: 30 build/run/destroy cycles over every format leave the

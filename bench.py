@@ -52,6 +52,48 @@ def alg_bytes(R, C, nnz):
     return 8 * nnz + 4 * (R + 1) + 4 * C + 8 * R
 
 
+def pages_bytes(R, nnz):
+    """The pages' own traffic model: 12 B per nonzero (value, column and the x
+    element it gathers) plus 8 B per row (y).  x elements are counted once per
+    nonzero, so on cached x this is not a fraction of any peak."""
+    return 12 * nnz + 8 * R
+
+
+def input_hashes(w):
+    import hashlib
+    return {k: hashlib.sha256(getattr(w, k).tobytes()).hexdigest()[:16]
+            for k in ("row_ptrs", "col_idx", "values", "x", "y")}
+
+
+def copy_reference(torch, dev, flush_buf, steps=10):
+    """A plain 512 MiB device-to-device copy by torch's elementwise kernel
+    (dst = src + 0; 5.5 TB/s against 4.7 for the runtime's copy_ blit),
+    timed like a step: what this device's HBM delivers to a simple streaming
+    kernel, for context beside the 8 TB/s specification."""
+    n = 512 << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.add(src, 0.0, out=dst)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ts = []
+    for _ in range(steps):
+        flush_buf.zero_()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        torch.add(src, 0.0, out=dst)
+        b.record(stream)
+        b.synchronize()
+        ts.append(a.elapsed_time(b))
+    us = statistics.median(ts) * 1e3
+    del src, dst
+    gbs = 2 * n / (us * 1e-6) / 1e9
+    return {"kernel": "device copy (torch elementwise dst = src + 0), 512 MiB read + "
+                      "512 MiB written",
+            "us_median": round(us, 2), "gbs": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def time_format(spmv, torch, h, x, y, steps, warmup, flush_buf, flush=True):
     """Per-step kernel time (ms) with an untimed cache flush before each step."""
     stream = torch.cuda.current_stream()
@@ -114,10 +156,25 @@ def cpu_baseline(w, budget_s=10.0):
         n += 1
     t = t_total / n
     return {"value": round(2 * w.nnz / t / 1e9, 4), "unit": "GFLOP/s", "cores": 1,
-            "kind": "oracle",
+            "kind": "oracle", "host": host_cpu(),
             "sample": f"{n} full passes of the same {w.num_rows}-row matrix "
                       f"({w.nnz} nnz), {t * 1e3:.1f} ms each, single thread, fp64 sums",
             "openmp": openmp_baseline(w, budget_s / 2)}
+
+
+def host_cpu():
+    """Model name and logical CPU count of the host the baseline ran on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "logical_cpus": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
 def openmp_baseline(w, budget_s=5.0):
@@ -155,7 +212,9 @@ def main():
     ap.add_argument("--only-selected", action="store_true",
                     help="time only the selected format (for profiling runs)")
     ap.add_argument("--warm", action="store_true",
-                    help="also time the selected format without cache flushes")
+                    help="also time the selected format without cache flushes (off by default "
+                         "so that every launch of the selected kernel in a profiled run is a "
+                         "cold step)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--col-blocks", type=int, default=0,
                     help="x slices for every build (0 = library default)")
@@ -249,11 +308,13 @@ def main():
     ms = statistics.mean(times)
     med = statistics.median(times)
     gbs = B / (ms * 1e-3) / 1e9
-    warm_ms = None
+    warm_ms = warm_med = None
     if args.warm:
         warm_times, _ = time_format(spmv, torch, h, x, y, args.steps, args.warmup, flush_buf,
                                     flush=False)
         warm_ms = round(statistics.mean(warm_times), 5)
+        warm_med = round(statistics.median(warm_times), 5)
+    q = statistics.quantiles(times, n=10) if len(times) >= 2 else [med] * 9
 
     traffic = measured_traffic(f"{args.config}/{selected}")
     overhead_us = event_overhead_us(torch)
@@ -277,12 +338,17 @@ def main():
         "data": "synthetic (seeded), inputs resident in HBM, caches flushed before each step",
         "config": {"workload": WORKLOAD_NAMES[args.config], "format": selected,
                    "col_blocks": h.info["col_blocks"],
-                   "rows": R, "cols": C, "nnz": nnz, "parallelism": "single GPU"},
+                   "rows": R, "cols": C, "nnz": nnz, "max_row_length": int(h.info["max_len"]),
+                   "parallelism": "single GPU", "inputs_sha256": input_hashes(w)},
         "effective_gbs": round(gbs, 1),
         "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
         "ms_median": round(med, 5),
         "event_overhead_us": overhead_us,
+        "step_us": {"p10": round(q[0] * 1e3, 2), "median": round(med * 1e3, 2),
+                    "p90": round(q[8] * 1e3, 2), "mean": round(ms * 1e3, 2)},
         "warm_ms_per_step": warm_ms,
+        "warm_ms_median": warm_med,
+        "pages_model_gbs": round(pages_bytes(R, nnz) / (ms * 1e-3) / 1e9, 1),
         "wall_s_timed_loop_incl_flush": round(wall, 4),
         "build_ms": round(build_ms, 2),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
@@ -291,6 +357,9 @@ def main():
         "formats": per_format,
         "gather_reference": gather_ref,
     }
+    cref = copy_reference(torch, dev, flush_buf)
+    cref["spmv_frac_of_copy"] = round(gbs / cref["gbs"], 4)
+    result["copy_reference"] = cref
     if not args.only_selected:
         result["coo_to_csr"] = coo_section(spmv, torch, w, dev)
     if args.cg:

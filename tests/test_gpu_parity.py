@@ -735,6 +735,32 @@ def test_ell_four_rows_per_lane_ragged(dev, fmt, kw):
     assert np.array_equal(yg[empty].view(np.uint32), w.y[empty].view(np.uint32))
 
 
+def _ragged_wide():
+    """2^20 rows of 0..40 random entries: the 4-rows-per-lane ELL path at widths
+    past one 4-slot step, with ragged and empty rows."""
+    key = ("ragged_wide",)
+    if key not in _cache:
+        rng = np.random.default_rng(4048)
+        w = synth.small_random(rng, 1 << 20, 1 << 20, max_len=40, empty_frac=0.05)
+        _cache[key] = (w, oracle.spmv_csr(w.row_ptrs, w.col_idx, w.values, w.x, w.y))
+    return _cache[key]
+
+
+@pytest.mark.parametrize("fmt,kw", [("ell", {}), ("hyb", {"hyb_width": 12}),
+                                    ("hyb", {"hyb_width": 20})])
+def test_ell_four_rows_per_lane_wide(dev, fmt, kw):
+    w, (yref, bound) = _ragged_wide()
+    lens = np.diff(w.row_ptrs)
+    assert int(lens.max()) == 40 and (lens == 0).any()
+    rp, ci, v, x, y0 = to_dev(w, dev)
+    h = spmv.build(fmt, rp, ci, v, w.num_cols, **kw)
+    yg = run_once(h, x, y0)
+    n_bad, first, worst = oracle.check(yg, yref, bound)
+    assert n_bad == 0, (first, worst)
+    empty = lens == 0
+    assert np.array_equal(yg[empty].view(np.uint32), w.y[empty].view(np.uint32))
+
+
 def test_ell_unaligned_y_takes_the_row_per_lane_path(dev):
     """y at a 4-byte offset (not 16-byte aligned): the launcher falls back to
     one row per lane; results are the same."""

@@ -14,6 +14,11 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kHistLds = 4096;   // lengths below this are binned in LDS first
+// Capped grids of the check kernels (one partial record or flags word per
+// block, added or ORed on the host).
+constexpr int kRowCheckMaxBlocks = 2048;
+constexpr int kCooCheckMaxBlocks = 4096;
+constexpr int kRowsInFlight = 4;   // rows a thread of k_row_checks loads at a time
 
 __device__ inline int wave_max(int v) {
     for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
@@ -43,21 +48,41 @@ __global__ __launch_bounds__(kThreads) void k_row_checks(int32_t R, int32_t C, i
     int bad = 0, wlen = 0;
     unsigned long long sq = 0, empty = 0, dist = 0;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-    for (int64_t r = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; r < R;
-         r += stride) {
-        const int a = rp[r], b = rp[r + 1];
-        int len = b - a;
-        if (len < 0) bad = 1;
-        if (r == 0 && a != 0) bad = 1;
-        if (r == R - 1 && b != nnz) bad = 1;
-        if (len < 0) len = 0;
-        wlen = max(wlen, len);
-        sq += static_cast<unsigned long long>(len) * static_cast<unsigned long long>(len);
-        empty += (len == 0);
-        if (len > 0 && a >= 0 && a < nnz) {
-            const int64_t diag = r * static_cast<int64_t>(C) / R;
-            const int64_t d = static_cast<int64_t>(col[a]) - diag;
-            dist += static_cast<unsigned long long>(d < 0 ? -d : d);
+    // kRowsInFlight rows at a time: their pointers, then their first columns,
+    // are loaded together (every reduction here is order-free)
+    for (int64_t r0 = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; r0 < R;
+         r0 += kRowsInFlight * stride) {
+        int a[kRowsInFlight], len[kRowsInFlight], c0[kRowsInFlight];
+#pragma unroll
+        for (int u = 0; u < kRowsInFlight; ++u) {
+            const int64_t r = r0 + u * stride;
+            a[u] = 0;
+            len[u] = 0;
+            if (r < R) {
+                const int b = rp[r + 1];
+                a[u] = rp[r];
+                len[u] = b - a[u];
+                if (len[u] < 0) bad = 1;
+                if (r == 0 && a[u] != 0) bad = 1;
+                if (r == R - 1 && b != nnz) bad = 1;
+                if (len[u] < 0) len[u] = 0;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kRowsInFlight; ++u)
+            c0[u] = (len[u] > 0 && a[u] >= 0 && a[u] < nnz) ? col[a[u]] : 0;
+#pragma unroll
+        for (int u = 0; u < kRowsInFlight; ++u) {
+            const int64_t r = r0 + u * stride;
+            if (r >= R) continue;
+            wlen = max(wlen, len[u]);
+            sq += static_cast<unsigned long long>(len[u]) * static_cast<unsigned long long>(len[u]);
+            empty += (len[u] == 0);
+            if (len[u] > 0 && a[u] >= 0 && a[u] < nnz) {
+                const int64_t diag = r * static_cast<int64_t>(C) / R;
+                const int64_t d = static_cast<int64_t>(c0[u]) - diag;
+                dist += static_cast<unsigned long long>(d < 0 ? -d : d);
+            }
         }
     }
     if (R == 0 && blockIdx.x == 0 && threadIdx.x == 0) {  // rowPtrs = [0], nnz must be 0
@@ -114,12 +139,24 @@ __global__ __launch_bounds__(kThreads) void k_coo_checks(int32_t nnz, int32_t R,
                                                          int *__restrict__ partial) {
     bool bad_row = false, bad_col = false, unsorted = false;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < nnz;
-         i += stride) {
-        const int32_t r = row[i];
-        bad_row |= static_cast<uint32_t>(r) >= static_cast<uint32_t>(R);
-        if (check_cols) bad_col |= static_cast<uint32_t>(col[i]) >= static_cast<uint32_t>(C);
-        if (i + 1 < nnz) unsorted |= row[i + 1] < r;
+    constexpr int U = 4;   // entries of a thread loaded together
+    for (int64_t i0 = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i0 < nnz;
+         i0 += U * stride) {
+        int32_t r[U], rn[U], c[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = i0 + u * stride;
+            r[u] = i < nnz ? ld_nt(row + i) : 0;
+            rn[u] = i + 1 < nnz ? row[i + 1] : INT32_MAX;
+            c[u] = (check_cols && i < nnz) ? ld_nt(col + i) : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (i0 + u * stride >= nnz) continue;
+            bad_row |= static_cast<uint32_t>(r[u]) >= static_cast<uint32_t>(R);
+            if (check_cols) bad_col |= static_cast<uint32_t>(c[u]) >= static_cast<uint32_t>(C);
+            unsorted |= rn[u] < r[u];
+        }
     }
     const int f = (__ballot(bad_row) ? kFlagBadRow : 0) | (__ballot(bad_col) ? kFlagBadCol : 0) |
                   (__ballot(unsorted) ? kFlagUnsortedRows : 0);

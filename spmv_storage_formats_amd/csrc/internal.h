@@ -231,17 +231,15 @@ struct RowStatsDev {                 // device-side accumulators
     unsigned long long empty_rows;
     unsigned long long sum_first_dist;   // sum over non-empty rows of |col[rp[r]] - r*C/R|
 };
-// Row checks write one RowStatsDev per block (row_check_blocks(R) records,
-// at most kRowCheckMaxBlocks); the caller adds them up.
-constexpr int kRowCheckMaxBlocks = 512;
+// Row checks write one RowStatsDev per block (row_check_blocks(R) records);
+// the caller adds them up.
 int row_check_blocks(int32_t R);
 hipError_t launch_row_checks(int32_t R, int32_t C, int32_t nnz, const int32_t *rp,
                              const int32_t *col, RowStatsDev *partial, hipStream_t s);
 hipError_t launch_col_checks(int32_t nnz, int32_t C, const int32_t *col, RowStatsDev *st,
                              hipStream_t s);
-// COO checks write one flags word per block (coo_check_blocks(nnz) words, at
-// most kCooCheckMaxBlocks); the caller ORs them.
-constexpr int kCooCheckMaxBlocks = 1024;
+// COO checks write one flags word per block (coo_check_blocks(nnz) words);
+// the caller ORs them.
 int coo_check_blocks(int32_t nnz);
 hipError_t launch_coo_checks(int32_t nnz, int32_t R, int32_t C, const int32_t *row,
                              const int32_t *col, int check_cols, int *partial, hipStream_t s);

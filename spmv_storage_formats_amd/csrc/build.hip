@@ -24,24 +24,38 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Per-row counts with one atomic per run of equal row indices in a wave: a
-// row-sorted COO list costs one atomic per row segment, not per entry.
+// Per-row counts with one atomic per run of equal row indices in a wave step:
+// a row-sorted COO list costs one atomic per row segment, not per entry.  A
+// wave takes kCountSteps consecutive steps of 64 entries, their loads issued
+// together.
+constexpr int kCountSteps = 4;
+
 __global__ __launch_bounds__(kThreads) void k_count_rows(int32_t nnz,
                                                          const int32_t *__restrict__ row,
                                                          int32_t *__restrict__ counts) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) / kWave;
     const int lane = __lane_id();
-    const bool valid = i < nnz;
-    const int32_t r = valid ? row[i] : -1;
-    const int32_t prev = __shfl_up(r, 1);
-    const bool head = valid && (lane == 0 || prev != r);
-    const unsigned long long heads = __ballot(head);
-    const unsigned long long live = __ballot(valid);
-    if (head) {
-        const unsigned long long after = heads & ~((2ull << lane) - 1ull);
-        const int end = after ? (__ffsll(static_cast<long long>(after)) - 1)
-                              : (64 - __clzll(static_cast<long long>(live)));
-        atomicAdd(&counts[r], end - lane);
+    const int64_t base = wave * kWave * kCountSteps + lane;
+    int32_t rv[kCountSteps];
+#pragma unroll
+    for (int k = 0; k < kCountSteps; ++k) {
+        const int64_t i = base + k * kWave;
+        rv[k] = i < nnz ? ld_nt(row + i) : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < kCountSteps; ++k) {
+        const bool valid = base + k * kWave < nnz;
+        const int32_t r = rv[k];
+        const int32_t prev = __shfl_up(r, 1);
+        const bool head = valid && (lane == 0 || prev != r);
+        const unsigned long long heads = __ballot(head);
+        const unsigned long long live = __ballot(valid);
+        if (head) {
+            const unsigned long long after = heads & ~((2ull << lane) - 1ull);
+            const int end = after ? (__ffsll(static_cast<long long>(after)) - 1)
+                                  : (64 - __clzll(static_cast<long long>(live)));
+            atomicAdd(&counts[r], end - lane);
+        }
     }
 }
 
@@ -581,7 +595,9 @@ __global__ __launch_bounds__(kThreads) void k_merge_partition(int32_t R, int32_t
 
 hipError_t launch_count_rows(int32_t nnz, const int32_t *row, int32_t *counts, hipStream_t s) {
     if (nnz <= 0) return hipSuccess;
-    k_count_rows<<<grid_for(nnz, kThreads), kThreads, 0, s>>>(nnz, row, counts);
+    const int64_t waves = (static_cast<int64_t>(nnz) + kWave * kCountSteps - 1) /
+                          (kWave * kCountSteps);
+    k_count_rows<<<grid_for(waves * kWave, kThreads), kThreads, 0, s>>>(nnz, row, counts);
     return hipGetLastError();
 }
 

@@ -316,7 +316,9 @@ def main():
         warm_med = round(statistics.median(warm_times), 5)
     q = statistics.quantiles(times, n=10) if len(times) >= 2 else [med] * 9
 
-    traffic = measured_traffic(f"{args.config}/{selected}")
+    prof = profiled_entry(f"{args.config}/{selected}")
+    traffic = prof["hbm_bytes_per_launch"] if prof else None
+    prof_us = prof.get("kernel_avg_us") if prof else None
     overhead_us = event_overhead_us(torch)
     gather_ref = None
     if args.config in ("c2", "c4", "c5"):   # uniformly random columns
@@ -353,7 +355,14 @@ def main():
         "build_ms": round(build_ms, 2),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "bytes_per_launch_alg": B},
+                     "traffic": traffic, "bytes_per_launch_alg": B,
+                     # the same kernel's average duration in the committed
+                     # rocprofv3 trace of this workload (no dispatch latency)
+                     # and the fraction it gives, beside the live event time
+                     "profiled_kernel_us": prof_us,
+                     "frac_by_profiled_kernel_us": (round(B / (prof_us * 1e-6) / 1e9 /
+                                                          HBM_PEAK_GBS, 4)
+                                                    if prof_us else None)},
         "formats": per_format,
         "gather_reference": gather_ref,
     }
@@ -506,10 +515,11 @@ def event_overhead_us(torch):
     return round(statistics.median(times) * 1e3, 2)
 
 
-def measured_traffic(key):
-    """HBM bytes per launch from the committed PMC summaries (profiles/
-    *_pmc_traffic.md, a JSON block each), or None when none has an entry for
-    `key` or the kernels changed since it was taken."""
+def profiled_entry(key):
+    """The committed PMC summary entry for `key` (profiles/*_pmc_traffic.md, a
+    JSON block each): HBM bytes per launch and the kernel's average duration
+    in the matching rocprofv3 kernel trace.  None when no summary has the key
+    or the kernels changed since it was taken."""
     pdir = os.path.join(ROOT, "profiles")
     if not os.path.isdir(pdir):
         return None
@@ -525,8 +535,14 @@ def measured_traffic(key):
         table.update(json.loads(text[start + 7:end]))
     entry = table.get(key)
     if entry and entry.get("kernel_source_sha") == kernel_source_sha():
-        return entry["hbm_bytes_per_launch"]
+        return entry
     return None
+
+
+def measured_traffic(key):
+    """HBM bytes per launch from the committed PMC summaries, or None."""
+    entry = profiled_entry(key)
+    return entry["hbm_bytes_per_launch"] if entry else None
 
 
 def kernel_source_sha():

@@ -761,6 +761,26 @@ def test_ell_four_rows_per_lane_wide(dev, fmt, kw):
     assert np.array_equal(yg[empty].view(np.uint32), w.y[empty].view(np.uint32))
 
 
+@pytest.mark.parametrize("max_len,empty,run", [(2, 0.0, 4), (8, 0.0, 8), (14, 0.1, 16),
+                                               (60, 0.05, 32)])
+def test_coo_atomic_runs(dev, max_len, empty, run):
+    """The COO atomic kernel takes RUN consecutive entries per lane, RUN chosen
+    from mean + one standard deviation of the row lengths; each choice on a
+    ragged matrix whose entry count is not a multiple of RUN."""
+    rng = np.random.default_rng(31 + max_len)
+    w = synth.small_random(rng, 200_003, 150_001, max_len=max_len, empty_frac=empty)
+    lens = np.diff(w.row_ptrs).astype(np.float64)
+    spread = lens.mean() + lens.std()
+    expect = 4
+    while expect < 32 and expect <= spread:
+        expect *= 2
+    assert expect == run and w.nnz % run != 0
+    yref, bound = oracle.spmv_csr(w.row_ptrs, w.col_idx, w.values, w.x, w.y)
+    h = build("coo_atomic", w, dev)
+    rp, ci, v, x, y0 = to_dev(w, dev)
+    assert_rows(run_once(h, x, y0), yref, bound, f"coo_atomic run {run}")
+
+
 def test_ell_unaligned_y_takes_the_row_per_lane_path(dev):
     """y at a 4-byte offset (not 16-byte aligned): the launcher falls back to
     one row per lane; results are the same."""

@@ -570,9 +570,16 @@ spmv_status build_csr_impl(spmv_handle **out, spmv_format fmt, int32_t R, int32_
                                     hipMemcpyDeviceToDevice, s));
         }
         break;
-    case SPMV_CSR_SCALAR:
+    case SPMV_CSR_SCALAR: {
         SPMV_TRY(copy_csr(h.get(), R, nnz, rp, col, val, s));
+        // LDS staging pays for rows longer than 8 on average when almost no
+        // wave holds a row longer than 32 (whose wave would fall back to
+        // direct loads at the staging kernel's lower occupancy)
+        int64_t over32 = 0;
+        for (size_t k = 33; k < an.hist.size(); ++k) over32 += an.hist[k];
+        h->csr_staged = (nnz > 8 * static_cast<int64_t>(R) && 100 * over32 < R) ? 1 : 0;
         break;
+    }
     case SPMV_CSR_VECTOR:
         h->lanes = L;
         SPMV_TRY(copy_csr(h.get(), R, nnz, rp, col, val, s));

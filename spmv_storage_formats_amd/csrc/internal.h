@@ -89,6 +89,7 @@ struct spmv_handle {
     int32_t hyb_width = 0;
     int32_t lanes = 0;
     int32_t ell_width = 0;
+    int32_t csr_staged = 0;         // CSR scalar: waves stage their rows' entries in LDS
     int32_t jds_depth = spmv::kJdsDepthDefault;
     spmv_stats stats{};
     std::vector<int64_t> hist;      // host copy of the row-length histogram

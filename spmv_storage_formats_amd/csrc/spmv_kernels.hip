@@ -147,6 +147,84 @@ __global__ __launch_bounds__(kThreads) void k_coo_segmented(int32_t nnz,
 // CSR scalar: one lane per row [COO/CSR page, CSR kernel; format-choice
 // article 2.1], with the block's 257 row pointers staged in LDS (article 4.2).
 // ---------------------------------------------------------------------------
+// CSR scalar with the rows' entries staged through LDS: a wave's 64 rows
+// are one contiguous CSR segment; when it holds at most kCsrStage entries the
+// wave copies its columns and values into LDS with coalesced loads (skewed one
+// word per 32 against bank conflicts), then every lane walks its own row from
+// LDS.  Longer segments read their rows directly.  The sum of each row is
+// taken in the same order as k_csr_scalar, so the two give the same bits.
+constexpr int kCsrStage = 2048;   // entries per wave staged in LDS
+__device__ inline int csr_skew(int i) { return i + (i >> 5); }
+constexpr int kCsrStageWords = kCsrStage + kCsrStage / 32;
+
+__global__ __launch_bounds__(kThreads) void k_csr_scalar_lds(int32_t R, const int32_t *__restrict__ rp,
+                                                         const int32_t *__restrict__ col,
+                                                         const float *__restrict__ val,
+                                                         const float *__restrict__ x,
+                                                         float *__restrict__ y) {
+    __shared__ int32_t s_col[kThreads / kWave][kCsrStageWords];
+    __shared__ float s_val[kThreads / kWave][kCsrStageWords];
+    const uint32_t b = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t r = static_cast<int64_t>(b) * kThreads + threadIdx.x;
+    const int w = threadIdx.x / kWave;
+    const int lane = __lane_id();
+    const bool ok = r < R;
+    const int32_t a = ok ? ld_nt(rp + r) : 0;
+    const int32_t e = ok ? ld_nt(rp + r + 1) : 0;
+    const unsigned long long live = __ballot(ok);
+    if (!live) return;
+    const int last = 63 - __clzll(static_cast<long long>(live));
+    const int32_t s0 = __builtin_amdgcn_readfirstlane(a);
+    const int32_t s1 = __shfl(e, last);
+    const int64_t seg = static_cast<int64_t>(s1) - s0;
+    const uint32_t len = static_cast<uint32_t>(e - a);
+    float sum = 0.f;
+    if (seg <= kCsrStage) {   // wave-uniform
+        const int32_t n = static_cast<int32_t>(seg);
+        int32_t i = lane;
+        for (; i + 3 * kWave < n; i += 4 * kWave) {
+            const int32_t c0 = ld_nt(col + s0 + i), c1 = ld_nt(col + s0 + i + kWave),
+                          c2 = ld_nt(col + s0 + i + 2 * kWave), c3 = ld_nt(col + s0 + i + 3 * kWave);
+            const float v0 = ld_nt(val + s0 + i), v1 = ld_nt(val + s0 + i + kWave),
+                        v2 = ld_nt(val + s0 + i + 2 * kWave), v3 = ld_nt(val + s0 + i + 3 * kWave);
+            s_col[w][csr_skew(i)] = c0; s_col[w][csr_skew(i + kWave)] = c1;
+            s_col[w][csr_skew(i + 2 * kWave)] = c2; s_col[w][csr_skew(i + 3 * kWave)] = c3;
+            s_val[w][csr_skew(i)] = v0; s_val[w][csr_skew(i + kWave)] = v1;
+            s_val[w][csr_skew(i + 2 * kWave)] = v2; s_val[w][csr_skew(i + 3 * kWave)] = v3;
+        }
+        for (; i < n; i += kWave) {
+            s_col[w][csr_skew(i)] = ld_nt(col + s0 + i);
+            s_val[w][csr_skew(i)] = ld_nt(val + s0 + i);
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        if (!ok || len == 0) return;
+        const int32_t off = a - s0;
+        for (uint32_t t = 0; t < len; ++t) {
+            const int k = csr_skew(off + static_cast<int32_t>(t));
+            sum += s_val[w][k] * x[s_col[w][k]];
+        }
+    } else {
+        if (!ok || len == 0) return;
+        const int32_t *rc = col + a;
+        const float *rv = val + a;
+        uint32_t o = 0;
+        for (; o + 4 <= len; o += 4) {
+            const int32_t c0 = ld_nt(rc + o), c1 = ld_nt(rc + o + 1), c2 = ld_nt(rc + o + 2),
+                          c3 = ld_nt(rc + o + 3);
+            const float v0 = ld_nt(rv + o), v1 = ld_nt(rv + o + 1), v2 = ld_nt(rv + o + 2),
+                        v3 = ld_nt(rv + o + 3);
+            sum += v0 * x[c0];
+            sum += v1 * x[c1];
+            sum += v2 * x[c2];
+            sum += v3 * x[c3];
+        }
+        for (; o < len; ++o) sum += ld_nt(rv + o) * x[ld_nt(rc + o)];
+    }
+    atomic_add_f32(&y[r], sum);
+}
+
 __global__ __launch_bounds__(kThreads) void k_csr_scalar(int32_t R, const int32_t *__restrict__ rp,
                                                          const int32_t *__restrict__ col,
                                                          const float *__restrict__ val,
@@ -782,8 +860,12 @@ spmv_status launch_spmv(const spmv_handle *h, const float *x, float *y, hipStrea
         e = run_coo_segmented(nnz, a.row_idx, a.col_idx, a.values, x, y, s);
         break;
     case SPMV_CSR_SCALAR:
-        k_csr_scalar<<<blocks_of(R, kThreads), kThreads, 0, s>>>(R, a.row_ptrs, a.col_idx,
-                                                                a.values, x, y);
+        if (h->csr_staged)
+            k_csr_scalar_lds<<<blocks_of(R, kThreads), kThreads, 0, s>>>(R, a.row_ptrs, a.col_idx,
+                                                                        a.values, x, y);
+        else
+            k_csr_scalar<<<blocks_of(R, kThreads), kThreads, 0, s>>>(R, a.row_ptrs, a.col_idx,
+                                                                    a.values, x, y);
         e = hipGetLastError();
         break;
     case SPMV_CSR_VECTOR:

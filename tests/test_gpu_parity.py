@@ -781,6 +781,24 @@ def test_coo_atomic_runs(dev, max_len, empty, run):
     assert_rows(run_once(h, x, y0), yref, bound, f"coo_atomic run {run}")
 
 
+@pytest.mark.parametrize("name", ["c3s", "c4s", "c3"])
+def test_csr_scalar_staged_rows_match_direct_loads(dev, name):
+    """On matrices whose rows average more than 8 entries with under 1 % longer
+    than 32, CSR scalar stages each wave's rows through LDS; each row's sum is
+    taken in the same order as the direct-load kernel (which CSR vector with
+    one lane per row runs), so y is bit-identical."""
+    w = W(name)
+    lens = np.diff(w.row_ptrs)
+    assert lens.mean() > 8 and 100 * (lens > 32).sum() < len(lens)
+    rp, ci, v, x, y0 = to_dev(w, dev)
+    ys = spmv.build("csr_scalar", rp, ci, v, w.num_cols)
+    yd = spmv.build("csr_vector", rp, ci, v, w.num_cols, lanes=1)
+    a, b = run_once(ys, x, y0), run_once(yd, x, y0)
+    assert np.array_equal(bits(a), bits(b))
+    yref, bound = ref(name)
+    assert_rows(a, yref, bound, f"csr_scalar staged {name}")
+
+
 def test_ell_unaligned_y_takes_the_row_per_lane_path(dev):
     """y at a 4-byte offset (not 16-byte aligned): the launcher falls back to
     one row per lane; results are the same."""

@@ -82,10 +82,23 @@ __global__ __launch_bounds__(kThreads) void k_coo_atomic(int32_t nnz,
 // ---------------------------------------------------------------------------
 // COO segmented: the COO entries are sorted by row.  One wave walks 64*8
 // consecutive entries, 64 at a time (coalesced); a segmented inclusive scan
-// over the wave sums each run of equal rows, the last lane of a run adds the
+// over the wave (DPP row shifts and row broadcasts, no LDS permutes) sums each
+// run of equal rows, the last lane of a run adds the
 // run's total into y, and the wave's last run is carried into the next 64
 // entries.  Used for COO input, the HYB tail and short-row x slices.
 // ---------------------------------------------------------------------------
+
+// one step of a segmented inclusive scan by DPP (GFX9 wave scan: row shifts
+// 1/2/4/8, then row_bcast:15 and row_bcast:31); lanes without a source get a
+// key no row has
+template <int CTRL, int RMASK>
+__device__ inline void seg_step(int32_t r, float &p) {
+    const int32_t ru = __builtin_amdgcn_update_dpp(INT32_MIN, r, CTRL, RMASK, 0xF, false);
+    const float pu = __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, p), CTRL, RMASK, 0xF, false));
+    if (ru == r) p += pu;
+}
+
 constexpr int kSegIters = 8;
 
 __global__ __launch_bounds__(kThreads) void k_coo_segmented(int32_t nnz,
@@ -123,12 +136,12 @@ __global__ __launch_bounds__(kThreads) void k_coo_segmented(int32_t nnz,
         const bool valid = i < nnz;
         const int32_t r = rr[it];
         float p = pp[it];
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const int32_t ru = __shfl_up(r, off);
-            const float pu = __shfl_up(p, off);
-            if (lane >= off && ru == r) p += pu;
-        }
+        seg_step<0x111, 0xF>(r, p);
+        seg_step<0x112, 0xF>(r, p);
+        seg_step<0x114, 0xF>(r, p);
+        seg_step<0x118, 0xF>(r, p);
+        seg_step<0x142, 0xA>(r, p);
+        seg_step<0x143, 0xC>(r, p);
         // The carried run either continues into this batch (same row as lane
         // 0) or ended exactly at the previous batch's last entry: flush it.
         const int32_t r_first = __builtin_amdgcn_readfirstlane(r);

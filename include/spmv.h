@@ -104,12 +104,17 @@ typedef struct spmv_opts {
     int32_t validate;       /* nonzero: also check every column index (one pass over
                                colIdx).  Row pointers are always checked.                  */
     int32_t jds_depth;      /* JDS: depth of one tile (jagged columns per wave).  0: 128.  */
-    int32_t col_blocks;     /* x slices (column blocks), each run as its own pass over y.
-                               0: automatic for SPMV_AUTO builds (slices of at most 4 MiB
-                               of x when x exceeds the 4 MiB L2 of one XCD and the rows'
-                               columns are scattered; otherwise 1); an automatic sliced
-                               build runs every slice as merge-path CSR.  1: never split.
-                               K > 1: exactly K slices, each in the requested format.     */
+    int32_t col_blocks;     /* x slices (column blocks), each a pass over y.
+                               0: automatic for SPMV_AUTO builds when x exceeds the 4 MiB
+                               L2 of one XCD and the rows' columns are scattered
+                               (otherwise 1): up to 16 MiB of x, 2, 4 or 8 slices of at
+                               most 2 MiB; beyond, slices of 4 MiB.  An automatic sliced
+                               build runs every slice as merge-path CSR.  When every
+                               slice is merge CSR and their number divides 8, spmv_run
+                               runs them in one launch, each slice on its own XCDs;
+                               otherwise one launch per slice in order.  1: never
+                               split.  K > 1: exactly K slices, each in the requested
+                               format.                                                    */
     int32_t reserved;       /* must be 0                                                   */
     int64_t max_bytes;      /* > 0: refuse (SPMV_ERR_TOO_LARGE) a format whose device
                                arrays would exceed this many bytes.                        */

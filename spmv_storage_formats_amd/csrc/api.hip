@@ -403,15 +403,23 @@ spmv_status build_ell_xtile(spmv_handle *h, int32_t R, int32_t W, const int32_t 
 // Number of x slices.  Automatic only for SPMV_AUTO: when x is larger than
 // one XCD's L2 and the rows' columns are scattered (their first column lies
 // more than C/8 from the diagonal on average), gathers from the whole x miss
-// the L2 and go to the Infinity Cache; slices of kXSliceBytes keep every
-// pass's gathers L2-resident at the price of one extra y read+write per slice.
+// the L2 and go to the Infinity Cache; slices keep the gathers L2-resident at
+// the price of one more visit to every row per slice.  Up to 16 MiB of x: 2,
+// 4 or 8 slices of at most kXSliceXcdBytes, run side by side on their own
+// XCDs; beyond that, kXSliceBytes slices run one after another.
 int32_t choose_col_blocks(const spmv_stats &st, spmv_format fmt, const spmv_opts &o) {
     const int64_t C = st.num_cols;
     int64_t K = 1;
     if (o.col_blocks > 0) {
         K = o.col_blocks;
     } else if (fmt == SPMV_AUTO && 4 * C > kL2Bytes && st.col_spread * 8 > C && st.nnz > 0) {
-        K = (4 * C + kXSliceBytes - 1) / kXSliceBytes;
+        const int64_t xbytes = 4 * C;
+        if (xbytes <= kNumXcd * kXSliceXcdBytes) {
+            K = 2;
+            while (K < kNumXcd && xbytes > K * kXSliceXcdBytes) K *= 2;
+        } else {
+            K = (xbytes + kXSliceBytes - 1) / kXSliceBytes;
+        }
     }
     K = std::min<int64_t>(K, kMaxColBlocks);
     K = std::min<int64_t>(K, std::max<int64_t>(C, 1));

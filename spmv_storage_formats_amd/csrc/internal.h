@@ -16,9 +16,13 @@ namespace spmv {
 constexpr int kWave = 64;       // CDNA wavefront width
 constexpr int kNumXcd = 8;      // MI355X: 8 accelerator complex dies, 32 CUs each
 constexpr int kJdsDepthDefault = 128;
-// x slice for column splitting: the 4 MiB L2 of one XCD.  (Measured on
-// MI355X: 4 MiB slices beat 2 MiB ones once each slice pays its own pass over
-// the rows and y.)
+// x slices for column splitting.  Up to 8 * kXSliceXcdBytes of x, the
+// slices (2, 4 or 8, each at most kXSliceXcdBytes) run side by side in one
+// launch, each on its own XCDs, so a slice leaves room in the 4 MiB L2 for
+// the stream (skewed 2M rows: 4 slices 196 us, 2 slices 210 us).  Larger x
+// is cut into kXSliceBytes slices run one pass after another (one XCD's L2
+// each; 4 MiB beat 2 MiB once each slice pays its own pass over the rows).
+constexpr int64_t kXSliceXcdBytes = 2 << 20;
 constexpr int64_t kXSliceBytes = 4 << 20;
 constexpr int64_t kL2Bytes = 4 << 20;
 constexpr int kMaxColBlocks = 64;

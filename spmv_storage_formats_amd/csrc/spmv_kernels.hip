@@ -682,6 +682,8 @@ __global__ __launch_bounds__(kThreads) void k_sell(int32_t R, int32_t ntiles, in
     if (len > t0) atomic_add_f32(&y[ld_nt(perm + s)], sum);
 }
 
+constexpr int kMaxMergeSlices = 8;
+
 // ---------------------------------------------------------------------------
 // Merge-path CSR [format-choice article 5.2: merge-based CSR for power-law
 // graphs; "Introduction to sparse computing", parallel efficiency: split by
@@ -694,24 +696,23 @@ __global__ __launch_bounds__(kThreads) void k_sell(int32_t R, int32_t ntiles, in
 // into LDS accumulators, then the block adds each row's sum into y (a row cut
 // by the block's ends receives one piece from each block it touches).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kMergeThreads) void k_merge(int32_t R, int32_t nnz,
+__device__ inline void merge_tile(int32_t tile, int32_t R, int32_t nnz,
                                                          const int32_t *__restrict__ row_start,
                                                          const int32_t *__restrict__ rp,
                                                          const int32_t *__restrict__ col,
                                                          const float *__restrict__ val,
                                                          const float *__restrict__ x,
-                                                         float *__restrict__ y) {
+                                                         float *__restrict__ y,
+                                                         int32_t *s_end, float *s_prod,
+                                                         float *s_acc) {
     constexpr int NB = kMergeItemsPerBlock;
     constexpr int IPT = kMergeItemsPerThread;
-    __shared__ int32_t s_end[NB];
-    __shared__ float s_prod[NB];
-    __shared__ float s_acc[NB + 1];
     const int tid = threadIdx.x;
     const int64_t total = static_cast<int64_t>(R) + nnz;
-    const int64_t d0 = static_cast<int64_t>(blockIdx.x) * NB;
+    const int64_t d0 = static_cast<int64_t>(tile) * NB;
     const int64_t d1 = min(d0 + NB, total);
-    const int32_t r0 = row_start[blockIdx.x];
-    const int32_t r1 = row_start[blockIdx.x + 1];
+    const int32_t r0 = row_start[tile];
+    const int32_t r1 = row_start[tile + 1];
     const int32_t k0 = static_cast<int32_t>(d0 - r0);
     const int32_t k1 = static_cast<int32_t>(d1 - r1);
     const int32_t nr = r1 - r0;
@@ -762,6 +763,51 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(int32_t R, int32_t nnz,
         if (hi_k <= lo_k) continue;                 // no nonzero of row r in this block
         atomic_add_f32(&y[r], s_acc[li]);
     }
+}
+
+__global__ __launch_bounds__(kMergeThreads) void k_merge(int32_t R, int32_t nnz,
+                                                         const int32_t *__restrict__ row_start,
+                                                         const int32_t *__restrict__ rp,
+                                                         const int32_t *__restrict__ col,
+                                                         const float *__restrict__ val,
+                                                         const float *__restrict__ x,
+                                                         float *__restrict__ y) {
+    __shared__ int32_t s_end[kMergeItemsPerBlock];
+    __shared__ float s_prod[kMergeItemsPerBlock];
+    __shared__ float s_acc[kMergeItemsPerBlock + 1];
+    merge_tile(static_cast<int32_t>(blockIdx.x), R, nnz, row_start, rp, col, val, x, y, s_end,
+               s_prod, s_acc);
+}
+
+// All x slices of a handle in one launch, each slice pinned to its own XCDs:
+// blocks reach the 8 XCDs round-robin (block b on XCD b % 8), slice k takes
+// XCDs [k * per, (k + 1) * per) with per = 8 / n, so every XCD's L2 holds
+// one slice of x while the slices run side by side.  Every row's sum goes to
+// y by an atomic add, so slices may overlap in time.  Blocks past their
+// slice's tile count exit at once.
+struct MergeSlices {
+    int32_t n;
+    int32_t nnz[kMaxMergeSlices];
+    int32_t tiles[kMaxMergeSlices];
+    const int32_t *row_start[kMaxMergeSlices];
+    const int32_t *rp[kMaxMergeSlices];
+    const int32_t *col[kMaxMergeSlices];
+    const float *val[kMaxMergeSlices];
+};
+
+__global__ __launch_bounds__(kMergeThreads) void k_merge_slices(int32_t R, MergeSlices m,
+                                                                const float *__restrict__ x,
+                                                                float *__restrict__ y) {
+    __shared__ int32_t s_end[kMergeItemsPerBlock];
+    __shared__ float s_prod[kMergeItemsPerBlock];
+    __shared__ float s_acc[kMergeItemsPerBlock + 1];
+    const int per = 8 / m.n;
+    const int xcd = static_cast<int>(blockIdx.x % 8);
+    const int k = xcd / per;
+    const int32_t tile = static_cast<int32_t>((blockIdx.x / 8) * per + xcd % per);
+    if (tile >= m.tiles[k]) return;
+    merge_tile(tile, R, m.nnz[k], m.row_start[k], m.rp[k], m.col[k], m.val[k], x, y, s_end,
+               s_prod, s_acc);
 }
 
 unsigned blocks_of(int64_t n, int per_block) { return grid_for(n, per_block); }
@@ -853,7 +899,32 @@ spmv_status launch_spmv(const spmv_handle *h, const float *x, float *y, hipStrea
     const int32_t nnz = static_cast<int32_t>(h->stats.nnz);
     if (R == 0 || nnz == 0) return SPMV_OK;
     if (!h->parts.empty()) {
-        // x slices, one pass each over y, in stream order
+        // x slices that are all merge CSR, 2, 4 or 8 of them: one launch with
+        // each slice on its own XCDs
+        const int np = static_cast<int>(h->parts.size());
+        bool together = np >= 2 && np <= kMaxMergeSlices && 8 % np == 0;
+        for (const spmv_handle *p : h->parts)
+            together = together && p->format == SPMV_CSR_MERGE && p->num_tiles > 0;
+        if (together) {
+            MergeSlices m{};
+            m.n = np;
+            int64_t most = 0;
+            for (int k = 0; k < np; ++k) {
+                const spmv_handle *p = h->parts[k];
+                m.nnz[k] = static_cast<int32_t>(p->stats.nnz);
+                m.tiles[k] = static_cast<int32_t>(p->num_tiles);
+                m.row_start[k] = p->a.merge_row_start;
+                m.rp[k] = p->a.row_ptrs;
+                m.col[k] = p->a.col_idx;
+                m.val[k] = p->a.values;
+                most = std::max<int64_t>(most, p->num_tiles);
+            }
+            const int per = 8 / np;
+            const int64_t grid = 8 * ((most + per - 1) / per);
+            k_merge_slices<<<static_cast<unsigned>(grid), kMergeThreads, 0, s>>>(R, m, x, y);
+            return hipGetLastError() == hipSuccess ? SPMV_OK : SPMV_ERR_HIP;
+        }
+        // otherwise one pass per slice over y, in stream order
         for (const spmv_handle *p : h->parts) {
             const spmv_status st = launch_spmv(p, x, y, s);
             if (st != SPMV_OK) return st;

@@ -492,8 +492,8 @@ def test_full_size_parity(dev, name, fmt):
     h = build(fmt, w, dev, **kw)
     if fmt == "auto":
         # x fits one XCD's L2 (c1, c2) or rows are banded (c3): one slice;
-        # scattered columns over 8 / 16 MB of x: 4 MiB x slices
-        assert h.info["col_blocks"] == {"c1": 1, "c2": 1, "c3": 1, "c4": 2, "c5": 4}[name]
+        # scattered columns over 8 / 16 MB of x: 2 MiB slices, side by side
+        assert h.info["col_blocks"] == {"c1": 1, "c2": 1, "c3": 1, "c4": 4, "c5": 8}[name]
         if name in ("c1", "c2", "c3"):
             # the 3-D stencil reuses each staged x word ~4.5 times: x tiles
             assert h.format == ("ell_xtile" if name == "c3" else "ell")
@@ -557,6 +557,28 @@ def test_col_slices_parity(dev, name, fmt):
     assert not h.has_array("col_idx") and not h.has_array("ell_col")
     _, _, _, x, y0 = to_dev(w, dev)
     assert_rows(run_once(h, x, y0), *ref(name), f"{name}/{fmt} 3 slices")
+
+
+@pytest.mark.parametrize("name", ["c4s", "c5s", "c2s"])
+@pytest.mark.parametrize("k", [2, 4, 8])
+def test_merge_slices_in_one_launch(dev, name, k):
+    """Merge-CSR slices whose count divides 8 run in one launch, each slice on
+    its own XCDs, with every row's sum added to y atomically; y meets the row
+    bound, and so does a y that already holds data (accumulation, not
+    overwrite)."""
+    w = W(name)
+    h = build("csr_merge", w, dev, col_blocks=k)
+    assert h.info["col_blocks"] == k and h.format == "csr_merge"
+    _, _, _, x, y0 = to_dev(w, dev)
+    y_ref, bound = ref(name)
+    assert_rows(run_once(h, x, y0), y_ref, bound, f"{name} merge {k} slices")
+    # twice in a row: y + 2 A x
+    y = y0.clone()
+    h.run(x, y)
+    h.run(x, y)
+    torch.cuda.synchronize()
+    y2 = 2 * (y_ref - w.y.astype(np.float64)) + w.y.astype(np.float64)
+    assert_rows(y.cpu().numpy(), y2, 2 * bound, f"{name} merge {k} slices twice")
 
 
 @pytest.mark.parametrize("fmt", ["auto", "csr_merge", "coo_segmented", "csr_vector", "jds", "hyb"])

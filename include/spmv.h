@@ -108,7 +108,8 @@ typedef struct spmv_opts {
                                0: automatic for SPMV_AUTO builds when x exceeds the 4 MiB
                                L2 of one XCD and the rows' columns are scattered
                                (otherwise 1): up to 16 MiB of x, 2, 4 or 8 slices of at
-                               most 2 MiB; beyond, slices of 4 MiB.  An automatic sliced
+                               most 2 MiB, fewer while slices x rows exceeds nnz / 3;
+                               beyond 16 MiB, slices of 4 MiB.  An automatic sliced
                                build runs every slice as merge-path CSR.  When every
                                slice is merge CSR and their number divides 8, spmv_run
                                runs them in one launch, each slice on its own XCDs;

@@ -405,8 +405,9 @@ spmv_status build_ell_xtile(spmv_handle *h, int32_t R, int32_t W, const int32_t 
 // more than C/8 from the diagonal on average), gathers from the whole x miss
 // the L2 and go to the Infinity Cache; slices keep the gathers L2-resident at
 // the price of one more visit to every row per slice.  Up to 16 MiB of x: 2,
-// 4 or 8 slices of at most kXSliceXcdBytes, run side by side on their own
-// XCDs; beyond that, kXSliceBytes slices run one after another.
+// 4 or 8 slices of at most kXSliceXcdBytes (fewer while slices x rows would
+// exceed a third of the nonzeros), run side by side on their own XCDs;
+// beyond that, kXSliceBytes slices run one after another.
 int32_t choose_col_blocks(const spmv_stats &st, spmv_format fmt, const spmv_opts &o) {
     const int64_t C = st.num_cols;
     int64_t K = 1;
@@ -417,6 +418,10 @@ int32_t choose_col_blocks(const spmv_stats &st, spmv_format fmt, const spmv_opts
         if (xbytes <= kNumXcd * kXSliceXcdBytes) {
             K = 2;
             while (K < kNumXcd && xbytes > K * kXSliceXcdBytes) K *= 2;
+            // every slice visits every row: keep that work (K * R merge items)
+            // within a third of the nonzeros (power law 4M: 8 slices 445 us,
+            // 4 slices 440 us)
+            while (K > 2 && 3 * K * st.num_rows > st.nnz) K /= 2;
         } else {
             K = (xbytes + kXSliceBytes - 1) / kXSliceBytes;
         }

@@ -582,6 +582,25 @@ def test_merge_slices_in_one_launch(dev, name, k):
     assert_rows(y.cpu().numpy(), y2, 2 * bound, f"{name} merge {k} slices twice")
 
 
+def test_merge_slices_uneven_and_empty(dev):
+    """Columns crowded into the first quarter of x: with 4 slices, slice 0
+    holds most entries and the others few (uneven tile counts; blocks of the
+    short slices exit early); with 8 slices some slices are empty and are
+    dropped, and a count that no longer divides 8 runs one launch per slice.
+    Every case meets the row bound."""
+    rng = np.random.default_rng(404)
+    w = synth.small_random(rng, 100_000, 400_000, max_len=20, empty_frac=0.1)
+    # squeeze 90 % of the columns into [0, 100000)
+    squeeze = rng.random(w.nnz) < 0.9
+    w.col_idx = np.where(squeeze, w.col_idx % 100_000, w.col_idx).astype(np.int32)
+    w.col_idx[:200] = 399_999            # keep the last slice non-empty for k = 4
+    yref, bound = oracle.spmv_csr(w.row_ptrs, w.col_idx, w.values, w.x, w.y)
+    rp, ci, v, x, y0 = to_dev(w, dev)
+    for k in (2, 4, 8, 16):
+        h = spmv.build("csr_merge", rp, ci, v, w.num_cols, col_blocks=k)
+        assert_rows(run_once(h, x, y0), yref, bound, f"uneven slices k={k}")
+
+
 @pytest.mark.parametrize("fmt", ["auto", "csr_merge", "coo_segmented", "csr_vector", "jds", "hyb"])
 def test_full_size_power_law_slices(dev, fmt):
     w = W("c5")

@@ -950,6 +950,38 @@ def test_cg_fused_ell_wide_rows(dev, k, monkeypatch):
     assert np.max(np.abs(xs["1"].astype(np.float64) - xo)) <= tol
 
 
+@pytest.mark.parametrize("grid", [512, 640])
+@pytest.mark.parametrize("k", [5, 16])
+def test_cg_ell_at_and_past_the_fused_size(dev, grid, k, monkeypatch):
+    """Laplacians of 262,144 rows (the largest ELL handle that takes the fused
+    iteration: 1,024 blocks of partials) and 409,600 rows (four launches with
+    grid-stride vector kernels): x is the same with SPMV_CG_FUSED=0, bit for
+    bit, and matches the oracle's CG iterate within k * kappa * 2^-24 * max|x|."""
+    key = ("lap", grid)
+    if key not in _cache:
+        _cache[key] = synth.laplacian2d(grid)
+    w = _cache[key]
+    b32 = _cg_rhs(w)
+    b = torch.from_numpy(b32).to(dev)
+    h = build("ell", w, dev)
+    assert h.format == "ell"
+    xs = {}
+    for mode in ("1", "0"):
+        monkeypatch.setenv("SPMV_CG_FUSED", mode)
+        x = torch.zeros(w.num_rows, device=dev)
+        iters, rel = h.cg(b, x, max_iter=k, rtol=0.0)
+        assert iters == k
+        xs[mode] = (x.cpu().numpy(), rel)
+    assert np.array_equal(xs["1"][0].view(np.uint32), xs["0"][0].view(np.uint32))
+    assert xs["1"][1] == xs["0"][1]
+    xo, ko, _ = oracle.cg(w.row_ptrs, w.col_idx, w.values, b32.astype(np.float64),
+                          max_iter=k, rtol=0.0)
+    assert ko == k
+    kappa = (2 * (grid + 1) / np.pi) ** 2
+    tol = k * kappa * 2.0**-24 * np.max(np.abs(xo))
+    assert np.max(np.abs(xs["1"][0].astype(np.float64) - xo)) <= tol
+
+
 @pytest.mark.parametrize("fmt", ALL_FORMATS + ["sliced"])
 def test_run_captured_in_a_graph(dev, fmt):
     """spmv_run allocates, sets and synchronises nothing, so a caller can capture

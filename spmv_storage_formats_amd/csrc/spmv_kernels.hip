@@ -352,10 +352,13 @@ __global__ __launch_bounds__(kThreads) void k_csr_vector(int32_t R, const int32_
 // ELL: one lane per row, slot t of row r at t*R + r, so at every step the
 // lanes of a wave read one contiguous 256-byte run of values and of columns
 // [Regularized formats page, ELL section].  Slots past nnzPerRow[r] are
-// padding and contribute nothing (the padded loads are part of the stream).
-// The slots are walked U at a time with the next U slots' loads issued before
-// the current U gathers, so every wave keeps its HBM stream in flight while
-// it waits on x.
+// padding and contribute nothing.  The slots are walked U at a time with the
+// next U slots' loads issued before the current U gathers, so every wave keeps
+// its HBM stream in flight while it waits on x.  The first U slots are loaded
+// alongside nnzPerRow[r]; later slots only up to the row's length, so a lane
+// past its row issues no loads (the page's kernel likewise stops at each row's
+// own length): HYB's width-150 ELL part on the power-law matrix 1.52 -> 1.27 ms,
+// no change on full rows.
 // ---------------------------------------------------------------------------
 template <int U>
 __global__ __launch_bounds__(kThreads) void k_ell(int32_t R, int32_t W,
@@ -389,8 +392,8 @@ __global__ __launch_bounds__(kThreads) void k_ell(int32_t R, int32_t W,
         for (int u = 0; u < U; ++u) {
             const uint32_t t = t0 + U + u;
             const uint32_t slot = t * ru + r;
-            cn[u] = t < wu ? ld_nt(ell_col + slot) : 0;
-            vn[u] = t < wu ? ld_nt(ell_val + slot) : 0.f;
+            cn[u] = t < nu ? ld_nt(ell_col + slot) : 0;
+            vn[u] = t < nu ? ld_nt(ell_val + slot) : 0.f;
         }
         float xv[U];
 #pragma unroll
@@ -444,8 +447,8 @@ __global__ __launch_bounds__(kThreads) void k_ell4(int32_t R, int32_t W,
         for (int u = 0; u < U; ++u) {
             const uint32_t t = t0 + U + u;
             const uint32_t slot = t * ru + r;
-            cn[u] = t < wu ? ld_nt(reinterpret_cast<const i32x4 *>(ell_col + slot)) : i32x4(0);
-            vn[u] = t < wu ? ld_nt(reinterpret_cast<const f32x4 *>(ell_val + slot)) : f32x4(0.f);
+            cn[u] = t < nmax ? ld_nt(reinterpret_cast<const i32x4 *>(ell_col + slot)) : i32x4(0);
+            vn[u] = t < nmax ? ld_nt(reinterpret_cast<const f32x4 *>(ell_val + slot)) : f32x4(0.f);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -535,8 +538,8 @@ __global__ __launch_bounds__(kThreads) void k_ell_xtile(int32_t R, int32_t W,
         for (int u = 0; u < U; ++u) {
             const uint32_t t = t0 + U + u;
             const uint32_t slot = t * ru + r;
-            cn[u] = t < wu ? ld_nt(lidx + slot) : 0;
-            vn[u] = t < wu ? ld_nt(ell_val + slot) : 0.f;
+            cn[u] = t < static_cast<uint32_t>(n) ? ld_nt(lidx + slot) : 0;
+            vn[u] = t < static_cast<uint32_t>(n) ? ld_nt(ell_val + slot) : 0.f;
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)

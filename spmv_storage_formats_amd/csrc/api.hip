@@ -919,6 +919,9 @@ spmv_status spmv_get_info(const spmv_handle *h, spmv_info *info) {
     return SPMV_OK;
 }
 
+}  // extern "C"
+
+// Internal helper (C++ linkage): where an exportable array lives.
 namespace {
 struct ArrayRef {
     const void *dev = nullptr;
@@ -970,6 +973,8 @@ ArrayRef array_ref(const spmv_handle *h, spmv_array which) {
     return r;
 }
 }  // namespace
+
+extern "C" {
 
 spmv_status spmv_array_bytes(const spmv_handle *h, spmv_array which, size_t *bytes) {
     if (!h || !bytes) return SPMV_ERR_INVALID_ARG;

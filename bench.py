@@ -319,6 +319,7 @@ def main():
     prof = profiled_entry(f"{args.config}/{selected}")
     traffic = prof["hbm_bytes_per_launch"] if prof else None
     prof_us = prof.get("kernel_avg_us") if prof else None
+    l2_req = prof.get("l2_requests_per_launch") if prof else None
     overhead_us = event_overhead_us(torch)
     gather_ref = None
     if args.config in ("c2", "c4", "c5"):   # uniformly random columns
@@ -362,7 +363,17 @@ def main():
                      "profiled_kernel_us": prof_us,
                      "frac_by_profiled_kernel_us": (round(B / (prof_us * 1e-6) / 1e9 /
                                                           HBM_PEAK_GBS, 4)
-                                                    if prof_us else None)},
+                                                    if prof_us else None),
+                     # L2 requests per launch from the committed L2 counter
+                     # run (random columns: about one per nonzero), and the
+                     # rate they give by the live step time and by the
+                     # profiled kernel time
+                     "l2_requests_per_launch": l2_req,
+                     "l2_g_requests_per_s": (round(l2_req / (ms * 1e-3) / 1e9, 1)
+                                             if l2_req else None),
+                     "l2_g_requests_per_s_by_profiled_kernel_us": (
+                         round(l2_req / (prof_us * 1e-6) / 1e9, 1)
+                         if l2_req and prof_us else None)},
         "formats": per_format,
         "gather_reference": gather_ref,
     }

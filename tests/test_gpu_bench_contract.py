@@ -57,6 +57,11 @@ def test_roofline_fields(line):
     # are null when the kernel sources changed since they were taken
     assert r["traffic"] is None or (isinstance(r["traffic"], int) and r["traffic"] > 0)
     assert (r["profiled_kernel_us"] is None) == (r["traffic"] is None)
+    # L2 requests from the same summaries: about one per random gather
+    if r["l2_requests_per_launch"] is not None:
+        assert r["l2_requests_per_launch"] >= nnz
+        rate = r["l2_requests_per_launch"] / (line["ms_per_step"] * 1e-3) / 1e9
+        assert abs(r["l2_g_requests_per_s"] - rate) <= 0.01 * rate
 
 
 def test_cpu_baseline_fields(line):

@@ -83,7 +83,7 @@ typedef enum spmv_format {
                                into sections of 64 sorted rows, each an ELL padded to its
                                own longest row [REG, JDS variant].  Never picked by
                                SPMV_AUTO (the selector rule has no branch for it).         */
-    SPMV_ELL_XTILE = 10     /* ELL whose x gathers come from LDS [REG, ELL slot layout;
+    SPMV_ELL_XTILE = 10,    /* ELL whose x gathers come from LDS [REG, ELL slot layout;
                                INTRO x blocking; CHOICE 4.2 staging]: rows in blocks of
                                256; a block's tile is the sorted set of the distinct
                                columns of its entries, kept as runs of consecutive
@@ -94,6 +94,19 @@ typedef enum spmv_format {
                                for R >= 16384 when every block qualifies and nnz >= 2 *
                                (sum over blocks of the tile sizes): each x word staged
                                serves two gathers or more, as on banded 3-D stencils.    */
+    SPMV_COO_BLOCKED = 11   /* blocked COO [INTRO x blocking and split by nonzeros; CHOICE
+                               3.2 segmented COO]: rows in blocks of 16384, columns in S
+                               x slices (S = opts.col_blocks in {1,2,4,8}; 0: the smallest
+                               power of two that keeps a slice of x within 2 MiB, at most
+                               8); the entries of each (slice, block) are ordered by
+                               column, cut into chunks of 65536 and groups of 64, and each
+                               group is reordered by row so that runs of one row are
+                               neighbouring lanes.  Neighbouring lanes therefore gather
+                               neighbouring x words, and row partials are summed in LDS.
+                               SPMV_AUTO takes it (with the automatic S) when the columns
+                               are scattered (col_spread * 8 > C), x exceeds 4 MiB and a
+                               block holds at least one entry per 128-byte line of x on
+                               average (32 * nnz * min(R, 16384) >= R * C).            */
 } spmv_format;
 
 typedef struct spmv_opts {
@@ -105,8 +118,11 @@ typedef struct spmv_opts {
                                colIdx).  Row pointers are always checked.                  */
     int32_t jds_depth;      /* JDS: depth of one tile (jagged columns per wave).  0: 128.  */
     int32_t col_blocks;     /* x slices (column blocks), each a pass over y.
+                               SPMV_COO_BLOCKED: its slice count S (0, 1, 2, 4 or 8; other
+                               values are SPMV_ERR_INVALID_ARG), see above.  Otherwise:
                                0: automatic for SPMV_AUTO builds when x exceeds the 4 MiB
-                               L2 of one XCD and the rows' columns are scattered
+                               L2 of one XCD, the rows' columns are scattered and the
+                               matrix is too sparse for SPMV_COO_BLOCKED's rule
                                (otherwise 1): up to 16 MiB of x, 2, 4 or 8 slices of at
                                most 2 MiB, fewer while slices x rows exceeds nnz / 3;
                                beyond 16 MiB, slices of 4 MiB.  An automatic sliced
@@ -147,8 +163,14 @@ typedef struct spmv_info {
     int32_t slice_cols;    /* columns per x slice (num_cols if unsplit)   */
     spmv_stats stats;
     int64_t tail_nnz;      /* HYB: entries in the COO tail                */
-    int64_t num_tiles;     /* JDS: wave tiles; CSR merge: blocks          */
+    int64_t num_tiles;     /* JDS: wave tiles; CSR merge: blocks; blocked COO: chunks */
     int64_t device_bytes;  /* device memory owned by the handle           */
+    int64_t groups;        /* blocked COO: groups of 64 slots             */
+    int64_t wide_groups;   /* blocked COO: groups whose columns span > 65535 */
+    int32_t block_rows;    /* blocked COO: rows per block (16384)         */
+    int32_t chunk_entries; /* blocked COO: entries per chunk (65536)      */
+    int32_t hot_slots;     /* blocked COO: hot rows per block (32)        */
+    int32_t hot_min_len;   /* blocked COO: rows this long or longer may be hot (64*S+1) */
 } spmv_info;
 
 /* Arrays a handle can export (spmv_export) for bit-exact comparison. */
@@ -179,9 +201,29 @@ typedef enum spmv_array {
                               256b+255) are [run_ptr[b], run_ptr[b+1]), B = ceil(R/256) */
     SPMV_A_XT_RUNS = 20,   /* int32 [3*runs] run k: first column, offset in its block's
                               tile, length                                          */
-    SPMV_A_XT_LIDX = 21    /* int16 [R*W]   slot t of row r at t*R+r: tile position of
+    SPMV_A_XT_LIDX = 21,   /* int16 [R*W]   slot t of row r at t*R+r: tile position of
                               the entry's column, padding 0.  Values and row lengths:
                               SPMV_A_ELL_VAL, SPMV_A_ELL_NNZ.                       */
+    /* blocked COO: segment k*B + b holds the entries of x slice k and row block b
+       (B = ceil(R/16384) blocks) ordered by column, ties in CSR order; chunks are
+       its consecutive runs of 65536 entries, groups a chunk's runs of 64.          */
+    SPMV_A_BC_CHUNK_GRP = 22,  /* int32 [chunks+1] first group of chunk c          */
+    SPMV_A_BC_CHUNK_BLK = 23,  /* int32 [chunks]   row block of chunk c             */
+    SPMV_A_BC_SLICE_CHUNK = 24,/* int32 [S+1]      first chunk of x slice k         */
+    SPMV_A_BC_HOT = 25,        /* int32 [B*32]     hot rows of block b: rows with at
+                                  least hot_min_len entries, longest first, ties by
+                                  row, at most 32; -1 fills                          */
+    SPMV_A_BC_BASE = 26,       /* int32 [groups]   smallest column of group g, or
+                                  -(w+1) if its columns span more than 65535 (wide
+                                  group w)                                           */
+    SPMV_A_BC_PK = 27,         /* uint32 [groups*64] slot g*64+i: code << 16 | column
+                                  - base (0 in wide groups); code = row - 16384*b, or
+                                  16384 + h for hot row h; the group's entries
+                                  reordered by code, ties in column order; padding
+                                  0xFFFF0000                                         */
+    SPMV_A_BC_VAL = 28,        /* fp32 [groups*64]  values, padding +0.0f            */
+    SPMV_A_BC_WIDE = 29        /* int32 [wide*64]   columns of wide group w's slots,
+                                  padding 0                                          */
 } spmv_array;
 
 typedef struct spmv_handle spmv_handle;
@@ -283,8 +325,9 @@ spmv_status spmv_coo_to_csr(int32_t num_rows, int32_t num_cols, int32_t nnz,
  * spmv_build_tuned -- the empirical selector [CHOICE 4.3: a tool that times
  * the formats on the matrix itself and keeps the fastest].
  *   Tries every concrete format whose bit is set in `format_mask` (bit f for
- *   spmv_format f, 1..10; 0 = all ten), each unsplit and -- when the matrix
- *   is one that SPMV_AUTO would cut into x slices -- also sliced.  Each
+ *   spmv_format f, 1..11; 0 = all eleven), each unsplit and -- when the matrix
+ *   is one that SPMV_AUTO would cut into x slices -- also sliced (blocked COO
+ *   once, with its automatic slice count).  Each
  *   candidate that builds is run once to warm up and then `runs` times
  *   (0: 5) back to back on device scratch vectors (x = 0, y = 0: the kernels
  *   do the same work for any values), each run timed with HIP events on

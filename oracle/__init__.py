@@ -29,7 +29,8 @@ _lib = None
 
 OK, ERR_INVALID_ARG, ERR_BAD_ROWPTRS, ERR_BAD_COLIDX, ERR_BAD_ROWIDX, ERR_TOO_LARGE = range(6)
 FMT_NAMES = {1: "coo_atomic", 2: "coo_segmented", 3: "csr_scalar", 4: "csr_vector",
-             5: "ell", 6: "hyb", 7: "jds", 8: "csr_merge", 9: "sell"}
+             5: "ell", 6: "hyb", 7: "jds", 8: "csr_merge", 9: "sell", 10: "ell_xtile",
+             11: "coo_blocked"}
 RTOL = 1e-5
 
 _i32p = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
@@ -92,6 +93,9 @@ def _load():
                                                 ctypes.c_void_p, ctypes.c_void_p,
                                                 ctypes.c_void_p, ctypes.c_void_p,
                                                 ctypes.c_void_p, ctypes.POINTER(_i64)]),
+        "orc_coo_blocked": (ctypes.c_int, [_i64, _i64, _i64, _i32p, _i32p, _u32p, _i64, _i64,
+                                           _i64, _i64, _i64, _i64p] + [ctypes.c_void_p] * 8),
+        "orc_select_build": (ctypes.c_int, [_i64, _i64, _i64, _i32p, _i32p, _i64, _i64p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -277,6 +281,52 @@ def csr_to_ell_xtile(row_ptrs, col_idx, values, block_rows=256):
     return {"run_ptr": run_ptr, "runs": runs[:3 * total.value].reshape(-1, 3),
             "lidx": lidx[:R * W], "val": val[:R * W].view(np.float32), "nnz": nnz[:R],
             "width": W, "block_rows": block_rows}
+
+
+def csr_to_coo_blocked(row_ptrs, col_idx, values, num_cols, slices, block_rows, chunk_entries,
+                       hot_slots, hot_min_len):
+    """Blocked COO: the arrays chunk_grp, chunk_blk, slice_chunk, hot, base, pk (uint32),
+    val (fp32 bit copies) and wide, as oracle.c defines them."""
+    rp = _i32(row_ptrs)
+    R = rp.shape[0] - 1
+    ci = _i32(col_idx)
+    vb = _bits(values)
+    nnz = ci.shape[0]
+    lib = _load()
+    sizes = np.zeros(3, np.int64)
+    args = (R, num_cols, nnz, rp, ci, vb, slices, block_rows, chunk_entries, hot_slots,
+            hot_min_len, sizes)
+    st = lib.orc_coo_blocked(*args, None, None, None, None, None, None, None, None)
+    if st != OK:
+        raise ValueError(f"orc_coo_blocked: status {st}")
+    nch, ng, nw = (int(v) for v in sizes)
+    nblk = (R + block_rows - 1) // block_rows
+    out = {"chunk_grp": np.zeros(nch + 1, np.int32), "chunk_blk": np.zeros(max(nch, 1), np.int32),
+           "slice_chunk": np.zeros(slices + 1, np.int32),
+           "hot": np.zeros(max(nblk * hot_slots, 1), np.int32),
+           "base": np.zeros(max(ng, 1), np.int32), "pk": np.zeros(max(64 * ng, 1), np.uint32),
+           "val": np.zeros(max(64 * ng, 1), np.uint32), "wide": np.zeros(max(64 * nw, 1), np.int32)}
+    st = lib.orc_coo_blocked(*args, *(out[k].ctypes.data for k in (
+        "chunk_grp", "chunk_blk", "slice_chunk", "hot", "base", "pk", "val", "wide")))
+    assert st == OK
+    out["chunk_blk"] = out["chunk_blk"][:nch]
+    out["hot"] = out["hot"][:nblk * hot_slots]
+    out["base"] = out["base"][:ng]
+    out["pk"] = out["pk"][:64 * ng]
+    out["val"] = out["val"][:64 * ng].view(np.float32)
+    out["wide"] = out["wide"][:64 * nw]
+    return out
+
+
+def select_build(row_ptrs, col_idx, num_cols, block_rows=16384):
+    """The automatic build's (format name, K, lanes, x slices) for this matrix."""
+    rp = _i32(row_ptrs)
+    ci = _i32(col_idx)
+    out = np.zeros(4, np.int64)
+    st = _load().orc_select_build(rp.shape[0] - 1, num_cols, ci.shape[0], rp, ci, block_rows,
+                                  out)
+    assert st == OK
+    return FMT_NAMES[int(out[0])], int(out[1]), int(out[2]), int(out[3])
 
 
 def csr_to_sell(row_ptrs, col_idx, values, section=64):

@@ -691,3 +691,313 @@ int orc_csr_to_ell_xtile(int64_t R, const int32_t *row_ptrs, const int32_t *col_
         *runs_total = total;
     return status;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Blocked COO: x blocking and a split of the work by nonzeros [INTRO,      */
+/* memory- and parallel-efficiency checks], with the entries of one row     */
+/* that meet in a group summed as a run [P3 3.2, segmented COO].  This is   */
+/* an encoding, so the oracle writes out its definition:                    */
+/*   entry i of row r, column c: slice k = c / sc (sc = ceil(C/S), at least */
+/*   1), row block b = r / RT, segment s = k*B + b (B = ceil(R/RT) blocks). */
+/*   Entries in order of (s, c), ties in CSR order.  Each segment's run is  */
+/*   cut into chunks of E entries (the last shorter), chunks numbered in    */
+/*   segment order; each chunk into groups of 64 entries (the last shorter, */
+/*   padded to 64 slots).                                                   */
+/*   Hot rows of block b: its rows with at least hot_min_len entries,       */
+/*   longest first, ties by row, the first H (hot[b*H + h], -1 for unused). */
+/*   The code of an entry is r - b*RT, or RT + h when r is hot row h.       */
+/*   In a group the entries are reordered by code, ties kept in column      */
+/*   order.  base[g] = the group's smallest column (its first in column     */
+/*   order) -- unless its largest minus smallest column exceeds 65535: then */
+/*   the group is wide group w (w = wide groups before it), base[g] =       */
+/*   -(w+1), its slots' columns go to wide[w*64 + lane] and their offsets   */
+/*   are 0.  pk = code << 16 | (column - base).  Padding: pk 0xFFFF0000,    */
+/*   value bits 0, wide column 0.                                           */
+/*   chunk_grp[c] = first group of chunk c (chunks+1 entries),              */
+/*   chunk_blk[c] = its row block, slice_chunk[k] = first chunk of slice k  */
+/*   (S+1 entries).                                                         */
+/* sizes[0..2] = chunks, groups, wide groups; with chunk_grp == NULL only   */
+/* the sizes are computed.                                                  */
+/* ------------------------------------------------------------------------ */
+
+static const int64_t *g_hot_len;
+
+static int orc_cmp_hot(const void *a, const void *b)
+{
+    /* (block, length descending, row) for rows packed as block<<32 | row */
+    const int64_t x = *(const int64_t *)a, y = *(const int64_t *)b;
+    const int64_t bx = x >> 32, by = y >> 32;
+    if (bx != by)
+        return bx < by ? -1 : 1;
+    const int64_t lx = g_hot_len[x & 0xFFFFFFFF], ly = g_hot_len[y & 0xFFFFFFFF];
+    if (lx != ly)
+        return lx > ly ? -1 : 1;
+    return (x > y) - (x < y);
+}
+
+int orc_coo_blocked(int64_t R, int64_t C, int64_t nnz, const int32_t *row_ptrs,
+                    const int32_t *col_idx, const uint32_t *val_bits, int64_t S, int64_t RT,
+                    int64_t E, int64_t H, int64_t hot_min_len, int64_t *sizes,
+                    int32_t *chunk_grp, int32_t *chunk_blk, int32_t *slice_chunk, int32_t *hot,
+                    int32_t *base, uint32_t *pk, uint32_t *val, int32_t *wide)
+{
+    if (R < 0 || C < 0 || nnz < 0 || S < 1 || RT < 1 || E < 1 || H < 0 || RT + H > 0xFFFF)
+        return ORC_ERR_INVALID_ARG;
+    const int64_t sc = C > 0 ? (C + S - 1) / S : 1;
+    const int64_t B = (R + RT - 1) / RT;
+    const int64_t nseg = S * B;
+    int64_t *row = (int64_t *)malloc(sizeof(int64_t) * (size_t)(nnz > 0 ? nnz : 1));
+    int64_t *by_col = (int64_t *)malloc(sizeof(int64_t) * (size_t)(nnz > 0 ? nnz : 1));
+    int64_t *order = (int64_t *)malloc(sizeof(int64_t) * (size_t)(nnz > 0 ? nnz : 1));
+    int64_t *cnt_col = (int64_t *)calloc((size_t)(C + 1), sizeof(int64_t));
+    int64_t *seg_start = (int64_t *)calloc((size_t)(nseg + 1), sizeof(int64_t));
+    int64_t *len = (int64_t *)malloc(sizeof(int64_t) * (size_t)(R > 0 ? R : 1));
+    int64_t *code = (int64_t *)malloc(sizeof(int64_t) * (size_t)(R > 0 ? R : 1));
+    int64_t *cand = (int64_t *)malloc(sizeof(int64_t) * (size_t)(R > 0 ? R : 1));
+    if (!row || !by_col || !order || !cnt_col || !seg_start || !len || !code || !cand) {
+        free(row); free(by_col); free(order); free(cnt_col); free(seg_start);
+        free(len); free(code); free(cand);
+        return ORC_ERR_INVALID_ARG;
+    }
+    for (int64_t r = 0; r < R; ++r) {
+        len[r] = (int64_t)row_ptrs[r + 1] - row_ptrs[r];
+        for (int64_t i = row_ptrs[r]; i < row_ptrs[r + 1]; ++i)
+            row[i] = r;
+    }
+    /* stable counting sort by column, then stable counting sort by segment */
+    for (int64_t i = 0; i < nnz; ++i)
+        cnt_col[col_idx[i] + 1]++;
+    for (int64_t c = 0; c < C; ++c)
+        cnt_col[c + 1] += cnt_col[c];
+    for (int64_t i = 0; i < nnz; ++i)
+        by_col[cnt_col[col_idx[i]]++] = i;
+    for (int64_t j = 0; j < nnz; ++j) {
+        int64_t i = by_col[j];
+        int64_t s = (col_idx[i] / sc) * B + row[i] / RT;
+        seg_start[s + 1]++;
+    }
+    for (int64_t s = 0; s < nseg; ++s)
+        seg_start[s + 1] += seg_start[s];
+    {
+        int64_t *next = (int64_t *)malloc(sizeof(int64_t) * (size_t)(nseg > 0 ? nseg : 1));
+        if (!next) {
+            free(row); free(by_col); free(order); free(cnt_col); free(seg_start);
+            free(len); free(code); free(cand);
+            return ORC_ERR_INVALID_ARG;
+        }
+        for (int64_t s = 0; s < nseg; ++s)
+            next[s] = seg_start[s];
+        for (int64_t j = 0; j < nnz; ++j) {
+            int64_t i = by_col[j];
+            int64_t s = (col_idx[i] / sc) * B + row[i] / RT;
+            order[next[s]++] = i;
+        }
+        free(next);
+    }
+    /* hot rows and codes */
+    int64_t ncand = 0;
+    for (int64_t r = 0; r < R; ++r) {
+        code[r] = r % RT;
+        if (len[r] >= hot_min_len)
+            cand[ncand++] = ((r / RT) << 32) | r;
+    }
+    g_hot_len = len;
+    qsort(cand, (size_t)ncand, sizeof(int64_t), orc_cmp_hot);
+    if (hot)
+        for (int64_t i = 0; i < B * H; ++i)
+            hot[i] = -1;
+    for (int64_t i = 0, h = 0; i < ncand; ++i) {
+        int64_t b = cand[i] >> 32, r = cand[i] & 0xFFFFFFFF;
+        h = (i > 0 && (cand[i - 1] >> 32) == b) ? h + 1 : 0;
+        if (h < H) {
+            code[r] = RT + h;
+            if (hot)
+                hot[b * H + h] = (int32_t)r;
+        }
+    }
+    /* chunks and groups */
+    int64_t nch = 0, ngrp = 0, nwide = 0;
+    if (chunk_grp)
+        chunk_grp[0] = 0;
+    for (int64_t s = 0; s < nseg; ++s) {
+        if (s % B == 0 && slice_chunk)
+            slice_chunk[s / B] = (int32_t)nch;
+        for (int64_t e0 = seg_start[s]; e0 < seg_start[s + 1]; e0 += E) {
+            int64_t e1 = e0 + E < seg_start[s + 1] ? e0 + E : seg_start[s + 1];
+            for (int64_t g0 = e0; g0 < e1; g0 += 64) {
+                int64_t n = e1 - g0 < 64 ? e1 - g0 : 64;
+                int64_t lo = col_idx[order[g0]], hi = col_idx[order[g0 + n - 1]];
+                int is_wide = hi - lo > 65535;
+                if (pk) {
+                    /* lanes: the group's entries, stably reordered by code */
+                    int64_t lane_of[64];
+                    for (int64_t q = 0; q < n; ++q) {
+                        int64_t p = q;
+                        while (p > 0 && code[row[order[g0 + lane_of[p - 1]]]] >
+                                            code[row[order[g0 + q]]]) {
+                            lane_of[p] = lane_of[p - 1];
+                            --p;
+                        }
+                        lane_of[p] = q;
+                    }
+                    base[ngrp] = is_wide ? (int32_t)(-(nwide + 1)) : (int32_t)lo;
+                    for (int64_t l = 0; l < 64; ++l) {
+                        int64_t slot = ngrp * 64 + l;
+                        if (l < n) {
+                            int64_t i = order[g0 + lane_of[l]];
+                            int64_t off = is_wide ? 0 : col_idx[i] - lo;
+                            pk[slot] = (uint32_t)(code[row[i]] << 16) | (uint32_t)off;
+                            val[slot] = val_bits[i];
+                            if (is_wide)
+                                wide[nwide * 64 + l] = col_idx[i];
+                        } else {
+                            pk[slot] = 0xFFFF0000u;
+                            val[slot] = 0u;
+                            if (is_wide)
+                                wide[nwide * 64 + l] = 0;
+                        }
+                    }
+                }
+                nwide += is_wide;
+                ++ngrp;
+            }
+            if (chunk_grp) {
+                chunk_grp[nch + 1] = (int32_t)ngrp;
+                chunk_blk[nch] = (int32_t)(s % B);
+            }
+            ++nch;
+        }
+    }
+    if (slice_chunk)
+        slice_chunk[S] = (int32_t)nch;
+    sizes[0] = nch;
+    sizes[1] = ngrp;
+    sizes[2] = nwide;
+    free(row); free(by_col); free(order); free(cnt_col); free(seg_start);
+    free(len); free(code); free(cand);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* The automatic build's choice (the library's SPMV_AUTO), written out: the */
+/* selector of orc_select, then the build-time readings of x blocking       */
+/* [INTRO, memory-efficiency check: gathers from an x that does not fit the */
+/* cache; keep the x a block touches close]:                                */
+/*   spread = floor(mean over non-empty rows r of |first column of r -      */
+/*            floor(r*C/R)|); scattered = spread*8 > C; big_x = 4C > 4 MiB. */
+/*   1. scattered, big_x and 32*nnz*min(R, RT) >= R*C (a row block holds an */
+/*      entry per 128-byte line of x on average) -> blocked COO with S =    */
+/*      the smallest power of two with 4C <= S * 2 MiB, at most 8.          */
+/*   2. scattered and big_x otherwise -> x slices, each merge-based CSR:    */
+/*      4C <= 16 MiB: K = the smallest of 2, 4, 8 with 4C <= K * 2 MiB,     */
+/*      halved (not below 2) while 3*K*R > nnz; beyond: K = ceil(4C/4 MiB); */
+/*      K capped at 64 and at C; the slices number ceil(C / ceil(C/K)).     */
+/*   3. otherwise the selector's format, except that ELL becomes ELL with x */
+/*      tiles when R >= 16384, W*R <= INT32_MAX, every 256-row block's tile */
+/*      qualifies (orc_csr_to_ell_xtile's limits) and nnz >= 2 * (sum of    */
+/*      the blocks' distinct column counts).                                */
+/* out[0] format, out[1] HYB width, out[2] CSR-vector lanes, out[3] x       */
+/* slices (1 when unsplit; S for blocked COO).                              */
+/* ------------------------------------------------------------------------ */
+
+#define ORC_FMT_ELL_XTILE 10
+#define ORC_FMT_COO_BLOCKED 11
+
+int orc_select_build(int64_t R, int64_t C, int64_t nnz, const int32_t *row_ptrs,
+                     const int32_t *col_idx, int64_t RT, int64_t *out)
+{
+    int64_t W = 0, nonempty = 0, dist = 0;
+    for (int64_t r = 0; r < R; ++r) {
+        int64_t len = (int64_t)row_ptrs[r + 1] - row_ptrs[r];
+        if (len > W)
+            W = len;
+        if (len > 0) {
+            int64_t diag = r * C / R;
+            int64_t d = (int64_t)col_idx[row_ptrs[r]] - diag;
+            dist += d < 0 ? -d : d;
+            ++nonempty;
+        }
+    }
+    int64_t *hist = (int64_t *)calloc((size_t)(W + 1), sizeof(int64_t));
+    if (!hist)
+        return ORC_ERR_INVALID_ARG;
+    for (int64_t r = 0; r < R; ++r)
+        hist[row_ptrs[r + 1] - row_ptrs[r]]++;
+    int64_t sel[3];
+    orc_select(R, nnz, W, hist, 0, 0, sel);
+    free(hist);
+    out[0] = sel[0];
+    out[1] = sel[1];
+    out[2] = sel[2];
+    out[3] = 1;
+    int64_t spread = nonempty > 0 ? dist / nonempty : 0;
+    int scattered = spread * 8 > C;
+    int big_x = 4 * C > (4 << 20);
+    int64_t rows = R < RT ? R : RT;
+    if (nnz > 0 && R > 0 && scattered && big_x && 32 * nnz * rows >= R * C) {
+        int64_t S = 1;
+        while (S < 8 && 4 * C > S * (2 << 20))
+            S *= 2;
+        out[0] = ORC_FMT_COO_BLOCKED;
+        out[1] = 0;
+        out[2] = 0;
+        out[3] = S;
+        return ORC_OK;
+    }
+    if (nnz > 0 && scattered && big_x) {
+        int64_t K;
+        if (4 * C <= 8 * (2 << 20)) {
+            K = 2;
+            while (K < 8 && 4 * C > K * (2 << 20))
+                K *= 2;
+            while (K > 2 && 3 * K * R > nnz)
+                K /= 2;
+        } else {
+            K = (4 * C + (4 << 20) - 1) / (4 << 20);
+        }
+        if (K > 64)
+            K = 64;
+        if (K > C)
+            K = C;
+        if (K < 1)
+            K = 1;
+        if (K > 1) {
+            int64_t slice = (C + K - 1) / K;
+            out[0] = ORC_FMT_CSR_MERGE;
+            out[1] = 0;
+            out[2] = 0;
+            out[3] = (C + slice - 1) / slice;
+            return ORC_OK;
+        }
+    }
+    if (out[0] == ORC_FMT_ELL && R >= 64 * 256 && W * R <= ORC_INT32_MAX) {
+        int64_t runs = 0;
+        if (orc_csr_to_ell_xtile(R, row_ptrs, col_idx, NULL, W, 256, NULL, NULL, NULL, NULL,
+                                 NULL, &runs) == ORC_OK) {
+            /* distinct columns of each 256-row block */
+            int64_t tiles = 0, maxn = 0;
+            for (int64_t b = 0; b * 256 < R; ++b) {
+                int64_t r1 = (b + 1) * 256 < R ? (b + 1) * 256 : R;
+                int64_t n = (int64_t)row_ptrs[r1] - row_ptrs[b * 256];
+                if (n > maxn)
+                    maxn = n;
+            }
+            int32_t *t = (int32_t *)malloc(sizeof(int32_t) * (size_t)(maxn > 0 ? maxn : 1));
+            if (!t)
+                return ORC_ERR_INVALID_ARG;
+            for (int64_t b = 0; b * 256 < R; ++b) {
+                int64_t r1 = (b + 1) * 256 < R ? (b + 1) * 256 : R;
+                int64_t s0 = row_ptrs[b * 256], n = (int64_t)row_ptrs[r1] - s0;
+                for (int64_t i = 0; i < n; ++i)
+                    t[i] = col_idx[s0 + i];
+                qsort(t, (size_t)n, sizeof(int32_t), orc_cmp_i32);
+                for (int64_t i = 0; i < n; ++i)
+                    tiles += (i == 0 || t[i] != t[i - 1]);
+            }
+            free(t);
+            if (nnz >= 2 * tiles)
+                out[0] = ORC_FMT_ELL_XTILE;
+        }
+    }
+    return ORC_OK;
+}

@@ -30,7 +30,8 @@ _LIB_PATH = os.path.join(_PKG, "libspmv_mi355x.so")
 _HEADER = os.path.join(_ROOT, "include", "spmv.h")
 
 FORMATS = {"auto": 0, "coo_atomic": 1, "coo_segmented": 2, "csr_scalar": 3, "csr_vector": 4,
-           "ell": 5, "hyb": 6, "jds": 7, "csr_merge": 8, "sell": 9, "ell_xtile": 10}
+           "ell": 5, "hyb": 6, "jds": 7, "csr_merge": 8, "sell": 9, "ell_xtile": 10,
+           "coo_blocked": 11}
 FORMAT_NAMES = {v: k for k, v in FORMATS.items()}
 # name -> (enum value, numpy dtype)
 ARRAYS = {
@@ -41,7 +42,9 @@ ARRAYS = {
     "jds_iter_ptr": (12, np.int32), "jds_col": (13, np.int32), "jds_val": (14, np.float32),
     "len_hist": (15, np.int64), "sell_sect_ptr": (16, np.int32), "sell_col": (17, np.int32),
     "sell_val": (18, np.float32), "xt_run_ptr": (19, np.int32), "xt_runs": (20, np.int32),
-    "xt_lidx": (21, np.int16),
+    "xt_lidx": (21, np.int16), "bc_chunk_grp": (22, np.int32), "bc_chunk_blk": (23, np.int32),
+    "bc_slice_chunk": (24, np.int32), "bc_hot": (25, np.int32), "bc_base": (26, np.int32),
+    "bc_pk": (27, np.uint32), "bc_val": (28, np.float32), "bc_wide": (29, np.int32),
 }
 STATUS = {0: "SPMV_OK", 1: "SPMV_ERR_INVALID_ARG", 2: "SPMV_ERR_BAD_ROWPTRS",
           3: "SPMV_ERR_BAD_COLIDX", 4: "SPMV_ERR_BAD_ROWIDX", 5: "SPMV_ERR_TOO_LARGE",
@@ -75,7 +78,10 @@ class _Info(ctypes.Structure):
                 ("lanes_per_row", ctypes.c_int32), ("ell_width", ctypes.c_int32),
                 ("col_blocks", ctypes.c_int32), ("slice_cols", ctypes.c_int32),
                 ("stats", _Stats), ("tail_nnz", ctypes.c_int64), ("num_tiles", ctypes.c_int64),
-                ("device_bytes", ctypes.c_int64)]
+                ("device_bytes", ctypes.c_int64), ("groups", ctypes.c_int64),
+                ("wide_groups", ctypes.c_int64), ("block_rows", ctypes.c_int32),
+                ("chunk_entries", ctypes.c_int32), ("hot_slots", ctypes.c_int32),
+                ("hot_min_len", ctypes.c_int32)]
 
 
 class _TuneEntry(ctypes.Structure):
@@ -249,7 +255,10 @@ class Handle:
                      "lanes_per_row": info.lanes_per_row, "ell_width": info.ell_width,
                      "col_blocks": info.col_blocks, "slice_cols": info.slice_cols,
                      "tail_nnz": info.tail_nnz, "num_tiles": info.num_tiles,
-                     "device_bytes": info.device_bytes, **_stats_dict(info.stats)}
+                     "device_bytes": info.device_bytes, "groups": info.groups,
+                     "wide_groups": info.wide_groups, "block_rows": info.block_rows,
+                     "chunk_entries": info.chunk_entries, "hot_slots": info.hot_slots,
+                     "hot_min_len": info.hot_min_len, **_stats_dict(info.stats)}
 
     @property
     def format(self) -> str:

@@ -61,11 +61,14 @@ __global__ __launch_bounds__(kThreads) void k_row_checks(int32_t R, int32_t C, i
             if (r < R) {
                 const int b = rp[r + 1];
                 a[u] = rp[r];
-                len[u] = b - a[u];
-                if (len[u] < 0) bad = 1;
+                // compared directly (no subtraction that could wrap) and kept
+                // within [0, nnz], so a wrapped pair such as INT32_MAX then
+                // INT32_MIN is flagged like any decreasing pair
+                const bool ok = b >= a[u] && a[u] >= 0 && b <= nnz;
+                if (!ok) bad = 1;
                 if (r == 0 && a[u] != 0) bad = 1;
                 if (r == R - 1 && b != nnz) bad = 1;
-                if (len[u] < 0) len[u] = 0;
+                len[u] = ok ? b - a[u] : 0;
             }
         }
 #pragma unroll

@@ -74,7 +74,7 @@ bool valid_opts(const spmv_opts &o) {
            o.col_blocks >= 0 && o.col_blocks <= kMaxColBlocks && o.reserved == 0;
 }
 
-bool valid_format(int32_t f) { return f >= SPMV_AUTO && f <= SPMV_ELL_XTILE; }
+bool valid_format(int32_t f) { return f >= SPMV_AUTO && f <= SPMV_COO_BLOCKED; }
 
 // ---------------------------------------------------------------- analysis
 struct Analysis {
@@ -336,6 +336,12 @@ int64_t format_bytes(int32_t fmt, int64_t R, int64_t nnz, int64_t W, int64_t K,
         const int64_t slots = sell_slots_from_hist(R, hist);
         return 8 * slots + 8 * R + 4 * (R / kWave + 2) + 8 * (R / kWave + 1 + slots / kWave);
     }
+    case SPMV_COO_BLOCKED: {
+        // upper bound: every segment and chunk may end in a partial group
+        const int64_t nblk = (R + kBcRows - 1) / kBcRows;
+        const int64_t groups = nnz / kWave + nnz / kBcChunk + kNumXcd * nblk + 1;
+        return 8 * kWave * groups + 4 * groups + 4 * nblk * kBcHot + 8 * (groups + kNumXcd);
+    }
     default: return 0;
     }
 }
@@ -413,7 +419,8 @@ int32_t choose_col_blocks(const spmv_stats &st, spmv_format fmt, const spmv_opts
     int64_t K = 1;
     if (o.col_blocks > 0) {
         K = o.col_blocks;
-    } else if (fmt == SPMV_AUTO && 4 * C > kL2Bytes && st.col_spread * 8 > C && st.nnz > 0) {
+    } else if (fmt == SPMV_AUTO && 4 * C > kL2Bytes && st.col_spread * 8 > C && st.nnz > 0 &&
+               !bc_auto_rule(st)) {
         const int64_t xbytes = 4 * C;
         if (xbytes <= kNumXcd * kXSliceXcdBytes) {
             K = 2;
@@ -529,10 +536,22 @@ spmv_status build_csr_impl(spmv_handle **out, spmv_format fmt, int32_t R, int32_
                            Scratch &scratch) {
     Analysis an;
     SPMV_TRY(analyze_csr(R, C, nnz, rp, col, o.validate != 0, true, an, s, scratch));
-    const int32_t K_slices = choose_col_blocks(an.st, fmt, o);
-    if (K_slices > 1) return build_sliced(out, fmt, R, C, nnz, rp, col, val, o, K_slices, an, s,
-                                          scratch);
-    int32_t f = fmt, K = 0, L = 0;
+    // Blocked COO: asked for, or taken by SPMV_AUTO (without an explicit slice
+    // count) for scattered columns over an x larger than one L2, when a row
+    // block holds at least one entry per 128-byte line of x on average.
+    int32_t bc_slices = 0;
+    if (fmt == SPMV_COO_BLOCKED) {
+        bc_slices = o.col_blocks > 0 ? o.col_blocks : bc_auto_slices(C);
+        if (bc_slices != 1 && bc_slices != 2 && bc_slices != 4 && bc_slices != 8)
+            return SPMV_ERR_INVALID_ARG;
+    } else if (fmt == SPMV_AUTO && o.col_blocks == 0 && bc_auto_rule(an.st)) {
+        bc_slices = bc_auto_slices(C);
+    } else {
+        const int32_t K_slices = choose_col_blocks(an.st, fmt, o);
+        if (K_slices > 1)
+            return build_sliced(out, fmt, R, C, nnz, rp, col, val, o, K_slices, an, s, scratch);
+    }
+    int32_t f = bc_slices > 0 ? static_cast<int32_t>(SPMV_COO_BLOCKED) : fmt, K = 0, L = 0;
     if (f == SPMV_AUTO) {
         select_format(an.st, an.hist.data(), o, &f, &K, &L);
     } else if (f == SPMV_HYB) {
@@ -625,6 +644,9 @@ spmv_status build_csr_impl(spmv_handle **out, spmv_format fmt, int32_t R, int32_
         break;
     case SPMV_ELL_XTILE:
         SPMV_TRY(build_ell_xtile(h.get(), R, static_cast<int32_t>(W), rp, col, val, xt, s));
+        break;
+    case SPMV_COO_BLOCKED:
+        SPMV_TRY(build_coo_blocked(h.get(), R, C, nnz, rp, col, val, bc_slices, s, scratch));
         break;
     default:
         return SPMV_ERR_INVALID_ARG;
@@ -753,9 +775,9 @@ spmv_status spmv_build_tuned(spmv_handle **out, int32_t R, int32_t C, int32_t nn
     *out = nullptr;
     const spmv_opts o = resolve_opts(opts);
     if (bad_sizes(R, C, nnz) || !rp || (nnz > 0 && (!col || !val)) || !valid_opts(o) ||
-        runs < 0 || runs > 1000 || (format_mask & ~0x7FEu) != 0)
+        runs < 0 || runs > 1000 || (format_mask & ~0xFFEu) != 0)
         return SPMV_ERR_INVALID_ARG;
-    if (format_mask == 0) format_mask = 0x7FEu;   // formats 1..10
+    if (format_mask == 0) format_mask = 0xFFEu;   // formats 1..11
     if (runs == 0) runs = 5;
     hipStream_t s = static_cast<hipStream_t>(stream);
     Scratch scratch(s);
@@ -781,15 +803,17 @@ spmv_status spmv_build_tuned(spmv_handle **out, int32_t R, int32_t C, int32_t nn
     float best_us = 0.f;
     spmv_status first_err = SPMV_OK;
     spmv_status fatal = SPMV_OK;
-    for (int f = SPMV_COO_ATOMIC; f <= SPMV_ELL_XTILE && fatal == SPMV_OK; ++f) {
+    for (int f = SPMV_COO_ATOMIC; f <= SPMV_COO_BLOCKED && fatal == SPMV_OK; ++f) {
         if (!(format_mask & (1u << f))) continue;
         for (int variant = 0; variant < 2 && fatal == SPMV_OK; ++variant) {
-            const int32_t K = variant == 0 ? 1 : auto_slices;
-            if (variant == 1 && auto_slices <= 1) continue;
+            // blocked COO slices x itself: one candidate, its automatic count
+            const bool blocked = f == SPMV_COO_BLOCKED;
+            const int32_t K = blocked ? 0 : variant == 0 ? 1 : auto_slices;
+            if (variant == 1 && (blocked || auto_slices <= 1)) continue;
             if (rep.count >= SPMV_TUNE_MAX) break;
             spmv_tune_entry &ent = rep.entry[rep.count++];
             ent.format = f;
-            ent.col_blocks = K;
+            ent.col_blocks = blocked ? bc_auto_slices(C) : K;
             spmv_opts oc = o;
             oc.validate = 0;
             oc.col_blocks = K;
@@ -916,6 +940,14 @@ spmv_status spmv_get_info(const spmv_handle *h, spmv_info *info) {
     info->tail_nnz = h->tail_nnz;
     info->num_tiles = h->num_tiles;
     info->device_bytes = h->device_bytes;
+    if (h->format == SPMV_COO_BLOCKED) {
+        info->groups = h->bc_groups;
+        info->wide_groups = h->bc_wide_groups;
+        info->block_rows = kBcRows;
+        info->chunk_entries = kBcChunk;
+        info->hot_slots = kBcHot;
+        info->hot_min_len = h->bc_hot_min_len;
+    }
     return SPMV_OK;
 }
 
@@ -964,6 +996,14 @@ ArrayRef array_ref(const spmv_handle *h, spmv_array which) {
         break;
     case SPMV_A_XT_RUNS: set(a.xt_runs, 3 * h->xt_runs, 4); break;
     case SPMV_A_XT_LIDX: set(a.xt_lidx, slots, 2); break;
+    case SPMV_A_BC_CHUNK_GRP: set(a.bc_chunk_grp, h->num_tiles + 1, 4); break;
+    case SPMV_A_BC_CHUNK_BLK: set(a.bc_chunk_blk, h->num_tiles, 4); break;
+    case SPMV_A_BC_SLICE_CHUNK: set(a.bc_slice_chunk, h->col_blocks + 1, 4); break;
+    case SPMV_A_BC_HOT: set(a.bc_hot, h->bc_blocks * kBcHot, 4); break;
+    case SPMV_A_BC_BASE: set(a.bc_base, h->bc_groups, 4); break;
+    case SPMV_A_BC_PK: set(a.bc_pk, h->bc_groups * kWave, 4); break;
+    case SPMV_A_BC_VAL: set(a.bc_val, h->bc_groups * kWave, 4); break;
+    case SPMV_A_BC_WIDE: set(a.bc_wide, h->bc_wide_groups * kWave, 4); break;
     case SPMV_A_LEN_HIST:
         r.host = h->hist.data();
         r.bytes = h->hist.size() * sizeof(int64_t);
@@ -1035,6 +1075,7 @@ const char *spmv_format_name(spmv_format f) {
     case SPMV_CSR_MERGE: return "csr_merge";
     case SPMV_SELL: return "sell";
     case SPMV_ELL_XTILE: return "ell_xtile";
+    case SPMV_COO_BLOCKED: return "coo_blocked";
     default: return "unknown";
     }
 }

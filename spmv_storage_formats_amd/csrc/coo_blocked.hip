@@ -1,0 +1,487 @@
+// Blocked COO for matrices whose columns are scattered over an x larger than
+// one XCD's L2: the device builder and the SpMV kernel.
+//
+// Why: a random 4-byte x gather costs the memory pipeline one cache line per
+// lane; when the 64 lanes of a wave instruction gather from nearby columns
+// they share lines and the instruction costs far less (measured on MI355X,
+// 64M gathers from a 2 MB x: random 206 G/s, two lanes per 128-byte line
+// 338 G/s, eight per line 744 G/s).  Row-major formats give each lane its own
+// row and hence an unrelated column.  This format orders a block of rows'
+// entries by column instead, so neighbouring lanes gather neighbouring x, and
+// sums the products into per-row partials held in LDS -- x blocking and
+// splitting the work by nonzeros ("Introduction to sparse computing", the
+// memory-efficiency and parallel-efficiency checks), with row runs summed by
+// a segmented scan as in COO's segmented reduction (format-choice article,
+// 3.2).
+//
+// Layout (every array owned by the handle; R rows, C columns):
+//   - rows in blocks of kBcRows; columns in S slices of sc = ceil(C/S); the
+//     entries of (slice k, block b) form segment k*nblk + b, ordered by column
+//     (ties keep CSR order); segments are cut into chunks of kBcChunk entries
+//     and chunks into groups of 64 consecutive entries;
+//   - inside a group the entries are reordered by row code (stable), so equal
+//     rows are neighbouring lanes; the code of an entry is its row's index
+//     within the block, or kBcRows + h for the block's hot row h (the
+//     kBcHot longest rows with more than kBcHotPerSlice * S entries, longest
+//     first, ties by row): hot rows get per-wave partials, so waves never
+//     contend for them;
+//   - bc_pk[g*64 + lane] = code << 16 | (col - base[g]); pads 0xFFFF0000;
+//     bc_val the values (pads +0.0f); bc_base[g] the group's smallest column,
+//     or -(w+1) when its columns span more than 65535, in which case the
+//     columns are bc_wide[w*64 + lane] (pads 0);
+//   - bc_chunk_grp[c] first group of chunk c, bc_chunk_blk[c] its row block,
+//     bc_slice_chunk[k] the first chunk of slice k, bc_hot[b*kBcHot + h] the
+//     hot rows of block b (-1 unused).
+//
+// Kernel: one workgroup per chunk (slice k's chunks on the XCDs k*8/S ..
+// (k+1)*8/S - 1, so each XCD's L2 holds one slice of x); the block's row
+// partials live in LDS; each wave takes groups, gathers x, sums runs of equal
+// codes with a DPP segmented scan and adds each run's total to its partial:
+// hot rows by a plain add into the wave's own slot, other rows by a
+// compare-and-swap loop (an LDS float atomic add costs ~190 clocks per wave
+// instruction on gfx950, a CAS ~28, a plain read-modify-write ~16); finally
+// every non-zero partial is added to y with a global atomic (chunks of the
+// same rows run concurrently).
+#include <algorithm>
+#include <vector>
+
+#include "internal.h"
+
+namespace spmv {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBcWaves = kBcThreads / kWave;
+constexpr uint32_t kBcPadCode = 0xFFFFu;
+
+// ------------------------------------------------------------------ builder
+
+// Rows longer than min_len (hot candidates): appended in any order; the host
+// sorts them.  At most nnz / (min_len + 1) rows qualify, the list's capacity.
+__global__ __launch_bounds__(kThreads) void k_bc_hot_candidates(int32_t R,
+                                                                const int32_t *__restrict__ rp,
+                                                                int32_t min_len, int32_t cap,
+                                                                int32_t *__restrict__ count,
+                                                                int32_t *__restrict__ rows,
+                                                                int32_t *__restrict__ lens) {
+    const int64_t r = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (r >= R) return;
+    const int32_t len = rp[r + 1] - rp[r];
+    if (len <= min_len) return;
+    const int32_t i = atomicAdd(count, 1);
+    if (i < cap) {
+        rows[i] = static_cast<int32_t>(r);
+        lens[i] = len;
+    }
+}
+
+// code[r] = r mod kBcRows, then kBcRows + h for hot row h of each block.
+__global__ __launch_bounds__(kThreads) void k_bc_codes(int32_t R, int32_t *__restrict__ code) {
+    const int64_t r = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (r < R) code[r] = static_cast<int32_t>(r % kBcRows);
+}
+
+__global__ __launch_bounds__(kThreads) void k_bc_hot_codes(int64_t slots,
+                                                           const int32_t *__restrict__ hot,
+                                                           int32_t *__restrict__ code) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (i >= slots) return;
+    const int32_t r = hot[i];
+    if (r >= 0) code[r] = kBcRows + static_cast<int32_t>(i % kBcHot);
+}
+
+// Segment of each (column-sorted) entry: slice * nblk + block.
+__global__ __launch_bounds__(kThreads) void k_bc_seg_keys(int32_t nnz, const int32_t *__restrict__ row,
+                                                          const uint32_t *__restrict__ col,
+                                                          int32_t slice_cols, int32_t nblk,
+                                                          uint32_t *__restrict__ key) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (i >= nnz) return;
+    const uint32_t k = col[i] / static_cast<uint32_t>(slice_cols);
+    key[i] = k * static_cast<uint32_t>(nblk) + static_cast<uint32_t>(row[i] / kBcRows);
+}
+
+// Entry range of group g: its chunk by binary search over chunk_grp.
+__device__ inline void bc_group_range(int64_t g, int32_t nch, const int32_t *chunk_grp,
+                                      const int32_t *chunk_e0, const int32_t *chunk_e1,
+                                      int64_t &e0, int64_t &e1) {
+    const int64_t c = upper_index(chunk_grp, nch, g);   // chunk_grp[c] <= g < chunk_grp[c+1]
+    e0 = chunk_e0[c] + (g - chunk_grp[c]) * kWave;
+    e1 = min(e0 + kWave, static_cast<int64_t>(chunk_e1[c]));
+}
+
+// wide[g] = 1 when group g's columns span more than 65535 (its first entry
+// holds the smallest column, its last the largest).
+__global__ __launch_bounds__(kThreads) void k_bc_wide(int64_t G, int32_t nch,
+                                                      const int32_t *__restrict__ chunk_grp,
+                                                      const int32_t *__restrict__ chunk_e0,
+                                                      const int32_t *__restrict__ chunk_e1,
+                                                      const int32_t *__restrict__ col,
+                                                      int32_t *__restrict__ wide) {
+    const int64_t g = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (g >= G) return;
+    int64_t e0, e1;
+    bc_group_range(g, nch, chunk_grp, chunk_e0, chunk_e1, e0, e1);
+    wide[g] = (col[e1 - 1] - col[e0] > 65535) ? 1 : 0;
+}
+
+// One wave per group: codes, a 64-lane bitonic sort on (code, lane) -- the
+// lane is the entry's position in column order, so equal codes keep column
+// order -- then the packed words, values, base and wide columns.
+__global__ __launch_bounds__(kThreads) void k_bc_fill(int64_t G, int32_t nch,
+                                                      const int32_t *__restrict__ chunk_grp,
+                                                      const int32_t *__restrict__ chunk_e0,
+                                                      const int32_t *__restrict__ chunk_e1,
+                                                      const int32_t *__restrict__ row,
+                                                      const int32_t *__restrict__ col,
+                                                      const uint32_t *__restrict__ val,
+                                                      const int32_t *__restrict__ code_of_row,
+                                                      const int32_t *__restrict__ wide_idx,
+                                                      int32_t *__restrict__ base,
+                                                      uint32_t *__restrict__ pk,
+                                                      uint32_t *__restrict__ pval,
+                                                      int32_t *__restrict__ wide_col) {
+    const int64_t g = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) / kWave;
+    if (g >= G) return;   // wave-uniform
+    const int lane = __lane_id();
+    int64_t e0, e1;
+    bc_group_range(g, nch, chunk_grp, chunk_e0, chunk_e1, e0, e1);
+    const bool ok = e0 + lane < e1;
+    const int32_t c = ok ? col[e0 + lane] : 0;
+    const uint32_t v = ok ? val[e0 + lane] : 0u;
+    const uint32_t code = ok ? static_cast<uint32_t>(code_of_row[row[e0 + lane]]) : kBcPadCode;
+    uint32_t key = (code << 6) | static_cast<uint32_t>(lane);
+    for (int k = 2; k <= kWave; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const uint32_t other = static_cast<uint32_t>(__shfl_xor(static_cast<int>(key), j));
+            const bool ascending = (lane & k) == 0;
+            const bool lower = (lane & j) == 0;
+            key = (lower == ascending) ? min(key, other) : max(key, other);
+        }
+    }
+    const int src = static_cast<int>(key & 63u);
+    const uint32_t code_s = key >> 6;
+    const int32_t col_s = __shfl(c, src);
+    const uint32_t val_s = static_cast<uint32_t>(__shfl(static_cast<int>(v), src));
+    const int32_t first = __shfl(c, 0);
+    const int32_t w0 = wide_idx[g], w1 = wide_idx[g + 1];
+    const int64_t slot = g * kWave + lane;
+    if (w1 > w0) {   // wide group w0: full columns on the side
+        pk[slot] = code_s << 16;
+        wide_col[static_cast<int64_t>(w0) * kWave + lane] = code_s == kBcPadCode ? 0 : col_s;
+        if (lane == 0) base[g] = -(w0 + 1);
+    } else {
+        pk[slot] = (code_s << 16) | (code_s == kBcPadCode ? 0u : static_cast<uint32_t>(col_s - first));
+        if (lane == 0) base[g] = first;
+    }
+    pval[slot] = code_s == kBcPadCode ? 0u : val_s;
+}
+
+// -------------------------------------------------------------------- SpMV
+
+template <int CTRL, int RMASK>
+__device__ inline void bc_seg_step(int32_t r, float &p) {
+    const int32_t ru = __builtin_amdgcn_update_dpp(INT32_MIN, r, CTRL, RMASK, 0xF, false);
+    const float pu = __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, p), CTRL, RMASK, 0xF, false));
+    if (ru == r) p += pu;
+}
+
+__device__ inline void lds_cas_add(float *a, float v) {
+    uint32_t *p = reinterpret_cast<uint32_t *>(a);
+    uint32_t old = *p;
+    while (!__hip_atomic_compare_exchange_strong(p, &old, __float_as_uint(__uint_as_float(old) + v),
+                                                 __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_WORKGROUP)) {
+    }
+}
+
+template <int U>
+__global__ __launch_bounds__(kBcThreads) void k_coo_blocked(
+    int32_t R, int32_t per, const int32_t *__restrict__ slice_chunk,
+    const int32_t *__restrict__ chunk_grp, const int32_t *__restrict__ chunk_blk,
+    const int32_t *__restrict__ hot, const int32_t *__restrict__ base,
+    const uint32_t *__restrict__ pk, const float *__restrict__ val,
+    const int32_t *__restrict__ wide_col, const float *__restrict__ x, float *__restrict__ y) {
+    __shared__ float part[kBcRows];
+    __shared__ float priv[kBcWaves * kBcHot];
+    // slice k's chunks on XCDs [k*per, (k+1)*per): block b runs on XCD b % 8
+    const int xcd = static_cast<int>(blockIdx.x % kNumXcd);
+    const int k = xcd / per;
+    const int idx = static_cast<int>(blockIdx.x / kNumXcd) * per + xcd % per;
+    const int c = slice_chunk[k] + idx;
+    if (c >= slice_chunk[k + 1]) return;   // whole workgroup
+    const int b = chunk_blk[c];
+    const int64_t g0 = chunk_grp[c], g1 = chunk_grp[c + 1];
+    const int64_t r0 = static_cast<int64_t>(b) * kBcRows;
+    const int nrows = static_cast<int>(min(static_cast<int64_t>(kBcRows), R - r0));
+    // -0.0 is the additive identity bit for bit: an untouched partial is
+    // recognised and never added, so rows without entries keep their y bits
+    for (int i = threadIdx.x; i < nrows; i += kBcThreads) part[i] = -0.0f;
+    for (int i = threadIdx.x; i < kBcWaves * kBcHot; i += kBcThreads) priv[i] = -0.0f;
+    __syncthreads();
+    const int lane = __lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    float *mine = priv + wave * kBcHot;
+    for (int64_t gb = g0 + wave; gb < g1; gb += kBcWaves * U) {
+        uint32_t w[U];
+        float v[U];
+        int32_t bs[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t g = gb + u * kBcWaves;
+            const bool ok = g < g1;
+            bs[u] = ok ? base[g] : 0;
+            w[u] = ok ? ld_nt(pk + g * kWave + lane) : (kBcPadCode << 16);
+            v[u] = ok ? ld_nt(val + g * kWave + lane) : 0.f;
+        }
+        float p[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t g = gb + u * kBcWaves;
+            int32_t cx = bs[u] + static_cast<int32_t>(w[u] & 0xFFFFu);
+            if (bs[u] < 0) cx = ld_nt(wide_col + static_cast<int64_t>(-bs[u] - 1) * kWave + lane);
+            p[u] = (w[u] >> 16) != kBcPadCode && g < g1 ? v[u] * x[cx] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int32_t r = static_cast<int32_t>(w[u] >> 16);
+            float q = p[u];
+            bc_seg_step<0x111, 0xF>(r, q);   // row shr 1, 2, 4, 8
+            bc_seg_step<0x112, 0xF>(r, q);
+            bc_seg_step<0x114, 0xF>(r, q);
+            bc_seg_step<0x118, 0xF>(r, q);
+            bc_seg_step<0x142, 0xA>(r, q);   // row_bcast:15
+            bc_seg_step<0x143, 0xC>(r, q);   // row_bcast:31
+            const int32_t rn = __shfl_down(r, 1);
+            if (r != static_cast<int32_t>(kBcPadCode) && (lane == kWave - 1 || rn != r)) {
+                if (r >= kBcRows) mine[r - kBcRows] += q;   // this wave's own slot
+                else lds_cas_add(&part[r], q);
+            }
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < nrows; i += kBcThreads) {
+        const float s = part[i];
+        if (__float_as_uint(s) != 0x80000000u) unsafeAtomicAdd(&y[r0 + i], s);
+    }
+    if (threadIdx.x < kBcHot) {
+        const int32_t hr = hot[static_cast<int64_t>(b) * kBcHot + threadIdx.x];
+        if (hr >= 0) {
+            float s = -0.0f;
+            for (int wv = 0; wv < kBcWaves; ++wv) s += priv[wv * kBcHot + threadIdx.x];
+            if (__float_as_uint(s) != 0x80000000u) unsafeAtomicAdd(&y[hr], s);
+        }
+    }
+}
+
+template <typename T>
+spmv_status owned(spmv_handle *h, T **p, int64_t count) {
+    *p = nullptr;
+    const size_t bytes = static_cast<size_t>(std::max<int64_t>(count, 1)) * sizeof(T);
+    void *q = nullptr;
+    hipError_t e = hipMalloc(&q, bytes);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return from_hip(e);
+    }
+    h->owned.push_back(q);
+    h->device_bytes += static_cast<int64_t>(bytes);
+    *p = static_cast<T *>(q);
+    return SPMV_OK;
+}
+
+}  // namespace
+
+int32_t bc_auto_slices(int64_t num_cols) {
+    int32_t S = 1;
+    while (S < kNumXcd && 4 * num_cols > S * kBcSliceBytes) S *= 2;
+    return S;
+}
+
+bool bc_auto_rule(const spmv_stats &st) {
+    const int64_t R = st.num_rows, C = st.num_cols, nnz = st.nnz;
+    if (nnz <= 0 || R <= 0) return false;
+    const bool scattered = st.col_spread * 8 > C;
+    const int64_t rows = std::min<int64_t>(R, kBcRows);
+    // 32 * nnz * rows / (R * C) = expected entries of a block per 128-byte x line
+    return scattered && 4 * C > kL2Bytes && 32 * nnz * rows >= R * C;
+}
+
+spmv_status build_coo_blocked(spmv_handle *h, int32_t R, int32_t C, int32_t nnz,
+                              const int32_t *rp, const int32_t *col, const float *val, int32_t S,
+                              hipStream_t s, Scratch &scratch) {
+    const int64_t sc = std::max<int64_t>((static_cast<int64_t>(C) + S - 1) / S, 1);
+    const int64_t nblk = (static_cast<int64_t>(R) + kBcRows - 1) / kBcRows;
+    const int64_t nseg = S * nblk;
+    h->col_blocks = S;
+    h->slice_cols = static_cast<int32_t>(sc);
+    h->bc_blocks = nblk;
+    h->bc_hot_min_len = kBcHotPerSlice * S + 1;
+    if (nnz == 0 || R == 0) return SPMV_OK;
+    if (nseg > 2147483647LL) return SPMV_ERR_TOO_LARGE;
+
+    // 1. hot rows of each block: rows longer than kBcHotPerSlice * S, longest
+    //    first (ties by row), at most kBcHot per block
+    const int32_t min_len = kBcHotPerSlice * S;
+    const int32_t cap = nnz / (min_len + 1) + 1;
+    int32_t *cand = nullptr;
+    SPMV_TRY(scratch.alloc(&cand, 2 * static_cast<size_t>(cap) + 1));
+    SPMV_HIP(hipMemsetAsync(cand, 0, sizeof(int32_t), s));
+    SPMV_HIP(hipGetLastError());
+    k_bc_hot_candidates<<<grid_for(R, kThreads), kThreads, 0, s>>>(R, rp, min_len, cap, cand,
+                                                                   cand + 1, cand + 1 + cap);
+    SPMV_HIP(hipGetLastError());
+    int32_t ncand = 0;
+    SPMV_HIP(hipMemcpyAsync(&ncand, cand, sizeof(int32_t), hipMemcpyDeviceToHost, s));
+    SPMV_HIP(hipStreamSynchronize(s));
+    ncand = std::min(ncand, cap);
+    std::vector<int32_t> crow(static_cast<size_t>(ncand)), clen(static_cast<size_t>(ncand));
+    if (ncand > 0) {
+        SPMV_HIP(hipMemcpyAsync(crow.data(), cand + 1, sizeof(int32_t) * ncand,
+                                hipMemcpyDeviceToHost, s));
+        SPMV_HIP(hipMemcpyAsync(clen.data(), cand + 1 + cap, sizeof(int32_t) * ncand,
+                                hipMemcpyDeviceToHost, s));
+        SPMV_HIP(hipStreamSynchronize(s));
+    }
+    std::vector<int32_t> order(static_cast<size_t>(ncand));
+    for (int32_t i = 0; i < ncand; ++i) order[i] = i;
+    std::sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+        const int32_t ba = crow[a] / kBcRows, bb = crow[b] / kBcRows;
+        if (ba != bb) return ba < bb;
+        if (clen[a] != clen[b]) return clen[a] > clen[b];
+        return crow[a] < crow[b];
+    });
+    std::vector<int32_t> hot(static_cast<size_t>(nblk * kBcHot), -1);
+    for (int32_t i = 0, prev = -1, h_in = 0; i < ncand; ++i) {
+        const int32_t r = crow[order[i]], b = r / kBcRows;
+        h_in = (b == prev) ? h_in + 1 : 0;
+        prev = b;
+        if (h_in < kBcHot) hot[static_cast<size_t>(b) * kBcHot + h_in] = r;
+    }
+    SPMV_TRY(owned(h, &h->a.bc_hot, nblk * kBcHot));
+    SPMV_HIP(hipMemcpyAsync(h->a.bc_hot, hot.data(), sizeof(int32_t) * hot.size(),
+                            hipMemcpyHostToDevice, s));
+    int32_t *code = nullptr;
+    SPMV_TRY(scratch.alloc(&code, static_cast<size_t>(R)));
+    k_bc_codes<<<grid_for(R, kThreads), kThreads, 0, s>>>(R, code);
+    SPMV_HIP(hipGetLastError());
+    k_bc_hot_codes<<<grid_for(nblk * kBcHot, kThreads), kThreads, 0, s>>>(nblk * kBcHot,
+                                                                         h->a.bc_hot, code);
+    SPMV_HIP(hipGetLastError());
+
+    // 2. entries ordered by (segment, column), ties in CSR order: a stable
+    //    sort by column, then a stable sort by segment
+    const size_t nw = (static_cast<size_t>(nnz) + 63) & ~size_t{63};
+    uint32_t *arr = nullptr;
+    SPMV_TRY(scratch.alloc(&arr, 8 * nw));
+    int32_t *row0 = reinterpret_cast<int32_t *>(arr);
+    uint32_t *col1 = arr + nw;
+    int32_t *row1 = reinterpret_cast<int32_t *>(arr + 2 * nw);
+    uint32_t *val1 = arr + 3 * nw;
+    uint32_t *seg = arr + 4 * nw;
+    int32_t *row2 = reinterpret_cast<int32_t *>(arr + 5 * nw);
+    int32_t *col2 = reinterpret_cast<int32_t *>(arr + 6 * nw);
+    uint32_t *val2 = arr + 7 * nw;
+    SPMV_HIP(launch_expand_rows(R, nnz, rp, row0, s));
+    {
+        const uint32_t *pin[2] = {reinterpret_cast<const uint32_t *>(row0),
+                                  reinterpret_cast<const uint32_t *>(val)};
+        uint32_t *pout[2] = {reinterpret_cast<uint32_t *>(row1), val1};
+        SPMV_TRY(radix_sort(reinterpret_cast<const uint32_t *>(col), col1, 2, pin, pout, nnz,
+                            bits_for(static_cast<uint64_t>(C > 0 ? C - 1 : 0)), s, scratch));
+    }
+    k_bc_seg_keys<<<grid_for(nnz, kThreads), kThreads, 0, s>>>(
+        nnz, row1, col1, static_cast<int32_t>(sc), static_cast<int32_t>(nblk), seg);
+    SPMV_HIP(hipGetLastError());
+    const uint32_t *seg_sorted = nullptr;
+    {
+        const uint32_t *pin[3] = {reinterpret_cast<const uint32_t *>(row1), val1, col1};
+        uint32_t *pout[3] = {reinterpret_cast<uint32_t *>(row2), val2,
+                             reinterpret_cast<uint32_t *>(col2)};
+        SPMV_TRY(radix_sort(seg, nullptr, 3, pin, pout, nnz,
+                            bits_for(static_cast<uint64_t>(nseg - 1)), s, scratch, &seg_sorted));
+    }
+    int32_t *bounds = nullptr;
+    SPMV_TRY(scratch.alloc(&bounds, static_cast<size_t>(nseg) + 1));
+    SPMV_HIP(launch_slice_bounds(nnz, static_cast<int32_t>(nseg), seg_sorted, bounds, s));
+    std::vector<int32_t> hb(static_cast<size_t>(nseg) + 1);
+    SPMV_HIP(hipMemcpyAsync(hb.data(), bounds, sizeof(int32_t) * hb.size(), hipMemcpyDeviceToHost,
+                            s));
+    SPMV_HIP(hipStreamSynchronize(s));
+
+    // 3. chunks of kBcChunk entries per segment, groups of 64 per chunk
+    std::vector<int32_t> cgrp{0}, cblk, ce0, ce1, schunk(static_cast<size_t>(S) + 1, 0);
+    int64_t groups = 0;
+    for (int64_t sg = 0; sg < nseg; ++sg) {
+        if (sg % nblk == 0) schunk[static_cast<size_t>(sg / nblk)] = static_cast<int32_t>(cblk.size());
+        for (int64_t e = hb[sg]; e < hb[sg + 1]; e += kBcChunk) {
+            const int64_t e1 = std::min<int64_t>(e + kBcChunk, hb[sg + 1]);
+            groups += (e1 - e + kWave - 1) / kWave;
+            if (groups * kWave > (int64_t{1} << 40)) return SPMV_ERR_TOO_LARGE;
+            cgrp.push_back(static_cast<int32_t>(groups));
+            cblk.push_back(static_cast<int32_t>(sg % nblk));
+            ce0.push_back(static_cast<int32_t>(e));
+            ce1.push_back(static_cast<int32_t>(e1));
+        }
+    }
+    schunk[static_cast<size_t>(S)] = static_cast<int32_t>(cblk.size());
+    const int32_t nch = static_cast<int32_t>(cblk.size());
+    int32_t most = 0;
+    for (int32_t k = 0; k < S; ++k) most = std::max(most, schunk[k + 1] - schunk[k]);
+    const int32_t per = kNumXcd / S;
+    h->bc_grid = static_cast<int64_t>(kNumXcd) * ((most + per - 1) / per);
+    h->num_tiles = nch;
+    h->bc_groups = groups;
+    SPMV_TRY(owned(h, &h->a.bc_chunk_grp, nch + 1));
+    SPMV_TRY(owned(h, &h->a.bc_chunk_blk, nch));
+    SPMV_TRY(owned(h, &h->a.bc_slice_chunk, S + 1));
+    SPMV_HIP(hipMemcpyAsync(h->a.bc_chunk_grp, cgrp.data(), sizeof(int32_t) * cgrp.size(),
+                            hipMemcpyHostToDevice, s));
+    SPMV_HIP(hipMemcpyAsync(h->a.bc_chunk_blk, cblk.data(), sizeof(int32_t) * cblk.size(),
+                            hipMemcpyHostToDevice, s));
+    SPMV_HIP(hipMemcpyAsync(h->a.bc_slice_chunk, schunk.data(), sizeof(int32_t) * schunk.size(),
+                            hipMemcpyHostToDevice, s));
+    int32_t *e01 = nullptr;
+    SPMV_TRY(scratch.alloc(&e01, 2 * static_cast<size_t>(nch)));
+    SPMV_HIP(hipMemcpyAsync(e01, ce0.data(), sizeof(int32_t) * nch, hipMemcpyHostToDevice, s));
+    SPMV_HIP(hipMemcpyAsync(e01 + nch, ce1.data(), sizeof(int32_t) * nch, hipMemcpyHostToDevice,
+                            s));
+
+    // 4. wide groups (columns spanning more than 16 bits) and their numbering
+    int32_t *widx = nullptr;
+    SPMV_TRY(scratch.alloc(&widx, static_cast<size_t>(groups) + 1));
+    k_bc_wide<<<grid_for(groups, kThreads), kThreads, 0, s>>>(groups, nch, h->a.bc_chunk_grp, e01,
+                                                              e01 + nch, col2, widx);
+    SPMV_HIP(hipGetLastError());
+    SPMV_TRY(exclusive_scan(widx, widx, groups, true, s, scratch));
+    int32_t nwide = 0;
+    SPMV_HIP(hipMemcpyAsync(&nwide, widx + groups, sizeof(int32_t), hipMemcpyDeviceToHost, s));
+    SPMV_HIP(hipStreamSynchronize(s));
+    h->bc_wide_groups = nwide;
+
+    // 5. the groups themselves
+    SPMV_TRY(owned(h, &h->a.bc_base, groups));
+    SPMV_TRY(owned(h, &h->a.bc_pk, groups * kWave));
+    SPMV_TRY(owned(h, &h->a.bc_val, groups * kWave));
+    SPMV_TRY(owned(h, &h->a.bc_wide, static_cast<int64_t>(nwide) * kWave));
+    k_bc_fill<<<grid_for(groups * kWave, kThreads), kThreads, 0, s>>>(
+        groups, nch, h->a.bc_chunk_grp, e01, e01 + nch, row2, col2, val2, code, widx,
+        h->a.bc_base, h->a.bc_pk, reinterpret_cast<uint32_t *>(h->a.bc_val), h->a.bc_wide);
+    SPMV_HIP(hipGetLastError());
+    SPMV_HIP(hipStreamSynchronize(s));
+    return SPMV_OK;
+}
+
+hipError_t launch_coo_blocked(const spmv_handle *h, const float *x, float *y, hipStream_t s) {
+    if (h->bc_grid <= 0) return hipSuccess;
+    const int32_t R = static_cast<int32_t>(h->stats.num_rows);
+    const int32_t per = kNumXcd / h->col_blocks;
+    const DevArrays &a = h->a;
+    k_coo_blocked<kBcUnroll><<<static_cast<unsigned>(h->bc_grid), kBcThreads, 0, s>>>(
+        R, per, a.bc_slice_chunk, a.bc_chunk_grp, a.bc_chunk_blk, a.bc_hot, a.bc_base, a.bc_pk,
+        a.bc_val, a.bc_wide, x, y);
+    return hipGetLastError();
+}
+
+}  // namespace spmv

@@ -738,13 +738,19 @@ __device__ inline void merge_tile(int32_t tile, int32_t R, int32_t nnz,
         const int32_t mid = (lo + hi) >> 1;
         if (s_end[mid] + mid < dt) lo = mid + 1; else hi = mid;
     }
+    // A row whose end item lies in this thread's range has exactly one such
+    // thread: it stores its part of the row with a plain LDS write.  What a
+    // thread holds of the row still open at the end of its range (its tail)
+    // belongs to a row ending in a later thread; the tails are combined below.
+    // (LDS float atomics cost ~190 clocks per wave instruction on gfx950,
+    // plain LDS writes a few clocks.)
     int32_t i = lo, k = dt - lo;
     const int32_t dend = min(dt + IPT, items);
     float sum = 0.f;
     bool any = false;
     for (int32_t d = dt; d < dend; ++d) {
         if (i < nr && k >= s_end[i]) {   // row i ends here
-            if (any) lds_add_f32(&s_acc[i], sum);
+            if (any) s_acc[i] = sum;
             sum = 0.f;
             any = false;
             ++i;
@@ -754,7 +760,30 @@ __device__ inline void merge_tile(int32_t tile, int32_t R, int32_t nnz,
             any = true;
         }
     }
-    if (any) lds_add_f32(&s_acc[i], sum);
+    __syncthreads();
+    // Tails, in thread order, have non-decreasing rows: a segmented scan over
+    // the wave sums each run of equal rows, and the run's last lane adds it to
+    // the row's LDS accumulator.  A run that starts at lane 0 or reaches lane
+    // 63 may share its row with a neighbouring wave's run: those two add
+    // atomically; every other run is the only writer of its row after the
+    // barrier above.
+    {
+        const int lane = __lane_id();
+        const int32_t tr = any ? i : INT32_MAX;
+        float p = any ? sum : 0.f;
+        seg_step<0x111, 0xF>(tr, p);
+        seg_step<0x112, 0xF>(tr, p);
+        seg_step<0x114, 0xF>(tr, p);
+        seg_step<0x118, 0xF>(tr, p);
+        seg_step<0x142, 0xA>(tr, p);
+        seg_step<0x143, 0xC>(tr, p);
+        const int32_t tn = __shfl_down(tr, 1);
+        const int32_t t_first = __builtin_amdgcn_readfirstlane(tr);
+        if (tr != INT32_MAX && (lane == kWave - 1 || tn != tr)) {
+            if (lane == kWave - 1 || tr == t_first) lds_add_f32(&s_acc[tr], p);
+            else s_acc[tr] += p;
+        }
+    }
     __syncthreads();
 
     for (int li = tid; li <= nr; li += kMergeThreads) {
@@ -1010,6 +1039,9 @@ spmv_status launch_spmv(const spmv_handle *h, const float *x, float *y, hipStrea
                 a.sell_ptr, a.jds_perm, a.sell_col, a.sell_val, x, y);
             e = hipGetLastError();
         }
+        break;
+    case SPMV_COO_BLOCKED:
+        e = launch_coo_blocked(h, x, y, s);
         break;
     case SPMV_CSR_MERGE:
         k_merge<<<static_cast<unsigned>(h->num_tiles), kMergeThreads, 0, s>>>(

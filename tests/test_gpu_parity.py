@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 import spmv_storage_formats_amd as spmv  # noqa: E402
 
 ALL_FORMATS = ["coo_atomic", "coo_segmented", "csr_scalar", "csr_vector", "ell", "hyb", "jds",
-               "csr_merge", "sell", "ell_xtile"]
+               "csr_merge", "sell", "ell_xtile", "coo_blocked"]
 # formats whose rows are each summed by one lane group with a plain y update
 DETERMINISTIC = ["csr_scalar", "csr_vector", "ell", "ell_xtile"]
 
@@ -175,6 +175,8 @@ def check_builder(h, w, K=None):
         assert np.array_equal(h.array("xt_lidx"), o["lidx"])
         assert np.array_equal(bits(h.array("ell_val")), bits(o["val"]))
         assert np.array_equal(h.array("ell_nnz"), o["nnz"])
+    elif fmt == "coo_blocked":
+        check_blocked(h, w)
     elif fmt == "sell":
         o = oracle.csr_to_sell(w.row_ptrs, w.col_idx, w.values, 64)
         assert np.array_equal(h.array("jds_perm"), o["perm"])
@@ -186,6 +188,21 @@ def check_builder(h, w, K=None):
     assert np.array_equal(h.array("len_hist"), st["hist"])
     assert (h.info["max_len"], h.info["sum_len_sq"], h.info["empty_rows"]) == \
         (st["W"], st["sum_len_sq"], st["empty_rows"])
+
+
+def check_blocked(h, w):
+    """Every blocked-COO array equals the oracle's, built with the handle's own
+    slice count, block height, chunk size and hot-row rule (spmv_info)."""
+    i = h.info
+    o = oracle.csr_to_coo_blocked(w.row_ptrs, w.col_idx, w.values, w.num_cols, i["col_blocks"],
+                                  i["block_rows"], i["chunk_entries"], i["hot_slots"],
+                                  i["hot_min_len"])
+    assert i["slice_cols"] == max(-(-w.num_cols // i["col_blocks"]), 1)
+    assert i["num_tiles"] == o["chunk_blk"].size and i["groups"] == o["base"].size
+    assert i["wide_groups"] * 64 == o["wide"].size
+    for name in ("chunk_grp", "chunk_blk", "slice_chunk", "hot", "base", "pk", "wide"):
+        assert np.array_equal(h.array("bc_" + name), o[name]), name
+    assert np.array_equal(bits(h.array("bc_val")), bits(o["val"]))
 
 
 REDUCED = ["c1s", "c2s", "c3s", "c4s", "c5s"]
@@ -361,10 +378,16 @@ def _bad_inputs():
     b = ci.copy(); b[3] = 4; cases.append(("col high", rp.copy(), b, 4))
     b = ci.copy(); b[0] = -1; cases.append(("col negative", rp.copy(), b, 4))
     cases.append(("too few columns", rp.copy(), ci.copy(), 3))
+    # pointers whose difference wraps in int32: INT32_MAX then INT32_MIN
+    b = rp.copy(); b[1] = np.iinfo(np.int32).max; b[2] = np.iinfo(np.int32).min
+    cases.append(("wrapping pair", b, ci.copy(), 4))
+    # non-decreasing until a pointer far past nnz, then back down to nnz
+    b = rp.copy(); b[2] = np.iinfo(np.int32).max; b[3] = np.iinfo(np.int32).max
+    cases.append(("pointer past nnz", b, ci.copy(), 4))
     return cases
 
 
-@pytest.mark.parametrize("case", range(7))
+@pytest.mark.parametrize("case", range(9))
 def test_validation_codes_match_oracle(dev, case):
     name, rp, ci, C = _bad_inputs()[case]
     expect = oracle.validate_csr(4, C, rp, ci)
@@ -491,13 +514,17 @@ def test_full_size_parity(dev, name, fmt):
     kw = {"hyb_width": 20} if (fmt == "hyb" and name == "c4") else {}
     h = build(fmt, w, dev, **kw)
     if fmt == "auto":
-        # x fits one XCD's L2 (c1, c2) or rows are banded (c3): one slice;
-        # scattered columns over 8 / 16 MB of x: slices of 2 MiB (c4) or, with
-        # slices x rows capped at a third of nnz, 4 MiB (c5), side by side
-        assert h.info["col_blocks"] == {"c1": 1, "c2": 1, "c3": 1, "c4": 4, "c5": 4}[name]
-        if name in ("c1", "c2", "c3"):
-            # the 3-D stencil reuses each staged x word ~4.5 times: x tiles
-            assert h.format == ("ell_xtile" if name == "c3" else "ell")
+        # the automatic build's whole decision (selector, x tiles, blocked COO
+        # and its slice count) equals the oracle's written-out rule
+        f, K, L, S = oracle.select_build(w.row_ptrs, w.col_idx, w.num_cols)
+        assert (h.format, h.info["hyb_width"], h.info["lanes_per_row"],
+                h.info["col_blocks"]) == (f, K, L, S)
+        # the 2-D stencil and the random 5-per-row matrix: ELL; the 3-D
+        # stencil: x tiles; skewed and power law (x of 8 / 16 MB): blocked COO
+        assert f == {"c1": "ell", "c2": "ell", "c3": "ell_xtile", "c4": "coo_blocked",
+                     "c5": "coo_blocked"}[name]
+    elif fmt == "coo_blocked":
+        assert h.info["col_blocks"] == {"c1": 1, "c2": 2, "c3": 4, "c4": 4, "c5": 8}[name]
     else:
         assert h.info["col_blocks"] == 1
     _, _, _, x, y0 = to_dev(w, dev)
@@ -508,7 +535,9 @@ def test_full_size_parity(dev, name, fmt):
 @pytest.mark.parametrize("name,fmt", [("c1", "ell"), ("c2", "ell"), ("c3", "ell"),
                                       ("c1", "ell_xtile"), ("c3", "ell_xtile"),
                                       ("c4", "hyb"), ("c4", "jds"), ("c5", "jds"),
-                                      ("c5", "coo_segmented"), ("c4", "sell"), ("c5", "sell")])
+                                      ("c5", "coo_segmented"), ("c4", "sell"), ("c5", "sell"),
+                                      ("c2", "coo_blocked"), ("c4", "coo_blocked"),
+                                      ("c5", "coo_blocked")])
 def test_full_size_builders_bitexact(dev, name, fmt):
     w = W(name)
     print(f"[case] full builder {name} {fmt}", flush=True)
@@ -523,6 +552,86 @@ def test_full_size_selector_unsliced(dev, name, expect):
     width the format-choice article found best) and merge CSR for power law."""
     h = build("auto", W(name), dev, col_blocks=1)
     assert (h.format, h.info["hyb_width"]) == expect and h.info["col_blocks"] == 1
+
+
+# ------------------------------------------------------------- blocked COO
+
+@pytest.mark.parametrize("name", ["c2s", "c4s", "c5s", "c1s"])
+@pytest.mark.parametrize("S", [1, 2, 4, 8])
+def test_blocked_slice_counts(dev, name, S):
+    """Blocked COO with 1, 2, 4 and 8 x slices (slice k's chunks on their own
+    XCDs): every array bit-exact against the oracle, y within the row bound,
+    and twice in a row y + 2 A x (partials accumulate into y, never overwrite)."""
+    w = W(name)
+    print(f"[case] blocked {name} S={S}", flush=True)
+    h = build("coo_blocked", w, dev, col_blocks=S)
+    assert h.format == "coo_blocked" and h.info["col_blocks"] == S
+    check_builder(h, w)
+    _, _, _, x, y0 = to_dev(w, dev)
+    y_ref, bound = ref(name)
+    assert_rows(run_once(h, x, y0), y_ref, bound, f"{name} blocked S={S}")
+    y = y0.clone()
+    h.run(x, y)
+    h.run(x, y)
+    torch.cuda.synchronize()
+    y2 = 2 * (y_ref - w.y.astype(np.float64)) + w.y.astype(np.float64)
+    assert_rows(y.cpu().numpy(), y2, 2 * bound, f"{name} blocked S={S} twice")
+
+
+def _wide_mix():
+    """2,000 rows over 10M columns: half the rows keep their columns in a
+    narrow band (groups spanning < 2^16 columns), the rest scatter them over
+    all of x (groups spanning more: wide groups with full columns)."""
+    rng = np.random.default_rng(77)
+    R, C = 2000, 10_000_000
+    lens = rng.integers(1, 9, size=R)
+    cols = []
+    for r, l in enumerate(lens):
+        lo, hi = (5_000_000, 5_030_000) if r % 2 else (0, C)
+        cols.append(np.sort(rng.choice(np.arange(lo, hi), l, replace=False)))
+    ci = np.concatenate(cols).astype(np.int32)
+    rp = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return synth.Workload("wide_mix", R, C, rp, ci, rng.uniform(-1, 1, ci.size).astype(np.float32),
+                          rng.uniform(-1, 1, C).astype(np.float32),
+                          rng.uniform(-1, 1, R).astype(np.float32))
+
+
+@pytest.mark.parametrize("S", [1, 8])
+def test_blocked_wide_groups(dev, S):
+    w = _wide_mix()
+    h = build("coo_blocked", w, dev, col_blocks=S)
+    assert h.info["wide_groups"] > 0 and h.info["wide_groups"] < h.info["groups"]
+    check_builder(h, w)
+    y_ref, bound = oracle.spmv_csr(w.row_ptrs, w.col_idx, w.values, w.x, w.y)
+    _, _, _, x, y0 = to_dev(w, dev)
+    assert_rows(run_once(h, x, y0), y_ref, bound, f"wide groups S={S}")
+
+
+def test_blocked_hot_rows(dev):
+    """Two row blocks over 3M columns; block 0 has 40 rows longer than the hot
+    threshold (more than its 32 hot slots; several of equal length, so the
+    row-number tie rule decides), block 1 a few, one of them 30,000 long: hot
+    rows get per-wave partials, the rest compare-and-swap.  Bit-exact arrays,
+    y within the bound."""
+    rng = np.random.default_rng(91)
+    R, C = 20000, 3_000_000
+    lens = rng.integers(0, 8, size=R)
+    long0 = rng.choice(16384, 40, replace=False)
+    lens[long0] = rng.choice([100, 150, 150, 200, 300], size=40)
+    lens[[17000, 18000, 19999]] = [30000, 70, 500]
+    cols = [np.sort(rng.choice(C, l, replace=False)) if l else np.zeros(0, np.int64) for l in lens]
+    ci = np.concatenate(cols).astype(np.int32)
+    rp = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    w = synth.Workload("hot_rows", R, C, rp, ci, rng.uniform(-1, 1, ci.size).astype(np.float32),
+                       rng.uniform(-1, 1, C).astype(np.float32),
+                       rng.uniform(-1, 1, R).astype(np.float32))
+    h = build("coo_blocked", w, dev, col_blocks=1)
+    hot = h.array("bc_hot").reshape(-1, h.info["hot_slots"])
+    assert (hot[0] >= 0).all() and (hot[1] >= 0).sum() == 3
+    check_builder(h, w)
+    y_ref, bound = oracle.spmv_csr(w.row_ptrs, w.col_idx, w.values, w.x, w.y)
+    _, _, _, x, y0 = to_dev(w, dev)
+    assert_rows(run_once(h, x, y0), y_ref, bound, "hot rows")
 
 
 def _slices(w, K):
@@ -551,6 +660,17 @@ def test_col_slices_parity(dev, name, fmt):
         pytest.skip("ELL of a skewed slice is mostly padding")
     if fmt == "ell_xtile" and any(xtile_refused(*sl) for sl in _slices(w, 3)):
         expect_refused(fmt, w, dev, col_blocks=3)
+        return
+    if fmt == "coo_blocked":
+        # its slice count is 1, 2, 4 or 8; 3 is an invalid argument
+        with pytest.raises(spmv.SpmvError) as ei:
+            build(fmt, w, dev, col_blocks=3)
+        assert ei.value.name == "SPMV_ERR_INVALID_ARG"
+        h = build(fmt, w, dev, col_blocks=4)
+        assert h.info["col_blocks"] == 4 and h.info["slice_cols"] == -(-w.num_cols // 4)
+        check_blocked(h, w)
+        _, _, _, x, y0 = to_dev(w, dev)
+        assert_rows(run_once(h, x, y0), *ref(name), f"{name}/{fmt} 4 slices")
         return
     h = build(fmt, w, dev, col_blocks=3)
     assert h.info["col_blocks"] == 3

@@ -732,3 +732,211 @@ def test_xtile_refusals():
                                 (2 * np.arange(n)).astype(np.int32), np.ones(n, np.float32))
     oracle.csr_to_ell_xtile(np.array([0, 1024], np.int32),
                             (2 * np.arange(1024)).astype(np.int32), np.ones(1024, np.float32))
+
+
+# ------------------------------------------------------------- blocked COO
+
+def test_coo_blocked_hand_derived_example():
+    """Fig. 14.1 in blocked COO with 2-row blocks and 2 x slices, derived by
+    hand (tests/golden/coo_blocked_fig14_1.json).  Catches a row-major instead
+    of column order, a lost hot code, unstable order within a group and a
+    wrong base or offset."""
+    g = _gold("coo_blocked_fig14_1.json")
+    p = g["params"]
+    w = _fig()
+    o = oracle.csr_to_coo_blocked(w.row_ptrs, w.col_idx, w.values, p["num_cols"], p["slices"],
+                                  p["block_rows"], p["chunk_entries"], p["hot_slots"],
+                                  p["hot_min_len"])
+    for k in ("chunk_grp", "chunk_blk", "slice_chunk", "hot", "base"):
+        assert o[k].tolist() == g[k], k
+    assert o["wide"].size == 64 * g["wide_groups"]
+    pk, val = o["pk"].reshape(-1, 64), o["val"].reshape(-1, 64)
+    assert pk.shape[0] == len(g["groups"])
+    for gi, grp in enumerate(g["groups"]):
+        n = len(grp["code"])
+        assert (pk[gi, :n] >> 16).tolist() == grp["code"]
+        assert (pk[gi, :n] & 0xFFFF).tolist() == grp["offset"]
+        assert val[gi, :n].tolist() == grp["value"]
+        assert (pk[gi, n:] == 0xFFFF0000).all() and (val[gi, n:] == 0).all()
+
+
+def _decode_blocked(o, R, block_rows, hot_slots):
+    """(row, column, value bits, chunk, group, lane) of every real slot,
+    decoded from the blocked arrays with plain loops."""
+    out = []
+    pk = o["pk"].reshape(-1, 64)
+    vb = o["val"].view(np.uint32).reshape(-1, 64)
+    hot = o["hot"].reshape(-(-R // block_rows), hot_slots)
+    for c in range(len(o["chunk_blk"])):
+        b = int(o["chunk_blk"][c])
+        for g in range(int(o["chunk_grp"][c]), int(o["chunk_grp"][c + 1])):
+            base = int(o["base"][g])
+            for lane in range(64):
+                word = int(pk[g, lane])
+                code = word >> 16
+                if code == 0xFFFF:
+                    continue
+                col = (int(o["wide"][(-base - 1) * 64 + lane]) if base < 0
+                       else base + (word & 0xFFFF))
+                row = (int(hot[b, code - block_rows]) if code >= block_rows
+                       else b * block_rows + code)
+                out.append((row, col, int(vb[g, lane]), c, g, lane))
+    return out
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_coo_blocked_semantics_bruteforce(seed):
+    """Random matrices (empty rows, duplicates, long rows, a narrow and a
+    scattered column band) with small blocks, chunks and hot thresholds:
+    decoding the arrays gives back exactly the matrix's entries, and every
+    ordering rule of the definition holds, checked with plain loops."""
+    rng = np.random.default_rng(300 + seed)
+    R = int(rng.integers(1, 400))
+    C = int(rng.choice([7, 300, 70_000, 200_000]))
+    w = synth.small_random(rng, R, C, max_len=int(rng.integers(1, 60)))
+    S, RT, E, H = int(rng.choice([1, 2, 4, 8])), int(rng.choice([1, 5, 64])), \
+        int(rng.choice([1, 64, 100])), int(rng.choice([0, 1, 3]))
+    hot_min = int(rng.integers(1, 20))
+    o = oracle.csr_to_coo_blocked(w.row_ptrs, w.col_idx, w.values, C, S, RT, E, H, hot_min)
+    nblk = -(-R // RT)
+    sc = max(-(-C // S), 1)
+    rows = np.repeat(np.arange(R), np.diff(w.row_ptrs))
+    # hot rows by the rule, by plain sorting
+    lens = np.diff(w.row_ptrs)
+    hot = -np.ones((nblk, H), np.int64)
+    for b in range(nblk):
+        cand = sorted((r for r in range(b * RT, min(R, (b + 1) * RT)) if lens[r] >= hot_min),
+                      key=lambda r: (-lens[r], r))[:H]
+        hot[b, :len(cand)] = cand
+    assert o["hot"].tolist() == hot.reshape(-1).tolist()
+    dec = _decode_blocked(o, R, RT, H)
+    # the same multiset of (row, column, value bits)
+    got = sorted((r, c, v) for r, c, v, *_ in dec)
+    want = sorted(zip(rows.tolist(), w.col_idx.tolist(), w.values.view(np.uint32).tolist()))
+    assert got == want
+    # expected entry order: by (segment, column), ties in CSR order
+    seg = (w.col_idx // sc) * nblk + rows // RT
+    order = sorted(range(w.nnz), key=lambda i: (seg[i], w.col_idx[i], i))
+    # chunks and groups cut that order into runs of E and 64
+    pos = 0
+    expect_grp = []
+    for s in range(S * nblk):
+        run = [i for i in order if seg[i] == s]
+        for e0 in range(0, len(run), E):
+            chunk = run[e0:e0 + E]
+            expect_grp.append([chunk[g0:g0 + 64] for g0 in range(0, len(chunk), 64)])
+    assert len(o["chunk_blk"]) == len(expect_grp)
+    assert o["chunk_grp"].tolist() == np.cumsum([0] + [len(c) for c in expect_grp]).tolist()
+    code = {r: r % RT for r in range(R)}
+    for b in range(nblk):
+        for h in range(H):
+            if hot[b, h] >= 0:
+                code[int(hot[b, h])] = RT + h
+    by_group = {}
+    for r, c, v, ch, g, lane in dec:
+        by_group.setdefault(g, []).append((lane, r, c, v))
+    gi = 0
+    nwide = 0
+    for ch, groups in enumerate(expect_grp):
+        for grp in groups:
+            lanes = sorted(by_group[gi])
+            # reordered stably by code
+            want_lanes = sorted(grp, key=lambda i: code[rows[i]])
+            assert [(r, c) for _, r, c, _ in lanes] == \
+                [(int(rows[i]), int(w.col_idx[i])) for i in want_lanes]
+            assert lanes[-1][0] == len(grp) - 1          # real slots first, then padding
+            lo, hi = int(w.col_idx[grp[0]]), int(w.col_idx[grp[-1]])
+            if hi - lo > 65535:
+                assert o["base"][gi] == -(nwide + 1)
+                nwide += 1
+            else:
+                assert o["base"][gi] == lo
+            gi += 1
+    assert o["wide"].size == 64 * nwide
+    assert o["slice_chunk"][0] == 0 and o["slice_chunk"][-1] == len(expect_grp)
+
+
+def test_coo_blocked_y_by_decoding():
+    """y from the decoded slots (a plain loop) equals the dense product on a
+    matrix with wide groups and hot rows."""
+    rng = np.random.default_rng(9)
+    w = synth.small_random(rng, 200, 500_000, max_len=50)
+    o = oracle.csr_to_coo_blocked(w.row_ptrs, w.col_idx, w.values, w.num_cols, 2, 64, 100, 2,
+                                  30)
+    y = w.y.astype(np.float64).copy()
+    for r, c, v, *_ in _decode_blocked(o, w.num_rows, 64, 2):
+        y[r] += float(np.uint32(v).view(np.float32)) * float(w.x[c])
+    A = _dense_from_csr(w.num_rows, w.num_cols, w.row_ptrs, w.col_idx, w.values)
+    assert np.allclose(y, A @ w.x.astype(np.float64) + w.y, rtol=0, atol=1e-9)
+    assert o["wide"].size > 0 and (o["hot"] >= 0).any()
+
+
+# --------------------------------------------------- the automatic build's rule
+
+def _csr_random(rng, R, C, per_row):
+    lens = np.full(R, per_row) if np.isscalar(per_row) else np.asarray(per_row)
+    cols = [np.sort(rng.choice(C, int(l), replace=False)) for l in lens]
+    rp = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return rp, np.concatenate(cols).astype(np.int32)
+
+
+def _spread(rp, ci, C):
+    """The column-spread statistic, by a plain loop."""
+    R = len(rp) - 1
+    d = [abs(int(ci[rp[r]]) - r * C // R) for r in range(R) if rp[r + 1] > rp[r]]
+    return sum(d) // len(d)
+
+
+def test_select_build_fig14_1():
+    w = _fig()
+    assert oracle.select_build(w.row_ptrs, w.col_idx, 4) == ("ell", 0, 0, 1)
+
+
+def test_select_build_blocked_branch():
+    """65,536 rows x 2^21 columns (8 MiB of x), 16 random columns per row:
+    scattered, and 32 * nnz * 16384 = 2^39 >= R * C = 2^37 -> blocked COO
+    with 4 slices (8 MiB <= 4 * 2 MiB)."""
+    rng = np.random.default_rng(1)
+    R, C = 1 << 16, 1 << 21
+    rp, ci = _csr_random(rng, R, C, 16)
+    assert _spread(rp, ci, C) * 8 > C
+    assert oracle.select_build(rp, ci, C) == ("coo_blocked", 0, 0, 4)
+
+
+@pytest.mark.parametrize("nnz,slices", [(98304, 8), (98303, 4)])
+def test_select_build_slice_halving_boundary(nnz, slices):
+    """4,096 rows x 2^22 columns (16 MiB of x): 32 * nnz * 4096 < R * C, so
+    not blocked; x slices start at 8 (16 MiB / 2 MiB) and halve while
+    3 * K * R > nnz: 3 * 8 * 4096 = 98,304 -- at nnz 98,304 K stays 8, one
+    entry fewer and K = 4 (3 * 4 * 4096 = 49,152 <= 98,303)."""
+    rng = np.random.default_rng(2)
+    R, C = 4096, 1 << 22
+    lens = np.full(R, 24)
+    lens[0] -= 98304 - nnz
+    rp, ci = _csr_random(rng, R, C, lens)
+    assert rp[-1] == nnz and 32 * nnz * R < R * C and _spread(rp, ci, C) * 8 > C
+    assert oracle.select_build(rp, ci, C) == ("csr_merge", 0, 0, slices)
+
+
+def test_select_build_four_mib_x_is_not_split():
+    """x of exactly 4 MiB (2^20 columns) is not larger than one L2: the
+    selector's format, one slice (16 random columns per row: ELL)."""
+    rng = np.random.default_rng(3)
+    rp, ci = _csr_random(rng, 20000, 1 << 20, 16)
+    assert oracle.select_build(rp, ci, 1 << 20) == ("ell", 0, 0, 1)
+
+
+def test_select_build_x_tiles_on_stencils():
+    """Banded rows, R >= 16384.  The 27-point stencil on 26^3 reuses each tile
+    column more than twice: x tiles.  The 5-point Laplacian on 512^2: a
+    256-row block lies inside one grid line and touches its own 256 columns,
+    the 256 above, the 256 below and one on each side, 770 in all, for 1,280
+    entries -- fewer than 2 * 770, so plain ELL.  On 128^2 a block spans two
+    grid lines (512 + 2 columns for 1,280 entries): x tiles."""
+    w = synth.stencil27(26)
+    assert w.num_rows >= 16384
+    assert oracle.select_build(w.row_ptrs, w.col_idx, w.num_cols)[0] == "ell_xtile"
+    w = synth.laplacian2d(512)
+    assert oracle.select_build(w.row_ptrs, w.col_idx, w.num_cols)[0] == "ell"
+    w = synth.laplacian2d(128)
+    assert oracle.select_build(w.row_ptrs, w.col_idx, w.num_cols)[0] == "ell_xtile"

@@ -1,31 +1,41 @@
 """SpMV benchmark on one MI355X: y <- A*x + y, fp32, synthetic matrices.
 
-Default workload: 1,000,000 x 1,000,000, exactly 5 random columns per row
-(5M nonzeros), the format the selector picks (ELL).  One step = one full
-y <- A x + y pass of that format with every input resident in HBM and the
-caches flushed just before it (a 1 GiB fill kernel, untimed), timed with HIP
-events on the stream the kernels run on.
+Headline: the power-law matrix (4,000,000 rows, Zipf-like row lengths, about
+65M nonzeros), the largest workload, in the format the automatic build picks.
+One step = one full y <- A x + y pass with every input resident in HBM and
+the caches flushed just before it (a 1 GiB fill kernel, untimed), timed with
+HIP events on the stream the kernels run on.  The same line carries one entry
+per other workload (2-D Laplacian 256^2, random 1M x 5, 27-point 128^3,
+skewed 2M rows -- the last also in HYB with ELL width 20), every format's
+figures on the headline matrix, the device's gather and LDS-update rates
+(microbenchmarks), the builders' times and the CPU baselines.
 
-Printed (one JSON line on stdout): GFLOP/s (2 flops per nonzero), effective
-GB/s on the algorithmic bytes
+GFLOP/s count 2 flops per nonzero; effective GB/s use the algorithmic bytes
     B_alg = 8*nnz + 4*(R+1) + 4*C + 8*R      (values+columns, row structure,
                                                x once, y read+write)
-the fraction of the 8 TB/s HBM peak, every format's figures on the same
-matrix, the builders' times, and the single-threaded CPU oracle as baseline.
-Before it is timed, every format's y is checked row by row against an fp64
-host product (scipy.sparse) within 1e-5 * (sum_j |a_ij x_j| + |y_i|); the
-oracle itself runs only in the CPU-baseline leg.
+and the fraction is B_alg / time / 8 TB/s.  Before it is timed, every format's
+y is checked row by row against an fp64 host product (scipy.sparse) within
+1e-5 * (sum_j |a_ij x_j| + |y_i|); the oracle itself runs only in the
+CPU-baseline leg.
 
-    python bench.py [--steps K] [--warmup W] [--config c2] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--config cN] [--no-cpu]
 """
 from __future__ import annotations
 
-import argparse
-import json
 import os
-import statistics
-import sys
-import time
+
+# CPUs this process may use, recorded before an OpenMP runtime with thread
+# binding pins the main thread to one of them
+_AFFINITY_CPUS = len(os.sched_getaffinity(0))
+# CPU baseline thread placement (read when the OpenMP runtime starts)
+os.environ.setdefault("OMP_PROC_BIND", "close")
+os.environ.setdefault("OMP_PLACES", "cores")
+
+import argparse  # noqa: E402
+import json  # noqa: E402
+import statistics  # noqa: E402
+import sys  # noqa: E402
+import time  # noqa: E402
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -34,13 +44,14 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, vendor figure
 FLUSH_BYTES = 1 << 30       # > 256 MB MALL + 8 x 4 MB L2
 FORMATS = ["coo_atomic", "coo_segmented", "csr_scalar", "csr_vector", "ell", "hyb", "jds",
-           "csr_merge", "sell", "ell_xtile"]
+           "csr_merge", "sell", "ell_xtile", "coo_blocked"]
+HEADLINE = "c5"
 WORKLOAD_NAMES = {
     "c1": "laplacian2d_256 (65,536 rows, 5-point, 326,656 nnz)",
     "c2": "random_rows_1Mx5 (1,000,000 x 1,000,000, 5 random cols/row, 5,000,000 nnz)",
     "c3": "stencil27_128 (2,097,152 rows, 27-point truncated, 55,742,968 nnz)",
-    "c4": "skewed_2M (2,000,000 rows, 10-20 nnz + 50 rows of 1000-5000, HYB width 20)",
-    "c5": "power_law_4M (4,000,000 rows, Zipf 2.1 row lengths, ~64M nnz)",
+    "c4": "skewed_2M (2,000,000 rows, 10-20 nnz + 50 rows of 1000-5000)",
+    "c5": "power_law_4M (4,000,000 rows, Zipf 2.1 row lengths, ~65M nnz)",
 }
 
 
@@ -143,23 +154,25 @@ def check_rows(y, y_ref, bound):
     return int(bad.size), int(bad[0]) if bad.size else -1, worst
 
 
-def cpu_baseline(w, budget_s=10.0):
+def cpu_baseline(w, y_ref, bound, budget_s=10.0):
     """The oracle as it is (single thread, fp64 sums) on full passes of the
-    same matrix, repeated for about `budget_s` seconds."""
+    same matrix, for about `budget_s` seconds (at least 3 passes; median), and
+    beside it the OpenMP CSR baseline."""
     import oracle
     oracle.spmv_csr(w.row_ptrs, w.col_idx, w.values, w.x, w.y)  # load / warm
-    n, t_total = 0, 0.0
-    while t_total < budget_s or n < 3:
+    ts, t_total = [], 0.0
+    while t_total < budget_s or len(ts) < 3:
         t0 = time.perf_counter()
         oracle.spmv_csr(w.row_ptrs, w.col_idx, w.values, w.x, w.y)
-        t_total += time.perf_counter() - t0
-        n += 1
-    t = t_total / n
+        ts.append(time.perf_counter() - t0)
+        t_total += ts[-1]
+    t = statistics.median(ts)
     return {"value": round(2 * w.nnz / t / 1e9, 4), "unit": "GFLOP/s", "cores": 1,
             "kind": "oracle", "host": host_cpu(),
-            "sample": f"{n} full passes of the same {w.num_rows}-row matrix "
-                      f"({w.nnz} nnz), {t * 1e3:.1f} ms each, single thread, fp64 sums",
-            "openmp": openmp_baseline(w, budget_s / 2)}
+            "sample": f"{len(ts)} full passes of the same {w.num_rows}-row matrix "
+                      f"({w.nnz} nnz), median {t * 1e3:.1f} ms, single thread, fp64 sums",
+            "gbs_alg": round(alg_bytes(w.num_rows, w.num_cols, w.nnz) / t / 1e9, 3),
+            "openmp": openmp_baseline(w, y_ref, bound)}
 
 
 def host_cpu():
@@ -173,32 +186,129 @@ def host_cpu():
                     break
     except OSError:
         pass
-    return {"model": model, "logical_cpus": os.cpu_count(),
-            "affinity_cpus": len(os.sched_getaffinity(0))}
+    return {"model": model, "logical_cpus": os.cpu_count(), "affinity_cpus": _AFFINITY_CPUS}
 
 
-def openmp_baseline(w, budget_s=5.0):
-    """An OpenMP CSR SpMV (rows split over the host's threads, fp64 row sums)
-    on full passes of the same matrix, checked against the oracle first."""
+def openmp_baseline(w, y_ref, bound, reps=10):
+    """OpenMP CSR SpMV (oracle/csr_omp.c): rows over all OpenMP threads, fp32
+    row sums, first-touch copies of the arrays, OMP_PROC_BIND=close; the
+    median of `reps` timed passes with schedule(static) and with
+    schedule(dynamic,64).  Each y is first checked against the oracle within
+    the bound of recursive fp32 summation, (n + 2) * 2^-24 * (|y| + sum |a x|)."""
     import numpy as np
     import oracle
-    y_ref, bound = oracle.spmv_csr(w.row_ptrs, w.col_idx, w.values, w.x, w.y)
-    y = oracle.spmv_csr_omp(w.row_ptrs, w.col_idx, w.values, w.x, w.y)
-    n_bad, _, _ = oracle.check(y, y_ref, bound)
-    if n_bad:
-        raise RuntimeError(f"OpenMP CSR baseline: {n_bad} rows out of bound")
-    n, t_total = 0, 0.0
-    while t_total < budget_s or n < 3:
+    out = {"kind": "openmp_csr", "unit": "GFLOP/s", "cores": oracle.omp_threads(),
+           "env": {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OMP_PROC_BIND",
+                                                  "OMP_PLACES")}}
+    n = np.diff(w.row_ptrs.astype(np.int64))
+    mag = bound / 1e-5
+    B = alg_bytes(w.num_rows, w.num_cols, w.nnz)
+    for label, dyn in (("static", False), ("dynamic64", True)):
+        y, t = oracle.spmv_csr_omp(w.row_ptrs, w.col_idx, w.values, w.x, w.y, dynamic=dyn,
+                                   reps=reps)
+        err = np.abs(y.astype(np.float64) - y_ref)
+        bad = int(np.sum(err > (n + 2) * 2.0**-24 * mag))
+        if bad:
+            raise RuntimeError(f"OpenMP CSR baseline ({label}): {bad} rows out of bound")
+        out[label] = {"value": round(2 * w.nnz / t / 1e9, 3), "ms_median": round(t * 1e3, 3),
+                      "gbs_alg": round(B / t / 1e9, 2)}
+    best = max(("static", "dynamic64"), key=lambda k: out[k]["value"])
+    out["value"] = out[best]["value"]
+    out["schedule"] = best
+    out["sample"] = (f"median of {reps} full passes per schedule of the same "
+                     f"{w.num_rows}-row matrix, {out['cores']} OpenMP threads, fp32 row sums")
+    return out
+
+
+def run_config(spmv, torch, dev, cfg, steps, warmup, flush_buf, formats=False, fmt="auto",
+               col_blocks=0, log_prefix=""):
+    """Build and time one workload.  Returns (entry, context) where entry is the
+    JSON-ready summary of the selected format (and, if asked, every format) and
+    context keeps what the headline needs (handle, tensors, times)."""
+    from spmv_storage_formats_amd import synth
+    log(f"{log_prefix}generating {cfg}")
+    w = synth.workload(cfg)
+    R, C, nnz = w.num_rows, w.num_cols, w.nnz
+    B = alg_bytes(R, C, nnz)
+    flops = 2 * nnz
+    rp = torch.from_numpy(w.row_ptrs).to(dev)
+    ci = torch.from_numpy(w.col_idx).to(dev)
+    va = torch.from_numpy(w.values).to(dev)
+    x = torch.from_numpy(w.x).to(dev)
+    y0 = torch.from_numpy(w.y).to(dev)
+    y_ref, bound = host_reference(w)
+
+    def build_and_check(f, **kw):
+        if col_blocks:
+            kw.setdefault("col_blocks", col_blocks)
+        torch.cuda.synchronize()
         t0 = time.perf_counter()
-        oracle.spmv_csr_omp(w.row_ptrs, w.col_idx, w.values, w.x, w.y)
-        t_total += time.perf_counter() - t0
-        n += 1
-    t = t_total / n
-    threads = oracle.omp_threads()
-    return {"value": round(2 * w.nnz / t / 1e9, 4), "unit": "GFLOP/s", "cores": threads,
-            "kind": "openmp_csr",
-            "sample": f"{n} full passes of the same {w.num_rows}-row matrix, {t * 1e3:.2f} ms "
-                      f"each, {threads} OpenMP threads, fp64 row sums (includes a y copy)"}
+        h = spmv.build(f, rp, ci, va, C, **kw)
+        bms = (time.perf_counter() - t0) * 1e3
+        y = y0.clone()
+        h.run(x, y)
+        torch.cuda.synchronize()
+        n_bad, first, worst = check_rows(y.cpu().numpy(), y_ref, bound)
+        if n_bad:
+            raise SystemExit(f"parity failure {cfg}/{f}: {n_bad} rows (first {first})")
+        return h, bms, worst
+
+    def summary(h, times, bms, worst):
+        med = statistics.median(times)
+        mean = statistics.mean(times)
+        prof = profiled_entry(f"{cfg}/{h.format}")
+        traffic = prof["hbm_bytes_per_launch"] if prof else None
+        prof_us = prof.get("kernel_avg_us") if prof else None
+        e = {"format": h.format, "col_blocks": h.info["col_blocks"],
+             "us_median": round(med * 1e3, 2), "us_mean": round(mean * 1e3, 2),
+             "gflops": round(flops / (mean * 1e-3) / 1e9, 1),
+             "gbs_alg": round(B / (mean * 1e-3) / 1e9, 1),
+             "frac_by_events": round(B / (mean * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+             "profiled_kernel": prof.get("kernel") if prof else None,
+             "profiled_kernel_us": prof_us,
+             "frac_by_profiled_kernel_us": (round(B / (prof_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                                            if prof_us else None),
+             "traffic_bytes": traffic,
+             "traffic_over_alg": round(traffic / B, 3) if traffic else None,
+             "frac_by_counter_bytes": (round(traffic / (prof_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                                       if traffic and prof_us else None),
+             "build_ms": round(bms, 2), "device_MB": round(h.info["device_bytes"] / 1e6, 1),
+             "worst_err_over_bound": float(f"{worst:.3g}")}
+        return e
+
+    per_format = {}
+    if formats:
+        for f in FORMATS:
+            try:
+                hf, bms, wst = build_and_check(f, **({"hyb_width": 20} if cfg == "c4" else {}))
+            except spmv.SpmvError as e:
+                per_format[f] = {"refused": e.name}
+                continue
+            tf, _ = time_format(spmv, torch, hf, x, y0.clone(), max(10, steps // 2), 2,
+                                flush_buf)
+            per_format[f] = summary(hf, tf, bms, wst)
+            log(f"{log_prefix}{cfg} {f}: {per_format[f]['us_median']} us")
+            hf.close()
+    log(f"{log_prefix}{cfg}: building {fmt}")
+    h, bms, worst = build_and_check(fmt)
+    y = y0.clone()
+    times, wall = time_format(spmv, torch, h, x, y, steps, warmup, flush_buf)
+    entry = {"workload": WORKLOAD_NAMES[cfg], "rows": R, "cols": C, "nnz": nnz,
+             "alg_bytes": B, **summary(h, times, bms, worst)}
+    log(f"{log_prefix}{cfg}: {entry['format']} {entry['us_median']} us, "
+        f"frac {entry['frac_by_events']}")
+    if cfg == "c4":
+        # the configuration names HYB with ELL width 20: reported beside the
+        # automatic format
+        hh, hbms, hw = build_and_check("hyb", hyb_width=20)
+        th, _ = time_format(spmv, torch, hh, x, y0.clone(), max(10, steps // 2), 2, flush_buf)
+        entry["hyb_width20"] = summary(hh, th, hbms, hw)
+        hh.close()
+    if per_format:
+        entry["formats"] = per_format
+    ctx = {"w": w, "h": h, "times": times, "wall": wall, "x": x, "y0": y0, "y_ref": y_ref,
+           "bound": bound, "B": B}
+    return entry, ctx
 
 
 def main():
@@ -206,15 +316,19 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="c2", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--config", default=None, choices=sorted(WORKLOAD_NAMES),
+                    help="time only this workload (as the headline); default: the power-law "
+                         "matrix as the headline plus one entry per other workload")
     ap.add_argument("--format", default="auto")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only-selected", action="store_true",
-                    help="time only the selected format (for profiling runs)")
+                    help="time only the selected format of the headline workload (for "
+                         "profiling runs)")
+    ap.add_argument("--all-formats", action="store_true",
+                    help="every format on every workload (default: on the headline only)")
+    ap.add_argument("--no-micro", action="store_true", help="skip the microbenchmarks")
     ap.add_argument("--warm", action="store_true",
-                    help="also time the selected format without cache flushes (off by default "
-                         "so that every launch of the selected kernel in a profiled run is a "
-                         "cold step)")
+                    help="also time the selected format without cache flushes")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--col-blocks", type=int, default=0,
                     help="x slices for every build (0 = library default)")
@@ -232,99 +346,51 @@ def main():
               "(the row-sharded multi-GPU design is documented, not built)", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import spmv_storage_formats_amd as spmv
-    from spmv_storage_formats_amd import synth
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
     spmv.load_library()
-    log(f"generating {args.config}")
-    w = synth.workload(args.config)
-    R, C, nnz = w.num_rows, w.num_cols, w.nnz
-    B = alg_bytes(R, C, nnz)
-    flops = 2 * nnz
-    rp = torch.from_numpy(w.row_ptrs).to(dev)
-    ci = torch.from_numpy(w.col_idx).to(dev)
-    va = torch.from_numpy(w.values).to(dev)
-    x = torch.from_numpy(w.x).to(dev)
-    y0 = torch.from_numpy(w.y).to(dev)
     flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
-    y_ref, bound = host_reference(w)
+    headline = args.config or HEADLINE
+    others = [] if (args.config or args.only_selected) else \
+        [c for c in ("c1", "c2", "c3", "c4") if c != headline]
 
-    kw = {"hyb_width": 20} if args.config == "c4" else {}
-    if args.col_blocks:
-        kw["col_blocks"] = args.col_blocks
+    configs = {}
+    for cfg in others:
+        entry, ctx = run_config(spmv, torch, dev, cfg, min(args.steps, 30), args.warmup,
+                                flush_buf, formats=args.all_formats, col_blocks=args.col_blocks)
+        ctx["h"].close()
+        configs[cfg] = entry
+        del ctx
+        torch.cuda.empty_cache()
 
-    def build_and_check(fmt):
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        h = spmv.build(fmt, rp, ci, va, C, **kw)
-        build_ms = (time.perf_counter() - t0) * 1e3
-        y = y0.clone()
-        h.run(x, y)
-        torch.cuda.synchronize()
-        n_bad, first, worst = check_rows(y.cpu().numpy(), y_ref, bound)
-        if n_bad:
-            raise SystemExit(f"parity failure {args.config}/{fmt}: {n_bad} rows (first {first})")
-        return h, build_ms, worst
-
-    # 1) the same matrix in every format (parity-checked, cold-cache timing)
-    per_format = {}
-    if not args.only_selected:
-        for fmt in FORMATS:
-            try:
-                hf, bms, wst = build_and_check(fmt)
-            except spmv.SpmvError as e:
-                per_format[fmt] = {"refused": e.name}
-                continue
-            tf, _ = time_format(spmv, torch, hf, x, y0.clone(), max(10, args.steps // 2), 2,
-                                flush_buf)
-            mf = statistics.median(tf)
-            per_format[fmt] = {
-                "us_median": round(mf * 1e3, 2),
-                "gflops": round(flops / (mf * 1e-3) / 1e9, 1),
-                "gbs_alg": round(B / (mf * 1e-3) / 1e9, 1),
-                "frac_hbm": round(B / (mf * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                "build_ms": round(bms, 2),
-                "device_MB": round(hf.info["device_bytes"] / 1e6, 1),
-                "col_blocks": hf.info["col_blocks"],
-                "worst_err_over_bound": float(f"{wst:.3g}"),
-            }
-            log(f"{fmt}: {per_format[fmt]}")
-            hf.close()
-
-    # 2) the selected format: K timed steps, each after an untimed cache flush
-    log(f"building {args.format}")
-    h, build_ms, worst = build_and_check(args.format)
-    selected = h.format
-    log(f"selected {selected}; parity ok (worst err/bound {worst:.2e}); timing {args.steps} steps")
-    y = y0.clone()
-    times, wall = time_format(spmv, torch, h, x, y, args.steps, args.warmup, flush_buf)
+    entry, ctx = run_config(spmv, torch, dev, headline, args.steps, args.warmup, flush_buf,
+                            formats=not args.only_selected, fmt=args.format,
+                            col_blocks=args.col_blocks)
+    configs[headline] = entry
+    w, h, times, wall, B = ctx["w"], ctx["h"], ctx["times"], ctx["wall"], ctx["B"]
+    R, C, nnz = w.num_rows, w.num_cols, w.nnz
+    flops = 2 * nnz
     ms = statistics.mean(times)
     med = statistics.median(times)
     gbs = B / (ms * 1e-3) / 1e9
     warm_ms = warm_med = None
     if args.warm:
-        warm_times, _ = time_format(spmv, torch, h, x, y, args.steps, args.warmup, flush_buf,
-                                    flush=False)
+        warm_times, _ = time_format(spmv, torch, h, ctx["x"], ctx["y0"].clone(), args.steps,
+                                    args.warmup, flush_buf, flush=False)
         warm_ms = round(statistics.mean(warm_times), 5)
         warm_med = round(statistics.median(warm_times), 5)
     q = statistics.quantiles(times, n=10) if len(times) >= 2 else [med] * 9
-
-    prof = profiled_entry(f"{args.config}/{selected}")
+    prof = profiled_entry(f"{headline}/{h.format}")
     traffic = prof["hbm_bytes_per_launch"] if prof else None
     prof_us = prof.get("kernel_avg_us") if prof else None
     l2_req = prof.get("l2_requests_per_launch") if prof else None
     overhead_us = event_overhead_us(torch)
-    gather_ref = None
-    if args.config in ("c2", "c4", "c5"):   # uniformly random columns
-        gather_ref = gather_reference(torch, dev, C, nnz, flush_buf)
-        gather_ref["spmv_g_gathers_per_s"] = round(nnz / (med * 1e3) / 1e3, 1)
 
     result = {
         "metric": "SpMV GFLOP/s and effective HBM GB/s (% of MI355X peak) per format, 1 GPU",
@@ -339,7 +405,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded), inputs resident in HBM, caches flushed before each step",
-        "config": {"workload": WORKLOAD_NAMES[args.config], "format": selected,
+        "config": {"workload": WORKLOAD_NAMES[headline], "format": h.format,
                    "col_blocks": h.info["col_blocks"],
                    "rows": R, "cols": C, "nnz": nnz, "max_row_length": int(h.info["max_len"]),
                    "parallelism": "single GPU", "inputs_sha256": input_hashes(w)},
@@ -353,36 +419,38 @@ def main():
         "warm_ms_median": warm_med,
         "pages_model_gbs": round(pages_bytes(R, nnz) / (ms * 1e-3) / 1e9, 1),
         "wall_s_timed_loop_incl_flush": round(wall, 4),
-        "build_ms": round(build_ms, 2),
+        "build_ms": entry["build_ms"],
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "bytes_per_launch_alg": B,
+                     "kernel": prof.get("kernel") if prof else None,
                      # the same kernel's average duration in the committed
                      # rocprofv3 trace of this workload (no dispatch latency)
-                     # and the fraction it gives, beside the live event time
+                     # and the fractions it gives, beside the live event time
                      "profiled_kernel_us": prof_us,
                      "frac_by_profiled_kernel_us": (round(B / (prof_us * 1e-6) / 1e9 /
                                                           HBM_PEAK_GBS, 4)
                                                     if prof_us else None),
-                     # L2 requests per launch from the committed L2 counter
-                     # run (random columns: about one per nonzero), and the
-                     # rate they give by the live step time and by the
-                     # profiled kernel time
+                     "traffic_over_alg": round(traffic / B, 3) if traffic else None,
                      "l2_requests_per_launch": l2_req,
-                     "l2_g_requests_per_s": (round(l2_req / (ms * 1e-3) / 1e9, 1)
-                                             if l2_req else None),
                      "l2_g_requests_per_s_by_profiled_kernel_us": (
                          round(l2_req / (prof_us * 1e-6) / 1e9, 1)
-                         if l2_req and prof_us else None)},
-        "formats": per_format,
-        "gather_reference": gather_ref,
+                         if l2_req and prof_us else None),
+                     "spmv_g_gathers_per_s": round(nnz / (med * 1e3) / 1e3, 1)},
+        "configs": configs,
     }
+    if not args.no_micro:
+        from spmv_storage_formats_amd import microbench
+        log("microbenchmarks")
+        result["device_rates"] = {"gather": microbench.gather_rates(torch, dev, flush_buf),
+                                  "lds": microbench.lds_rates(torch, dev)}
     cref = copy_reference(torch, dev, flush_buf)
     cref["spmv_frac_of_copy"] = round(gbs / cref["gbs"], 4)
     result["copy_reference"] = cref
     if not args.only_selected:
         result["coo_to_csr"] = coo_section(spmv, torch, w, dev)
     if args.cg:
+        from spmv_storage_formats_amd import synth
         result["cg"] = cg_section(spmv, torch, synth, dev, flush_buf)
     if args.calibrate_copy:
         n = 512 << 20
@@ -394,8 +462,8 @@ def main():
         torch.cuda.synchronize()
         result["copy_calibration_bytes"] = {"read": n, "write": n}
     if not args.no_cpu:
-        log("cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        log("cpu baseline (oracle, OpenMP)")
+        result["cpu_baseline"] = cpu_baseline(w, ctx["y_ref"], ctx["bound"], args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
@@ -479,36 +547,6 @@ def cg_section(spmv, torch, synth, dev, flush_buf):
     return out
 
 
-def gather_reference(torch, dev, num_cols, n, flush_buf, steps=20):
-    """A library random gather for context on the random-column workloads:
-    torch.index_select of n uniform random int32 column indices from an x of
-    num_cols floats, timed like a step (cache flush, HIP events).  It moves
-    no matrix values and no y, so an SpMV that does the same number of
-    gathers in less time is at the device's random-gather limit, not at a
-    byte limit."""
-    g = torch.Generator(device=dev)
-    g.manual_seed(12345)
-    x = torch.rand(num_cols, device=dev, generator=g)
-    idx = torch.randint(0, num_cols, (n,), device=dev, generator=g, dtype=torch.int64)
-    idx = idx.to(torch.int32)
-    out = torch.empty(n, device=dev)
-    stream = torch.cuda.current_stream()
-    torch.index_select(x, 0, idx, out=out)
-    torch.cuda.synchronize()
-    ts = []
-    for _ in range(steps):
-        flush_buf.zero_()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        torch.index_select(x, 0, idx, out=out)
-        b.record(stream)
-        b.synchronize()
-        ts.append(a.elapsed_time(b))
-    us = statistics.median(ts) * 1e3
-    return {"kernel": "torch.index_select, int32 indices", "gathers": n, "x_floats": num_cols,
-            "us_median": round(us, 2), "g_gathers_per_s": round(n / us / 1e3, 1)}
-
-
 def event_overhead_us(torch):
     """Median HIP-event time around one empty kernel (torch's spin kernel with
     a zero count) on the same stream: the dispatch latency that per-step event
@@ -558,11 +596,11 @@ def measured_traffic(key):
 
 def kernel_source_sha():
     """Hash of the sources the SpMV kernels are compiled from (the kernels
-    file and the shared header); builders and CG live elsewhere."""
+    files and the shared header; the blocked-COO builder shares its file)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "spmv_storage_formats_amd", "csrc")
-    for f in ("internal.h", "spmv_kernels.hip"):
+    for f in ("internal.h", "spmv_kernels.hip", "coo_blocked.hip"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

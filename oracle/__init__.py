@@ -393,8 +393,9 @@ def _load_omp():
     lib = ctypes.CDLL(_OMP_LIB)
     lib.csr_omp_threads.restype = ctypes.c_int
     lib.csr_omp_threads.argtypes = []
-    lib.csr_spmv_omp.restype = None
-    lib.csr_spmv_omp.argtypes = [_i64, _i32p, _i32p, _f32p, _f32p, _f32p]
+    lib.csr_omp_bench.restype = ctypes.c_double
+    lib.csr_omp_bench.argtypes = [_i64, _i64, _i32p, _i32p, _f32p, _f32p, _f32p, _f32p,
+                                  ctypes.c_int, ctypes.c_int]
     _omp = lib
     return lib
 
@@ -404,9 +405,15 @@ def omp_threads() -> int:
     return int(_load_omp().csr_omp_threads())
 
 
-def spmv_csr_omp(row_ptrs, col_idx, values, x, y):
-    """OpenMP CSR baseline: returns fp32 y + A x (fp64 row sums, row order)."""
+def spmv_csr_omp(row_ptrs, col_idx, values, x, y, dynamic=False, reps=1):
+    """OpenMP CSR baseline (fp32 row sums in row order, schedule static or
+    dynamic,64): returns (fp32 y + A x, median seconds of `reps` timed runs)."""
     rp = _i32(row_ptrs)
-    out = np.array(y, dtype=np.float32, copy=True)
-    _load_omp().csr_spmv_omp(rp.shape[0] - 1, rp, _i32(col_idx), _f32(values), _f32(x), out)
-    return out
+    xs = _f32(x)
+    out = np.empty(rp.shape[0] - 1, np.float32)
+    t = _load_omp().csr_omp_bench(rp.shape[0] - 1, xs.shape[0], rp, _i32(col_idx),
+                                  _f32(values), xs, _f32(y), out, 1 if dynamic else 0,
+                                  int(reps))
+    if t < 0:
+        raise MemoryError("csr_omp_bench: allocation failed")
+    return out, t

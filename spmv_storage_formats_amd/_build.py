@@ -43,6 +43,23 @@ def _compile(src: str) -> str:
     return obj
 
 
+BENCH_SRC = os.path.join(PKG, "bench_csrc", "microbench.hip")
+BENCH_LIB = os.path.join(PKG, "libspmv_microbench.so")
+
+
+def build_microbench(verbose: bool = True) -> str:
+    """The benchmark's gather / LDS-update microbenchmarks (not the library)."""
+    tmp = BENCH_LIB + f".tmp{os.getpid()}"
+    cmd = [HIPCC, *CFLAGS, "-shared", BENCH_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {BENCH_SRC}:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, BENCH_LIB)
+    if verbose:
+        print(f"built {BENCH_LIB}", file=sys.stderr)
+    return BENCH_LIB
+
+
 def build(verbose: bool = True) -> str:
     """Compile every HIP source and link the library.  Always rebuilds."""
     os.makedirs(OBJDIR, exist_ok=True)
@@ -62,3 +79,4 @@ def build(verbose: bool = True) -> str:
 
 if __name__ == "__main__":
     build()
+    build_microbench()

@@ -1,6 +1,8 @@
-"""The OpenMP CSR baseline the benchmark times beside the oracle: it must
-compute the same y as the oracle (both sum each row in fp64 in row order), so
-the reported CPU throughput is for a correct SpMV."""
+"""The OpenMP CSR baseline the benchmark times beside the oracle must compute
+y + A x: each row is summed in fp32 in row order, so it agrees with the
+oracle's fp64 row sum within the classical bound for recursive fp32
+summation, |err| <= (n + 2) u (|y| + sum |a x|) with n the row length and
+u = 2^-24 (the error bound of n additions, each rounding to nearest)."""
 import numpy as np
 import pytest
 
@@ -8,12 +10,34 @@ import oracle
 from spmv_storage_formats_amd import synth
 
 
+@pytest.mark.parametrize("dynamic", [False, True])
 @pytest.mark.parametrize("name", ["fig14_1", "c1s", "c2s", "c4s", "c5s"])
-def test_openmp_csr_equals_oracle(name):
+def test_openmp_csr_within_fp32_summation_bound(name, dynamic):
     w = synth.workload(name)
-    y_omp = oracle.spmv_csr_omp(w.row_ptrs, w.col_idx, w.values, w.x, w.y)
-    y_ref, _ = oracle.spmv_csr(w.row_ptrs, w.col_idx, w.values, w.x, w.y)
-    assert np.array_equal(y_omp.view(np.uint32), y_ref.astype(np.float32).view(np.uint32))
+    y_omp, t = oracle.spmv_csr_omp(w.row_ptrs, w.col_idx, w.values, w.x, w.y, dynamic=dynamic,
+                                   reps=3)
+    y_ref, bound = oracle.spmv_csr(w.row_ptrs, w.col_idx, w.values, w.x, w.y)
+    mag = bound / oracle.RTOL                       # |y| + sum |a x| per row
+    n = np.diff(w.row_ptrs.astype(np.int64))
+    err = np.abs(y_omp.astype(np.float64) - y_ref)
+    assert np.all(err <= (n + 2) * 2.0**-24 * mag)
+    assert t > 0
+
+
+def test_openmp_detects_a_wrong_row():
+    """The bound above is tight enough to see a dropped entry."""
+    w = synth.workload("c2s")
+    rp = w.row_ptrs.copy()
+    y_omp, _ = oracle.spmv_csr_omp(rp, w.col_idx, w.values, w.x, w.y)
+    y_ref, bound = oracle.spmv_csr(rp, w.col_idx, w.values, w.x, w.y)
+    # drop the first entry of row 10 from the reference
+    i = rp[10]
+    y_ref = y_ref.copy()
+    y_ref[10] -= float(w.values[i]) * float(w.x[w.col_idx[i]])
+    mag = bound / oracle.RTOL
+    n = np.diff(rp.astype(np.int64))
+    err = np.abs(y_omp.astype(np.float64) - y_ref)
+    assert err[10] > (n[10] + 2) * 2.0**-24 * mag[10]
 
 
 def test_openmp_thread_count_positive():

@@ -389,6 +389,31 @@ spmv_status spmv_run(const spmv_handle *h, const float *x_dev, float *y_dev, voi
 spmv_status spmv_cg(const spmv_handle *h, const float *b_dev, float *x_dev, int32_t max_iter,
                     float rtol, int32_t *iters, float *rel_resid, void *stream);
 
+/*
+ * spmv_cg_noalloc -- spmv_cg for callers that cannot allocate device memory
+ * (code that must not call hipMalloc: work inside tight serving loops,
+ * harnesses that forbid allocation).
+ *   Same arguments, checks, arithmetic and results as spmv_cg, except:
+ *   - the four work vectors and the dot partials live in one library-owned
+ *     static device array per GPU, sized for SPMV_CG_NOALLOC_MAX_ROWS rows
+ *     (about 16 MiB; reserved when the library's code is loaded on that GPU
+ *     and held until the process ends).  A system with more rows is refused
+ *     with SPMV_ERR_TOO_LARGE before any work;
+ *   - no HIP graphs: every iteration is launched directly (SPMV_CG_GRAPH is
+ *     ignored), so the results equal spmv_cg's with SPMV_CG_GRAPH=0, which
+ *     are spmv_cg's own bit for bit;
+ *   - it calls no hipMalloc, hipFree or other allocating routine.
+ *   Every call on one GPU uses that GPU's array, which keeps the previous
+ *   call's contents (each call initialises what it reads).  Calls that
+ *   overlap in time on the same GPU -- from several host threads or streams
+ *   -- race on the array and must be serialised by the caller.
+ *   Must be called on the handle's device (SPMV_ERR_DEVICE).  Host-synchronous.
+ */
+#define SPMV_CG_NOALLOC_MAX_ROWS 1048576
+spmv_status spmv_cg_noalloc(const spmv_handle *h, const float *b_dev, float *x_dev,
+                            int32_t max_iter, float rtol, int32_t *iters, float *rel_resid,
+                            void *stream);
+
 spmv_status spmv_get_info(const spmv_handle *h, spmv_info *info_host);
 
 /* Size in bytes of an exportable array (0 if the handle's format has none;

@@ -46,6 +46,7 @@ ARRAYS = {
     "bc_slice_chunk": (24, np.int32), "bc_hot": (25, np.int32), "bc_base": (26, np.int32),
     "bc_pk": (27, np.uint32), "bc_val": (28, np.float32), "bc_wide": (29, np.int32),
 }
+CG_NOALLOC_MAX_ROWS = 1048576   # SPMV_CG_NOALLOC_MAX_ROWS in include/spmv.h
 STATUS = {0: "SPMV_OK", 1: "SPMV_ERR_INVALID_ARG", 2: "SPMV_ERR_BAD_ROWPTRS",
           3: "SPMV_ERR_BAD_COLIDX", 4: "SPMV_ERR_BAD_ROWIDX", 5: "SPMV_ERR_TOO_LARGE",
           6: "SPMV_ERR_OOM", 7: "SPMV_ERR_HIP", 8: "SPMV_ERR_DEVICE"}
@@ -143,6 +144,8 @@ def load_library():
             "spmv_run": (ctypes.c_int, [_vp, _vp, _vp, _vp]),
             "spmv_cg": (ctypes.c_int, [_vp, _vp, _vp, _i32, ctypes.c_float, P(_i32),
                                        P(ctypes.c_float), _vp]),
+            "spmv_cg_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _i32, ctypes.c_float, P(_i32),
+                                               P(ctypes.c_float), _vp]),
             "spmv_get_info": (ctypes.c_int, [_vp, P(_Info)]),
             "spmv_array_bytes": (ctypes.c_int, [_vp, ctypes.c_int, P(ctypes.c_size_t)]),
             "spmv_export": (ctypes.c_int, [_vp, ctypes.c_int, _vp, ctypes.c_size_t]),
@@ -304,6 +307,20 @@ class Handle:
         _check(load_library().spmv_cg(self._ptr, bp, xp, int(max_iter), float(rtol),
                                       ctypes.byref(it), ctypes.byref(rr),
                                       _stream(stream, x.device)), "spmv_cg")
+        return it.value, rr.value
+
+    def cg_noalloc(self, b, x, max_iter: int = 1000, rtol: float = 1e-6, stream=None):
+        """The same solve as cg() on the library's static per-GPU workspace
+        (spmv_cg_noalloc: no device allocation, at most CG_NOALLOC_MAX_ROWS rows;
+        calls overlapping on one GPU race)."""
+        import torch
+        bp = _dev(b, torch.float32, "b", self.num_rows)
+        xp = _dev(x, torch.float32, "x", self.num_rows)
+        it = _i32()
+        rr = ctypes.c_float()
+        _check(load_library().spmv_cg_noalloc(self._ptr, bp, xp, int(max_iter), float(rtol),
+                                              ctypes.byref(it), ctypes.byref(rr),
+                                              _stream(stream, x.device)), "spmv_cg_noalloc")
         return it.value, rr.value
 
     def array(self, name: str) -> np.ndarray:

@@ -927,6 +927,17 @@ spmv_status spmv_cg(const spmv_handle *h, const float *b, float *x, int32_t max_
     return conjugate_gradient(h, b, x, max_iter, rtol, iters, rel_resid, s, scratch);
 }
 
+spmv_status spmv_cg_noalloc(const spmv_handle *h, const float *b, float *x, int32_t max_iter,
+                            float rtol, int32_t *iters, float *rel_resid, void *stream) {
+    if (!h || !iters || !rel_resid || max_iter < 0 || !(rtol >= 0.f) ||
+        h->stats.num_rows != h->stats.num_cols)
+        return SPMV_ERR_INVALID_ARG;
+    if (h->stats.num_rows > 0 && (!b || !x)) return SPMV_ERR_INVALID_ARG;
+    SPMV_TRY(check_device(h));
+    return conjugate_gradient_noalloc(h, b, x, max_iter, rtol, iters, rel_resid,
+                                      static_cast<hipStream_t>(stream));
+}
+
 spmv_status spmv_get_info(const spmv_handle *h, spmv_info *info) {
     if (!h || !info) return SPMV_ERR_INVALID_ARG;
     std::memset(info, 0, sizeof(*info));

@@ -19,10 +19,11 @@
 // partials' writes before their reads).  rr partials alternate between two
 // buffers.  The host adds the rr partials every kCheckEvery iterations to test
 // convergence.
+#include <array>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
-#include <vector>
+#include <mutex>
 
 #include "internal.h"
 
@@ -317,8 +318,8 @@ bool graphs_enabled() {
 }
 
 // Host sum of device partials, in block order.
-spmv_status host_sum(const double *part, int np, std::vector<double> &buf, double *out,
-                     hipStream_t s) {
+spmv_status host_sum(const double *part, int np, std::array<double, kDotBlocks> &buf,
+                     double *out, hipStream_t s) {
     SPMV_HIP(hipMemcpyAsync(buf.data(), part, sizeof(double) * np, hipMemcpyDeviceToHost, s));
     SPMV_HIP(hipStreamSynchronize(s));
     double t = 0.0;
@@ -329,19 +330,25 @@ spmv_status host_sum(const double *part, int np, std::vector<double> &buf, doubl
 
 }  // namespace
 
-spmv_status conjugate_gradient(const spmv_handle *A, const float *b, float *x, int32_t max_iter,
-                               float rtol, int32_t *iters, float *rel_resid, hipStream_t s,
-                               Scratch &scratch) {
+// Floats of the CG workspace for n rows: r, two p buffers, Ap (each padded to
+// 64 floats, 256 bytes), then the fp64 partials [pAp | rr slot 0 | rr slot 1 |
+// bb], kDotBlocks each.
+size_t cg_workspace_floats(int64_t n) {
+    const size_t nv = (static_cast<size_t>(n) + 63) & ~size_t{63};
+    return 4 * nv + 2 * 4 * kDotBlocks;
+}
+
+// The solve on a caller-provided workspace of cg_workspace_floats(R) floats;
+// with allow_graph false every iteration is launched directly.
+spmv_status cg_on_workspace(const spmv_handle *A, const float *b, float *x, int32_t max_iter,
+                            float rtol, int32_t *iters, float *rel_resid, hipStream_t s,
+                            float *vecs, bool allow_graph) {
     const int32_t n = static_cast<int32_t>(A->stats.num_rows);
     *iters = 0;
     *rel_resid = 0.f;
     if (n == 0) return SPMV_OK;
     const bool fused = fused_ell(A);
-    // one allocation: r, two p buffers, Ap (each 256-byte aligned), then the
-    // partials [pAp | rr slot 0 | rr slot 1 | bb], kDotBlocks each
     const size_t nv = (static_cast<size_t>(n) + 63) & ~size_t{63};
-    float *vecs = nullptr;
-    SPMV_TRY(scratch.alloc(&vecs, 4 * nv + 2 * 4 * kDotBlocks));
     float *r = vecs, *ap = vecs + 3 * nv;
     float *const pbuf[2] = {vecs + nv, vecs + 2 * nv};
     double *part = reinterpret_cast<double *>(vecs + 4 * nv);
@@ -349,7 +356,7 @@ spmv_status conjugate_gradient(const spmv_handle *A, const float *b, float *x, i
     double *part_rr[2] = {part + kDotBlocks, part + 2 * kDotBlocks};
     const unsigned gn = grid_for(n, kThreads);
     const int np = static_cast<int>(gn < static_cast<unsigned>(kDotBlocks) ? gn : kDotBlocks);
-    std::vector<double> host(kDotBlocks);
+    std::array<double, kDotBlocks> host{};
 
     // Ap = A x (into zeros); r = p = b - A x; Ap = 0; partials of r·r and b·b
     k_fill<<<gn, kThreads, 0, s>>>(n, 0.f, ap);
@@ -375,7 +382,7 @@ spmv_status conjugate_gradient(const spmv_handle *A, const float *b, float *x, i
     int cur = 0;   // part_rr[cur] holds the current r·r partials
     int32_t it = 0;
     // a graph pays for its capture from the second full batch on
-    const bool use_graph = graphs_enabled() && max_iter >= 2 * kCheckEvery;
+    const bool use_graph = allow_graph && graphs_enabled() && max_iter >= 2 * kCheckEvery;
     BatchGraph g(s);
     while (it < max_iter && rnorm > target) {
         const int32_t batch = std::min(kCheckEvery, max_iter - it);
@@ -399,6 +406,58 @@ spmv_status conjugate_gradient(const spmv_handle *A, const float *b, float *x, i
     *iters = it;
     *rel_resid = static_cast<float>(bnorm > 0.0 ? rnorm / bnorm : rnorm);
     return SPMV_OK;
+}
+
+spmv_status conjugate_gradient(const spmv_handle *A, const float *b, float *x, int32_t max_iter,
+                               float rtol, int32_t *iters, float *rel_resid, hipStream_t s,
+                               Scratch &scratch) {
+    float *vecs = nullptr;
+    if (A->stats.num_rows > 0)
+        SPMV_TRY(scratch.alloc(&vecs, cg_workspace_floats(A->stats.num_rows)));
+    return cg_on_workspace(A, b, x, max_iter, rtol, iters, rel_resid, s, vecs, true);
+}
+
+// ------------------------------------------------------------------------
+// The allocation-free variant: the workspace is this file-scope device array,
+// one per GPU the library runs on (reserved when the code object is loaded
+// there and held until the process ends).  Its device address is looked up
+// once per device with that device current; host code uses only that
+// address, never the array's name (a host-side stand-in).
+// ------------------------------------------------------------------------
+constexpr int64_t kCgNoAllocFloats =
+    4 * static_cast<int64_t>(SPMV_CG_NOALLOC_MAX_ROWS) + 2 * 4 * kDotBlocks;
+static __device__ __align__(256) float scratch[kCgNoAllocFloats];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+float *g_scratch_ptr[kMaxDevices] = {};
+
+spmv_status device_scratch(int device, float **out) {
+    if (device < 0 || device >= kMaxDevices) return SPMV_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[device]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return SPMV_ERR_HIP;
+        }
+        g_scratch_ptr[device] = static_cast<float *>(p);
+    }
+    *out = g_scratch_ptr[device];
+    return SPMV_OK;
+}
+}  // namespace
+
+spmv_status conjugate_gradient_noalloc(const spmv_handle *A, const float *b, float *x,
+                                       int32_t max_iter, float rtol, int32_t *iters,
+                                       float *rel_resid, hipStream_t s) {
+    if (A->stats.num_rows > SPMV_CG_NOALLOC_MAX_ROWS) return SPMV_ERR_TOO_LARGE;
+    static_assert(2 * 4 * kDotBlocks % 64 == 0, "partials keep 256-byte alignment");
+    float *ws = nullptr;
+    SPMV_TRY(device_scratch(A->device, &ws));
+    return cg_on_workspace(A, b, x, max_iter, rtol, iters, rel_resid, s, ws, false);
 }
 
 }  // namespace spmv

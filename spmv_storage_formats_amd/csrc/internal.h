@@ -361,9 +361,14 @@ spmv_status build_coo_blocked(spmv_handle *h, int32_t R, int32_t C, int32_t nnz,
                               hipStream_t s, Scratch &scratch);
 hipError_t launch_coo_blocked(const spmv_handle *h, const float *x, float *y, hipStream_t s);
 
-// cg.hip: conjugate gradient on a square handle (host-synchronous)
+// cg.hip: conjugate gradient on a square handle (host-synchronous); the
+// allocation-free variant uses a static per-device workspace and direct
+// launches (the caller must be on the handle's device)
 spmv_status conjugate_gradient(const spmv_handle *A, const float *b, float *x, int32_t max_iter,
                                float rtol, int32_t *iters, float *rel_resid, hipStream_t s,
                                Scratch &scratch);
+spmv_status conjugate_gradient_noalloc(const spmv_handle *A, const float *b, float *x,
+                                       int32_t max_iter, float rtol, int32_t *iters,
+                                       float *rel_resid, hipStream_t s);
 
 }  // namespace spmv

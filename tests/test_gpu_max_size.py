@@ -1,7 +1,8 @@
 """The largest matrix the C ABI accepts: nnz = 2^31 - 1 = INT32_MAX, 2^26 rows of
 32 entries (the last of 31), columns spread over all of x (synth.BandMatrix).
 
-Every format that fits int32 slots is built on the device and its y is checked
+Every format that fits int32 slots (and blocked COO, whose slot indices are 64-bit)
+is built on the device and its y is checked
 against the oracle on 4,000 sampled rows (plus the first and last rows and the
 middle), to the same row bound as every other parity test.  ELL (2^31 slots)
 and sectioned ELL are refused with SPMV_ERR_TOO_LARGE, and an automatic build
@@ -54,7 +55,8 @@ def big():
 
 @pytest.mark.parametrize("fmt,kw", [("csr_scalar", {}), ("csr_vector", {}), ("csr_merge", {}),
                                     ("coo_segmented", {}), ("coo_atomic", {}),
-                                    ("hyb", {"hyb_width": 31}), ("jds", {}), ("auto", {})])
+                                    ("hyb", {"hyb_width": 31}), ("jds", {}), ("coo_blocked", {}),
+                                    ("auto", {})])
 def test_max_size_parity(big, fmt, kw):
     b = big
     print(f"max-size {fmt}", flush=True)
@@ -63,6 +65,9 @@ def test_max_size_parity(big, fmt, kw):
         assert h.format == "csr_vector" and h.info["lanes_per_row"] == 32
     if fmt == "hyb":
         assert h.info["tail_nnz"] == b["m"].num_rows - 1
+    if fmt == "coo_blocked":
+        # 2^26 rows in 4096 blocks, x of 256 MiB in 8 slices; slots past 2^31
+        assert h.info["col_blocks"] == 8 and h.info["groups"] * 64 >= b["m"].nnz
     y = b["y0"].clone()
     h.run(b["x"], y)
     yg = y[b["rows_t"]].cpu().numpy()

@@ -8,7 +8,8 @@ library).
 HIP events after a 1 GiB cache flush (median of 9): random indices, indices
 sorted inside each 64-lane group with mean spacing 16 (two lanes per 128-byte
 line) or 4 (eight per line), and consecutive indices; from an x of 2 MiB (one
-XCD's L2 keeps it) and of 16 MiB (more than an L2).
+XCD's L2 keeps it with room to spare), 4 MiB (the size of an L2), 8 MiB and
+16 MiB.
 ``lds_rates``: random-address float adds into LDS, 512 workgroups of 1024
 threads x 2048 adds each, by the hardware float atomic, a compare-and-swap
 loop and the integer atomic; reported as GPU clocks per wave instruction per
@@ -82,7 +83,7 @@ def gather_rates(torch, dev, flush, n=64 << 20):
     out = torch.empty(int(lib.mb_gather_out_len(n)), device=dev)
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     res = {}
-    for mib in (2, 16):
+    for mib in (2, 4, 8, 16):
         X = (mib << 20) // 4
         x = torch.rand(X, device=dev, generator=gen)
         for name, idx in _patterns(torch, dev, n, X, gen).items():

@@ -86,6 +86,7 @@ def test_device_rates(line):
     g = line["device_rates"]["gather"]["rates"]
     # gathers that share cache lines run faster than random ones
     assert g["x2MiB_sorted_8_per_line"]["g_per_s"] > g["x2MiB_random"]["g_per_s"]
+    assert {f"x{m}MiB_random" for m in (2, 4, 8, 16)} <= set(g)
     lds = line["device_rates"]["lds"]
     assert set(lds) == {"lds_float_atomic_add", "cas_float_add", "lds_integer_atomic_add"}
 

@@ -526,6 +526,7 @@ spmv_status build_sliced(spmv_handle **out, spmv_format fmt, int32_t R, int32_t 
     }
     if (h->parts.empty()) h->format = SPMV_ELL;
     SPMV_HIP(hipStreamSynchronize(s));
+    if (o.max_bytes > 0 && h->device_bytes > o.max_bytes) return SPMV_ERR_TOO_LARGE;
     *out = h.release();
     return SPMV_OK;
 }
@@ -652,6 +653,10 @@ spmv_status build_csr_impl(spmv_handle **out, spmv_format fmt, int32_t R, int32_
         return SPMV_ERR_INVALID_ARG;
     }
     SPMV_HIP(hipStreamSynchronize(s));
+    // the estimate checked before building can fall short (blocked COO's wide
+    // groups, JDS tiles at a small depth): the budget bounds what the handle
+    // actually keeps, so a larger result is freed and refused
+    if (o.max_bytes > 0 && h->device_bytes > o.max_bytes) return SPMV_ERR_TOO_LARGE;
     *out = h.release();
     return SPMV_OK;
 }

@@ -418,6 +418,56 @@ def test_too_large_and_budget(dev):
     assert h.info["device_bytes"] <= 1 << 30
 
 
+def _one_long_row():
+    """200 rows: row 0 holds 5,000 entries, the others one each."""
+    rng = np.random.default_rng(5)
+    lens = np.ones(200, np.int64)
+    lens[0] = 5000
+    rp = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    ci = np.concatenate([np.sort(rng.choice(8000, l, replace=False)) for l in lens]).astype(np.int32)
+    return rp, ci, rng.standard_normal(ci.size).astype(np.float32), 8000
+
+
+@pytest.mark.parametrize("case", ALL_FORMATS + ["sliced", "coo_blocked_wide", "jds_depth1"])
+def test_budget_bounds_the_built_arrays(dev, case):
+    """opts.max_bytes bounds the device arrays a handle keeps: with a budget one
+    byte below what the same build keeps, the build is refused with
+    SPMV_ERR_TOO_LARGE; a build that succeeds under a budget keeps no more than
+    it.  The wide-group blocked build and JDS at depth 1 are the cases whose
+    size the pre-build estimate cannot see (wide groups; tiles per jagged
+    column)."""
+    kw = {}
+    fmt = case
+    if case == "coo_blocked_wide":
+        w = _wide_mix()
+        rp, ci, v, C = w.row_ptrs, w.col_idx, w.values, w.num_cols
+        fmt = "coo_blocked"
+    elif case == "jds_depth1":
+        rp, ci, v, C = _one_long_row()
+        fmt, kw = "jds", {"jds_depth": 1}
+    else:
+        w = W("c3s" if case == "ell_xtile" else "c2s")
+        rp, ci, v, C = w.row_ptrs, w.col_idx, w.values, w.num_cols
+        if case == "sliced":
+            fmt, kw = "csr_merge", {"col_blocks": 3}
+    t = [torch.from_numpy(a).to(dev) for a in (rp, ci, v)]
+    h = spmv.build(fmt, *t, C, **kw)
+    need = h.info["device_bytes"]
+    if case == "coo_blocked_wide":
+        assert h.info["wide_groups"] > 0
+    h.close()
+    with pytest.raises(spmv.SpmvError) as ei:
+        spmv.build(fmt, *t, C, max_bytes=need - 1, **kw)
+    assert ei.value.name == "SPMV_ERR_TOO_LARGE"
+    try:
+        h = spmv.build(fmt, *t, C, max_bytes=need, **kw)
+    except spmv.SpmvError as e:   # the pre-build estimate may be an overestimate
+        assert e.name == "SPMV_ERR_TOO_LARGE"
+    else:
+        assert h.info["device_bytes"] <= need
+        h.close()
+
+
 # ------------------------------------------------------------------ COO input
 
 def _coo_of(w, rng, shuffle):
@@ -582,6 +632,8 @@ def _wide_mix():
     """2,000 rows over 10M columns: half the rows keep their columns in a
     narrow band (groups spanning < 2^16 columns), the rest scatter them over
     all of x (groups spanning more: wide groups with full columns)."""
+    if "wide_mix" in _cache:
+        return _cache["wide_mix"]
     rng = np.random.default_rng(77)
     R, C = 2000, 10_000_000
     lens = rng.integers(1, 9, size=R)
@@ -591,9 +643,11 @@ def _wide_mix():
         cols.append(np.sort(rng.choice(np.arange(lo, hi), l, replace=False)))
     ci = np.concatenate(cols).astype(np.int32)
     rp = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    return synth.Workload("wide_mix", R, C, rp, ci, rng.uniform(-1, 1, ci.size).astype(np.float32),
-                          rng.uniform(-1, 1, C).astype(np.float32),
-                          rng.uniform(-1, 1, R).astype(np.float32))
+    _cache["wide_mix"] = synth.Workload("wide_mix", R, C, rp, ci,
+                                        rng.uniform(-1, 1, ci.size).astype(np.float32),
+                                        rng.uniform(-1, 1, C).astype(np.float32),
+                                        rng.uniform(-1, 1, R).astype(np.float32))
+    return _cache["wide_mix"]
 
 
 @pytest.mark.parametrize("S", [1, 8])
@@ -1180,12 +1234,12 @@ def test_build_destroy_cycles_release_device_memory(dev):
 
 
 def test_concurrent_host_threads_and_streams(dev):
-    """Four host threads each build a handle and run it 20 times on their own
+    """Five host threads each build a handle and run it 20 times on their own
     stream (ctypes releases the GIL during library calls); every result is
     checked against the oracle."""
     import threading
-    names = ["c1s", "c2s", "c3s", "c4s"]
-    fmts = ["ell", "csr_merge", "sell", "hyb"]
+    names = ["c1s", "c2s", "c3s", "c4s", "c5s"]
+    fmts = ["ell", "csr_merge", "sell", "hyb", "coo_blocked"]
     results, errors = {}, []
     inputs = {n: to_dev(W(n), dev) for n in names}
     torch.cuda.synchronize()   # the copies above ran on the default stream

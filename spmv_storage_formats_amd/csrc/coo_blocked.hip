@@ -36,7 +36,8 @@
 // Kernel: one workgroup per chunk (slice k's chunks on the XCDs k*8/S ..
 // (k+1)*8/S - 1, so each XCD's L2 holds one slice of x); the block's row
 // partials live in LDS; each wave takes groups, gathers x, sums runs of equal
-// codes with a DPP segmented scan and adds each run's total to its partial:
+// codes with a DPP segmented scan (skipped, by one ballot, when every row of
+// the group holds a single lane) and adds each run's total to its partial:
 // hot rows by a plain add into the wave's own slot, other rows by a
 // compare-and-swap loop (an LDS float atomic add costs ~190 clocks per wave
 // instruction on gfx950, a CAS ~28, a plain read-modify-write ~16); finally
@@ -179,12 +180,16 @@ __global__ __launch_bounds__(kThreads) void k_bc_fill(int64_t G, int32_t nch,
 
 // -------------------------------------------------------------------- SpMV
 
+// One step of a segmented inclusive scan by row code: lane l adds the partial
+// of the lane CTRL reads from when that lane holds the same row.  Keys are the
+// codes plus one, so a lane outside the DPP pattern (reading 0) never matches.
 template <int CTRL, int RMASK>
-__device__ inline void bc_seg_step(int32_t r, float &p) {
-    const int32_t ru = __builtin_amdgcn_update_dpp(INT32_MIN, r, CTRL, RMASK, 0xF, false);
+__device__ inline void bc_seg_step(uint32_t k, float &p) {
+    const uint32_t ku = static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(k), CTRL, RMASK, 0xF, true));
     const float pu = __builtin_bit_cast(
-        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, p), CTRL, RMASK, 0xF, false));
-    if (ru == r) p += pu;
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, p), CTRL, RMASK, 0xF, true));
+    if (ku == k) p += pu;
 }
 
 __device__ inline void lds_cas_add(float *a, float v) {
@@ -245,16 +250,24 @@ __global__ __launch_bounds__(kBcThreads) void k_coo_blocked(
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int32_t r = static_cast<int32_t>(w[u] >> 16);
+            const uint32_t r = w[u] >> 16;
+            // lane l + 1's code (wave_shl:1; lane 63 reads all ones, no code)
+            const uint32_t rn = static_cast<uint32_t>(
+                __builtin_amdgcn_update_dpp(-1, static_cast<int>(r), 0x130, 0xF, 0xF, false));
+            const bool real = r != kBcPadCode;
             float q = p[u];
-            bc_seg_step<0x111, 0xF>(r, q);   // row shr 1, 2, 4, 8
-            bc_seg_step<0x112, 0xF>(r, q);
-            bc_seg_step<0x114, 0xF>(r, q);
-            bc_seg_step<0x118, 0xF>(r, q);
-            bc_seg_step<0x142, 0xA>(r, q);   // row_bcast:15
-            bc_seg_step<0x143, 0xC>(r, q);   // row_bcast:31
-            const int32_t rn = __shfl_down(r, 1);
-            if (r != static_cast<int32_t>(kBcPadCode) && (lane == kWave - 1 || rn != r)) {
+            // the scan only when some row holds two lanes of the group
+            if (__builtin_amdgcn_ballot_w64(real && rn == r) != 0) {
+                const uint32_t k = r + 1;
+                bc_seg_step<0x111, 0xF>(k, q);   // row_shr:1, 2, 4, 8
+                bc_seg_step<0x112, 0xF>(k, q);
+                bc_seg_step<0x114, 0xF>(k, q);
+                bc_seg_step<0x118, 0xF>(k, q);
+                bc_seg_step<0x142, 0xA>(k, q);   // row_bcast:15
+                bc_seg_step<0x143, 0xC>(k, q);   // row_bcast:31
+            }
+            // the last lane of each run adds the run's total to its row
+            if (real && rn != r) {
                 if (r >= kBcRows) mine[r - kBcRows] += q;   // this wave's own slot
                 else lds_cas_add(&part[r], q);
             }

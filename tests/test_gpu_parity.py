@@ -688,6 +688,40 @@ def test_blocked_hot_rows(dev):
     assert_rows(run_once(h, x, y0), y_ref, bound, "hot rows")
 
 
+@pytest.mark.parametrize("S", [1, 2])
+def test_blocked_scan_runs(dev, S):
+    """Every row's entries sit in a column range of their own, so the column
+    order of a segment is row order and each group of 64 lanes holds runs of
+    one row: lengths 1..64 at every lane offset, runs that cross the 16-lane
+    DPP rows (lanes 15/16, 31/32, 47/48) and runs that fill whole groups, plus
+    hot rows (longer than 64 * S) whose runs go to per-wave slots.  Groups of
+    singletons (the scan skipped) sit beside groups of long runs.  Bit-exact
+    arrays, y within the bound."""
+    rng = np.random.default_rng(123 + S)
+    R = 6000
+    lens = rng.integers(1, 65, size=R)
+    lens[1000:2000] = 1                                # a stretch of one-entry rows
+    lens[rng.choice(R, 50, replace=False)] = rng.integers(64 * S + 1, 400, size=50)
+    starts = np.concatenate([[0], np.cumsum(lens + 3)[:-1]])
+    C = int(starts[-1] + lens[-1] + 3)
+    ci = np.concatenate([np.arange(a, a + l) for a, l in zip(starts, lens)]).astype(np.int32)
+    rp = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    w = synth.Workload("scan_runs", R, C, rp, ci, rng.uniform(-1, 1, ci.size).astype(np.float32),
+                       rng.uniform(-1, 1, C).astype(np.float32),
+                       rng.uniform(-1, 1, R).astype(np.float32))
+    h = build("coo_blocked", w, dev, col_blocks=S)
+    assert h.info["wide_groups"] == 0 and (h.array("bc_hot") >= 0).sum() > 0
+    check_builder(h, w)
+    codes = (h.array("bc_pk") >> 16).reshape(-1, 64)
+    real = codes != 0xFFFF
+    same = (codes[:, 1:] == codes[:, :-1]) & real[:, 1:]
+    assert (~same.any(axis=1)).any() and same.all(axis=1).any()   # both kinds of group
+    assert same[:, [14, 30, 46]].any(axis=0).all()                  # runs across DPP rows
+    y_ref, bound = oracle.spmv_csr(w.row_ptrs, w.col_idx, w.values, w.x, w.y)
+    _, _, _, x, y0 = to_dev(w, dev)
+    assert_rows(run_once(h, x, y0), y_ref, bound, f"scan runs S={S}")
+
+
 def _slices(w, K):
     """The CSR arrays of the K column slices (entries with column in
     [k*ceil(C/K), (k+1)*ceil(C/K)), row order kept), built with numpy."""

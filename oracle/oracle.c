@@ -12,6 +12,10 @@
  *   [P3] "SpMV storage-format choice and performance comparison" (CUDA tuning
  *        article), numbered sections
  *   [P5] SpGEMM/AIA article, section 5.3 "common problems" (input checks)
+ *   [INTRO] "Introduction to sparse computing and locating performance
+ *        bottlenecks" article, sections on the three core challenges and on
+ *        building the overall picture (irregular x gathers, memory and
+ *        parallel efficiency)
  *
  * Arithmetic: products of two fp32 numbers are exact in fp64 (24+24 < 53
  * significand bits); sums are taken in fp64 in row order.  Values are moved by
@@ -29,6 +33,10 @@
  *   - The selector's comparison operators (lost from P3 4.3) are restored as
  *     W*R <= 2*nnz -> ELL; nnz < 10*R -> COO; W*R > 5*nnz -> HYB; else CSR,
  *     with the HYB width/budget extension described at orc_select().
+ *   - ELL with x tiles, blocked COO and the automatic build's storage rules
+ *     are encodings and build-time rules, not formulas of the pages: each is
+ *     written out as a definition at orc_csr_to_ell_xtile(), orc_coo_blocked()
+ *     and orc_select_build().
  */
 #include <math.h>
 #include <stdint.h>

@@ -229,24 +229,43 @@ __global__ __launch_bounds__(kBcThreads) void k_coo_blocked(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     float *mine = priv + wave * kBcHot;
     for (int64_t gb = g0 + wave; gb < g1; gb += kBcWaves * U) {
+        // Every load below is unconditional and in bounds, so the U groups'
+        // stream loads, then their U gathers, are all in flight at once (a
+        // gather under a divergent branch would be waited for before the next
+        // is issued).  A group past the chunk's end re-reads the chunk's last
+        // group and is then marked as padding; a padding slot's offset is 0,
+        // so it gathers its group's base column (a real column), or column 0
+        // in a wide group.
         uint32_t w[U];
         float v[U];
         int32_t bs[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t g = gb + u * kBcWaves;
-            const bool ok = g < g1;
-            bs[u] = ok ? base[g] : 0;
-            w[u] = ok ? ld_nt(pk + g * kWave + lane) : (kBcPadCode << 16);
-            v[u] = ok ? ld_nt(val + g * kWave + lane) : 0.f;
+            const int64_t g = min(gb + u * kBcWaves, g1 - 1);
+            bs[u] = base[g];
+            w[u] = ld_nt(pk + g * kWave + lane);
+            v[u] = ld_nt(val + g * kWave + lane);
         }
+        int32_t cx[U];
+        bool wide = false;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            cx[u] = bs[u] + static_cast<int32_t>(w[u] & 0xFFFFu);
+            wide |= bs[u] < 0;
+        }
+        if (wide) {   // wave-uniform and rare: groups spanning more than 2^16 columns
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (bs[u] < 0) cx[u] = ld_nt(wide_col + static_cast<int64_t>(-bs[u] - 1) * kWave + lane);
+        }
+        float xv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) xv[u] = x[cx[u]];
         float p[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t g = gb + u * kBcWaves;
-            int32_t cx = bs[u] + static_cast<int32_t>(w[u] & 0xFFFFu);
-            if (bs[u] < 0) cx = ld_nt(wide_col + static_cast<int64_t>(-bs[u] - 1) * kWave + lane);
-            p[u] = (w[u] >> 16) != kBcPadCode && g < g1 ? v[u] * x[cx] : 0.f;
+            if (gb + u * kBcWaves >= g1) w[u] = kBcPadCode << 16;   // past the chunk
+            p[u] = (w[u] >> 16) != kBcPadCode ? v[u] * xv[u] : 0.f;
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {

@@ -23,6 +23,18 @@ constexpr int kThreads = 256;
 
 __device__ inline void atomic_add_f32(float *p, float v) { unsafeAtomicAdd(p, v); }
 
+// x[c], kept only where the lane's condition holds.  c must be a column on
+// every lane (the kernels set it to 0 where a lane has no entry), so the load
+// needs no per-lane branch: a branch around a gather makes the wave wait for
+// it before the next one is issued, while unconditional gathers all go out
+// before the first is used.  The condition goes through a lane mask (ballot,
+// then inverse ballot), since a select on a plain comparison whose operand is
+// a just-loaded value is turned back into a branch around the load.
+__device__ inline float gather_kept(const float *__restrict__ x, int32_t c, bool keep) {
+    const float g = x[c];
+    return __builtin_amdgcn_inverse_ballot_w64(__builtin_amdgcn_ballot_w64(keep)) ? g : 0.f;
+}
+
 __device__ inline void lds_add_f32(float *p, float v) {
     __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
@@ -73,7 +85,7 @@ __global__ __launch_bounds__(kThreads) void k_coo_atomic(int32_t nnz,
     }
     float xv[RUN];
 #pragma unroll
-    for (int k = 0; k < RUN; ++k) xv[k] = base + k < nnz ? x[c[k]] : 0.f;
+    for (int k = 0; k < RUN; ++k) xv[k] = gather_kept(x, c[k], base + k < nnz);
 #pragma unroll
     for (int k = 0; k < RUN; ++k)
         if (base + k < nnz) atomic_add_f32(&y[r[k]], v[k] * xv[k]);
@@ -127,7 +139,8 @@ __global__ __launch_bounds__(kThreads) void k_coo_segmented(int32_t nnz,
         vv[it] = valid ? ld_nt(val + i) : 0.f;
     }
 #pragma unroll
-    for (int it = 0; it < kSegIters; ++it) pp[it] = rr[it] != INT32_MAX ? vv[it] * x[cc[it]] : 0.f;
+    for (int it = 0; it < kSegIters; ++it)   // vv = 0 where there is no entry
+        pp[it] = vv[it] * gather_kept(x, cc[it], rr[it] != INT32_MAX);
     int carry_row = INT32_MAX;
     float carry = 0.f;
 #pragma unroll
@@ -606,7 +619,7 @@ __global__ __launch_bounds__(kThreads) void k_jds(int32_t R, int32_t ntiles, int
         load(tb + U, cn, vn);
         float xv[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) xv[u] = (tb + u < t1 && tb + u < len) ? x[c[u]] : 0.f;
+        for (int u = 0; u < U; ++u) xv[u] = gather_kept(x, c[u], tb + u < t1 && tb + u < len);
 #pragma unroll
         for (int u = 0; u < U; ++u) sum += v[u] * xv[u];
 #pragma unroll
@@ -673,7 +686,7 @@ __global__ __launch_bounds__(kThreads) void k_sell(int32_t R, int32_t ntiles, in
         load(tb + U, cn, vn);
         float xv[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) xv[u] = (tb + u < t1 && tb + u < len) ? x[c[u]] : 0.f;
+        for (int u = 0; u < U; ++u) xv[u] = gather_kept(x, c[u], tb + u < t1 && tb + u < len);
 #pragma unroll
         for (int u = 0; u < U; ++u) sum += v[u] * xv[u];
 #pragma unroll

@@ -51,13 +51,16 @@ constexpr int kXtileAutoRows = 64 * kTileRows;
 // workgroup's threads and groups in flight per wave, and the x slice size of
 // the automatic slice count (2 MiB: an XCD's L2 keeps room for the stream).
 // Measured on the power-law 4M-row matrix: 16384 rows 278-282 us against
-// 32768 rows 291 us; 1024 threads x 4 groups per wave.
+// 32768 rows 291 us; 1024 threads x 6 groups per wave, whose loads and
+// gathers are all in flight together (4, 5, 6, 7, 8 groups: 287, 283, 273,
+// 276, 277 us; more registers than 8 groups take would leave room for only
+// one workgroup per CU).
 constexpr int kBcRows = 16384;
 constexpr int kBcChunk = 65536;
 constexpr int kBcHot = 32;
 constexpr int kBcHotPerSlice = 64;
 constexpr int kBcThreads = 1024;
-constexpr int kBcUnroll = 4;
+constexpr int kBcUnroll = 6;
 constexpr int64_t kBcSliceBytes = 2 << 20;
 
 // Validation flags written by the analysis kernels.

@@ -66,6 +66,12 @@ typedef enum spmv_status {
     SPMV_ERR_DEVICE = 8        /* handle used on another device than its own    */
 } spmv_status;
 
+/* Blocked COO layout constants (SPMV_COO_BLOCKED): rows per row block, whose
+ * partials one workgroup keeps in LDS, and entries per chunk, one workgroup's
+ * work. */
+#define SPMV_BC_BLOCK_ROWS 32768
+#define SPMV_BC_CHUNK_ENTRIES 131072
+
 /* Storage formats / kernels.  SPMV_AUTO lets the selector choose. */
 typedef enum spmv_format {
     SPMV_AUTO = 0,
@@ -95,18 +101,18 @@ typedef enum spmv_format {
                                (sum over blocks of the tile sizes): each x word staged
                                serves two gathers or more, as on banded 3-D stencils.    */
     SPMV_COO_BLOCKED = 11   /* blocked COO [INTRO x blocking and split by nonzeros; CHOICE
-                               3.2 segmented COO]: rows in blocks of 16384, columns in S
+                               3.2 segmented COO]: rows in blocks of SPMV_BC_BLOCK_ROWS, columns in S
                                x slices (S = opts.col_blocks in {1,2,4,8}; 0: the smallest
                                power of two that keeps a slice of x within 2 MiB, at most
                                8); the entries of each (slice, block) are ordered by
-                               column, cut into chunks of 65536 and groups of 64, and each
+                               column, cut into chunks of SPMV_BC_CHUNK_ENTRIES and groups of 64, and each
                                group is reordered by row so that runs of one row are
                                neighbouring lanes.  Neighbouring lanes therefore gather
                                neighbouring x words, and row partials are summed in LDS.
                                SPMV_AUTO takes it (with the automatic S) when the columns
                                are scattered (col_spread * 8 > C), x exceeds 4 MiB and a
                                block holds at least one entry per 128-byte line of x on
-                               average (32 * nnz * min(R, 16384) >= R * C).            */
+                               average (32 * nnz * min(R, SPMV_BC_BLOCK_ROWS) >= R * C). */
 } spmv_format;
 
 typedef struct spmv_opts {
@@ -167,8 +173,8 @@ typedef struct spmv_info {
     int64_t device_bytes;  /* device memory owned by the handle           */
     int64_t groups;        /* blocked COO: groups of 64 slots             */
     int64_t wide_groups;   /* blocked COO: groups whose columns span > 65535 */
-    int32_t block_rows;    /* blocked COO: rows per block (16384)         */
-    int32_t chunk_entries; /* blocked COO: entries per chunk (65536)      */
+    int32_t block_rows;    /* blocked COO: SPMV_BC_BLOCK_ROWS             */
+    int32_t chunk_entries; /* blocked COO: SPMV_BC_CHUNK_ENTRIES          */
     int32_t hot_slots;     /* blocked COO: hot rows per block (32)        */
     int32_t hot_min_len;   /* blocked COO: rows this long or longer may be hot (64*S+1) */
 } spmv_info;
@@ -205,8 +211,9 @@ typedef enum spmv_array {
                               the entry's column, padding 0.  Values and row lengths:
                               SPMV_A_ELL_VAL, SPMV_A_ELL_NNZ.                       */
     /* blocked COO: segment k*B + b holds the entries of x slice k and row block b
-       (B = ceil(R/16384) blocks) ordered by column, ties in CSR order; chunks are
-       its consecutive runs of 65536 entries, groups a chunk's runs of 64.          */
+       (B = ceil(R/SPMV_BC_BLOCK_ROWS) blocks) ordered by column, ties in CSR order;
+       chunks are its consecutive runs of SPMV_BC_CHUNK_ENTRIES entries, groups a
+       chunk's runs of 64.                                                            */
     SPMV_A_BC_CHUNK_GRP = 22,  /* int32 [chunks+1] first group of chunk c          */
     SPMV_A_BC_CHUNK_BLK = 23,  /* int32 [chunks]   row block of chunk c             */
     SPMV_A_BC_SLICE_CHUNK = 24,/* int32 [S+1]      first chunk of x slice k         */
@@ -217,8 +224,9 @@ typedef enum spmv_array {
                                   -(w+1) if its columns span more than 65535 (wide
                                   group w)                                           */
     SPMV_A_BC_PK = 27,         /* uint32 [groups*64] slot g*64+i: code << 16 | column
-                                  - base (0 in wide groups); code = row - 16384*b, or
-                                  16384 + h for hot row h; the group's entries
+                                  - base (0 in wide groups); code = row - RB*b, or
+                                  RB + h for hot row h (RB = SPMV_BC_BLOCK_ROWS); the
+                                  group's entries
                                   reordered by code, ties in column order; padding
                                   0xFFFF0000                                         */
     SPMV_A_BC_VAL = 28,        /* fp32 [groups*64]  values, padding +0.0f            */

@@ -318,7 +318,7 @@ def csr_to_coo_blocked(row_ptrs, col_idx, values, num_cols, slices, block_rows, 
     return out
 
 
-def select_build(row_ptrs, col_idx, num_cols, block_rows=16384):
+def select_build(row_ptrs, col_idx, num_cols, block_rows):
     """The automatic build's (format name, K, lanes, x slices) for this matrix."""
     rp = _i32(row_ptrs)
     ci = _i32(col_idx)

@@ -50,13 +50,13 @@ constexpr int kXtileAutoRows = 64 * kTileRows;
 // and the length above which a row is hot (kBcHotPerSlice * slices), one
 // workgroup's threads and groups in flight per wave, and the x slice size of
 // the automatic slice count (2 MiB: an XCD's L2 keeps room for the stream).
-// Measured on the power-law 4M-row matrix: 16384 rows 278-282 us against
-// 32768 rows 291 us; 1024 threads x 6 groups per wave, whose loads and
-// gathers are all in flight together (4, 5, 6, 7, 8 groups: 287, 283, 273,
-// 276, 277 us; more registers than 8 groups take would leave room for only
-// one workgroup per CU).
-constexpr int kBcRows = 16384;
-constexpr int kBcChunk = 65536;
+// Measured on the power-law 4M-row matrix and the 2M-row skewed one, with
+// every group's loads and gathers in flight together: 16384-row blocks in
+// chunks of 65536 with 6 groups per wave (two workgroups per CU) 274 and 107
+// us; 32768-row blocks in chunks of 131072 (one workgroup per CU, twice the
+// entries per x line) with 6, 8, 10 groups per wave 267, 272, 274 and 97 us.
+constexpr int kBcRows = SPMV_BC_BLOCK_ROWS;
+constexpr int kBcChunk = SPMV_BC_CHUNK_ENTRIES;
 constexpr int kBcHot = 32;
 constexpr int kBcHotPerSlice = 64;
 constexpr int kBcThreads = 1024;

@@ -23,6 +23,18 @@ def test_exports_every_declared_function(lib):
     assert not missing, missing
 
 
+def test_binding_constants_match_the_header():
+    """The binding's copies of the header's layout and limit constants."""
+    import os
+    import re
+    hdr = open(os.path.join(os.path.dirname(spmv.__file__), "..", "include", "spmv.h")).read()
+    defs = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define (SPMV_\w+) (\d+)", hdr)}
+    assert defs["SPMV_BC_BLOCK_ROWS"] == spmv.BC_BLOCK_ROWS
+    assert defs["SPMV_BC_CHUNK_ENTRIES"] == spmv.BC_CHUNK_ENTRIES
+    assert defs["SPMV_CG_NOALLOC_MAX_ROWS"] == spmv.CG_NOALLOC_MAX_ROWS
+    assert spmv.BC_BLOCK_ROWS + 32 < 0xFFFF   # row codes and hot codes fit 16 bits
+
+
 def test_library_is_gfx950_only():
     """The shared library carries a gfx950 code object and no other target."""
     data = open(spmv.library_path(), "rb").read()

@@ -566,7 +566,7 @@ def test_full_size_parity(dev, name, fmt):
     if fmt == "auto":
         # the automatic build's whole decision (selector, x tiles, blocked COO
         # and its slice count) equals the oracle's written-out rule
-        f, K, L, S = oracle.select_build(w.row_ptrs, w.col_idx, w.num_cols)
+        f, K, L, S = oracle.select_build(w.row_ptrs, w.col_idx, w.num_cols, spmv.BC_BLOCK_ROWS)
         assert (h.format, h.info["hyb_width"], h.info["lanes_per_row"],
                 h.info["col_blocks"]) == (f, K, L, S)
         # the 2-D stencil and the random 5-per-row matrix: ELL; the 3-D
@@ -668,11 +668,12 @@ def test_blocked_hot_rows(dev):
     rows get per-wave partials, the rest compare-and-swap.  Bit-exact arrays,
     y within the bound."""
     rng = np.random.default_rng(91)
-    R, C = 20000, 3_000_000
+    RB = spmv.BC_BLOCK_ROWS
+    R, C = RB + 3616, 3_000_000
     lens = rng.integers(0, 8, size=R)
-    long0 = rng.choice(16384, 40, replace=False)
+    long0 = rng.choice(RB, 40, replace=False)
     lens[long0] = rng.choice([100, 150, 150, 200, 300], size=40)
-    lens[[17000, 18000, 19999]] = [30000, 70, 500]
+    lens[[RB + 616, RB + 1616, R - 1]] = [30000, 70, 500]
     cols = [np.sort(rng.choice(C, l, replace=False)) if l else np.zeros(0, np.int64) for l in lens]
     ci = np.concatenate(cols).astype(np.int32)
     rp = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)

@@ -889,7 +889,7 @@ def _spread(rp, ci, C):
 
 def test_select_build_fig14_1():
     w = _fig()
-    assert oracle.select_build(w.row_ptrs, w.col_idx, 4) == ("ell", 0, 0, 1)
+    assert oracle.select_build(w.row_ptrs, w.col_idx, 4, 16384) == ("ell", 0, 0, 1)
 
 
 def test_select_build_blocked_branch():
@@ -900,7 +900,21 @@ def test_select_build_blocked_branch():
     R, C = 1 << 16, 1 << 21
     rp, ci = _csr_random(rng, R, C, 16)
     assert _spread(rp, ci, C) * 8 > C
-    assert oracle.select_build(rp, ci, C) == ("coo_blocked", 0, 0, 4)
+    assert oracle.select_build(rp, ci, C, 16384) == ("coo_blocked", 0, 0, 4)
+
+
+def test_select_build_block_rows_term():
+    """The min(R, RT) term: 65,536 rows x 2^21 columns, 3 random columns per
+    row.  32 * nnz * RT >= R * C reads 32 * 3 * RT >= 2^21: true for RT =
+    32,768 (blocked COO, 4 slices), false for RT = 16,384.  Then x slices:
+    8 MiB of x gives K = 4, and 3 * 4 * 65,536 > nnz = 196,608 halves it to
+    K = 2 (the floor)."""
+    rng = np.random.default_rng(4)
+    R, C = 1 << 16, 1 << 21
+    rp, ci = _csr_random(rng, R, C, 3)
+    assert _spread(rp, ci, C) * 8 > C
+    assert oracle.select_build(rp, ci, C, 32768) == ("coo_blocked", 0, 0, 4)
+    assert oracle.select_build(rp, ci, C, 16384) == ("csr_merge", 0, 0, 2)
 
 
 @pytest.mark.parametrize("nnz,slices", [(98304, 8), (98303, 4)])
@@ -915,7 +929,7 @@ def test_select_build_slice_halving_boundary(nnz, slices):
     lens[0] -= 98304 - nnz
     rp, ci = _csr_random(rng, R, C, lens)
     assert rp[-1] == nnz and 32 * nnz * R < R * C and _spread(rp, ci, C) * 8 > C
-    assert oracle.select_build(rp, ci, C) == ("csr_merge", 0, 0, slices)
+    assert oracle.select_build(rp, ci, C, 16384) == ("csr_merge", 0, 0, slices)
 
 
 def test_select_build_four_mib_x_is_not_split():
@@ -923,7 +937,7 @@ def test_select_build_four_mib_x_is_not_split():
     selector's format, one slice (16 random columns per row: ELL)."""
     rng = np.random.default_rng(3)
     rp, ci = _csr_random(rng, 20000, 1 << 20, 16)
-    assert oracle.select_build(rp, ci, 1 << 20) == ("ell", 0, 0, 1)
+    assert oracle.select_build(rp, ci, 1 << 20, 16384) == ("ell", 0, 0, 1)
 
 
 def test_select_build_x_tiles_on_stencils():
@@ -935,8 +949,8 @@ def test_select_build_x_tiles_on_stencils():
     grid lines (512 + 2 columns for 1,280 entries): x tiles."""
     w = synth.stencil27(26)
     assert w.num_rows >= 16384
-    assert oracle.select_build(w.row_ptrs, w.col_idx, w.num_cols)[0] == "ell_xtile"
+    assert oracle.select_build(w.row_ptrs, w.col_idx, w.num_cols, 16384)[0] == "ell_xtile"
     w = synth.laplacian2d(512)
-    assert oracle.select_build(w.row_ptrs, w.col_idx, w.num_cols)[0] == "ell"
+    assert oracle.select_build(w.row_ptrs, w.col_idx, w.num_cols, 16384)[0] == "ell"
     w = synth.laplacian2d(128)
-    assert oracle.select_build(w.row_ptrs, w.col_idx, w.num_cols)[0] == "ell_xtile"
+    assert oracle.select_build(w.row_ptrs, w.col_idx, w.num_cols, 16384)[0] == "ell_xtile"

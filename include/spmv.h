@@ -104,7 +104,10 @@ typedef enum spmv_format {
                                3.2 segmented COO]: rows in blocks of SPMV_BC_BLOCK_ROWS, columns in S
                                x slices (S = opts.col_blocks in {1,2,4,8}; 0: the smallest
                                power of two that keeps a slice of x within 2 MiB, at most
-                               8); the entries of each (slice, block) are ordered by
+                               8, and 8 become 4 when a 4-slice slice fits 4 MiB and the
+                               expected (row, slice) pairs, sum over rows of length k of
+                               S * (1 - (1 - 1/S)^k) in fp64, exceed 0.3 nnz: each pair is
+                               one more atomic flush of a row partial); the entries of each (slice, block) are ordered by
                                column, cut into chunks of SPMV_BC_CHUNK_ENTRIES and groups of 64, and each
                                group is reordered by row so that runs of one row are
                                neighbouring lanes.  Neighbouring lanes therefore gather

@@ -895,7 +895,11 @@ int orc_coo_blocked(int64_t R, int64_t C, int64_t nnz, const int32_t *row_ptrs,
 /*            floor(r*C/R)|); scattered = spread*8 > C; big_x = 4C > 4 MiB. */
 /*   1. scattered, big_x and 32*nnz*min(R, RT) >= R*C (a row block holds an */
 /*      entry per 128-byte line of x on average) -> blocked COO with S =    */
-/*      the smallest power of two with 4C <= S * 2 MiB, at most 8.          */
+/*      the smallest power of two with 4C <= S * 2 MiB, at most 8; then,    */
+/*      when S = 8 and 4C <= (S/2) * 4 MiB, S is halved if the expected     */
+/*      (row, slice) pairs, sum over row lengths k of hist[k] * S * (1 -    */
+/*      (1 - 1/S)^k) in fp64 with k ascending, exceed 3/10 of nnz (each     */
+/*      pair is one flush of a row partial).                                */
 /*   2. scattered and big_x otherwise -> x slices, each merge-based CSR:    */
 /*      4C <= 16 MiB: K = the smallest of 2, 4, 8 with 4C <= K * 2 MiB,     */
 /*      halved (not below 2) while 3*K*R > nnz; beyond: K = ceil(4C/4 MiB); */
@@ -933,7 +937,6 @@ int orc_select_build(int64_t R, int64_t C, int64_t nnz, const int32_t *row_ptrs,
         hist[row_ptrs[r + 1] - row_ptrs[r]]++;
     int64_t sel[3];
     orc_select(R, nnz, W, hist, 0, 0, sel);
-    free(hist);
     out[0] = sel[0];
     out[1] = sel[1];
     out[2] = sel[2];
@@ -946,12 +949,24 @@ int orc_select_build(int64_t R, int64_t C, int64_t nnz, const int32_t *row_ptrs,
         int64_t S = 1;
         while (S < 8 && 4 * C > S * (2 << 20))
             S *= 2;
+        if (S == 8 && 4 * C <= (S / 2) * (4 << 20)) {
+            double pairs = 0.0;
+            const double q = 1.0 - 1.0 / (double)S;
+            for (int64_t k = 0; k <= W; ++k) {
+                const double term = (double)hist[k] * ((double)S * (1.0 - pow(q, (double)k)));
+                pairs = pairs + term;
+            }
+            if (10.0 * pairs > 3.0 * (double)nnz)
+                S /= 2;
+        }
+        free(hist);
         out[0] = ORC_FMT_COO_BLOCKED;
         out[1] = 0;
         out[2] = 0;
         out[3] = S;
         return ORC_OK;
     }
+    free(hist);
     if (nnz > 0 && scattered && big_x) {
         int64_t K;
         if (4 * C <= 8 * (2 << 20)) {

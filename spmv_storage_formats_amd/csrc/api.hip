@@ -542,11 +542,11 @@ spmv_status build_csr_impl(spmv_handle **out, spmv_format fmt, int32_t R, int32_
     // block holds at least one entry per 128-byte line of x on average.
     int32_t bc_slices = 0;
     if (fmt == SPMV_COO_BLOCKED) {
-        bc_slices = o.col_blocks > 0 ? o.col_blocks : bc_auto_slices(C);
+        bc_slices = o.col_blocks > 0 ? o.col_blocks : bc_auto_slices(C, nnz, an.hist);
         if (bc_slices != 1 && bc_slices != 2 && bc_slices != 4 && bc_slices != 8)
             return SPMV_ERR_INVALID_ARG;
     } else if (fmt == SPMV_AUTO && o.col_blocks == 0 && bc_auto_rule(an.st)) {
-        bc_slices = bc_auto_slices(C);
+        bc_slices = bc_auto_slices(C, nnz, an.hist);
     } else {
         const int32_t K_slices = choose_col_blocks(an.st, fmt, o);
         if (K_slices > 1)
@@ -818,7 +818,7 @@ spmv_status spmv_build_tuned(spmv_handle **out, int32_t R, int32_t C, int32_t nn
             if (rep.count >= SPMV_TUNE_MAX) break;
             spmv_tune_entry &ent = rep.entry[rep.count++];
             ent.format = f;
-            ent.col_blocks = blocked ? bc_auto_slices(C) : K;
+            ent.col_blocks = blocked ? bc_auto_slices(C, nnz, an.hist) : K;
             spmv_opts oc = o;
             oc.validate = 0;
             oc.col_blocks = K;

@@ -44,6 +44,7 @@
 // every non-zero partial is added to y with a global atomic (chunks of the
 // same rows run concurrently).
 #include <algorithm>
+#include <cmath>
 #include <vector>
 
 #include "internal.h"
@@ -325,9 +326,26 @@ spmv_status owned(spmv_handle *h, T **p, int64_t count) {
 
 }  // namespace
 
-int32_t bc_auto_slices(int64_t num_cols) {
+int32_t bc_auto_slices(int64_t num_cols, int64_t nnz, const std::vector<int64_t> &hist) {
     int32_t S = 1;
     while (S < kNumXcd && 4 * num_cols > S * kBcSliceBytes) S *= 2;
+    // Each (row, slice) pair that a row touches costs one flush of its partial
+    // to y; with a row's columns spread evenly over S slices, a row of k
+    // entries touches S * (1 - (1 - 1/S)^k) of them.  When those pairs exceed
+    // 3/10 of the nonzeros (rows of 15 entries on 8 slices: 0.46, against
+    // 0.24 on the power-law matrix), 4 slices are faster than 8 while a slice
+    // still fits one XCD's L2 (4M x 4M, 15 per row: 8 slices 251 us, 4 slices
+    // 213 us; the power-law matrix: 267 against 289 us).  Fewer slices than
+    // that are not taken this way: 2 -> 1 cost the random 1M x 5 matrix 58 ->
+    // 85 us (its 4 MB x and the stream overflow one L2).
+    if (S == kNumXcd && 4 * num_cols <= static_cast<int64_t>(S / 2) * kL2Bytes) {
+#pragma clang fp contract(off)   // the same fp64 sum, rounding for rounding, as a plain C loop
+        double pairs = 0.0;
+        const double q = 1.0 - 1.0 / S;
+        for (size_t k = 0; k < hist.size(); ++k)
+            pairs += static_cast<double>(hist[k]) * (S * (1.0 - std::pow(q, static_cast<double>(k))));
+        if (10.0 * pairs > 3.0 * static_cast<double>(nnz)) S /= 2;
+    }
     return S;
 }
 

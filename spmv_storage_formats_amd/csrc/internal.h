@@ -358,7 +358,7 @@ spmv_status launch_spmv(const spmv_handle *h, const float *x, float *y, hipStrea
 // at least one entry of a row block per 128-byte x line on average), the
 // automatic slice count, the builder and the launcher.
 bool bc_auto_rule(const spmv_stats &st);
-int32_t bc_auto_slices(int64_t num_cols);
+int32_t bc_auto_slices(int64_t num_cols, int64_t nnz, const std::vector<int64_t> &hist);
 spmv_status build_coo_blocked(spmv_handle *h, int32_t R, int32_t C, int32_t nnz,
                               const int32_t *rp, const int32_t *col, const float *val, int32_t S,
                               hipStream_t s, Scratch &scratch);

@@ -574,6 +574,8 @@ def test_full_size_parity(dev, name, fmt):
         assert f == {"c1": "ell", "c2": "ell", "c3": "ell_xtile", "c4": "coo_blocked",
                      "c5": "coo_blocked"}[name]
     elif fmt == "coo_blocked":
+        # x within 2 MiB slices (8 would halve to 4 only if rows touched
+        # more than 0.3 slices per nonzero; the power law: 0.24)
         assert h.info["col_blocks"] == {"c1": 1, "c2": 2, "c3": 4, "c4": 4, "c5": 8}[name]
     else:
         assert h.info["col_blocks"] == 1

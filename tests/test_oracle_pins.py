@@ -895,7 +895,8 @@ def test_select_build_fig14_1():
 def test_select_build_blocked_branch():
     """65,536 rows x 2^21 columns (8 MiB of x), 16 random columns per row:
     scattered, and 32 * nnz * 16384 = 2^39 >= R * C = 2^37 -> blocked COO
-    with 4 slices (8 MiB <= 4 * 2 MiB)."""
+    with 4 slices (8 MiB <= 4 * 2 MiB; rows of 16 touch 4 * (1 - (3/4)^16) / 16
+    = 0.25 slices per nonzero <= 0.3, so no halving)."""
     rng = np.random.default_rng(1)
     R, C = 1 << 16, 1 << 21
     rp, ci = _csr_random(rng, R, C, 16)
@@ -906,15 +907,34 @@ def test_select_build_blocked_branch():
 def test_select_build_block_rows_term():
     """The min(R, RT) term: 65,536 rows x 2^21 columns, 3 random columns per
     row.  32 * nnz * RT >= R * C reads 32 * 3 * RT >= 2^21: true for RT =
-    32,768 (blocked COO, 4 slices), false for RT = 16,384.  Then x slices:
-    8 MiB of x gives K = 4, and 3 * 4 * 65,536 > nnz = 196,608 halves it to
-    K = 2 (the floor)."""
+    32,768 (blocked COO, 4 slices of 2 MiB; the slice pairs, 4 * (1 - (3/4)^3)
+    / 3 = 0.77 per nonzero, would halve only 8 slices), false for RT =
+    16,384.  Then x slices: 8 MiB of x gives K = 4, and 3 * 4 * 65,536 > nnz
+    = 196,608 halves it to K = 2 (the floor)."""
     rng = np.random.default_rng(4)
     R, C = 1 << 16, 1 << 21
     rp, ci = _csr_random(rng, R, C, 3)
     assert _spread(rp, ci, C) * 8 > C
     assert oracle.select_build(rp, ci, C, 32768) == ("coo_blocked", 0, 0, 4)
     assert oracle.select_build(rp, ci, C, 16384) == ("csr_merge", 0, 0, 2)
+
+
+@pytest.mark.parametrize("row_len,C,slices", [(15, 1 << 22, 4), (40, 1 << 22, 8),
+                                               (15, (1 << 22) + 1, 8)])
+def test_select_build_blocked_slice_halving(row_len, C, slices):
+    """65,536 rows of row_len random columns.  x of 2^22 columns is 16 MiB:
+    8 slices of 2 MiB, and 4C = 16 MiB <= 4 slices x 4 MiB, so the count may
+    halve.  Expected (row, slice) pairs per nonzero on 8 slices:
+    8 * (1 - (7/8)^15) / 15 = 0.461 > 0.3 -> 4 slices; 8 * (1 - (7/8)^40) / 40
+    = 0.199 -> 8 slices.  One column more and a half-count slice no longer
+    fits 4 MiB: 8 slices whatever the pairs."""
+    assert abs(8 * (1 - (7 / 8) ** 15) / 15 - 0.4614) < 1e-4
+    assert abs(8 * (1 - (7 / 8) ** 40) / 40 - 0.1990) < 1e-4
+    rng = np.random.default_rng(5)
+    R = 1 << 16
+    rp, ci = _csr_random(rng, R, C, row_len)
+    assert _spread(rp, ci, C) * 8 > C and 32 * int(rp[-1]) * 32768 >= R * C
+    assert oracle.select_build(rp, ci, C, 32768) == ("coo_blocked", 0, 0, slices)
 
 
 @pytest.mark.parametrize("nnz,slices", [(98304, 8), (98303, 4)])

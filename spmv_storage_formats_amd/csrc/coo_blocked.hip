@@ -202,9 +202,9 @@ __device__ inline void lds_cas_add(float *a, float v) {
     }
 }
 
-template <int U>
+template <int U, bool kFarX>
 __global__ __launch_bounds__(kBcThreads) void k_coo_blocked(
-    int32_t R, int32_t per, const int32_t *__restrict__ slice_chunk,
+    int32_t R, int32_t per, int32_t slice_cols, const int32_t *__restrict__ slice_chunk,
     const int32_t *__restrict__ chunk_grp, const int32_t *__restrict__ chunk_blk,
     const int32_t *__restrict__ hot, const int32_t *__restrict__ base,
     const uint32_t *__restrict__ pk, const float *__restrict__ val,
@@ -218,9 +218,17 @@ __global__ __launch_bounds__(kBcThreads) void k_coo_blocked(
     const int c = slice_chunk[k] + idx;
     if (c >= slice_chunk[k + 1]) return;   // whole workgroup
     const int b = chunk_blk[c];
-    const int64_t g0 = chunk_grp[c], g1 = chunk_grp[c + 1];
+    const int32_t g0 = chunk_grp[c];
+    const int32_t n = chunk_grp[c + 1] - g0;   // groups of this chunk
     const int64_t r0 = static_cast<int64_t>(b) * kBcRows;
     const int nrows = static_cast<int>(min(static_cast<int64_t>(kBcRows), R - r0));
+    // the chunk's arrays and the slice's x through wave-uniform pointers, so
+    // every load below takes a 32-bit offset (slots past 2^31 included)
+    const uint32_t *pkc = pk + static_cast<int64_t>(g0) * kWave;
+    const float *valc = val + static_cast<int64_t>(g0) * kWave;
+    const int32_t *basec = base + g0;
+    const int32_t col0 = k * slice_cols;   // a slice with a chunk starts below C
+    const float *xs = x + col0;
     // -0.0 is the additive identity bit for bit: an untouched partial is
     // recognised and never added, so rows without entries keep their y bits
     for (int i = threadIdx.x; i < nrows; i += kBcThreads) part[i] = -0.0f;
@@ -229,45 +237,55 @@ __global__ __launch_bounds__(kBcThreads) void k_coo_blocked(
     const int lane = __lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     float *mine = priv + wave * kBcHot;
-    for (int64_t gb = g0 + wave; gb < g1; gb += kBcWaves * U) {
-        // Every load below is unconditional and in bounds, so the U groups'
-        // stream loads, then their U gathers, are all in flight at once (a
-        // gather under a divergent branch would be waited for before the next
-        // is issued).  A group past the chunk's end re-reads the chunk's last
-        // group and is then marked as padding; a padding slot's offset is 0,
-        // so it gathers its group's base column (a real column), or column 0
-        // in a wide group.
+    // The workgroup walks the chunk U * 16 groups at a time, wave w taking
+    // the U consecutive groups lw .. lw + U - 1.  Every load is unconditional,
+    // so the U groups' stream loads, then their U gathers, are all in flight
+    // at once (a gather under a divergent branch would be waited for before
+    // the next is issued).  Groups past the chunk's end (at most U - 1 of
+    // them, which the arrays' tail padding keeps in bounds) become padding
+    // that gathers the slice's first column; a padding slot inside a group
+    // has offset 0 and gathers its group's base column.
+    for (int lw = wave * U; lw < n; lw += kBcWaves * U) {
+        const uint32_t off = static_cast<uint32_t>(lw * kWave + lane);
         uint32_t w[U];
         float v[U];
         int32_t bs[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t g = min(gb + u * kBcWaves, g1 - 1);
-            bs[u] = base[g];
-            w[u] = ld_nt(pk + g * kWave + lane);
-            v[u] = ld_nt(val + g * kWave + lane);
+            bs[u] = basec[lw + u];
+            w[u] = ld_nt(pkc + off + u * kWave);
+            v[u] = ld_nt(valc + off + u * kWave);
         }
         int32_t cx[U];
         bool wide = false;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            cx[u] = bs[u] + static_cast<int32_t>(w[u] & 0xFFFFu);
+            if (lw + u >= n) {   // past the chunk: wave-uniform
+                w[u] = kBcPadCode << 16;
+                bs[u] = col0;
+            }
+            cx[u] = (bs[u] - col0) + static_cast<int32_t>(w[u] & 0xFFFFu);
             wide |= bs[u] < 0;
         }
         if (wide) {   // wave-uniform and rare: groups spanning more than 2^16 columns
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                if (bs[u] < 0) cx[u] = ld_nt(wide_col + static_cast<int64_t>(-bs[u] - 1) * kWave + lane);
+                if (bs[u] < 0)   // a padding slot's column 0 becomes the slice's first
+                    cx[u] = max(ld_nt(wide_col + static_cast<int64_t>(-bs[u] - 1) * kWave + lane) - col0, 0);
         }
         float xv[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) xv[u] = x[cx[u]];
+        for (int u = 0; u < U; ++u) {
+            if constexpr (kFarX) {
+                xv[u] = xs[cx[u]];
+            } else {   // a slice of at most 2^30 columns: a 32-bit byte offset
+                xv[u] = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(xs) +
+                                                         (static_cast<uint32_t>(cx[u]) << 2));
+            }
+        }
         float p[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (gb + u * kBcWaves >= g1) w[u] = kBcPadCode << 16;   // past the chunk
-            p[u] = (w[u] >> 16) != kBcPadCode ? v[u] * xv[u] : 0.f;
-        }
+        for (int u = 0; u < U; ++u) p[u] = v[u] * xv[u];   // padding lanes' products are never read
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint32_t r = w[u] >> 16;
@@ -511,9 +529,17 @@ spmv_status build_coo_blocked(spmv_handle *h, int32_t R, int32_t C, int32_t nnz,
     h->bc_wide_groups = nwide;
 
     // 5. the groups themselves
-    SPMV_TRY(owned(h, &h->a.bc_base, groups));
-    SPMV_TRY(owned(h, &h->a.bc_pk, groups * kWave));
-    SPMV_TRY(owned(h, &h->a.bc_val, groups * kWave));
+    // kBcUnroll - 1 groups of tail padding: a wave's last step may read that
+    // far past the final chunk (the kernel marks those groups as padding)
+    const int64_t padded = groups + kBcUnroll - 1;
+    SPMV_TRY(owned(h, &h->a.bc_base, padded));
+    SPMV_TRY(owned(h, &h->a.bc_pk, padded * kWave));
+    SPMV_TRY(owned(h, &h->a.bc_val, padded * kWave));
+    SPMV_HIP(hipMemsetAsync(h->a.bc_base + groups, 0, sizeof(int32_t) * (kBcUnroll - 1), s));
+    SPMV_HIP(hipMemsetAsync(h->a.bc_pk + groups * kWave, 0,
+                            sizeof(uint32_t) * kWave * (kBcUnroll - 1), s));
+    SPMV_HIP(hipMemsetAsync(h->a.bc_val + groups * kWave, 0,
+                            sizeof(float) * kWave * (kBcUnroll - 1), s));
     SPMV_TRY(owned(h, &h->a.bc_wide, static_cast<int64_t>(nwide) * kWave));
     k_bc_fill<<<grid_for(groups * kWave, kThreads), kThreads, 0, s>>>(
         groups, nch, h->a.bc_chunk_grp, e01, e01 + nch, row2, col2, val2, code, widx,
@@ -528,9 +554,15 @@ hipError_t launch_coo_blocked(const spmv_handle *h, const float *x, float *y, hi
     const int32_t R = static_cast<int32_t>(h->stats.num_rows);
     const int32_t per = kNumXcd / h->col_blocks;
     const DevArrays &a = h->a;
-    k_coo_blocked<kBcUnroll><<<static_cast<unsigned>(h->bc_grid), kBcThreads, 0, s>>>(
-        R, per, a.bc_slice_chunk, a.bc_chunk_grp, a.bc_chunk_blk, a.bc_hot, a.bc_base, a.bc_pk,
-        a.bc_val, a.bc_wide, x, y);
+    const dim3 grid(static_cast<unsigned>(h->bc_grid));
+    if (h->slice_cols > (1 << 30))
+        k_coo_blocked<kBcUnroll, true><<<grid, kBcThreads, 0, s>>>(
+            R, per, h->slice_cols, a.bc_slice_chunk, a.bc_chunk_grp, a.bc_chunk_blk, a.bc_hot,
+            a.bc_base, a.bc_pk, a.bc_val, a.bc_wide, x, y);
+    else
+        k_coo_blocked<kBcUnroll, false><<<grid, kBcThreads, 0, s>>>(
+            R, per, h->slice_cols, a.bc_slice_chunk, a.bc_chunk_grp, a.bc_chunk_blk, a.bc_hot,
+            a.bc_base, a.bc_pk, a.bc_val, a.bc_wide, x, y);
     return hipGetLastError();
 }
 

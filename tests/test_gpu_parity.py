@@ -725,6 +725,55 @@ def test_blocked_scan_runs(dev, S):
     assert_rows(run_once(h, x, y0), y_ref, bound, f"scan runs S={S}")
 
 
+@pytest.fixture(scope="module")
+def x_past_2_30(dev):
+    """x of 2^30 + 1 columns (4 GiB), generated on the device."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(2030)
+    x = torch.rand((1 << 30) + 1, generator=g, device=dev)
+    x.mul_(2).sub_(1)
+    yield x
+    del x
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("C,S", [(1 << 30, 1), ((1 << 30) + 1, 1), ((1 << 30) + 1, 8)])
+def test_blocked_x_of_2_30_columns(dev, x_past_2_30, C, S):
+    """x slices at the edge of 32-bit byte offsets: one slice of exactly 2^30
+    columns (gathers up to byte 2^32 - 4 of the slice), one of 2^30 + 1 (the
+    64-bit gather path), and 8 slices of the larger x.  Odd rows keep their
+    columns in a band below C (narrow groups whose offsets reach the top of
+    the slice), even rows scatter them over all of x (wide groups).  y against
+    the oracle on the same matrix with its columns renumbered densely (the
+    oracle sees the same products in the same row order)."""
+    rng = np.random.default_rng(2030 + S + C)
+    R = 4096
+    lens = rng.integers(1, 17, size=R)
+    cols = []
+    for r, n in enumerate(lens):
+        lo = C - 40_000 if r % 2 else 0
+        c = np.sort(rng.choice(C - lo, n, replace=False) + lo)
+        cols.append(c)
+    cols[1][-1] = C - 1                                   # the last column itself
+    ci = np.concatenate(cols).astype(np.int32)
+    rp = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    va = rng.uniform(-1, 1, ci.size).astype(np.float32)
+    y0 = rng.uniform(-1, 1, R).astype(np.float32)
+    print(f"[case] blocked x of {C} columns, S={S}", flush=True)
+    h = spmv.build("coo_blocked", torch.from_numpy(rp).to(dev), torch.from_numpy(ci).to(dev),
+                   torch.from_numpy(va).to(dev), C, col_blocks=S)
+    assert h.info["col_blocks"] == S and h.info["slice_cols"] == -(-C // S)
+    assert 0 < h.info["wide_groups"] < h.info["groups"]
+    y = torch.from_numpy(y0).to(dev)
+    h.run(x_past_2_30[:C], y)
+    torch.cuda.synchronize()
+    uniq, local = np.unique(ci, return_inverse=True)
+    xl = x_past_2_30[torch.from_numpy(uniq.astype(np.int64)).to(dev)].cpu().numpy()
+    y_ref, bound = oracle.spmv_csr(rp, local.astype(np.int32), va, xl, y0)
+    assert_rows(y.cpu().numpy(), y_ref, bound, f"x of {C} columns S={S}")
+    h.close()
+
+
 def _slices(w, K):
     """The CSR arrays of the K column slices (entries with column in
     [k*ceil(C/K), (k+1)*ceil(C/K)), row order kept), built with numpy."""

@@ -202,6 +202,95 @@ __device__ inline void lds_cas_add(float *a, float v) {
     }
 }
 
+// One step of a wave: the U consecutive groups lw .. lw + U - 1 of its
+// chunk (n groups).  Every load is unconditional, so the U groups' stream
+// loads, then their U gathers, are all in flight at once (a gather under a
+// divergent branch would be waited for before the next is issued).  In the
+// chunk's last step (kTail) groups past its end, at most U - 1 of them and
+// kept in bounds by the arrays' tail padding, become padding that gathers
+// the slice's first column; a padding slot inside a group has offset 0 and
+// gathers its group's base column.
+template <int U, bool kFarX, bool kTail>
+__device__ __forceinline__ void bc_wave_step(int lw, int n, int lane, const uint32_t *pkc,
+                                             const float *valc, const int32_t *basec,
+                                             const int32_t *wide_col, int32_t col0,
+                                             const float *xs, float *part, float *mine) {
+    const uint32_t off = static_cast<uint32_t>(lw * kWave + lane);
+    uint32_t w[U];
+    float v[U];
+    int32_t bs[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        bs[u] = basec[lw + u];
+        w[u] = ld_nt(pkc + off + u * kWave);
+        v[u] = ld_nt(valc + off + u * kWave);
+    }
+    int32_t cx[U];
+    bool wide = false;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (kTail && lw + u >= n) {   // past the chunk: wave-uniform
+            w[u] = kBcPadCode << 16;
+            bs[u] = col0;
+        }
+        cx[u] = (bs[u] - col0) + static_cast<int32_t>(w[u] & 0xFFFFu);
+        wide |= bs[u] < 0;
+    }
+    if (wide) {   // wave-uniform and rare: groups spanning more than 2^16 columns
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (bs[u] < 0)   // a padding slot's column 0 becomes the slice's first
+                cx[u] = max(ld_nt(wide_col + static_cast<int64_t>(-bs[u] - 1) * kWave + lane) - col0, 0);
+    }
+    float xv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if constexpr (kFarX) {
+            xv[u] = xs[cx[u]];
+        } else {   // a slice of at most 2^30 columns: a 32-bit byte offset
+            xv[u] = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(xs) +
+                                                     (static_cast<uint32_t>(cx[u]) << 2));
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        float q = v[u] * xv[u];   // padding lanes' products are never read
+        const uint32_t k = (w[u] >> 16) + 1;   // code + 1: a lane that DPP fills with 0 never matches
+        // lane l + 1's key (wave_shl:1; lane 63 reads 0)
+        const uint32_t kn = static_cast<uint32_t>(
+            __builtin_amdgcn_update_dpp(0, static_cast<int>(k), 0x130, 0xF, 0xF, true));
+        const bool real = k != kBcPadCode + 1;
+        // bit l: lanes l and l + 1 hold the same row.  The scan runs only the
+        // steps some run needs: shift s when a run spans more than s lanes
+        // (m & m >> 1, ... find spans of 3, 5, 9), the broadcasts when a run
+        // crosses a 16-lane DPP row
+        // (padding lanes pair with each other only, and only a tail step has
+        // whole groups of them: elsewhere their pairs cost nothing)
+        const uint64_t m = kTail ? __builtin_amdgcn_ballot_w64(real && kn == k)
+                                 : __builtin_amdgcn_ballot_w64(kn == k);
+        if (m != 0) {
+            bc_seg_step<0x111, 0xF>(k, q);   // row_shr:1
+            const uint64_t m2 = m & (m >> 1);
+            if (m2 != 0) {
+                bc_seg_step<0x112, 0xF>(k, q);   // row_shr:2
+                const uint64_t m4 = m2 & (m2 >> 2);
+                if (m4 != 0) {
+                    bc_seg_step<0x114, 0xF>(k, q);   // row_shr:4
+                    if ((m4 & (m4 >> 4)) != 0) bc_seg_step<0x118, 0xF>(k, q);   // row_shr:8
+                }
+            }
+            if ((m & 0x0000800000008000ull) != 0) bc_seg_step<0x142, 0xA>(k, q);   // row_bcast:15
+            if ((m & 0x0000000080000000ull) != 0) bc_seg_step<0x143, 0xC>(k, q);   // row_bcast:31
+        }
+        // the last lane of each run adds the run's total to its row
+        if (real && kn != k) {
+            const uint32_t r = k - 1;
+            if (r >= kBcRows) mine[r - kBcRows] += q;   // this wave's own slot
+            else lds_cas_add(&part[r], q);
+        }
+    }
+}
+
 template <int U, bool kFarX>
 __global__ __launch_bounds__(kBcThreads) void k_coo_blocked(
     int32_t R, int32_t per, int32_t slice_cols, const int32_t *__restrict__ slice_chunk,
@@ -238,79 +327,12 @@ __global__ __launch_bounds__(kBcThreads) void k_coo_blocked(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     float *mine = priv + wave * kBcHot;
     // The workgroup walks the chunk U * 16 groups at a time, wave w taking
-    // the U consecutive groups lw .. lw + U - 1.  Every load is unconditional,
-    // so the U groups' stream loads, then their U gathers, are all in flight
-    // at once (a gather under a divergent branch would be waited for before
-    // the next is issued).  Groups past the chunk's end (at most U - 1 of
-    // them, which the arrays' tail padding keeps in bounds) become padding
-    // that gathers the slice's first column; a padding slot inside a group
-    // has offset 0 and gathers its group's base column.
-    for (int lw = wave * U; lw < n; lw += kBcWaves * U) {
-        const uint32_t off = static_cast<uint32_t>(lw * kWave + lane);
-        uint32_t w[U];
-        float v[U];
-        int32_t bs[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            bs[u] = basec[lw + u];
-            w[u] = ld_nt(pkc + off + u * kWave);
-            v[u] = ld_nt(valc + off + u * kWave);
-        }
-        int32_t cx[U];
-        bool wide = false;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (lw + u >= n) {   // past the chunk: wave-uniform
-                w[u] = kBcPadCode << 16;
-                bs[u] = col0;
-            }
-            cx[u] = (bs[u] - col0) + static_cast<int32_t>(w[u] & 0xFFFFu);
-            wide |= bs[u] < 0;
-        }
-        if (wide) {   // wave-uniform and rare: groups spanning more than 2^16 columns
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (bs[u] < 0)   // a padding slot's column 0 becomes the slice's first
-                    cx[u] = max(ld_nt(wide_col + static_cast<int64_t>(-bs[u] - 1) * kWave + lane) - col0, 0);
-        }
-        float xv[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if constexpr (kFarX) {
-                xv[u] = xs[cx[u]];
-            } else {   // a slice of at most 2^30 columns: a 32-bit byte offset
-                xv[u] = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(xs) +
-                                                         (static_cast<uint32_t>(cx[u]) << 2));
-            }
-        }
-        float p[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) p[u] = v[u] * xv[u];   // padding lanes' products are never read
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint32_t r = w[u] >> 16;
-            // lane l + 1's code (wave_shl:1; lane 63 reads all ones, no code)
-            const uint32_t rn = static_cast<uint32_t>(
-                __builtin_amdgcn_update_dpp(-1, static_cast<int>(r), 0x130, 0xF, 0xF, false));
-            const bool real = r != kBcPadCode;
-            float q = p[u];
-            // the scan only when some row holds two lanes of the group
-            if (__builtin_amdgcn_ballot_w64(real && rn == r) != 0) {
-                const uint32_t k = r + 1;
-                bc_seg_step<0x111, 0xF>(k, q);   // row_shr:1, 2, 4, 8
-                bc_seg_step<0x112, 0xF>(k, q);
-                bc_seg_step<0x114, 0xF>(k, q);
-                bc_seg_step<0x118, 0xF>(k, q);
-                bc_seg_step<0x142, 0xA>(k, q);   // row_bcast:15
-                bc_seg_step<0x143, 0xC>(k, q);   // row_bcast:31
-            }
-            // the last lane of each run adds the run's total to its row
-            if (real && rn != r) {
-                if (r >= kBcRows) mine[r - kBcRows] += q;   // this wave's own slot
-                else lds_cas_add(&part[r], q);
-            }
-        }
-    }
+    // the U consecutive groups lw .. lw + U - 1
+    int lw = wave * U;
+    for (; lw + U <= n; lw += kBcWaves * U)
+        bc_wave_step<U, kFarX, false>(lw, n, lane, pkc, valc, basec, wide_col, col0, xs, part, mine);
+    if (lw < n)
+        bc_wave_step<U, kFarX, true>(lw, n, lane, pkc, valc, basec, wide_col, col0, xs, part, mine);
     __syncthreads();
     for (int i = threadIdx.x; i < nrows; i += kBcThreads) {
         const float s = part[i];

@@ -595,14 +595,20 @@ def measured_traffic(key):
 
 
 def kernel_source_sha():
-    """Hash of the sources the SpMV kernels are compiled from (the kernels
-    files and the shared header; the blocked-COO builder shares its file)."""
+    """Hash of the code the SpMV kernels are compiled from (the kernels files
+    and the shared header; the blocked-COO builder shares its file), with
+    comments and whitespace removed, so that an edit to a comment keeps the
+    profiles valid and any change to the code does not."""
     import hashlib
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "spmv_storage_formats_amd", "csrc")
     for f in ("internal.h", "spmv_kernels.hip", "coo_blocked.hip"):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)   # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                # line comments
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -35,9 +35,10 @@
 //
 // Kernel: one workgroup per chunk (slice k's chunks on the XCDs k*8/S ..
 // (k+1)*8/S - 1, so each XCD's L2 holds one slice of x); the block's row
-// partials live in LDS; each wave takes groups, gathers x, sums runs of equal
-// codes with a DPP segmented scan (skipped, by one ballot, when every row of
-// the group holds a single lane) and adds each run's total to its partial:
+// partials live in LDS; each wave takes six consecutive groups at a time,
+// gathers x, sums runs of equal codes with a DPP segmented scan (one ballot
+// of neighbouring equal codes picks the steps the group's runs need, none
+// when every row holds a single lane) and adds each run's total to its partial:
 // hot rows by a plain add into the wave's own slot, other rows by a
 // compare-and-swap loop (an LDS float atomic add costs ~190 clocks per wave
 // instruction on gfx950, a CAS ~28, a plain read-modify-write ~16); finally

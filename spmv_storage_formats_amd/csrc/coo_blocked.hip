@@ -335,15 +335,34 @@ __global__ __launch_bounds__(kBcThreads) void k_coo_blocked(
     if (lw < n)
         bc_wave_step<U, kFarX, true>(lw, n, lane, pkc, valc, basec, wide_col, col0, xs, part, mine);
     __syncthreads();
-    for (int i = threadIdx.x; i < nrows; i += kBcThreads) {
-        const float s = part[i];
-        if (__float_as_uint(s) != 0x80000000u) unsafeAtomicAdd(&y[r0 + i], s);
+    // every partial that was touched goes to y; a full block's partials are
+    // read 8 at a time, so one LDS wait covers 8 of them
+    if (nrows == kBcRows) {
+#pragma unroll
+        for (int j0 = 0; j0 < kBcRows / kBcThreads; j0 += 8) {
+            float s[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) s[j] = part[threadIdx.x + (j0 + j) * kBcThreads];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (__float_as_uint(s[j]) != 0x80000000u)
+                    unsafeAtomicAdd(&y[r0 + threadIdx.x + (j0 + j) * kBcThreads], s[j]);
+        }
+    } else {
+        for (int i = threadIdx.x; i < nrows; i += kBcThreads) {
+            const float s = part[i];
+            if (__float_as_uint(s) != 0x80000000u) unsafeAtomicAdd(&y[r0 + i], s);
+        }
     }
     if (threadIdx.x < kBcHot) {
         const int32_t hr = hot[static_cast<int64_t>(b) * kBcHot + threadIdx.x];
         if (hr >= 0) {
-            float s = -0.0f;
-            for (int wv = 0; wv < kBcWaves; ++wv) s += priv[wv * kBcHot + threadIdx.x];
+            float w[kBcWaves];
+#pragma unroll
+            for (int wv = 0; wv < kBcWaves; ++wv) w[wv] = priv[wv * kBcHot + threadIdx.x];
+            float s = -0.0f;   // summed in wave order
+#pragma unroll
+            for (int wv = 0; wv < kBcWaves; ++wv) s += w[wv];
             if (__float_as_uint(s) != 0x80000000u) unsafeAtomicAdd(&y[hr], s);
         }
     }

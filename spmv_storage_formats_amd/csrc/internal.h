@@ -54,7 +54,8 @@ constexpr int kXtileAutoRows = 64 * kTileRows;
 // every group's loads and gathers in flight together: 16384-row blocks in
 // chunks of 65536 with 6 groups per wave (two workgroups per CU) 274 and 107
 // us; 32768-row blocks in chunks of 131072 (one workgroup per CU, twice the
-// entries per x line) with 6, 8, 10 groups per wave 267, 272, 274 and 97 us.
+// entries per x line) with 6, 8, 10 groups per wave 267, 272, 274 and 97 us
+// (with 4 and 5 groups: 264 us); all before the chunk-relative addressing.
 constexpr int kBcRows = SPMV_BC_BLOCK_ROWS;
 constexpr int kBcChunk = SPMV_BC_CHUNK_ENTRIES;
 constexpr int kBcHot = 32;

@@ -66,11 +66,12 @@ typedef enum spmv_status {
     SPMV_ERR_DEVICE = 8        /* handle used on another device than its own    */
 } spmv_status;
 
-/* Blocked COO layout constants (SPMV_COO_BLOCKED): rows per row block, whose
- * partials one workgroup keeps in LDS, and entries per chunk, one workgroup's
- * work. */
+/* Blocked COO layout constant (SPMV_COO_BLOCKED): rows per row block, whose
+ * partials one workgroup keeps in LDS.  A chunk, one workgroup's work, holds
+ * T = max(8192, ceil(ceil(11 * nnz / 2560) / 64) * 64) entries (about 1.1 *
+ * nnz / 256, in whole groups of 64: the chunks cover the 256 CUs about once);
+ * spmv_info.chunk_entries reports it. */
 #define SPMV_BC_BLOCK_ROWS 32768
-#define SPMV_BC_CHUNK_ENTRIES 131072
 
 /* Storage formats / kernels.  SPMV_AUTO lets the selector choose. */
 typedef enum spmv_format {
@@ -103,12 +104,10 @@ typedef enum spmv_format {
     SPMV_COO_BLOCKED = 11   /* blocked COO [INTRO x blocking and split by nonzeros; CHOICE
                                3.2 segmented COO]: rows in blocks of SPMV_BC_BLOCK_ROWS, columns in S
                                x slices (S = opts.col_blocks in {1,2,4,8}; 0: the smallest
-                               power of two that keeps a slice of x within 2 MiB, at most
-                               8, and 8 become 4 when a 4-slice slice fits 4 MiB and the
-                               expected (row, slice) pairs, sum over rows of length k of
-                               S * (1 - (1 - 1/S)^k) in fp64, exceed 0.3 nnz: each pair is
-                               one more atomic flush of a row partial); the entries of each (slice, block) are ordered by
-                               column, cut into chunks of SPMV_BC_CHUNK_ENTRIES and groups of 64, and each
+                               power of two that keeps a slice of x within 4 MiB, at most
+                               8); the entries of each (slice, block) are ordered by
+                               column, cut into chunks of T entries (see
+                               SPMV_BC_BLOCK_ROWS above) and groups of 64, and each
                                group is reordered by row so that runs of one row are
                                neighbouring lanes.  Neighbouring lanes therefore gather
                                neighbouring x words, and row partials are summed in LDS.
@@ -177,7 +176,7 @@ typedef struct spmv_info {
     int64_t groups;        /* blocked COO: groups of 64 slots             */
     int64_t wide_groups;   /* blocked COO: groups whose columns span > 65535 */
     int32_t block_rows;    /* blocked COO: SPMV_BC_BLOCK_ROWS             */
-    int32_t chunk_entries; /* blocked COO: SPMV_BC_CHUNK_ENTRIES          */
+    int32_t chunk_entries; /* blocked COO: T, entries per chunk           */
     int32_t hot_slots;     /* blocked COO: hot rows per block (32)        */
     int32_t hot_min_len;   /* blocked COO: rows this long or longer may be hot (64*S+1) */
 } spmv_info;
@@ -215,8 +214,8 @@ typedef enum spmv_array {
                               SPMV_A_ELL_VAL, SPMV_A_ELL_NNZ.                       */
     /* blocked COO: segment k*B + b holds the entries of x slice k and row block b
        (B = ceil(R/SPMV_BC_BLOCK_ROWS) blocks) ordered by column, ties in CSR order;
-       chunks are its consecutive runs of SPMV_BC_CHUNK_ENTRIES entries, groups a
-       chunk's runs of 64.                                                            */
+       chunks are its consecutive runs of T (spmv_info.chunk_entries) entries, the
+       last one the remainder; groups a chunk's runs of 64.                           */
     SPMV_A_BC_CHUNK_GRP = 22,  /* int32 [chunks+1] first group of chunk c          */
     SPMV_A_BC_CHUNK_BLK = 23,  /* int32 [chunks]   row block of chunk c             */
     SPMV_A_BC_SLICE_CHUNK = 24,/* int32 [S+1]      first chunk of x slice k         */

@@ -96,6 +96,7 @@ def _load():
         "orc_coo_blocked": (ctypes.c_int, [_i64, _i64, _i64, _i32p, _i32p, _u32p, _i64, _i64,
                                            _i64, _i64, _i64, _i64p] + [ctypes.c_void_p] * 8),
         "orc_select_build": (ctypes.c_int, [_i64, _i64, _i64, _i32p, _i32p, _i64, _i64p]),
+        "orc_bc_chunk_entries": (_i64, [_i64]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -316,6 +317,11 @@ def csr_to_coo_blocked(row_ptrs, col_idx, values, num_cols, slices, block_rows, 
     out["val"] = out["val"][:64 * ng].view(np.float32)
     out["wide"] = out["wide"][:64 * nw]
     return out
+
+
+def bc_chunk_entries(nnz):
+    """Blocked COO entries per chunk for a matrix of nnz nonzeros."""
+    return int(_load().orc_bc_chunk_entries(int(nnz)))
 
 
 def select_build(row_ptrs, col_idx, num_cols, block_rows):

@@ -35,8 +35,8 @@
  *     with the HYB width/budget extension described at orc_select().
  *   - ELL with x tiles, blocked COO and the automatic build's storage rules
  *     are encodings and build-time rules, not formulas of the pages: each is
- *     written out as a definition at orc_csr_to_ell_xtile(), orc_coo_blocked()
- *     and orc_select_build().
+ *     written out as a definition at orc_csr_to_ell_xtile(), orc_coo_blocked(),
+ *     orc_bc_chunk_entries() and orc_select_build().
  */
 #include <math.h>
 #include <stdint.h>
@@ -887,6 +887,20 @@ int orc_coo_blocked(int64_t R, int64_t C, int64_t nnz, const int32_t *row_ptrs,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Blocked COO chunk size (reading of [INTRO, split by nonzeros]: each      */
+/* workgroup gets an equal share of the nonzeros, one share per CU): T =    */
+/* ceil(11*nnz / 2560) rounded up to a multiple of 64, at least 8192; a     */
+/* segment is cut into runs of T entries, the last one the remainder        */
+/* (orc_coo_blocked's E).                                                   */
+/* ------------------------------------------------------------------------ */
+int64_t orc_bc_chunk_entries(int64_t nnz)
+{
+    int64_t t = (11 * nnz + 2559) / 2560;
+    t = (t + 63) / 64 * 64;
+    return t < 8192 ? 8192 : t;
+}
+
+/* ------------------------------------------------------------------------ */
 /* The automatic build's choice (the library's SPMV_AUTO), written out: the */
 /* selector of orc_select, then the build-time readings of x blocking       */
 /* [INTRO, memory-efficiency check: gathers from an x that does not fit the */
@@ -895,11 +909,7 @@ int orc_coo_blocked(int64_t R, int64_t C, int64_t nnz, const int32_t *row_ptrs,
 /*            floor(r*C/R)|); scattered = spread*8 > C; big_x = 4C > 4 MiB. */
 /*   1. scattered, big_x and 32*nnz*min(R, RT) >= R*C (a row block holds an */
 /*      entry per 128-byte line of x on average) -> blocked COO with S =    */
-/*      the smallest power of two with 4C <= S * 2 MiB, at most 8; then,    */
-/*      when S = 8 and 4C <= (S/2) * 4 MiB, S is halved if the expected     */
-/*      (row, slice) pairs, sum over row lengths k of hist[k] * S * (1 -    */
-/*      (1 - 1/S)^k) in fp64 with k ascending, exceed 3/10 of nnz (each     */
-/*      pair is one flush of a row partial).                                */
+/*      the smallest power of two with 4C <= S * 4 MiB, at most 8.          */
 /*   2. scattered and big_x otherwise -> x slices, each merge-based CSR:    */
 /*      4C <= 16 MiB: K = the smallest of 2, 4, 8 with 4C <= K * 2 MiB,     */
 /*      halved (not below 2) while 3*K*R > nnz; beyond: K = ceil(4C/4 MiB); */
@@ -947,18 +957,8 @@ int orc_select_build(int64_t R, int64_t C, int64_t nnz, const int32_t *row_ptrs,
     int64_t rows = R < RT ? R : RT;
     if (nnz > 0 && R > 0 && scattered && big_x && 32 * nnz * rows >= R * C) {
         int64_t S = 1;
-        while (S < 8 && 4 * C > S * (2 << 20))
+        while (S < 8 && 4 * C > S * (4 << 20))
             S *= 2;
-        if (S == 8 && 4 * C <= (S / 2) * (4 << 20)) {
-            double pairs = 0.0;
-            const double q = 1.0 - 1.0 / (double)S;
-            for (int64_t k = 0; k <= W; ++k) {
-                const double term = (double)hist[k] * ((double)S * (1.0 - pow(q, (double)k)));
-                pairs = pairs + term;
-            }
-            if (10.0 * pairs > 3.0 * (double)nnz)
-                S /= 2;
-        }
         free(hist);
         out[0] = ORC_FMT_COO_BLOCKED;
         out[1] = 0;

@@ -339,7 +339,7 @@ int64_t format_bytes(int32_t fmt, int64_t R, int64_t nnz, int64_t W, int64_t K,
     case SPMV_COO_BLOCKED: {
         // upper bound: every segment and chunk may end in a partial group
         const int64_t nblk = (R + kBcRows - 1) / kBcRows;
-        const int64_t groups = nnz / kWave + nnz / kBcChunk + kNumXcd * nblk + 1;
+        const int64_t groups = nnz / kWave + nnz / bc_chunk_entries(nnz) + kNumXcd * nblk + 1;
         return 8 * kWave * groups + 4 * groups + 4 * nblk * kBcHot + 8 * (groups + kNumXcd);
     }
     default: return 0;
@@ -542,11 +542,11 @@ spmv_status build_csr_impl(spmv_handle **out, spmv_format fmt, int32_t R, int32_
     // block holds at least one entry per 128-byte line of x on average.
     int32_t bc_slices = 0;
     if (fmt == SPMV_COO_BLOCKED) {
-        bc_slices = o.col_blocks > 0 ? o.col_blocks : bc_auto_slices(C, nnz, an.hist);
+        bc_slices = o.col_blocks > 0 ? o.col_blocks : bc_auto_slices(C);
         if (bc_slices != 1 && bc_slices != 2 && bc_slices != 4 && bc_slices != 8)
             return SPMV_ERR_INVALID_ARG;
     } else if (fmt == SPMV_AUTO && o.col_blocks == 0 && bc_auto_rule(an.st)) {
-        bc_slices = bc_auto_slices(C, nnz, an.hist);
+        bc_slices = bc_auto_slices(C);
     } else {
         const int32_t K_slices = choose_col_blocks(an.st, fmt, o);
         if (K_slices > 1)
@@ -818,7 +818,7 @@ spmv_status spmv_build_tuned(spmv_handle **out, int32_t R, int32_t C, int32_t nn
             if (rep.count >= SPMV_TUNE_MAX) break;
             spmv_tune_entry &ent = rep.entry[rep.count++];
             ent.format = f;
-            ent.col_blocks = blocked ? bc_auto_slices(C, nnz, an.hist) : K;
+            ent.col_blocks = blocked ? bc_auto_slices(C) : K;
             spmv_opts oc = o;
             oc.validate = 0;
             oc.col_blocks = K;
@@ -960,7 +960,7 @@ spmv_status spmv_get_info(const spmv_handle *h, spmv_info *info) {
         info->groups = h->bc_groups;
         info->wide_groups = h->bc_wide_groups;
         info->block_rows = kBcRows;
-        info->chunk_entries = kBcChunk;
+        info->chunk_entries = static_cast<int32_t>(h->bc_chunk);
         info->hot_slots = kBcHot;
         info->hot_min_len = h->bc_hot_min_len;
     }

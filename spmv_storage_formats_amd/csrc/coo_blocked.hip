@@ -17,8 +17,9 @@
 // Layout (every array owned by the handle; R rows, C columns):
 //   - rows in blocks of kBcRows; columns in S slices of sc = ceil(C/S); the
 //     entries of (slice k, block b) form segment k*nblk + b, ordered by column
-//     (ties keep CSR order); segments are cut into chunks of kBcChunk entries
-//     and chunks into groups of 64 consecutive entries;
+//     (ties keep CSR order); segments are cut into chunks of T entries (the
+//     last of a segment the remainder; T = bc_chunk_entries(nnz)) and chunks
+//     into groups of 64 consecutive entries;
 //   - inside a group the entries are reordered by row code (stable), so equal
 //     rows are neighbouring lanes; the code of an entry is its row's index
 //     within the block, or kBcRows + h for the block's hot row h (the
@@ -45,7 +46,6 @@
 // every non-zero partial is added to y with a global atomic (chunks of the
 // same rows run concurrently).
 #include <algorithm>
-#include <cmath>
 #include <vector>
 
 #include "internal.h"
@@ -386,27 +386,22 @@ spmv_status owned(spmv_handle *h, T **p, int64_t count) {
 
 }  // namespace
 
-int32_t bc_auto_slices(int64_t num_cols, int64_t nnz, const std::vector<int64_t> &hist) {
+int32_t bc_auto_slices(int64_t num_cols) {
+    // Fewer slices mean fewer chunks, and each chunk flushes its block's
+    // partials to y; a slice of x up to one L2 (4 MiB) keeps the gathers
+    // cheap (power-law 4M x 4M, one chunk per segment: 4 slices 221 us, 8
+    // slices 251 us, 2 slices of 8 MB 267 us).
     int32_t S = 1;
     while (S < kNumXcd && 4 * num_cols > S * kBcSliceBytes) S *= 2;
-    // Each (row, slice) pair that a row touches costs one flush of its partial
-    // to y; with a row's columns spread evenly over S slices, a row of k
-    // entries touches S * (1 - (1 - 1/S)^k) of them.  When those pairs exceed
-    // 3/10 of the nonzeros (rows of 15 entries on 8 slices: 0.46, against
-    // 0.24 on the power-law matrix), 4 slices are faster than 8 while a slice
-    // still fits one XCD's L2 (4M x 4M, 15 per row: 8 slices 251 us, 4 slices
-    // 213 us; the power-law matrix: 267 against 289 us).  Fewer slices than
-    // that are not taken this way: 2 -> 1 cost the random 1M x 5 matrix 58 ->
-    // 85 us (its 4 MB x and the stream overflow one L2).
-    if (S == kNumXcd && 4 * num_cols <= static_cast<int64_t>(S / 2) * kL2Bytes) {
-#pragma clang fp contract(off)   // the same fp64 sum, rounding for rounding, as a plain C loop
-        double pairs = 0.0;
-        const double q = 1.0 - 1.0 / S;
-        for (size_t k = 0; k < hist.size(); ++k)
-            pairs += static_cast<double>(hist[k]) * (S * (1.0 - std::pow(q, static_cast<double>(k))));
-        if (10.0 * pairs > 3.0 * static_cast<double>(nnz)) S /= 2;
-    }
     return S;
+}
+
+int64_t bc_chunk_entries(int64_t nnz) {
+    // about 1.1 * nnz / 256 entries, in whole groups: the chunks, one
+    // workgroup per CU, cover the 256 CUs about once, so no workgroup's
+    // partials are flushed for a sliver of work
+    const int64_t t = (11 * nnz + 10 * kBcCus - 1) / (10 * kBcCus);
+    return std::max<int64_t>((t + kWave - 1) / kWave * kWave, kBcChunkMin);
 }
 
 bool bc_auto_rule(const spmv_stats &st) {
@@ -428,6 +423,7 @@ spmv_status build_coo_blocked(spmv_handle *h, int32_t R, int32_t C, int32_t nnz,
     h->slice_cols = static_cast<int32_t>(sc);
     h->bc_blocks = nblk;
     h->bc_hot_min_len = kBcHotPerSlice * S + 1;
+    h->bc_chunk = bc_chunk_entries(nnz);
     if (nnz == 0 || R == 0) return SPMV_OK;
     if (nseg > 2147483647LL) return SPMV_ERR_TOO_LARGE;
 
@@ -520,13 +516,15 @@ spmv_status build_coo_blocked(spmv_handle *h, int32_t R, int32_t C, int32_t nnz,
                             s));
     SPMV_HIP(hipStreamSynchronize(s));
 
-    // 3. chunks of kBcChunk entries per segment, groups of 64 per chunk
+    // 3. chunks of T entries per segment (the last one the remainder), groups
+    //    of 64 per chunk
+    const int64_t T = h->bc_chunk;
     std::vector<int32_t> cgrp{0}, cblk, ce0, ce1, schunk(static_cast<size_t>(S) + 1, 0);
     int64_t groups = 0;
     for (int64_t sg = 0; sg < nseg; ++sg) {
         if (sg % nblk == 0) schunk[static_cast<size_t>(sg / nblk)] = static_cast<int32_t>(cblk.size());
-        for (int64_t e = hb[sg]; e < hb[sg + 1]; e += kBcChunk) {
-            const int64_t e1 = std::min<int64_t>(e + kBcChunk, hb[sg + 1]);
+        for (int64_t e = hb[sg]; e < hb[sg + 1]; e += T) {
+            const int64_t e1 = std::min<int64_t>(e + T, hb[sg + 1]);
             groups += (e1 - e + kWave - 1) / kWave;
             if (groups * kWave > (int64_t{1} << 40)) return SPMV_ERR_TOO_LARGE;
             cgrp.push_back(static_cast<int32_t>(groups));

@@ -46,10 +46,12 @@ constexpr int kTileMaxRuns = 1024;
 constexpr int kXtileAutoRows = 64 * kTileRows;
 
 // Blocked COO (x-scattered matrices): rows per block (the LDS partials of one
-// workgroup), entries per chunk (one workgroup's work), hot-row slots per block
-// and the length above which a row is hot (kBcHotPerSlice * slices), one
-// workgroup's threads and groups in flight per wave, and the x slice size of
-// the automatic slice count (2 MiB: an XCD's L2 keeps room for the stream).
+// workgroup), hot-row slots per block and the length above which a row is hot
+// (kBcHotPerSlice * slices), one workgroup's threads and groups in flight per
+// wave, the largest x slice of the automatic slice count (4 MiB: one XCD's
+// L2), and the chunk rule (bc_chunk_entries): a chunk, one workgroup's work,
+// holds about 1.1 * nnz / kBcCus entries, so that the chunks fill the CUs
+// about once, and at least kBcChunkMin.
 // Measured on the power-law 4M-row matrix and the 2M-row skewed one, with
 // every group's loads and gathers in flight together: 16384-row blocks in
 // chunks of 65536 with 6 groups per wave (two workgroups per CU) 274 and 107
@@ -57,12 +59,13 @@ constexpr int kXtileAutoRows = 64 * kTileRows;
 // entries per x line) with 6, 8, 10 groups per wave 267, 272, 274 and 97 us
 // (with 4 and 5 groups: 264 us); all before the chunk-relative addressing.
 constexpr int kBcRows = SPMV_BC_BLOCK_ROWS;
-constexpr int kBcChunk = SPMV_BC_CHUNK_ENTRIES;
 constexpr int kBcHot = 32;
 constexpr int kBcHotPerSlice = 64;
 constexpr int kBcThreads = 1024;
 constexpr int kBcUnroll = 6;
-constexpr int64_t kBcSliceBytes = 2 << 20;
+constexpr int64_t kBcSliceBytes = 4 << 20;
+constexpr int64_t kBcCus = 256;
+constexpr int64_t kBcChunkMin = kBcRows / 4;
 
 // Validation flags written by the analysis kernels.
 enum : int { kFlagBadRowPtrs = 1, kFlagBadCol = 2, kFlagBadRow = 4, kFlagUnsortedRows = 8 };
@@ -141,6 +144,7 @@ struct spmv_handle {
     // blocked COO
     int64_t bc_blocks = 0;          // row blocks
     int64_t bc_groups = 0;          // groups of 64 slots
+    int64_t bc_chunk = 0;           // entries per chunk (a segment's last may hold fewer)
     int64_t bc_wide_groups = 0;
     int64_t bc_grid = 0;            // workgroups of one launch
     int32_t bc_hot_min_len = 0;     // rows of at least this length may be hot
@@ -359,7 +363,8 @@ spmv_status launch_spmv(const spmv_handle *h, const float *x, float *y, hipStrea
 // at least one entry of a row block per 128-byte x line on average), the
 // automatic slice count, the builder and the launcher.
 bool bc_auto_rule(const spmv_stats &st);
-int32_t bc_auto_slices(int64_t num_cols, int64_t nnz, const std::vector<int64_t> &hist);
+int32_t bc_auto_slices(int64_t num_cols);
+int64_t bc_chunk_entries(int64_t nnz);
 spmv_status build_coo_blocked(spmv_handle *h, int32_t R, int32_t C, int32_t nnz,
                               const int32_t *rp, const int32_t *col, const float *val, int32_t S,
                               hipStream_t s, Scratch &scratch);

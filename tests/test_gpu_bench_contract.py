@@ -43,7 +43,7 @@ def test_contract_fields(line):
     # the headline is the largest workload, the power-law matrix
     assert cfg["workload"].startswith("power_law_4M")
     assert (cfg["rows"], cfg["cols"]) == (4_000_000, 4_000_000) and cfg["nnz"] > 60_000_000
-    assert cfg["format"] == "coo_blocked" and cfg["col_blocks"] == 8
+    assert cfg["format"] == "coo_blocked" and cfg["col_blocks"] == 4
     # value = 2 nnz / mean step time
     assert d["value"] > 0
     assert abs(d["value"] - 2 * cfg["nnz"] / (d["ms_per_step"] * 1e-3) / 1e9) <= 0.01 * d["value"]

@@ -66,7 +66,7 @@ def test_max_size_parity(big, fmt, kw):
     if fmt == "hyb":
         assert h.info["tail_nnz"] == b["m"].num_rows - 1
     if fmt == "coo_blocked":
-        # 2^26 rows in 4096 blocks, x of 256 MiB in 8 slices; slots past 2^31
+        # 2^26 rows in 2048 blocks, x of 256 MiB in 8 slices; slots past 2^31
         assert h.info["col_blocks"] == 8 and h.info["groups"] * 64 >= b["m"].nnz
     y = b["y0"].clone()
     h.run(b["x"], y)

@@ -198,6 +198,7 @@ def check_blocked(h, w):
                                   i["block_rows"], i["chunk_entries"], i["hot_slots"],
                                   i["hot_min_len"])
     assert i["slice_cols"] == max(-(-w.num_cols // i["col_blocks"]), 1)
+    assert i["chunk_entries"] == oracle.bc_chunk_entries(w.nnz)
     assert i["num_tiles"] == o["chunk_blk"].size and i["groups"] == o["base"].size
     assert i["wide_groups"] * 64 == o["wide"].size
     for name in ("chunk_grp", "chunk_blk", "slice_chunk", "hot", "base", "pk", "wide"):
@@ -574,9 +575,8 @@ def test_full_size_parity(dev, name, fmt):
         assert f == {"c1": "ell", "c2": "ell", "c3": "ell_xtile", "c4": "coo_blocked",
                      "c5": "coo_blocked"}[name]
     elif fmt == "coo_blocked":
-        # x within 2 MiB slices (8 would halve to 4 only if rows touched
-        # more than 0.3 slices per nonzero; the power law: 0.24)
-        assert h.info["col_blocks"] == {"c1": 1, "c2": 2, "c3": 4, "c4": 4, "c5": 8}[name]
+        # x within 4 MiB slices
+        assert h.info["col_blocks"] == {"c1": 1, "c2": 1, "c3": 2, "c4": 2, "c5": 4}[name]
     else:
         assert h.info["col_blocks"] == 1
     _, _, _, x, y0 = to_dev(w, dev)

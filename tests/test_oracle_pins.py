@@ -895,46 +895,55 @@ def test_select_build_fig14_1():
 def test_select_build_blocked_branch():
     """65,536 rows x 2^21 columns (8 MiB of x), 16 random columns per row:
     scattered, and 32 * nnz * 16384 = 2^39 >= R * C = 2^37 -> blocked COO
-    with 4 slices (8 MiB <= 4 * 2 MiB; rows of 16 touch 4 * (1 - (3/4)^16) / 16
-    = 0.25 slices per nonzero <= 0.3, so no halving)."""
+    with 2 slices (8 MiB <= 2 * 4 MiB)."""
     rng = np.random.default_rng(1)
     R, C = 1 << 16, 1 << 21
     rp, ci = _csr_random(rng, R, C, 16)
     assert _spread(rp, ci, C) * 8 > C
-    assert oracle.select_build(rp, ci, C, 16384) == ("coo_blocked", 0, 0, 4)
+    assert oracle.select_build(rp, ci, C, 16384) == ("coo_blocked", 0, 0, 2)
 
 
 def test_select_build_block_rows_term():
     """The min(R, RT) term: 65,536 rows x 2^21 columns, 3 random columns per
     row.  32 * nnz * RT >= R * C reads 32 * 3 * RT >= 2^21: true for RT =
-    32,768 (blocked COO, 4 slices of 2 MiB; the slice pairs, 4 * (1 - (3/4)^3)
-    / 3 = 0.77 per nonzero, would halve only 8 slices), false for RT =
-    16,384.  Then x slices: 8 MiB of x gives K = 4, and 3 * 4 * 65,536 > nnz
+    32,768 (blocked COO, 2 slices of 4 MiB), false for RT = 16,384.  Then x slices: 8 MiB of x gives K = 4, and 3 * 4 * 65,536 > nnz
     = 196,608 halves it to K = 2 (the floor)."""
     rng = np.random.default_rng(4)
     R, C = 1 << 16, 1 << 21
     rp, ci = _csr_random(rng, R, C, 3)
     assert _spread(rp, ci, C) * 8 > C
-    assert oracle.select_build(rp, ci, C, 32768) == ("coo_blocked", 0, 0, 4)
+    assert oracle.select_build(rp, ci, C, 32768) == ("coo_blocked", 0, 0, 2)
     assert oracle.select_build(rp, ci, C, 16384) == ("csr_merge", 0, 0, 2)
 
 
-@pytest.mark.parametrize("row_len,C,slices", [(15, 1 << 22, 4), (40, 1 << 22, 8),
-                                               (15, (1 << 22) + 1, 8)])
-def test_select_build_blocked_slice_halving(row_len, C, slices):
-    """65,536 rows of row_len random columns.  x of 2^22 columns is 16 MiB:
-    8 slices of 2 MiB, and 4C = 16 MiB <= 4 slices x 4 MiB, so the count may
-    halve.  Expected (row, slice) pairs per nonzero on 8 slices:
-    8 * (1 - (7/8)^15) / 15 = 0.461 > 0.3 -> 4 slices; 8 * (1 - (7/8)^40) / 40
-    = 0.199 -> 8 slices.  One column more and a half-count slice no longer
-    fits 4 MiB: 8 slices whatever the pairs."""
-    assert abs(8 * (1 - (7 / 8) ** 15) / 15 - 0.4614) < 1e-4
-    assert abs(8 * (1 - (7 / 8) ** 40) / 40 - 0.1990) < 1e-4
+@pytest.mark.parametrize("C,slices", [(1 << 21, 2), ((1 << 21) + 1, 4), (1 << 22, 4),
+                                      ((1 << 22) + 1, 8), (1 << 23, 8), ((1 << 23) + 1, 8)])
+def test_select_build_blocked_slice_count(C, slices):
+    """65,536 rows of 15 random columns (blocked COO: 32 * 983,040 * 32,768 >=
+    R * C up to C = 2^23 + 1).  Slices: the smallest power of two, at most 8,
+    that keeps one within 4 MiB, i.e. 4C <= S * 2^22: 2^21 columns (8 MiB)
+    -> 2, one more -> 4; 2^22 (16 MiB) -> 4, one more -> 8; 2^23 (32 MiB)
+    -> 8, and 8 is the cap."""
     rng = np.random.default_rng(5)
     R = 1 << 16
-    rp, ci = _csr_random(rng, R, C, row_len)
+    rp, ci = _csr_random(rng, R, C, 15)
     assert _spread(rp, ci, C) * 8 > C and 32 * int(rp[-1]) * 32768 >= R * C
     assert oracle.select_build(rp, ci, C, 32768) == ("coo_blocked", 0, 0, slices)
+
+
+@pytest.mark.parametrize("nnz,chunk", [(0, 8192), (8, 8192), (1_906_501, 8192),
+                                       (1_906_502, 8256), (5_000_000, 21_504),
+                                       (65_343_801, 280_832), (2**31 - 1, 9_227_520)])
+def test_bc_chunk_entries(nnz, chunk):
+    """Blocked COO entries per chunk: ceil(11 nnz / 2560) in whole groups of
+    64, at least 8192.  By hand: 11 * 1,906,501 = 20,971,511 < 8192 * 2560 =
+    20,971,520, so 8192; 11 * 1,906,502 = 20,971,522 -> 8193 -> 129 groups =
+    8256.  11 * 5,000,000 / 2560 = 21,484.4 -> 21,485 -> 336 groups = 21,504.
+    11 * 65,343,801 = 718,781,811; / 2560 = 280,774.1 -> 280,775 -> 4,388
+    groups = 280,832.  11 * (2^31 - 1) = 23,622,320,117; / 2560 =
+    9,227,468.8 -> 9,227,469 -> 144,180 groups = 9,227,520."""
+    assert oracle.bc_chunk_entries(nnz) == chunk
+    assert chunk % 64 == 0 and chunk >= 8192
 
 
 @pytest.mark.parametrize("nnz,slices", [(98304, 8), (98303, 4)])

@@ -708,8 +708,10 @@ int orc_csr_to_ell_xtile(int64_t R, const int32_t *row_ptrs, const int32_t *col_
 /*   entry i of row r, column c: slice k = c / sc (sc = ceil(C/S), at least */
 /*   1), row block b = r / RT, segment s = k*B + b (B = ceil(R/RT) blocks). */
 /*   Entries in order of (s, c), ties in CSR order.  Each segment's run is  */
-/*   cut into chunks of E entries (the last shorter), chunks numbered in    */
-/*   segment order; each chunk into groups of 64 entries (the last shorter, */
+/*   cut into chunks of E entries, the last one the remainder, which joins  */
+/*   the chunk before it when shorter than E/2 (integer halving); chunks    */
+/*   numbered in segment order; each chunk into groups of 64 entries (the   */
+/*   last shorter,                                                          */
 /*   padded to 64 slots).                                                   */
 /*   Hot rows of block b: its rows with at least hot_min_len entries,       */
 /*   longest first, ties by row, the first H (hot[b*H + h], -1 for unused). */
@@ -830,8 +832,11 @@ int orc_coo_blocked(int64_t R, int64_t C, int64_t nnz, const int32_t *row_ptrs,
     for (int64_t s = 0; s < nseg; ++s) {
         if (s % B == 0 && slice_chunk)
             slice_chunk[s / B] = (int32_t)nch;
-        for (int64_t e0 = seg_start[s]; e0 < seg_start[s + 1]; e0 += E) {
-            int64_t e1 = e0 + E < seg_start[s + 1] ? e0 + E : seg_start[s + 1];
+        for (int64_t e0 = seg_start[s], e1 = 0; e0 < seg_start[s + 1]; e0 = e1) {
+            /* runs of E entries; a last piece shorter than E/2 joins the run before it */
+            e1 = e0 + E < seg_start[s + 1] ? e0 + E : seg_start[s + 1];
+            if (seg_start[s + 1] - e1 < E / 2)
+                e1 = seg_start[s + 1];
             for (int64_t g0 = e0; g0 < e1; g0 += 64) {
                 int64_t n = e1 - g0 < 64 ? e1 - g0 : 64;
                 int64_t lo = col_idx[order[g0]], hi = col_idx[order[g0 + n - 1]];

@@ -817,13 +817,16 @@ def test_coo_blocked_semantics_bruteforce(seed):
     # expected entry order: by (segment, column), ties in CSR order
     seg = (w.col_idx // sc) * nblk + rows // RT
     order = sorted(range(w.nnz), key=lambda i: (seg[i], w.col_idx[i], i))
-    # chunks and groups cut that order into runs of E and 64
-    pos = 0
+    # chunks and groups cut that order into runs of E (a last piece shorter
+    # than E // 2 joining the run before it) and 64
     expect_grp = []
     for s in range(S * nblk):
         run = [i for i in order if seg[i] == s]
-        for e0 in range(0, len(run), E):
-            chunk = run[e0:e0 + E]
+        cuts = list(range(0, len(run), E)) + [len(run)]
+        if len(cuts) > 2 and cuts[-1] - cuts[-2] < E // 2:
+            del cuts[-2]
+        for e0, e1 in zip(cuts[:-1], cuts[1:]):
+            chunk = run[e0:e1]
             expect_grp.append([chunk[g0:g0 + 64] for g0 in range(0, len(chunk), 64)])
     assert len(o["chunk_blk"]) == len(expect_grp)
     assert o["chunk_grp"].tolist() == np.cumsum([0] + [len(c) for c in expect_grp]).tolist()
@@ -854,6 +857,21 @@ def test_coo_blocked_semantics_bruteforce(seed):
             gi += 1
     assert o["wide"].size == 64 * nwide
     assert o["slice_chunk"][0] == 0 and o["slice_chunk"][-1] == len(expect_grp)
+
+
+@pytest.mark.parametrize("E,chunk_grp", [(100, [0, 2, 3]), (120, [0, 3]), (160, [0, 3]),
+                                          (40, [0, 1, 2, 3, 4])])
+def test_coo_blocked_chunk_remainder(E, chunk_grp):
+    """One segment of 160 entries (2 rows of one block, one slice).  E = 100:
+    runs of 100 and 60 (60 >= 50 stays a chunk): 2 + 1 groups.  E = 120: 120
+    and 40, and 40 < 60 joins the first: one chunk of 160, 3 groups.  E = 160:
+    one chunk.  E = 40: four runs of 40, no remainder: one group each."""
+    rp = np.array([0, 130, 160], np.int32)
+    ci = np.concatenate([np.arange(130), np.arange(200, 230)]).astype(np.int32)
+    v = np.ones(160, np.float32)
+    o = oracle.csr_to_coo_blocked(rp, ci, v, 1000, 1, 2, E, 0, 1000)
+    assert o["chunk_grp"].tolist() == chunk_grp
+    assert o["slice_chunk"].tolist() == [0, len(chunk_grp) - 1]
 
 
 def test_coo_blocked_y_by_decoding():

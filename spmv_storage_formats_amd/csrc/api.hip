@@ -337,9 +337,11 @@ int64_t format_bytes(int32_t fmt, int64_t R, int64_t nnz, int64_t W, int64_t K,
         return 8 * slots + 8 * R + 4 * (R / kWave + 2) + 8 * (R / kWave + 1 + slots / kWave);
     }
     case SPMV_COO_BLOCKED: {
-        // upper bound: every segment and chunk may end in a partial group
+        // upper bound: every segment and chunk may end in a partial group, and
+        // the group arrays carry kBcUnroll - 1 groups of tail padding
         const int64_t nblk = (R + kBcRows - 1) / kBcRows;
-        const int64_t groups = nnz / kWave + nnz / bc_chunk_entries(nnz) + kNumXcd * nblk + 1;
+        const int64_t groups =
+            nnz / kWave + nnz / bc_chunk_entries(nnz) + kNumXcd * nblk + kBcUnroll;
         return 8 * kWave * groups + 4 * groups + 4 * nblk * kBcHot + 8 * (groups + kNumXcd);
     }
     default: return 0;

@@ -67,10 +67,26 @@ typedef enum spmv_status {
 } spmv_status;
 
 /* Blocked COO layout constant (SPMV_COO_BLOCKED): rows per row block, whose
- * partials one workgroup keeps in LDS.  A chunk, one workgroup's work, holds
- * T = max(8192, ceil(ceil(11 * nnz / 2560) / 64) * 64) entries (about 1.1 *
- * nnz / 256, in whole groups of 64: the chunks cover the 256 CUs about once);
- * spmv_info.chunk_entries reports it. */
+ * partials one workgroup keeps in LDS.  A chunk is a run of one segment's
+ * entries (one x slice, one row block) whose partials are flushed to y
+ * together; a work item, one workgroup's work, is one or more consecutive
+ * chunks.  Each x slice takes one of two rules:
+ *   - by chunk: segments cut into chunks of T = max(8192, ceil(ceil(11 * nnz /
+ *     2560) / 64) * 64) entries (about 1.1 * nnz / 256, in whole groups of 64:
+ *     the chunks cover the 256 CUs about once), the last one the remainder,
+ *     joined to the chunk before it when shorter than T/2; one chunk per item;
+ *     spmv_info.chunk_entries reports T;
+ *   - balanced: P = 256 / S items of about equal cost.  An entry of segment s
+ *     costs r_s = floor((n_s + 3 * lines_s) * 1024 / n_s), n_s being the
+ *     segment's entries and lines_s the 128-byte lines of x they touch (an
+ *     entry costs 1024, each line 3 * 1024 more, spread evenly over the
+ *     segment); item w < P - 1 ends at the first position of the slice whose
+ *     preceding entries cost at least floor(total * (w + 1) / P), and each
+ *     item's range is cut at segment boundaries into chunks.
+ * A slice takes the balanced rule when it holds at least P * 8192 entries and
+ * its by-chunk chunks, dealt in order each to the least loaded of P
+ * workgroups (a chunk costing its entries times r_s), would leave the most
+ * loaded with more than 9/8 of total / P (8 * most * P > 9 * total). */
 #define SPMV_BC_BLOCK_ROWS 32768
 
 /* Storage formats / kernels.  SPMV_AUTO lets the selector choose. */
@@ -106,7 +122,7 @@ typedef enum spmv_format {
                                x slices (S = opts.col_blocks in {1,2,4,8}; 0: the smallest
                                power of two that keeps a slice of x within 4 MiB, at most
                                8); the entries of each (slice, block) are ordered by
-                               column, cut into chunks of T entries (see
+                               column, cut into chunks and work items (see
                                SPMV_BC_BLOCK_ROWS above) and groups of 64, and each
                                group is reordered by row so that runs of one row are
                                neighbouring lanes.  Neighbouring lanes therefore gather
@@ -179,6 +195,7 @@ typedef struct spmv_info {
     int32_t chunk_entries; /* blocked COO: T, entries per chunk           */
     int32_t hot_slots;     /* blocked COO: hot rows per block (32)        */
     int32_t hot_min_len;   /* blocked COO: rows this long or longer may be hot (64*S+1) */
+    int32_t work_items;    /* blocked COO: work items, one workgroup each */
 } spmv_info;
 
 /* Arrays a handle can export (spmv_export) for bit-exact comparison. */
@@ -214,8 +231,8 @@ typedef enum spmv_array {
                               SPMV_A_ELL_VAL, SPMV_A_ELL_NNZ.                       */
     /* blocked COO: segment k*B + b holds the entries of x slice k and row block b
        (B = ceil(R/SPMV_BC_BLOCK_ROWS) blocks) ordered by column, ties in CSR order;
-       chunks are its consecutive runs of T (spmv_info.chunk_entries) entries, the
-       last one the remainder; groups a chunk's runs of 64.                           */
+       chunks are consecutive runs of a segment's entries and work items runs of
+       chunks, by the rules at SPMV_BC_BLOCK_ROWS; groups a chunk's runs of 64.     */
     SPMV_A_BC_CHUNK_GRP = 22,  /* int32 [chunks+1] first group of chunk c          */
     SPMV_A_BC_CHUNK_BLK = 23,  /* int32 [chunks]   row block of chunk c             */
     SPMV_A_BC_SLICE_CHUNK = 24,/* int32 [S+1]      first chunk of x slice k         */
@@ -232,8 +249,10 @@ typedef enum spmv_array {
                                   reordered by code, ties in column order; padding
                                   0xFFFF0000                                         */
     SPMV_A_BC_VAL = 28,        /* fp32 [groups*64]  values, padding +0.0f            */
-    SPMV_A_BC_WIDE = 29        /* int32 [wide*64]   columns of wide group w's slots,
+    SPMV_A_BC_WIDE = 29,       /* int32 [wide*64]   columns of wide group w's slots,
                                   padding 0                                          */
+    SPMV_A_BC_SLICE_ITEM = 30, /* int32 [S+1]      first work item of x slice k      */
+    SPMV_A_BC_ITEM_CHUNK = 31  /* int32 [items+1]  first chunk of work item i        */
 } spmv_array;
 
 typedef struct spmv_handle spmv_handle;

@@ -94,7 +94,7 @@ def _load():
                                                 ctypes.c_void_p, ctypes.c_void_p,
                                                 ctypes.c_void_p, ctypes.POINTER(_i64)]),
         "orc_coo_blocked": (ctypes.c_int, [_i64, _i64, _i64, _i32p, _i32p, _u32p, _i64, _i64,
-                                           _i64, _i64, _i64, _i64p] + [ctypes.c_void_p] * 8),
+                                           _i64, _i64, _i64, _i64p] + [ctypes.c_void_p] * 10),
         "orc_select_build": (ctypes.c_int, [_i64, _i64, _i64, _i32p, _i32p, _i64, _i64p]),
         "orc_bc_chunk_entries": (_i64, [_i64]),
     }
@@ -286,29 +286,31 @@ def csr_to_ell_xtile(row_ptrs, col_idx, values, block_rows=256):
 
 def csr_to_coo_blocked(row_ptrs, col_idx, values, num_cols, slices, block_rows, chunk_entries,
                        hot_slots, hot_min_len):
-    """Blocked COO: the arrays chunk_grp, chunk_blk, slice_chunk, hot, base, pk (uint32),
-    val (fp32 bit copies) and wide, as oracle.c defines them."""
+    """Blocked COO: the arrays chunk_grp, chunk_blk, slice_chunk, slice_item, item_chunk,
+    hot, base, pk (uint32), val (fp32 bit copies) and wide, as oracle.c defines them."""
     rp = _i32(row_ptrs)
     R = rp.shape[0] - 1
     ci = _i32(col_idx)
     vb = _bits(values)
     nnz = ci.shape[0]
     lib = _load()
-    sizes = np.zeros(3, np.int64)
+    sizes = np.zeros(4, np.int64)
     args = (R, num_cols, nnz, rp, ci, vb, slices, block_rows, chunk_entries, hot_slots,
             hot_min_len, sizes)
-    st = lib.orc_coo_blocked(*args, None, None, None, None, None, None, None, None)
+    st = lib.orc_coo_blocked(*args, *([None] * 10))
     if st != OK:
         raise ValueError(f"orc_coo_blocked: status {st}")
-    nch, ng, nw = (int(v) for v in sizes)
+    nch, ng, nw, nit = (int(v) for v in sizes)
     nblk = (R + block_rows - 1) // block_rows
     out = {"chunk_grp": np.zeros(nch + 1, np.int32), "chunk_blk": np.zeros(max(nch, 1), np.int32),
            "slice_chunk": np.zeros(slices + 1, np.int32),
+           "slice_item": np.zeros(slices + 1, np.int32), "item_chunk": np.zeros(nit + 1, np.int32),
            "hot": np.zeros(max(nblk * hot_slots, 1), np.int32),
            "base": np.zeros(max(ng, 1), np.int32), "pk": np.zeros(max(64 * ng, 1), np.uint32),
            "val": np.zeros(max(64 * ng, 1), np.uint32), "wide": np.zeros(max(64 * nw, 1), np.int32)}
     st = lib.orc_coo_blocked(*args, *(out[k].ctypes.data for k in (
-        "chunk_grp", "chunk_blk", "slice_chunk", "hot", "base", "pk", "val", "wide")))
+        "chunk_grp", "chunk_blk", "slice_chunk", "slice_item", "item_chunk", "hot", "base", "pk",
+        "val", "wide")))
     assert st == OK
     out["chunk_blk"] = out["chunk_blk"][:nch]
     out["hot"] = out["hot"][:nblk * hot_slots]

@@ -707,12 +707,27 @@ int orc_csr_to_ell_xtile(int64_t R, const int32_t *row_ptrs, const int32_t *col_
 /* an encoding, so the oracle writes out its definition:                    */
 /*   entry i of row r, column c: slice k = c / sc (sc = ceil(C/S), at least */
 /*   1), row block b = r / RT, segment s = k*B + b (B = ceil(R/RT) blocks). */
-/*   Entries in order of (s, c), ties in CSR order.  Each segment's run is  */
-/*   cut into chunks of E entries, the last one the remainder, which joins  */
-/*   the chunk before it when shorter than E/2 (integer halving); chunks    */
-/*   numbered in segment order; each chunk into groups of 64 entries (the   */
-/*   last shorter,                                                          */
-/*   padded to 64 slots).                                                   */
+/*   Entries in order of (s, c), ties in CSR order.  Chunks are runs of one */
+/*   segment's entries and work items runs of chunks, chosen slice by slice */
+/*   (P = 256 / S work items of a balanced slice, one per CU of its XCDs):  */
+/*   - by chunk: each segment's run cut into chunks of E entries, the last  */
+/*     one the remainder, which joins the chunk before it when shorter than */
+/*     E/2 (integer halving); each chunk its own work item;                 */
+/*   - balanced: cost of an entry of segment s, in 1/1024:                  */
+/*     r_s = floor((n_s + 3*lines_s) * 1024 / n_s), n_s its entries and     */
+/*     lines_s the entries that are the segment's first or whose column     */
+/*     c >> 5 (128-byte line of x) differs from the entry before; total =   */
+/*     sum of n_s*r_s over the slice; item w (0 <= w < P) runs from cut[w]  */
+/*     to cut[w+1], cut[0] the slice's first entry, cut[P] its end, cut[w]  */
+/*     the first position whose preceding entries of the slice cost at      */
+/*     least floor(total*w/P); an item's entries cut at segment ends into   */
+/*     chunks.                                                              */
+/*   A slice is balanced when it holds at least P*max(RT/4, 64) entries and */
+/*   its by-chunk chunks, each given in order to the least loaded of P      */
+/*   loads (a chunk adding its entries times r_s), leave the largest load   */
+/*   `most` with 8*most*P > 9*total.  Chunks and items are numbered slice   */
+/*   by slice; each chunk is cut into groups of 64 entries (the last        */
+/*   shorter, padded to 64 slots).                                          */
 /*   Hot rows of block b: its rows with at least hot_min_len entries,       */
 /*   longest first, ties by row, the first H (hot[b*H + h], -1 for unused). */
 /*   The code of an entry is r - b*RT, or RT + h when r is hot row h.       */
@@ -725,9 +740,10 @@ int orc_csr_to_ell_xtile(int64_t R, const int32_t *row_ptrs, const int32_t *col_
 /*   value bits 0, wide column 0.                                           */
 /*   chunk_grp[c] = first group of chunk c (chunks+1 entries),              */
 /*   chunk_blk[c] = its row block, slice_chunk[k] = first chunk of slice k  */
-/*   (S+1 entries).                                                         */
-/* sizes[0..2] = chunks, groups, wide groups; with chunk_grp == NULL only   */
-/* the sizes are computed.                                                  */
+/*   (S+1 entries), slice_item[k] = first work item of slice k (S+1),       */
+/*   item_chunk[i] = first chunk of work item i (items+1).                  */
+/* sizes[0..3] = chunks, groups, wide groups, work items; with chunk_grp == */
+/* NULL only the sizes are computed.                                        */
 /* ------------------------------------------------------------------------ */
 
 static const int64_t *g_hot_len;
@@ -748,10 +764,12 @@ static int orc_cmp_hot(const void *a, const void *b)
 int orc_coo_blocked(int64_t R, int64_t C, int64_t nnz, const int32_t *row_ptrs,
                     const int32_t *col_idx, const uint32_t *val_bits, int64_t S, int64_t RT,
                     int64_t E, int64_t H, int64_t hot_min_len, int64_t *sizes,
-                    int32_t *chunk_grp, int32_t *chunk_blk, int32_t *slice_chunk, int32_t *hot,
-                    int32_t *base, uint32_t *pk, uint32_t *val, int32_t *wide)
+                    int32_t *chunk_grp, int32_t *chunk_blk, int32_t *slice_chunk,
+                    int32_t *slice_item, int32_t *item_chunk, int32_t *hot, int32_t *base,
+                    uint32_t *pk, uint32_t *val, int32_t *wide)
 {
-    if (R < 0 || C < 0 || nnz < 0 || S < 1 || RT < 1 || E < 1 || H < 0 || RT + H > 0xFFFF)
+    if (R < 0 || C < 0 || nnz < 0 || S < 1 || S > 256 || RT < 1 || E < 1 || H < 0 ||
+        RT + H > 0xFFFF)
         return ORC_ERR_INVALID_ARG;
     const int64_t sc = C > 0 ? (C + S - 1) / S : 1;
     const int64_t B = (R + RT - 1) / RT;
@@ -825,67 +843,160 @@ int orc_coo_blocked(int64_t R, int64_t C, int64_t nnz, const int32_t *row_ptrs,
                 hot[b * H + h] = (int32_t)r;
         }
     }
-    /* chunks and groups */
-    int64_t nch = 0, ngrp = 0, nwide = 0;
-    if (chunk_grp)
-        chunk_grp[0] = 0;
+    /* chunks and work items: (segment, first entry, end) of every chunk, */
+    /* slice by slice, and the first chunk of every work item               */
+    const int64_t P = 256 / S;
+    int64_t *lines = (int64_t *)calloc((size_t)(nseg > 0 ? nseg : 1), sizeof(int64_t));
+    int64_t *rate = (int64_t *)calloc((size_t)(nseg > 0 ? nseg : 1), sizeof(int64_t));
+    int64_t *load = (int64_t *)calloc((size_t)P, sizeof(int64_t));
+    int64_t *cut = (int64_t *)calloc((size_t)P + 1, sizeof(int64_t));
+    /* at most one chunk per entry, plus one per work item's cut */
+    int64_t cap = nnz + S * P + 1;
+    int64_t *ch = (int64_t *)malloc(sizeof(int64_t) * 3 * (size_t)cap);
+    int64_t *item_first = (int64_t *)malloc(sizeof(int64_t) * (size_t)cap);
+    int64_t *slice_first_item = (int64_t *)malloc(sizeof(int64_t) * (size_t)(S + 1));
+    int64_t *slice_first_chunk = (int64_t *)malloc(sizeof(int64_t) * (size_t)(S + 1));
+    if (!lines || !rate || !load || !cut || !ch || !item_first || !slice_first_item ||
+        !slice_first_chunk) {
+        free(lines); free(rate); free(load); free(cut); free(ch); free(item_first);
+        free(slice_first_item); free(slice_first_chunk);
+        free(row); free(by_col); free(order); free(cnt_col); free(seg_start);
+        free(len); free(code); free(cand);
+        return ORC_ERR_INVALID_ARG;
+    }
     for (int64_t s = 0; s < nseg; ++s) {
-        if (s % B == 0 && slice_chunk)
-            slice_chunk[s / B] = (int32_t)nch;
-        for (int64_t e0 = seg_start[s], e1 = 0; e0 < seg_start[s + 1]; e0 = e1) {
-            /* runs of E entries; a last piece shorter than E/2 joins the run before it */
-            e1 = e0 + E < seg_start[s + 1] ? e0 + E : seg_start[s + 1];
-            if (seg_start[s + 1] - e1 < E / 2)
-                e1 = seg_start[s + 1];
-            for (int64_t g0 = e0; g0 < e1; g0 += 64) {
-                int64_t n = e1 - g0 < 64 ? e1 - g0 : 64;
-                int64_t lo = col_idx[order[g0]], hi = col_idx[order[g0 + n - 1]];
-                int is_wide = hi - lo > 65535;
-                if (pk) {
-                    /* lanes: the group's entries, stably reordered by code */
-                    int64_t lane_of[64];
-                    for (int64_t q = 0; q < n; ++q) {
-                        int64_t p = q;
-                        while (p > 0 && code[row[order[g0 + lane_of[p - 1]]]] >
-                                            code[row[order[g0 + q]]]) {
-                            lane_of[p] = lane_of[p - 1];
-                            --p;
-                        }
-                        lane_of[p] = q;
-                    }
-                    base[ngrp] = is_wide ? (int32_t)(-(nwide + 1)) : (int32_t)lo;
-                    for (int64_t l = 0; l < 64; ++l) {
-                        int64_t slot = ngrp * 64 + l;
-                        if (l < n) {
-                            int64_t i = order[g0 + lane_of[l]];
-                            int64_t off = is_wide ? 0 : col_idx[i] - lo;
-                            pk[slot] = (uint32_t)(code[row[i]] << 16) | (uint32_t)off;
-                            val[slot] = val_bits[i];
-                            if (is_wide)
-                                wide[nwide * 64 + l] = col_idx[i];
-                        } else {
-                            pk[slot] = 0xFFFF0000u;
-                            val[slot] = 0u;
-                            if (is_wide)
-                                wide[nwide * 64 + l] = 0;
-                        }
-                    }
+        const int64_t n = seg_start[s + 1] - seg_start[s];
+        for (int64_t j = seg_start[s]; j < seg_start[s + 1]; ++j)
+            if (j == seg_start[s] || (col_idx[order[j]] >> 5) != (col_idx[order[j - 1]] >> 5))
+                lines[s]++;
+        rate[s] = n > 0 ? (n + 3 * lines[s]) * 1024 / n : 0;
+    }
+    int64_t nch = 0, nitem = 0;
+    for (int64_t k = 0; k < S; ++k) {
+        const int64_t first = seg_start[k * B], end = seg_start[(k + 1) * B];
+        slice_first_item[k] = nitem;
+        slice_first_chunk[k] = nch;
+        /* the by-chunk cut, and its loads */
+        int64_t total = 0, most = 0;
+        for (int64_t p = 0; p < P; ++p)
+            load[p] = 0;
+        for (int64_t s = k * B; s < (k + 1) * B; ++s) {
+            total += (seg_start[s + 1] - seg_start[s]) * rate[s];
+            for (int64_t e0 = seg_start[s], e1 = 0; e0 < seg_start[s + 1]; e0 = e1) {
+                /* runs of E entries; a last piece shorter than E/2 joins the run before it */
+                e1 = e0 + E < seg_start[s + 1] ? e0 + E : seg_start[s + 1];
+                if (seg_start[s + 1] - e1 < E / 2)
+                    e1 = seg_start[s + 1];
+                int64_t least = 0;
+                for (int64_t p = 1; p < P; ++p)
+                    if (load[p] < load[least])
+                        least = p;
+                load[least] += (e1 - e0) * rate[s];
+                if (load[least] > most)
+                    most = load[least];
+                ch[3 * nch] = s;
+                ch[3 * nch + 1] = e0;
+                ch[3 * nch + 2] = e1;
+                item_first[nitem++] = nch++;
+            }
+        }
+        if (end - first >= P * (RT / 4 > 64 ? RT / 4 : 64) && 8 * most * P > 9 * total) {
+            /* balanced: drop the by-chunk cut of this slice, cut by cost */
+            nch = slice_first_chunk[k];
+            nitem = slice_first_item[k];
+            int64_t spent = 0, w = 1;   /* spent: cost of the entries before entry j */
+            cut[0] = first;
+            cut[P] = end;
+            for (int64_t s = k * B; s < (k + 1) * B; ++s)
+                for (int64_t j = seg_start[s]; j < seg_start[s + 1]; ++j) {
+                    while (w < P && spent >= total * w / P)
+                        cut[w++] = j;
+                    spent += rate[s];
                 }
-                nwide += is_wide;
-                ++ngrp;
+            while (w < P)
+                cut[w++] = end;
+            for (int64_t i = 0; i < P; ++i) {
+                item_first[nitem++] = nch;
+                int64_t s = k * B;
+                for (int64_t e0 = cut[i]; e0 < cut[i + 1];) {
+                    while (seg_start[s + 1] <= e0)
+                        ++s;
+                    int64_t e1 = cut[i + 1] < seg_start[s + 1] ? cut[i + 1] : seg_start[s + 1];
+                    ch[3 * nch] = s;
+                    ch[3 * nch + 1] = e0;
+                    ch[3 * nch + 2] = e1;
+                    ++nch;
+                    e0 = e1;
+                }
             }
-            if (chunk_grp) {
-                chunk_grp[nch + 1] = (int32_t)ngrp;
-                chunk_blk[nch] = (int32_t)(s % B);
-            }
-            ++nch;
         }
     }
-    if (slice_chunk)
-        slice_chunk[S] = (int32_t)nch;
+    slice_first_item[S] = nitem;
+    slice_first_chunk[S] = nch;
+    item_first[nitem] = nch;
+
+    /* groups of every chunk */
+    int64_t ngrp = 0, nwide = 0;
+    if (chunk_grp)
+        chunk_grp[0] = 0;
+    for (int64_t c = 0; c < nch; ++c) {
+        const int64_t s = ch[3 * c], e0 = ch[3 * c + 1], e1 = ch[3 * c + 2];
+        for (int64_t g0 = e0; g0 < e1; g0 += 64) {
+            int64_t n = e1 - g0 < 64 ? e1 - g0 : 64;
+            int64_t lo = col_idx[order[g0]], hi = col_idx[order[g0 + n - 1]];
+            int is_wide = hi - lo > 65535;
+            if (pk) {
+                /* lanes: the group's entries, stably reordered by code */
+                int64_t lane_of[64];
+                for (int64_t q = 0; q < n; ++q) {
+                    int64_t p = q;
+                    while (p > 0 && code[row[order[g0 + lane_of[p - 1]]]] >
+                                        code[row[order[g0 + q]]]) {
+                        lane_of[p] = lane_of[p - 1];
+                        --p;
+                    }
+                    lane_of[p] = q;
+                }
+                base[ngrp] = is_wide ? (int32_t)(-(nwide + 1)) : (int32_t)lo;
+                for (int64_t l = 0; l < 64; ++l) {
+                    int64_t slot = ngrp * 64 + l;
+                    if (l < n) {
+                        int64_t i = order[g0 + lane_of[l]];
+                        int64_t off = is_wide ? 0 : col_idx[i] - lo;
+                        pk[slot] = (uint32_t)(code[row[i]] << 16) | (uint32_t)off;
+                        val[slot] = val_bits[i];
+                        if (is_wide)
+                            wide[nwide * 64 + l] = col_idx[i];
+                    } else {
+                        pk[slot] = 0xFFFF0000u;
+                        val[slot] = 0u;
+                        if (is_wide)
+                            wide[nwide * 64 + l] = 0;
+                    }
+                }
+            }
+            nwide += is_wide;
+            ++ngrp;
+        }
+        if (chunk_grp) {
+            chunk_grp[c + 1] = (int32_t)ngrp;
+            chunk_blk[c] = (int32_t)(s % B);
+        }
+    }
+    if (chunk_grp) {
+        for (int64_t k = 0; k <= S; ++k) {
+            slice_chunk[k] = (int32_t)slice_first_chunk[k];
+            slice_item[k] = (int32_t)slice_first_item[k];
+        }
+        for (int64_t i = 0; i <= nitem; ++i)
+            item_chunk[i] = (int32_t)item_first[i];
+    }
     sizes[0] = nch;
     sizes[1] = ngrp;
     sizes[2] = nwide;
+    sizes[3] = nitem;
+    free(lines); free(rate); free(load); free(cut); free(ch); free(item_first);
+    free(slice_first_item); free(slice_first_chunk);
     free(row); free(by_col); free(order); free(cnt_col); free(seg_start);
     free(len); free(code); free(cand);
     return ORC_OK;

@@ -45,6 +45,7 @@ ARRAYS = {
     "xt_lidx": (21, np.int16), "bc_chunk_grp": (22, np.int32), "bc_chunk_blk": (23, np.int32),
     "bc_slice_chunk": (24, np.int32), "bc_hot": (25, np.int32), "bc_base": (26, np.int32),
     "bc_pk": (27, np.uint32), "bc_val": (28, np.float32), "bc_wide": (29, np.int32),
+    "bc_slice_item": (30, np.int32), "bc_item_chunk": (31, np.int32),
 }
 CG_NOALLOC_MAX_ROWS = 1048576   # SPMV_CG_NOALLOC_MAX_ROWS in include/spmv.h
 BC_BLOCK_ROWS = 32768           # SPMV_BC_BLOCK_ROWS: blocked COO rows per row block
@@ -83,7 +84,7 @@ class _Info(ctypes.Structure):
                 ("device_bytes", ctypes.c_int64), ("groups", ctypes.c_int64),
                 ("wide_groups", ctypes.c_int64), ("block_rows", ctypes.c_int32),
                 ("chunk_entries", ctypes.c_int32), ("hot_slots", ctypes.c_int32),
-                ("hot_min_len", ctypes.c_int32)]
+                ("hot_min_len", ctypes.c_int32), ("work_items", ctypes.c_int32)]
 
 
 class _TuneEntry(ctypes.Structure):
@@ -262,7 +263,8 @@ class Handle:
                      "device_bytes": info.device_bytes, "groups": info.groups,
                      "wide_groups": info.wide_groups, "block_rows": info.block_rows,
                      "chunk_entries": info.chunk_entries, "hot_slots": info.hot_slots,
-                     "hot_min_len": info.hot_min_len, **_stats_dict(info.stats)}
+                     "hot_min_len": info.hot_min_len, "work_items": info.work_items,
+                     **_stats_dict(info.stats)}
 
     @property
     def format(self) -> str:

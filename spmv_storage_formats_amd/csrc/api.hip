@@ -337,12 +337,14 @@ int64_t format_bytes(int32_t fmt, int64_t R, int64_t nnz, int64_t W, int64_t K,
         return 8 * slots + 8 * R + 4 * (R / kWave + 2) + 8 * (R / kWave + 1 + slots / kWave);
     }
     case SPMV_COO_BLOCKED: {
-        // upper bound: every segment and chunk may end in a partial group, and
-        // the group arrays carry kBcUnroll - 1 groups of tail padding
+        // upper bound: every segment, chunk and work-item cut may end in a
+        // partial group, and the group arrays carry kBcUnroll - 1 groups of
+        // tail padding; chunks and work items are at most one per group
         const int64_t nblk = (R + kBcRows - 1) / kBcRows;
-        const int64_t groups =
-            nnz / kWave + nnz / bc_chunk_entries(nnz) + kNumXcd * nblk + kBcUnroll;
-        return 8 * kWave * groups + 4 * groups + 4 * nblk * kBcHot + 8 * (groups + kNumXcd);
+        const int64_t groups = nnz / kWave + nnz / bc_chunk_entries(nnz) + kNumXcd * nblk +
+                               kBcCus + kBcUnroll;
+        return 8 * kWave * groups + 4 * groups + 4 * nblk * kBcHot + 12 * (groups + 1) +
+               8 * (kNumXcd + 1);
     }
     default: return 0;
     }
@@ -965,6 +967,7 @@ spmv_status spmv_get_info(const spmv_handle *h, spmv_info *info) {
         info->chunk_entries = static_cast<int32_t>(h->bc_chunk);
         info->hot_slots = kBcHot;
         info->hot_min_len = h->bc_hot_min_len;
+        info->work_items = static_cast<int32_t>(h->bc_items);
     }
     return SPMV_OK;
 }
@@ -1022,6 +1025,8 @@ ArrayRef array_ref(const spmv_handle *h, spmv_array which) {
     case SPMV_A_BC_PK: set(a.bc_pk, h->bc_groups * kWave, 4); break;
     case SPMV_A_BC_VAL: set(a.bc_val, h->bc_groups * kWave, 4); break;
     case SPMV_A_BC_WIDE: set(a.bc_wide, h->bc_wide_groups * kWave, 4); break;
+    case SPMV_A_BC_SLICE_ITEM: set(a.bc_slice_item, h->col_blocks + 1, 4); break;
+    case SPMV_A_BC_ITEM_CHUNK: set(a.bc_item_chunk, h->bc_items + 1, 4); break;
     case SPMV_A_LEN_HIST:
         r.host = h->hist.data();
         r.bytes = h->hist.size() * sizeof(int64_t);

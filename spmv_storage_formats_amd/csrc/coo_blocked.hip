@@ -105,6 +105,26 @@ __global__ __launch_bounds__(kThreads) void k_bc_seg_keys(int32_t nnz, const int
     key[i] = k * static_cast<uint32_t>(nblk) + static_cast<uint32_t>(row[i] / kBcRows);
 }
 
+// 1 where an entry, in (segment, column) order, is its segment's first or
+// lies in another 128-byte line of x than the entry before it: summed over a
+// segment, the x lines the segment touches.
+__global__ __launch_bounds__(kThreads) void k_bc_new_line(int32_t nnz,
+                                                          const uint32_t *__restrict__ seg,
+                                                          const int32_t *__restrict__ col,
+                                                          int32_t *__restrict__ flag) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (i >= nnz) return;
+    flag[i] = (i == 0 || seg[i] != seg[i - 1] || (col[i] >> 5) != (col[i - 1] >> 5)) ? 1 : 0;
+}
+
+// out[i] = src[at[i]]
+__global__ __launch_bounds__(kThreads) void k_bc_take(int64_t n, const int32_t *__restrict__ at,
+                                                      const int32_t *__restrict__ src,
+                                                      int32_t *__restrict__ out) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (i < n) out[i] = src[at[i]];
+}
+
 // Entry range of group g: its chunk by binary search over chunk_grp.
 __device__ inline void bc_group_range(int64_t g, int32_t nch, const int32_t *chunk_grp,
                                       const int32_t *chunk_e0, const int32_t *chunk_e1,
@@ -295,77 +315,98 @@ __device__ __forceinline__ void bc_wave_step(int lw, int n, int lane, const uint
 
 template <int U, bool kFarX>
 __global__ __launch_bounds__(kBcThreads) void k_coo_blocked(
-    int32_t R, int32_t per, int32_t slice_cols, const int32_t *__restrict__ slice_chunk,
-    const int32_t *__restrict__ chunk_grp, const int32_t *__restrict__ chunk_blk,
-    const int32_t *__restrict__ hot, const int32_t *__restrict__ base,
-    const uint32_t *__restrict__ pk, const float *__restrict__ val,
-    const int32_t *__restrict__ wide_col, const float *__restrict__ x, float *__restrict__ y) {
+    int32_t R, int32_t per, int32_t slice_cols, const int32_t *__restrict__ slice_item,
+    const int32_t *__restrict__ item_chunk, const int32_t *__restrict__ chunk_grp,
+    const int32_t *__restrict__ chunk_blk, const int32_t *__restrict__ hot,
+    const int32_t *__restrict__ base, const uint32_t *__restrict__ pk,
+    const float *__restrict__ val, const int32_t *__restrict__ wide_col,
+    const float *__restrict__ x, float *__restrict__ y) {
     __shared__ float part[kBcRows];
     __shared__ float priv[kBcWaves * kBcHot];
-    // slice k's chunks on XCDs [k*per, (k+1)*per): block b runs on XCD b % 8
+    // slice k's work items on XCDs [k*per, (k+1)*per): block b runs on XCD b % 8
     const int xcd = static_cast<int>(blockIdx.x % kNumXcd);
     const int k = xcd / per;
-    const int idx = static_cast<int>(blockIdx.x / kNumXcd) * per + xcd % per;
-    const int c = slice_chunk[k] + idx;
-    if (c >= slice_chunk[k + 1]) return;   // whole workgroup
-    const int b = chunk_blk[c];
-    const int32_t g0 = chunk_grp[c];
-    const int32_t n = chunk_grp[c + 1] - g0;   // groups of this chunk
-    const int64_t r0 = static_cast<int64_t>(b) * kBcRows;
-    const int nrows = static_cast<int>(min(static_cast<int64_t>(kBcRows), R - r0));
-    // the chunk's arrays and the slice's x through wave-uniform pointers, so
-    // every load below takes a 32-bit offset (slots past 2^31 included)
-    const uint32_t *pkc = pk + static_cast<int64_t>(g0) * kWave;
-    const float *valc = val + static_cast<int64_t>(g0) * kWave;
-    const int32_t *basec = base + g0;
+    const int it = slice_item[k] + static_cast<int>(blockIdx.x / kNumXcd) * per + xcd % per;
+    if (it >= slice_item[k + 1]) return;   // whole workgroup
+    const int c0 = item_chunk[it], c1 = item_chunk[it + 1];
+    if (c0 >= c1) return;                  // whole workgroup
     const int32_t col0 = k * slice_cols;   // a slice with a chunk starts below C
     const float *xs = x + col0;
     // -0.0 is the additive identity bit for bit: an untouched partial is
     // recognised and never added, so rows without entries keep their y bits
-    for (int i = threadIdx.x; i < nrows; i += kBcThreads) part[i] = -0.0f;
+    for (int i = threadIdx.x; i < kBcRows; i += kBcThreads) part[i] = -0.0f;
     for (int i = threadIdx.x; i < kBcWaves * kBcHot; i += kBcThreads) priv[i] = -0.0f;
     __syncthreads();
     const int lane = __lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     float *mine = priv + wave * kBcHot;
-    // The workgroup walks the chunk U * 16 groups at a time, wave w taking
-    // the U consecutive groups lw .. lw + U - 1
-    int lw = wave * U;
-    for (; lw + U <= n; lw += kBcWaves * U)
-        bc_wave_step<U, kFarX, false>(lw, n, lane, pkc, valc, basec, wide_col, col0, xs, part, mine);
-    if (lw < n)
-        bc_wave_step<U, kFarX, true>(lw, n, lane, pkc, valc, basec, wide_col, col0, xs, part, mine);
-    __syncthreads();
-    // every partial that was touched goes to y; a full block's partials are
-    // read 8 at a time, so one LDS wait covers 8 of them
-    if (nrows == kBcRows) {
+    // The item's chunks one after another, each with its block's partials
+    // flushed to y before the next
+    for (int c = c0; c < c1; ++c) {
+        const int b = chunk_blk[c];
+        const int32_t g0 = chunk_grp[c];
+        const int32_t n = chunk_grp[c + 1] - g0;   // groups of this chunk
+        const int64_t r0 = static_cast<int64_t>(b) * kBcRows;
+        const int nrows = static_cast<int>(min(static_cast<int64_t>(kBcRows), R - r0));
+        // the chunk's arrays through wave-uniform pointers, so every load
+        // below takes a 32-bit offset (slots past 2^31 included)
+        const uint32_t *pkc = pk + static_cast<int64_t>(g0) * kWave;
+        const float *valc = val + static_cast<int64_t>(g0) * kWave;
+        const int32_t *basec = base + g0;
+        // The workgroup walks the chunk U * 16 groups at a time, wave w taking
+        // the U consecutive groups lw .. lw + U - 1
+        int lw = wave * U;
+        for (; lw + U <= n; lw += kBcWaves * U)
+            bc_wave_step<U, kFarX, false>(lw, n, lane, pkc, valc, basec, wide_col, col0, xs, part,
+                                          mine);
+        if (lw < n)
+            bc_wave_step<U, kFarX, true>(lw, n, lane, pkc, valc, basec, wide_col, col0, xs, part,
+                                         mine);
+        __syncthreads();
+        // every partial that was touched goes to y (a full block's partials
+        // read 8 at a time, so one LDS wait covers 8 of them); when another
+        // chunk follows, each thread resets the partials it has just read
+        const bool more = c + 1 < c1;
+        if (nrows == kBcRows) {
 #pragma unroll
-        for (int j0 = 0; j0 < kBcRows / kBcThreads; j0 += 8) {
-            float s[8];
+            for (int j0 = 0; j0 < kBcRows / kBcThreads; j0 += 8) {
+                float s[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) s[j] = part[threadIdx.x + (j0 + j) * kBcThreads];
+                for (int j = 0; j < 8; ++j) s[j] = part[threadIdx.x + (j0 + j) * kBcThreads];
+                if (more) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if (__float_as_uint(s[j]) != 0x80000000u)
-                    unsafeAtomicAdd(&y[r0 + threadIdx.x + (j0 + j) * kBcThreads], s[j]);
+                    for (int j = 0; j < 8; ++j) part[threadIdx.x + (j0 + j) * kBcThreads] = -0.0f;
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (__float_as_uint(s[j]) != 0x80000000u)
+                        unsafeAtomicAdd(&y[r0 + threadIdx.x + (j0 + j) * kBcThreads], s[j]);
+            }
+        } else {
+            for (int i = threadIdx.x; i < nrows; i += kBcThreads) {
+                const float s = part[i];
+                if (more) part[i] = -0.0f;
+                if (__float_as_uint(s) != 0x80000000u) unsafeAtomicAdd(&y[r0 + i], s);
+            }
         }
-    } else {
-        for (int i = threadIdx.x; i < nrows; i += kBcThreads) {
-            const float s = part[i];
-            if (__float_as_uint(s) != 0x80000000u) unsafeAtomicAdd(&y[r0 + i], s);
-        }
-    }
-    if (threadIdx.x < kBcHot) {
-        const int32_t hr = hot[static_cast<int64_t>(b) * kBcHot + threadIdx.x];
-        if (hr >= 0) {
+        if (threadIdx.x < kBcHot) {
+            const int32_t hr = hot[static_cast<int64_t>(b) * kBcHot + threadIdx.x];
             float w[kBcWaves];
 #pragma unroll
             for (int wv = 0; wv < kBcWaves; ++wv) w[wv] = priv[wv * kBcHot + threadIdx.x];
-            float s = -0.0f;   // summed in wave order
+            if (more) {
 #pragma unroll
-            for (int wv = 0; wv < kBcWaves; ++wv) s += w[wv];
-            if (__float_as_uint(s) != 0x80000000u) unsafeAtomicAdd(&y[hr], s);
+                for (int wv = 0; wv < kBcWaves; ++wv) priv[wv * kBcHot + threadIdx.x] = -0.0f;
+            }
+            if (hr >= 0) {
+                float s = -0.0f;   // summed in wave order
+#pragma unroll
+                for (int wv = 0; wv < kBcWaves; ++wv) s += w[wv];
+                if (__float_as_uint(s) != 0x80000000u) unsafeAtomicAdd(&y[hr], s);
+            }
         }
+        if (!more) break;
+        __syncthreads();   // the resets land before the next chunk's updates
     }
 }
 
@@ -519,33 +560,121 @@ spmv_status build_coo_blocked(spmv_handle *h, int32_t R, int32_t C, int32_t nnz,
                             s));
     SPMV_HIP(hipStreamSynchronize(s));
 
-    // 3. chunks of T entries per segment, the last one the remainder, which
-    //    joins the chunk before it when shorter than T/2 (a sliver chunk would
-    //    flush a whole block's partials for a sliver of work: on 3.6M x 2M,
-    //    15 per row, 2 slices, 444 chunks 232 us against 222 chunks 146 us);
-    //    groups of 64 per chunk
+    // x lines touched per segment: new-line flags, their exclusive sum, read
+    // at the segment bounds
+    std::vector<int32_t> hl(static_cast<size_t>(nseg) + 1);
+    {
+        int32_t *flag = nullptr, *at = nullptr;
+        SPMV_TRY(scratch.alloc(&flag, static_cast<size_t>(nnz) + 1));
+        SPMV_TRY(scratch.alloc(&at, static_cast<size_t>(nseg) + 1));
+        k_bc_new_line<<<grid_for(nnz, kThreads), kThreads, 0, s>>>(nnz, seg_sorted, col2, flag);
+        SPMV_HIP(hipGetLastError());
+        SPMV_TRY(exclusive_scan(flag, flag, nnz, true, s, scratch));
+        k_bc_take<<<grid_for(nseg + 1, kThreads), kThreads, 0, s>>>(nseg + 1, bounds, flag, at);
+        SPMV_HIP(hipGetLastError());
+        SPMV_HIP(hipMemcpyAsync(hl.data(), at, sizeof(int32_t) * hl.size(),
+                                hipMemcpyDeviceToHost, s));
+        SPMV_HIP(hipStreamSynchronize(s));
+    }
+
+    // 3. chunks and work items, slice by slice.  By chunk: chunks of T
+    //    entries per segment, the last one the remainder, which joins the
+    //    chunk before it when shorter than T/2 (a sliver chunk would flush a
+    //    whole block's partials for a sliver of work: on 3.6M x 2M, 15 per
+    //    row, 2 slices, 444 chunks 232 us against 222 chunks 146 us), one
+    //    chunk per work item.  When those chunks, dealt in order each to the
+    //    least loaded of the slice's P CUs, would load one CU with more than
+    //    9/8 of an even share (a last round of a few chunks: 2 x 65 blocks of
+    //    32,768 rows, 15 per row, 149 us against 93 for 2 x 64), the slice is
+    //    cut instead into P work items of equal cost, each an entry plus
+    //    kBcLineCost per x line of its segment (2 x 65 blocks: 100 us; a
+    //    partial last block, whose few rows share fewer x lines, costs more
+    //    per entry: 118 against 135 us with items of equal entries); groups
+    //    of 64 per chunk
     const int64_t T = h->bc_chunk;
-    std::vector<int32_t> cgrp{0}, cblk, ce0, ce1, schunk(static_cast<size_t>(S) + 1, 0);
+    const int32_t per = kNumXcd / S;
+    const int64_t P = kBcCus / S;
+    std::vector<int32_t> cgrp{0}, cblk, ce0, ce1, schunk(static_cast<size_t>(S) + 1, 0),
+        sitem(static_cast<size_t>(S) + 1, 0), ichunk;
+    std::vector<int64_t> dyn, load, cut(static_cast<size_t>(P) + 1);
     int64_t groups = 0;
-    for (int64_t sg = 0; sg < nseg; ++sg) {
-        if (sg % nblk == 0) schunk[static_cast<size_t>(sg / nblk)] = static_cast<int32_t>(cblk.size());
-        for (int64_t e = hb[sg], e1 = 0; e < hb[sg + 1]; e = e1) {
-            e1 = std::min<int64_t>(e + T, hb[sg + 1]);
-            if (hb[sg + 1] - e1 < T / 2) e1 = hb[sg + 1];   // a short last piece joins this chunk
-            groups += (e1 - e + kWave - 1) / kWave;
-            if (groups * kWave > (int64_t{1} << 40)) return SPMV_ERR_TOO_LARGE;
-            cgrp.push_back(static_cast<int32_t>(groups));
-            cblk.push_back(static_cast<int32_t>(sg % nblk));
-            ce0.push_back(static_cast<int32_t>(e));
-            ce1.push_back(static_cast<int32_t>(e1));
+    auto add_chunk = [&](int64_t sg, int64_t e, int64_t e1) {
+        groups += (e1 - e + kWave - 1) / kWave;
+        cgrp.push_back(static_cast<int32_t>(groups));
+        cblk.push_back(static_cast<int32_t>(sg % nblk));
+        ce0.push_back(static_cast<int32_t>(e));
+        ce1.push_back(static_cast<int32_t>(e1));
+    };
+    // cost of one entry of segment sg, in 1/1024
+    auto rate = [&](int64_t sg) -> int64_t {
+        const int64_t n = hb[sg + 1] - hb[sg];
+        return n > 0 ? (n + kBcLineCost * (hl[sg + 1] - hl[sg])) * 1024 / n : 0;
+    };
+    for (int32_t k = 0; k < S; ++k) {
+        const int64_t sg0 = static_cast<int64_t>(k) * nblk, sg1 = sg0 + nblk;
+        const int64_t s0 = hb[sg0], s1 = hb[sg1];
+        schunk[k] = static_cast<int32_t>(cblk.size());
+        sitem[k] = static_cast<int32_t>(ichunk.size());
+        dyn.clear();
+        int64_t total = 0;
+        for (int64_t sg = sg0; sg < sg1; ++sg) {
+            total += (hb[sg + 1] - hb[sg]) * rate(sg);
+            for (int64_t e = hb[sg], e1 = 0; e < hb[sg + 1]; e = e1) {
+                e1 = std::min<int64_t>(e + T, hb[sg + 1]);
+                if (hb[sg + 1] - e1 < T / 2) e1 = hb[sg + 1];   // a short last piece joins this chunk
+                dyn.insert(dyn.end(), {sg, e, e1});
+            }
         }
+        bool balanced = false;
+        if (s1 - s0 >= P * kBcChunkMin) {
+            load.assign(static_cast<size_t>(P), 0);
+            int64_t most = 0;
+            for (size_t i = 0; i < dyn.size(); i += 3) {
+                auto least = std::min_element(load.begin(), load.end());
+                *least += (dyn[i + 2] - dyn[i + 1]) * rate(dyn[i]);
+                most = std::max(most, *least);
+            }
+            balanced = kBcSkewDen * most * P > kBcSkewNum * total;
+        }
+        if (!balanced) {
+            for (size_t i = 0; i < dyn.size(); i += 3) {
+                ichunk.push_back(static_cast<int32_t>(cblk.size()));
+                add_chunk(dyn[i], dyn[i + 1], dyn[i + 2]);
+            }
+        } else {
+            // item w ends at the first position whose preceding entries of
+            // the slice cost at least total * (w + 1) / P
+            cut[0] = s0;
+            cut[static_cast<size_t>(P)] = s1;
+            for (int64_t w = 1, sg = sg0, acc = 0; w < P; ++w) {
+                const int64_t t = total * w / P;
+                while (acc + (hb[sg + 1] - hb[sg]) * rate(sg) < t) {
+                    acc += (hb[sg + 1] - hb[sg]) * rate(sg);
+                    ++sg;
+                }
+                const int64_t r = rate(sg);
+                cut[static_cast<size_t>(w)] = hb[sg] + (r > 0 ? (t - acc + r - 1) / r : 0);
+            }
+            for (int64_t w = 0, sg = sg0; w < P; ++w) {
+                ichunk.push_back(static_cast<int32_t>(cblk.size()));
+                for (int64_t e = cut[static_cast<size_t>(w)]; e < cut[static_cast<size_t>(w) + 1];) {
+                    while (hb[sg + 1] <= e) ++sg;
+                    const int64_t e1 = std::min<int64_t>(cut[static_cast<size_t>(w) + 1], hb[sg + 1]);
+                    add_chunk(sg, e, e1);
+                    e = e1;
+                }
+            }
+        }
+        if (groups * kWave > (int64_t{1} << 40)) return SPMV_ERR_TOO_LARGE;
     }
     schunk[static_cast<size_t>(S)] = static_cast<int32_t>(cblk.size());
+    sitem[static_cast<size_t>(S)] = static_cast<int32_t>(ichunk.size());
+    ichunk.push_back(static_cast<int32_t>(cblk.size()));
     const int32_t nch = static_cast<int32_t>(cblk.size());
-    int32_t most = 0;
-    for (int32_t k = 0; k < S; ++k) most = std::max(most, schunk[k + 1] - schunk[k]);
-    const int32_t per = kNumXcd / S;
-    h->bc_grid = static_cast<int64_t>(kNumXcd) * ((most + per - 1) / per);
+    int32_t most_items = 0;
+    for (int32_t k = 0; k < S; ++k) most_items = std::max(most_items, sitem[k + 1] - sitem[k]);
+    h->bc_grid = static_cast<int64_t>(kNumXcd) * ((most_items + per - 1) / per);
+    h->bc_items = sitem[static_cast<size_t>(S)];
     h->num_tiles = nch;
     h->bc_groups = groups;
     SPMV_TRY(owned(h, &h->a.bc_chunk_grp, nch + 1));
@@ -556,6 +685,12 @@ spmv_status build_coo_blocked(spmv_handle *h, int32_t R, int32_t C, int32_t nnz,
     SPMV_HIP(hipMemcpyAsync(h->a.bc_chunk_blk, cblk.data(), sizeof(int32_t) * cblk.size(),
                             hipMemcpyHostToDevice, s));
     SPMV_HIP(hipMemcpyAsync(h->a.bc_slice_chunk, schunk.data(), sizeof(int32_t) * schunk.size(),
+                            hipMemcpyHostToDevice, s));
+    SPMV_TRY(owned(h, &h->a.bc_slice_item, S + 1));
+    SPMV_TRY(owned(h, &h->a.bc_item_chunk, static_cast<int64_t>(ichunk.size())));
+    SPMV_HIP(hipMemcpyAsync(h->a.bc_slice_item, sitem.data(), sizeof(int32_t) * sitem.size(),
+                            hipMemcpyHostToDevice, s));
+    SPMV_HIP(hipMemcpyAsync(h->a.bc_item_chunk, ichunk.data(), sizeof(int32_t) * ichunk.size(),
                             hipMemcpyHostToDevice, s));
     int32_t *e01 = nullptr;
     SPMV_TRY(scratch.alloc(&e01, 2 * static_cast<size_t>(nch)));
@@ -604,12 +739,12 @@ hipError_t launch_coo_blocked(const spmv_handle *h, const float *x, float *y, hi
     const dim3 grid(static_cast<unsigned>(h->bc_grid));
     if (h->slice_cols > (1 << 30))
         k_coo_blocked<kBcUnroll, true><<<grid, kBcThreads, 0, s>>>(
-            R, per, h->slice_cols, a.bc_slice_chunk, a.bc_chunk_grp, a.bc_chunk_blk, a.bc_hot,
-            a.bc_base, a.bc_pk, a.bc_val, a.bc_wide, x, y);
+            R, per, h->slice_cols, a.bc_slice_item, a.bc_item_chunk, a.bc_chunk_grp,
+            a.bc_chunk_blk, a.bc_hot, a.bc_base, a.bc_pk, a.bc_val, a.bc_wide, x, y);
     else
         k_coo_blocked<kBcUnroll, false><<<grid, kBcThreads, 0, s>>>(
-            R, per, h->slice_cols, a.bc_slice_chunk, a.bc_chunk_grp, a.bc_chunk_blk, a.bc_hot,
-            a.bc_base, a.bc_pk, a.bc_val, a.bc_wide, x, y);
+            R, per, h->slice_cols, a.bc_slice_item, a.bc_item_chunk, a.bc_chunk_grp,
+            a.bc_chunk_blk, a.bc_hot, a.bc_base, a.bc_pk, a.bc_val, a.bc_wide, x, y);
     return hipGetLastError();
 }
 

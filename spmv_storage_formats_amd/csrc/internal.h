@@ -49,9 +49,12 @@ constexpr int kXtileAutoRows = 64 * kTileRows;
 // workgroup), hot-row slots per block and the length above which a row is hot
 // (kBcHotPerSlice * slices), one workgroup's threads and groups in flight per
 // wave, the largest x slice of the automatic slice count (4 MiB: one XCD's
-// L2), and the chunk rule (bc_chunk_entries): a chunk, one workgroup's work,
-// holds about 1.1 * nnz / kBcCus entries, so that the chunks fill the CUs
-// about once, and at least kBcChunkMin.
+// L2), and the chunk rule (bc_chunk_entries): a chunk holds about 1.1 * nnz /
+// kBcCus entries, so that the chunks fill the CUs about once, and at least
+// kBcChunkMin.  A slice whose chunks would leave the most loaded of its CUs
+// with more than kBcSkewNum / kBcSkewDen of an even share is cut instead into
+// one work item per CU of equal cost, an entry costing 1 and each x line its
+// segment touches kBcLineCost more.
 // Measured on the power-law 4M-row matrix and the 2M-row skewed one, with
 // every group's loads and gathers in flight together: 16384-row blocks in
 // chunks of 65536 with 6 groups per wave (two workgroups per CU) 274 and 107
@@ -66,6 +69,8 @@ constexpr int kBcUnroll = 6;
 constexpr int64_t kBcSliceBytes = 4 << 20;
 constexpr int64_t kBcCus = 256;
 constexpr int64_t kBcChunkMin = kBcRows / 4;
+constexpr int64_t kBcLineCost = 3;
+constexpr int64_t kBcSkewNum = 9, kBcSkewDen = 8;
 
 // Validation flags written by the analysis kernels.
 enum : int { kFlagBadRowPtrs = 1, kFlagBadCol = 2, kFlagBadRow = 4, kFlagUnsortedRows = 8 };
@@ -109,6 +114,8 @@ struct DevArrays {
     int32_t *bc_chunk_grp = nullptr;   // [chunks + 1] first group of each chunk
     int32_t *bc_chunk_blk = nullptr;   // [chunks] row block of each chunk
     int32_t *bc_slice_chunk = nullptr; // [slices + 1] first chunk of each x slice
+    int32_t *bc_slice_item = nullptr;  // [slices + 1] first work item of each x slice
+    int32_t *bc_item_chunk = nullptr;  // [items + 1] first chunk of each work item
     int32_t *bc_hot = nullptr;         // [blocks * kBcHot] hot rows, -1 unused
     int32_t *bc_base = nullptr;        // [groups] smallest column, or -(w+1): wide group w
     uint32_t *bc_pk = nullptr;         // [groups * 64] code << 16 | column offset
@@ -147,6 +154,7 @@ struct spmv_handle {
     int64_t bc_chunk = 0;           // entries per chunk (a segment's last may hold fewer)
     int64_t bc_wide_groups = 0;
     int64_t bc_grid = 0;            // workgroups of one launch
+    int64_t bc_items = 0;           // work items, one workgroup each
     int32_t bc_hot_min_len = 0;     // rows of at least this length may be hot
 };
 

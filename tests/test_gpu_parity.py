@@ -201,7 +201,9 @@ def check_blocked(h, w):
     assert i["chunk_entries"] == oracle.bc_chunk_entries(w.nnz)
     assert i["num_tiles"] == o["chunk_blk"].size and i["groups"] == o["base"].size
     assert i["wide_groups"] * 64 == o["wide"].size
-    for name in ("chunk_grp", "chunk_blk", "slice_chunk", "hot", "base", "pk", "wide"):
+    assert i["work_items"] + 1 == o["item_chunk"].size
+    for name in ("chunk_grp", "chunk_blk", "slice_chunk", "slice_item", "item_chunk", "hot",
+                 "base", "pk", "wide"):
         assert np.array_equal(h.array("bc_" + name), o[name]), name
     assert np.array_equal(bits(h.array("bc_val")), bits(o["val"]))
 
@@ -689,6 +691,45 @@ def test_blocked_hot_rows(dev):
     y_ref, bound = oracle.spmv_csr(w.row_ptrs, w.col_idx, w.values, w.x, w.y)
     _, _, _, x, y0 = to_dev(w, dev)
     assert_rows(run_once(h, x, y0), y_ref, bound, "hot rows")
+
+
+@pytest.mark.parametrize("blocks,extra_rows,balanced", [(64, 0, False), (65, 0, True),
+                                                        (65, 11_000, True)])
+def test_blocked_balanced_items(dev, blocks, extra_rows, balanced):
+    """2 x slices of 2M columns, 2 entries per row.  With 64 row blocks each
+    slice's 128 chunks fill its 128 CUs once and stay one chunk per work
+    item; with 65 blocks (and with a partial 66th) the 130-odd chunks would
+    leave a short second round, so each slice is cut into 128 work items of
+    equal cost, chunks split at the items' ends, several chunks per item.
+    Arrays bit-exact against the oracle; y within the row bound, once and
+    twice in a row (the partials reset between an item's chunks)."""
+    rng = np.random.default_rng(4100 + blocks + extra_rows)
+    R, C = blocks * spmv.BC_BLOCK_ROWS + extra_rows, 2_000_000
+    ci = np.sort(rng.integers(0, C, size=(R, 2)), axis=1)
+    ci[:, 1] += ci[:, 0] == ci[:, 1]
+    ci = np.minimum(ci, C - 1).reshape(-1).astype(np.int32)
+    rp = np.arange(0, 2 * R + 1, 2, dtype=np.int32)
+    w = synth.Workload("balanced", R, C, rp, ci, rng.uniform(-1, 1, ci.size).astype(np.float32),
+                       rng.uniform(-1, 1, C).astype(np.float32),
+                       rng.uniform(-1, 1, R).astype(np.float32))
+    print(f"[case] blocked items R={R} nnz={w.nnz}", flush=True)
+    h = build("coo_blocked", w, dev)
+    assert h.info["col_blocks"] == 2
+    items = h.info["work_items"]
+    if balanced:
+        assert items == 256 and h.info["num_tiles"] > items
+    else:
+        assert items == h.info["num_tiles"]
+    check_builder(h, w)
+    y_ref, bound = oracle.spmv_csr(w.row_ptrs, w.col_idx, w.values, w.x, w.y)
+    _, _, _, x, y0 = to_dev(w, dev)
+    assert_rows(run_once(h, x, y0), y_ref, bound, f"items {blocks}+{extra_rows}")
+    y = y0.clone()
+    h.run(x, y)
+    h.run(x, y)
+    torch.cuda.synchronize()
+    y2 = 2 * (y_ref - w.y.astype(np.float64)) + w.y.astype(np.float64)
+    assert_rows(y.cpu().numpy(), y2, 2 * bound, f"items {blocks}+{extra_rows} twice")
 
 
 @pytest.mark.parametrize("S", [1, 2])

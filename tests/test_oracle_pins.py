@@ -874,6 +874,143 @@ def test_coo_blocked_chunk_remainder(E, chunk_grp):
     assert o["slice_chunk"].tolist() == [0, len(chunk_grp) - 1]
 
 
+def _one_line_per_entry(rows, per_row, S, sc):
+    """rows one-row blocks (RT = 1) of per_row entries in x slice 0, columns
+    32 apart so every entry has a 128-byte line of x to itself."""
+    rp = np.arange(0, (rows + 1) * per_row, per_row).astype(np.int32)
+    ci = np.tile(32 * np.arange(per_row), rows).astype(np.int32)
+    assert ci.max() < sc
+    return rp, ci, np.ones(rows * per_row, np.float32), S * sc
+
+
+def test_coo_blocked_balanced_uniform_rate():
+    """Hand-derived balanced slice.  8 slices (P = 32 items each), 33 one-row
+    blocks of 100 entries in slice 0, each entry on its own x line: every
+    entry costs (100 + 3*100) * 1024 / 100 = 4096.  By chunk (T = 200: one
+    chunk per segment) 33 chunks go to 32 loads, the last onto the first:
+    most = 2 * 100 * 4096, total = 3300 * 4096, and 8*most*32 = 209,715,200
+    > 9*total = 121,651,200, so the slice is balanced.  With one rate the
+    cost before position j is 4096*j, so item w starts at the first j with
+    4096*j >= floor(3300*4096*w/32), i.e. j = ceil(3300*w/32); its range is
+    cut at multiples of 100 (segment ends) into chunks.  Slices 1..7 are
+    empty: no items, no chunks."""
+    S, P, rows, n = 8, 32, 33, 100
+    rp, ci, v, C = _one_line_per_entry(rows, n, S, 3200)
+    o = oracle.csr_to_coo_blocked(rp, ci, v, C, S, 1, 200, 0, 10**6)
+    cut = [-(-rows * n * w // P) for w in range(P + 1)]
+    assert cut[1] == 104 and cut[2] == 207 and cut[16] == 1650 and cut[P] == 3300
+    chunks, first = [], []
+    for w in range(P):
+        first.append(len(chunks))
+        e = cut[w]
+        while e < cut[w + 1]:
+            e1 = min(cut[w + 1], (e // n + 1) * n)
+            chunks.append((e // n, e, e1))
+            e = e1
+    first.append(len(chunks))
+    assert o["slice_item"].tolist() == [0] + [P] * S
+    assert o["item_chunk"].tolist() == first
+    assert o["chunk_blk"].tolist() == [b for b, _, _ in chunks]
+    assert o["slice_chunk"].tolist() == [0] + [len(chunks)] * S
+    assert o["chunk_grp"].tolist() == np.cumsum(
+        [0] + [-(-(e1 - e0) // 64) for _, e0, e1 in chunks]).tolist()
+    # each item holds 103 or 104 entries, the even share of 3300 over 32
+    assert {cut[w + 1] - cut[w] for w in range(P)} == {103, 104}
+
+
+def test_coo_blocked_even_slice_stays_by_chunk():
+    """As above with 32 blocks: the 32 chunks fill the 32 loads once, most =
+    100 * 4096 = total / 32, 8*most*32 = 104,857,600 <= 9*total =
+    117,964,800: one chunk per segment, each its own item."""
+    S, rows, n = 8, 32, 100
+    rp, ci, v, C = _one_line_per_entry(rows, n, S, 3200)
+    o = oracle.csr_to_coo_blocked(rp, ci, v, C, S, 1, 200, 0, 10**6)
+    assert o["chunk_blk"].tolist() == list(range(rows))
+    assert o["item_chunk"].tolist() == list(range(rows + 1))
+    assert o["slice_item"].tolist() == [0] + [rows] * S
+
+
+def test_coo_blocked_small_slice_stays_by_chunk():
+    """33 blocks of 60 entries (1980 < 32 * max(RT/4, 64) = 2048 entries):
+    the slice is too small to balance, whatever its loads."""
+    S, rows, n = 8, 33, 60
+    rp, ci, v, C = _one_line_per_entry(rows, n, S, 3200)
+    o = oracle.csr_to_coo_blocked(rp, ci, v, C, S, 1, 200, 0, 10**6)
+    assert o["item_chunk"].tolist() == list(range(rows + 1))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_coo_blocked_balanced_cuts_follow_cost(seed):
+    """Slices whose by-chunk chunks overload one CU (a few row blocks past a
+    multiple of P, x lines shared unevenly between blocks): every balanced
+    item starts where the cost of the slice's entries before it first
+    reaches floor(total * w / P), with each entry's cost recomputed here from
+    the matrix (lines counted by a plain loop over the column-sorted
+    segment); chunks never cross a segment; a by-chunk slice has one chunk
+    per item."""
+    rng = np.random.default_rng(700 + seed)
+    S, RT = 2, 64
+    P = 256 // S
+    nblk = P + int(rng.integers(1, 5))
+    R = nblk * RT - int(rng.integers(0, RT // 2))
+    C = S * 4096
+    lens = rng.integers(2, 6, R)
+    lens[: R // 3] = rng.integers(4, 12, R // 3)
+    cols, vals = [], []
+    for r in range(R):
+        k = int(rng.integers(0, S))
+        span = 256 if r % 5 else 4096          # some rows keep to a few lines
+        cols.append(np.sort(rng.choice(span, int(lens[r]), replace=False)) + k * 4096)
+    rp = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    ci = np.concatenate(cols).astype(np.int32)
+    v = np.ones(ci.size, np.float32)
+    T = 64
+    o = oracle.csr_to_coo_blocked(rp, ci, v, C, S, RT, T, 0, 10**6)
+    rows = np.repeat(np.arange(R), lens)
+    sc = C // S
+    seg = (ci // sc) * nblk + rows // RT
+    runs = [sorted((int(ci[i]), i) for i in np.flatnonzero(seg == s)) for s in range(S * nblk)]
+    rate = []
+    for run in runs:
+        lines = sum(1 for j in range(len(run))
+                    if j == 0 or run[j][0] >> 5 != run[j - 1][0] >> 5)
+        rate.append((len(run) + 3 * lines) * 1024 // len(run) if run else 0)
+    start = np.cumsum([0] + [len(r) for r in runs])
+    chunk_e = []                               # (segment, first, end) in entry positions
+    grp = o["chunk_grp"]
+    pos = 0
+    for c, b in enumerate(o["chunk_blk"].tolist()):
+        # each chunk's entry count from its groups' real slots
+        pk = o["pk"].reshape(-1, 64)[grp[c]:grp[c + 1]]
+        n = int((pk >> 16 != 0xFFFF).sum())
+        s = next(s for s in range(S * nblk) if start[s] <= pos < start[s + 1])
+        assert s % nblk == b and pos + n <= start[s + 1]   # inside one segment
+        chunk_e.append((s, pos, pos + n))
+        pos += n
+    assert pos == ci.size
+    balanced = 0
+    for k in range(S):
+        items = range(o["slice_item"][k], o["slice_item"][k + 1])
+        first, end = start[k * nblk], start[(k + 1) * nblk]
+        cost = [0]
+        for s in range(k * nblk, (k + 1) * nblk):
+            for _ in range(len(runs[s])):
+                cost.append(cost[-1] + rate[s])
+        total = cost[-1]
+        if len(items) == P and end - first >= P * 64:
+            balanced += 1
+            for w, it in enumerate(items):
+                if w == 0:
+                    continue
+                e0 = chunk_e[o["item_chunk"][it]][1] - first if o["item_chunk"][it] < len(chunk_e) \
+                    else end - first
+                t = total * w // P
+                assert cost[e0] >= t and (e0 == 0 or cost[e0 - 1] < t)
+        else:
+            assert all(o["item_chunk"][it + 1] - o["item_chunk"][it] == 1 for it in items)
+    assert balanced >= 1
+
+
 def test_coo_blocked_y_by_decoding():
     """y from the decoded slots (a plain loop) equals the dense product on a
     matrix with wide groups and hot rows."""

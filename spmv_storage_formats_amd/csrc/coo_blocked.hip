@@ -19,8 +19,12 @@
 //     entries of (slice k, block b) form segment k*nblk + b, ordered by column
 //     (ties keep CSR order); segments are cut into chunks of T entries (T =
 //     bc_chunk_entries(nnz); the last of a segment the remainder, joined to
-//     the chunk before it when shorter than T/2) and chunks into groups of 64
-//     consecutive entries;
+//     the chunk before it when shorter than T/2), one chunk per work item --
+//     unless those chunks would leave a short last round on the slice's CUs:
+//     then the slice is cut into one work item per CU of equal cost (an entry
+//     1, each x line its segment touches kBcLineCost more) and each item's
+//     range into chunks at segment ends; chunks into groups of 64 consecutive
+//     entries;
 //   - inside a group the entries are reordered by row code (stable), so equal
 //     rows are neighbouring lanes; the code of an entry is its row's index
 //     within the block, or kBcRows + h for the block's hot row h (the
@@ -32,20 +36,23 @@
 //     or -(w+1) when its columns span more than 65535, in which case the
 //     columns are bc_wide[w*64 + lane] (pads 0);
 //   - bc_chunk_grp[c] first group of chunk c, bc_chunk_blk[c] its row block,
-//     bc_slice_chunk[k] the first chunk of slice k, bc_hot[b*kBcHot + h] the
-//     hot rows of block b (-1 unused).
+//     bc_slice_chunk[k] the first chunk of slice k, bc_slice_item[k] its first
+//     work item, bc_item_chunk[i] the first chunk of item i,
+//     bc_hot[b*kBcHot + h] the hot rows of block b (-1 unused).
 //
-// Kernel: one workgroup per chunk (slice k's chunks on the XCDs k*8/S ..
-// (k+1)*8/S - 1, so each XCD's L2 holds one slice of x); the block's row
-// partials live in LDS; each wave takes six consecutive groups at a time,
+// Kernel: one workgroup per work item (slice k's items on the XCDs k*8/S ..
+// (k+1)*8/S - 1, so each XCD's L2 holds one slice of x), walking the item's
+// chunks one after another; a chunk's block's row partials live in LDS; each
+// wave takes six consecutive groups at a time,
 // gathers x, sums runs of equal codes with a DPP segmented scan (one ballot
 // of neighbouring equal codes picks the steps the group's runs need, none
 // when every row holds a single lane) and adds each run's total to its partial:
 // hot rows by a plain add into the wave's own slot, other rows by a
 // compare-and-swap loop (an LDS float atomic add costs ~190 clocks per wave
 // instruction on gfx950, a CAS ~28, a plain read-modify-write ~16); finally
-// every non-zero partial is added to y with a global atomic (chunks of the
-// same rows run concurrently).
+// every touched partial is added to y with a global atomic (chunks of the
+// same rows run concurrently) and, when another chunk of the item follows,
+// reset.
 #include <algorithm>
 #include <vector>
 

@@ -693,43 +693,59 @@ def test_blocked_hot_rows(dev):
     assert_rows(run_once(h, x, y0), y_ref, bound, "hot rows")
 
 
-@pytest.mark.parametrize("blocks,extra_rows,balanced", [(64, 0, False), (65, 0, True),
-                                                        (65, 11_000, True)])
-def test_blocked_balanced_items(dev, blocks, extra_rows, balanced):
+@pytest.mark.parametrize("blocks,extra_rows,mode", [(64, 0, "chunk"), (65, 0, "balanced"),
+                                                     (65, 11_000, "balanced"), (65, 0, "mixed")])
+def test_blocked_balanced_items(dev, blocks, extra_rows, mode):
     """2 x slices of 2M columns, 2 entries per row.  With 64 row blocks each
     slice's 128 chunks fill its 128 CUs once and stay one chunk per work
     item; with 65 blocks (and with a partial 66th) the 130-odd chunks would
     leave a short second round, so each slice is cut into 128 work items of
     equal cost, chunks split at the items' ends, several chunks per item.
-    Arrays bit-exact against the oracle; y within the row bound, once and
-    twice in a row (the partials reset between an item's chunks)."""
-    rng = np.random.default_rng(4100 + blocks + extra_rows)
+    Mixed: every row's entries in the first slice but one row in 8 with a
+    third entry in the second, which is then too small to balance (one chunk
+    per item) while the first is balanced.  Arrays bit-exact against the
+    oracle; y within the row bound, once and twice in a row (the partials
+    reset between an item's chunks)."""
+    rng = np.random.default_rng(4100 + blocks + extra_rows + (mode == "mixed"))
     R, C = blocks * spmv.BC_BLOCK_ROWS + extra_rows, 2_000_000
-    ci = np.sort(rng.integers(0, C, size=(R, 2)), axis=1)
-    ci[:, 1] += ci[:, 0] == ci[:, 1]
-    ci = np.minimum(ci, C - 1).reshape(-1).astype(np.int32)
-    rp = np.arange(0, 2 * R + 1, 2, dtype=np.int32)
+    lo = C // 2 if mode == "mixed" else C
+    cols = np.sort(rng.integers(0, lo, size=(R, 2)), axis=1)
+    cols[:, 1] += cols[:, 0] == cols[:, 1]
+    cols = np.minimum(cols, C - 1)
+    if mode == "mixed":
+        third = np.where(np.arange(R) % 8 == 0, rng.integers(C // 2, C, size=R), -1)
+        lens = 2 + (third >= 0)
+        ci = np.concatenate([np.concatenate([c, [t]]) if t >= 0 else c
+                             for c, t in zip(cols, third)]).astype(np.int32)
+        rp = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    else:
+        ci = cols.reshape(-1).astype(np.int32)
+        rp = np.arange(0, 2 * R + 1, 2, dtype=np.int32)
     w = synth.Workload("balanced", R, C, rp, ci, rng.uniform(-1, 1, ci.size).astype(np.float32),
                        rng.uniform(-1, 1, C).astype(np.float32),
                        rng.uniform(-1, 1, R).astype(np.float32))
-    print(f"[case] blocked items R={R} nnz={w.nnz}", flush=True)
+    print(f"[case] blocked items {mode} R={R} nnz={w.nnz}", flush=True)
     h = build("coo_blocked", w, dev)
     assert h.info["col_blocks"] == 2
     items = h.info["work_items"]
-    if balanced:
-        assert items == 256 and h.info["num_tiles"] > items
+    sitem, ichunk = h.array("bc_slice_item"), h.array("bc_item_chunk")
+    per_slice = np.diff(sitem).tolist()
+    if mode == "balanced":
+        assert per_slice == [128, 128] and h.info["num_tiles"] > items
+    elif mode == "mixed":
+        assert per_slice[0] == 128 and np.diff(ichunk[sitem[1]:]).tolist() == [1] * per_slice[1]
     else:
         assert items == h.info["num_tiles"]
     check_builder(h, w)
     y_ref, bound = oracle.spmv_csr(w.row_ptrs, w.col_idx, w.values, w.x, w.y)
     _, _, _, x, y0 = to_dev(w, dev)
-    assert_rows(run_once(h, x, y0), y_ref, bound, f"items {blocks}+{extra_rows}")
+    assert_rows(run_once(h, x, y0), y_ref, bound, f"items {mode} {blocks}+{extra_rows}")
     y = y0.clone()
     h.run(x, y)
     h.run(x, y)
     torch.cuda.synchronize()
     y2 = 2 * (y_ref - w.y.astype(np.float64)) + w.y.astype(np.float64)
-    assert_rows(y.cpu().numpy(), y2, 2 * bound, f"items {blocks}+{extra_rows} twice")
+    assert_rows(y.cpu().numpy(), y2, 2 * bound, f"items {mode} {blocks}+{extra_rows} twice")
 
 
 @pytest.mark.parametrize("S", [1, 2])

@@ -850,8 +850,9 @@ int orc_coo_blocked(int64_t R, int64_t C, int64_t nnz, const int32_t *row_ptrs,
     int64_t *rate = (int64_t *)calloc((size_t)(nseg > 0 ? nseg : 1), sizeof(int64_t));
     int64_t *load = (int64_t *)calloc((size_t)P, sizeof(int64_t));
     int64_t *cut = (int64_t *)calloc((size_t)P + 1, sizeof(int64_t));
-    /* at most one chunk per entry, plus one per work item's cut */
-    int64_t cap = nnz + S * P + 1;
+    /* chunks: by chunk at most ceil(n/E) <= n/E + 1 per segment of n entries; */
+    /* balanced at most one per segment plus one per cut                       */
+    int64_t cap = nnz / E + nseg + S * P + 2;
     int64_t *ch = (int64_t *)malloc(sizeof(int64_t) * 3 * (size_t)cap);
     int64_t *item_first = (int64_t *)malloc(sizeof(int64_t) * (size_t)cap);
     int64_t *slice_first_item = (int64_t *)malloc(sizeof(int64_t) * (size_t)(S + 1));

@@ -694,7 +694,8 @@ def test_blocked_hot_rows(dev):
 
 
 @pytest.mark.parametrize("blocks,extra_rows,mode", [(64, 0, "chunk"), (65, 0, "balanced"),
-                                                     (65, 11_000, "balanced"), (65, 0, "mixed")])
+                                                     (65, 11_000, "balanced"), (65, 0, "mixed"),
+                                                     (81, 0, "holes")])
 def test_blocked_balanced_items(dev, blocks, extra_rows, mode):
     """2 x slices of 2M columns, 2 entries per row.  With 64 row blocks each
     slice's 128 chunks fill its 128 CUs once and stay one chunk per work
@@ -703,7 +704,9 @@ def test_blocked_balanced_items(dev, blocks, extra_rows, mode):
     equal cost, chunks split at the items' ends, several chunks per item.
     Mixed: every row's entries in the first slice but one row in 8 with a
     third entry in the second, which is then too small to balance (one chunk
-    per item) while the first is balanced.  Arrays bit-exact against the
+    per item) while the first is balanced.  Holes: 81 blocks, every fifth
+    one empty (65 with entries): empty segments inside balanced slices.
+    Arrays bit-exact against the
     oracle; y within the row bound, once and twice in a row (the partials
     reset between an item's chunks)."""
     rng = np.random.default_rng(4100 + blocks + extra_rows + (mode == "mixed"))
@@ -718,6 +721,10 @@ def test_blocked_balanced_items(dev, blocks, extra_rows, mode):
         ci = np.concatenate([np.concatenate([c, [t]]) if t >= 0 else c
                              for c, t in zip(cols, third)]).astype(np.int32)
         rp = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    elif mode == "holes":
+        keep = (np.arange(R) // spmv.BC_BLOCK_ROWS) % 5 != 4
+        ci = cols[keep].reshape(-1).astype(np.int32)
+        rp = np.concatenate([[0], np.cumsum(2 * keep)]).astype(np.int32)
     else:
         ci = cols.reshape(-1).astype(np.int32)
         rp = np.arange(0, 2 * R + 1, 2, dtype=np.int32)
@@ -730,7 +737,7 @@ def test_blocked_balanced_items(dev, blocks, extra_rows, mode):
     items = h.info["work_items"]
     sitem, ichunk = h.array("bc_slice_item"), h.array("bc_item_chunk")
     per_slice = np.diff(sitem).tolist()
-    if mode == "balanced":
+    if mode in ("balanced", "holes"):
         assert per_slice == [128, 128] and h.info["num_tiles"] > items
     elif mode == "mixed":
         assert per_slice[0] == 128 and np.diff(ichunk[sitem[1]:]).tolist() == [1] * per_slice[1]

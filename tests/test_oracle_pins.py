@@ -918,6 +918,31 @@ def test_coo_blocked_balanced_uniform_rate():
     assert {cut[w + 1] - cut[w] for w in range(P)} == {103, 104}
 
 
+def test_coo_blocked_balanced_skips_empty_blocks():
+    """The slice of the hand-derived balanced example with an empty row block
+    after each full one: empty segments cost nothing, so the items' cuts fall
+    at the same entry positions, ceil(3300*w/32), and only the chunks' block
+    numbers change (2*b instead of b)."""
+    S, P, rows, n = 8, 32, 33, 100
+    rp1, ci, v, C = _one_line_per_entry(rows, n, S, 3200)
+    lens = np.zeros(2 * rows, np.int64)
+    lens[0::2] = n
+    rp = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    o = oracle.csr_to_coo_blocked(rp, ci, v, C, S, 1, 200, 0, 10**6)
+    cut = [-(-rows * n * w // P) for w in range(P + 1)]
+    blk, first = [], []
+    for w in range(P):
+        first.append(len(blk))
+        e = cut[w]
+        while e < cut[w + 1]:
+            e1 = min(cut[w + 1], (e // n + 1) * n)
+            blk.append(2 * (e // n))
+            e = e1
+    first.append(len(blk))
+    assert o["item_chunk"].tolist() == first
+    assert o["chunk_blk"].tolist() == blk
+
+
 def test_coo_blocked_even_slice_stays_by_chunk():
     """As above with 32 blocks: the 32 chunks fill the 32 loads once, most =
     100 * 4096 = total / 32, 8*most*32 = 104,857,600 <= 9*total =

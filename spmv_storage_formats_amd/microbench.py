@@ -6,8 +6,9 @@ library).
 
 ``gather_rates``: 64M 4-byte gathers x[idx[i]] per pattern, each timed with
 HIP events after a 1 GiB cache flush (median of 9): random indices, indices
-sorted inside each 64-lane group with mean spacing 16 (two lanes per 128-byte
-line) or 4 (eight per line), and consecutive indices; from an x of 2 MiB (one
+sorted inside each 64-lane group with mean spacing 16, 8 or 4 (two, four or
+eight lanes per 128-byte line), the four-per-line sets with each group's
+lanes shuffled, and consecutive indices; from an x of 2 MiB (one
 XCD's L2 keeps it with room to spare), 4 MiB (the size of an L2), 8 MiB and
 16 MiB.
 ``lds_rates``: random-address float adds into LDS, 512 workgroups of 1024
@@ -65,13 +66,20 @@ def _time(torch, fn, flush, reps=9):
 
 
 def _patterns(torch, dev, n, X, gen):
-    """Index tensors (int32) of n gathers from an x of X floats."""
+    """Index tensors (int32) of n gathers from an x of X floats.  The
+    shuffled pattern holds the same index sets per 64-lane group as the
+    4-per-line one, each group's lanes in a random order."""
     g = n // 64
     out = {"random": torch.randint(0, X, (n,), device=dev, generator=gen, dtype=torch.int64)}
     start = torch.randint(0, X, (g, 1), device=dev, generator=gen, dtype=torch.int64)
-    for name, hi in (("sorted_2_per_line", 32), ("sorted_8_per_line", 8)):
+    for name, hi in (("sorted_2_per_line", 32), ("sorted_4_per_line", 16),
+                     ("sorted_8_per_line", 8)):
         gaps = torch.randint(1, hi, (g, 64), device=dev, generator=gen, dtype=torch.int64)
-        out[name] = ((start + torch.cumsum(gaps, dim=1)) % X).reshape(-1)
+        idx = (start + torch.cumsum(gaps, dim=1)) % X
+        out[name] = idx.reshape(-1)
+        if hi == 16:
+            perm = torch.argsort(torch.rand(g, 64, device=dev, generator=gen), dim=1)
+            out["sorted_4_per_line_shuffled"] = torch.gather(idx, 1, perm).reshape(-1)
     out["consecutive"] = torch.arange(n, device=dev, dtype=torch.int64) % X
     return {k: v.to(torch.int32) for k, v in out.items()}
 

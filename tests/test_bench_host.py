@@ -59,3 +59,24 @@ def test_bench_refuses_more_than_one_gpu():
     assert p.returncode == 2
     assert "one GPU" in p.stderr
     assert p.stdout == ""
+
+
+@pytest.mark.parametrize("key,kernel,trace", [
+    ("c1/ell", "k_ell", "k_ell_laplacian2d_256_kernel_trace.md"),
+    ("c2/ell", "k_ell4", "k_ell4_random_rows_1Mx5_kernel_trace.md"),
+    ("c3/ell_xtile", "k_ell_xtile", "k_ell_xtile_stencil27_128_kernel_trace.md"),
+    ("c4/coo_blocked", "k_coo_blocked", "k_coo_blocked_skewed_2M_kernel_trace.md"),
+    ("c5/coo_blocked", "k_coo_blocked", "k_coo_blocked_power_law_4M_kernel_trace.md")])
+def test_committed_profiles_match_the_kernel_sources(key, kernel, trace):
+    """Every workload's automatic format has a committed counter summary
+    taken on the current kernel code (its source hash matches), so the bench
+    line's traffic and profiled duration are filled in; the duration it
+    carries is the one in the kernel's rocprofv3 trace summary."""
+    import re
+    e = bench.profiled_entry(key)
+    assert e is not None, f"{key}: no summary for the current kernel sources"
+    assert e["kernel"] == kernel
+    text = open(os.path.join(ROOT, "profiles", trace)).read()
+    m = re.search(r"^\| " + re.escape(kernel) + r" \| (\d+) \| ([0-9.]+) \|", text, re.M)
+    assert m is not None and float(m.group(2)) == e["kernel_avg_us"]
+    assert e["hbm_bytes_per_launch"] > 0 and e["alg_bytes"] > 0

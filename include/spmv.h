@@ -88,6 +88,11 @@ typedef enum spmv_status {
  * workgroups (a chunk costing its entries times r_s), would leave the most
  * loaded with more than 9/8 of total / P (8 * most * P > 9 * total). */
 #define SPMV_BC_BLOCK_ROWS 32768
+/* A blocked-COO build whose SPMV_BC_BLOCK_ROWS-row layout cuts some x slice
+ * into balanced work items is redone with blocks of SPMV_BC_BLOCK_ROWS_TALL
+ * rows (the most whose partials fit the LDS); spmv_info.block_rows tells
+ * which. */
+#define SPMV_BC_BLOCK_ROWS_TALL 38912
 
 /* Storage formats / kernels.  SPMV_AUTO lets the selector choose. */
 typedef enum spmv_format {
@@ -191,7 +196,7 @@ typedef struct spmv_info {
     int64_t device_bytes;  /* device memory owned by the handle           */
     int64_t groups;        /* blocked COO: groups of 64 slots             */
     int64_t wide_groups;   /* blocked COO: groups whose columns span > 65535 */
-    int32_t block_rows;    /* blocked COO: SPMV_BC_BLOCK_ROWS             */
+    int32_t block_rows;    /* blocked COO: SPMV_BC_BLOCK_ROWS or SPMV_BC_BLOCK_ROWS_TALL */
     int32_t chunk_entries; /* blocked COO: T, entries per chunk           */
     int32_t hot_slots;     /* blocked COO: hot rows per block (32)        */
     int32_t hot_min_len;   /* blocked COO: rows this long or longer may be hot (64*S+1) */

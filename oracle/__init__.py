@@ -97,6 +97,7 @@ def _load():
                                            _i64, _i64, _i64, _i64p] + [ctypes.c_void_p] * 10),
         "orc_select_build": (ctypes.c_int, [_i64, _i64, _i64, _i32p, _i32p, _i64, _i64p]),
         "orc_bc_chunk_entries": (_i64, [_i64]),
+        "orc_bc_block_rows": (_i64, [_i64, _i64, _i64, _i32p, _i32p, _i64, _i64, _i64, _i64]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -294,13 +295,13 @@ def csr_to_coo_blocked(row_ptrs, col_idx, values, num_cols, slices, block_rows, 
     vb = _bits(values)
     nnz = ci.shape[0]
     lib = _load()
-    sizes = np.zeros(4, np.int64)
+    sizes = np.zeros(5, np.int64)
     args = (R, num_cols, nnz, rp, ci, vb, slices, block_rows, chunk_entries, hot_slots,
             hot_min_len, sizes)
     st = lib.orc_coo_blocked(*args, *([None] * 10))
     if st != OK:
         raise ValueError(f"orc_coo_blocked: status {st}")
-    nch, ng, nw, nit = (int(v) for v in sizes)
+    nch, ng, nw, nit, nbal = (int(v) for v in sizes)
     nblk = (R + block_rows - 1) // block_rows
     out = {"chunk_grp": np.zeros(nch + 1, np.int32), "chunk_blk": np.zeros(max(nch, 1), np.int32),
            "slice_chunk": np.zeros(slices + 1, np.int32),
@@ -318,7 +319,16 @@ def csr_to_coo_blocked(row_ptrs, col_idx, values, num_cols, slices, block_rows, 
     out["pk"] = out["pk"][:64 * ng]
     out["val"] = out["val"][:64 * ng].view(np.float32)
     out["wide"] = out["wide"][:64 * nw]
+    out["balanced_slices"] = nbal
     return out
+
+
+def bc_block_rows(row_ptrs, col_idx, num_cols, slices, chunk_entries, hot_slots, hot_min_len):
+    """Blocked COO block height for this matrix (orc_bc_block_rows)."""
+    rp = _i32(row_ptrs)
+    ci = _i32(col_idx)
+    return int(_load().orc_bc_block_rows(rp.shape[0] - 1, num_cols, ci.shape[0], rp, ci,
+                                         slices, chunk_entries, hot_slots, hot_min_len))
 
 
 def bc_chunk_entries(nnz):

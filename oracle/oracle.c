@@ -742,8 +742,8 @@ int orc_csr_to_ell_xtile(int64_t R, const int32_t *row_ptrs, const int32_t *col_
 /*   chunk_blk[c] = its row block, slice_chunk[k] = first chunk of slice k  */
 /*   (S+1 entries), slice_item[k] = first work item of slice k (S+1),       */
 /*   item_chunk[i] = first chunk of work item i (items+1).                  */
-/* sizes[0..3] = chunks, groups, wide groups, work items; with chunk_grp == */
-/* NULL only the sizes are computed.                                        */
+/* sizes[0..4] = chunks, groups, wide groups, work items, balanced slices; */
+/* with chunk_grp == NULL only the sizes are computed.                      */
 /* ------------------------------------------------------------------------ */
 
 static const int64_t *g_hot_len;
@@ -872,7 +872,7 @@ int orc_coo_blocked(int64_t R, int64_t C, int64_t nnz, const int32_t *row_ptrs,
                 lines[s]++;
         rate[s] = n > 0 ? (n + 3 * lines[s]) * 1024 / n : 0;
     }
-    int64_t nch = 0, nitem = 0;
+    int64_t nch = 0, nitem = 0, nbal = 0;
     for (int64_t k = 0; k < S; ++k) {
         const int64_t first = seg_start[k * B], end = seg_start[(k + 1) * B];
         slice_first_item[k] = nitem;
@@ -903,6 +903,7 @@ int orc_coo_blocked(int64_t R, int64_t C, int64_t nnz, const int32_t *row_ptrs,
         }
         if (end - first >= P * (RT / 4 > 64 ? RT / 4 : 64) && 8 * most * P > 9 * total) {
             /* balanced: drop the by-chunk cut of this slice, cut by cost */
+            ++nbal;
             nch = slice_first_chunk[k];
             nitem = slice_first_item[k];
             int64_t spent = 0, w = 1;   /* spent: cost of the entries before entry j */
@@ -996,11 +997,32 @@ int orc_coo_blocked(int64_t R, int64_t C, int64_t nnz, const int32_t *row_ptrs,
     sizes[1] = ngrp;
     sizes[2] = nwide;
     sizes[3] = nitem;
+    sizes[4] = nbal;
     free(lines); free(rate); free(load); free(cut); free(ch); free(item_first);
     free(slice_first_item); free(slice_first_chunk);
     free(row); free(by_col); free(order); free(cnt_col); free(seg_start);
     free(len); free(code); free(cand);
     return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Blocked COO block height: RT = 32768, unless that layout (orc_coo_blocked */
+/* with the given chunk size and hot-row rule) cuts some slice into         */
+/* balanced work items; then RT = 38912.  Reading of [INTRO, memory-        */
+/* efficiency check]: a taller block puts more of a segment's entries on    */
+/* each x line; it is taken only where the chunks no longer fill the CUs in */
+/* whole rounds anyway.  Returns -1 on a refused layout.                    */
+/* ------------------------------------------------------------------------ */
+int64_t orc_bc_block_rows(int64_t R, int64_t C, int64_t nnz, const int32_t *row_ptrs,
+                          const int32_t *col_idx, int64_t S, int64_t E, int64_t H,
+                          int64_t hot_min_len)
+{
+    int64_t sizes[5] = {0, 0, 0, 0, 0};
+    int st = orc_coo_blocked(R, C, nnz, row_ptrs, col_idx, NULL, S, 32768, E, H, hot_min_len,
+                             sizes, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL);
+    if (st != ORC_OK)
+        return -1;
+    return sizes[4] > 0 ? 38912 : 32768;
 }
 
 /* ------------------------------------------------------------------------ */

@@ -49,6 +49,7 @@ ARRAYS = {
 }
 CG_NOALLOC_MAX_ROWS = 1048576   # SPMV_CG_NOALLOC_MAX_ROWS in include/spmv.h
 BC_BLOCK_ROWS = 32768           # SPMV_BC_BLOCK_ROWS: blocked COO rows per row block
+BC_BLOCK_ROWS_TALL = 38912      # SPMV_BC_BLOCK_ROWS_TALL: blocks of balanced layouts
 STATUS = {0: "SPMV_OK", 1: "SPMV_ERR_INVALID_ARG", 2: "SPMV_ERR_BAD_ROWPTRS",
           3: "SPMV_ERR_BAD_COLIDX", 4: "SPMV_ERR_BAD_ROWIDX", 5: "SPMV_ERR_TOO_LARGE",
           6: "SPMV_ERR_OOM", 7: "SPMV_ERR_HIP", 8: "SPMV_ERR_DEVICE"}

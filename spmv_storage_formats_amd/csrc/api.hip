@@ -963,7 +963,7 @@ spmv_status spmv_get_info(const spmv_handle *h, spmv_info *info) {
     if (h->format == SPMV_COO_BLOCKED) {
         info->groups = h->bc_groups;
         info->wide_groups = h->bc_wide_groups;
-        info->block_rows = kBcRows;
+        info->block_rows = h->bc_rows;
         info->chunk_entries = static_cast<int32_t>(h->bc_chunk);
         info->hot_slots = kBcHot;
         info->hot_min_len = h->bc_hot_min_len;

@@ -86,30 +86,31 @@ __global__ __launch_bounds__(kThreads) void k_bc_hot_candidates(int32_t R,
     }
 }
 
-// code[r] = r mod kBcRows, then kBcRows + h for hot row h of each block.
-__global__ __launch_bounds__(kThreads) void k_bc_codes(int32_t R, int32_t *__restrict__ code) {
+// code[r] = r mod RB, then RB + h for hot row h of each block.
+__global__ __launch_bounds__(kThreads) void k_bc_codes(int32_t R, int32_t RB,
+                                                       int32_t *__restrict__ code) {
     const int64_t r = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-    if (r < R) code[r] = static_cast<int32_t>(r % kBcRows);
+    if (r < R) code[r] = static_cast<int32_t>(r % RB);
 }
 
-__global__ __launch_bounds__(kThreads) void k_bc_hot_codes(int64_t slots,
+__global__ __launch_bounds__(kThreads) void k_bc_hot_codes(int64_t slots, int32_t RB,
                                                            const int32_t *__restrict__ hot,
                                                            int32_t *__restrict__ code) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
     if (i >= slots) return;
     const int32_t r = hot[i];
-    if (r >= 0) code[r] = kBcRows + static_cast<int32_t>(i % kBcHot);
+    if (r >= 0) code[r] = RB + static_cast<int32_t>(i % kBcHot);
 }
 
 // Segment of each (column-sorted) entry: slice * nblk + block.
 __global__ __launch_bounds__(kThreads) void k_bc_seg_keys(int32_t nnz, const int32_t *__restrict__ row,
                                                           const uint32_t *__restrict__ col,
                                                           int32_t slice_cols, int32_t nblk,
-                                                          uint32_t *__restrict__ key) {
+                                                          int32_t RB, uint32_t *__restrict__ key) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
     if (i >= nnz) return;
     const uint32_t k = col[i] / static_cast<uint32_t>(slice_cols);
-    key[i] = k * static_cast<uint32_t>(nblk) + static_cast<uint32_t>(row[i] / kBcRows);
+    key[i] = k * static_cast<uint32_t>(nblk) + static_cast<uint32_t>(row[i] / RB);
 }
 
 // 1 where an entry, in (segment, column) order, is its segment's first or
@@ -239,7 +240,7 @@ __device__ inline void lds_cas_add(float *a, float v) {
 // kept in bounds by the arrays' tail padding, become padding that gathers
 // the slice's first column; a padding slot inside a group has offset 0 and
 // gathers its group's base column.
-template <int U, bool kFarX, bool kTail>
+template <int U, bool kFarX, bool kTail, int RB>
 __device__ __forceinline__ void bc_wave_step(int lw, int n, int lane, const uint32_t *pkc,
                                              const float *valc, const int32_t *basec,
                                              const int32_t *wide_col, int32_t col0,
@@ -314,13 +315,13 @@ __device__ __forceinline__ void bc_wave_step(int lw, int n, int lane, const uint
         // the last lane of each run adds the run's total to its row
         if (real && kn != k) {
             const uint32_t r = k - 1;
-            if (r >= kBcRows) mine[r - kBcRows] += q;   // this wave's own slot
+            if (r >= RB) mine[r - RB] += q;   // this wave's own slot
             else lds_cas_add(&part[r], q);
         }
     }
 }
 
-template <int U, bool kFarX>
+template <int U, bool kFarX, int RB>
 __global__ __launch_bounds__(kBcThreads) void k_coo_blocked(
     int32_t R, int32_t per, int32_t slice_cols, const int32_t *__restrict__ slice_item,
     const int32_t *__restrict__ item_chunk, const int32_t *__restrict__ chunk_grp,
@@ -328,7 +329,7 @@ __global__ __launch_bounds__(kBcThreads) void k_coo_blocked(
     const int32_t *__restrict__ base, const uint32_t *__restrict__ pk,
     const float *__restrict__ val, const int32_t *__restrict__ wide_col,
     const float *__restrict__ x, float *__restrict__ y) {
-    __shared__ float part[kBcRows];
+    __shared__ float part[RB];
     __shared__ float priv[kBcWaves * kBcHot];
     // slice k's work items on XCDs [k*per, (k+1)*per): block b runs on XCD b % 8
     const int xcd = static_cast<int>(blockIdx.x % kNumXcd);
@@ -341,7 +342,7 @@ __global__ __launch_bounds__(kBcThreads) void k_coo_blocked(
     const float *xs = x + col0;
     // -0.0 is the additive identity bit for bit: an untouched partial is
     // recognised and never added, so rows without entries keep their y bits
-    for (int i = threadIdx.x; i < kBcRows; i += kBcThreads) part[i] = -0.0f;
+    for (int i = threadIdx.x; i < RB; i += kBcThreads) part[i] = -0.0f;
     for (int i = threadIdx.x; i < kBcWaves * kBcHot; i += kBcThreads) priv[i] = -0.0f;
     __syncthreads();
     const int lane = __lane_id();
@@ -353,8 +354,8 @@ __global__ __launch_bounds__(kBcThreads) void k_coo_blocked(
         const int b = chunk_blk[c];
         const int32_t g0 = chunk_grp[c];
         const int32_t n = chunk_grp[c + 1] - g0;   // groups of this chunk
-        const int64_t r0 = static_cast<int64_t>(b) * kBcRows;
-        const int nrows = static_cast<int>(min(static_cast<int64_t>(kBcRows), R - r0));
+        const int64_t r0 = static_cast<int64_t>(b) * RB;
+        const int nrows = static_cast<int>(min(static_cast<int64_t>(RB), R - r0));
         // the chunk's arrays through wave-uniform pointers, so every load
         // below takes a 32-bit offset (slots past 2^31 included)
         const uint32_t *pkc = pk + static_cast<int64_t>(g0) * kWave;
@@ -364,25 +365,28 @@ __global__ __launch_bounds__(kBcThreads) void k_coo_blocked(
         // the U consecutive groups lw .. lw + U - 1
         int lw = wave * U;
         for (; lw + U <= n; lw += kBcWaves * U)
-            bc_wave_step<U, kFarX, false>(lw, n, lane, pkc, valc, basec, wide_col, col0, xs, part,
+            bc_wave_step<U, kFarX, false, RB>(lw, n, lane, pkc, valc, basec, wide_col, col0, xs, part,
                                           mine);
         if (lw < n)
-            bc_wave_step<U, kFarX, true>(lw, n, lane, pkc, valc, basec, wide_col, col0, xs, part,
+            bc_wave_step<U, kFarX, true, RB>(lw, n, lane, pkc, valc, basec, wide_col, col0, xs, part,
                                          mine);
         __syncthreads();
         // every partial that was touched goes to y (a full block's partials
         // read 8 at a time, so one LDS wait covers 8 of them); when another
         // chunk follows, each thread resets the partials it has just read
         const bool more = c + 1 < c1;
-        if (nrows == kBcRows) {
+        if (nrows == RB) {
+            constexpr int P = RB / kBcThreads;   // partials per thread
 #pragma unroll
-            for (int j0 = 0; j0 < kBcRows / kBcThreads; j0 += 8) {
+            for (int j0 = 0; j0 < P; j0 += 8) {
                 float s[8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) s[j] = part[threadIdx.x + (j0 + j) * kBcThreads];
+                for (int j = 0; j < 8; ++j)
+                    s[j] = j0 + j < P ? part[threadIdx.x + (j0 + j) * kBcThreads] : -0.0f;
                 if (more) {
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) part[threadIdx.x + (j0 + j) * kBcThreads] = -0.0f;
+                    for (int j = 0; j < 8; ++j)
+                        if (j0 + j < P) part[threadIdx.x + (j0 + j) * kBcThreads] = -0.0f;
                 }
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
@@ -464,14 +468,21 @@ bool bc_auto_rule(const spmv_stats &st) {
     return scattered && 4 * C > kL2Bytes && 32 * nnz * rows >= R * C;
 }
 
-spmv_status build_coo_blocked(spmv_handle *h, int32_t R, int32_t C, int32_t nnz,
-                              const int32_t *rp, const int32_t *col, const float *val, int32_t S,
-                              hipStream_t s, Scratch &scratch) {
+namespace {
+
+// One build at block height RB; *balanced tells whether some slice took
+// balanced work items.
+spmv_status build_coo_blocked_at(spmv_handle *h, int32_t R, int32_t C, int32_t nnz,
+                                 const int32_t *rp, const int32_t *col, const float *val,
+                                 int32_t S, int32_t RB, bool *balanced_any, hipStream_t s,
+                                 Scratch &scratch) {
+    *balanced_any = false;
     const int64_t sc = std::max<int64_t>((static_cast<int64_t>(C) + S - 1) / S, 1);
-    const int64_t nblk = (static_cast<int64_t>(R) + kBcRows - 1) / kBcRows;
+    const int64_t nblk = (static_cast<int64_t>(R) + RB - 1) / RB;
     const int64_t nseg = S * nblk;
     h->col_blocks = S;
     h->slice_cols = static_cast<int32_t>(sc);
+    h->bc_rows = RB;
     h->bc_blocks = nblk;
     h->bc_hot_min_len = kBcHotPerSlice * S + 1;
     h->bc_chunk = bc_chunk_entries(nnz);
@@ -504,14 +515,14 @@ spmv_status build_coo_blocked(spmv_handle *h, int32_t R, int32_t C, int32_t nnz,
     std::vector<int32_t> order(static_cast<size_t>(ncand));
     for (int32_t i = 0; i < ncand; ++i) order[i] = i;
     std::sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
-        const int32_t ba = crow[a] / kBcRows, bb = crow[b] / kBcRows;
+        const int32_t ba = crow[a] / RB, bb = crow[b] / RB;
         if (ba != bb) return ba < bb;
         if (clen[a] != clen[b]) return clen[a] > clen[b];
         return crow[a] < crow[b];
     });
     std::vector<int32_t> hot(static_cast<size_t>(nblk * kBcHot), -1);
     for (int32_t i = 0, prev = -1, h_in = 0; i < ncand; ++i) {
-        const int32_t r = crow[order[i]], b = r / kBcRows;
+        const int32_t r = crow[order[i]], b = r / RB;
         h_in = (b == prev) ? h_in + 1 : 0;
         prev = b;
         if (h_in < kBcHot) hot[static_cast<size_t>(b) * kBcHot + h_in] = r;
@@ -521,9 +532,9 @@ spmv_status build_coo_blocked(spmv_handle *h, int32_t R, int32_t C, int32_t nnz,
                             hipMemcpyHostToDevice, s));
     int32_t *code = nullptr;
     SPMV_TRY(scratch.alloc(&code, static_cast<size_t>(R)));
-    k_bc_codes<<<grid_for(R, kThreads), kThreads, 0, s>>>(R, code);
+    k_bc_codes<<<grid_for(R, kThreads), kThreads, 0, s>>>(R, RB, code);
     SPMV_HIP(hipGetLastError());
-    k_bc_hot_codes<<<grid_for(nblk * kBcHot, kThreads), kThreads, 0, s>>>(nblk * kBcHot,
+    k_bc_hot_codes<<<grid_for(nblk * kBcHot, kThreads), kThreads, 0, s>>>(nblk * kBcHot, RB,
                                                                          h->a.bc_hot, code);
     SPMV_HIP(hipGetLastError());
 
@@ -549,7 +560,7 @@ spmv_status build_coo_blocked(spmv_handle *h, int32_t R, int32_t C, int32_t nnz,
                             bits_for(static_cast<uint64_t>(C > 0 ? C - 1 : 0)), s, scratch));
     }
     k_bc_seg_keys<<<grid_for(nnz, kThreads), kThreads, 0, s>>>(
-        nnz, row1, col1, static_cast<int32_t>(sc), static_cast<int32_t>(nblk), seg);
+        nnz, row1, col1, static_cast<int32_t>(sc), static_cast<int32_t>(nblk), RB, seg);
     SPMV_HIP(hipGetLastError());
     const uint32_t *seg_sorted = nullptr;
     {
@@ -633,7 +644,7 @@ spmv_status build_coo_blocked(spmv_handle *h, int32_t R, int32_t C, int32_t nnz,
             }
         }
         bool balanced = false;
-        if (s1 - s0 >= P * kBcChunkMin) {
+        if (s1 - s0 >= P * std::max<int64_t>(RB / 4, kWave)) {
             load.assign(static_cast<size_t>(P), 0);
             int64_t most = 0;
             for (size_t i = 0; i < dyn.size(); i += 3) {
@@ -643,6 +654,7 @@ spmv_status build_coo_blocked(spmv_handle *h, int32_t R, int32_t C, int32_t nnz,
             }
             balanced = kBcSkewDen * most * P > kBcSkewNum * total;
         }
+        *balanced_any = *balanced_any || balanced;
         if (!balanced) {
             for (size_t i = 0; i < dyn.size(); i += 3) {
                 ichunk.push_back(static_cast<int32_t>(cblk.size()));
@@ -738,20 +750,51 @@ spmv_status build_coo_blocked(spmv_handle *h, int32_t R, int32_t C, int32_t nnz,
     return SPMV_OK;
 }
 
+}  // namespace
+
+spmv_status build_coo_blocked(spmv_handle *h, int32_t R, int32_t C, int32_t nnz,
+                              const int32_t *rp, const int32_t *col, const float *val, int32_t S,
+                              hipStream_t s, Scratch &scratch) {
+    // Blocks of kBcRows rows; when that cuts some slice into balanced work
+    // items (the chunks would not fill the CUs in whole rounds), the chunk
+    // rounds no longer matter and the build is redone with kBcRowsTall-row
+    // blocks, the tallest whose partials still fit the LDS: more of a
+    // segment's entries then share each x line
+    const size_t mark = h->owned.size();
+    const int64_t bytes = h->device_bytes;
+    const DevArrays arrays = h->a;
+    bool balanced = false;
+    SPMV_TRY(build_coo_blocked_at(h, R, C, nnz, rp, col, val, S, kBcRows, &balanced, s, scratch));
+    if (!balanced) return SPMV_OK;
+    SPMV_HIP(hipStreamSynchronize(s));
+    for (size_t i = mark; i < h->owned.size(); ++i) SPMV_HIP(hipFree(h->owned[i]));
+    h->owned.resize(mark);
+    h->device_bytes = bytes;
+    h->a = arrays;
+    return build_coo_blocked_at(h, R, C, nnz, rp, col, val, S, kBcRowsTall, &balanced, s, scratch);
+}
+
 hipError_t launch_coo_blocked(const spmv_handle *h, const float *x, float *y, hipStream_t s) {
     if (h->bc_grid <= 0) return hipSuccess;
     const int32_t R = static_cast<int32_t>(h->stats.num_rows);
     const int32_t per = kNumXcd / h->col_blocks;
     const DevArrays &a = h->a;
     const dim3 grid(static_cast<unsigned>(h->bc_grid));
-    if (h->slice_cols > (1 << 30))
-        k_coo_blocked<kBcUnroll, true><<<grid, kBcThreads, 0, s>>>(
-            R, per, h->slice_cols, a.bc_slice_item, a.bc_item_chunk, a.bc_chunk_grp,
-            a.bc_chunk_blk, a.bc_hot, a.bc_base, a.bc_pk, a.bc_val, a.bc_wide, x, y);
+    const bool far = h->slice_cols > (1 << 30);
+    const bool tall = h->bc_rows == kBcRowsTall;
+#define SPMV_BC_LAUNCH(FAR, RB)                                                                   \
+    k_coo_blocked<kBcUnroll, FAR, RB><<<grid, kBcThreads, 0, s>>>(                                \
+        R, per, h->slice_cols, a.bc_slice_item, a.bc_item_chunk, a.bc_chunk_grp, a.bc_chunk_blk,  \
+        a.bc_hot, a.bc_base, a.bc_pk, a.bc_val, a.bc_wide, x, y)
+    if (far && tall)
+        SPMV_BC_LAUNCH(true, kBcRowsTall);
+    else if (far)
+        SPMV_BC_LAUNCH(true, kBcRows);
+    else if (tall)
+        SPMV_BC_LAUNCH(false, kBcRowsTall);
     else
-        k_coo_blocked<kBcUnroll, false><<<grid, kBcThreads, 0, s>>>(
-            R, per, h->slice_cols, a.bc_slice_item, a.bc_item_chunk, a.bc_chunk_grp,
-            a.bc_chunk_blk, a.bc_hot, a.bc_base, a.bc_pk, a.bc_val, a.bc_wide, x, y);
+        SPMV_BC_LAUNCH(false, kBcRows);
+#undef SPMV_BC_LAUNCH
     return hipGetLastError();
 }
 

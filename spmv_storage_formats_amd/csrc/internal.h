@@ -62,6 +62,7 @@ constexpr int kXtileAutoRows = 64 * kTileRows;
 // entries per x line) with 6, 8, 10 groups per wave 267, 272, 274 and 97 us
 // (with 4 and 5 groups: 264 us); all before the chunk-relative addressing.
 constexpr int kBcRows = SPMV_BC_BLOCK_ROWS;
+constexpr int kBcRowsTall = SPMV_BC_BLOCK_ROWS_TALL;
 constexpr int kBcHot = 32;
 constexpr int kBcHotPerSlice = 64;
 constexpr int kBcThreads = 1024;
@@ -149,6 +150,7 @@ struct spmv_handle {
     int32_t col_blocks = 1;
     int32_t slice_cols = 0;
     // blocked COO
+    int32_t bc_rows = 0;            // rows per row block (kBcRows or kBcRowsTall)
     int64_t bc_blocks = 0;          // row blocks
     int64_t bc_groups = 0;          // groups of 64 slots
     int64_t bc_chunk = 0;           // entries per chunk (a segment's last may hold fewer)

@@ -30,6 +30,8 @@ def test_binding_constants_match_the_header():
     hdr = open(os.path.join(os.path.dirname(spmv.__file__), "..", "include", "spmv.h")).read()
     defs = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define (SPMV_\w+) (\d+)", hdr)}
     assert defs["SPMV_BC_BLOCK_ROWS"] == spmv.BC_BLOCK_ROWS
+    assert defs["SPMV_BC_BLOCK_ROWS_TALL"] == spmv.BC_BLOCK_ROWS_TALL
+    assert spmv.BC_BLOCK_ROWS_TALL + 32 < 0xFFFF
     assert defs["SPMV_CG_NOALLOC_MAX_ROWS"] == spmv.CG_NOALLOC_MAX_ROWS
     assert spmv.BC_BLOCK_ROWS + 32 < 0xFFFF   # row codes and hot codes fit 16 bits
 

@@ -194,6 +194,9 @@ def check_blocked(h, w):
     """Every blocked-COO array equals the oracle's, built with the handle's own
     slice count, block height, chunk size and hot-row rule (spmv_info)."""
     i = h.info
+    assert i["block_rows"] == oracle.bc_block_rows(w.row_ptrs, w.col_idx, w.num_cols,
+                                                   i["col_blocks"], i["chunk_entries"],
+                                                   i["hot_slots"], i["hot_min_len"])
     o = oracle.csr_to_coo_blocked(w.row_ptrs, w.col_idx, w.values, w.num_cols, i["col_blocks"],
                                   i["block_rows"], i["chunk_entries"], i["hot_slots"],
                                   i["hot_min_len"])

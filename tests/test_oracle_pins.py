@@ -1067,6 +1067,29 @@ def _spread(rp, ci, C):
     return sum(d) // len(d)
 
 
+@pytest.mark.parametrize("blocks,tall", [(64, False), (65, True)])
+def test_bc_block_rows_rule(blocks, tall):
+    """2 x slices of 2M columns, one entry per row in each slice, 32768-row
+    blocks: 64 blocks give each slice 128 chunks (2 per segment) that fill its
+    128 CUs once, so the layout stays by chunk and the height 32768; with 65
+    blocks the 130 chunks would leave a short second round, the slice is
+    balanced, and the rule takes the taller height."""
+    rng = np.random.default_rng(77 + blocks)
+    R, C = blocks * 32768, 2_000_000
+    ci = np.stack([rng.integers(0, C // 2, size=R), rng.integers(C // 2, C, size=R)],
+                  1).reshape(-1).astype(np.int32)
+    rp = np.arange(0, 2 * R + 1, 2, dtype=np.int32)
+    E = oracle.bc_chunk_entries(ci.size)
+    o = oracle.csr_to_coo_blocked(rp, ci, np.ones(ci.size, np.float32), C, 2, 32768, E, 32, 129)
+    if not tall:   # by chunk: two chunks per segment, one work item each
+        assert np.diff(o["slice_chunk"]).tolist() == [2 * blocks, 2 * blocks]
+        assert np.diff(o["slice_item"]).tolist() == [2 * blocks, 2 * blocks]
+    else:          # balanced: one work item per CU of each slice
+        assert np.diff(o["slice_item"]).tolist() == [128, 128]
+    assert o["balanced_slices"] == (2 if tall else 0)
+    assert oracle.bc_block_rows(rp, ci, C, 2, E, 32, 129) == (38912 if tall else 32768)
+
+
 def test_select_build_fig14_1():
     w = _fig()
     assert oracle.select_build(w.row_ptrs, w.col_idx, 4, 16384) == ("ell", 0, 0, 1)

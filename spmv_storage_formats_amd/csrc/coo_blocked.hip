@@ -15,7 +15,9 @@
 // 3.2).
 //
 // Layout (every array owned by the handle; R rows, C columns):
-//   - rows in blocks of kBcRows; columns in S slices of sc = ceil(C/S); the
+//   - rows in blocks of RB = kBcRows, or kBcRowsTall when the kBcRows layout
+//     cuts some slice into balanced work items (build_coo_blocked); columns in
+//     S slices of sc = ceil(C/S); the
 //     entries of (slice k, block b) form segment k*nblk + b, ordered by column
 //     (ties keep CSR order); segments are cut into chunks of T entries (T =
 //     bc_chunk_entries(nnz); the last of a segment the remainder, joined to
@@ -27,7 +29,7 @@
 //     entries;
 //   - inside a group the entries are reordered by row code (stable), so equal
 //     rows are neighbouring lanes; the code of an entry is its row's index
-//     within the block, or kBcRows + h for the block's hot row h (the
+//     within the block, or RB + h for the block's hot row h (the
 //     kBcHot longest rows with more than kBcHotPerSlice * S entries, longest
 //     first, ties by row): hot rows get per-wave partials, so waves never
 //     contend for them;

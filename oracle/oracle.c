@@ -36,7 +36,7 @@
  *   - ELL with x tiles, blocked COO and the automatic build's storage rules
  *     are encodings and build-time rules, not formulas of the pages: each is
  *     written out as a definition at orc_csr_to_ell_xtile(), orc_coo_blocked(),
- *     orc_bc_chunk_entries() and orc_select_build().
+ *     orc_bc_chunk_entries(), orc_bc_block_rows() and orc_select_build().
  */
 #include <math.h>
 #include <stdint.h>
